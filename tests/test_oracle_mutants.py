@@ -1,0 +1,58 @@
+"""Planted mistakes in the oracle must be caught by the pins.
+
+Each mutant is a copy of oracle.c with one plausible mistake (a dropped term,
+a wrong sign, index or divisor, a rounding mode), compiled on the CPU into a
+temporary directory.  The pin battery of tests/pins.py must fail on every one
+of them; the real oracle passes it (tests/test_oracle_pins.py).
+"""
+import os
+
+import pytest
+
+import oracle
+import pins
+
+LN_GAMMA = ("double g = gamma ? load_elem(gamma, i, dtype) : 1.0;\n"
+            "                double b = beta")
+
+MUTANTS = {
+    "unbiased_variance": ("double var = q / (double)N;", "double var = q / (double)(N - 1);"),
+    "ln_eps_outside_root": ("double rs = 1.0 / sqrt(var + eps);", "double rs = 1.0 / sqrt(var) + eps;"),
+    "ln_rstd_without_root": ("double rs = 1.0 / sqrt(var + eps);", "double rs = 1.0 / (var + eps);"),
+    "ln_drop_beta": ("* rs * g + b;", "* rs * g;"),
+    "ln_gamma_reversed": (LN_GAMMA, LN_GAMMA.replace("load_elem(gamma, i,", "load_elem(gamma, N - 1 - i,")),
+    "ln_mean_sign": ("y[base + i] = (load_elem(x, base + i, dtype) - mu)",
+                     "y[base + i] = (load_elem(x, base + i, dtype) + mu)"),
+    "ln_naive_variance": ("double d = load_elem(x, base + i, dtype) - mu;\n            q += d * d;",
+                          "double d = load_elem(x, base + i, dtype);\n            q += d * d - mu * mu;"),
+    "ln_mean_divisor": ("double mu = s / (double)N;", "double mu = s / (double)(N + 1);"),
+    "ln_row_stride": ("int64_t base = r * N;\n        double s", "int64_t base = r * (N - 1);\n        double s"),
+    "rms_drop_gamma": ("y[base + i] = load_elem(x, base + i, dtype) * rs * g;",
+                       "y[base + i] = load_elem(x, base + i, dtype) * rs;"),
+    "rms_eps_outside_root": ("double rs = 1.0 / sqrt(ms + eps);", "double rs = 1.0 / sqrt(ms) + eps;"),
+    "rms_divisor": ("double ms = q / (double)N;", "double ms = q / (double)(N + 1);"),
+    "round_truncates": ("double r = rint(k);", "double r = trunc(k);"),
+    "f16_widen_bias": ("ex - 25", "ex - 24"),
+    "bf16_widen_shift": ("(uint32_t)b << 16", "(uint32_t)b << 15"),
+    "bf16_precision_off_by_one": ("rne_to_format(v, 8, -126)", "rne_to_format(v, 7, -126)"),
+    "f16_min_normal_wrong": ("rne_to_format(a, 11, -14)", "rne_to_format(a, 11, -15)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(oracle.SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique"
+    mpath = tmp_path / f"{name}.c"
+    mpath.write_text(src.replace(old, new))
+    lib = oracle.compile_c(str(mpath), str(tmp_path / f"lib{name}.so"))
+    orc = oracle.Oracle(lib)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(orc)
+        except Exception as e:          # AssertionError or a numeric failure
+            caught.append(pin.__name__)
+            break
+    assert caught, f"no pin caught the planted mistake {name}"
