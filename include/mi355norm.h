@@ -1,0 +1,117 @@
+/*
+ * mi355norm.h -- C ABI of the row-wise LayerNorm / RMSNorm forward library
+ * for AMD Instinct MI355X (gfx950, CDNA4).  Library: libmi355norm.so.
+ *
+ * The operations (page titles as printed on the pages they come from):
+ *
+ *   LayerNorm forward, per row r of x[M, N]:
+ *       mean_r = (1/N) * sum_i x[r,i]
+ *       var_r  = (1/N) * sum_i (x[r,i] - mean_r)^2          (biased: divide by N)
+ *       rstd_r = 1 / sqrt(var_r + eps)
+ *       y[r,i] = (x[r,i] - mean_r) * rstd_r * gamma[i] + beta[i]
+ *     -- "CUDA 算子工程：手写 FlashAttention v2 之路", ch. 7 "LayerNorm 与 RMSNorm",
+ *        section 7.1 (definition) and 7.6 (fused kernel storing mean and rstd per
+ *        row for the backward pass); "T3 讲解：LayerNorm / RMSNorm 的 forward",
+ *        part ② (true-N divisor, biased variance, rstd stored, fp32 statistics)
+ *        and part ⑥ (mean and rstd are fp32 whatever the I/O dtype).
+ *
+ *   RMSNorm forward, per row r:
+ *       rstd_r = 1 / sqrt((1/N) * sum_i x[r,i]^2 + eps)
+ *       y[r,i] = x[r,i] * rstd_r * gamma[i]
+ *     -- "CUDA 算子工程" ch. 7, section 7.5; "CUDA算子优化(2)：RMSNorm", section 1;
+ *        "T3 讲解" part ③.
+ *
+ * The variance is computed by a stable method (two passes over register-
+ * resident data for rows that fit one workgroup, Chan's parallel merge of
+ * (n, mean, M2) partials for rows split across workgroups), never by
+ * E[x^2] - E[x]^2 ("CUDA 算子工程" ch. 7, sections 7.3-7.4).
+ *
+ * Statistics and arithmetic are fp32 for every I/O dtype; y is rounded to
+ * the I/O dtype with round-to-nearest-even.
+ *
+ * Conventions shared by ln_fwd and rms_fwd
+ * ----------------------------------------
+ *   x, y      device pointers to row-major, contiguous [M, N] arrays of `dtype`.
+ *   gamma     device pointer to [N] of `dtype`, or NULL meaning gamma = 1.
+ *   beta      device pointer to [N] of `dtype`, or NULL meaning beta = 0
+ *             (LayerNorm only; must be NULL for rms_fwd).
+ *   mean      device pointer to fp32 [M], or NULL: not written
+ *             (LayerNorm only; must be NULL for rms_fwd).
+ *   rstd      device pointer to fp32 [M], or NULL: not written.
+ *   M         number of rows, >= 0.  M == 0 returns NORM_OK and launches nothing.
+ *   N         row length, 1 <= N <= 2^24 (16,777,216).
+ *   eps       finite and >= 0, added to the variance (or mean square) inside
+ *             the square root.  eps == 0 on a constant row gives rstd = +inf
+ *             and y = NaN, as IEEE arithmetic dictates.
+ *   dtype     one of norm_dtype.
+ *   stream    a hipStream_t, or NULL for the null stream of the current device.
+ *
+ *   Every pointer must be aligned to its element size.  16-byte aligned x, y,
+ *   gamma, beta with N * sizeof(dtype) a multiple of 16 take the 128-bit
+ *   vector path; anything else takes an element-wise path (slower, same
+ *   results).  Buffers must not overlap (y may not alias x: no in-place use).
+ *
+ * Ownership: the caller allocates and owns every buffer and keeps it alive
+ * until the stream has passed the call.  The library keeps no pointer after
+ * return.  Rows too long for one workgroup (about N > 2^17 for 2-byte and
+ * N > 2^16 for 4-byte types) use a small device workspace of
+ * M * ceil(N / chunk) * 8 bytes, taken from and returned to the device's
+ * stream-ordered memory pool on `stream` (hipMallocAsync / hipFreeAsync).
+ *
+ * Errors: arguments are validated on the host before any HIP call; a bad
+ * argument returns its status and touches nothing.  A launch failure returns
+ * NORM_ERR_HIP.  Execution is asynchronous on `stream`: faults surface at the
+ * caller's next synchronisation.  The library never changes the current
+ * device.  All functions are thread-safe.
+ */
+#ifndef MI355NORM_H
+#define MI355NORM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { NORM_F32 = 0, NORM_F16 = 1, NORM_BF16 = 2 } norm_dtype;
+
+typedef enum {
+    NORM_OK = 0,
+    NORM_ERR_NULL_ARG = 1,   /* x or y is NULL while M > 0                      */
+    NORM_ERR_BAD_SHAPE = 2,  /* M < 0, N < 1, N > 2^24, or M * N overflows       */
+    NORM_ERR_BAD_DTYPE = 3,  /* dtype not in norm_dtype                          */
+    NORM_ERR_BAD_EPS = 4,    /* eps negative, NaN or infinite                    */
+    NORM_ERR_BAD_ARG = 5,    /* misaligned pointer; beta or mean given to rms_fwd */
+    NORM_ERR_ALIAS = 6,      /* two of the buffers overlap                       */
+    NORM_ERR_HIP = 7         /* a HIP runtime call or kernel launch failed       */
+} norm_status;
+
+/* LayerNorm forward.  Returns a norm_status. */
+int ln_fwd(const void *x, const void *gamma, const void *beta, void *y,
+           float *mean, float *rstd, int64_t M, int64_t N, float eps,
+           int dtype, void *stream);
+
+/* RMSNorm forward.  beta and mean must be NULL.  Returns a norm_status. */
+int rms_fwd(const void *x, const void *gamma, const void *beta, void *y,
+            float *mean, float *rstd, int64_t M, int64_t N, float eps,
+            int dtype, void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *norm_status_str(int status);
+
+/*
+ * Describe, without launching anything, how a call with these arguments
+ * would be executed: path ("rows" or "split"), lanes per row, 16-byte vectors
+ * per lane, workgroup size, grid size, and the vector width.  `op` is 0 for
+ * LayerNorm, 1 for RMSNorm; `aligned` says whether every pointer is 16-byte
+ * aligned.  Writes at most buflen bytes (NUL-terminated) into buf and
+ * returns a norm_status.  For tests and the benchmark's reports.
+ */
+int norm_describe(int op, int64_t M, int64_t N, int dtype, int aligned,
+                  char *buf, int buflen);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI355NORM_H */

@@ -1,0 +1,154 @@
+"""rmsnorm_forward_amd -- row-wise LayerNorm / RMSNorm forward on AMD MI355X.
+
+A thin ctypes binding of libmi355norm.so (C ABI in include/mi355norm.h).
+Every step of the computation runs in the library's HIP kernels; this module
+only marshals arguments.  PyTorch is used for device memory and streams.
+
+Two layers:
+  * ln_fwd / rms_fwd / norm_status_str / norm_describe -- the C ABI entry
+    points under the same names, taking raw device addresses (ints) and
+    returning the status code;
+  * layer_norm / rms_norm -- the same calls on torch tensors: they allocate
+    y (and fp32 mean / rstd), pass the current stream, and raise
+    RuntimeError with the library's message on a non-zero status.
+
+Importing this package raises ImportError if the library has not been built
+(`python rmsnorm_forward_amd/build.py`): there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmi355norm.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python rmsnorm_forward_amd/build.py` "
+        "(hipcc, gfx950).  There is no non-HIP fallback.")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i64, _f32, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+for _name in ("ln_fwd", "rms_fwd"):
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _int, _vp]
+    _fn.restype = _int
+_lib.norm_status_str.argtypes = [_int]
+_lib.norm_status_str.restype = ctypes.c_char_p
+_lib.norm_describe.argtypes = [_int, _i64, _i64, _int, _int, ctypes.c_char_p, _int]
+_lib.norm_describe.restype = _int
+
+NORM_F32, NORM_F16, NORM_BF16 = 0, 1, 2
+NORM_OK = 0
+STATUS = {0: "NORM_OK", 1: "NORM_ERR_NULL_ARG", 2: "NORM_ERR_BAD_SHAPE", 3: "NORM_ERR_BAD_DTYPE",
+          4: "NORM_ERR_BAD_EPS", 5: "NORM_ERR_BAD_ARG", 6: "NORM_ERR_ALIAS", 7: "NORM_ERR_HIP"}
+DTYPE_NAMES = {"f32": NORM_F32, "f16": NORM_F16, "bf16": NORM_BF16}
+
+
+def _addr(p):
+    return None if not p else int(p)
+
+
+# ---------------------------------------------------------------------------
+# C ABI, same names
+# ---------------------------------------------------------------------------
+
+def ln_fwd(x, gamma, beta, y, mean, rstd, M, N, eps, dtype, stream) -> int:
+    """LayerNorm forward on device addresses; returns the norm_status code."""
+    return _lib.ln_fwd(_addr(x), _addr(gamma), _addr(beta), _addr(y), _addr(mean), _addr(rstd),
+                       int(M), int(N), float(eps), int(dtype), _addr(stream))
+
+
+def rms_fwd(x, gamma, beta, y, mean, rstd, M, N, eps, dtype, stream) -> int:
+    """RMSNorm forward on device addresses; returns the norm_status code."""
+    return _lib.rms_fwd(_addr(x), _addr(gamma), _addr(beta), _addr(y), _addr(mean), _addr(rstd),
+                        int(M), int(N), float(eps), int(dtype), _addr(stream))
+
+
+def norm_status_str(status: int) -> str:
+    return _lib.norm_status_str(int(status)).decode()
+
+
+def norm_describe(op: str, M: int, N: int, dtype, aligned: bool = True) -> str:
+    """How the library would run this call (path, tile, grid); launches nothing."""
+    code = {"ln": 0, "rms": 1}[op]
+    dt = DTYPE_NAMES.get(dtype, dtype)
+    buf = ctypes.create_string_buffer(256)
+    st = _lib.norm_describe(code, int(M), int(N), int(dt), int(bool(aligned)), buf, 256)
+    if st != NORM_OK:
+        raise RuntimeError(norm_status_str(st))
+    return buf.value.decode()
+
+
+# ---------------------------------------------------------------------------
+# torch tensors
+# ---------------------------------------------------------------------------
+
+def _torch_dtype_code(t):
+    import torch
+    m = {torch.float32: NORM_F32, torch.float16: NORM_F16, torch.bfloat16: NORM_BF16}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32, float16 or bfloat16")
+    return m[t.dtype]
+
+
+def _param(p, N, x):
+    if p is None:
+        return None
+    if p.dtype != x.dtype or p.device != x.device or p.numel() != N:
+        raise ValueError("gamma/beta must have N elements and x's dtype and device")
+    return p.contiguous()
+
+
+def _check(st):
+    if st != NORM_OK:
+        raise RuntimeError(f"{STATUS.get(st, st)}: {norm_status_str(st)}")
+
+
+def layer_norm(x, gamma=None, beta=None, eps: float = 1e-5, want_stats: bool = True):
+    """LayerNorm over the last dimension.  Returns (y, mean, rstd); mean and
+    rstd are fp32 [M] (None when want_stats is False)."""
+    import torch
+    N = x.shape[-1]
+    x2 = x.reshape(-1, N)
+    if not x2.is_contiguous():
+        x2 = x2.contiguous()
+    M = x2.shape[0]
+    g, b = _param(gamma, N, x), _param(beta, N, x)
+    y = torch.empty_like(x2)
+    mean = torch.empty(M, device=x.device, dtype=torch.float32) if want_stats else None
+    rstd = torch.empty(M, device=x.device, dtype=torch.float32) if want_stats else None
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        _check(ln_fwd(x2.data_ptr(), g.data_ptr() if g is not None else None,
+                      b.data_ptr() if b is not None else None, y.data_ptr(),
+                      mean.data_ptr() if mean is not None else None,
+                      rstd.data_ptr() if rstd is not None else None,
+                      M, N, eps, _torch_dtype_code(x2), stream))
+    return y.view(x.shape), mean, rstd
+
+
+def rms_norm(x, gamma=None, eps: float = 1e-6, want_rstd: bool = True):
+    """RMSNorm over the last dimension.  Returns (y, rstd); rstd is fp32 [M]
+    (None when want_rstd is False)."""
+    import torch
+    N = x.shape[-1]
+    x2 = x.reshape(-1, N)
+    if not x2.is_contiguous():
+        x2 = x2.contiguous()
+    M = x2.shape[0]
+    g = _param(gamma, N, x)
+    y = torch.empty_like(x2)
+    rstd = torch.empty(M, device=x.device, dtype=torch.float32) if want_rstd else None
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        _check(rms_fwd(x2.data_ptr(), g.data_ptr() if g is not None else None, None,
+                       y.data_ptr(), None, rstd.data_ptr() if rstd is not None else None,
+                       M, N, eps, _torch_dtype_code(x2), stream))
+    return y.view(x.shape), rstd
+
+
+__all__ = ["ln_fwd", "rms_fwd", "norm_status_str", "norm_describe", "layer_norm", "rms_norm",
+           "NORM_F32", "NORM_F16", "NORM_BF16", "NORM_OK", "STATUS", "LIB_PATH"]

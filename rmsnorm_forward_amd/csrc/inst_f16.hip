@@ -1,0 +1,11 @@
+// inst_f16.hip -- f16 instantiations of the row and split-row kernels.
+#include "inst_impl.hpp"
+
+namespace mi355norm {
+hipError_t launch_rows_f16(bool rms, const NormCall& c, const Plan& p) {
+    return detail::launch_rows<F16>(rms, c, p);
+}
+hipError_t launch_split_f16(bool rms, const NormCall& c, const Plan& p, float2* ws) {
+    return detail::launch_split<F16>(rms, c, p, ws);
+}
+}  // namespace mi355norm

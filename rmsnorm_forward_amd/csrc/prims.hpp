@@ -1,0 +1,179 @@
+// prims.hpp -- gfx950 device primitives for the row-wise norm kernels:
+// storage-type conversion, 128-bit vector I/O, DPP wavefront reductions,
+// and Chan's parallel merge of (n, mean, M2) partial statistics.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mi355norm {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// --------------------------------------------------------------------------
+// Storage types.  Each describes one I/O dtype: its storage word, how to
+// widen an element to fp32 and how to round fp32 back (round-to-nearest-even,
+// the hardware conversion's default mode).
+// --------------------------------------------------------------------------
+
+struct F32 {
+    using storage = float;
+    static constexpr int bytes = 4;
+    __device__ static __forceinline__ float widen(float v) { return v; }
+};
+
+struct BF16 {
+    using storage = uint16_t;
+    static constexpr int bytes = 2;
+    // bfloat16 is the high half of a binary32 word
+    __device__ static __forceinline__ float widen(uint16_t b) {
+        return __uint_as_float((unsigned)b << 16);
+    }
+    __device__ static __forceinline__ float lo(unsigned w) { return __uint_as_float(w << 16); }
+    __device__ static __forceinline__ float hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+    // v_cvt_pk_bf16_f32: two fp32 -> two bf16, RNE
+    __device__ static __forceinline__ unsigned pack(float a, float b) {
+        f32x2 v = {a, b};
+        bf16x2 r = __builtin_convertvector(v, bf16x2);
+        return __builtin_bit_cast(unsigned, r);
+    }
+    __device__ static __forceinline__ uint16_t narrow(float a) {
+        return __builtin_bit_cast(uint16_t, (__bf16)a);
+    }
+};
+
+struct F16 {
+    using storage = uint16_t;
+    static constexpr int bytes = 2;
+    __device__ static __forceinline__ float widen(uint16_t h) {
+        return (float)__builtin_bit_cast(_Float16, h);
+    }
+    __device__ static __forceinline__ float lo(unsigned w) { return widen((uint16_t)(w & 0xffffu)); }
+    __device__ static __forceinline__ float hi(unsigned w) { return widen((uint16_t)(w >> 16)); }
+    __device__ static __forceinline__ unsigned pack(float a, float b) {
+        f32x2 v = {a, b};
+        f16x2 r = __builtin_convertvector(v, f16x2);
+        return __builtin_bit_cast(unsigned, r);
+    }
+    __device__ static __forceinline__ uint16_t narrow(float a) {
+        return __builtin_bit_cast(uint16_t, (_Float16)a);
+    }
+};
+
+// --------------------------------------------------------------------------
+// A "vector" is the unit one lane moves with one memory instruction: 16 bytes
+// (EPV = 16 / element size) on the aligned path, one element (EPV = 1) on the
+// element-wise path.  Elements are widened to fp32 on access.
+// --------------------------------------------------------------------------
+
+template <class T, int EPV> struct Vec;
+
+template <> struct Vec<F32, 4> {
+    u32x4 w;
+    __device__ __forceinline__ void load(const float* p) { w = *reinterpret_cast<const u32x4*>(p); }
+    __device__ __forceinline__ void zero() { w = u32x4{0u, 0u, 0u, 0u}; }
+    __device__ __forceinline__ float get(int k) const { return __uint_as_float(w[k]); }
+    __device__ static __forceinline__ void store(float* p, const float (&v)[4]) {
+        u32x4 o = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+        *reinterpret_cast<u32x4*>(p) = o;
+    }
+};
+
+template <class H> struct VecHalf8 {
+    u32x4 w;
+    __device__ __forceinline__ void load(const uint16_t* p) { w = *reinterpret_cast<const u32x4*>(p); }
+    __device__ __forceinline__ void zero() { w = u32x4{0u, 0u, 0u, 0u}; }
+    __device__ __forceinline__ float get(int k) const { return (k & 1) ? H::hi(w[k >> 1]) : H::lo(w[k >> 1]); }
+    __device__ static __forceinline__ void store(uint16_t* p, const float (&v)[8]) {
+        u32x4 o = {H::pack(v[0], v[1]), H::pack(v[2], v[3]), H::pack(v[4], v[5]), H::pack(v[6], v[7])};
+        *reinterpret_cast<u32x4*>(p) = o;
+    }
+};
+template <> struct Vec<BF16, 8> : VecHalf8<BF16> {};
+template <> struct Vec<F16, 8> : VecHalf8<F16> {};
+
+template <class T> struct Vec<T, 1> {
+    typename T::storage s;
+    __device__ __forceinline__ void load(const typename T::storage* p) { s = *p; }
+    __device__ __forceinline__ void zero() { s = 0; }
+    __device__ __forceinline__ float get(int) const { return T::widen(s); }
+    __device__ static __forceinline__ void store(typename T::storage* p, const float (&v)[1]) {
+        if constexpr (sizeof(typename T::storage) == 4) *p = v[0];
+        else *p = T::narrow(v[0]);
+    }
+};
+
+// --------------------------------------------------------------------------
+// Cross-lane primitives (wave64).
+// --------------------------------------------------------------------------
+
+// DPP controls of the GFX9 family (gfx950 keeps them).
+constexpr int DPP_QUAD_XOR1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;   // lane i <- lane 7-i within 8
+constexpr int DPP_ROW_MIRROR = 0x140;        // lane i <- lane 15-i within 16
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_amdgcn_update_dpp(0.0f, v, CTRL, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ float readlane(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+// Sum over aligned groups of TEAM lanes (TEAM a power of two <= 64).  Every
+// lane of a group ends with the bitwise-identical group total: each xor /
+// mirror step adds a lane's value to its partner's, and IEEE addition is
+// commutative, so both partners compute the same sum; the mirror steps pair
+// quads (resp. 8-lane halves) only once those are already uniform.  All 64
+// lanes must be active.
+template <int TEAM>
+__device__ __forceinline__ float team_sum(float v) {
+    static_assert(TEAM >= 1 && TEAM <= 64 && (TEAM & (TEAM - 1)) == 0, "TEAM");
+    if constexpr (TEAM >= 2) v += dpp<DPP_QUAD_XOR1>(v);
+    if constexpr (TEAM >= 4) v += dpp<DPP_QUAD_XOR2>(v);
+    if constexpr (TEAM >= 8) v += dpp<DPP_ROW_HALF_MIRROR>(v);
+    if constexpr (TEAM >= 16) v += dpp<DPP_ROW_MIRROR>(v);
+    if constexpr (TEAM == 32) {
+        float a = readlane(v, 0), b = readlane(v, 16), c = readlane(v, 32), d = readlane(v, 48);
+        v = (lane_id() < 32) ? (a + b) : (c + d);
+    }
+    if constexpr (TEAM == 64) {
+        float a = readlane(v, 0), b = readlane(v, 16), c = readlane(v, 32), d = readlane(v, 48);
+        v = (a + b) + (c + d);
+    }
+    return v;
+}
+
+// --------------------------------------------------------------------------
+// Chan's parallel merge of partial statistics ("CUDA 算子工程" ch. 7,
+// section 7.4.1): (na, ma, M2a) + (nb, mb, M2b) with n = na + nb,
+// delta = mb - ma, mean = ma + delta * nb / n,
+// M2 = M2a + M2b + delta^2 * na * nb / n.  Counts are fp32 (exact below 2^24).
+// An empty operand returns the other one unchanged.
+// --------------------------------------------------------------------------
+
+struct Welford {
+    float n, mean, m2;
+};
+
+__device__ __forceinline__ Welford chan_merge(Welford a, Welford b) {
+    float n = a.n + b.n;
+    float w = b.n / n;
+    float d = b.mean - a.mean;
+    Welford r;
+    r.n = n;
+    r.mean = a.mean + d * w;
+    r.m2 = (a.m2 + b.m2) + (d * d) * (a.n * w);
+    if (a.n == 0.0f) r = b;
+    if (b.n == 0.0f) r = a;
+    return r;
+}
+
+}  // namespace mi355norm

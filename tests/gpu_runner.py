@@ -1,0 +1,59 @@
+"""Run the library's C ABI on the GPU with numpy-held inputs (test helper)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import rmsnorm_forward_amd as rn
+
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+CODE = {"f32": rn.NORM_F32, "f16": rn.NORM_F16, "bf16": rn.NORM_BF16}
+NP_STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
+
+
+def to_device(a: np.ndarray, dtype: str, offset: int = 0) -> torch.Tensor:
+    """Copy a storage array to the GPU as a flat tensor.  With offset > 0 the
+    data starts `offset` elements into a fresh allocation, so its address is
+    not 16-byte aligned (the element-wise path)."""
+    a = np.ascontiguousarray(a).reshape(-1)
+    if dtype == "bf16":
+        host = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    else:
+        host = torch.from_numpy(a)
+    buf = torch.empty(a.size + offset, dtype=TORCH_DT[dtype], device="cuda")
+    view = buf[offset:]
+    view.copy_(host)
+    return view
+
+
+def to_host(t: torch.Tensor, dtype: str) -> np.ndarray:
+    t = t.detach().cpu().contiguous()
+    if dtype == "bf16":
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+    return t.numpy().copy()
+
+
+def run(op: str, dtype: str, x: np.ndarray, gamma, beta, eps: float, *, stats: bool = True,
+        offset: int = 0, keep_device: bool = False):
+    """One ln_fwd / rms_fwd call; returns (y, mean, rstd) as host arrays
+    (mean is None for RMSNorm or stats=False)."""
+    M, N = x.shape
+    xt = to_device(x, dtype, offset)
+    gt = to_device(gamma, dtype, offset) if gamma is not None else None
+    bt = to_device(beta, dtype, offset) if (beta is not None and op == "ln") else None
+    ybuf = torch.empty(M * N + offset, dtype=TORCH_DT[dtype], device="cuda")
+    yt = ybuf[offset:]
+    mean = torch.empty(M, dtype=torch.float32, device="cuda") if (stats and op == "ln") else None
+    rstd = torch.empty(M, dtype=torch.float32, device="cuda") if stats else None
+    p = lambda t: t.data_ptr() if t is not None else None
+    fn = rn.ln_fwd if op == "ln" else rn.rms_fwd
+    stream = torch.cuda.current_stream().cuda_stream
+    st = fn(p(xt), p(gt), p(bt), p(yt), p(mean), p(rstd), M, N, eps, CODE[dtype], stream)
+    assert st == rn.NORM_OK, f"{rn.STATUS.get(st)}: {rn.norm_status_str(st)}"
+    torch.cuda.synchronize()
+    y = to_host(yt, dtype).reshape(M, N)
+    m = mean.cpu().numpy() if mean is not None else None
+    r = rstd.cpu().numpy() if rstd is not None else None
+    if keep_device:
+        return y, m, r, (xt, gt, bt, yt, mean, rstd)
+    return y, m, r

@@ -1,0 +1,87 @@
+"""GPU-vs-oracle comparison at the stated tolerances.
+
+Tolerances (fixed by the task's target; the readings where it is open are
+marked):
+  fp32 y        max |y_gpu - y_oracle| <= 2e-5
+  bf16/fp16 y   within one unit in the last place of the oracle's value
+                rounded to the I/O dtype (round-to-nearest-even), where the
+                unit is that of the rounded value's binade; reading: a floor
+                of 2^-20 applies to values so small that fp32 rounding of
+                order-one intermediate terms exceeds their own ulp
+  mean          |mean_gpu - mean_oracle| <= 1e-5 * max(|mean|, sqrt(var + eps));
+                reading: plain relative error is ill-conditioned for rows whose
+                mean is near zero, so the row's scale bounds it from below
+  rstd          relative error <= 1e-5
+  stress rows   no NaN, no infinity, variance >= 0 (rstd <= 1/sqrt(eps))
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+Y_F32_ABS = 2e-5
+STAT_REL = 1e-5
+HALF_FLOOR = 2.0 ** -20
+SIG_BITS = {"bf16": 8, "f16": 11}
+
+
+def ulp_of(v: np.ndarray, dtype: str) -> np.ndarray:
+    """Spacing of the I/O dtype at |v| (v already representable in it)."""
+    p = SIG_BITS[dtype]
+    emin = -126 if dtype == "bf16" else -14
+    a = np.maximum(np.abs(v), 2.0 ** emin)
+    return np.exp2(np.floor(np.log2(a)) - (p - 1))
+
+
+def check_y(y_gpu: np.ndarray, y_ref: np.ndarray, dtype: str, what: str = "") -> dict:
+    """y_gpu: storage array; y_ref: float64 oracle result (same shape)."""
+    if dtype == "f32":
+        err = np.abs(y_gpu.astype(np.float64) - y_ref)
+        bad = ~(err <= Y_F32_ABS)
+        stats = {"max_abs_err": float(np.nanmax(err)) if err.size else 0.0}
+    else:
+        want = oracle.widen(oracle.round_to(y_ref, dtype), dtype)
+        got = oracle.widen(y_gpu, dtype)
+        err = np.abs(got - want)
+        tol = np.maximum(ulp_of(want, dtype), HALF_FLOOR)
+        bad = ~(err <= tol)
+        both_nan = np.isnan(got) & np.isnan(want)
+        bad &= ~both_nan
+        stats = {"max_ulp_err": float(np.nanmax(err / tol)) if err.size else 0.0,
+                 "exact_frac": float(np.mean(err == 0)) if err.size else 1.0}
+    if np.any(bad):
+        idx = np.unravel_index(np.argmax(bad), bad.shape)
+        raise AssertionError(f"{what} y mismatch at {idx}: gpu={np.asarray(y_gpu)[idx]!r} "
+                             f"oracle={y_ref[idx]!r} ({int(bad.sum())} bad of {bad.size}); {stats}")
+    return stats
+
+
+def check_stats(mean_gpu, rstd_gpu, mean_ref, rstd_ref, eps: float, what: str = "") -> dict:
+    e = oracle.eps_as_kernel_sees(eps)
+    out = {}
+    if rstd_gpu is not None:
+        rel = np.abs(rstd_gpu.astype(np.float64) - rstd_ref) / np.abs(rstd_ref)
+        if not np.all(rel <= STAT_REL):
+            i = int(np.nanargmax(rel))
+            raise AssertionError(f"{what} rstd row {i}: gpu={rstd_gpu[i]!r} oracle={rstd_ref[i]!r} rel={rel[i]:.3g}")
+        out["rstd_max_rel"] = float(rel.max()) if rel.size else 0.0
+    if mean_gpu is not None:
+        var = 1.0 / rstd_ref ** 2 - e
+        scale = np.maximum(np.abs(mean_ref), np.sqrt(np.maximum(var, 0.0) + e))
+        err = np.abs(mean_gpu.astype(np.float64) - mean_ref) / scale
+        if not np.all(err <= STAT_REL):
+            i = int(np.nanargmax(err))
+            raise AssertionError(f"{what} mean row {i}: gpu={mean_gpu[i]!r} oracle={mean_ref[i]!r} err={err[i]:.3g}")
+        out["mean_max_scaled_err"] = float(err.max()) if err.size else 0.0
+    return out
+
+
+def check_stress_invariants(rstd_gpu, y_gpu, dtype: str, eps: float, what: str = ""):
+    """No NaN/inf anywhere; rstd finite and <= 1/sqrt(eps) (i.e. variance >= 0)."""
+    e = oracle.eps_as_kernel_sees(eps)
+    r = rstd_gpu.astype(np.float64)
+    assert np.all(np.isfinite(r)), f"{what}: non-finite rstd"
+    assert np.all(r <= (1 + 1e-6) / np.sqrt(e)), f"{what}: rstd implies a negative variance"
+    yv = y_gpu.astype(np.float64) if dtype == "f32" else oracle.widen(y_gpu, dtype)
+    assert np.all(np.isfinite(yv)), f"{what}: non-finite y"

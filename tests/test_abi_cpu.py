@@ -1,0 +1,159 @@
+"""The C ABI on the CPU: the library loads, exports every symbol the header
+declares, rejects every bad argument with its status before any HIP call,
+and plans the row-to-workgroup mapping as documented.  No kernel runs here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import __graft_entry__
+
+__graft_entry__.ensure_built()
+
+import rmsnorm_forward_amd as rn  # noqa: E402
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mi355norm.h")
+
+OK, NULL_ARG, BAD_SHAPE, BAD_DTYPE, BAD_EPS, BAD_ARG, ALIAS, HIP = range(8)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["ln_fwd", "norm_describe", "norm_status_str", "rms_fwd"]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(rn.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = os.popen(f"nm -D --defined-only {rn.LIB_PATH}").read()
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}$", out, flags=re.M), name
+
+
+def test_status_strings():
+    for code in range(8):
+        s = rn.norm_status_str(code)
+        assert s and s != "unknown status"
+    assert rn.norm_status_str(99) == "unknown status"
+
+
+# fake, never dereferenced device addresses: validation only does arithmetic
+X, G, B, Y, MEAN, RSTD = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000, 0x600000
+
+
+def call(op="ln", x=X, g=G, b=B, y=Y, mean=MEAN, rstd=RSTD, M=4, N=64, eps=1e-5, dtype=0):
+    fn = rn.ln_fwd if op == "ln" else rn.rms_fwd
+    if op == "rms" and b == B:
+        b = None
+    if op == "rms" and mean == MEAN:
+        mean = None
+    return fn(x, g, b, y, mean, rstd, M, N, eps, dtype, None)
+
+
+@pytest.mark.parametrize("op", ["ln", "rms"])
+def test_validation_paths(op):
+    assert call(op, dtype=3) == BAD_DTYPE
+    assert call(op, dtype=-1) == BAD_DTYPE
+    assert call(op, M=-1) == BAD_SHAPE
+    assert call(op, N=0) == BAD_SHAPE
+    assert call(op, N=-5) == BAD_SHAPE
+    assert call(op, N=(1 << 24) + 1) == BAD_SHAPE
+    assert call(op, M=(1 << 62), N=1 << 20) == BAD_SHAPE
+    assert call(op, eps=-1e-5) == BAD_EPS
+    assert call(op, eps=float("nan")) == BAD_EPS
+    assert call(op, eps=float("inf")) == BAD_EPS
+    assert call(op, M=0, x=None, y=None) == OK          # nothing to do, nothing launched
+    assert call(op, x=None) == NULL_ARG
+    assert call(op, y=None) == NULL_ARG
+    assert call(op, x=X + 2) == BAD_ARG                 # f32 element misaligned
+    assert call(op, y=Y + 1, dtype=2) == BAD_ARG        # bf16 element misaligned
+    assert call(op, rstd=RSTD + 2) == BAD_ARG
+    assert call(op, y=X + 64) == ALIAS                  # y inside x
+    assert call(op, y=X) == ALIAS                       # in place
+    assert call(op, rstd=Y + 16) == ALIAS               # stats inside y
+    assert call(op, g=Y + 4) == ALIAS                   # gamma inside y
+
+
+def test_rms_rejects_beta_and_mean():
+    assert rn.rms_fwd(X, G, B, Y, None, RSTD, 4, 64, 1e-6, 0, None) == BAD_ARG
+    assert rn.rms_fwd(X, G, None, Y, MEAN, RSTD, 4, 64, 1e-6, 0, None) == BAD_ARG
+
+
+def test_ln_mean_rstd_overlap_rejected():
+    assert call("ln", mean=RSTD) == ALIAS
+    assert call("ln", mean=RSTD - 8, M=4) == ALIAS      # [RSTD-8, RSTD+8) overlaps
+
+
+def parse(desc):
+    return dict(kv.split("=") for kv in desc.split())
+
+
+@pytest.mark.parametrize("op,M,N,dtype,want", [
+    ("ln", 128, 1024, "f32", dict(path="rows", team="32", vpl="8", epv="4")),
+    ("rms", 8192, 4096, "f32", dict(path="rows", team="256", vpl="4", epv="4")),
+    ("ln", 16384, 8192, "bf16", dict(path="rows", team="256", vpl="4", epv="8")),
+    ("rms", 65536, 2048, "f32", dict(path="rows", team="32", vpl="16", epv="4")),
+    ("rms", 65536, 2048, "bf16", dict(path="rows", team="32", vpl="8", epv="8")),
+    ("ln", 4096, 5120, "bf16", dict(path="rows", team="256", vpl="4", epv="8")),
+    ("ln", 64, 1 << 20, "bf16", dict(path="split", chunks="128", epv="8")),
+])
+def test_plans_of_the_measured_configurations(op, M, N, dtype, want):
+    d = parse(rn.norm_describe(op, M, N, dtype))
+    for k, v in want.items():
+        assert d[k] == v, (k, d)
+
+
+def test_small_rows_share_a_wavefront():
+    for N in (16, 100, 512, 1024, 2048):
+        d = parse(rn.norm_describe("rms", 1000, N, "bf16"))
+        assert int(d["team"]) <= 32 and int(d["rows_per_wg"]) >= 8
+
+
+def test_unaligned_plans_take_the_elementwise_path():
+    d = parse(rn.norm_describe("ln", 1, 10, "f32"))          # 40-byte rows
+    assert d["epv"] == "1" and d["path"] == "rows"
+    d = parse(rn.norm_describe("ln", 64, 4096, "bf16", aligned=False))
+    assert d["epv"] == "1"
+
+
+def test_every_row_fits_its_tile():
+    for dtype, e in (("f32", 4), ("bf16", 2), ("f16", 2)):
+        for N in list(range(1, 70)) + [127, 1000, 1023, 1025, 5120, 8191, 8193, 65536, 131072, 131073, 1 << 20]:
+            for aligned in (True, False):
+                d = parse(rn.norm_describe("ln", 3, N, dtype, aligned))
+                epv = int(d["epv"])
+                if aligned and (N * e) % 16 == 0:
+                    assert epv == 16 // e
+                else:
+                    assert epv == 1
+                nv = N // epv
+                if d["path"] == "rows":
+                    assert int(d["team"]) * int(d["vpl"]) >= nv
+                else:
+                    assert int(d["chunks"]) * int(d["wg"]) * int(d["vpl"]) >= nv
+
+
+def test_overrides(monkeypatch):
+    monkeypatch.setenv("MI355NORM_PATH", "split")
+    assert parse(rn.norm_describe("ln", 64, 8192, "bf16"))["path"] == "split"
+    monkeypatch.setenv("MI355NORM_PATH", "rows")
+    with pytest.raises(RuntimeError):
+        rn.norm_describe("ln", 64, 1 << 20, "bf16")     # does not fit one workgroup
+    monkeypatch.delenv("MI355NORM_PATH")
+    monkeypatch.setenv("MI355NORM_TILE", "64x16")
+    d = parse(rn.norm_describe("ln", 64, 8192, "bf16"))
+    assert (d["team"], d["vpl"]) == ("64", "16")
+    monkeypatch.setenv("MI355NORM_TILE", "64x2")         # too small for the row
+    with pytest.raises(RuntimeError):
+        rn.norm_describe("ln", 64, 8192, "bf16")
+    monkeypatch.delenv("MI355NORM_TILE")
+    monkeypatch.setenv("MI355NORM_GRID", "1024")
+    assert parse(rn.norm_describe("ln", 16384, 8192, "bf16"))["grid"] == "1024"

@@ -1,0 +1,280 @@
+"""HIP path vs the CPU oracle, element by element, through the C ABI.
+
+Shapes: every measured configuration at full size (sampled rows checked
+against the oracle, properties checked on every row), plus small shapes that
+span several tiles with ragged tails, the degenerate cases (N = 1, constant
+rows, eps = 0, M = 0), unaligned pointers, every forced path and tile, and
+bitwise determinism.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import __graft_entry__
+
+__graft_entry__.ensure_built()
+
+import oracle  # noqa: E402
+import parity  # noqa: E402
+import workloads  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+gpu_runner = pytest.importorskip("gpu_runner")
+run = gpu_runner.run
+
+
+def oracle_for(op, dtype, x, gamma, beta, eps):
+    if op == "ln":
+        return oracle.ln_fwd(x, gamma, beta, dtype, eps)
+    y, r = oracle.rms_fwd(x, gamma, dtype, eps)
+    return y, None, r
+
+
+def compare(op, dtype, x, gamma, beta, eps, y, mean, rstd, rows=None, what=""):
+    xs = x if rows is None else x[rows]
+    yr, mr, rr = oracle_for(op, dtype, xs, gamma, beta if op == "ln" else None, eps)
+    ys = y if rows is None else y[rows]
+    out = parity.check_y(ys, yr, dtype, what)
+    ms = None if mean is None else (mean if rows is None else mean[rows])
+    rsv = None if rstd is None else (rstd if rows is None else rstd[rows])
+    out.update(parity.check_stats(ms, rsv, mr, rr, eps, what))
+    return out
+
+
+def sample_rows(M, n=256, seed=0, extra=()):
+    rng = np.random.default_rng(seed)
+    rows = set(range(min(4, M))) | set(range(max(0, M - 4), M)) | set(extra)
+    rows |= set(rng.choice(M, size=min(n, M), replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+# ---------------------------------------------------------------------------
+# measured configurations at full size
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(workloads.CONFIGS))
+def test_measured_configuration(name):
+    w = workloads.CONFIGS[name]
+    print(f"[gpu] config {name}: {w.op} {w.dtype} M={w.M} N={w.N}", flush=True)
+    inp = workloads.generate(name)
+    y, mean, rstd = run(w.op, w.dtype, inp["x"], inp["gamma"], inp["beta"], w.eps)
+    extra = ()
+    if "big_rows" in inp:
+        extra = inp["big_rows"][:512]
+    rows = None if w.M * w.N <= (1 << 25) else sample_rows(w.M, 256, seed=w.seed, extra=extra)
+    if w.N >= (1 << 20):
+        rows = sample_rows(w.M, 6, seed=w.seed)
+    st = compare(w.op, w.dtype, inp["x"], inp["gamma"], inp["beta"], w.eps, y, mean, rstd, rows, name)
+    parity.check_stress_invariants(rstd, y, w.dtype, w.eps, name)
+    print(f"[gpu] {name}: {st}", flush=True)
+
+
+def test_check_row_large_mean():
+    """The 10-value row 1000.001..1000.010 as its own M=1, N=10 fp32 call with
+    gamma = 1 and beta = 0 (NULL), eps = 1e-5."""
+    x = workloads.check_row_f32()
+    y, mean, rstd = run("ln", "f32", x, None, None, 1e-5)
+    st = compare("ln", "f32", x, None, None, 1e-5, y, mean, rstd, what="check row")
+    assert st["max_abs_err"] <= 2e-5
+    yr, mr, rr = oracle.ln_fwd(x, None, None, "f32", 1e-5)
+    var_gpu = 1.0 / float(rstd[0]) ** 2 - oracle.eps_as_kernel_sees(1e-5)
+    var_ref = 1.0 / rr[0] ** 2 - oracle.eps_as_kernel_sees(1e-5)
+    assert abs(var_gpu - var_ref) <= 1e-4 * var_ref
+
+
+# ---------------------------------------------------------------------------
+# shapes across tiles, ragged tails, all dtypes, both ops
+# ---------------------------------------------------------------------------
+
+EDGE_N = [1, 2, 3, 5, 7, 8, 10, 16, 63, 64, 65, 127, 128, 1000, 1023, 1024, 1025,
+          2047, 2048, 4096, 5120, 8191, 8192, 8193, 16384, 32768, 65536, 131072, 131080]
+
+
+def inputs(op, dtype, M, N, seed):
+    if op == "ln":
+        return workloads.gen_ln_normal(seed, M, N, dtype, loc=3.0, scale=2.0)
+    return workloads.gen_rms_uniform(seed, M, N, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("op", ["ln", "rms"])
+@pytest.mark.parametrize("N", EDGE_N)
+def test_edge_shapes(op, dtype, N):
+    M = 37 if N <= 8192 else 5
+    print(f"[gpu] edge {op} {dtype} M={M} N={N}", flush=True)
+    inp = inputs(op, dtype, M, N, seed=N)
+    y, mean, rstd = run(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5)
+    compare(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, y, mean, rstd, what=f"N={N}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("op", ["ln", "rms"])
+@pytest.mark.parametrize("N", [10, 1000, 8192, 65544, 300000])
+def test_forced_split_path(monkeypatch, op, dtype, N):
+    monkeypatch.setenv("MI355NORM_PATH", "split")
+    M = 9
+    print(f"[gpu] split {op} {dtype} M={M} N={N}", flush=True)
+    inp = inputs(op, dtype, M, N, seed=N + 1)
+    y, mean, rstd = run(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5)
+    compare(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, y, mean, rstd, what=f"split N={N}")
+
+
+TILES = [(t, v) for t in (4, 8, 16, 32, 64, 128, 256, 512, 1024) for v in (1, 2, 4, 8, 16)]
+
+
+@pytest.mark.parametrize("dtype,N", [("bf16", 4096), ("f32", 1000), ("f16", 2056)])
+@pytest.mark.parametrize("op", ["ln", "rms"])
+def test_every_tile(monkeypatch, op, dtype, N):
+    """Every instantiated tile that covers the row gives oracle-exact results."""
+    M = 19
+    inp = inputs(op, dtype, M, N, seed=17)
+    e = 4 if dtype == "f32" else 2
+    epv = 16 // e if (N * e) % 16 == 0 else 1
+    nv = N // epv
+    ran = 0
+    for t, v in TILES:
+        if t * v < nv:
+            continue
+        monkeypatch.setenv("MI355NORM_TILE", f"{t}x{v}")
+        print(f"[gpu] tile {t}x{v} {op} {dtype} N={N}", flush=True)
+        y, mean, rstd = run(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5)
+        compare(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, y, mean, rstd, what=f"tile {t}x{v}")
+        ran += 1
+    assert ran >= 5
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("op", ["ln", "rms"])
+def test_unaligned_pointers(op, dtype):
+    """Pointers one element past a 16-byte boundary take the element-wise path."""
+    M, N = 23, 4096
+    inp = inputs(op, dtype, M, N, seed=5)
+    y, mean, rstd = run(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, offset=1)
+    compare(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, y, mean, rstd, what="unaligned")
+
+
+@pytest.mark.parametrize("has_g,has_b", [(False, False), (True, False), (False, True)])
+def test_optional_gamma_beta(has_g, has_b):
+    M, N = 33, 3000
+    inp = inputs("ln", "bf16", M, N, seed=21)
+    g = inp["gamma"] if has_g else None
+    b = inp["beta"] if has_b else None
+    y, mean, rstd = run("ln", "bf16", inp["x"], g, b, 1e-5)
+    compare("ln", "bf16", inp["x"], g, b, 1e-5, y, mean, rstd, what="optional gamma/beta")
+    y2, m2, r2 = run("ln", "bf16", inp["x"], g, b, 1e-5, stats=False)
+    assert np.array_equal(y, y2) and m2 is None and r2 is None
+
+
+def test_rms_without_gamma_or_rstd():
+    M, N = 40, 2048
+    inp = inputs("rms", "f32", M, N, seed=22)
+    y, _, rstd = run("rms", "f32", inp["x"], None, None, 1e-6)
+    compare("rms", "f32", inp["x"], None, None, 1e-6, y, None, rstd, what="rms no gamma")
+    y2, _, r2 = run("rms", "f32", inp["x"], None, None, 1e-6, stats=False)
+    assert np.array_equal(y, y2) and r2 is None
+
+
+@pytest.mark.parametrize("N", [1, 7, 4096])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_constant_rows(dtype, N):
+    """Constant rows (and N = 1): y = beta exactly, mean = the constant,
+    rstd = 1/sqrt(eps); with eps = 0, rstd = inf and y = NaN like the oracle."""
+    M = 6
+    x32 = np.repeat(np.array([0.0, 1.0, -3.5, 1000.0, 99840.0, 2.0 ** -10], np.float32)[:, None], N, axis=1)
+    x = workloads.to_storage(x32, dtype)
+    rng = np.random.default_rng(3)
+    g = workloads.to_storage(rng.uniform(0.5, 1.5, N).astype(np.float32), dtype)
+    b = workloads.to_storage(rng.normal(0, 0.1, N).astype(np.float32), dtype)
+    y, mean, rstd = run("ln", dtype, x, g, b, 1e-5)
+    assert np.array_equal(y, np.broadcast_to(b, y.shape))
+    assert np.array_equal(mean.astype(np.float64), oracle.widen(x[:, 0], dtype))
+    compare("ln", dtype, x, g, b, 1e-5, y, mean, rstd, what="constant rows")
+    y0, mean0, rstd0 = run("ln", dtype, x, g, b, 0.0)
+    assert np.all(np.isinf(rstd0))
+    yv = y0.astype(np.float64) if dtype == "f32" else oracle.widen(y0, dtype)
+    assert np.all(np.isnan(yv))
+
+
+def test_rms_zero_row_eps0():
+    x = np.zeros((3, 256), np.float32)
+    y, _, rstd = run("rms", "f32", x, None, None, 0.0)
+    assert np.all(np.isinf(rstd)) and np.all(np.isnan(y))
+
+
+def test_fp32_large_mean_stress():
+    """Every row 1000 + N(0, 1e-2) in fp32 at N = 8192: the naive E[x^2]-E[x]^2
+    formula goes negative on such rows; here variance must stay >= 0 and
+    every output within the fp32 tolerances of the oracle."""
+    inp = workloads.gen_ln_large_mean(1006, 64, 8192, "f32")
+    y, mean, rstd = run("ln", "f32", inp["x"], inp["gamma"], inp["beta"], 1e-5)
+    parity.check_stress_invariants(rstd, y, "f32", 1e-5, "fp32 stress")
+    compare("ln", "f32", inp["x"], inp["gamma"], inp["beta"], 1e-5, y, mean, rstd, what="fp32 stress")
+
+
+def test_stress_rows_small_bf16():
+    """The large-mean + outlier-channel recipe at a size the oracle checks fully."""
+    inp = workloads.gen_ln_stress(77, 512, 8192, "bf16", chan_frac=0.002)
+    y, mean, rstd = run("ln", "bf16", inp["x"], inp["gamma"], inp["beta"], 1e-5)
+    parity.check_stress_invariants(rstd, y, "bf16", 1e-5, "bf16 stress")
+    compare("ln", "bf16", inp["x"], inp["gamma"], inp["beta"], 1e-5, y, mean, rstd, what="bf16 stress")
+
+
+@pytest.mark.parametrize("path", ["auto", "split"])
+def test_bitwise_deterministic(monkeypatch, path):
+    if path == "split":
+        monkeypatch.setenv("MI355NORM_PATH", "split")
+    inp = inputs("ln", "bf16", 300, 8192, seed=31)
+    a = run("ln", "bf16", inp["x"], inp["gamma"], inp["beta"], 1e-5)
+    b = run("ln", "bf16", inp["x"], inp["gamma"], inp["beta"], 1e-5)
+    for u, v in zip(a, b):
+        assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
+
+
+def test_split_statistics_shared_by_all_chunks():
+    """All workgroups of a split row must normalise with the same mean and
+    rstd: with x, gamma and beta periodic in the chunk length, every full
+    chunk of a row holds the same data, so its output must be bitwise equal
+    to every other full chunk's."""
+    import rmsnorm_forward_amd as rn
+    N = 300000
+    d = dict(kv.split("=") for kv in rn.norm_describe("ln", 2, N, "bf16").split())
+    assert d["path"] == "split"
+    C = int(d["wg"]) * int(d["vpl"]) * int(d["epv"])     # elements per chunk
+    base = inputs("ln", "bf16", 2, C, seed=41)
+    reps = -(-N // C)
+    x = np.tile(base["x"], (1, reps))[:, :N].copy()
+    g = np.tile(base["gamma"], reps)[:N].copy()
+    b = np.tile(base["beta"], reps)[:N].copy()
+    y, mean, rstd = run("ln", "bf16", x, g, b, 1e-5)
+    full = N // C
+    for r in range(2):
+        for c in range(1, full):
+            assert np.array_equal(y[r, :C], y[r, c * C:(c + 1) * C]), (r, c)
+    compare("ln", "bf16", x, g, b, 1e-5, y, mean, rstd, what="periodic split")
+
+
+def test_m_zero_launches_nothing():
+    import rmsnorm_forward_amd as rn
+    st = rn.ln_fwd(None, None, None, None, None, None, 0, 128, 1e-5, rn.NORM_BF16,
+                   torch.cuda.current_stream().cuda_stream)
+    assert st == rn.NORM_OK
+
+
+def test_tensor_api_matches_abi():
+    import rmsnorm_forward_amd as rn
+    inp = inputs("ln", "bf16", 2 * 3 * 7, 768, seed=51)
+    xt = gpu_runner.to_device(inp["x"], "bf16").view(2, 3, 7, 768)
+    gt = gpu_runner.to_device(inp["gamma"], "bf16")
+    bt = gpu_runner.to_device(inp["beta"], "bf16")
+    y, mean, rstd = rn.layer_norm(xt, gt, bt, eps=1e-5)
+    torch.cuda.synchronize()
+    assert y.shape == (2, 3, 7, 768) and mean.dtype == torch.float32 and mean.shape == (42,)
+    y2, m2, r2 = run("ln", "bf16", inp["x"], inp["gamma"], inp["beta"], 1e-5)
+    assert np.array_equal(gpu_runner.to_host(y.reshape(42, 768), "bf16"), y2)
+    yr, rr = rn.rms_norm(xt, gt, eps=1e-6)
+    torch.cuda.synchronize()
+    y3, _, r3 = run("rms", "bf16", inp["x"], inp["gamma"], None, 1e-6)
+    assert np.array_equal(gpu_runner.to_host(yr.reshape(42, 768), "bf16"), y3)
