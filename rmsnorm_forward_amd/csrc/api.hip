@@ -1,16 +1,20 @@
 // api.hip -- the C ABI (include/mi355norm.h): argument validation, choice of
 // the row-to-workgroup mapping from (N, dtype, alignment), and launch.
 //
-// Mapping regimes (chosen by row length in 16-byte vectors, NV):
-//   small rows  (N * elem <= 8 KiB): a team of 4..32 lanes per row, so 2..16
-//               rows share a wavefront and reduce with DPP only;
-//   mid rows    (up to 1024 lanes x 16 vectors): 64..1024 lanes per row, one
-//               LDS exchange per reduction across the row's wavefronts;
-//   long rows   : split across workgroups, per-chunk partial statistics
-//               merged in chunk order (Chan) in a second kernel.
-// A fourfold vector unroll per lane is the default: every lane issues its
-// loads back to back before any arithmetic, which keeps enough bytes in
-// flight per CU to stream HBM.
+// Mapping regimes (chosen by row length in 16-byte vectors, NV; every lane
+// holds two vectors, the team is as large as the row needs):
+//   small rows  (up to 1 KiB): a team of 4..32 lanes per row, so 2..16 rows
+//               share a wavefront and reduce with DPP only;
+//   mid rows    (1 KiB .. 32 KiB): 64..1024 lanes per row, one LDS exchange
+//               per reduction across the row's wavefronts; beyond 32 KiB the
+//               1024-lane team holds 4..16 vectors per lane;
+//   long rows   (beyond 1024 lanes x 16 vectors): split across workgroups,
+//               per-chunk partial statistics merged in chunk order (Chan) in
+//               a second kernel.
+// Two vectors per lane measured best on MI355X for 4..16 KiB rows (e.g. bf16
+// 16384 x 8192 LayerNorm: 512x2 90.5 us, 256x4 91.5 us, 128x8 93.6 us; bf16
+// 2048-wide RMSNorm: 128x2 86.5 us against 100.3 us for two rows per
+// wavefront at 32x8).
 //
 // Test/benchmark hooks (environment, read per call):
 //   MI355NORM_PATH = rows | split      force the path (rows only if it fits)
@@ -131,15 +135,12 @@ int make_plan(int op, int64_t M, int64_t N, int dtype, bool aligned, const Overr
             team = o.team;
             vpl = o.vpl;
             if (!tile_instantiated(team, vpl) || int64_t(team) * vpl < NV) return NORM_ERR_BAD_ARG;
-        } else if (N * e <= 8192 && NV <= 32 * kMaxVpl) {
-            // small rows: several rows per wavefront
-            team = next_pow2((NV + 7) / 8);
-            if (team < 4) team = 4;
-            if (team > 32) team = 32;
-            vpl = round_vpl((NV + team - 1) / team);
         } else {
-            team = next_pow2((NV + 3) / 4);
-            if (team < 64) team = 64;
+            // two vectors per lane, team as large as the row needs: rows of
+            // up to 64 vectors share a wavefront (4..32 lanes each), up to
+            // 2048 vectors take 1..16 wavefronts; longer rows add vectors
+            team = next_pow2((NV + 1) / 2);
+            if (team < 4) team = 4;
             if (team > kMaxTeam) team = kMaxTeam;
             vpl = round_vpl((NV + team - 1) / team);
         }

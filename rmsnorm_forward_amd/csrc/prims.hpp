@@ -64,32 +64,66 @@ struct F16 {
 };
 
 // --------------------------------------------------------------------------
+// Cache policy.  x is read exactly once and y written exactly once, so their
+// accesses carry the nontemporal hint (streamed through the caches without
+// being kept); gamma and beta are reused by every row and use ordinary loads.
+// --------------------------------------------------------------------------
+
+#ifndef MI355_NT_LOAD
+#define MI355_NT_LOAD 1
+#endif
+#ifndef MI355_NT_STORE
+#define MI355_NT_STORE 1
+#endif
+
+template <class P>
+__device__ __forceinline__ P ld_stream(const P* p) {
+    if constexpr (MI355_NT_LOAD) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+template <class P>
+__device__ __forceinline__ void st_stream(P v, P* p) {
+    if constexpr (MI355_NT_STORE) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+// --------------------------------------------------------------------------
 // A "vector" is the unit one lane moves with one memory instruction: 16 bytes
 // (EPV = 16 / element size) on the aligned path, one element (EPV = 1) on the
 // element-wise path.  Elements are widened to fp32 on access.
+//   load()        cached load (gamma, beta)
+//   load_stream() nontemporal load (x)
+//   store()       nontemporal store (y)
 // --------------------------------------------------------------------------
 
 template <class T, int EPV> struct Vec;
 
 template <> struct Vec<F32, 4> {
     u32x4 w;
+    __device__ __forceinline__ void opaque() { asm volatile("" : "+v"(w)); }
     __device__ __forceinline__ void load(const float* p) { w = *reinterpret_cast<const u32x4*>(p); }
+    __device__ __forceinline__ void load_stream(const float* p) { w = ld_stream(reinterpret_cast<const u32x4*>(p)); }
     __device__ __forceinline__ void zero() { w = u32x4{0u, 0u, 0u, 0u}; }
     __device__ __forceinline__ float get(int k) const { return __uint_as_float(w[k]); }
     __device__ static __forceinline__ void store(float* p, const float (&v)[4]) {
         u32x4 o = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
-        *reinterpret_cast<u32x4*>(p) = o;
+        st_stream(o, reinterpret_cast<u32x4*>(p));
     }
 };
 
 template <class H> struct VecHalf8 {
     u32x4 w;
+    // Make the packed words opaque to the optimiser so that widened copies
+    // made before this point cannot be reused after it (they are recomputed
+    // from the packed registers instead of being kept live).
+    __device__ __forceinline__ void opaque() { asm volatile("" : "+v"(w)); }
     __device__ __forceinline__ void load(const uint16_t* p) { w = *reinterpret_cast<const u32x4*>(p); }
+    __device__ __forceinline__ void load_stream(const uint16_t* p) { w = ld_stream(reinterpret_cast<const u32x4*>(p)); }
     __device__ __forceinline__ void zero() { w = u32x4{0u, 0u, 0u, 0u}; }
     __device__ __forceinline__ float get(int k) const { return (k & 1) ? H::hi(w[k >> 1]) : H::lo(w[k >> 1]); }
     __device__ static __forceinline__ void store(uint16_t* p, const float (&v)[8]) {
         u32x4 o = {H::pack(v[0], v[1]), H::pack(v[2], v[3]), H::pack(v[4], v[5]), H::pack(v[6], v[7])};
-        *reinterpret_cast<u32x4*>(p) = o;
+        st_stream(o, reinterpret_cast<u32x4*>(p));
     }
 };
 template <> struct Vec<BF16, 8> : VecHalf8<BF16> {};
@@ -97,12 +131,14 @@ template <> struct Vec<F16, 8> : VecHalf8<F16> {};
 
 template <class T> struct Vec<T, 1> {
     typename T::storage s;
+    __device__ __forceinline__ void opaque() {}
     __device__ __forceinline__ void load(const typename T::storage* p) { s = *p; }
+    __device__ __forceinline__ void load_stream(const typename T::storage* p) { s = ld_stream(p); }
     __device__ __forceinline__ void zero() { s = 0; }
     __device__ __forceinline__ float get(int) const { return T::widen(s); }
     __device__ static __forceinline__ void store(typename T::storage* p, const float (&v)[1]) {
-        if constexpr (sizeof(typename T::storage) == 4) *p = v[0];
-        else *p = T::narrow(v[0]);
+        if constexpr (sizeof(typename T::storage) == 4) st_stream(v[0], p);
+        else st_stream(T::narrow(v[0]), p);
     }
 };
 

@@ -8,7 +8,8 @@
 //
 // Lane t of a team holds VPL vectors; vector j covers elements
 // [(j*TEAM + t)*EPV, (j*TEAM + t + 1)*EPV), so each load instruction of the
-// team reads TEAM*EPV contiguous elements (fully coalesced).
+// team reads TEAM*EPV contiguous elements (fully coalesced).  A vector is
+// either wholly inside the row or wholly past its end (EPV divides N).
 //
 // LayerNorm statistics are the stable two-pass of "T3 讲解" part ② taken over
 // the register copy of the row, with a shift: K = x[row, 0] is subtracted
@@ -18,6 +19,7 @@
 // rounding of the mean never enters y (the large-mean rows of "CUDA 算子工程"
 // ch. 7 section 7.3 need this: at |x| ~ 1000 an fp32 mean is only known to
 // ~3e-5).  RMSNorm needs a single sum of squares.
+
 #pragma once
 
 #include "prims.hpp"
@@ -48,6 +50,41 @@ __device__ __forceinline__ float team_reduce(float v, float* slots, int wave_in_
     return v;
 }
 
+// Keep the shifted fp32 copy of a lane's elements in VGPRs (instead of
+// re-widening the packed copy in each pass) when a lane holds at most this
+// many elements.
+#ifndef MI355_CACHE_F32_MAX
+#define MI355_CACHE_F32_MAX 32
+#endif
+// Issue the gamma/beta loads together with the x loads (their latency then
+// overlaps the statistics) rather than after the reductions.
+#ifndef MI355_GB_EARLY
+#define MI355_GB_EARLY 0
+#endif
+// Persistent grids: load gamma/beta once per workgroup and keep them in
+// VGPRs across the rows the workgroup visits.
+#ifndef MI355_GB_RESIDENT
+#define MI355_GB_RESIDENT 0
+#endif
+
+template <bool B>
+struct bool_c {
+    static constexpr bool value = B;
+};
+
+// sum of the EPV widened elements of a vector minus K, as a pairwise tree
+template <class V, int EPV>
+__device__ __forceinline__ float vec_sum_shifted(const V& v, float K) {
+    float t[EPV];
+#pragma unroll
+    for (int k = 0; k < EPV; ++k) t[k] = v.get(k) - K;
+#pragma unroll
+    for (int h = 1; h < EPV; h *= 2)
+#pragma unroll
+        for (int k = 0; k + h < EPV; k += 2 * h) t[k] += t[k + h];
+    return t[0];
+}
+
 template <class T, bool RMS, int TEAM, int VPL, int EPV>
 __global__ __launch_bounds__(TeamGeom<TEAM>::WG)
 void norm_rows_kernel(const typename T::storage* __restrict__ x,
@@ -62,125 +99,168 @@ void norm_rows_kernel(const typename T::storage* __restrict__ x,
     using S = typename T::storage;
     using V = Vec<T, EPV>;
     constexpr int E = VPL * EPV;               // elements per lane
-    // keep the shifted fp32 copy of the row when it fits comfortably in VGPRs
-    constexpr bool CACHE_F32 = E <= 32;
+    constexpr bool CACHE_F32 = E <= MI355_CACHE_F32_MAX;
+    constexpr bool GB_EARLY = MI355_GB_EARLY != 0;
+    constexpr bool GB_RES = MI355_GB_RESIDENT != 0;
 
+    // cross-wavefront exchange slots: two sets, one float per wavefront
     __shared__ float red[2][G::ROWS][G::WPT];
 
     const int tid = threadIdx.x;
-    const int team = tid / TEAM;
+    const int team = TEAM >= 64 ? __builtin_amdgcn_readfirstlane(tid / TEAM) : tid / TEAM;
     const int tl = tid % TEAM;
     const int wave_in_team = TEAM > 64 ? __builtin_amdgcn_readfirstlane(tl >> 6) : 0;
     const int NV = N / EPV;                    // EPV divides N on every path
-    const float fN = (float)N;
+    const float inv_n = 1.0f / (float)N;        // divisor is the true N
     const bool has_g = gamma != nullptr;
     const bool has_b = beta != nullptr;
+
+    // gamma / beta held in VGPRs for the whole kernel (persistent grids)
+    V gres[GB_RES ? VPL : 1], bres[GB_RES ? VPL : 1];
+    if constexpr (GB_RES) {
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+            const unsigned v = (unsigned)(j * TEAM + tl);
+            if ((int)v < NV) {
+                if (has_g) gres[j].load(gamma + v * EPV);
+                if (!RMS && has_b) bres[j].load(beta + v * EPV);
+            }
+        }
+    }
 
     const int64_t groups = (M + G::ROWS - 1) / G::ROWS;
     int par = 0;    // RMS alternates LDS slot sets between iterations
     for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x, par ^= 1) {
         const int64_t row = grp * G::ROWS + team;
         const bool row_ok = row < M;
-        const S* xr = x + (row_ok ? row : 0) * (int64_t)N;
-        S* yr = y + (row_ok ? row : 0) * (int64_t)N;
+        // row base (wavefront-uniform when TEAM >= 64) plus 32-bit lane offsets
+        const int64_t base = (row_ok ? row : 0) * (int64_t)N;
+        const S* xr = x + base;
+        S* yr = y + base;
 
         V xv[VPL];
         bool ok[VPL];
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
-            const int v = j * TEAM + tl;
-            ok[j] = row_ok && v < NV;
-            if (ok[j]) xv[j].load(xr + (int64_t)v * EPV);
-            else xv[j].zero();
+            const unsigned v = (unsigned)(j * TEAM + tl);
+            ok[j] = row_ok && (int)v < NV;
+            if (ok[j]) xv[j].load_stream(xr + v * EPV);   // masked vectors stay undefined:
+        }                                                 // every use below is masked per vector
+        V gv[GB_EARLY ? VPL : 1], bv[GB_EARLY ? VPL : 1];
+        if constexpr (GB_EARLY && !GB_RES) {
+#pragma unroll
+            for (int j = 0; j < VPL; ++j) {
+                const unsigned off = (unsigned)(j * TEAM + tl) * EPV;
+                if (ok[j] && has_g) gv[j].load(gamma + off);
+                if (!RMS && ok[j] && has_b) bv[j].load(beta + off);
+            }
         }
 
         float rs, mu = 0.0f, K = 0.0f;
         float d[CACHE_F32 ? VPL : 1][EPV];
         if constexpr (RMS) {
-            float acc[EPV];
+            float acc = 0.0f;
 #pragma unroll
-            for (int k = 0; k < EPV; ++k) acc[k] = 0.0f;
+            for (int j = 0; j < VPL; ++j) {
+                float t = 0.0f;
 #pragma unroll
-            for (int j = 0; j < VPL; ++j)
-#pragma unroll
-                for (int k = 0; k < EPV; ++k) {
-                    const float v = xv[j].get(k);       // masked vectors hold zeros
-                    acc[k] = __builtin_fmaf(v, v, acc[k]);
-                }
-            float q = acc[0];
-#pragma unroll
-            for (int k = 1; k < EPV; ++k) q += acc[k];
+                for (int k = 0; k < EPV; ++k) t = __builtin_fmaf(xv[j].get(k), xv[j].get(k), t);
+                acc += ok[j] ? t : 0.0f;
+            }
             // one exchange per iteration: alternating slot sets keep a fast
             // wavefront's next write away from slots a slow one still reads
-            q = team_reduce<TEAM>(q, red[par][team], wave_in_team);
-            rs = 1.0f / __builtin_sqrtf(q / fN + eps);
+            acc = team_reduce<TEAM>(acc, red[par][team], wave_in_team);
+            rs = 1.0f / __builtin_sqrtf(__builtin_fmaf(acc, inv_n, eps));
         } else {
-            // two exchanges per iteration (slot sets 0 then 1): the barrier of
-            // the second orders every read of set 0 before the next write
             K = row_ok ? T::widen(xr[0]) : 0.0f;
-            // pass 1: sum of d = x - K over the valid elements
-            float acc[EPV];
+            // pass 1: sum of d = x - K over the valid vectors
+            float s = 0.0f;
 #pragma unroll
-            for (int k = 0; k < EPV; ++k) acc[k] = 0.0f;
+            for (int j = 0; j < VPL; ++j) {
+                if constexpr (CACHE_F32) {
 #pragma unroll
-            for (int j = 0; j < VPL; ++j)
-#pragma unroll
-                for (int k = 0; k < EPV; ++k) {
-                    const float dv = ok[j] ? xv[j].get(k) - K : 0.0f;
-                    if constexpr (CACHE_F32) d[j][k] = dv;
-                    acc[k] += dv;
+                    for (int k = 0; k < EPV; ++k) d[j][k] = xv[j].get(k) - K;
                 }
-            float s = acc[0];
-#pragma unroll
-            for (int k = 1; k < EPV; ++k) s += acc[k];
+                const float t = vec_sum_shifted<V, EPV>(xv[j], K);
+                s += ok[j] ? t : 0.0f;
+            }
             s = team_reduce<TEAM>(s, red[0][team], wave_in_team);
-            mu = s / fN;
-            // pass 2: sum of (d - mu')^2 over the valid elements
+            mu = s * inv_n;
+            if constexpr (!CACHE_F32) {
 #pragma unroll
-            for (int k = 0; k < EPV; ++k) acc[k] = 0.0f;
+                for (int j = 0; j < VPL; ++j) xv[j].opaque();
+            }
+            // pass 2: sum of (d - mu')^2 over the valid vectors
+            float q = 0.0f;
 #pragma unroll
-            for (int j = 0; j < VPL; ++j)
+            for (int j = 0; j < VPL; ++j) {
+                float t = 0.0f;
 #pragma unroll
                 for (int k = 0; k < EPV; ++k) {
                     float dv;
                     if constexpr (CACHE_F32) dv = d[j][k];
                     else dv = xv[j].get(k) - K;
-                    const float e = ok[j] ? dv - mu : 0.0f;
+                    const float e = dv - mu;
                     if constexpr (CACHE_F32) d[j][k] = e;
-                    acc[k] = __builtin_fmaf(e, e, acc[k]);
+                    t = __builtin_fmaf(e, e, t);
                 }
-            float q = acc[0];
-#pragma unroll
-            for (int k = 1; k < EPV; ++k) q += acc[k];
+                q += ok[j] ? t : 0.0f;
+            }
+            // two exchanges per iteration (slot sets 0 then 1): the barrier of
+            // the second orders every read of set 0 before the next write
             q = team_reduce<TEAM>(q, red[1][team], wave_in_team);
-            rs = 1.0f / __builtin_sqrtf(q / fN + eps);
+            rs = 1.0f / __builtin_sqrtf(__builtin_fmaf(q, inv_n, eps));
         }
 
+        if constexpr (!CACHE_F32) {
+#pragma unroll
+            for (int j = 0; j < VPL; ++j) xv[j].opaque();
+        }
         if (tl == 0 && row_ok) {
             if (!RMS && mean_out) mean_out[row] = K + mu;
             if (rstd_out) rstd_out[row] = rs;
         }
 
-        // normalise from the register copy, apply the affine, store
+        // normalise from the register copy, apply the affine, store; the
+        // presence of gamma / beta is resolved by a uniform branch, so the
+        // inner loop carries no per-element selects
+        auto emit = [&](auto hg, auto hb) {
+            constexpr bool HG = decltype(hg)::value;
+            constexpr bool HB = !RMS && decltype(hb)::value;
 #pragma unroll
-        for (int j = 0; j < VPL; ++j) {
-            if (!ok[j]) continue;
-            const int64_t off = (int64_t)(j * TEAM + tl) * EPV;
-            V gv, bv;
-            if (has_g) gv.load(gamma + off);
-            if (!RMS && has_b) bv.load(beta + off);
-            float o[EPV];
+            for (int j = 0; j < VPL; ++j) {
+                if (!ok[j]) continue;
+                const unsigned off = (unsigned)(j * TEAM + tl) * EPV;
+                V gl, bl;
+                if constexpr (!GB_EARLY && !GB_RES) {
+                    if constexpr (HG) gl.load(gamma + off);
+                    if constexpr (HB) bl.load(beta + off);
+                }
+                const V& gj = GB_RES ? gres[GB_RES ? j : 0] : GB_EARLY ? gv[GB_EARLY ? j : 0] : gl;
+                const V& bj = GB_RES ? bres[GB_RES ? j : 0] : GB_EARLY ? bv[GB_EARLY ? j : 0] : bl;
+                float o[EPV];
 #pragma unroll
-            for (int k = 0; k < EPV; ++k) {
-                float t;
-                if constexpr (RMS) t = xv[j].get(k) * rs;
-                else if constexpr (CACHE_F32) t = d[j][k] * rs;
-                else t = ((xv[j].get(k) - K) - mu) * rs;
-                const float g = has_g ? gv.get(k) : 1.0f;
-                if constexpr (RMS) o[k] = t * g;
-                else o[k] = __builtin_fmaf(t, g, has_b ? bv.get(k) : 0.0f);
+                for (int k = 0; k < EPV; ++k) {
+                    float t;
+                    if constexpr (RMS) t = xv[j].get(k) * rs;
+                    else if constexpr (CACHE_F32) t = d[j][k] * rs;
+                    else t = ((xv[j].get(k) - K) - mu) * rs;
+                    if constexpr (HG && HB) o[k] = __builtin_fmaf(t, gj.get(k), bj.get(k));
+                    else if constexpr (HG) o[k] = t * gj.get(k);
+                    else if constexpr (HB) o[k] = t + bj.get(k);
+                    else o[k] = t;
+                }
+                V::store(yr + off, o);
             }
-            V::store(yr + off, o);
+        };
+        using TT = bool_c<true>;
+        using FF = bool_c<false>;
+        if (has_g) {
+            if (has_b) emit(TT{}, TT{});
+            else emit(TT{}, FF{});
+        } else {
+            if (has_b) emit(FF{}, TT{});
+            else emit(FF{}, FF{});
         }
     }
 }

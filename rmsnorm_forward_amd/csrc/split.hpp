@@ -63,7 +63,7 @@ void norm_split_stats_kernel(const typename T::storage* __restrict__ x,
         for (int j = 0; j < VPL; ++j) {
             const int v = v0 + j * WG + tid;
             ok[j] = v < NV;
-            if (ok[j]) xv[j].load(xr + (int64_t)v * EPV);
+            if (ok[j]) xv[j].load_stream(xr + (int64_t)v * EPV);
             else xv[j].zero();
         }
         float2 out;
@@ -169,7 +169,7 @@ void norm_split_apply_kernel(const typename T::storage* __restrict__ x,
         for (int j = 0; j < VPL; ++j) {
             const int v = v0 + j * WG + tid;
             ok[j] = v < NV;
-            if (ok[j]) xv[j].load(xr + (int64_t)v * EPV);
+            if (ok[j]) xv[j].load_stream(xr + (int64_t)v * EPV);
             else xv[j].zero();
         }
         const float2* pr = ws + row * (int64_t)S;
