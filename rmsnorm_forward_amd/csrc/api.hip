@@ -1,20 +1,22 @@
 // api.hip -- the C ABI (include/mi355norm.h): argument validation, choice of
 // the row-to-workgroup mapping from (N, dtype, alignment), and launch.
 //
-// Mapping regimes (chosen by row length in 16-byte vectors, NV; every lane
-// holds two vectors, the team is as large as the row needs):
-//   small rows  (up to 1 KiB): a team of 4..32 lanes per row, so 2..16 rows
-//               share a wavefront and reduce with DPP only;
-//   mid rows    (1 KiB .. 32 KiB): 64..1024 lanes per row, one LDS exchange
-//               per reduction across the row's wavefronts; beyond 32 KiB the
-//               1024-lane team holds 4..16 vectors per lane;
+// Mapping regimes, chosen by row length in 16-byte vectors (NV).  Every lane
+// holds four vectors for 2-byte types (32 elements) and two for fp32 (8
+// elements); the team is as large as the row needs (at least 8 lanes):
+//   small rows  (bf16 N <= 1024, fp32 N <= 256): 8..32 lanes per row, 2..8
+//               rows share a wavefront and reduce with DPP only;
+//   mid rows    (up to 1024 lanes): 64..1024 lanes per row, one LDS exchange
+//               per reduction across the row's wavefronts; longer rows give
+//               the 1024-lane team up to 16 vectors per lane;
 //   long rows   (beyond 1024 lanes x 16 vectors): split across workgroups,
 //               per-chunk partial statistics merged in chunk order (Chan) in
 //               a second kernel.
-// Two vectors per lane measured best on MI355X for 4..16 KiB rows (e.g. bf16
-// 16384 x 8192 LayerNorm: 512x2 90.5 us, 256x4 91.5 us, 128x8 93.6 us; bf16
-// 2048-wide RMSNorm: 128x2 86.5 us against 100.3 us for two rows per
-// wavefront at 32x8).
+// Measured on MI355X in steady state (200 back-to-back launches): bf16
+// 1024-wide RMSNorm 32x4 (2 rows per wavefront) 85.3 us vs 64x2 87.1, 16x8
+// 95.1; bf16 2048-wide 64x4 87.6 vs 32x8 99.4; fp32 2048-wide 256x2 175.0
+// vs 128x4 177.6, 64x8 189.6.  More than four vectors per lane, or 4-lane
+// teams, always lost.
 //
 // Test/benchmark hooks (environment, read per call):
 //   MI355NORM_PATH = rows | split      force the path (rows only if it fits)
@@ -136,11 +138,9 @@ int make_plan(int op, int64_t M, int64_t N, int dtype, bool aligned, const Overr
             vpl = o.vpl;
             if (!tile_instantiated(team, vpl) || int64_t(team) * vpl < NV) return NORM_ERR_BAD_ARG;
         } else {
-            // two vectors per lane, team as large as the row needs: rows of
-            // up to 64 vectors share a wavefront (4..32 lanes each), up to
-            // 2048 vectors take 1..16 wavefronts; longer rows add vectors
-            team = next_pow2((NV + 1) / 2);
-            if (team < 4) team = 4;
+            const int per_lane = e == 2 ? 4 : 2;
+            team = next_pow2((NV + per_lane - 1) / per_lane);
+            if (team < 8) team = 8;
             if (team > kMaxTeam) team = kMaxTeam;
             vpl = round_vpl((NV + team - 1) / team);
         }

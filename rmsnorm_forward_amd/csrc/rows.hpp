@@ -62,7 +62,7 @@ __device__ __forceinline__ float team_reduce(float v, float* slots, int wave_in_
 #define MI355_GB_EARLY 0
 #endif
 // Persistent grids: load gamma/beta once per workgroup and keep them in
-// VGPRs across the rows the workgroup visits.
+// VGPRs, widened to fp32, across the rows the workgroup visits.
 #ifndef MI355_GB_RESIDENT
 #define MI355_GB_RESIDENT 0
 #endif
@@ -115,15 +115,21 @@ void norm_rows_kernel(const typename T::storage* __restrict__ x,
     const bool has_g = gamma != nullptr;
     const bool has_b = beta != nullptr;
 
-    // gamma / beta held in VGPRs for the whole kernel (persistent grids)
-    V gres[GB_RES ? VPL : 1], bres[GB_RES ? VPL : 1];
+    // gamma / beta held in VGPRs as fp32 for the whole kernel (persistent grids)
+    float gres[GB_RES ? VPL : 1][EPV], bres[GB_RES ? VPL : 1][EPV];
     if constexpr (GB_RES) {
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
             const unsigned v = (unsigned)(j * TEAM + tl);
+            V gt, bt;
             if ((int)v < NV) {
-                if (has_g) gres[j].load(gamma + v * EPV);
-                if (!RMS && has_b) bres[j].load(beta + v * EPV);
+                if (has_g) gt.load(gamma + v * EPV);
+                if (!RMS && has_b) bt.load(beta + v * EPV);
+            }
+#pragma unroll
+            for (int k = 0; k < EPV; ++k) {
+                gres[j][k] = has_g ? gt.get(k) : 1.0f;
+                bres[j][k] = (!RMS && has_b) ? bt.get(k) : 0.0f;
             }
         }
     }
@@ -170,7 +176,7 @@ void norm_rows_kernel(const typename T::storage* __restrict__ x,
             // one exchange per iteration: alternating slot sets keep a fast
             // wavefront's next write away from slots a slow one still reads
             acc = team_reduce<TEAM>(acc, red[par][team], wave_in_team);
-            rs = 1.0f / __builtin_sqrtf(__builtin_fmaf(acc, inv_n, eps));
+            rs = rsqrt_hw(__builtin_fmaf(acc, inv_n, eps));
         } else {
             K = row_ok ? T::widen(xr[0]) : 0.0f;
             // pass 1: sum of d = x - K over the valid vectors
@@ -209,7 +215,7 @@ void norm_rows_kernel(const typename T::storage* __restrict__ x,
             // two exchanges per iteration (slot sets 0 then 1): the barrier of
             // the second orders every read of set 0 before the next write
             q = team_reduce<TEAM>(q, red[1][team], wave_in_team);
-            rs = 1.0f / __builtin_sqrtf(__builtin_fmaf(q, inv_n, eps));
+            rs = rsqrt_hw(__builtin_fmaf(q, inv_n, eps));
         }
 
         if constexpr (!CACHE_F32) {
@@ -236,8 +242,8 @@ void norm_rows_kernel(const typename T::storage* __restrict__ x,
                     if constexpr (HG) gl.load(gamma + off);
                     if constexpr (HB) bl.load(beta + off);
                 }
-                const V& gj = GB_RES ? gres[GB_RES ? j : 0] : GB_EARLY ? gv[GB_EARLY ? j : 0] : gl;
-                const V& bj = GB_RES ? bres[GB_RES ? j : 0] : GB_EARLY ? bv[GB_EARLY ? j : 0] : bl;
+                const V& gj = GB_EARLY ? gv[GB_EARLY ? j : 0] : gl;
+                const V& bj = GB_EARLY ? bv[GB_EARLY ? j : 0] : bl;
                 float o[EPV];
 #pragma unroll
                 for (int k = 0; k < EPV; ++k) {
@@ -245,9 +251,12 @@ void norm_rows_kernel(const typename T::storage* __restrict__ x,
                     if constexpr (RMS) t = xv[j].get(k) * rs;
                     else if constexpr (CACHE_F32) t = d[j][k] * rs;
                     else t = ((xv[j].get(k) - K) - mu) * rs;
-                    if constexpr (HG && HB) o[k] = __builtin_fmaf(t, gj.get(k), bj.get(k));
-                    else if constexpr (HG) o[k] = t * gj.get(k);
-                    else if constexpr (HB) o[k] = t + bj.get(k);
+                    const float g = GB_RES ? gres[GB_RES ? j : 0][k] : (HG ? gj.get(k) : 1.0f);
+                    const float b = GB_RES ? bres[GB_RES ? j : 0][k] : (HB ? bj.get(k) : 0.0f);
+                    if constexpr (GB_RES) o[k] = RMS ? t * g : __builtin_fmaf(t, g, b);
+                    else if constexpr (HG && HB) o[k] = __builtin_fmaf(t, g, b);
+                    else if constexpr (HG) o[k] = t * g;
+                    else if constexpr (HB) o[k] = t + b;
                     else o[k] = t;
                 }
                 V::store(yr + off, o);

@@ -178,12 +178,12 @@ void norm_split_apply_kernel(const typename T::storage* __restrict__ x,
             float q = 0.0f;
             for (int cc = lane_id(); cc < S; cc += 64) q += pr[cc].x;
             q = team_sum<64>(q);
-            rs = 1.0f / __builtin_sqrtf(q / fN + eps);
+            rs = rsqrt_hw(q / fN + eps);
         } else {
             K = T::widen(xr[0]);
             const Welford w = merge_row_partials(pr, S, CV * EPV, N);
             mu = w.mean;
-            rs = 1.0f / __builtin_sqrtf(w.m2 / fN + eps);
+            rs = rsqrt_hw(w.m2 / fN + eps);
         }
         if (c == 0 && tid == 0) {
             if (!RMS && mean_out) mean_out[row] = K + mu;

@@ -99,10 +99,10 @@ def parse(desc):
 @pytest.mark.parametrize("op,M,N,dtype,want", [
     ("ln", 128, 1024, "f32", dict(path="rows", team="128", vpl="2", epv="4")),
     ("rms", 8192, 4096, "f32", dict(path="rows", team="512", vpl="2", epv="4")),
-    ("ln", 16384, 8192, "bf16", dict(path="rows", team="512", vpl="2", epv="8")),
+    ("ln", 16384, 8192, "bf16", dict(path="rows", team="256", vpl="4", epv="8")),
     ("rms", 65536, 2048, "f32", dict(path="rows", team="256", vpl="2", epv="4")),
-    ("rms", 65536, 2048, "bf16", dict(path="rows", team="128", vpl="2", epv="8")),
-    ("ln", 4096, 5120, "bf16", dict(path="rows", team="512", vpl="2", epv="8")),
+    ("rms", 65536, 2048, "bf16", dict(path="rows", team="64", vpl="4", epv="8")),
+    ("ln", 4096, 5120, "bf16", dict(path="rows", team="256", vpl="4", epv="8")),
     ("ln", 64, 1 << 20, "bf16", dict(path="split", chunks="128", epv="8")),
 ])
 def test_plans_of_the_measured_configurations(op, M, N, dtype, want):
@@ -112,9 +112,12 @@ def test_plans_of_the_measured_configurations(op, M, N, dtype, want):
 
 
 def test_small_rows_share_a_wavefront():
-    for N in (16, 64, 200, 256, 512):             # aligned rows of at most 1 KiB
+    for N in (16, 64, 200, 256, 512, 1024):       # aligned bf16 rows of at most 2 KiB
         d = parse(rn.norm_describe("rms", 1000, N, "bf16"))
         assert int(d["team"]) <= 32 and int(d["rows_per_wg"]) >= 8, (N, d)
+    for N in (16, 64, 256):                        # fp32 rows of at most 1 KiB
+        d = parse(rn.norm_describe("ln", 1000, N, "f32"))
+        assert int(d["team"]) <= 32, (N, d)
 
 
 def test_unaligned_plans_take_the_elementwise_path():
