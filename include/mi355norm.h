@@ -52,11 +52,15 @@
  *   results).  Buffers must not overlap (y may not alias x: no in-place use).
  *
  * Ownership: the caller allocates and owns every buffer and keeps it alive
- * until the stream has passed the call.  The library keeps no pointer after
- * return.  Rows too long for one workgroup (about N > 2^17 for 2-byte and
- * N > 2^16 for 4-byte types) use a small device workspace of
- * M * ceil(N / chunk) * 8 bytes, taken from and returned to the device's
- * stream-ordered memory pool on `stream` (hipMallocAsync / hipFreeAsync).
+ * until the stream has passed the call.  The library keeps no pointer to
+ * them after return.  Rows too long for one workgroup (N > 2^17 for 2-byte
+ * and N > 2^16 for 4-byte types, with 16-byte alignment; N > 2^14 without)
+ * are processed in batches of rows holding about 256 MiB of x, two kernel
+ * launches per batch, and use a library-owned device workspace of at most a
+ * few MiB (per row of a batch: 264 bytes plus 8 bytes per chunk of the row),
+ * one per (device, stream), allocated on first need, grown when a larger
+ * call needs it (the only time a call waits for its stream), and kept until
+ * the process exits.
  *
  * Errors: arguments are validated on the host before any HIP call; a bad
  * argument returns its status and touches nothing.  A launch failure returns
@@ -98,6 +102,14 @@ int rms_fwd(const void *x, const void *gamma, const void *beta, void *y,
 
 /* Static, NUL-terminated description of a status code. */
 const char *norm_status_str(int status);
+
+/*
+ * The HIP failure behind the calling thread's most recent NORM_ERR_HIP: the
+ * failing call and HIP's error name and text ("" if none yet).  The string
+ * belongs to the library and stays valid until that thread's next failing
+ * call.
+ */
+const char *norm_last_error(void);
 
 /*
  * Describe, without launching anything, how a call with these arguments

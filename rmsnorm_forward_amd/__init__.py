@@ -28,6 +28,15 @@ if not os.path.exists(LIB_PATH):
         f"{LIB_PATH} is missing: build it with `python rmsnorm_forward_amd/build.py` "
         "(hipcc, gfx950).  There is no non-HIP fallback.")
 
+# The library is handed torch's allocations and stream handles, so it must
+# run on the HIP runtime torch runs on.  torch ships its own libamdhip64 with
+# the same soname as the system one; loading torch first makes the dynamic
+# loader bind the library to that copy instead of mapping a second runtime.
+try:
+    import torch as _torch  # noqa: F401
+except ImportError:  # a process without torch uses the system runtime
+    _torch = None
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 _vp, _i64, _f32, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
@@ -37,11 +46,14 @@ for _name in ("ln_fwd", "rms_fwd"):
     _fn.restype = _int
 _lib.norm_status_str.argtypes = [_int]
 _lib.norm_status_str.restype = ctypes.c_char_p
+_lib.norm_last_error.argtypes = []
+_lib.norm_last_error.restype = ctypes.c_char_p
 _lib.norm_describe.argtypes = [_int, _i64, _i64, _int, _int, ctypes.c_char_p, _int]
 _lib.norm_describe.restype = _int
 
 NORM_F32, NORM_F16, NORM_BF16 = 0, 1, 2
 NORM_OK = 0
+NORM_ERR_HIP = 7
 STATUS = {0: "NORM_OK", 1: "NORM_ERR_NULL_ARG", 2: "NORM_ERR_BAD_SHAPE", 3: "NORM_ERR_BAD_DTYPE",
           4: "NORM_ERR_BAD_EPS", 5: "NORM_ERR_BAD_ARG", 6: "NORM_ERR_ALIAS", 7: "NORM_ERR_HIP"}
 DTYPE_NAMES = {"f32": NORM_F32, "f16": NORM_F16, "bf16": NORM_BF16}
@@ -69,6 +81,11 @@ def rms_fwd(x, gamma, beta, y, mean, rstd, M, N, eps, dtype, stream) -> int:
 
 def norm_status_str(status: int) -> str:
     return _lib.norm_status_str(int(status)).decode()
+
+
+def norm_last_error() -> str:
+    """The HIP failure behind this thread's last NORM_ERR_HIP ("" if none)."""
+    return _lib.norm_last_error().decode()
 
 
 def norm_describe(op: str, M: int, N: int, dtype, aligned: bool = True) -> str:
@@ -104,7 +121,8 @@ def _param(p, N, x):
 
 def _check(st):
     if st != NORM_OK:
-        raise RuntimeError(f"{STATUS.get(st, st)}: {norm_status_str(st)}")
+        extra = f" [{norm_last_error()}]" if st == NORM_ERR_HIP else ""
+        raise RuntimeError(f"{STATUS.get(st, st)}: {norm_status_str(st)}{extra}")
 
 
 def layer_norm(x, gamma=None, beta=None, eps: float = 1e-5, want_stats: bool = True):
@@ -150,5 +168,5 @@ def rms_norm(x, gamma=None, eps: float = 1e-6, want_rstd: bool = True):
     return y.view(x.shape), rstd
 
 
-__all__ = ["ln_fwd", "rms_fwd", "norm_status_str", "norm_describe", "layer_norm", "rms_norm",
+__all__ = ["ln_fwd", "rms_fwd", "norm_status_str", "norm_last_error", "norm_describe", "layer_norm", "rms_norm",
            "NORM_F32", "NORM_F16", "NORM_BF16", "NORM_OK", "STATUS", "LIB_PATH"]

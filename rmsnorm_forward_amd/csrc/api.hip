@@ -9,9 +9,11 @@
 //   mid rows    (up to 1024 lanes): 64..1024 lanes per row, one LDS exchange
 //               per reduction across the row's wavefronts; longer rows give
 //               the 1024-lane team up to 16 vectors per lane;
-//   long rows   (beyond 1024 lanes x 16 vectors): split across workgroups,
-//               per-chunk partial statistics merged in chunk order (Chan) in
-//               a second kernel.
+//   long rows   (beyond 1024 lanes x 16 vectors): split across workgroups
+//               in chunks of 256 lanes x 4 vectors; per-chunk partial
+//               statistics merged in chunk order (Chan).  Single pass when all
+//               chunks of a row fit on the device at once (cooperative launch,
+//               per-row team barrier, x read once); otherwise two kernels.
 // Measured on MI355X in steady state (200 back-to-back launches): bf16
 // 1024-wide RMSNorm 32x4 (2 rows per wavefront) 85.3 us vs 64x2 87.1, 16x8
 // 95.1; bf16 2048-wide 64x4 87.6 vs 32x8 99.4; fp32 2048-wide 256x2 175.0
@@ -19,17 +21,24 @@
 // teams, always lost.
 //
 // Test/benchmark hooks (environment, read per call):
-//   MI355NORM_PATH = rows | split      force the path (rows only if it fits)
+//   MI355NORM_PATH = rows | split | split2 | splitcoop
+//                                       force the path (rows only if it fits;
+//                                       splitcoop only if a row fits resident)
 //   MI355NORM_TILE = <team>x<vpl>       force the row-kernel tile
 //   MI355NORM_GRID = <n>                cap the number of workgroups
+//   MI355NORM_SPIN_LIMIT = <n>          bound of the single-pass split's wait
+//   MI355NORM_FORCE_TIMEOUT = 1         make that wait time out (failure-path test)
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <map>
 #include <mutex>
+#include <utility>
 
 #include "../../include/mi355norm.h"
 #include "dispatch.hpp"
@@ -39,6 +48,11 @@ using namespace mi355norm;
 namespace {
 
 enum { OP_LN = 0, OP_RMS = 1 };
+
+__global__ void norm_zero_u32(unsigned* p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
 
 constexpr int64_t kMaxN = int64_t(1) << 24;
 constexpr int64_t kMaxGrid = int64_t(1) << 20;
@@ -90,9 +104,13 @@ int round_vpl(int64_t v) {
 
 // Environment hooks for tests and the benchmark.
 struct Overrides {
-    int path = -1;   // -1 auto
+    int path = -1;        // -1 auto
+    int split_mode = -1;  // -1 auto
     int team = 0, vpl = 0;
     int64_t grid = 0;
+    unsigned spin_limit = 1u << 20;
+    bool force_timeout = false;
+    int64_t batch_bytes = 0;  // two-kernel split: bytes of x per batch (0: default)
 };
 
 Overrides read_overrides() {
@@ -100,12 +118,17 @@ Overrides read_overrides() {
     if (const char* s = std::getenv("MI355NORM_PATH")) {
         if (!std::strcmp(s, "rows")) o.path = PATH_ROWS;
         else if (!std::strcmp(s, "split")) o.path = PATH_SPLIT;
+        else if (!std::strcmp(s, "split2")) { o.path = PATH_SPLIT; o.split_mode = SPLIT_TWO; }
+        else if (!std::strcmp(s, "splitcoop")) { o.path = PATH_SPLIT; o.split_mode = SPLIT_COOP; }
     }
+    if (const char* s = std::getenv("MI355NORM_SPIN_LIMIT")) o.spin_limit = (unsigned)std::strtoul(s, nullptr, 10);
+    if (const char* s = std::getenv("MI355NORM_FORCE_TIMEOUT")) o.force_timeout = std::atoi(s) != 0;
     if (const char* s = std::getenv("MI355NORM_TILE")) {
         int t = 0, v = 0;
         if (std::sscanf(s, "%dx%d", &t, &v) == 2) { o.team = t; o.vpl = v; }
     }
     if (const char* s = std::getenv("MI355NORM_GRID")) o.grid = std::atoll(s);
+    if (const char* s = std::getenv("MI355NORM_SPLIT_BATCH")) o.batch_bytes = std::atoll(s);
     return o;
 }
 
@@ -116,9 +139,37 @@ bool tile_instantiated(int team, int vpl) {
     return t && v;
 }
 
+// How many workgroups of the single-pass split kernel the current device can
+// hold at once (0 if cooperative launch is unavailable or no device is
+// present).  Cached per (device, dtype, op, vector width).
+int64_t coop_capacity(int dtype, bool rms, int epv) {
+    static std::mutex mu;
+    static int64_t cache[64][3][2][2];
+    static bool known[64][3][2][2];
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) return 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    const int vi = epv == 1 ? 0 : 1;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!known[dev][dtype][rms][vi]) {
+        int coop = 0, cus = 0;
+        int64_t cap = 0;
+        if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && coop &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) {
+            int per_cu = dtype == NORM_F32 ? coop_blocks_per_cu_f32(rms, epv)
+                         : dtype == NORM_BF16 ? coop_blocks_per_cu_bf16(rms, epv)
+                                              : coop_blocks_per_cu_f16(rms, epv);
+            cap = int64_t(per_cu) * cus;
+        }
+        cache[dev][dtype][rms][vi] = cap;
+        known[dev][dtype][rms][vi] = true;
+    }
+    return cache[dev][dtype][rms][vi];
+}
+
 // Returns NORM_OK and fills *p, or NORM_ERR_BAD_ARG if an override cannot run.
 int make_plan(int op, int64_t M, int64_t N, int dtype, bool aligned, const Overrides& o, Plan* p) {
-    (void)op;
     const int e = elem_bytes(dtype);
     std::memset(p, 0, sizeof *p);
     p->epv = aligned ? 16 / e : 1;
@@ -150,15 +201,96 @@ int make_plan(int op, int64_t M, int64_t N, int dtype, bool aligned, const Overr
         p->rows_per_wg = p->wg / team;
         p->work = (M + p->rows_per_wg - 1) / p->rows_per_wg;
     } else {
-        p->wg = kSplitWG;
-        p->vpl = kSplitVPL;
-        const int64_t cv = int64_t(kSplitWG) * kSplitVPL;
-        p->chunks = (int)((NV + cv - 1) / cv);
-        p->work = M * p->chunks;
+        // Two kernels by default: they measure faster than the single pass
+        // here because x's second read is served by the Infinity Cache.  The
+        // single pass runs when asked for and every chunk of at least one row
+        // can be resident.
+        if (o.split_mode == SPLIT_COOP) {
+            const int64_t ccv = int64_t(kCoopWG) * kCoopVPL;
+            const int64_t cchunks = (NV + ccv - 1) / ccv;
+            const int64_t cap = coop_capacity(dtype, op == OP_RMS, p->epv);
+            if (cap < cchunks) return NORM_ERR_BAD_ARG;
+            p->split_mode = SPLIT_COOP;
+            p->wg = kCoopWG;
+            p->vpl = kCoopVPL;
+            p->chunks = (int)cchunks;
+            p->teams = (int)std::min<int64_t>(M, cap / cchunks);
+            p->batch_rows = M;
+            p->work = M * p->chunks;
+        } else {
+            const int64_t cv = int64_t(kSplitWG) * kSplitVPL;
+            p->split_mode = SPLIT_TWO;
+            p->wg = kSplitWG;
+            p->vpl = kSplitVPL;
+            p->chunks = (int)((NV + cv - 1) / cv);
+            const int64_t bb = o.batch_bytes > 0 ? o.batch_bytes : kSplitBatchBytes;
+            const int64_t rows = bb / (N * e);
+            p->batch_rows = std::min<int64_t>(M, rows > 0 ? rows : 1);
+            p->work = p->batch_rows * p->chunks;   // per launch
+        }
     }
     int64_t cap = o.grid > 0 ? o.grid : kMaxGrid;
     p->grid = p->work < cap ? p->work : cap;
+    if (p->path == PATH_SPLIT && p->split_mode == SPLIT_COOP) p->grid = int64_t(p->teams) * p->chunks;
     return NORM_OK;
+}
+
+// Workspace of the split-row path, one per (device, stream), kept across
+// calls.  Calls on one stream run in stream order, so they can share it;
+// calls on different streams get different buffers.  Layout: barrier
+// counters first, at a fixed base (their capacity fixed per allocation), then
+// the per-chunk partials.  Everything is zero when allocated, and the
+// single-pass kernel leaves every counter it used at zero when it finishes,
+// so counters are zero at the start of every call whatever its shape.
+// Growing (only on a new largest call) waits for the stream, since the old
+// buffer may still be in use, and reallocates both regions.
+struct Workspace {
+    unsigned* sync;   // >= 2 * M counters
+    float2* part;     // >= M * chunks partials
+};
+
+// The HIP failure behind the calling thread's most recent NORM_ERR_HIP.
+thread_local char g_last_error[192] = "";
+
+bool hip_ok(hipError_t e, const char* what) {
+    if (e == hipSuccess) return true;
+    std::snprintf(g_last_error, sizeof g_last_error, "%s: %s (%s, code %d)", what, hipGetErrorName(e),
+                  hipGetErrorString(e), (int)e);
+    return false;
+}
+
+bool stream_workspace(hipStream_t stream, size_t sync_words, size_t part_bytes, Workspace* out) {
+    struct Buf { void* ptr; size_t sync_words; size_t part_bytes; };   // sync_words >= 64 * M
+    static std::mutex mu;
+    static std::map<std::pair<int, hipStream_t>, Buf> bufs;
+    int dev = 0;
+    if (!hip_ok(hipGetDevice(&dev), "hipGetDevice")) return false;
+    std::lock_guard<std::mutex> lock(mu);
+    Buf& b = bufs[{dev, stream}];
+    if (!b.ptr || b.sync_words < sync_words || b.part_bytes < part_bytes) {
+        if (b.ptr) {
+            if (!hip_ok(hipStreamSynchronize(stream), "hipStreamSynchronize (workspace growth)")) return false;
+            (void)hipFree(b.ptr);   // the stream is idle: nothing uses it any more
+        }
+        const size_t sw = std::max({sync_words, 2 * b.sync_words, size_t(4096)});
+        const size_t pb = std::max({part_bytes, 2 * b.part_bytes, size_t(1) << 20});
+        const size_t sync_bytes = (sw * sizeof(unsigned) + 255) & ~size_t(255);
+        const size_t total = sync_bytes + ((pb + 255) & ~size_t(255));
+        b = Buf{nullptr, 0, 0};
+        void* ptr = nullptr;
+        if (!hip_ok(hipMalloc(&ptr, total), "hipMalloc (workspace)")) return false;
+        const size_t words = total / sizeof(unsigned);
+        hipLaunchKernelGGL(norm_zero_u32, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
+                           static_cast<unsigned*>(ptr), (int64_t)words);
+        if (!hip_ok(hipGetLastError(), "launch of the workspace fill kernel")) {
+            (void)hipFree(ptr);
+            return false;
+        }
+        b = Buf{ptr, sync_bytes / sizeof(unsigned), total - sync_bytes};
+    }
+    out->sync = static_cast<unsigned*>(b.ptr);
+    out->part = reinterpret_cast<float2*>(static_cast<char*>(b.ptr) + b.sync_words * sizeof(unsigned));
+    return true;
 }
 
 bool all_aligned16(const void* x, const void* g, const void* b, const void* y, int64_t N, int e) {
@@ -183,19 +315,52 @@ int run(int op, const void* x, const void* gamma, const void* beta, void* y, flo
         case NORM_BF16: err = launch_rows_bf16(rms, c, p); break;
         default: err = launch_rows_f16(rms, c, p); break;
         }
-        return err == hipSuccess ? NORM_OK : NORM_ERR_HIP;
+        return hip_ok(err, "row kernel launch") ? NORM_OK : NORM_ERR_HIP;
     }
-    // split path: stream-ordered workspace of M * chunks partials
-    float2* ws = nullptr;
-    const size_t ws_bytes = size_t(M) * size_t(p.chunks) * sizeof(float2);
-    if (hipMallocAsync(reinterpret_cast<void**>(&ws), ws_bytes, c.stream) != hipSuccess) return NORM_ERR_HIP;
-    switch (dtype) {
-    case NORM_F32: err = launch_split_f32(rms, c, p, ws); break;
-    case NORM_BF16: err = launch_split_bf16(rms, c, p, ws); break;
-    default: err = launch_split_f16(rms, c, p, ws); break;
+    // split path: partials, per-row statistics and barrier counters live in
+    // the workspace this (device, stream) keeps
+    const bool coop = p.split_mode == SPLIT_COOP;
+    const int64_t rows = p.batch_rows;   // rows per launch (pair of launches)
+    Workspace w;
+    const size_t part_elems = size_t(rows) * size_t(p.chunks) + (coop ? 0 : size_t(rows));
+    if (!stream_workspace(c.stream, size_t(rows) * kSyncStride, part_elems * sizeof(float2), &w))
+        return NORM_ERR_HIP;
+    float2* part = w.part;
+    if (coop) {
+        unsigned* sync = w.sync;
+        const Overrides o = read_overrides();
+        const unsigned need = (unsigned)p.chunks + (o.force_timeout ? 1u : 0u);
+        const unsigned spin = o.force_timeout ? 64u : o.spin_limit;
+        switch (dtype) {
+        case NORM_F32: err = launch_split_coop_f32(rms, c, p, part, sync, need, spin); break;
+        case NORM_BF16: err = launch_split_coop_bf16(rms, c, p, part, sync, need, spin); break;
+        default: err = launch_split_coop_f16(rms, c, p, part, sync, need, spin); break;
+        }
+    } else {
+        // Row batches in stream order; each batch reuses the workspace (its
+        // counters are back at zero when the batch's first kernel ends).
+        float2* rowstat = part + size_t(rows) * size_t(p.chunks);
+        err = hipSuccess;
+        for (int64_t r0 = 0; r0 < M && err == hipSuccess; r0 += rows) {
+            const int64_t mb = std::min(rows, M - r0);
+            NormCall cb = c;
+            cb.x = static_cast<const char*>(c.x) + r0 * N * e;
+            cb.y = static_cast<char*>(c.y) + r0 * N * e;
+            cb.mean = c.mean ? c.mean + r0 : nullptr;
+            cb.rstd = c.rstd ? c.rstd + r0 : nullptr;
+            cb.M = mb;
+            Plan pb = p;
+            pb.work = mb * p.chunks;
+            pb.grid = std::min(p.grid, pb.work);
+            switch (dtype) {
+            case NORM_F32: err = launch_split_f32(rms, cb, pb, part, w.sync, rowstat); break;
+            case NORM_BF16: err = launch_split_bf16(rms, cb, pb, part, w.sync, rowstat); break;
+            default: err = launch_split_f16(rms, cb, pb, part, w.sync, rowstat); break;
+            }
+        }
     }
-    const hipError_t ferr = hipFreeAsync(ws, c.stream);
-    return (err == hipSuccess && ferr == hipSuccess) ? NORM_OK : NORM_ERR_HIP;
+    return hip_ok(err, coop ? "single-pass split kernel launch" : "two-kernel split launch") ? NORM_OK
+                                                                                               : NORM_ERR_HIP;
 }
 
 }  // namespace
@@ -226,6 +391,8 @@ const char* norm_status_str(int status) {
     return "unknown status";
 }
 
+const char* norm_last_error(void) { return g_last_error; }
+
 int norm_describe(int op, int64_t M, int64_t N, int dtype, int aligned, char* buf, int buflen) {
     if (op != OP_LN && op != OP_RMS) return NORM_ERR_BAD_ARG;
     if (dtype != NORM_F32 && dtype != NORM_F16 && dtype != NORM_BF16) return NORM_ERR_BAD_DTYPE;
@@ -241,9 +408,13 @@ int norm_describe(int op, int64_t M, int64_t N, int dtype, int aligned, char* bu
                       p.team, p.vpl, p.epv, p.wg, p.rows_per_wg, (long long)p.grid, (long long)p.work);
     else
         std::snprintf(buf, (size_t)buflen,
-                      "path=split wg=%d vpl=%d epv=%d chunks=%d grid=%lld work=%lld workspace=%lld",
-                      p.wg, p.vpl, p.epv, p.chunks, (long long)p.grid, (long long)p.work,
-                      (long long)(M * p.chunks * 8));
+                      "path=split mode=%s wg=%d vpl=%d epv=%d chunks=%d teams=%d batch_rows=%lld grid=%lld "
+                      "work=%lld workspace=%lld",
+                      p.split_mode == SPLIT_COOP ? "coop" : "two", p.wg, p.vpl, p.epv, p.chunks,
+                      p.split_mode == SPLIT_COOP ? p.teams : 0, (long long)p.batch_rows, (long long)p.grid,
+                      (long long)p.work,
+                      (long long)(p.batch_rows * p.chunks * 8 + p.batch_rows * kSyncStride * 4 +
+                                  (p.split_mode == SPLIT_COOP ? 0 : p.batch_rows * 8)));
     return NORM_OK;
 }
 

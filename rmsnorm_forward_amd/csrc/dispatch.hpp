@@ -21,6 +21,7 @@ struct NormCall {
 };
 
 enum { PATH_ROWS = 0, PATH_SPLIT = 1 };
+enum { SPLIT_TWO = 0, SPLIT_COOP = 1 };
 
 struct Plan {
     int path;       // PATH_ROWS or PATH_SPLIT
@@ -32,6 +33,9 @@ struct Plan {
     int64_t grid;   // workgroups launched (grid-stride loops cover the rest)
     int chunks;     // split: chunks per row
     int64_t work;   // rows: row groups; split: M * chunks
+    int split_mode; // SPLIT_TWO or SPLIT_COOP
+    int teams;      // coop: rows processed concurrently (grid = teams * chunks)
+    int64_t batch_rows;  // two-kernel split: rows per pair of launches
 };
 
 // Tiles instantiated for the row kernel.
@@ -39,15 +43,57 @@ constexpr int kTeams[] = {4, 8, 16, 32, 64, 128, 256, 512, 1024};
 constexpr int kVpls[] = {1, 2, 4, 8, 16};
 constexpr int kMaxTeam = 1024;
 constexpr int kMaxVpl = 16;
-// Split-row chunk geometry.
-constexpr int kSplitWG = 256;
-constexpr int kSplitVPL = 4;
+// Split-row chunk geometry: two-kernel form, and the single pass (fewer,
+// larger chunks: fewer arrivals per row at its barrier).
+#ifndef MI355_SPLIT_WG
+#define MI355_SPLIT_WG 256
+#endif
+#ifndef MI355_SPLIT_VPL
+#define MI355_SPLIT_VPL 4
+#endif
+constexpr int kSplitWG = MI355_SPLIT_WG;
+constexpr int kSplitVPL = MI355_SPLIT_VPL;
+#ifndef MI355_COOP_WG
+#define MI355_COOP_WG 1024
+#endif
+#ifndef MI355_COOP_VPL
+#define MI355_COOP_VPL 8
+#endif
+constexpr int kCoopWG = MI355_COOP_WG;
+constexpr int kCoopVPL = MI355_COOP_VPL;
+// Two-kernel split: rows per pair of launches are chosen so that one batch of
+// x (about this many bytes) mostly stays in the 256 MB Infinity Cache between the
+// statistics pass and the normalising pass.
+#ifndef MI355_SPLIT_BATCH_BYTES
+#define MI355_SPLIT_BATCH_BYTES (int64_t(256) << 20)
+#endif
+constexpr int64_t kSplitBatchBytes = MI355_SPLIT_BATCH_BYTES;
+// barrier counters of one row are 64 words (256 bytes) apart
+constexpr int kSyncStride = 64;
 
 hipError_t launch_rows_f32(bool rms, const NormCall& c, const Plan& p);
 hipError_t launch_rows_bf16(bool rms, const NormCall& c, const Plan& p);
 hipError_t launch_rows_f16(bool rms, const NormCall& c, const Plan& p);
-hipError_t launch_split_f32(bool rms, const NormCall& c, const Plan& p, float2* ws);
-hipError_t launch_split_bf16(bool rms, const NormCall& c, const Plan& p, float2* ws);
-hipError_t launch_split_f16(bool rms, const NormCall& c, const Plan& p, float2* ws);
+// two-kernel split: ws M*chunks partials, sync 64*M counters (zero before and
+// after), rowstat M per-row (mean about the shift, rstd)
+hipError_t launch_split_f32(bool rms, const NormCall& c, const Plan& p, float2* ws, unsigned* sync,
+                            float2* rowstat);
+hipError_t launch_split_bf16(bool rms, const NormCall& c, const Plan& p, float2* ws, unsigned* sync,
+                             float2* rowstat);
+hipError_t launch_split_f16(bool rms, const NormCall& c, const Plan& p, float2* ws, unsigned* sync,
+                            float2* rowstat);
+// single-pass split: ws holds M*chunks partials, sync 2*M counters that are
+// zero before the launch and zero again after it; each row waits for `need`
+// arrivals (its chunk count) for at most spin_limit polls
+hipError_t launch_split_coop_f32(bool rms, const NormCall& c, const Plan& p, float2* ws,
+                                 unsigned* sync, unsigned need, unsigned spin_limit);
+hipError_t launch_split_coop_bf16(bool rms, const NormCall& c, const Plan& p, float2* ws,
+                                  unsigned* sync, unsigned need, unsigned spin_limit);
+hipError_t launch_split_coop_f16(bool rms, const NormCall& c, const Plan& p, float2* ws,
+                                 unsigned* sync, unsigned need, unsigned spin_limit);
+// workgroups of the single-pass split kernel that fit on one CU at once
+int coop_blocks_per_cu_f32(bool rms, int epv);
+int coop_blocks_per_cu_bf16(bool rms, int epv);
+int coop_blocks_per_cu_f16(bool rms, int epv);
 
 }  // namespace mi355norm

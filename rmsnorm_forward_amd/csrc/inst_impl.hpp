@@ -66,7 +66,7 @@ hipError_t launch_rows(bool rms, const NormCall& c, const Plan& p) {
 }
 
 template <class T, bool RMS, int EPV>
-hipError_t go_split(const NormCall& c, const Plan& p, float2* ws) {
+hipError_t go_split(const NormCall& c, const Plan& p, float2* ws, unsigned* sync, float2* rowstat) {
     const St<T>* x = static_cast<const St<T>*>(c.x);
     const St<T>* g = static_cast<const St<T>*>(c.gamma);
     const St<T>* b = static_cast<const St<T>*>(c.beta);
@@ -78,24 +78,77 @@ hipError_t go_split(const NormCall& c, const Plan& p, float2* ws) {
     int S = p.chunks;
     float eps = c.eps;
     {
-        void* args[] = {&x, &ws, &M, &N, &S};
+        void* args[] = {&x, &ws, &sync, &rowstat, &mean, &rstd, &M, &N, &S, &eps};
         hipError_t e = hipLaunchKernel(
             reinterpret_cast<const void*>(&norm_split_stats_kernel<T, RMS, kSplitWG, kSplitVPL, EPV>),
             dim3((unsigned)p.grid), dim3(kSplitWG), args, 0, c.stream);
         if (e != hipSuccess) return e;
     }
-    const float2* wsc = ws;
-    void* args[] = {&x, &g, &b, &y, &mean, &rstd, &wsc, &M, &N, &S, &eps};
+    const float2* rs = rowstat;
+    const float2* pp = ws;
+    void* args[] = {&x, &g, &b, &y, &pp, &rs, &mean, &rstd, &M, &N, &S, &eps};
     return hipLaunchKernel(
         reinterpret_cast<const void*>(&norm_split_apply_kernel<T, RMS, kSplitWG, kSplitVPL, EPV>),
         dim3((unsigned)p.grid), dim3(kSplitWG), args, 0, c.stream);
 }
 
+template <class T, bool RMS, int EPV>
+const void* coop_kernel() {
+    return reinterpret_cast<const void*>(&norm_split_coop_kernel<T, RMS, kCoopWG, kCoopVPL, EPV>);
+}
+
 template <class T>
-hipError_t launch_split(bool rms, const NormCall& c, const Plan& p, float2* ws) {
+int coop_blocks_per_cu(bool rms, int epv) {
     constexpr int VEC = 16 / T::bytes;
-    if (p.epv == VEC) return rms ? go_split<T, true, VEC>(c, p, ws) : go_split<T, false, VEC>(c, p, ws);
-    if (p.epv == 1) return rms ? go_split<T, true, 1>(c, p, ws) : go_split<T, false, 1>(c, p, ws);
+    const void* f = nullptr;
+    if (epv == VEC) f = rms ? coop_kernel<T, true, VEC>() : coop_kernel<T, false, VEC>();
+    else if (epv == 1) f = rms ? coop_kernel<T, true, 1>() : coop_kernel<T, false, 1>();
+    if (!f) return 0;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, kCoopWG, 0) != hipSuccess) return 0;
+    return n;
+}
+
+template <class T, bool RMS, int EPV>
+hipError_t go_split_coop(const NormCall& c, const Plan& p, float2* ws, unsigned* sync,
+                         unsigned need, unsigned spin_limit) {
+    const St<T>* x = static_cast<const St<T>*>(c.x);
+    const St<T>* g = static_cast<const St<T>*>(c.gamma);
+    const St<T>* b = static_cast<const St<T>*>(c.beta);
+    St<T>* y = static_cast<St<T>*>(c.y);
+    float* mean = c.mean;
+    float* rstd = c.rstd;
+    int64_t M = c.M;
+    int N = c.N;
+    int S = p.chunks;
+    int teams = p.teams;
+    float eps = c.eps;
+    void* args[] = {&x, &g, &b, &y, &mean, &rstd, &ws, &sync, &M, &N, &S, &teams, &eps, &need, &spin_limit};
+    return hipLaunchCooperativeKernel(coop_kernel<T, RMS, EPV>(), dim3((unsigned)(teams * S)),
+                                      dim3(kCoopWG), args, 0, c.stream);
+}
+
+template <class T>
+hipError_t launch_split_coop(bool rms, const NormCall& c, const Plan& p, float2* ws, unsigned* sync,
+                             unsigned need, unsigned spin_limit) {
+    constexpr int VEC = 16 / T::bytes;
+    if (p.epv == VEC)
+        return rms ? go_split_coop<T, true, VEC>(c, p, ws, sync, need, spin_limit)
+                   : go_split_coop<T, false, VEC>(c, p, ws, sync, need, spin_limit);
+    if (p.epv == 1)
+        return rms ? go_split_coop<T, true, 1>(c, p, ws, sync, need, spin_limit)
+                   : go_split_coop<T, false, 1>(c, p, ws, sync, need, spin_limit);
+    return hipErrorInvalidValue;
+}
+
+template <class T>
+hipError_t launch_split(bool rms, const NormCall& c, const Plan& p, float2* ws, unsigned* sync,
+                        float2* rowstat) {
+    constexpr int VEC = 16 / T::bytes;
+    if (p.epv == VEC)
+        return rms ? go_split<T, true, VEC>(c, p, ws, sync, rowstat) : go_split<T, false, VEC>(c, p, ws, sync, rowstat);
+    if (p.epv == 1)
+        return rms ? go_split<T, true, 1>(c, p, ws, sync, rowstat) : go_split<T, false, 1>(c, p, ws, sync, rowstat);
     return hipErrorInvalidValue;
 }
 

@@ -1,21 +1,30 @@
 // split.hpp -- rows too long for one workgroup's registers.  A row is cut
 // into chunks of CV = WG*VPL vectors; a chunk is one workgroup's work item.
 //
-//   norm_split_stats_kernel : per chunk, LayerNorm (n_c, mu_c, M2_c) relative
-//                             to the row shift K = x[row, 0] (two passes over
-//                             the chunk in registers), or RMSNorm sum of
-//                             squares; written to a [M, S] float2 workspace.
-//   norm_split_apply_kernel : per chunk, merge the row's S partials in chunk
-//                             order with Chan's formula (every workgroup of a
-//                             row runs the identical merge, so all chunks of a
-//                             row use bitwise-identical mean and rstd), then
-//                             normalise the chunk and store it.
+// Per chunk, LayerNorm computes (mean about K, M2) over its n_c elements by
+// two passes over the chunk in registers, K = x[row, 0] being the row shift
+// every chunk of the row shares; RMSNorm computes its sum of squares.  A row's
+// partials are merged in chunk order with Chan's formula; every workgroup of
+// the row runs the identical merge, so all chunks of a row normalise with
+// bitwise-identical mean and rstd.  Merging (n, mean, M2) partials is what
+// "T3 讲解" part ② recommends once a row has to be read in segments, with the
+// associative merge of "CUDA 算子工程" ch. 7 section 7.4.1.
 //
-// Merging (n, mean, M2) partials is what "T3 讲解" part ② recommends once a
-// row has to be read in segments, with the associative merge of
-// "CUDA 算子工程" ch. 7 section 7.4.1.  This two-kernel form reads x twice;
-// rows are independent, so the second read of a chunk is issued soon after
-// the first for small M and often hits the on-die caches.
+// Two schedules:
+//   norm_split_coop_kernel   single pass, x read once: each workgroup keeps
+//                            its chunk in VGPRs, publishes its partial, waits
+//                            at a per-row team barrier (all S workgroups of a
+//                            team are co-resident: cooperative launch), merges
+//                            and normalises from registers.  Teams walk the
+//                            rows with a stride of the team count.  The
+//                            barrier's counters return to zero by the end of
+//                            every launch, so a kept workspace needs no reset.
+//   norm_split_stats_kernel  two kernels: partials (x read through the
+//   + norm_split_apply_kernel  caches), then a second kernel that merges the
+//                            row's partials, re-reads x and stores y.  When
+//                            a batch of rows fits in the 256 MB Infinity
+//                            Cache the re-read is served on-die, so HBM
+//                            sees x about once.
 #pragma once
 
 #include "prims.hpp"
@@ -39,47 +48,51 @@ __device__ __forceinline__ float wg_sum(float v, float* slots) {
     return v;
 }
 
-template <class T, bool RMS, int WG, int VPL, int EPV>
-__global__ __launch_bounds__(WG)
-void norm_split_stats_kernel(const typename T::storage* __restrict__ x,
-                             float2* __restrict__ ws,
-                             int64_t M, int N, int S)
-{
+template <class T, int WG, int VPL, int EPV>
+struct Chunk {
     using V = Vec<T, EPV>;
-    constexpr int CV = WG * VPL;
-    __shared__ float red[2][WG / 64];
-    const int tid = threadIdx.x;
-    const int NV = N / EPV;
-    const int64_t items = M * (int64_t)S;
+    static constexpr int CV = WG * VPL;      // vectors per chunk
+    V xv[VPL];
+    bool ok[VPL];
+    int v0;                                  // first vector of the chunk
 
-    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-        const int64_t row = it / S;
-        const int c = (int)(it - row * S);
-        const typename T::storage* xr = x + row * (int64_t)N;
-        const int v0 = c * CV;
-        V xv[VPL];
-        bool ok[VPL];
+    // xr: the row (wavefront-uniform); lane offsets are 32-bit (N < 2^24).
+    // STREAM: nontemporal (x's last read); otherwise cached, so that a second
+    // read soon after can be served by the on-die caches.
+    template <bool STREAM = true>
+    __device__ __forceinline__ void load(const typename T::storage* xr, int c, int NV) {
+        v0 = c * CV;
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
-            const int v = v0 + j * WG + tid;
-            ok[j] = v < NV;
-            if (ok[j]) xv[j].load_stream(xr + (int64_t)v * EPV);
-            else xv[j].zero();
+            const unsigned v = (unsigned)(v0 + j * WG) + threadIdx.x;
+            ok[j] = (int)v < NV;
+            if (ok[j]) {
+                if constexpr (STREAM) xv[j].load_stream(xr + v * EPV);
+                else xv[j].load(xr + v * EPV);
+            } else {
+                xv[j].zero();
+            }
         }
-        float2 out;
+    }
+
+    // keep widened copies from living across phases: re-widen instead
+    __device__ __forceinline__ void opaque() {
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) xv[j].opaque();
+    }
+
+    // LayerNorm: (mean of x - K, M2 about that mean) over the chunk's valid
+    // elements; RMSNorm: (sum of squares, 0).  Uses both LDS slot sets.
+    template <bool RMS>
+    __device__ __forceinline__ float2 partial(float K, int NV, float (*red)[WG / 64]) {
         if constexpr (RMS) {
             float q = 0.0f;
 #pragma unroll
             for (int j = 0; j < VPL; ++j)
 #pragma unroll
-                for (int k = 0; k < EPV; ++k) {
-                    const float v = xv[j].get(k);
-                    q = __builtin_fmaf(v, v, q);
-                }
-            q = wg_sum<WG>(q, red[0]);
-            out = make_float2(q, 0.0f);
+                for (int k = 0; k < EPV; ++k) q = __builtin_fmaf(xv[j].get(k), xv[j].get(k), q);
+            return make_float2(wg_sum<WG>(q, red[0]), 0.0f);
         } else {
-            const float K = T::widen(xr[0]);
             const int nvec = min(CV, NV - v0);
             const float nc = (float)nvec * (float)EPV;
             float s = 0.0f;
@@ -89,6 +102,7 @@ void norm_split_stats_kernel(const typename T::storage* __restrict__ x,
                 for (int k = 0; k < EPV; ++k) s += ok[j] ? xv[j].get(k) - K : 0.0f;
             s = wg_sum<WG>(s, red[0]);
             const float mc = s / nc;
+            opaque();
             float q = 0.0f;
 #pragma unroll
             for (int j = 0; j < VPL; ++j)
@@ -97,25 +111,72 @@ void norm_split_stats_kernel(const typename T::storage* __restrict__ x,
                     const float e = ok[j] ? (xv[j].get(k) - K) - mc : 0.0f;
                     q = __builtin_fmaf(e, e, q);
                 }
-            q = wg_sum<WG>(q, red[1]);
-            out = make_float2(mc, q);
+            return make_float2(mc, wg_sum<WG>(q, red[1]));
         }
-        if (tid == 0) ws[it] = out;
-        // the LDS slots are rewritten by the next item
-        __syncthreads();
     }
-}
+
+    // normalise the chunk from registers, apply the affine, store; gamma /
+    // beta loads run at most four vectors ahead of their use
+    template <bool RMS>
+    __device__ __forceinline__ void apply(typename T::storage* yr, const typename T::storage* gamma,
+                                          const typename T::storage* beta, float K, float mu,
+                                          float rs) {
+        const bool has_g = gamma != nullptr;
+        const bool has_b = beta != nullptr;
+        opaque();
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+            if (j % 4 == 0 && j > 0) __builtin_amdgcn_sched_barrier(0);
+            if (!ok[j]) continue;
+            const unsigned off = ((unsigned)(v0 + j * WG) + threadIdx.x) * EPV;
+            V gv, bv;
+            if (has_g) gv.load(gamma + off);
+            if (!RMS && has_b) bv.load(beta + off);
+            float o[EPV];
+#pragma unroll
+            for (int k = 0; k < EPV; ++k) {
+                const float g = has_g ? gv.get(k) : 1.0f;
+                if constexpr (RMS) o[k] = (xv[j].get(k) * rs) * g;
+                else o[k] = __builtin_fmaf(((xv[j].get(k) - K) - mu) * rs, g, has_b ? bv.get(k) : 0.0f);
+            }
+            V::store(yr + off, o);
+        }
+    }
+};
 
 // Merge a row's S partials (S arbitrary) inside one wavefront; the result is
 // wave-uniform and identical in every wavefront that runs it on the same data.
 // Lane l folds partials l, l+64, l+128, ... in order; the 64 lane states are
 // then merged by a butterfly whose every step puts the lower lane's state
 // first, so partners compute bitwise-identical results.
+// A partial as one 64-bit atomic access at agent scope: coherent across the
+// XCDs' L2 caches without any cache write-back or invalidation.
+__device__ __forceinline__ void store_partial_coherent(float2* p, float2 v) {
+    const unsigned long long bits =
+        ((unsigned long long)__float_as_uint(v.y) << 32) | (unsigned long long)__float_as_uint(v.x);
+    __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), bits, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float2 load_partial_coherent(const float2* p) {
+    const unsigned long long bits = __hip_atomic_load(
+        reinterpret_cast<unsigned long long*>(const_cast<float2*>(p)), __ATOMIC_RELAXED,
+        __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__uint_as_float((unsigned)bits), __uint_as_float((unsigned)(bits >> 32)));
+}
+
+template <bool COHERENT>
+__device__ __forceinline__ float2 read_partial(const float2* p) {
+    if constexpr (COHERENT) return load_partial_coherent(p);
+    else return *p;
+}
+
+template <bool COHERENT = false>
 __device__ __forceinline__ Welford merge_row_partials(const float2* p, int S, int CE, int N) {
     const int l = lane_id();
     Welford a = {0.0f, 0.0f, 0.0f};
     for (int c = l; c < S; c += 64) {
-        const float2 v = p[c];
+        const float2 v = read_partial<COHERENT>(p + c);
         const int n = min(CE, N - c * CE);
         a = chan_merge(a, Welford{(float)n, v.x, v.y});
     }
@@ -137,74 +198,215 @@ __device__ __forceinline__ Welford merge_row_partials(const float2* p, int S, in
     return chan_merge(chan_merge(r[0], r[1]), chan_merge(r[2], r[3]));
 }
 
+// Row statistics from its S partials: (mean about K, rstd).
+template <bool RMS, bool COHERENT = false>
+__device__ __forceinline__ float2 row_stats(const float2* pr, int S, int CE, int N, float eps) {
+    const float inv_n = 1.0f / (float)N;
+    if constexpr (RMS) {
+        float q = 0.0f;
+        for (int cc = lane_id(); cc < S; cc += 64) q += read_partial<COHERENT>(pr + cc).x;
+        q = team_sum<64>(q);
+        return make_float2(0.0f, rsqrt_hw(__builtin_fmaf(q, inv_n, eps)));
+    } else {
+        const Welford w = merge_row_partials<COHERENT>(pr, S, CE, N);
+        return make_float2(w.mean, rsqrt_hw(__builtin_fmaf(w.m2, inv_n, eps)));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// single pass, cooperative
+// ---------------------------------------------------------------------------
+
+// Publication of the partials:
+//   0  plain stores, release add / acquire fence at agent scope
+//      (write-back and invalidation of the L2 by every workgroup, every row)
+//   1  as 0, the departure count relaxed
+//   2  partials as coherent 64-bit atomic stores and loads; the store is
+//      complete before the arrival count is incremented; no L2 maintenance
+#ifndef MI355_COOP_SYNC
+#define MI355_COOP_SYNC 2
+#endif
+
+
+template <class T, bool RMS, int WG, int VPL, int EPV>
+__global__ __launch_bounds__(WG)
+void norm_split_coop_kernel(const typename T::storage* __restrict__ x,
+                            const typename T::storage* __restrict__ gamma,
+                            const typename T::storage* __restrict__ beta,
+                            typename T::storage* __restrict__ y,
+                            float* __restrict__ mean_out,
+                            float* __restrict__ rstd_out,
+                            float2* __restrict__ part,      // [M, S] partials
+                            unsigned* __restrict__ sync,    // row r: [64r], [64r+32]; zero at
+                                                            // launch and again at exit
+                            int64_t M, int N, int S, int teams, float eps,
+                            unsigned need, unsigned spin_limit)
+{
+    using C = Chunk<T, WG, VPL, EPV>;
+    __shared__ float red[2][WG / 64];
+    __shared__ int late;
+    const int tid = threadIdx.x;
+    const int NV = N / EPV;
+    const int team = blockIdx.x / S;          // grid is exactly teams * S
+    const int c = blockIdx.x - team * S;
+
+    for (int64_t row = team; row < M; row += teams) {
+        const typename T::storage* xr = x + row * (int64_t)N;
+        C ch;
+        ch.load(xr, c, NV);
+        const float K = RMS ? 0.0f : T::widen(xr[0]);
+        const float2 p = ch.template partial<RMS>(K, NV, red);
+        // one 256-byte line per row: rows in flight never share a line
+        unsigned* arrived = sync + row * 64;
+        unsigned* departed = arrived + 32;
+        constexpr bool COH = MI355_COOP_SYNC == 2;
+        if (tid == 0) {
+            // publish the partial before the arrival count, then wait for the
+            // row's other S-1 workgroups.  Polling uses relaxed loads.  The
+            // wait is bounded so a broken co-residency assumption cannot hang.
+            if constexpr (COH) {
+                store_partial_coherent(part + row * S + c, p);
+                __builtin_amdgcn_s_waitcnt(0);     // the store has completed
+                __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                part[row * S + c] = p;
+                __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            unsigned spins = 0;
+            int timed_out = 0;
+            // need = S (a host test hook can ask for S + 1, which never comes)
+            while (__hip_atomic_load(arrived, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+                if (++spins > spin_limit) {
+                    timed_out = 1;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(8);
+            }
+            late = timed_out;
+        }
+        __syncthreads();
+        if constexpr (!COH) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        float2 st = row_stats<RMS, COH>(part + row * S, S, C::CV * EPV, N, eps);
+        if (late) st = make_float2(__builtin_nanf(""), __builtin_nanf(""));   // visible failure
+        if (tid == 0) {
+            // every workgroup has passed the wait once all S have departed:
+            // the last one out returns both counters to zero for the next call
+            if (__hip_atomic_fetch_add(departed, 1u,
+                                       MI355_COOP_SYNC == 0 ? __ATOMIC_ACQ_REL : __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT) == (unsigned)S - 1) {
+                __hip_atomic_store(arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(departed, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        if (c == 0 && tid == 0) {
+            if (!RMS && mean_out) mean_out[row] = K + st.x;
+            if (rstd_out) rstd_out[row] = st.y;
+        }
+        ch.template apply<RMS>(y + row * (int64_t)N, gamma, beta, K, st.x, st.y);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// two kernels
+// ---------------------------------------------------------------------------
+
+// Where the two-kernel form merges a row's partials:
+//   0  in kernel 1, by the last workgroup of the row to publish (an atomic
+//      arrival count), once per row; kernel 2 reads the finished statistics
+//   1  in kernel 2, by every wavefront, after it has issued its loads of x
+//      (the merge's latency hides behind them); kernel 1 only stores partials
+#ifndef MI355_SPLIT_MERGE
+#define MI355_SPLIT_MERGE 1
+#endif
+
+// Kernel 1: per-chunk partials, x read through the caches.
+template <class T, bool RMS, int WG, int VPL, int EPV>
+__global__ __launch_bounds__(WG)
+void norm_split_stats_kernel(const typename T::storage* __restrict__ x,
+                             float2* __restrict__ part,      // [M, S] partials
+                             unsigned* __restrict__ sync,    // row r: [64r]; zero at launch and exit
+                             float2* __restrict__ rowstat,   // [M] (mean about K, rstd)
+                             float* __restrict__ mean_out,
+                             float* __restrict__ rstd_out,
+                             int64_t M, int N, int S, float eps)
+{
+    using C = Chunk<T, WG, VPL, EPV>;
+    __shared__ float red[2][WG / 64];
+    __shared__ int last;
+    const int NV = N / EPV;
+    const int64_t items = M * (int64_t)S;
+    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+        const int64_t row = it / S;
+        const int c = (int)(it - row * S);
+        const typename T::storage* xr = x + row * (int64_t)N;
+        C ch;
+        ch.template load<false>(xr, c, NV);
+        const float K = RMS ? 0.0f : T::widen(xr[0]);
+        const float2 p = ch.template partial<RMS>(K, NV, red);
+#if MI355_SPLIT_MERGE == 0
+        unsigned* arrived = sync + row * 64;
+        if (threadIdx.x == 0) {
+            // the partial is complete at the coherence point before the count
+            store_partial_coherent(part + row * S + c, p);
+            __builtin_amdgcn_s_waitcnt(0);
+            last = __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   (unsigned)S - 1;
+        }
+        __syncthreads();
+        if (last && threadIdx.x < 64) {     // one wavefront finishes the row
+            const float2 st = row_stats<RMS, true>(part + row * S, S, C::CV * EPV, N, eps);
+            if (threadIdx.x == 0) {
+                rowstat[row] = st;
+                if (!RMS && mean_out) mean_out[row] = K + st.x;
+                if (rstd_out) rstd_out[row] = st.y;
+                __hip_atomic_store(arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+#else
+        (void)sync; (void)rowstat; (void)mean_out; (void)rstd_out; (void)eps; (void)last;
+        if (threadIdx.x == 0) part[row * S + c] = p;
+#endif
+        __syncthreads();          // LDS slots are rewritten by the next item
+    }
+}
+
+// Kernel 2: normalise each chunk with its row's statistics (x's last read).
 template <class T, bool RMS, int WG, int VPL, int EPV>
 __global__ __launch_bounds__(WG)
 void norm_split_apply_kernel(const typename T::storage* __restrict__ x,
                              const typename T::storage* __restrict__ gamma,
                              const typename T::storage* __restrict__ beta,
                              typename T::storage* __restrict__ y,
+                             const float2* __restrict__ part,
+                             const float2* __restrict__ rowstat,
                              float* __restrict__ mean_out,
                              float* __restrict__ rstd_out,
-                             const float2* __restrict__ ws,
                              int64_t M, int N, int S, float eps)
 {
-    using V = Vec<T, EPV>;
-    constexpr int CV = WG * VPL;
-    const int tid = threadIdx.x;
+    using C = Chunk<T, WG, VPL, EPV>;
     const int NV = N / EPV;
-    const float fN = (float)N;
     const int64_t items = M * (int64_t)S;
-    const bool has_g = gamma != nullptr;
-    const bool has_b = beta != nullptr;
-
     for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
         const int64_t row = it / S;
         const int c = (int)(it - row * S);
         const typename T::storage* xr = x + row * (int64_t)N;
-        typename T::storage* yr = y + row * (int64_t)N;
-        const int v0 = c * CV;
-        V xv[VPL];
-        bool ok[VPL];
-#pragma unroll
-        for (int j = 0; j < VPL; ++j) {
-            const int v = v0 + j * WG + tid;
-            ok[j] = v < NV;
-            if (ok[j]) xv[j].load_stream(xr + (int64_t)v * EPV);
-            else xv[j].zero();
+        C ch;
+        ch.load(xr, c, NV);
+        const float K = RMS ? 0.0f : T::widen(xr[0]);
+#if MI355_SPLIT_MERGE == 0
+        (void)part; (void)mean_out; (void)rstd_out; (void)eps;
+        const float2 st = rowstat[row];
+#else
+        (void)rowstat;
+        // every wavefront merges the row's partials in chunk order: the same
+        // bits in every wavefront of every workgroup of the row
+        const float2 st = row_stats<RMS>(part + row * S, S, C::CV * EPV, N, eps);
+        if (c == 0 && threadIdx.x == 0) {
+            if (!RMS && mean_out) mean_out[row] = K + st.x;
+            if (rstd_out) rstd_out[row] = st.y;
         }
-        const float2* pr = ws + row * (int64_t)S;
-        float rs, mu = 0.0f, K = 0.0f;
-        if constexpr (RMS) {
-            float q = 0.0f;
-            for (int cc = lane_id(); cc < S; cc += 64) q += pr[cc].x;
-            q = team_sum<64>(q);
-            rs = rsqrt_hw(q / fN + eps);
-        } else {
-            K = T::widen(xr[0]);
-            const Welford w = merge_row_partials(pr, S, CV * EPV, N);
-            mu = w.mean;
-            rs = rsqrt_hw(w.m2 / fN + eps);
-        }
-        if (c == 0 && tid == 0) {
-            if (!RMS && mean_out) mean_out[row] = K + mu;
-            if (rstd_out) rstd_out[row] = rs;
-        }
-#pragma unroll
-        for (int j = 0; j < VPL; ++j) {
-            if (!ok[j]) continue;
-            const int64_t off = (int64_t)(v0 + j * WG + tid) * EPV;
-            V gv, bv;
-            if (has_g) gv.load(gamma + off);
-            if (!RMS && has_b) bv.load(beta + off);
-            float o[EPV];
-#pragma unroll
-            for (int k = 0; k < EPV; ++k) {
-                const float g = has_g ? gv.get(k) : 1.0f;
-                if constexpr (RMS) o[k] = (xv[j].get(k) * rs) * g;
-                else o[k] = __builtin_fmaf(((xv[j].get(k) - K) - mu) * rs, g, has_b ? bv.get(k) : 0.0f);
-            }
-            V::store(yr + off, o);
-        }
+#endif
+        ch.template apply<RMS>(y + row * (int64_t)N, gamma, beta, K, st.x, st.y);
     }
 }
 

@@ -49,7 +49,7 @@ def run(op: str, dtype: str, x: np.ndarray, gamma, beta, eps: float, *, stats: b
     fn = rn.ln_fwd if op == "ln" else rn.rms_fwd
     stream = torch.cuda.current_stream().cuda_stream
     st = fn(p(xt), p(gt), p(bt), p(yt), p(mean), p(rstd), M, N, eps, CODE[dtype], stream)
-    assert st == rn.NORM_OK, f"{rn.STATUS.get(st)}: {rn.norm_status_str(st)}"
+    assert st == rn.NORM_OK, f"{rn.STATUS.get(st)}: {rn.norm_status_str(st)} [{rn.norm_last_error()}]"
     torch.cuda.synchronize()
     y = to_host(yt, dtype).reshape(M, N)
     m = mean.cpu().numpy() if mean is not None else None

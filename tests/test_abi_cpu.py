@@ -26,7 +26,7 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["ln_fwd", "norm_describe", "norm_status_str", "rms_fwd"]
+    assert declared_functions() == ["ln_fwd", "norm_describe", "norm_last_error", "norm_status_str", "rms_fwd"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -38,11 +38,33 @@ def test_library_exports_every_declared_symbol():
         assert re.search(rf"\bT {name}$", out, flags=re.M), name
 
 
+def test_one_hip_runtime_in_the_process():
+    # the library must bind to the HIP runtime torch loaded, not map a second
+    import subprocess
+    import sys
+    code = ("import rmsnorm_forward_amd\n"
+            "m = open('/proc/self/maps').read()\n"
+            "print(len({l.split()[-1] for l in m.splitlines() if 'libamdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True,
+                         cwd=os.path.dirname(os.path.dirname(rn.LIB_PATH)))
+    assert out.stdout.strip() == "1"
+
+
 def test_status_strings():
     for code in range(8):
         s = rn.norm_status_str(code)
         assert s and s != "unknown status"
     assert rn.norm_status_str(99) == "unknown status"
+
+
+def test_last_error_starts_empty():
+    # the record is per thread: a new thread has seen no failure
+    import threading
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(rn.norm_last_error()))
+    t.start()
+    t.join()
+    assert seen == [""]
 
 
 # fake, never dereferenced device addresses: validation only does arithmetic
@@ -103,7 +125,8 @@ def parse(desc):
     ("rms", 65536, 2048, "f32", dict(path="rows", team="256", vpl="2", epv="4")),
     ("rms", 65536, 2048, "bf16", dict(path="rows", team="64", vpl="4", epv="8")),
     ("ln", 4096, 5120, "bf16", dict(path="rows", team="256", vpl="4", epv="8")),
-    ("ln", 64, 1 << 20, "bf16", dict(path="split", chunks="128", epv="8")),
+    ("ln", 64, 1 << 20, "bf16", dict(path="split", mode="two", chunks="128", epv="8", batch_rows="64",
+                                      grid="8192")),
 ])
 def test_plans_of_the_measured_configurations(op, M, N, dtype, want):
     d = parse(rn.norm_describe(op, M, N, dtype))
@@ -144,9 +167,29 @@ def test_every_row_fits_its_tile():
                     assert int(d["chunks"]) * int(d["wg"]) * int(d["vpl"]) >= nv
 
 
+def test_split_rows_run_in_batches_of_about_256_mib():
+    d = parse(rn.norm_describe("ln", 4096, 1 << 18, "bf16"))      # 512 KiB rows: 512 per batch
+    assert (d["mode"], d["batch_rows"], d["chunks"]) == ("two", "512", "32")
+    assert int(d["grid"]) == 512 * 32
+    d = parse(rn.norm_describe("rms", 5, 1 << 24, "f32"))          # 64 MiB rows: 4 per batch
+    assert d["batch_rows"] == "4" and int(d["chunks"]) * 4096 == 1 << 24
+    d = parse(rn.norm_describe("ln", 1, 200000, "f16", aligned=False))
+    assert (d["batch_rows"], d["epv"], d["chunks"]) == ("1", "1", str(-(-200000 // 1024)))
+
+
+def test_split_batch_override(monkeypatch):
+    monkeypatch.setenv("MI355NORM_SPLIT_BATCH", str(3 * 140000 * 2))
+    d = parse(rn.norm_describe("ln", 7, 140000, "bf16"))
+    assert d["batch_rows"] == "3" and int(d["work"]) == 3 * int(d["chunks"])
+    monkeypatch.setenv("MI355NORM_SPLIT_BATCH", "1")               # below one row: one row per batch
+    assert parse(rn.norm_describe("ln", 7, 140000, "bf16"))["batch_rows"] == "1"
+
+
 def test_overrides(monkeypatch):
     monkeypatch.setenv("MI355NORM_PATH", "split")
     assert parse(rn.norm_describe("ln", 64, 8192, "bf16"))["path"] == "split"
+    monkeypatch.setenv("MI355NORM_PATH", "split2")
+    assert parse(rn.norm_describe("ln", 64, 8192, "bf16"))["mode"] == "two"
     monkeypatch.setenv("MI355NORM_PATH", "rows")
     with pytest.raises(RuntimeError):
         rn.norm_describe("ln", 64, 1 << 20, "bf16")     # does not fit one workgroup

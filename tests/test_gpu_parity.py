@@ -110,13 +110,14 @@ def test_edge_shapes(op, dtype, N):
     compare(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, y, mean, rstd, what=f"N={N}")
 
 
+@pytest.mark.parametrize("mode", ["split2", "splitcoop"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("op", ["ln", "rms"])
 @pytest.mark.parametrize("N", [10, 1000, 8192, 65544, 300000])
-def test_forced_split_path(monkeypatch, op, dtype, N):
-    monkeypatch.setenv("MI355NORM_PATH", "split")
+def test_forced_split_path(monkeypatch, op, dtype, N, mode):
+    monkeypatch.setenv("MI355NORM_PATH", mode)
     M = 9
-    print(f"[gpu] split {op} {dtype} M={M} N={N}", flush=True)
+    print(f"[gpu] {mode} {op} {dtype} M={M} N={N}", flush=True)
     inp = inputs(op, dtype, M, N, seed=N + 1)
     y, mean, rstd = run(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5)
     compare(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, y, mean, rstd, what=f"split N={N}")
@@ -222,10 +223,10 @@ def test_stress_rows_small_bf16():
     compare("ln", "bf16", inp["x"], inp["gamma"], inp["beta"], 1e-5, y, mean, rstd, what="bf16 stress")
 
 
-@pytest.mark.parametrize("path", ["auto", "split"])
+@pytest.mark.parametrize("path", ["auto", "split2", "splitcoop"])
 def test_bitwise_deterministic(monkeypatch, path):
-    if path == "split":
-        monkeypatch.setenv("MI355NORM_PATH", "split")
+    if path != "auto":
+        monkeypatch.setenv("MI355NORM_PATH", path)
     inp = inputs("ln", "bf16", 300, 8192, seed=31)
     a = run("ln", "bf16", inp["x"], inp["gamma"], inp["beta"], 1e-5)
     b = run("ln", "bf16", inp["x"], inp["gamma"], inp["beta"], 1e-5)
@@ -254,6 +255,69 @@ def test_split_statistics_shared_by_all_chunks():
         for c in range(1, full):
             assert np.array_equal(y[r, :C], y[r, c * C:(c + 1) * C]), (r, c)
     compare("ln", "bf16", x, g, b, 1e-5, y, mean, rstd, what="periodic split")
+
+
+def test_two_kernel_split_is_the_default_and_agrees_with_the_single_pass(monkeypatch):
+    """The long-row configuration runs the two-kernel split by default.  It
+    and the single pass (different chunk sizes, so different partials) both
+    meet the oracle's bar, and their statistics agree to fp32 rounding."""
+    import rmsnorm_forward_amd as rn
+    d = dict(kv.split("=") for kv in rn.norm_describe("ln", 64, 1 << 20, "bf16").split())
+    assert d["path"] == "split" and d["mode"] == "two", d
+    inp = inputs("ln", "bf16", 40, 1 << 18, seed=61)
+    monkeypatch.setenv("MI355NORM_PATH", "splitcoop")
+    a = run("ln", "bf16", inp["x"], inp["gamma"], inp["beta"], 1e-5)
+    monkeypatch.delenv("MI355NORM_PATH")
+    b = run("ln", "bf16", inp["x"], inp["gamma"], inp["beta"], 1e-5)
+    compare("ln", "bf16", inp["x"], inp["gamma"], inp["beta"], 1e-5, *a, what="single pass")
+    compare("ln", "bf16", inp["x"], inp["gamma"], inp["beta"], 1e-5, *b, what="two-kernel")
+    assert np.max(np.abs(a[2] / b[2] - 1)) < 1e-5 and np.max(np.abs(a[1] - b[1])) < 1e-4
+
+
+@pytest.mark.parametrize("dtype,N,offset", [("bf16", 140000, 0), ("f32", 70000, 0), ("f16", 20000, 1)])
+@pytest.mark.parametrize("op", ["ln", "rms"])
+def test_split_row_batches(monkeypatch, op, dtype, N, offset):
+    """Rows split across workgroups run in batches (here 3 rows, so batches of
+    3, 3 and 1): every batch's rows, means and rstds land at their own offsets
+    and meet the oracle's bar."""
+    e = 4 if dtype == "f32" else 2
+    monkeypatch.setenv("MI355NORM_SPLIT_BATCH", str(3 * N * e))
+    M = 7
+    print(f"[gpu] split batches {op} {dtype} M={M} N={N} offset={offset}", flush=True)
+    inp = inputs(op, dtype, M, N, seed=N + 3)
+    y, mean, rstd = run(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, offset=offset)
+    compare(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, y, mean, rstd, what=f"batches N={N}")
+
+
+@pytest.mark.parametrize("mode", ["split2", "splitcoop"])
+def test_split_workspace_reused_across_shapes(monkeypatch, mode):
+    """Split calls of different shapes back to back on one stream share the
+    kept workspace; each must see its counters at zero (a regression test:
+    counters placed after shape-dependent partials once started a call
+    non-zero and let a workgroup read partials early)."""
+    monkeypatch.setenv("MI355NORM_PATH", mode)
+    shapes = [(9, 300000), (5, 131080), (3, 1 << 18), (11, 140000), (2, 131080), (7, 65544 * 3)]
+    for i, (M, N) in enumerate(shapes):
+        for op in ("ln", "rms"):
+            inp = inputs(op, "f32", M, N, seed=70 + i)
+            y, mean, rstd = run(op, "f32", inp["x"], inp["gamma"], inp["beta"], 1e-5)
+            compare(op, "f32", inp["x"], inp["gamma"], inp["beta"], 1e-5, y, mean, rstd,
+                    what=f"reuse {mode} {op} M={M} N={N}")
+
+
+def test_single_pass_split_bounded_wait(monkeypatch):
+    """Forced from the host, every row waits for one arrival more than it has
+    chunks, with a short bound: every workgroup stops waiting, the kernel
+    completes, the failure is visible (all outputs NaN), the barrier counters
+    are back at zero, and the next normal call is correct."""
+    inp = inputs("ln", "bf16", 6, 1 << 18, seed=62)
+    monkeypatch.setenv("MI355NORM_PATH", "splitcoop")
+    monkeypatch.setenv("MI355NORM_FORCE_TIMEOUT", "1")
+    y, mean, rstd = run("ln", "bf16", inp["x"], inp["gamma"], inp["beta"], 1e-5)
+    assert np.isnan(oracle.widen(y, "bf16")).all() and np.isnan(rstd).all() and np.isnan(mean).all()
+    monkeypatch.delenv("MI355NORM_FORCE_TIMEOUT")
+    y, mean, rstd = run("ln", "bf16", inp["x"], inp["gamma"], inp["beta"], 1e-5)
+    compare("ln", "bf16", inp["x"], inp["gamma"], inp["beta"], 1e-5, y, mean, rstd, what="after timeout")
 
 
 def test_m_zero_launches_nothing():
