@@ -10,10 +10,13 @@
 //               per reduction across the row's wavefronts; longer rows give
 //               the 1024-lane team up to 16 vectors per lane;
 //   long rows   (beyond 1024 lanes x 16 vectors): split across workgroups
-//               in chunks of 256 lanes x 4 vectors; per-chunk partial
-//               statistics merged in chunk order (Chan).  Single pass when all
-//               chunks of a row fit on the device at once (cooperative launch,
-//               per-row team barrier, x read once); otherwise two kernels.
+//               in chunks of 256 lanes x 8 vectors; per-chunk partial
+//               statistics merged in chunk order (Chan).  Two kernels per
+//               batch of rows holding about 256 MiB of x: partials (x read
+//               through the caches), then merge + normalise (x re-read,
+//               mostly from the Infinity Cache).  A single pass (cooperative
+//               launch, per-row barrier, x read once) is available on request;
+//               it measured slower (LN bf16 64 x 2^20: 92 us vs 72 us).
 // Measured on MI355X in steady state (200 back-to-back launches): bf16
 // 1024-wide RMSNorm 32x4 (2 rows per wavefront) 85.3 us vs 64x2 87.1, 16x8
 // 95.1; bf16 2048-wide 64x4 87.6 vs 32x8 99.4; fp32 2048-wide 256x2 175.0
@@ -24,6 +27,7 @@
 //   MI355NORM_PATH = rows | split | split2 | splitcoop
 //                                       force the path (rows only if it fits;
 //                                       splitcoop only if a row fits resident)
+//   MI355NORM_SPLIT_BATCH = <bytes>     bytes of x per two-kernel split batch
 //   MI355NORM_TILE = <team>x<vpl>       force the row-kernel tile
 //   MI355NORM_GRID = <n>                cap the number of workgroups
 //   MI355NORM_SPIN_LIMIT = <n>          bound of the single-pass split's wait
@@ -218,11 +222,13 @@ int make_plan(int op, int64_t M, int64_t N, int dtype, bool aligned, const Overr
             p->batch_rows = M;
             p->work = M * p->chunks;
         } else {
-            const int64_t cv = int64_t(kSplitWG) * kSplitVPL;
+            const int64_t cv = int64_t(kStatsWG) * kStatsVPL;
+            const int64_t av = int64_t(kApplyWG) * kApplyVPL;
             p->split_mode = SPLIT_TWO;
-            p->wg = kSplitWG;
-            p->vpl = kSplitVPL;
+            p->wg = kStatsWG;
+            p->vpl = kStatsVPL;
             p->chunks = (int)((NV + cv - 1) / cv);
+            p->apply_chunks = (int)((NV + av - 1) / av);
             const int64_t bb = o.batch_bytes > 0 ? o.batch_bytes : kSplitBatchBytes;
             const int64_t rows = bb / (N * e);
             p->batch_rows = std::min<int64_t>(M, rows > 0 ? rows : 1);
@@ -232,6 +238,10 @@ int make_plan(int op, int64_t M, int64_t N, int dtype, bool aligned, const Overr
     int64_t cap = o.grid > 0 ? o.grid : kMaxGrid;
     p->grid = p->work < cap ? p->work : cap;
     if (p->path == PATH_SPLIT && p->split_mode == SPLIT_COOP) p->grid = int64_t(p->teams) * p->chunks;
+    if (p->path == PATH_SPLIT && p->split_mode == SPLIT_TWO) {
+        const int64_t aw = p->batch_rows * p->apply_chunks;
+        p->apply_grid = aw < cap ? aw : cap;
+    }
     return NORM_OK;
 }
 
@@ -245,8 +255,8 @@ int make_plan(int op, int64_t M, int64_t N, int dtype, bool aligned, const Overr
 // Growing (only on a new largest call) waits for the stream, since the old
 // buffer may still be in use, and reallocates both regions.
 struct Workspace {
-    unsigned* sync;   // >= 2 * M counters
-    float2* part;     // >= M * chunks partials
+    unsigned* sync;   // single pass: >= 64 counters per row of a launch
+    float2* part;     // >= rows * chunks partials
 };
 
 // The HIP failure behind the calling thread's most recent NORM_ERR_HIP.
@@ -317,29 +327,27 @@ int run(int op, const void* x, const void* gamma, const void* beta, void* y, flo
         }
         return hip_ok(err, "row kernel launch") ? NORM_OK : NORM_ERR_HIP;
     }
-    // split path: partials, per-row statistics and barrier counters live in
-    // the workspace this (device, stream) keeps
+    // split path: partials and counters live in the workspace this (device,
+    // stream) keeps
     const bool coop = p.split_mode == SPLIT_COOP;
-    const int64_t rows = p.batch_rows;   // rows per launch (pair of launches)
+    const int64_t rows = p.batch_rows;   // rows per launch (two-kernel form: per pair)
+    const Overrides o = read_overrides();
+    const unsigned need = (unsigned)p.chunks + (o.force_timeout ? 1u : 0u);
+    const unsigned spin = o.force_timeout ? 64u : o.spin_limit;
     Workspace w;
-    const size_t part_elems = size_t(rows) * size_t(p.chunks) + (coop ? 0 : size_t(rows));
-    if (!stream_workspace(c.stream, size_t(rows) * kSyncStride, part_elems * sizeof(float2), &w))
+    const size_t sync_words = coop ? size_t(rows) * kSyncStride : 0;
+    if (!stream_workspace(c.stream, sync_words, size_t(rows) * size_t(p.chunks) * sizeof(float2), &w))
         return NORM_ERR_HIP;
     float2* part = w.part;
     if (coop) {
         unsigned* sync = w.sync;
-        const Overrides o = read_overrides();
-        const unsigned need = (unsigned)p.chunks + (o.force_timeout ? 1u : 0u);
-        const unsigned spin = o.force_timeout ? 64u : o.spin_limit;
         switch (dtype) {
         case NORM_F32: err = launch_split_coop_f32(rms, c, p, part, sync, need, spin); break;
         case NORM_BF16: err = launch_split_coop_bf16(rms, c, p, part, sync, need, spin); break;
         default: err = launch_split_coop_f16(rms, c, p, part, sync, need, spin); break;
         }
     } else {
-        // Row batches in stream order; each batch reuses the workspace (its
-        // counters are back at zero when the batch's first kernel ends).
-        float2* rowstat = part + size_t(rows) * size_t(p.chunks);
+        // Row batches in stream order; each batch reuses the partials.
         err = hipSuccess;
         for (int64_t r0 = 0; r0 < M && err == hipSuccess; r0 += rows) {
             const int64_t mb = std::min(rows, M - r0);
@@ -350,12 +358,12 @@ int run(int op, const void* x, const void* gamma, const void* beta, void* y, flo
             cb.rstd = c.rstd ? c.rstd + r0 : nullptr;
             cb.M = mb;
             Plan pb = p;
-            pb.work = mb * p.chunks;
-            pb.grid = std::min(p.grid, pb.work);
+            pb.grid = std::min(p.grid, mb * p.chunks);
+            pb.apply_grid = std::min(p.apply_grid, mb * p.apply_chunks);
             switch (dtype) {
-            case NORM_F32: err = launch_split_f32(rms, cb, pb, part, w.sync, rowstat); break;
-            case NORM_BF16: err = launch_split_bf16(rms, cb, pb, part, w.sync, rowstat); break;
-            default: err = launch_split_f16(rms, cb, pb, part, w.sync, rowstat); break;
+            case NORM_F32: err = launch_split_f32(rms, cb, pb, part); break;
+            case NORM_BF16: err = launch_split_bf16(rms, cb, pb, part); break;
+            default: err = launch_split_f16(rms, cb, pb, part); break;
             }
         }
     }
@@ -408,13 +416,15 @@ int norm_describe(int op, int64_t M, int64_t N, int dtype, int aligned, char* bu
                       p.team, p.vpl, p.epv, p.wg, p.rows_per_wg, (long long)p.grid, (long long)p.work);
     else
         std::snprintf(buf, (size_t)buflen,
-                      "path=split mode=%s wg=%d vpl=%d epv=%d chunks=%d teams=%d batch_rows=%lld grid=%lld "
-                      "work=%lld workspace=%lld",
+                      "path=split mode=%s wg=%d vpl=%d epv=%d chunks=%d apply_wg=%d apply_vpl=%d "
+                      "apply_chunks=%d teams=%d batch_rows=%lld grid=%lld apply_grid=%lld work=%lld "
+                      "workspace=%lld",
                       p.split_mode == SPLIT_COOP ? "coop" : "two", p.wg, p.vpl, p.epv, p.chunks,
-                      p.split_mode == SPLIT_COOP ? p.teams : 0, (long long)p.batch_rows, (long long)p.grid,
-                      (long long)p.work,
-                      (long long)(p.batch_rows * p.chunks * 8 + p.batch_rows * kSyncStride * 4 +
-                                  (p.split_mode == SPLIT_COOP ? 0 : p.batch_rows * 8)));
+                      p.split_mode == SPLIT_TWO ? kApplyWG : 0, p.split_mode == SPLIT_TWO ? kApplyVPL : 0,
+                      p.apply_chunks, p.teams, (long long)p.batch_rows, (long long)p.grid,
+                      (long long)p.apply_grid, (long long)p.work,
+                      (long long)(p.batch_rows * p.chunks * 8 +
+                                  (p.split_mode == SPLIT_COOP ? p.batch_rows * kSyncStride * 4 : 0)));
     return NORM_OK;
 }
 

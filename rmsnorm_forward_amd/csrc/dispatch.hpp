@@ -31,7 +31,9 @@ struct Plan {
     int wg;         // threads per workgroup
     int rows_per_wg;
     int64_t grid;   // workgroups launched (grid-stride loops cover the rest)
-    int chunks;     // split: chunks per row
+    int chunks;     // split: chunks per row (two-kernel form: of the statistics kernel)
+    int apply_chunks;     // two-kernel form: chunks per row of the normalising kernel
+    int64_t apply_grid;   // two-kernel form: workgroups of the normalising kernel
     int64_t work;   // rows: row groups; split: M * chunks
     int split_mode; // SPLIT_TWO or SPLIT_COOP
     int teams;      // coop: rows processed concurrently (grid = teams * chunks)
@@ -43,16 +45,25 @@ constexpr int kTeams[] = {4, 8, 16, 32, 64, 128, 256, 512, 1024};
 constexpr int kVpls[] = {1, 2, 4, 8, 16};
 constexpr int kMaxTeam = 1024;
 constexpr int kMaxVpl = 16;
-// Split-row chunk geometry: two-kernel form, and the single pass (fewer,
-// larger chunks: fewer arrivals per row at its barrier).
-#ifndef MI355_SPLIT_WG
-#define MI355_SPLIT_WG 256
+// Split-row chunk geometry: the two kernels of the two-kernel form (each
+// its own chunk size), and the single pass (fewer, larger chunks: fewer
+// arrivals per row at its barrier).
+#ifndef MI355_STATS_WG
+#define MI355_STATS_WG 256
 #endif
-#ifndef MI355_SPLIT_VPL
-#define MI355_SPLIT_VPL 4
+#ifndef MI355_STATS_VPL
+#define MI355_STATS_VPL 8
 #endif
-constexpr int kSplitWG = MI355_SPLIT_WG;
-constexpr int kSplitVPL = MI355_SPLIT_VPL;
+#ifndef MI355_APPLY_WG
+#define MI355_APPLY_WG 256
+#endif
+#ifndef MI355_APPLY_VPL
+#define MI355_APPLY_VPL 8
+#endif
+constexpr int kStatsWG = MI355_STATS_WG;
+constexpr int kStatsVPL = MI355_STATS_VPL;
+constexpr int kApplyWG = MI355_APPLY_WG;
+constexpr int kApplyVPL = MI355_APPLY_VPL;
 #ifndef MI355_COOP_WG
 #define MI355_COOP_WG 1024
 #endif
@@ -74,14 +85,10 @@ constexpr int kSyncStride = 64;
 hipError_t launch_rows_f32(bool rms, const NormCall& c, const Plan& p);
 hipError_t launch_rows_bf16(bool rms, const NormCall& c, const Plan& p);
 hipError_t launch_rows_f16(bool rms, const NormCall& c, const Plan& p);
-// two-kernel split: ws M*chunks partials, sync 64*M counters (zero before and
-// after), rowstat M per-row (mean about the shift, rstd)
-hipError_t launch_split_f32(bool rms, const NormCall& c, const Plan& p, float2* ws, unsigned* sync,
-                            float2* rowstat);
-hipError_t launch_split_bf16(bool rms, const NormCall& c, const Plan& p, float2* ws, unsigned* sync,
-                             float2* rowstat);
-hipError_t launch_split_f16(bool rms, const NormCall& c, const Plan& p, float2* ws, unsigned* sync,
-                            float2* rowstat);
+// two-kernel split: ws holds M*chunks partials
+hipError_t launch_split_f32(bool rms, const NormCall& c, const Plan& p, float2* ws);
+hipError_t launch_split_bf16(bool rms, const NormCall& c, const Plan& p, float2* ws);
+hipError_t launch_split_f16(bool rms, const NormCall& c, const Plan& p, float2* ws);
 // single-pass split: ws holds M*chunks partials, sync 2*M counters that are
 // zero before the launch and zero again after it; each row waits for `need`
 // arrivals (its chunk count) for at most spin_limit polls

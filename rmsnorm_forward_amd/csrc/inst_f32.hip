@@ -5,9 +5,8 @@ namespace mi355norm {
 hipError_t launch_rows_f32(bool rms, const NormCall& c, const Plan& p) {
     return detail::launch_rows<F32>(rms, c, p);
 }
-hipError_t launch_split_f32(bool rms, const NormCall& c, const Plan& p, float2* ws, unsigned* sync,
-                          float2* rowstat) {
-    return detail::launch_split<F32>(rms, c, p, ws, sync, rowstat);
+hipError_t launch_split_f32(bool rms, const NormCall& c, const Plan& p, float2* ws) {
+    return detail::launch_split<F32>(rms, c, p, ws);
 }
 hipError_t launch_split_coop_f32(bool rms, const NormCall& c, const Plan& p, float2* ws,
                                  unsigned* sync, unsigned need, unsigned spin_limit) {

@@ -66,7 +66,7 @@ hipError_t launch_rows(bool rms, const NormCall& c, const Plan& p) {
 }
 
 template <class T, bool RMS, int EPV>
-hipError_t go_split(const NormCall& c, const Plan& p, float2* ws, unsigned* sync, float2* rowstat) {
+hipError_t go_split(const NormCall& c, const Plan& p, float2* ws) {
     const St<T>* x = static_cast<const St<T>*>(c.x);
     const St<T>* g = static_cast<const St<T>*>(c.gamma);
     const St<T>* b = static_cast<const St<T>*>(c.beta);
@@ -76,20 +76,21 @@ hipError_t go_split(const NormCall& c, const Plan& p, float2* ws, unsigned* sync
     int64_t M = c.M;
     int N = c.N;
     int S = p.chunks;
+    int CE = kStatsWG * kStatsVPL * EPV;
+    int A = p.apply_chunks;
     float eps = c.eps;
     {
-        void* args[] = {&x, &ws, &sync, &rowstat, &mean, &rstd, &M, &N, &S, &eps};
+        void* args[] = {&x, &ws, &M, &N, &S};
         hipError_t e = hipLaunchKernel(
-            reinterpret_cast<const void*>(&norm_split_stats_kernel<T, RMS, kSplitWG, kSplitVPL, EPV>),
-            dim3((unsigned)p.grid), dim3(kSplitWG), args, 0, c.stream);
+            reinterpret_cast<const void*>(&norm_split_stats_kernel<T, RMS, kStatsWG, kStatsVPL, EPV>),
+            dim3((unsigned)p.grid), dim3(kStatsWG), args, 0, c.stream);
         if (e != hipSuccess) return e;
     }
-    const float2* rs = rowstat;
     const float2* pp = ws;
-    void* args[] = {&x, &g, &b, &y, &pp, &rs, &mean, &rstd, &M, &N, &S, &eps};
+    void* args[] = {&x, &g, &b, &y, &pp, &mean, &rstd, &M, &N, &S, &CE, &A, &eps};
     return hipLaunchKernel(
-        reinterpret_cast<const void*>(&norm_split_apply_kernel<T, RMS, kSplitWG, kSplitVPL, EPV>),
-        dim3((unsigned)p.grid), dim3(kSplitWG), args, 0, c.stream);
+        reinterpret_cast<const void*>(&norm_split_apply_kernel<T, RMS, kApplyWG, kApplyVPL, EPV>),
+        dim3((unsigned)p.apply_grid), dim3(kApplyWG), args, 0, c.stream);
 }
 
 template <class T, bool RMS, int EPV>
@@ -142,13 +143,10 @@ hipError_t launch_split_coop(bool rms, const NormCall& c, const Plan& p, float2*
 }
 
 template <class T>
-hipError_t launch_split(bool rms, const NormCall& c, const Plan& p, float2* ws, unsigned* sync,
-                        float2* rowstat) {
+hipError_t launch_split(bool rms, const NormCall& c, const Plan& p, float2* ws) {
     constexpr int VEC = 16 / T::bytes;
-    if (p.epv == VEC)
-        return rms ? go_split<T, true, VEC>(c, p, ws, sync, rowstat) : go_split<T, false, VEC>(c, p, ws, sync, rowstat);
-    if (p.epv == 1)
-        return rms ? go_split<T, true, 1>(c, p, ws, sync, rowstat) : go_split<T, false, 1>(c, p, ws, sync, rowstat);
+    if (p.epv == VEC) return rms ? go_split<T, true, VEC>(c, p, ws) : go_split<T, false, VEC>(c, p, ws);
+    if (p.epv == 1) return rms ? go_split<T, true, 1>(c, p, ws) : go_split<T, false, 1>(c, p, ws);
     return hipErrorInvalidValue;
 }
 

@@ -11,20 +11,24 @@
 // associative merge of "CUDA 算子工程" ch. 7 section 7.4.1.
 //
 // Two schedules:
-//   norm_split_coop_kernel   single pass, x read once: each workgroup keeps
-//                            its chunk in VGPRs, publishes its partial, waits
-//                            at a per-row team barrier (all S workgroups of a
-//                            team are co-resident: cooperative launch), merges
-//                            and normalises from registers.  Teams walk the
-//                            rows with a stride of the team count.  The
-//                            barrier's counters return to zero by the end of
-//                            every launch, so a kept workspace needs no reset.
-//   norm_split_stats_kernel  two kernels: partials (x read through the
-//   + norm_split_apply_kernel  caches), then a second kernel that merges the
-//                            row's partials, re-reads x and stores y.  When
-//                            a batch of rows fits in the 256 MB Infinity
-//                            Cache the re-read is served on-die, so HBM
-//                            sees x about once.
+//   norm_split_stats_kernel  the default: two kernels.  Partials (x read
+//   + norm_split_apply_kernel  through the caches), then a second kernel that
+//                            merges the row's partials, re-reads x and
+//                            stores y (the two may cut rows into chunks of
+//                            different sizes).  When a batch of rows fits in
+//                            the 256 MB Infinity Cache the re-read is served
+//                            on-die, so HBM sees x about once.
+//   norm_split_coop_kernel   on request: single pass, x read once.  Each
+//                            workgroup keeps its chunk in VGPRs, publishes
+//                            its partial, waits at a per-row team barrier
+//                            (all S workgroups of a team are co-resident:
+//                            cooperative launch), merges and normalises from
+//                            registers.  Teams walk the rows with a stride of
+//                            the team count.  The barrier's counters return
+//                            to zero by the end of every launch, so a kept
+//                            workspace needs no reset.  Waiting workgroups
+//                            issue no loads, which makes it the slower of
+//                            the two on MI355X.
 #pragma once
 
 #include "prims.hpp"
@@ -217,15 +221,10 @@ __device__ __forceinline__ float2 row_stats(const float2* pr, int S, int CE, int
 // single pass, cooperative
 // ---------------------------------------------------------------------------
 
-// Publication of the partials:
-//   0  plain stores, release add / acquire fence at agent scope
-//      (write-back and invalidation of the L2 by every workgroup, every row)
-//   1  as 0, the departure count relaxed
-//   2  partials as coherent 64-bit atomic stores and loads; the store is
-//      complete before the arrival count is incremented; no L2 maintenance
-#ifndef MI355_COOP_SYNC
-#define MI355_COOP_SYNC 2
-#endif
+// Publication of the partials: each is one coherent 64-bit atomic store,
+// complete before the arrival count is incremented, and read back with
+// coherent 64-bit loads; no L2 write-back or invalidation is needed (agent-
+// scope release / acquire would cost one of each per workgroup and row).
 
 
 template <class T, bool RMS, int WG, int VPL, int EPV>
@@ -259,19 +258,13 @@ void norm_split_coop_kernel(const typename T::storage* __restrict__ x,
         // one 256-byte line per row: rows in flight never share a line
         unsigned* arrived = sync + row * 64;
         unsigned* departed = arrived + 32;
-        constexpr bool COH = MI355_COOP_SYNC == 2;
         if (tid == 0) {
             // publish the partial before the arrival count, then wait for the
             // row's other S-1 workgroups.  Polling uses relaxed loads.  The
             // wait is bounded so a broken co-residency assumption cannot hang.
-            if constexpr (COH) {
-                store_partial_coherent(part + row * S + c, p);
-                __builtin_amdgcn_s_waitcnt(0);     // the store has completed
-                __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            } else {
-                part[row * S + c] = p;
-                __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-            }
+            store_partial_coherent(part + row * S + c, p);
+            __builtin_amdgcn_s_waitcnt(0);     // the store has completed
+            __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             unsigned spins = 0;
             int timed_out = 0;
             // need = S (a host test hook can ask for S + 1, which never comes)
@@ -285,15 +278,13 @@ void norm_split_coop_kernel(const typename T::storage* __restrict__ x,
             late = timed_out;
         }
         __syncthreads();
-        if constexpr (!COH) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        float2 st = row_stats<RMS, COH>(part + row * S, S, C::CV * EPV, N, eps);
+        float2 st = row_stats<RMS, true>(part + row * S, S, C::CV * EPV, N, eps);
         if (late) st = make_float2(__builtin_nanf(""), __builtin_nanf(""));   // visible failure
         if (tid == 0) {
             // every workgroup has passed the wait once all S have departed:
             // the last one out returns both counters to zero for the next call
-            if (__hip_atomic_fetch_add(departed, 1u,
-                                       MI355_COOP_SYNC == 0 ? __ATOMIC_ACQ_REL : __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT) == (unsigned)S - 1) {
+            if (__hip_atomic_fetch_add(departed, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                (unsigned)S - 1) {
                 __hip_atomic_store(arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 __hip_atomic_store(departed, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
@@ -310,29 +301,16 @@ void norm_split_coop_kernel(const typename T::storage* __restrict__ x,
 // two kernels
 // ---------------------------------------------------------------------------
 
-// Where the two-kernel form merges a row's partials:
-//   0  in kernel 1, by the last workgroup of the row to publish (an atomic
-//      arrival count), once per row; kernel 2 reads the finished statistics
-//   1  in kernel 2, by every wavefront, after it has issued its loads of x
-//      (the merge's latency hides behind them); kernel 1 only stores partials
-#ifndef MI355_SPLIT_MERGE
-#define MI355_SPLIT_MERGE 1
-#endif
-
-// Kernel 1: per-chunk partials, x read through the caches.
+// Kernel 1: per-chunk partials, x read through the caches (a second read
+// soon after is served on-die).  Chunks of CV = WG*VPL vectors.
 template <class T, bool RMS, int WG, int VPL, int EPV>
 __global__ __launch_bounds__(WG)
 void norm_split_stats_kernel(const typename T::storage* __restrict__ x,
                              float2* __restrict__ part,      // [M, S] partials
-                             unsigned* __restrict__ sync,    // row r: [64r]; zero at launch and exit
-                             float2* __restrict__ rowstat,   // [M] (mean about K, rstd)
-                             float* __restrict__ mean_out,
-                             float* __restrict__ rstd_out,
-                             int64_t M, int N, int S, float eps)
+                             int64_t M, int N, int S)
 {
     using C = Chunk<T, WG, VPL, EPV>;
     __shared__ float red[2][WG / 64];
-    __shared__ int last;
     const int NV = N / EPV;
     const int64_t items = M * (int64_t)S;
     for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
@@ -343,34 +321,16 @@ void norm_split_stats_kernel(const typename T::storage* __restrict__ x,
         ch.template load<false>(xr, c, NV);
         const float K = RMS ? 0.0f : T::widen(xr[0]);
         const float2 p = ch.template partial<RMS>(K, NV, red);
-#if MI355_SPLIT_MERGE == 0
-        unsigned* arrived = sync + row * 64;
-        if (threadIdx.x == 0) {
-            // the partial is complete at the coherence point before the count
-            store_partial_coherent(part + row * S + c, p);
-            __builtin_amdgcn_s_waitcnt(0);
-            last = __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                   (unsigned)S - 1;
-        }
-        __syncthreads();
-        if (last && threadIdx.x < 64) {     // one wavefront finishes the row
-            const float2 st = row_stats<RMS, true>(part + row * S, S, C::CV * EPV, N, eps);
-            if (threadIdx.x == 0) {
-                rowstat[row] = st;
-                if (!RMS && mean_out) mean_out[row] = K + st.x;
-                if (rstd_out) rstd_out[row] = st.y;
-                __hip_atomic_store(arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-#else
-        (void)sync; (void)rowstat; (void)mean_out; (void)rstd_out; (void)eps; (void)last;
         if (threadIdx.x == 0) part[row * S + c] = p;
-#endif
         __syncthreads();          // LDS slots are rewritten by the next item
     }
 }
 
-// Kernel 2: normalise each chunk with its row's statistics (x's last read).
+// Kernel 2: per chunk of its own size (A chunks per row), issue the loads of
+// x (its last read), merge the row's S partials of CE elements each while
+// they are in flight, normalise and store.  Every wavefront runs the same
+// merge in chunk order, so every chunk of a row uses the same bits of mean
+// and rstd.  The row's first chunk stores mean and rstd.
 template <class T, bool RMS, int WG, int VPL, int EPV>
 __global__ __launch_bounds__(WG)
 void norm_split_apply_kernel(const typename T::storage* __restrict__ x,
@@ -378,34 +338,25 @@ void norm_split_apply_kernel(const typename T::storage* __restrict__ x,
                              const typename T::storage* __restrict__ beta,
                              typename T::storage* __restrict__ y,
                              const float2* __restrict__ part,
-                             const float2* __restrict__ rowstat,
                              float* __restrict__ mean_out,
                              float* __restrict__ rstd_out,
-                             int64_t M, int N, int S, float eps)
+                             int64_t M, int N, int S, int CE, int A, float eps)
 {
     using C = Chunk<T, WG, VPL, EPV>;
     const int NV = N / EPV;
-    const int64_t items = M * (int64_t)S;
+    const int64_t items = M * (int64_t)A;
     for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-        const int64_t row = it / S;
-        const int c = (int)(it - row * S);
+        const int64_t row = it / A;
+        const int c = (int)(it - row * A);
         const typename T::storage* xr = x + row * (int64_t)N;
         C ch;
         ch.load(xr, c, NV);
         const float K = RMS ? 0.0f : T::widen(xr[0]);
-#if MI355_SPLIT_MERGE == 0
-        (void)part; (void)mean_out; (void)rstd_out; (void)eps;
-        const float2 st = rowstat[row];
-#else
-        (void)rowstat;
-        // every wavefront merges the row's partials in chunk order: the same
-        // bits in every wavefront of every workgroup of the row
-        const float2 st = row_stats<RMS>(part + row * S, S, C::CV * EPV, N, eps);
+        const float2 st = row_stats<RMS>(part + row * S, S, CE, N, eps);
         if (c == 0 && threadIdx.x == 0) {
             if (!RMS && mean_out) mean_out[row] = K + st.x;
             if (rstd_out) rstd_out[row] = st.y;
         }
-#endif
         ch.template apply<RMS>(y + row * (int64_t)N, gamma, beta, K, st.x, st.y);
     }
 }

@@ -125,8 +125,8 @@ def parse(desc):
     ("rms", 65536, 2048, "f32", dict(path="rows", team="256", vpl="2", epv="4")),
     ("rms", 65536, 2048, "bf16", dict(path="rows", team="64", vpl="4", epv="8")),
     ("ln", 4096, 5120, "bf16", dict(path="rows", team="256", vpl="4", epv="8")),
-    ("ln", 64, 1 << 20, "bf16", dict(path="split", mode="two", chunks="128", epv="8", batch_rows="64",
-                                      grid="8192")),
+    ("ln", 64, 1 << 20, "bf16", dict(path="split", mode="two", chunks="64", apply_chunks="64", epv="8",
+                                      batch_rows="64", grid="4096", apply_grid="4096")),
 ])
 def test_plans_of_the_measured_configurations(op, M, N, dtype, want):
     d = parse(rn.norm_describe(op, M, N, dtype))
@@ -165,16 +165,17 @@ def test_every_row_fits_its_tile():
                     assert int(d["team"]) * int(d["vpl"]) >= nv
                 else:
                     assert int(d["chunks"]) * int(d["wg"]) * int(d["vpl"]) >= nv
+                    assert int(d["apply_chunks"]) * int(d["apply_wg"]) * int(d["apply_vpl"]) >= nv
 
 
 def test_split_rows_run_in_batches_of_about_256_mib():
     d = parse(rn.norm_describe("ln", 4096, 1 << 18, "bf16"))      # 512 KiB rows: 512 per batch
-    assert (d["mode"], d["batch_rows"], d["chunks"]) == ("two", "512", "32")
-    assert int(d["grid"]) == 512 * 32
+    assert (d["mode"], d["batch_rows"], d["chunks"]) == ("two", "512", "16")
+    assert int(d["grid"]) == 512 * 16 and int(d["apply_grid"]) == 512 * int(d["apply_chunks"])
     d = parse(rn.norm_describe("rms", 5, 1 << 24, "f32"))          # 64 MiB rows: 4 per batch
-    assert d["batch_rows"] == "4" and int(d["chunks"]) * 4096 == 1 << 24
+    assert d["batch_rows"] == "4" and int(d["chunks"]) * 8192 == 1 << 24
     d = parse(rn.norm_describe("ln", 1, 200000, "f16", aligned=False))
-    assert (d["batch_rows"], d["epv"], d["chunks"]) == ("1", "1", str(-(-200000 // 1024)))
+    assert (d["batch_rows"], d["epv"], d["chunks"]) == ("1", "1", str(-(-200000 // 2048)))
 
 
 def test_split_batch_override(monkeypatch):

@@ -308,8 +308,8 @@ def test_split_workspace_reused_across_shapes(monkeypatch, mode):
 def test_single_pass_split_bounded_wait(monkeypatch):
     """Forced from the host, every row waits for one arrival more than it has
     chunks, with a short bound: every workgroup stops waiting, the kernel
-    completes, the failure is visible (all outputs NaN), the barrier counters
-    are back at zero, and the next normal call is correct."""
+    completes, the failure is visible (all outputs NaN), the counters are
+    back at zero, and the next normal call is correct."""
     inp = inputs("ln", "bf16", 6, 1 << 18, seed=62)
     monkeypatch.setenv("MI355NORM_PATH", "splitcoop")
     monkeypatch.setenv("MI355NORM_FORCE_TIMEOUT", "1")
