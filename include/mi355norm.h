@@ -53,8 +53,8 @@
  *
  * Ownership: the caller allocates and owns every buffer and keeps it alive
  * until the stream has passed the call.  The library keeps no pointer to
- * them after return.  Rows too long for one workgroup (N > 2^17 for 2-byte
- * and N > 2^16 for 4-byte types, with 16-byte alignment; N > 2^14 without)
+ * them after return.  Rows too long for one workgroup (N > 2^16 for 2-byte
+ * and N > 2^15 for 4-byte types, with 16-byte alignment; N > 2^14 without)
  * are processed in batches of rows holding about 256 MiB of x, two kernel
  * launches per batch, and use a library-owned device workspace of at most a
  * few MiB (per row of a batch: 264 bytes plus 8 bytes per chunk of the row),

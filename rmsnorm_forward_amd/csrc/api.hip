@@ -1,15 +1,17 @@
 // api.hip -- the C ABI (include/mi355norm.h): argument validation, choice of
 // the row-to-workgroup mapping from (N, dtype, alignment), and launch.
 //
-// Mapping regimes, chosen by row length in 16-byte vectors (NV).  Every lane
+// Mapping regimes, chosen by row length in 16-byte vectors (NV).  A lane
 // holds four vectors for 2-byte types (32 elements) and two for fp32 (8
-// elements); the team is as large as the row needs (at least 8 lanes):
+// elements); the team is as large as the row needs (at least 8 lanes), and
+// for LayerNorm at most 2048 elements wide, beyond which lanes take up to 8
+// vectors:
 //   small rows  (bf16 N <= 1024, fp32 N <= 256): 8..32 lanes per row, 2..8
 //               rows share a wavefront and reduce with DPP only;
-//   mid rows    (up to 1024 lanes): 64..1024 lanes per row, one LDS exchange
-//               per reduction across the row's wavefronts; longer rows give
-//               the 1024-lane team up to 16 vectors per lane;
-//   long rows   (beyond 1024 lanes x 16 vectors): split across workgroups
+//   mid rows    (up to 1024 lanes x 8 vectors: bf16 N <= 65536, fp32
+//               N <= 32768): 64..1024 lanes per row, one LDS exchange per
+//               reduction across the row's wavefronts;
+//   long rows   (beyond 1024 lanes x 8 vectors): split across workgroups
 //               in chunks of 256 lanes x 8 vectors; per-chunk partial
 //               statistics merged in chunk order (Chan).  Two kernels per
 //               batch of rows holding about 256 MiB of x: partials (x read
@@ -20,8 +22,8 @@
 // Measured on MI355X in steady state (200 back-to-back launches): bf16
 // 1024-wide RMSNorm 32x4 (2 rows per wavefront) 85.3 us vs 64x2 87.1, 16x8
 // 95.1; bf16 2048-wide 64x4 87.6 vs 32x8 99.4; fp32 2048-wide 256x2 175.0
-// vs 128x4 177.6, 64x8 189.6.  More than four vectors per lane, or 4-lane
-// teams, always lost.
+// vs 128x4 177.6, 64x8 189.6.  At these widths more than four vectors per
+// lane, or 4-lane teams, always lost.
 //
 // Test/benchmark hooks (environment, read per call):
 //   MI355NORM_PATH = rows | split | split2 | splitcoop
@@ -178,8 +180,12 @@ int make_plan(int op, int64_t M, int64_t N, int dtype, bool aligned, const Overr
     std::memset(p, 0, sizeof *p);
     p->epv = aligned ? 16 / e : 1;
     const int64_t NV = N / p->epv;
+    // any instantiated tile can hold up to 1024 x 16 vectors, but 16 full
+    // 16-byte vectors per lane spill (bf16 1024 x 131072: 205 us vs 125 us
+    // split), so the automatic choice keeps 16-byte rows at 8 per lane
     const bool fits_rows = NV <= int64_t(kMaxTeam) * kMaxVpl;
-    int path = fits_rows ? PATH_ROWS : PATH_SPLIT;
+    const bool rows_auto = NV <= int64_t(kMaxTeam) * (p->epv == 1 ? kMaxVpl : 8);
+    int path = rows_auto ? PATH_ROWS : PATH_SPLIT;
     if (o.path == PATH_SPLIT) path = PATH_SPLIT;
     if (o.path == PATH_ROWS) {
         if (!fits_rows) return NORM_ERR_BAD_ARG;
@@ -197,6 +203,15 @@ int make_plan(int op, int64_t M, int64_t N, int dtype, bool aligned, const Overr
             team = next_pow2((NV + per_lane - 1) / per_lane);
             if (team < 8) team = 8;
             if (team > kMaxTeam) team = kMaxTeam;
+            // LayerNorm keeps a team's vector row at <= 2048 elements and
+            // grows the vectors per lane instead (bf16 N = 16384: 256 x 8
+            // 92.6 us vs 512 x 4 99.9; fp32 N = 8192: 512 x 4 46.9 vs
+            // 1024 x 2 49.7), up to 8 per lane
+            if (op == OP_LN && p->epv > 1) {
+                const int cap = 2048 / p->epv;
+                if (team > cap) team = cap;
+                while ((NV + team - 1) / team > 8 && team < kMaxTeam) team *= 2;
+            }
             vpl = round_vpl((NV + team - 1) / team);
         }
         p->team = team;

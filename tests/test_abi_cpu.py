@@ -134,6 +134,27 @@ def test_plans_of_the_measured_configurations(op, M, N, dtype, want):
         assert d[k] == v, (k, d)
 
 
+@pytest.mark.parametrize("op,N,dtype,want", [
+    ("ln", 16384, "bf16", ("rows", "256", "8")),
+    ("ln", 32768, "bf16", ("rows", "512", "8")),
+    ("ln", 65536, "bf16", ("rows", "1024", "8")),
+    ("ln", 131072, "bf16", ("split", None, None)),
+    ("ln", 8192, "f32", ("rows", "512", "4")),
+    ("ln", 16384, "f32", ("rows", "512", "8")),
+    ("ln", 32768, "f32", ("rows", "1024", "8")),
+    ("ln", 65536, "f32", ("split", None, None)),
+    ("rms", 16384, "bf16", ("rows", "512", "4")),
+    ("rms", 8192, "f32", ("rows", "1024", "2")),
+    ("rms", 131072, "bf16", ("split", None, None)),
+])
+def test_long_row_tiles(op, N, dtype, want):
+    d = parse(rn.norm_describe(op, 64, N, dtype))
+    if want[0] == "split":
+        assert d["path"] == "split", d
+    else:
+        assert (d["path"], d["team"], d["vpl"]) == want, d
+
+
 def test_small_rows_share_a_wavefront():
     for N in (16, 64, 200, 256, 512, 1024):       # aligned bf16 rows of at most 2 KiB
         d = parse(rn.norm_describe("rms", 1000, N, "bf16"))

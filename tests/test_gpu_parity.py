@@ -90,7 +90,8 @@ def test_check_row_large_mean():
 # ---------------------------------------------------------------------------
 
 EDGE_N = [1, 2, 3, 5, 7, 8, 10, 16, 63, 64, 65, 127, 128, 1000, 1023, 1024, 1025,
-          2047, 2048, 4096, 5120, 8191, 8192, 8193, 16384, 32768, 65536, 131072, 131080]
+          2047, 2048, 4096, 5120, 8191, 8192, 8193, 16384, 24576, 32768, 40000, 65536, 65544,
+          131072, 131080]
 
 
 def inputs(op, dtype, M, N, seed):
