@@ -56,17 +56,6 @@ __device__ __forceinline__ float team_reduce(float v, float* slots, int wave_in_
 #ifndef MI355_CACHE_F32_MAX
 #define MI355_CACHE_F32_MAX 32
 #endif
-// Issue the gamma/beta loads together with the x loads (their latency then
-// overlaps the statistics) rather than after the reductions.
-#ifndef MI355_GB_EARLY
-#define MI355_GB_EARLY 0
-#endif
-// Persistent grids: load gamma/beta once per workgroup and keep them in
-// VGPRs, widened to fp32, across the rows the workgroup visits.
-#ifndef MI355_GB_RESIDENT
-#define MI355_GB_RESIDENT 0
-#endif
-
 template <bool B>
 struct bool_c {
     static constexpr bool value = B;
@@ -100,8 +89,6 @@ void norm_rows_kernel(const typename T::storage* __restrict__ x,
     using V = Vec<T, EPV>;
     constexpr int E = VPL * EPV;               // elements per lane
     constexpr bool CACHE_F32 = E <= MI355_CACHE_F32_MAX;
-    constexpr bool GB_EARLY = MI355_GB_EARLY != 0;
-    constexpr bool GB_RES = MI355_GB_RESIDENT != 0;
 
     // cross-wavefront exchange slots: two sets, one float per wavefront
     __shared__ float red[2][G::ROWS][G::WPT];
@@ -114,25 +101,6 @@ void norm_rows_kernel(const typename T::storage* __restrict__ x,
     const float inv_n = 1.0f / (float)N;        // divisor is the true N
     const bool has_g = gamma != nullptr;
     const bool has_b = beta != nullptr;
-
-    // gamma / beta held in VGPRs as fp32 for the whole kernel (persistent grids)
-    float gres[GB_RES ? VPL : 1][EPV], bres[GB_RES ? VPL : 1][EPV];
-    if constexpr (GB_RES) {
-#pragma unroll
-        for (int j = 0; j < VPL; ++j) {
-            const unsigned v = (unsigned)(j * TEAM + tl);
-            V gt, bt;
-            if ((int)v < NV) {
-                if (has_g) gt.load(gamma + v * EPV);
-                if (!RMS && has_b) bt.load(beta + v * EPV);
-            }
-#pragma unroll
-            for (int k = 0; k < EPV; ++k) {
-                gres[j][k] = has_g ? gt.get(k) : 1.0f;
-                bres[j][k] = (!RMS && has_b) ? bt.get(k) : 0.0f;
-            }
-        }
-    }
 
     const int64_t groups = (M + G::ROWS - 1) / G::ROWS;
     int par = 0;    // RMS alternates LDS slot sets between iterations
@@ -152,16 +120,6 @@ void norm_rows_kernel(const typename T::storage* __restrict__ x,
             ok[j] = row_ok && (int)v < NV;
             if (ok[j]) xv[j].load_stream(xr + v * EPV);   // masked vectors stay undefined:
         }                                                 // every use below is masked per vector
-        V gv[GB_EARLY ? VPL : 1], bv[GB_EARLY ? VPL : 1];
-        if constexpr (GB_EARLY && !GB_RES) {
-#pragma unroll
-            for (int j = 0; j < VPL; ++j) {
-                const unsigned off = (unsigned)(j * TEAM + tl) * EPV;
-                if (ok[j] && has_g) gv[j].load(gamma + off);
-                if (!RMS && ok[j] && has_b) bv[j].load(beta + off);
-            }
-        }
-
         float rs, mu = 0.0f, K = 0.0f;
         float d[CACHE_F32 ? VPL : 1][EPV];
         if constexpr (RMS) {
@@ -238,12 +196,8 @@ void norm_rows_kernel(const typename T::storage* __restrict__ x,
                 if (!ok[j]) continue;
                 const unsigned off = (unsigned)(j * TEAM + tl) * EPV;
                 V gl, bl;
-                if constexpr (!GB_EARLY && !GB_RES) {
-                    if constexpr (HG) gl.load(gamma + off);
-                    if constexpr (HB) bl.load(beta + off);
-                }
-                const V& gj = GB_EARLY ? gv[GB_EARLY ? j : 0] : gl;
-                const V& bj = GB_EARLY ? bv[GB_EARLY ? j : 0] : bl;
+                if constexpr (HG) gl.load(gamma + off);
+                if constexpr (HB) bl.load(beta + off);
                 float o[EPV];
 #pragma unroll
                 for (int k = 0; k < EPV; ++k) {
@@ -251,12 +205,9 @@ void norm_rows_kernel(const typename T::storage* __restrict__ x,
                     if constexpr (RMS) t = xv[j].get(k) * rs;
                     else if constexpr (CACHE_F32) t = d[j][k] * rs;
                     else t = ((xv[j].get(k) - K) - mu) * rs;
-                    const float g = GB_RES ? gres[GB_RES ? j : 0][k] : (HG ? gj.get(k) : 1.0f);
-                    const float b = GB_RES ? bres[GB_RES ? j : 0][k] : (HB ? bj.get(k) : 0.0f);
-                    if constexpr (GB_RES) o[k] = RMS ? t * g : __builtin_fmaf(t, g, b);
-                    else if constexpr (HG && HB) o[k] = __builtin_fmaf(t, g, b);
-                    else if constexpr (HG) o[k] = t * g;
-                    else if constexpr (HB) o[k] = t + b;
+                    if constexpr (HG && HB) o[k] = __builtin_fmaf(t, gl.get(k), bl.get(k));
+                    else if constexpr (HG) o[k] = t * gl.get(k);
+                    else if constexpr (HB) o[k] = t + bl.get(k);
                     else o[k] = t;
                 }
                 V::store(yr + off, o);

@@ -1,0 +1,51 @@
+"""bench.py host logic that runs without a GPU: the one-GPU guard, the
+counter-summary lookup, and the CPU baseline's byte accounting."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+import bench
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, cwd=ROOT)
+    assert out.returncode == 2
+    assert "one GPU" in out.stderr and out.stdout == ""
+
+
+def test_traffic_needs_matching_sources_and_plan(tmp_path, monkeypatch):
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "k__w_counters.txt").write_text(
+        "kernel_source_sha256: abc\nplan: path=rows team=256\ntraffic_bytes_per_launch: 123\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda: "abc")
+    assert bench.read_traffic("k", "w", "path=rows team=256") == 123.0
+    assert bench.read_traffic("k", "w", "path=rows team=512") is None      # another tile
+    assert bench.read_traffic("k", "other", "path=rows team=256") is None  # no summary
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda: "def")
+    assert bench.read_traffic("k", "w", "path=rows team=256") is None      # kernels changed
+
+
+def test_kernel_digest_covers_the_device_code():
+    for name in bench.KERNEL_SOURCES:
+        assert os.path.exists(os.path.join(ROOT, "rmsnorm_forward_amd", "csrc", name)), name
+    assert len(bench.kernel_source_digest()) == 64
+
+
+def test_cpu_baseline_counts_the_rows_it_ran():
+    w = workloads.Workload("t", "ln", "f32", 64, 256, 1e-5, 0, "")
+    rng = np.random.default_rng(0)
+    inp = {"x": rng.standard_normal((64, 256)).astype(np.float32),
+           "gamma": np.ones(256, np.float32), "beta": np.zeros(256, np.float32)}
+    cb = bench.cpu_baseline(w, inp, seconds=5.0)
+    assert cb["kind"] == "oracle" and cb["cores"] == 1 and cb["unit"] == "GB/s"
+    assert cb["sample"].startswith("64 of 64 rows") and cb["value"] > 0
