@@ -78,6 +78,9 @@ class Oracle:
         lib.oracle_rms_fwd.argtypes = [vp, vp, ctypes.c_int, i64, i64,
                                        ctypes.c_double, vp, vp]
         lib.oracle_rms_fwd.restype = ctypes.c_int
+        lib.oracle_add_rms_fwd.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64,
+                                           ctypes.c_double, vp, vp, vp]
+        lib.oracle_add_rms_fwd.restype = ctypes.c_int
         lib.oracle_round.argtypes = [vp, i64, ctypes.c_int, vp]
         lib.oracle_round.restype = None
         lib.oracle_widen.argtypes = [vp, i64, ctypes.c_int, vp]
@@ -117,6 +120,23 @@ class Oracle:
             raise ValueError("oracle_rms_fwd rejected its arguments")
         return y, rstd
 
+    def add_rms_fwd(self, x, res, gamma, dtype: str, eps: float, exact_eps: bool = False):
+        """Residual add then RMSNorm of x[M, N] + res[M, N] -> (h, y, rstd):
+        h the rounded sum in storage `dtype`, y and rstd float64."""
+        x = _check_storage(x, dtype)
+        M, N = x.shape
+        res = _check_storage(res, dtype, M * N)
+        gamma = _check_storage(gamma, dtype, N)
+        h = np.empty((M, N), NP_STORAGE[dtype])
+        y = np.empty((M, N), np.float64)
+        rstd = np.empty(M, np.float64)
+        e = float(eps) if exact_eps else eps_as_kernel_sees(eps)
+        rc = self.lib.oracle_add_rms_fwd(_ptr(x), _ptr(res), _ptr(gamma), DTYPE_CODE[dtype], M, N,
+                                         e, _ptr(h), _ptr(y), _ptr(rstd))
+        if rc != 0:
+            raise ValueError("oracle_add_rms_fwd rejected its arguments")
+        return h, y, rstd
+
     def round_to(self, v, dtype: str):
         """Round float64 values to storage `dtype`, direct round-to-nearest-even."""
         v = np.ascontiguousarray(v, dtype=np.float64)
@@ -150,6 +170,10 @@ def ln_fwd(x, gamma, beta, dtype: str, eps: float):
 
 def rms_fwd(x, gamma, dtype: str, eps: float):
     return default().rms_fwd(x, gamma, dtype, eps)
+
+
+def add_rms_fwd(x, res, gamma, dtype: str, eps: float):
+    return default().add_rms_fwd(x, res, gamma, dtype, eps)
 
 
 def round_to(v, dtype: str):

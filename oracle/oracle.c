@@ -22,6 +22,11 @@
  *                 eps) * gamma, no mean, no beta); "CUDA算子优化(2)：RMSNorm",
  *                 section 1 (same formula, eps inside the root);
  *                 "T3 讲解", part ③.
+ *   Residual add + RMSNorm -- the fused step "CUDA 算子工程" ch. 7 (sections
+ *                 7.9-7.10) and "T3 讲解" part ⑤ name after vLLM's
+ *                 fused_add_rms_norm: read as exactly what a separate add
+ *                 (whose rounded sum is stored as the new residual) followed by
+ *                 RMSNorm of that stored sum computes.
  *   Output rounding -- round-to-nearest-even from the double result straight
  *                 to the storage type (no intermediate float rounding).  The
  *                 pages only say the result is cast to the output dtype
@@ -235,4 +240,31 @@ int oracle_rms_fwd(const void *x, const void *gamma, int dtype,
         if (rstd) rstd[r] = rs;
     }
     return 0;
+}
+
+/* ---- residual add, then RMSNorm --------------------------------------------
+ *
+ * For every element of x[M, N] and res[M, N]:
+ *   h_i   = x_i + res_i, rounded to the storage type (the updated residual
+ *           a separate add would store)
+ * then RMSNorm of the stored h, row by row, as oracle_rms_fwd:
+ *   rstd  = 1 / sqrt((sum_i h_i^2) / N + eps),   y_i = h_i * rstd * gamma_i
+ * h is written in the storage type (it must not be NULL), y and rstd in
+ * double; gamma == NULL means gamma_i = 1; rstd may be NULL.  Returns 0 or -1.
+ */
+static int64_t elem_size(int dtype)
+{
+    return dtype == OR_F64 ? 8 : dtype == OR_F32 ? 4 : 2;
+}
+
+int oracle_add_rms_fwd(const void *x, const void *res, const void *gamma, int dtype,
+                       int64_t M, int64_t N, double eps, void *h, double *y, double *rstd)
+{
+    if (dtype < OR_F32 || dtype > OR_F64 || M < 0 || N < 1 || !h)
+        return -1;
+    for (int64_t i = 0; i < M * N; ++i) {
+        double s = load_elem(x, i, dtype) + load_elem(res, i, dtype);
+        oracle_round(&s, 1, dtype, (char *)h + i * elem_size(dtype));
+    }
+    return oracle_rms_fwd(h, gamma, dtype, M, N, eps, y, rstd);
 }

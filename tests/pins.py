@@ -14,7 +14,8 @@ Kinds of pins used:
   * invariants       -- normalised rows have mean 0 and variance
                         var/(var+eps); RMS-normalised rows have mean square
                         ms/(ms+eps);
-  * special cases    -- N=1, constant rows, eps=0;
+  * special cases    -- N=1, constant rows, eps=0; a zero residual makes
+                        the residual-add step a plain RMSNorm;
   * library routines -- float64 torch layer_norm / rms_norm on the CPU,
                         numpy mean / var(ddof=0), numpy's double->half
                         conversion, torch's bfloat16 conversions.
@@ -392,6 +393,133 @@ def pin_round_f16_f32(orc):
     assert np.array_equal(got32, v.astype(np.float32))
 
 
+# --------------------------------------------------------------------------
+# residual add + RMSNorm
+# --------------------------------------------------------------------------
+
+FORMATS = {"f32": (24, -126), "bf16": (8, -126), "f16": (11, -14)}
+
+
+def round_fraction(v: Fraction, dtype: str) -> Fraction:
+    """Exact round-to-nearest-even of a rational to a binary format (finite
+    results only), written from the definition: the quantum of v's binade
+    (or of the smallest normal binade for subnormals), then the nearest
+    multiple of it, ties to the even multiple."""
+    prec, emin = FORMATS[dtype]
+    if v == 0:
+        return Fraction(0)
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    if Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, emin)
+    q = Fraction(2) ** (e - prec + 1)
+    k = a / q
+    f = k.numerator // k.denominator
+    rem = k - f
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and f % 2 == 1):
+        f += 1
+    r = f * q
+    return r if v > 0 else -r
+
+
+def _add_cases(seed=17):
+    """Tiny rows whose sums mostly do not fit the storage type: x large,
+    the residual small and not aligned to x's quantum."""
+    from workloads import to_storage
+    rng = np.random.default_rng(seed)
+    cases = []
+    for dtype in ("f32", "bf16", "f16"):
+        for n in (1, 3, 8, 13):
+            x = (rng.choice([1.0, 37.0, -300.0]) * (1 + rng.random((2, n)))).astype(np.float32)
+            r = (rng.standard_normal((2, n)) * rng.choice([1e-3, 0.3, 3.0])).astype(np.float32)
+            gm = rng.uniform(-1.5, 1.5, n).astype(np.float32)
+            eps = float(rng.choice([1e-6, 0.5]))
+            cases.append((dtype, to_storage(x, dtype), to_storage(r, dtype), to_storage(gm, dtype), eps))
+    return cases
+
+
+def pin_add_rms_brute_force(orc):
+    """h = RNE(x + res) exactly (rational arithmetic), then the exact RMSNorm
+    of h; at least some sums must need rounding, or the pin would not see a
+    norm taken of the unrounded sum."""
+    rounded = 0
+    for dtype, x, r, gm, eps in _add_cases():
+        xs = exact_values(x, dtype)
+        rs_ = exact_values(r, dtype)
+        gs = exact_values(gm, dtype)
+        n = x.shape[1]
+        h, y, rstd = orc.add_rms_fwd(x, r, gm, dtype, eps)
+        hs = exact_values(h, dtype)
+        e = Fraction(float(np.float32(eps)))
+        for row in range(x.shape[0]):
+            hb = []
+            for i in range(n):
+                k = row * n + i
+                want = round_fraction(xs[k] + rs_[k], dtype)
+                rounded += want != xs[k] + rs_[k]
+                assert hs[k] == want, (dtype, n, row, i, hs[k], want)
+                hb.append(want)
+            ms, rsb, yb = brute_rms_row(hb, gs, e)
+            assert _rel(rstd[row], float(rsb)) <= 16 * n * U64, (dtype, n, row)
+            for i in range(n):
+                assert abs(y[row, i] - float(yb[i])) <= 16 * n * U64 * abs(float(yb[i])) + 1e-300
+    assert rounded > 20, rounded
+
+
+def pin_add_rms_reduces_to_rms(orc):
+    """A zero residual (or a zero x) makes the step a plain RMSNorm: h is the
+    other operand bit for bit, and y, rstd equal rms_fwd's exactly; the add is
+    commutative."""
+    from workloads import to_storage
+    rng = np.random.default_rng(19)
+    for dtype in ("f32", "bf16", "f16"):
+        x = to_storage((2.0 * rng.standard_normal((3, 40))).astype(np.float32), dtype)
+        r = to_storage((0.7 * rng.standard_normal((3, 40))).astype(np.float32), dtype)
+        gm = to_storage(rng.uniform(0.5, 1.5, 40).astype(np.float32), dtype)
+        z = np.zeros_like(x)
+        y0, rs0 = orc.rms_fwd(x, gm, dtype, 1e-6)
+        for a, b in ((x, z), (z, x)):
+            h, y, rstd = orc.add_rms_fwd(a, b, gm, dtype, 1e-6)
+            assert np.array_equal(h.view(np.uint8), x.view(np.uint8)), dtype
+            assert np.array_equal(y, y0) and np.array_equal(rstd, rs0), dtype
+        h1, y1, r1 = orc.add_rms_fwd(x, r, gm, dtype, 1e-6)
+        h2, y2, r2 = orc.add_rms_fwd(r, x, gm, dtype, 1e-6)
+        assert np.array_equal(h1.view(np.uint8), h2.view(np.uint8))
+        assert np.array_equal(y1, y2) and np.array_equal(r1, r2)
+
+
+def pin_add_rms_library(orc):
+    """h against the libraries' own storage-type addition (numpy float32 and
+    float16, torch bfloat16), y against float64 torch rms_norm of h, on
+    rows of realistic width."""
+    import torch
+    import torch.nn.functional as F
+    from workloads import to_storage
+    rng = np.random.default_rng(23)
+    n = 1536
+    xf = (rng.standard_normal((4, n)) * 3).astype(np.float32)
+    rf = (rng.standard_normal((4, n)) * 0.05).astype(np.float32)
+    gf = rng.uniform(0, 1, n).astype(np.float32)
+    for dtype in ("f32", "f16", "bf16"):
+        x, r, gm = to_storage(xf, dtype), to_storage(rf, dtype), to_storage(gf, dtype)
+        h, y, rstd = orc.add_rms_fwd(x, r, gm, dtype, 1e-6)
+        if dtype == "bf16":
+            tb = lambda a: torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16)
+            ref = (tb(x) + tb(r)).view(torch.int16).numpy().view(np.uint16)
+            hd = tb(h).double()
+            gd = tb(gm).double()
+        else:
+            ref = x + r                       # numpy adds in the storage type, RNE
+            hd = torch.from_numpy(h.astype(np.float64))
+            gd = torch.from_numpy(gm.astype(np.float64))
+        assert np.array_equal(h.view(np.uint8), ref.view(np.uint8)), dtype
+        yt = F.rms_norm(hd, (n,), gd, float(np.float32(1e-6))).numpy()
+        assert np.max(np.abs(y - yt)) <= 1e-12, dtype
+
+
 ALL_PINS = [
     pin_large_mean_row_decimal,
     pin_large_mean_row_fp32,
@@ -405,4 +533,7 @@ ALL_PINS = [
     pin_widen_exhaustive,
     pin_round_bf16,
     pin_round_f16_f32,
+    pin_add_rms_brute_force,
+    pin_add_rms_reduces_to_rms,
+    pin_add_rms_library,
 ]

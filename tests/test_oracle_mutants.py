@@ -15,6 +15,23 @@ import pins
 LN_GAMMA = ("double g = gamma ? load_elem(gamma, i, dtype) : 1.0;\n"
             "                double b = beta")
 
+# RMSNorm taken of the unrounded double sums instead of the stored h
+UNROUNDED_NORM = """for (int64_t r = 0; r < M; ++r) {
+        double q = 0.0;
+        for (int64_t i = 0; i < N; ++i) {
+            double v = load_elem(x, r * N + i, dtype) + load_elem(res, r * N + i, dtype);
+            q += v * v;
+        }
+        double rs = 1.0 / sqrt(q / (double)N + eps);
+        for (int64_t i = 0; i < N; ++i) {
+            double g = gamma ? load_elem(gamma, i, dtype) : 1.0;
+            double v = load_elem(x, r * N + i, dtype) + load_elem(res, r * N + i, dtype);
+            if (y) y[r * N + i] = v * rs * g;
+        }
+        if (rstd) rstd[r] = rs;
+    }
+    return 0;"""
+
 MUTANTS = {
     "unbiased_variance": ("double var = q / (double)N;", "double var = q / (double)(N - 1);"),
     "ln_eps_outside_root": ("double rs = 1.0 / sqrt(var + eps);", "double rs = 1.0 / sqrt(var) + eps;"),
@@ -36,6 +53,15 @@ MUTANTS = {
     "bf16_widen_shift": ("(uint32_t)b << 16", "(uint32_t)b << 15"),
     "bf16_precision_off_by_one": ("rne_to_format(v, 8, -126)", "rne_to_format(v, 7, -126)"),
     "f16_min_normal_wrong": ("rne_to_format(a, 11, -14)", "rne_to_format(a, 11, -15)"),
+    "add_residual_sign": ("double s = load_elem(x, i, dtype) + load_elem(res, i, dtype);",
+                          "double s = load_elem(x, i, dtype) - load_elem(res, i, dtype);"),
+    "add_residual_row0_broadcast": ("+ load_elem(res, i, dtype);", "+ load_elem(res, i % N, dtype);"),
+    "add_residual_dropped": ("double s = load_elem(x, i, dtype) + load_elem(res, i, dtype);",
+                             "double s = load_elem(x, i, dtype) + 0.0 * load_elem(res, i, dtype);"),
+    "add_rms_norm_of_unrounded_sum": ("return oracle_rms_fwd(h, gamma, dtype, M, N, eps, y, rstd);",
+                                      UNROUNDED_NORM),
+    "add_rms_wrong_operand": ("double s = load_elem(x, i, dtype) + load_elem(res, i, dtype);",
+                              "double s = load_elem(x, i, dtype) + load_elem(x, i, dtype);"),
 }
 
 
