@@ -21,6 +21,14 @@
  *     -- "CUDA 算子工程" ch. 7, section 7.5; "CUDA算子优化(2)：RMSNorm", section 1;
  *        "T3 讲解" part ③.
  *
+ *   Residual add + RMSNorm (the fused step named after vLLM's
+ *   fused_add_rms_norm in "CUDA 算子工程" ch. 7, sections 7.9-7.10, and
+ *   "T3 讲解" part ⑤), per row r:
+ *       h[r,i] = x[r,i] + residual[r,i], rounded to the I/O dtype
+ *                (stored: the updated residual stream)
+ *       y[r,i] = RMSNorm(h)[r,i], taken of the stored h
+ *     Read as exactly what a separate add followed by rms_fwd computes.
+ *
  * The variance is computed by a stable method (two passes over register-
  * resident data for rows that fit one workgroup, Chan's parallel merge of
  * (n, mean, M2) partials for rows split across workgroups), never by
@@ -81,7 +89,7 @@ typedef enum { NORM_F32 = 0, NORM_F16 = 1, NORM_BF16 = 2 } norm_dtype;
 
 typedef enum {
     NORM_OK = 0,
-    NORM_ERR_NULL_ARG = 1,   /* x or y is NULL while M > 0                      */
+    NORM_ERR_NULL_ARG = 1,   /* x or y (or residual, residual_out) NULL, M > 0  */
     NORM_ERR_BAD_SHAPE = 2,  /* M < 0, N < 1, N > 2^24, or M * N overflows       */
     NORM_ERR_BAD_DTYPE = 3,  /* dtype not in norm_dtype                          */
     NORM_ERR_BAD_EPS = 4,    /* eps negative, NaN or infinite                    */
@@ -100,6 +108,22 @@ int rms_fwd(const void *x, const void *gamma, const void *beta, void *y,
             float *mean, float *rstd, int64_t M, int64_t N, float eps,
             int dtype, void *stream);
 
+/*
+ * Residual add, then RMSNorm.  x, residual, y, residual_out: [M, N] of
+ * `dtype`; gamma [N] or NULL; rstd fp32 [M] or NULL.  residual_out receives
+ * x + residual (rounded to dtype), y the RMSNorm of it.  In-place use is
+ * allowed exactly as the fused step is used in a transformer block:
+ * residual_out may be residual itself and y may be x itself (the very same
+ * pointers; a partial overlap, or any other overlap, is NORM_ERR_ALIAS).
+ * Rows too long for one workgroup read residual_out back in a second pass
+ * (so the caller must not read or write it until the stream has passed the
+ * call, as for every output).  Other conventions as above.  Returns a
+ * norm_status.
+ */
+int add_rms_fwd(const void *x, const void *residual, const void *gamma, void *y,
+                void *residual_out, float *rstd, int64_t M, int64_t N, float eps,
+                int dtype, void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *norm_status_str(int status);
 
@@ -115,8 +139,8 @@ const char *norm_last_error(void);
  * Describe, without launching anything, how a call with these arguments
  * would be executed: path ("rows" or "split"), lanes per row, 16-byte vectors
  * per lane, workgroup size, grid size, and the vector width.  `op` is 0 for
- * LayerNorm, 1 for RMSNorm; `aligned` says whether every pointer is 16-byte
- * aligned.  Writes at most buflen bytes (NUL-terminated) into buf and
+ * LayerNorm, 1 for RMSNorm, 2 for residual add + RMSNorm; `aligned` says
+ * whether every pointer is 16-byte aligned.  Writes at most buflen bytes (NUL-terminated) into buf and
  * returns a norm_status.  For tests and the benchmark's reports.
  */
 int norm_describe(int op, int64_t M, int64_t N, int dtype, int aligned,

@@ -5,10 +5,11 @@ Every step of the computation runs in the library's HIP kernels; this module
 only marshals arguments.  PyTorch is used for device memory and streams.
 
 Two layers:
-  * ln_fwd / rms_fwd / norm_status_str / norm_describe -- the C ABI entry
-    points under the same names, taking raw device addresses (ints) and
-    returning the status code;
-  * layer_norm / rms_norm -- the same calls on torch tensors: they allocate
+  * ln_fwd / rms_fwd / add_rms_fwd / norm_status_str / norm_last_error /
+    norm_describe -- the C ABI entry points under the same names, taking raw
+    device addresses (ints) and returning the status code;
+  * layer_norm / rms_norm / fused_add_rms_norm -- the same calls on torch
+    tensors: they allocate
     y (and fp32 mean / rstd), pass the current stream, and raise
     RuntimeError with the library's message on a non-zero status.
 
@@ -44,6 +45,8 @@ for _name in ("ln_fwd", "rms_fwd"):
     _fn = getattr(_lib, _name)
     _fn.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _int, _vp]
     _fn.restype = _int
+_lib.add_rms_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _int, _vp]
+_lib.add_rms_fwd.restype = _int
 _lib.norm_status_str.argtypes = [_int]
 _lib.norm_status_str.restype = ctypes.c_char_p
 _lib.norm_last_error.argtypes = []
@@ -79,6 +82,12 @@ def rms_fwd(x, gamma, beta, y, mean, rstd, M, N, eps, dtype, stream) -> int:
                         int(M), int(N), float(eps), int(dtype), _addr(stream))
 
 
+def add_rms_fwd(x, residual, gamma, y, residual_out, rstd, M, N, eps, dtype, stream) -> int:
+    """Residual add then RMSNorm on device addresses; returns the norm_status code."""
+    return _lib.add_rms_fwd(_addr(x), _addr(residual), _addr(gamma), _addr(y), _addr(residual_out),
+                            _addr(rstd), int(M), int(N), float(eps), int(dtype), _addr(stream))
+
+
 def norm_status_str(status: int) -> str:
     return _lib.norm_status_str(int(status)).decode()
 
@@ -90,7 +99,7 @@ def norm_last_error() -> str:
 
 def norm_describe(op: str, M: int, N: int, dtype, aligned: bool = True) -> str:
     """How the library would run this call (path, tile, grid); launches nothing."""
-    code = {"ln": 0, "rms": 1}[op]
+    code = {"ln": 0, "rms": 1, "add_rms": 2}[op]
     dt = DTYPE_NAMES.get(dtype, dtype)
     buf = ctypes.create_string_buffer(256)
     st = _lib.norm_describe(code, int(M), int(N), int(dt), int(bool(aligned)), buf, 256)
@@ -168,5 +177,33 @@ def rms_norm(x, gamma=None, eps: float = 1e-6, want_rstd: bool = True):
     return y.view(x.shape), rstd
 
 
-__all__ = ["ln_fwd", "rms_fwd", "norm_status_str", "norm_last_error", "norm_describe", "layer_norm", "rms_norm",
+def fused_add_rms_norm(x, residual, gamma=None, eps: float = 1e-6, inplace: bool = False,
+                       want_rstd: bool = True):
+    """h = x + residual (rounded to x's dtype), y = RMSNorm(h) over the last
+    dimension.  Returns (y, h, rstd).  With inplace=True, y is written into
+    x and h into residual (both must be contiguous), the way a transformer
+    block updates its residual stream."""
+    import torch
+    N = x.shape[-1]
+    if residual.shape != x.shape or residual.dtype != x.dtype or residual.device != x.device:
+        raise ValueError("residual must have x's shape, dtype and device")
+    if inplace and not (x.is_contiguous() and residual.is_contiguous()):
+        raise ValueError("inplace=True needs contiguous x and residual")
+    x2 = x.reshape(-1, N).contiguous()
+    r2 = residual.reshape(-1, N).contiguous()
+    M = x2.shape[0]
+    g = _param(gamma, N, x)
+    y = x2 if inplace else torch.empty_like(x2)
+    h = r2 if inplace else torch.empty_like(r2)
+    rstd = torch.empty(M, device=x.device, dtype=torch.float32) if want_rstd else None
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        _check(add_rms_fwd(x2.data_ptr(), r2.data_ptr(), g.data_ptr() if g is not None else None,
+                           y.data_ptr(), h.data_ptr(), rstd.data_ptr() if rstd is not None else None,
+                           M, N, eps, _torch_dtype_code(x2), stream))
+    return y.view(x.shape), h.view(x.shape), rstd
+
+
+__all__ = ["ln_fwd", "rms_fwd", "add_rms_fwd", "norm_status_str", "norm_last_error", "norm_describe",
+           "layer_norm", "rms_norm", "fused_add_rms_norm",
            "NORM_F32", "NORM_F16", "NORM_BF16", "NORM_OK", "STATUS", "LIB_PATH"]

@@ -53,8 +53,6 @@ using namespace mi355norm;
 
 namespace {
 
-enum { OP_LN = 0, OP_RMS = 1 };
-
 __global__ void norm_zero_u32(unsigned* p, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i < n) p[i] = 0u;
@@ -73,26 +71,35 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
 
 bool misaligned(const void* p, int a) { return p && ((uintptr_t)p % (uintptr_t)a) != 0; }
 
-int validate(int op, const void* x, const void* gamma, const void* beta, const void* y,
-             const float* mean, const float* rstd, int64_t M, int64_t N, float eps, int dtype) {
+int validate(int op, const void* x, const void* res, const void* gamma, const void* beta, const void* y,
+             const void* hout, const float* mean, const float* rstd, int64_t M, int64_t N, float eps,
+             int dtype) {
     if (dtype != NORM_F32 && dtype != NORM_F16 && dtype != NORM_BF16) return NORM_ERR_BAD_DTYPE;
     if (M < 0 || N < 1 || N > kMaxN) return NORM_ERR_BAD_SHAPE;
     const int e = elem_bytes(dtype);
     if (M > INT64_MAX / N / e) return NORM_ERR_BAD_SHAPE;
     if (!(eps >= 0.0f) || std::isinf(eps)) return NORM_ERR_BAD_EPS;
-    if (op == OP_RMS && (beta || mean)) return NORM_ERR_BAD_ARG;
+    if (op != OP_LN && (beta || mean)) return NORM_ERR_BAD_ARG;
     if (M == 0) return NORM_OK;
     if (!x || !y) return NORM_ERR_NULL_ARG;
+    if (op == OP_ADD_RMS && (!res || !hout)) return NORM_ERR_NULL_ARG;
     if (misaligned(x, e) || misaligned(y, e) || misaligned(gamma, e) || misaligned(beta, e) ||
-        misaligned(mean, 4) || misaligned(rstd, 4))
+        misaligned(res, e) || misaligned(hout, e) || misaligned(mean, 4) || misaligned(rstd, 4))
         return NORM_ERR_BAD_ARG;
     const int64_t nx = M * N * e, nv = N * e, ns = M * 4;
-    struct R { const void* p; int64_t n; bool out; } r[6] = {
-        {x, nx, false}, {gamma, nv, false}, {beta, nv, false},
-        {y, nx, true}, {mean, ns, true}, {rstd, ns, true}};
-    for (int i = 0; i < 6; ++i)
-        for (int j = i + 1; j < 6; ++j)
-            if ((r[i].out || r[j].out) && overlaps(r[i].p, r[i].n, r[j].p, r[j].n)) return NORM_ERR_ALIAS;
+    // in: 0 x, 1 res, 2 gamma, 3 beta;  out: 4 y, 5 hout, 6 mean, 7 rstd
+    struct R { const void* p; int64_t n; bool out; } r[8] = {
+        {x, nx, false}, {res, nx, false}, {gamma, nv, false}, {beta, nv, false},
+        {y, nx, true}, {hout, nx, true}, {mean, ns, true}, {rstd, ns, true}};
+    for (int i = 0; i < 8; ++i)
+        for (int j = i + 1; j < 8; ++j) {
+            if (!(r[i].out || r[j].out) || !overlaps(r[i].p, r[i].n, r[j].p, r[j].n)) continue;
+            // the residual add may write y or the sum exactly over x or the
+            // residual: each element is read by the lane that writes it, first
+            const bool row_io = (i == 0 || i == 1) && (j == 4 || j == 5);
+            if (op == OP_ADD_RMS && row_io && r[i].p == r[j].p) continue;
+            return NORM_ERR_ALIAS;
+        }
     return NORM_OK;
 }
 
@@ -148,30 +155,30 @@ bool tile_instantiated(int team, int vpl) {
 // How many workgroups of the single-pass split kernel the current device can
 // hold at once (0 if cooperative launch is unavailable or no device is
 // present).  Cached per (device, dtype, op, vector width).
-int64_t coop_capacity(int dtype, bool rms, int epv) {
+int64_t coop_capacity(int dtype, int op, int epv) {
     static std::mutex mu;
-    static int64_t cache[64][3][2][2];
-    static bool known[64][3][2][2];
+    static int64_t cache[64][3][3][2];
+    static bool known[64][3][3][2];
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) return 0;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
     const int vi = epv == 1 ? 0 : 1;
     std::lock_guard<std::mutex> lock(mu);
-    if (!known[dev][dtype][rms][vi]) {
+    if (!known[dev][dtype][op][vi]) {
         int coop = 0, cus = 0;
         int64_t cap = 0;
         if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && coop &&
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) {
-            int per_cu = dtype == NORM_F32 ? coop_blocks_per_cu_f32(rms, epv)
-                         : dtype == NORM_BF16 ? coop_blocks_per_cu_bf16(rms, epv)
-                                              : coop_blocks_per_cu_f16(rms, epv);
+            int per_cu = dtype == NORM_F32 ? coop_blocks_per_cu_f32(op, epv)
+                         : dtype == NORM_BF16 ? coop_blocks_per_cu_bf16(op, epv)
+                                              : coop_blocks_per_cu_f16(op, epv);
             cap = int64_t(per_cu) * cus;
         }
-        cache[dev][dtype][rms][vi] = cap;
-        known[dev][dtype][rms][vi] = true;
+        cache[dev][dtype][op][vi] = cap;
+        known[dev][dtype][op][vi] = true;
     }
-    return cache[dev][dtype][rms][vi];
+    return cache[dev][dtype][op][vi];
 }
 
 // Returns NORM_OK and fills *p, or NORM_ERR_BAD_ARG if an override cannot run.
@@ -227,7 +234,7 @@ int make_plan(int op, int64_t M, int64_t N, int dtype, bool aligned, const Overr
         if (o.split_mode == SPLIT_COOP) {
             const int64_t ccv = int64_t(kCoopWG) * kCoopVPL;
             const int64_t cchunks = (NV + ccv - 1) / ccv;
-            const int64_t cap = coop_capacity(dtype, op == OP_RMS, p->epv);
+            const int64_t cap = coop_capacity(dtype, op, p->epv);
             if (cap < cchunks) return NORM_ERR_BAD_ARG;
             p->split_mode = SPLIT_COOP;
             p->wg = kCoopWG;
@@ -323,22 +330,22 @@ bool all_aligned16(const void* x, const void* g, const void* b, const void* y, i
     return (N * e) % 16 == 0 && a(x) && a(y) && a(g) && a(b);
 }
 
-int run(int op, const void* x, const void* gamma, const void* beta, void* y, float* mean,
-        float* rstd, int64_t M, int64_t N, float eps, int dtype, void* stream) {
-    int st = validate(op, x, gamma, beta, y, mean, rstd, M, N, eps, dtype);
+int run(int op, const void* x, const void* res, const void* gamma, const void* beta, void* y, void* hout,
+        float* mean, float* rstd, int64_t M, int64_t N, float eps, int dtype, void* stream) {
+    int st = validate(op, x, res, gamma, beta, y, hout, mean, rstd, M, N, eps, dtype);
     if (st != NORM_OK || M == 0) return st;
     const int e = elem_bytes(dtype);
     Plan p;
-    st = make_plan(op, M, N, dtype, all_aligned16(x, gamma, beta, y, N, e), read_overrides(), &p);
+    const bool aligned = all_aligned16(x, gamma, beta, y, N, e) && all_aligned16(res, hout, nullptr, nullptr, N, e);
+    st = make_plan(op, M, N, dtype, aligned, read_overrides(), &p);
     if (st != NORM_OK) return st;
-    NormCall c{x, gamma, beta, y, mean, rstd, M, (int)N, eps, (hipStream_t)stream};
-    const bool rms = op == OP_RMS;
+    NormCall c{x, res, gamma, beta, y, hout, mean, rstd, M, (int)N, eps, (hipStream_t)stream};
     hipError_t err;
     if (p.path == PATH_ROWS) {
         switch (dtype) {
-        case NORM_F32: err = launch_rows_f32(rms, c, p); break;
-        case NORM_BF16: err = launch_rows_bf16(rms, c, p); break;
-        default: err = launch_rows_f16(rms, c, p); break;
+        case NORM_F32: err = launch_rows_f32(op, c, p); break;
+        case NORM_BF16: err = launch_rows_bf16(op, c, p); break;
+        default: err = launch_rows_f16(op, c, p); break;
         }
         return hip_ok(err, "row kernel launch") ? NORM_OK : NORM_ERR_HIP;
     }
@@ -357,9 +364,9 @@ int run(int op, const void* x, const void* gamma, const void* beta, void* y, flo
     if (coop) {
         unsigned* sync = w.sync;
         switch (dtype) {
-        case NORM_F32: err = launch_split_coop_f32(rms, c, p, part, sync, need, spin); break;
-        case NORM_BF16: err = launch_split_coop_bf16(rms, c, p, part, sync, need, spin); break;
-        default: err = launch_split_coop_f16(rms, c, p, part, sync, need, spin); break;
+        case NORM_F32: err = launch_split_coop_f32(op, c, p, part, sync, need, spin); break;
+        case NORM_BF16: err = launch_split_coop_bf16(op, c, p, part, sync, need, spin); break;
+        default: err = launch_split_coop_f16(op, c, p, part, sync, need, spin); break;
         }
     } else {
         // Row batches in stream order; each batch reuses the partials.
@@ -369,6 +376,8 @@ int run(int op, const void* x, const void* gamma, const void* beta, void* y, flo
             NormCall cb = c;
             cb.x = static_cast<const char*>(c.x) + r0 * N * e;
             cb.y = static_cast<char*>(c.y) + r0 * N * e;
+            if (c.res) cb.res = static_cast<const char*>(c.res) + r0 * N * e;
+            if (c.hout) cb.hout = static_cast<char*>(c.hout) + r0 * N * e;
             cb.mean = c.mean ? c.mean + r0 : nullptr;
             cb.rstd = c.rstd ? c.rstd + r0 : nullptr;
             cb.M = mb;
@@ -376,9 +385,9 @@ int run(int op, const void* x, const void* gamma, const void* beta, void* y, flo
             pb.grid = std::min(p.grid, mb * p.chunks);
             pb.apply_grid = std::min(p.apply_grid, mb * p.apply_chunks);
             switch (dtype) {
-            case NORM_F32: err = launch_split_f32(rms, cb, pb, part); break;
-            case NORM_BF16: err = launch_split_bf16(rms, cb, pb, part); break;
-            default: err = launch_split_f16(rms, cb, pb, part); break;
+            case NORM_F32: err = launch_split_f32(op, cb, pb, part); break;
+            case NORM_BF16: err = launch_split_bf16(op, cb, pb, part); break;
+            default: err = launch_split_f16(op, cb, pb, part); break;
             }
         }
     }
@@ -392,12 +401,18 @@ extern "C" {
 
 int ln_fwd(const void* x, const void* gamma, const void* beta, void* y, float* mean, float* rstd,
            int64_t M, int64_t N, float eps, int dtype, void* stream) {
-    return run(OP_LN, x, gamma, beta, y, mean, rstd, M, N, eps, dtype, stream);
+    return run(OP_LN, x, nullptr, gamma, beta, y, nullptr, mean, rstd, M, N, eps, dtype, stream);
 }
 
 int rms_fwd(const void* x, const void* gamma, const void* beta, void* y, float* mean, float* rstd,
             int64_t M, int64_t N, float eps, int dtype, void* stream) {
-    return run(OP_RMS, x, gamma, beta, y, mean, rstd, M, N, eps, dtype, stream);
+    return run(OP_RMS, x, nullptr, gamma, beta, y, nullptr, mean, rstd, M, N, eps, dtype, stream);
+}
+
+int add_rms_fwd(const void* x, const void* residual, const void* gamma, void* y, void* residual_out,
+                float* rstd, int64_t M, int64_t N, float eps, int dtype, void* stream) {
+    return run(OP_ADD_RMS, x, residual, gamma, nullptr, y, residual_out, nullptr, rstd, M, N, eps, dtype,
+               stream);
 }
 
 const char* norm_status_str(int status) {
@@ -417,7 +432,7 @@ const char* norm_status_str(int status) {
 const char* norm_last_error(void) { return g_last_error; }
 
 int norm_describe(int op, int64_t M, int64_t N, int dtype, int aligned, char* buf, int buflen) {
-    if (op != OP_LN && op != OP_RMS) return NORM_ERR_BAD_ARG;
+    if (op != OP_LN && op != OP_RMS && op != OP_ADD_RMS) return NORM_ERR_BAD_ARG;
     if (dtype != NORM_F32 && dtype != NORM_F16 && dtype != NORM_BF16) return NORM_ERR_BAD_DTYPE;
     if (M < 0 || N < 1 || N > kMaxN) return NORM_ERR_BAD_SHAPE;
     const int e = elem_bytes(dtype);

@@ -7,11 +7,16 @@
 
 namespace mi355norm {
 
+// Operations: LayerNorm, RMSNorm, and residual add followed by RMSNorm.
+enum { OP_LN = 0, OP_RMS = 1, OP_ADD_RMS = 2 };
+
 struct NormCall {
     const void* x;
+    const void* res;     // OP_ADD_RMS: the residual added to x (else null)
     const void* gamma;
     const void* beta;
     void* y;
+    void* hout;          // OP_ADD_RMS: where x + res is stored (else null)
     float* mean;
     float* rstd;
     int64_t M;
@@ -82,25 +87,25 @@ constexpr int64_t kSplitBatchBytes = MI355_SPLIT_BATCH_BYTES;
 // barrier counters of one row are 64 words (256 bytes) apart
 constexpr int kSyncStride = 64;
 
-hipError_t launch_rows_f32(bool rms, const NormCall& c, const Plan& p);
-hipError_t launch_rows_bf16(bool rms, const NormCall& c, const Plan& p);
-hipError_t launch_rows_f16(bool rms, const NormCall& c, const Plan& p);
+hipError_t launch_rows_f32(int op, const NormCall& c, const Plan& p);
+hipError_t launch_rows_bf16(int op, const NormCall& c, const Plan& p);
+hipError_t launch_rows_f16(int op, const NormCall& c, const Plan& p);
 // two-kernel split: ws holds M*chunks partials
-hipError_t launch_split_f32(bool rms, const NormCall& c, const Plan& p, float2* ws);
-hipError_t launch_split_bf16(bool rms, const NormCall& c, const Plan& p, float2* ws);
-hipError_t launch_split_f16(bool rms, const NormCall& c, const Plan& p, float2* ws);
+hipError_t launch_split_f32(int op, const NormCall& c, const Plan& p, float2* ws);
+hipError_t launch_split_bf16(int op, const NormCall& c, const Plan& p, float2* ws);
+hipError_t launch_split_f16(int op, const NormCall& c, const Plan& p, float2* ws);
 // single-pass split: ws holds M*chunks partials, sync 2*M counters that are
 // zero before the launch and zero again after it; each row waits for `need`
 // arrivals (its chunk count) for at most spin_limit polls
-hipError_t launch_split_coop_f32(bool rms, const NormCall& c, const Plan& p, float2* ws,
+hipError_t launch_split_coop_f32(int op, const NormCall& c, const Plan& p, float2* ws,
                                  unsigned* sync, unsigned need, unsigned spin_limit);
-hipError_t launch_split_coop_bf16(bool rms, const NormCall& c, const Plan& p, float2* ws,
+hipError_t launch_split_coop_bf16(int op, const NormCall& c, const Plan& p, float2* ws,
                                   unsigned* sync, unsigned need, unsigned spin_limit);
-hipError_t launch_split_coop_f16(bool rms, const NormCall& c, const Plan& p, float2* ws,
+hipError_t launch_split_coop_f16(int op, const NormCall& c, const Plan& p, float2* ws,
                                  unsigned* sync, unsigned need, unsigned spin_limit);
 // workgroups of the single-pass split kernel that fit on one CU at once
-int coop_blocks_per_cu_f32(bool rms, int epv);
-int coop_blocks_per_cu_bf16(bool rms, int epv);
-int coop_blocks_per_cu_f16(bool rms, int epv);
+int coop_blocks_per_cu_f32(int op, int epv);
+int coop_blocks_per_cu_bf16(int op, int epv);
+int coop_blocks_per_cu_f16(int op, int epv);
 
 }  // namespace mi355norm

@@ -2,17 +2,17 @@
 #include "inst_impl.hpp"
 
 namespace mi355norm {
-hipError_t launch_rows_f16(bool rms, const NormCall& c, const Plan& p) {
-    return detail::launch_rows<F16>(rms, c, p);
+hipError_t launch_rows_f16(int op, const NormCall& c, const Plan& p) {
+    return detail::launch_rows<F16>(op, c, p);
 }
-hipError_t launch_split_f16(bool rms, const NormCall& c, const Plan& p, float2* ws) {
-    return detail::launch_split<F16>(rms, c, p, ws);
+hipError_t launch_split_f16(int op, const NormCall& c, const Plan& p, float2* ws) {
+    return detail::launch_split<F16>(op, c, p, ws);
 }
-hipError_t launch_split_coop_f16(bool rms, const NormCall& c, const Plan& p, float2* ws,
-                                 unsigned* sync, unsigned need, unsigned spin_limit) {
-    return detail::launch_split_coop<F16>(rms, c, p, ws, sync, need, spin_limit);
+hipError_t launch_split_coop_f16(int op, const NormCall& c, const Plan& p, float2* ws, unsigned* sync,
+                                 unsigned need, unsigned spin_limit) {
+    return detail::launch_split_coop<F16>(op, c, p, ws, sync, need, spin_limit);
 }
-int coop_blocks_per_cu_f16(bool rms, int epv) {
-    return detail::coop_blocks_per_cu<F16>(rms, epv);
+int coop_blocks_per_cu_f16(int op, int epv) {
+    return detail::coop_blocks_per_cu<F16>(op, epv);
 }
 }  // namespace mi355norm

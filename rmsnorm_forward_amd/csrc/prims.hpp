@@ -94,6 +94,8 @@ __device__ __forceinline__ void st_stream(P v, P* p) {
 //   load()        cached load (gamma, beta)
 //   load_stream() nontemporal load (x)
 //   store()       nontemporal store (y)
+//   set()         round fp32 values into the vector's storage (RNE)
+//   put() / put_stream()   cached / nontemporal store of the vector as held
 // --------------------------------------------------------------------------
 
 template <class T, int EPV> struct Vec;
@@ -109,6 +111,11 @@ template <> struct Vec<F32, 4> {
         u32x4 o = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
         st_stream(o, reinterpret_cast<u32x4*>(p));
     }
+    __device__ __forceinline__ void set(const float (&v)[4]) {
+        w = u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+    }
+    __device__ __forceinline__ void put(float* p) const { *reinterpret_cast<u32x4*>(p) = w; }
+    __device__ __forceinline__ void put_stream(float* p) const { st_stream(w, reinterpret_cast<u32x4*>(p)); }
 };
 
 template <class H> struct VecHalf8 {
@@ -125,6 +132,11 @@ template <class H> struct VecHalf8 {
         u32x4 o = {H::pack(v[0], v[1]), H::pack(v[2], v[3]), H::pack(v[4], v[5]), H::pack(v[6], v[7])};
         st_stream(o, reinterpret_cast<u32x4*>(p));
     }
+    __device__ __forceinline__ void set(const float (&v)[8]) {
+        w = u32x4{H::pack(v[0], v[1]), H::pack(v[2], v[3]), H::pack(v[4], v[5]), H::pack(v[6], v[7])};
+    }
+    __device__ __forceinline__ void put(uint16_t* p) const { *reinterpret_cast<u32x4*>(p) = w; }
+    __device__ __forceinline__ void put_stream(uint16_t* p) const { st_stream(w, reinterpret_cast<u32x4*>(p)); }
 };
 template <> struct Vec<BF16, 8> : VecHalf8<BF16> {};
 template <> struct Vec<F16, 8> : VecHalf8<F16> {};
@@ -140,7 +152,25 @@ template <class T> struct Vec<T, 1> {
         if constexpr (sizeof(typename T::storage) == 4) st_stream(v[0], p);
         else st_stream(T::narrow(v[0]), p);
     }
+    __device__ __forceinline__ void set(const float (&v)[1]) {
+        if constexpr (sizeof(typename T::storage) == 4) s = v[0];
+        else s = T::narrow(v[0]);
+    }
+    __device__ __forceinline__ void put(typename T::storage* p) const { *p = s; }
+    __device__ __forceinline__ void put_stream(typename T::storage* p) const { st_stream(s, p); }
 };
+
+// Residual add in the storage type: h = x + r rounded to T (RNE).  The fp32
+// sum of two values of one of these formats rounds, if at all, only when the
+// smaller is below half an ulp of the larger in T, so rounding the fp32 sum
+// to T equals rounding the exact sum.
+template <class T, int EPV>
+__device__ __forceinline__ void add_into(Vec<T, EPV>& x, const Vec<T, EPV>& r) {
+    float h[EPV];
+#pragma unroll
+    for (int k = 0; k < EPV; ++k) h[k] = x.get(k) + r.get(k);
+    x.set(h);
+}
 
 // 1/sqrt(v) with the hardware reciprocal square root (v_rsq_f32, about one
 // ulp): one instruction per row instead of a correctly rounded square root

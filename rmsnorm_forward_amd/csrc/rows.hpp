@@ -74,16 +74,23 @@ __device__ __forceinline__ float vec_sum_shifted(const V& v, float K) {
     return t[0];
 }
 
-template <class T, bool RMS, int TEAM, int VPL, int EPV>
+// ADD (RMSNorm only): the row is first h = x + res rounded to the storage
+// type; h is stored to hout (the updated residual) and normalised in place of
+// x.  res / hout may be the same buffer, and y may be x: every element is
+// read into registers by the lane that later writes it, before it writes.
+template <class T, bool RMS, bool ADD, int TEAM, int VPL, int EPV>
 __global__ __launch_bounds__(TeamGeom<TEAM>::WG)
-void norm_rows_kernel(const typename T::storage* __restrict__ x,
+void norm_rows_kernel(const typename T::storage* x,
+                      const typename T::storage* res,
                       const typename T::storage* __restrict__ gamma,
                       const typename T::storage* __restrict__ beta,
-                      typename T::storage* __restrict__ y,
+                      typename T::storage* y,
+                      typename T::storage* hout,
                       float* __restrict__ mean_out,
                       float* __restrict__ rstd_out,
                       int64_t M, int N, float eps)
 {
+    static_assert(!ADD || RMS, "the residual add is fused with RMSNorm only");
     using G = TeamGeom<TEAM>;
     using S = typename T::storage;
     using V = Vec<T, EPV>;
@@ -120,6 +127,18 @@ void norm_rows_kernel(const typename T::storage* __restrict__ x,
             ok[j] = row_ok && (int)v < NV;
             if (ok[j]) xv[j].load_stream(xr + v * EPV);   // masked vectors stay undefined:
         }                                                 // every use below is masked per vector
+        if constexpr (ADD) {
+            V rv[VPL];
+#pragma unroll
+            for (int j = 0; j < VPL; ++j)
+                if (ok[j]) rv[j].load_stream(res + base + (unsigned)(j * TEAM + tl) * EPV);
+#pragma unroll
+            for (int j = 0; j < VPL; ++j) {
+                if (!ok[j]) continue;
+                add_into(xv[j], rv[j]);
+                xv[j].put_stream(hout + base + (unsigned)(j * TEAM + tl) * EPV);
+            }
+        }
         float rs, mu = 0.0f, K = 0.0f;
         float d[CACHE_F32 ? VPL : 1][EPV];
         if constexpr (RMS) {

@@ -79,6 +79,30 @@ struct Chunk {
         }
     }
 
+    // residual add: the chunk becomes h = x + r (rounded to the storage
+    // type), which is also stored to hr (nontemporal if STREAM, else cached
+    // so that a second read soon after is served on-die)
+    template <bool STREAM>
+    __device__ __forceinline__ void add_residual(const typename T::storage* rr, typename T::storage* hr) {
+        V rv[VPL];
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+            const unsigned v = (unsigned)(v0 + j * WG) + threadIdx.x;
+            if (ok[j]) {
+                if constexpr (STREAM) rv[j].load_stream(rr + v * EPV);
+                else rv[j].load(rr + v * EPV);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+            if (!ok[j]) continue;
+            const unsigned v = (unsigned)(v0 + j * WG) + threadIdx.x;
+            add_into(xv[j], rv[j]);
+            if constexpr (STREAM) xv[j].put_stream(hr + v * EPV);
+            else xv[j].put(hr + v * EPV);
+        }
+    }
+
     // keep widened copies from living across phases: re-widen instead
     __device__ __forceinline__ void opaque() {
 #pragma unroll
@@ -227,12 +251,14 @@ __device__ __forceinline__ float2 row_stats(const float2* pr, int S, int CE, int
 // scope release / acquire would cost one of each per workgroup and row).
 
 
-template <class T, bool RMS, int WG, int VPL, int EPV>
+template <class T, bool RMS, bool ADD, int WG, int VPL, int EPV>
 __global__ __launch_bounds__(WG)
-void norm_split_coop_kernel(const typename T::storage* __restrict__ x,
+void norm_split_coop_kernel(const typename T::storage* x,
+                            const typename T::storage* res,
                             const typename T::storage* __restrict__ gamma,
                             const typename T::storage* __restrict__ beta,
-                            typename T::storage* __restrict__ y,
+                            typename T::storage* y,
+                            typename T::storage* hout,
                             float* __restrict__ mean_out,
                             float* __restrict__ rstd_out,
                             float2* __restrict__ part,      // [M, S] partials
@@ -241,6 +267,7 @@ void norm_split_coop_kernel(const typename T::storage* __restrict__ x,
                             int64_t M, int N, int S, int teams, float eps,
                             unsigned need, unsigned spin_limit)
 {
+    static_assert(!ADD || RMS, "the residual add is fused with RMSNorm only");
     using C = Chunk<T, WG, VPL, EPV>;
     __shared__ float red[2][WG / 64];
     __shared__ int late;
@@ -253,6 +280,7 @@ void norm_split_coop_kernel(const typename T::storage* __restrict__ x,
         const typename T::storage* xr = x + row * (int64_t)N;
         C ch;
         ch.load(xr, c, NV);
+        if constexpr (ADD) ch.template add_residual<true>(res + row * (int64_t)N, hout + row * (int64_t)N);
         const float K = RMS ? 0.0f : T::widen(xr[0]);
         const float2 p = ch.template partial<RMS>(K, NV, red);
         // one 256-byte line per row: rows in flight never share a line
@@ -303,12 +331,17 @@ void norm_split_coop_kernel(const typename T::storage* __restrict__ x,
 
 // Kernel 1: per-chunk partials, x read through the caches (a second read
 // soon after is served on-die).  Chunks of CV = WG*VPL vectors.
-template <class T, bool RMS, int WG, int VPL, int EPV>
+// ADD: the chunk is h = x + res (rounded), stored to hout through the caches;
+// the normalising kernel then reads hout in place of x.
+template <class T, bool RMS, bool ADD, int WG, int VPL, int EPV>
 __global__ __launch_bounds__(WG)
-void norm_split_stats_kernel(const typename T::storage* __restrict__ x,
+void norm_split_stats_kernel(const typename T::storage* x,
+                             const typename T::storage* res,
+                             typename T::storage* hout,
                              float2* __restrict__ part,      // [M, S] partials
                              int64_t M, int N, int S)
 {
+    static_assert(!ADD || RMS, "the residual add is fused with RMSNorm only");
     using C = Chunk<T, WG, VPL, EPV>;
     __shared__ float red[2][WG / 64];
     const int NV = N / EPV;
@@ -319,6 +352,7 @@ void norm_split_stats_kernel(const typename T::storage* __restrict__ x,
         const typename T::storage* xr = x + row * (int64_t)N;
         C ch;
         ch.template load<false>(xr, c, NV);
+        if constexpr (ADD) ch.template add_residual<false>(res + row * (int64_t)N, hout + row * (int64_t)N);
         const float K = RMS ? 0.0f : T::widen(xr[0]);
         const float2 p = ch.template partial<RMS>(K, NV, red);
         if (threadIdx.x == 0) part[row * S + c] = p;
@@ -333,10 +367,10 @@ void norm_split_stats_kernel(const typename T::storage* __restrict__ x,
 // and rstd.  The row's first chunk stores mean and rstd.
 template <class T, bool RMS, int WG, int VPL, int EPV>
 __global__ __launch_bounds__(WG)
-void norm_split_apply_kernel(const typename T::storage* __restrict__ x,
+void norm_split_apply_kernel(const typename T::storage* x,
                              const typename T::storage* __restrict__ gamma,
                              const typename T::storage* __restrict__ beta,
-                             typename T::storage* __restrict__ y,
+                             typename T::storage* y,
                              const float2* __restrict__ part,
                              float* __restrict__ mean_out,
                              float* __restrict__ rstd_out,

@@ -57,3 +57,28 @@ def run(op: str, dtype: str, x: np.ndarray, gamma, beta, eps: float, *, stats: b
     if keep_device:
         return y, m, r, (xt, gt, bt, yt, mean, rstd)
     return y, m, r
+
+
+def run_add(dtype: str, x: np.ndarray, res: np.ndarray, gamma, eps: float, *, stats: bool = True,
+            offset: int = 0, inplace: bool = False):
+    """One add_rms_fwd call; returns (y, h, rstd) as host arrays.  With
+    inplace=True, y is written over x and h over the residual."""
+    M, N = x.shape
+    xt = to_device(x, dtype, offset)
+    rt = to_device(res, dtype, offset)
+    gt = to_device(gamma, dtype, offset) if gamma is not None else None
+    if inplace:
+        yt, ht = xt, rt
+    else:
+        yt = torch.empty(M * N + offset, dtype=TORCH_DT[dtype], device="cuda")[offset:]
+        ht = torch.empty(M * N + offset, dtype=TORCH_DT[dtype], device="cuda")[offset:]
+    rstd = torch.empty(M, dtype=torch.float32, device="cuda") if stats else None
+    p = lambda t: t.data_ptr() if t is not None else None
+    stream = torch.cuda.current_stream().cuda_stream
+    st = rn.add_rms_fwd(p(xt), p(rt), p(gt), p(yt), p(ht), p(rstd), M, N, eps, CODE[dtype], stream)
+    assert st == rn.NORM_OK, f"{rn.STATUS.get(st)}: {rn.norm_status_str(st)} [{rn.norm_last_error()}]"
+    torch.cuda.synchronize()
+    y = to_host(yt, dtype).reshape(M, N)
+    h = to_host(ht, dtype).reshape(M, N)
+    r = rstd.cpu().numpy() if rstd is not None else None
+    return y, h, r

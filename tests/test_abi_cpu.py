@@ -26,7 +26,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["ln_fwd", "norm_describe", "norm_last_error", "norm_status_str", "rms_fwd"]
+    assert declared_functions() == ["add_rms_fwd", "ln_fwd", "norm_describe", "norm_last_error",
+                                    "norm_status_str", "rms_fwd"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -102,6 +103,46 @@ def test_validation_paths(op):
     assert call(op, y=X) == ALIAS                       # in place
     assert call(op, rstd=Y + 16) == ALIAS               # stats inside y
     assert call(op, g=Y + 4) == ALIAS                   # gamma inside y
+
+
+R, H = 0x700000, 0x800000
+
+
+def call_add(x=X, r=R, g=G, y=Y, h=H, rstd=RSTD, M=4, N=64, eps=1e-6, dtype=0):
+    return rn.add_rms_fwd(x, r, g, y, h, rstd, M, N, eps, dtype, None)
+
+
+def test_add_rms_validation():
+    assert call_add(dtype=5) == BAD_DTYPE
+    assert call_add(N=0) == BAD_SHAPE
+    assert call_add(eps=-1.0) == BAD_EPS
+    assert call_add(M=0, x=None, r=None, y=None, h=None) == OK
+    assert call_add(r=None) == NULL_ARG
+    assert call_add(h=None) == NULL_ARG
+    assert call_add(x=None) == NULL_ARG
+    assert call_add(r=R + 2) == BAD_ARG                 # misaligned residual
+    assert call_add(h=H + 2) == BAD_ARG
+    assert call_add(y=X + 64) == ALIAS                  # partial overlap is never allowed
+    assert call_add(h=R + 16) == ALIAS
+    assert call_add(h=Y) == ALIAS                       # the two outputs
+    assert call_add(y=R + 4) == ALIAS
+    assert call_add(g=H + 8) == ALIAS
+    assert call_add(rstd=H) == ALIAS
+
+
+def test_add_rms_exact_in_place_passes_validation():
+    # y over x and the sum over the residual (exactly the same pointers) are
+    # allowed; without a GPU the call then fails at the first HIP call
+    for kw in (dict(y=X), dict(h=R), dict(y=X, h=R), dict(y=R, h=X)):
+        st = call_add(**kw)
+        assert st not in (ALIAS, BAD_ARG, NULL_ARG), (kw, st)
+
+
+def test_add_rms_plans_like_rms():
+    for N in (1024, 2048, 8192, 16384, 1 << 20):
+        a = parse(rn.norm_describe("add_rms", 64, N, "bf16"))
+        b = parse(rn.norm_describe("rms", 64, N, "bf16"))
+        assert a == b, (N, a, b)
 
 
 def test_rms_rejects_beta_and_mean():

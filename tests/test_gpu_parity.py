@@ -44,6 +44,22 @@ def compare(op, dtype, x, gamma, beta, eps, y, mean, rstd, rows=None, what=""):
     return out
 
 
+def compare_add(dtype, x, res, gamma, eps, y, h, rstd, rows=None, what=""):
+    """Residual add + RMSNorm: the stored sum h bit for bit, y and rstd to
+    the same bar as rms_fwd."""
+    xs = x if rows is None else x[rows]
+    rs = res if rows is None else res[rows]
+    hr, yr, rr = oracle.add_rms_fwd(xs, rs, gamma, dtype, eps)
+    hs = h if rows is None else h[rows]
+    bad = hs.view(np.uint8).reshape(hs.shape[0], -1) != hr.view(np.uint8).reshape(hr.shape[0], -1)
+    assert not bad.any(), f"{what}: residual sum differs from the oracle at {np.argwhere(bad)[:4].tolist()}"
+    ys = y if rows is None else y[rows]
+    out = parity.check_y(ys, yr, dtype, what)
+    if rstd is not None:
+        out.update(parity.check_stats(None, rstd if rows is None else rstd[rows], None, rr, eps, what))
+    return out
+
+
 def sample_rows(M, n=256, seed=0, extra=()):
     rng = np.random.default_rng(seed)
     rows = set(range(min(4, M))) | set(range(max(0, M - 4), M)) | set(extra)
@@ -60,6 +76,13 @@ def test_measured_configuration(name):
     w = workloads.CONFIGS[name]
     print(f"[gpu] config {name}: {w.op} {w.dtype} M={w.M} N={w.N}", flush=True)
     inp = workloads.generate(name)
+    if w.op == "add_rms":
+        y, h, rstd = gpu_runner.run_add(w.dtype, inp["x"], inp["res"], inp["gamma"], w.eps)
+        rows = sample_rows(w.M, 256, seed=w.seed)
+        st = compare_add(w.dtype, inp["x"], inp["res"], inp["gamma"], w.eps, y, h, rstd, rows, name)
+        parity.check_stress_invariants(rstd, y, w.dtype, w.eps, name)
+        print(f"[gpu] {name}: {st}", flush=True)
+        return
     y, mean, rstd = run(w.op, w.dtype, inp["x"], inp["gamma"], inp["beta"], w.eps)
     extra = ()
     if "big_rows" in inp:
@@ -319,6 +342,95 @@ def test_single_pass_split_bounded_wait(monkeypatch):
     monkeypatch.delenv("MI355NORM_FORCE_TIMEOUT")
     y, mean, rstd = run("ln", "bf16", inp["x"], inp["gamma"], inp["beta"], 1e-5)
     compare("ln", "bf16", inp["x"], inp["gamma"], inp["beta"], 1e-5, y, mean, rstd, what="after timeout")
+
+
+# ---------------------------------------------------------------------------
+# residual add + RMSNorm
+# ---------------------------------------------------------------------------
+
+def add_inputs(dtype, M, N, seed):
+    return workloads.gen_add_rms(seed, M, N, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("N", EDGE_N)
+def test_add_rms_edge_shapes(dtype, N):
+    M = 37 if N <= 8192 else 5
+    print(f"[gpu] add_rms {dtype} M={M} N={N}", flush=True)
+    inp = add_inputs(dtype, M, N, seed=N + 7)
+    y, h, rstd = gpu_runner.run_add(dtype, inp["x"], inp["res"], inp["gamma"], 1e-6)
+    compare_add(dtype, inp["x"], inp["res"], inp["gamma"], 1e-6, y, h, rstd, what=f"add_rms N={N}")
+
+
+@pytest.mark.parametrize("dtype,N", [("bf16", 4096), ("f32", 3000), ("bf16", 300000), ("f16", 20000)])
+def test_add_rms_in_place(dtype, N):
+    """y written over x and the sum over the residual give the same bits as
+    separate buffers (rows, split and element-wise paths)."""
+    M = 6
+    print(f"[gpu] add_rms in place {dtype} M={M} N={N}", flush=True)
+    inp = add_inputs(dtype, M, N, seed=N + 8)
+    a = gpu_runner.run_add(dtype, inp["x"], inp["res"], inp["gamma"], 1e-6)
+    b = gpu_runner.run_add(dtype, inp["x"], inp["res"], inp["gamma"], 1e-6, inplace=True)
+    for u, v in zip(a, b):
+        assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
+    compare_add(dtype, inp["x"], inp["res"], inp["gamma"], 1e-6, *b, what="in place")
+
+
+@pytest.mark.parametrize("mode", ["split2", "splitcoop"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [1000, 8192, 65544, 300000])
+def test_add_rms_forced_split(monkeypatch, dtype, N, mode):
+    monkeypatch.setenv("MI355NORM_PATH", mode)
+    M = 9
+    print(f"[gpu] add_rms {mode} {dtype} M={M} N={N}", flush=True)
+    inp = add_inputs(dtype, M, N, seed=N + 9)
+    y, h, rstd = gpu_runner.run_add(dtype, inp["x"], inp["res"], inp["gamma"], 1e-6)
+    compare_add(dtype, inp["x"], inp["res"], inp["gamma"], 1e-6, y, h, rstd, what=f"add_rms {mode} N={N}")
+    yi, hi, ri = gpu_runner.run_add(dtype, inp["x"], inp["res"], inp["gamma"], 1e-6, inplace=True)
+    assert np.array_equal(yi.view(np.uint8), y.view(np.uint8)) and np.array_equal(hi.view(np.uint8), h.view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_add_rms_unaligned_and_optional(dtype):
+    M, N = 23, 4096
+    inp = add_inputs(dtype, M, N, seed=31)
+    y, h, rstd = gpu_runner.run_add(dtype, inp["x"], inp["res"], inp["gamma"], 1e-6, offset=1)
+    compare_add(dtype, inp["x"], inp["res"], inp["gamma"], 1e-6, y, h, rstd, what="add_rms unaligned")
+    y2, h2, r2 = gpu_runner.run_add(dtype, inp["x"], inp["res"], None, 1e-6, stats=False)
+    compare_add(dtype, inp["x"], inp["res"], None, 1e-6, y2, h2, None, what="add_rms no gamma")
+    assert r2 is None
+
+
+def test_add_rms_cancellation_and_bitwise_determinism():
+    """Residuals that cancel x exactly (h = 0 rows, eps > 0) and rows whose
+    sums all need rounding; two calls give the same bits."""
+    M, N = 8, 2048
+    inp = add_inputs("bf16", M, N, seed=33)
+    res = inp["res"].copy()
+    res[0] = inp["x"][0] ^ np.uint16(0x8000)            # -x: the sum is exactly zero
+    a = gpu_runner.run_add("bf16", inp["x"], res, inp["gamma"], 1e-6)
+    b = gpu_runner.run_add("bf16", inp["x"], res, inp["gamma"], 1e-6)
+    for u, v in zip(a, b):
+        assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
+    compare_add("bf16", inp["x"], res, inp["gamma"], 1e-6, *a, what="cancellation")
+    assert np.all(oracle.widen(a[1][0], "bf16") == 0.0)
+
+
+def test_fused_add_rms_norm_tensor_api():
+    import rmsnorm_forward_amd as rn
+    inp = add_inputs("bf16", 2 * 5 * 3, 1024, seed=35)
+    xt = gpu_runner.to_device(inp["x"], "bf16").view(2, 5, 3, 1024)
+    rt = gpu_runner.to_device(inp["res"], "bf16").view(2, 5, 3, 1024)
+    gt = gpu_runner.to_device(inp["gamma"], "bf16")
+    y, h, rstd = rn.fused_add_rms_norm(xt, rt, gt, eps=1e-6)
+    assert y.shape == xt.shape and h.shape == xt.shape and rstd.shape == (30,)
+    yh = gpu_runner.to_host(y.reshape(30, 1024), "bf16")
+    hh = gpu_runner.to_host(h.reshape(30, 1024), "bf16")
+    compare_add("bf16", inp["x"], inp["res"], inp["gamma"], 1e-6, yh, hh, rstd.cpu().numpy(), what="tensor api")
+    y2, h2, _ = rn.fused_add_rms_norm(xt, rt, gt, eps=1e-6, inplace=True)
+    assert y2.data_ptr() == xt.data_ptr() and h2.data_ptr() == rt.data_ptr()
+    assert np.array_equal(gpu_runner.to_host(xt.reshape(30, 1024), "bf16"), yh)
+    assert np.array_equal(gpu_runner.to_host(rt.reshape(30, 1024), "bf16"), hh)
 
 
 def test_m_zero_launches_nothing():

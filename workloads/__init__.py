@@ -108,6 +108,17 @@ def gen_rms_uniform(seed: int, M: int, N: int, dtype: str):
     return {"x": to_storage(x, dtype), "gamma": to_storage(w, dtype), "beta": None}
 
 
+def gen_add_rms(seed: int, M: int, N: int, dtype: str):
+    """Residual add + RMSNorm inputs: x ~ U(-1, 1) (a sublayer's output),
+    residual ~ N(0, 1) (the residual stream), weight ~ U(0, 1)."""
+    rng = np.random.default_rng(seed)
+    x = uniform(rng, (M, N), -1.0, 1.0)
+    res = normal(rng, (M, N), 0.0, 1.0)
+    w = uniform(rng, (N,), 0.0, 1.0)
+    return {"x": to_storage(x, dtype), "res": to_storage(res, dtype), "gamma": to_storage(w, dtype),
+            "beta": None}
+
+
 def gen_ln_stress(seed: int, M: int, N: int, dtype: str, row_frac: float = 0.1,
                   chan_frac: float = 0.001, big_mean: float = 1000.0,
                   big_sd: float = 1e-2, outlier_scale: float = 100.0):
@@ -151,13 +162,13 @@ def check_row_f32() -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
-# the five measured configurations
+# the five measured configurations, and the residual-add follow-on
 # --------------------------------------------------------------------------
 
 @dataclass(frozen=True)
 class Workload:
     name: str
-    op: str          # "ln" or "rms"
+    op: str          # "ln", "rms" or "add_rms" (residual add, then RMSNorm)
     dtype: str       # "f32", "bf16", "f16"
     M: int
     N: int
@@ -171,9 +182,10 @@ class Workload:
 
     def ideal_bytes(self, with_stats: bool = True) -> int:
         """Bytes the method must move: x read once, y written once, gamma
-        (and beta for LN) read once, fp32 mean+rstd (LN) or rstd (RMS)."""
+        (and beta for LN) read once, fp32 mean+rstd (LN) or rstd (RMS); with
+        the residual add also the residual read once and the sum written once."""
         e = self.elem_bytes
-        b = 2 * self.M * self.N * e
+        b = (4 if self.op == "add_rms" else 2) * self.M * self.N * e
         b += self.N * e * (2 if self.op == "ln" else 1)
         if with_stats:
             b += self.M * (8 if self.op == "ln" else 4)
@@ -202,6 +214,9 @@ CONFIGS = {
     "ln_bf16_64x1048576": Workload(
         "ln_bf16_64x1048576", "ln", "bf16", 64, 1048576, 1e-5, 1005,
         "x~N(3,2), gamma~U(0.5,1.5), beta~N(0,0.1); second draw of seed 1005"),
+    "add_rms_bf16_16384x8192": Workload(
+        "add_rms_bf16_16384x8192", "add_rms", "bf16", 16384, 8192, 1e-6, 1006,
+        "x~U(-1,1), residual~N(0,1), weight~U(0,1); residual add then RMSNorm"),
 }
 
 
@@ -221,4 +236,6 @@ def generate(name: str) -> dict:
         a = CONFIGS["ln_bf16_4096x5120"]
         gen_ln_normal(0, a.M, a.N, a.dtype, loc=3.0, scale=2.0, rng=rng)   # first draw
         return gen_ln_normal(0, w.M, w.N, w.dtype, loc=3.0, scale=2.0, rng=rng)
+    if name == "add_rms_bf16_16384x8192":
+        return gen_add_rms(w.seed, w.M, w.N, w.dtype)
     raise KeyError(name)
