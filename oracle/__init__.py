@@ -81,6 +81,8 @@ class Oracle:
         lib.oracle_add_rms_fwd.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64,
                                            ctypes.c_double, vp, vp, vp]
         lib.oracle_add_rms_fwd.restype = ctypes.c_int
+        lib.oracle_quant_e4m3.argtypes = [vp, i64, ctypes.c_double, vp]
+        lib.oracle_quant_e4m3.restype = None
         lib.oracle_round.argtypes = [vp, i64, ctypes.c_int, vp]
         lib.oracle_round.restype = None
         lib.oracle_widen.argtypes = [vp, i64, ctypes.c_int, vp]
@@ -137,6 +139,24 @@ class Oracle:
             raise ValueError("oracle_add_rms_fwd rejected its arguments")
         return h, y, rstd
 
+    def quant_e4m3(self, v, scale: float):
+        """OCP E4M3 codes (uint8) of v / scale, saturated to +-448, RNE."""
+        v = np.ascontiguousarray(v, dtype=np.float64)
+        out = np.empty(v.shape, np.uint8)
+        self.lib.oracle_quant_e4m3(_ptr(v), v.size, float(np.float32(scale)), _ptr(out))
+        return out
+
+    def rms_fp8_fwd(self, x, gamma, dtype: str, eps: float, scale: float):
+        """RMSNorm with FP8 output -> (codes uint8, y float64 before
+        quantisation, rstd)."""
+        y, rstd = self.rms_fwd(x, gamma, dtype, eps)
+        return self.quant_e4m3(y, scale), y, rstd
+
+    def add_rms_fp8_fwd(self, x, res, gamma, dtype: str, eps: float, scale: float):
+        """Residual add + RMSNorm with FP8 output -> (h, codes, y, rstd)."""
+        h, y, rstd = self.add_rms_fwd(x, res, gamma, dtype, eps)
+        return h, self.quant_e4m3(y, scale), y, rstd
+
     def round_to(self, v, dtype: str):
         """Round float64 values to storage `dtype`, direct round-to-nearest-even."""
         v = np.ascontiguousarray(v, dtype=np.float64)
@@ -174,6 +194,18 @@ def rms_fwd(x, gamma, dtype: str, eps: float):
 
 def add_rms_fwd(x, res, gamma, dtype: str, eps: float):
     return default().add_rms_fwd(x, res, gamma, dtype, eps)
+
+
+def quant_e4m3(v, scale: float):
+    return default().quant_e4m3(v, scale)
+
+
+def rms_fp8_fwd(x, gamma, dtype: str, eps: float, scale: float):
+    return default().rms_fp8_fwd(x, gamma, dtype, eps, scale)
+
+
+def add_rms_fp8_fwd(x, res, gamma, dtype: str, eps: float, scale: float):
+    return default().add_rms_fp8_fwd(x, res, gamma, dtype, eps, scale)
 
 
 def round_to(v, dtype: str):

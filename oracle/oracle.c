@@ -27,6 +27,12 @@
  *                 fused_add_rms_norm: read as exactly what a separate add
  *                 (whose rounded sum is stored as the new residual) followed by
  *                 RMSNorm of that stored sum computes.
+ *   FP8 output -- "CUDA 算子工程" ch. 7, section 7.9: the norm fused with the
+ *                 quantisation of its output for the next GEMM (vLLM's
+ *                 rms_norm_static_fp8_quant and its fused-add variant): read
+ *                 as code = FP8(clamp(y / scale, +-max)) with one static fp32
+ *                 scale per call, FP8 being OCP E4M3 (the format gfx950
+ *                 converts to natively), round-to-nearest-even.
  *   Output rounding -- round-to-nearest-even from the double result straight
  *                 to the storage type (no intermediate float rounding).  The
  *                 pages only say the result is cast to the output dtype
@@ -267,4 +273,38 @@ int oracle_add_rms_fwd(const void *x, const void *res, const void *gamma, int dt
         oracle_round(&s, 1, dtype, (char *)h + i * elem_size(dtype));
     }
     return oracle_rms_fwd(h, gamma, dtype, M, N, eps, y, rstd);
+}
+
+/* ---- FP8 (OCP E4M3) output ------------------------------------------------
+ *
+ * E4M3: 1 sign bit, 4 exponent bits (bias 7), 3 fraction bits; normal
+ * values (1 + f/8) * 2^(e - 7) for e = 1..15 except the all-ones pattern
+ * S.1111.111 (NaN); subnormals (f/8) * 2^-6; no infinities; largest finite
+ * value 448.  Quantisation divides by the static scale, saturates to
+ * +-448, rounds to nearest even; NaN stays NaN.
+ */
+static uint8_t double_to_e4m3_code(double v)
+{
+    if (isnan(v))
+        return 0x7f;
+    uint8_t sign = signbit(v) ? 0x80 : 0;
+    double a = fabs(v);
+    if (a > 448.0)
+        a = 448.0;
+    double r = rne_to_format(a, 4, -6);
+    if (r == 0.0)
+        return sign;
+    int e;
+    frexp(r, &e);                        /* r in [2^(e-1), 2^e) */
+    if (e - 1 < -6)                      /* subnormal: r = f * 2^-9 */
+        return (uint8_t)(sign | (uint8_t)ldexp(r, 9));
+    uint8_t f = (uint8_t)(ldexp(r, 3 - (e - 1)) - 8.0);    /* r / 2^(e-1) = 1 + f/8 */
+    return (uint8_t)(sign | (uint8_t)((e - 1 + 7) << 3) | f);
+}
+
+/* code[i] = E4M3(clamp(v[i] / scale)) for n doubles. */
+void oracle_quant_e4m3(const double *v, int64_t n, double scale, uint8_t *code)
+{
+    for (int64_t i = 0; i < n; ++i)
+        code[i] = double_to_e4m3_code(v[i] / scale);
 }

@@ -397,7 +397,7 @@ def pin_round_f16_f32(orc):
 # residual add + RMSNorm
 # --------------------------------------------------------------------------
 
-FORMATS = {"f32": (24, -126), "bf16": (8, -126), "f16": (11, -14)}
+FORMATS = {"f32": (24, -126), "bf16": (8, -126), "f16": (11, -14), "e4m3": (4, -6)}
 
 
 def round_fraction(v: Fraction, dtype: str) -> Fraction:
@@ -520,6 +520,100 @@ def pin_add_rms_library(orc):
         assert np.max(np.abs(y - yt)) <= 1e-12, dtype
 
 
+# --------------------------------------------------------------------------
+# FP8 (OCP E4M3) output
+# --------------------------------------------------------------------------
+
+def e4m3_value(code: int) -> float:
+    """Value of an E4M3 code from the format's definition (NaN for
+    S.1111.111): sign, 4-bit exponent with bias 7, 3-bit fraction."""
+    s = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    f = code & 7
+    if e == 0xF and f == 7:
+        return float("nan")
+    if e == 0:
+        return s * f / 8.0 * 2.0 ** -6
+    return s * (1.0 + f / 8.0) * 2.0 ** (e - 7)
+
+
+def e4m3_exact_code(v: Fraction) -> int:
+    """Code of the saturated, round-to-nearest-even E4M3 value of a rational."""
+    a = min(abs(v), Fraction(448))
+    r = round_fraction(a, "e4m3")
+    sign = 0x80 if v < 0 else 0
+    for c in range(0x7F):                  # the 127 non-negative finite codes
+        if Fraction(e4m3_value(c)) == r:
+            return sign | c
+    raise AssertionError(v)
+
+
+def pin_e4m3_quantisation(orc):
+    """Every code maps back to itself; midpoints between neighbours go to the
+    even code; values past 448 saturate; the scale divides; NaN stays NaN;
+    in-range values agree with torch's float8_e4m3fn conversion."""
+    import torch
+    vals = np.array([e4m3_value(c) for c in range(256)])
+    codes = orc.quant_e4m3(vals, 1.0)
+    for c in range(256):
+        if np.isnan(vals[c]):
+            assert codes[c] in (0x7F, 0xFF)
+        else:
+            assert codes[c] == c, (hex(c), hex(codes[c]))
+    pos = [e4m3_value(c) for c in range(0x7F)]
+    mids = np.array([(pos[i] + pos[i + 1]) / 2 for i in range(len(pos) - 1)])
+    got = orc.quant_e4m3(mids, 1.0)
+    for i, g in enumerate(got):
+        assert g == (i if i % 2 == 0 else i + 1), (i, mids[i], hex(g))
+    got = orc.quant_e4m3(np.nextafter(mids, np.inf), 1.0)
+    assert np.array_equal(got, np.arange(1, 0x7F))
+    got = orc.quant_e4m3(-np.nextafter(mids, 0), 1.0)
+    assert np.array_equal(got, 0x80 | np.arange(0, 0x7E))
+    big = orc.quant_e4m3(np.array([448.0, 463.9, 464.0, 1e6, np.inf, -500.0, -np.inf]), 1.0)
+    assert list(big) == [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE]
+    assert orc.quant_e4m3(np.array([np.nan]), 1.0)[0] == 0x7F
+    rng = np.random.default_rng(41)
+    v = rng.standard_normal(5000) * np.exp2(rng.integers(-12, 8, 5000))
+    for scale in (1.0, 0.0625, 3.0):
+        got = orc.quant_e4m3(v, scale)
+        w = torch.from_numpy(v / float(np.float32(scale)))
+        ok = w.abs() <= 448
+        ref = w[ok].to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(got[ok.numpy()], ref), scale
+    two = orc.quant_e4m3(v, 2.0)
+    assert np.array_equal(two, orc.quant_e4m3(v / 2.0, 1.0))
+
+
+def pin_rms_fp8_brute_force(orc):
+    """Codes of the exact RMSNorm output divided by the scale, saturated and
+    rounded exactly, on tiny rows (both with and without the residual add)."""
+    for dtype, x, gm, _, eps in _tiny_cases(seed=43):
+        xs_all = exact_values(x, dtype)
+        gs = exact_values(gm, dtype)
+        n = x.shape[1]
+        e = Fraction(float(np.float32(eps)))
+        for scale in (0.01, 1.0, 0.3):
+            sc = Fraction(float(np.float32(scale)))
+            q, y, rstd = orc.rms_fp8_fwd(x, gm, dtype, eps, scale)
+            for r in range(x.shape[0]):
+                xs = xs_all[r * n:(r + 1) * n]
+                _, rs, yb = brute_rms_row(xs, gs, e)
+                for i in range(n):
+                    want = e4m3_exact_code(Fraction(yb[i]) / sc)
+                    assert q[r, i] == want or (want & 0x7F) == 0 and (q[r, i] & 0x7F) == 0, \
+                        (dtype, n, r, i, hex(q[r, i]), hex(want))
+    for dtype, x, res, gm, eps in _add_cases(seed=45):
+        h, q, y, rstd = orc.add_rms_fp8_fwd(x, res, gm, dtype, eps, 0.05)
+        hs = exact_values(h, dtype)
+        gs = exact_values(gm, dtype)
+        n = x.shape[1]
+        for r in range(x.shape[0]):
+            _, rs, yb = brute_rms_row(hs[r * n:(r + 1) * n], gs, Fraction(float(np.float32(eps))))
+            for i in range(n):
+                want = e4m3_exact_code(Fraction(yb[i]) / Fraction(float(np.float32(0.05))))
+                assert q[r, i] == want, (dtype, n, r, i)
+
+
 ALL_PINS = [
     pin_large_mean_row_decimal,
     pin_large_mean_row_fp32,
@@ -536,4 +630,6 @@ ALL_PINS = [
     pin_add_rms_brute_force,
     pin_add_rms_reduces_to_rms,
     pin_add_rms_library,
+    pin_e4m3_quantisation,
+    pin_rms_fp8_brute_force,
 ]

@@ -60,6 +60,11 @@ MUTANTS = {
                              "double s = load_elem(x, i, dtype) + 0.0 * load_elem(res, i, dtype);"),
     "add_rms_norm_of_unrounded_sum": ("return oracle_rms_fwd(h, gamma, dtype, M, N, eps, y, rstd);",
                                       UNROUNDED_NORM),
+    "fp8_scale_multiplies": ("double_to_e4m3_code(v[i] / scale)", "double_to_e4m3_code(v[i] * scale)"),
+    "fp8_no_saturation": ("    if (a > 448.0)\n        a = 448.0;\n", ""),
+    "fp8_exponent_bias_8": ("(e - 1 + 7) << 3", "(e - 1 + 8) << 3"),
+    "fp8_subnormal_threshold": ("if (e - 1 < -6)", "if (e - 1 < -7)"),
+    "fp8_precision_off_by_one": ("rne_to_format(a, 4, -6)", "rne_to_format(a, 3, -6)"),
     "add_rms_wrong_operand": ("double s = load_elem(x, i, dtype) + load_elem(res, i, dtype);",
                               "double s = load_elem(x, i, dtype) + load_elem(x, i, dtype);"),
 }
