@@ -29,6 +29,14 @@
  *       y[r,i] = RMSNorm(h)[r,i], taken of the stored h
  *     Read as exactly what a separate add followed by rms_fwd computes.
  *
+ *   FP8 output (the norm fused with the quantisation of its output for the
+ *   next GEMM, "CUDA 算子工程" ch. 7, section 7.9: vLLM's static FP8
+ *   variants of rms_norm and fused_add_rms_norm), per element:
+ *       code = E4M3(clamp(y / scale, -448, 448))
+ *     y as above, computed in fp32; E4M3 = OCP FP8 E4M3 (1 sign, 4 exponent
+ *     bits with bias 7, 3 fraction bits, no infinities, max 448, NaN =
+ *     S.1111.111), round-to-nearest-even, one byte per element.
+ *
  * The variance is computed by a stable method (two passes over register-
  * resident data for rows that fit one workgroup, Chan's parallel merge of
  * (n, mean, M2) partials for rows split across workgroups), never by
@@ -93,7 +101,8 @@ typedef enum {
     NORM_ERR_BAD_SHAPE = 2,  /* M < 0, N < 1, N > 2^24, or M * N overflows       */
     NORM_ERR_BAD_DTYPE = 3,  /* dtype not in norm_dtype                          */
     NORM_ERR_BAD_EPS = 4,    /* eps negative, NaN or infinite                    */
-    NORM_ERR_BAD_ARG = 5,    /* misaligned pointer; beta or mean given to rms_fwd */
+    NORM_ERR_BAD_ARG = 5,    /* misaligned pointer; beta or mean given to an
+                                RMSNorm; a bad FP8 scale                      */
     NORM_ERR_ALIAS = 6,      /* two of the buffers overlap                       */
     NORM_ERR_HIP = 7         /* a HIP runtime call or kernel launch failed       */
 } norm_status;
@@ -124,6 +133,26 @@ int add_rms_fwd(const void *x, const void *residual, const void *gamma, void *y,
                 void *residual_out, float *rstd, int64_t M, int64_t N, float eps,
                 int dtype, void *stream);
 
+/*
+ * RMSNorm with FP8 E4M3 output.  y: [M, N] bytes (E4M3 codes); scale: the
+ * static dequantisation scale (finite, > 0, with 1/scale finite, else
+ * NORM_ERR_BAD_ARG); the codes are of y_norm / scale.  No in-place use.  A
+ * result of exactly zero may be coded as +0 or -0.  Other conventions as for
+ * rms_fwd.  Returns a norm_status.
+ */
+int rms_fp8_fwd(const void *x, const void *gamma, void *y, float *rstd,
+                int64_t M, int64_t N, float eps, float scale, int dtype, void *stream);
+
+/*
+ * Residual add, then RMSNorm with FP8 E4M3 output: residual_out receives
+ * x + residual in `dtype` (it may be residual itself), y the E4M3 codes of
+ * the norm of it divided by scale.  Other conventions as for add_rms_fwd and
+ * rms_fp8_fwd.  Returns a norm_status.
+ */
+int add_rms_fp8_fwd(const void *x, const void *residual, const void *gamma, void *y,
+                    void *residual_out, float *rstd, int64_t M, int64_t N, float eps,
+                    float scale, int dtype, void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *norm_status_str(int status);
 
@@ -139,8 +168,9 @@ const char *norm_last_error(void);
  * Describe, without launching anything, how a call with these arguments
  * would be executed: path ("rows" or "split"), lanes per row, 16-byte vectors
  * per lane, workgroup size, grid size, and the vector width.  `op` is 0 for
- * LayerNorm, 1 for RMSNorm, 2 for residual add + RMSNorm; `aligned` says
- * whether every pointer is 16-byte aligned.  Writes at most buflen bytes (NUL-terminated) into buf and
+ * LayerNorm, 1 for RMSNorm, 2 for residual add + RMSNorm, 3 and 4 for the
+ * same two RMSNorms with FP8 output; `aligned` says whether every pointer is
+ * 16-byte aligned.  Writes at most buflen bytes (NUL-terminated) into buf and
  * returns a norm_status.  For tests and the benchmark's reports.
  */
 int norm_describe(int op, int64_t M, int64_t N, int dtype, int aligned,

@@ -5,11 +5,12 @@ Every step of the computation runs in the library's HIP kernels; this module
 only marshals arguments.  PyTorch is used for device memory and streams.
 
 Two layers:
-  * ln_fwd / rms_fwd / add_rms_fwd / norm_status_str / norm_last_error /
-    norm_describe -- the C ABI entry points under the same names, taking raw
-    device addresses (ints) and returning the status code;
-  * layer_norm / rms_norm / fused_add_rms_norm -- the same calls on torch
-    tensors: they allocate
+  * ln_fwd / rms_fwd / add_rms_fwd / rms_fp8_fwd / add_rms_fp8_fwd /
+    norm_status_str / norm_last_error / norm_describe -- the C ABI entry
+    points under the same names, taking raw device addresses (ints) and
+    returning the status code;
+  * layer_norm / rms_norm / fused_add_rms_norm / rms_norm_fp8 /
+    fused_add_rms_norm_fp8 -- the same calls on torch tensors: they allocate
     y (and fp32 mean / rstd), pass the current stream, and raise
     RuntimeError with the library's message on a non-zero status.
 
@@ -47,6 +48,10 @@ for _name in ("ln_fwd", "rms_fwd"):
     _fn.restype = _int
 _lib.add_rms_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _int, _vp]
 _lib.add_rms_fwd.restype = _int
+_lib.rms_fp8_fwd.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _f32, _int, _vp]
+_lib.rms_fp8_fwd.restype = _int
+_lib.add_rms_fp8_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _f32, _int, _vp]
+_lib.add_rms_fp8_fwd.restype = _int
 _lib.norm_status_str.argtypes = [_int]
 _lib.norm_status_str.restype = ctypes.c_char_p
 _lib.norm_last_error.argtypes = []
@@ -88,6 +93,19 @@ def add_rms_fwd(x, residual, gamma, y, residual_out, rstd, M, N, eps, dtype, str
                             _addr(rstd), int(M), int(N), float(eps), int(dtype), _addr(stream))
 
 
+def rms_fp8_fwd(x, gamma, y, rstd, M, N, eps, scale, dtype, stream) -> int:
+    """RMSNorm with FP8 (E4M3) output on device addresses; returns the status."""
+    return _lib.rms_fp8_fwd(_addr(x), _addr(gamma), _addr(y), _addr(rstd), int(M), int(N), float(eps),
+                            float(scale), int(dtype), _addr(stream))
+
+
+def add_rms_fp8_fwd(x, residual, gamma, y, residual_out, rstd, M, N, eps, scale, dtype, stream) -> int:
+    """Residual add + RMSNorm with FP8 (E4M3) output on device addresses."""
+    return _lib.add_rms_fp8_fwd(_addr(x), _addr(residual), _addr(gamma), _addr(y), _addr(residual_out),
+                                _addr(rstd), int(M), int(N), float(eps), float(scale), int(dtype),
+                                _addr(stream))
+
+
 def norm_status_str(status: int) -> str:
     return _lib.norm_status_str(int(status)).decode()
 
@@ -99,7 +117,7 @@ def norm_last_error() -> str:
 
 def norm_describe(op: str, M: int, N: int, dtype, aligned: bool = True) -> str:
     """How the library would run this call (path, tile, grid); launches nothing."""
-    code = {"ln": 0, "rms": 1, "add_rms": 2}[op]
+    code = {"ln": 0, "rms": 1, "add_rms": 2, "rms_fp8": 3, "add_rms_fp8": 4}[op]
     dt = DTYPE_NAMES.get(dtype, dtype)
     buf = ctypes.create_string_buffer(256)
     st = _lib.norm_describe(code, int(M), int(N), int(dt), int(bool(aligned)), buf, 256)
@@ -204,6 +222,55 @@ def fused_add_rms_norm(x, residual, gamma=None, eps: float = 1e-6, inplace: bool
     return y.view(x.shape), h.view(x.shape), rstd
 
 
-__all__ = ["ln_fwd", "rms_fwd", "add_rms_fwd", "norm_status_str", "norm_last_error", "norm_describe",
-           "layer_norm", "rms_norm", "fused_add_rms_norm",
+def _fp8_tensor(shape, device):
+    import torch
+    return torch.empty(shape, dtype=torch.uint8, device=device)
+
+
+def rms_norm_fp8(x, gamma=None, scale: float = 1.0, eps: float = 1e-6, want_rstd: bool = True):
+    """RMSNorm over the last dimension with FP8 E4M3 output of y / scale.
+    Returns (codes, rstd); codes is a torch.float8_e4m3fn tensor of x's shape."""
+    import torch
+    N = x.shape[-1]
+    x2 = x.reshape(-1, N).contiguous()
+    M = x2.shape[0]
+    g = _param(gamma, N, x)
+    y = _fp8_tensor(x2.shape, x.device)
+    rstd = torch.empty(M, device=x.device, dtype=torch.float32) if want_rstd else None
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        _check(rms_fp8_fwd(x2.data_ptr(), g.data_ptr() if g is not None else None, y.data_ptr(),
+                           rstd.data_ptr() if rstd is not None else None, M, N, eps, scale,
+                           _torch_dtype_code(x2), stream))
+    return y.view(torch.float8_e4m3fn).view(x.shape), rstd
+
+
+def fused_add_rms_norm_fp8(x, residual, gamma=None, scale: float = 1.0, eps: float = 1e-6,
+                           inplace: bool = False, want_rstd: bool = True):
+    """h = x + residual, then RMSNorm of h with FP8 E4M3 output of y / scale.
+    Returns (codes, h, rstd); with inplace=True h is written into residual."""
+    import torch
+    N = x.shape[-1]
+    if residual.shape != x.shape or residual.dtype != x.dtype or residual.device != x.device:
+        raise ValueError("residual must have x's shape, dtype and device")
+    if inplace and not residual.is_contiguous():
+        raise ValueError("inplace=True needs a contiguous residual")
+    x2 = x.reshape(-1, N).contiguous()
+    r2 = residual.reshape(-1, N).contiguous()
+    M = x2.shape[0]
+    g = _param(gamma, N, x)
+    y = _fp8_tensor(x2.shape, x.device)
+    h = r2 if inplace else torch.empty_like(r2)
+    rstd = torch.empty(M, device=x.device, dtype=torch.float32) if want_rstd else None
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        _check(add_rms_fp8_fwd(x2.data_ptr(), r2.data_ptr(), g.data_ptr() if g is not None else None,
+                               y.data_ptr(), h.data_ptr(), rstd.data_ptr() if rstd is not None else None,
+                               M, N, eps, scale, _torch_dtype_code(x2), stream))
+    return y.view(torch.float8_e4m3fn).view(x.shape), h.view(x.shape), rstd
+
+
+__all__ = ["ln_fwd", "rms_fwd", "add_rms_fwd", "rms_fp8_fwd", "add_rms_fp8_fwd", "norm_status_str",
+           "norm_last_error", "norm_describe", "layer_norm", "rms_norm", "fused_add_rms_norm",
+           "rms_norm_fp8", "fused_add_rms_norm_fp8",
            "NORM_F32", "NORM_F16", "NORM_BF16", "NORM_OK", "STATUS", "LIB_PATH"]

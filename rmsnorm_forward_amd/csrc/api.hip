@@ -71,33 +71,40 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
 
 bool misaligned(const void* p, int a) { return p && ((uintptr_t)p % (uintptr_t)a) != 0; }
 
+bool has_add(int op) { return op == OP_ADD_RMS || op == OP_ADD_RMS_Q8; }
+bool has_q8(int op) { return op == OP_RMS_Q8 || op == OP_ADD_RMS_Q8; }
+
 int validate(int op, const void* x, const void* res, const void* gamma, const void* beta, const void* y,
              const void* hout, const float* mean, const float* rstd, int64_t M, int64_t N, float eps,
-             int dtype) {
+             float scale, int dtype) {
     if (dtype != NORM_F32 && dtype != NORM_F16 && dtype != NORM_BF16) return NORM_ERR_BAD_DTYPE;
     if (M < 0 || N < 1 || N > kMaxN) return NORM_ERR_BAD_SHAPE;
     const int e = elem_bytes(dtype);
     if (M > INT64_MAX / N / e) return NORM_ERR_BAD_SHAPE;
     if (!(eps >= 0.0f) || std::isinf(eps)) return NORM_ERR_BAD_EPS;
     if (op != OP_LN && (beta || mean)) return NORM_ERR_BAD_ARG;
+    if (has_q8(op) && !(scale > 0.0f && std::isfinite(scale) && std::isfinite(1.0f / scale)))
+        return NORM_ERR_BAD_ARG;
     if (M == 0) return NORM_OK;
     if (!x || !y) return NORM_ERR_NULL_ARG;
-    if (op == OP_ADD_RMS && (!res || !hout)) return NORM_ERR_NULL_ARG;
-    if (misaligned(x, e) || misaligned(y, e) || misaligned(gamma, e) || misaligned(beta, e) ||
+    if (has_add(op) && (!res || !hout)) return NORM_ERR_NULL_ARG;
+    if (misaligned(x, e) || misaligned(y, has_q8(op) ? 1 : e) || misaligned(gamma, e) || misaligned(beta, e) ||
         misaligned(res, e) || misaligned(hout, e) || misaligned(mean, 4) || misaligned(rstd, 4))
         return NORM_ERR_BAD_ARG;
     const int64_t nx = M * N * e, nv = N * e, ns = M * 4;
+    const int64_t ny = has_q8(op) ? M * N : nx;      // FP8 output: one byte per element
     // in: 0 x, 1 res, 2 gamma, 3 beta;  out: 4 y, 5 hout, 6 mean, 7 rstd
     struct R { const void* p; int64_t n; bool out; } r[8] = {
         {x, nx, false}, {res, nx, false}, {gamma, nv, false}, {beta, nv, false},
-        {y, nx, true}, {hout, nx, true}, {mean, ns, true}, {rstd, ns, true}};
+        {y, ny, true}, {hout, nx, true}, {mean, ns, true}, {rstd, ns, true}};
     for (int i = 0; i < 8; ++i)
         for (int j = i + 1; j < 8; ++j) {
             if (!(r[i].out || r[j].out) || !overlaps(r[i].p, r[i].n, r[j].p, r[j].n)) continue;
-            // the residual add may write y or the sum exactly over x or the
-            // residual: each element is read by the lane that writes it, first
+            // with the residual add, y or the sum may be written exactly over
+            // x or the residual when the element sizes match: each element is
+            // read by the lane that writes it, before it writes
             const bool row_io = (i == 0 || i == 1) && (j == 4 || j == 5);
-            if (op == OP_ADD_RMS && row_io && r[i].p == r[j].p) continue;
+            if (has_add(op) && row_io && r[i].p == r[j].p && r[i].n == r[j].n) continue;
             return NORM_ERR_ALIAS;
         }
     return NORM_OK;
@@ -157,8 +164,8 @@ bool tile_instantiated(int team, int vpl) {
 // present).  Cached per (device, dtype, op, vector width).
 int64_t coop_capacity(int dtype, int op, int epv) {
     static std::mutex mu;
-    static int64_t cache[64][3][3][2];
-    static bool known[64][3][3][2];
+    static int64_t cache[64][3][kOps][2];
+    static bool known[64][3][kOps][2];
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) return 0;
     int dev = 0;
@@ -331,15 +338,17 @@ bool all_aligned16(const void* x, const void* g, const void* b, const void* y, i
 }
 
 int run(int op, const void* x, const void* res, const void* gamma, const void* beta, void* y, void* hout,
-        float* mean, float* rstd, int64_t M, int64_t N, float eps, int dtype, void* stream) {
-    int st = validate(op, x, res, gamma, beta, y, hout, mean, rstd, M, N, eps, dtype);
+        float* mean, float* rstd, int64_t M, int64_t N, float eps, float scale, int dtype, void* stream) {
+    int st = validate(op, x, res, gamma, beta, y, hout, mean, rstd, M, N, eps, scale, dtype);
     if (st != NORM_OK || M == 0) return st;
     const int e = elem_bytes(dtype);
     Plan p;
     const bool aligned = all_aligned16(x, gamma, beta, y, N, e) && all_aligned16(res, hout, nullptr, nullptr, N, e);
     st = make_plan(op, M, N, dtype, aligned, read_overrides(), &p);
     if (st != NORM_OK) return st;
-    NormCall c{x, res, gamma, beta, y, hout, mean, rstd, M, (int)N, eps, (hipStream_t)stream};
+    NormCall c{x, res, gamma, beta, y, hout, mean, rstd, M, (int)N, eps, (hipStream_t)stream,
+               has_q8(op) ? 1.0f / scale : 1.0f};
+    const int ye = has_q8(op) ? 1 : e;    // bytes per element of y
     hipError_t err;
     if (p.path == PATH_ROWS) {
         switch (dtype) {
@@ -375,7 +384,7 @@ int run(int op, const void* x, const void* res, const void* gamma, const void* b
             const int64_t mb = std::min(rows, M - r0);
             NormCall cb = c;
             cb.x = static_cast<const char*>(c.x) + r0 * N * e;
-            cb.y = static_cast<char*>(c.y) + r0 * N * e;
+            cb.y = static_cast<char*>(c.y) + r0 * N * ye;
             if (c.res) cb.res = static_cast<const char*>(c.res) + r0 * N * e;
             if (c.hout) cb.hout = static_cast<char*>(c.hout) + r0 * N * e;
             cb.mean = c.mean ? c.mean + r0 : nullptr;
@@ -401,18 +410,30 @@ extern "C" {
 
 int ln_fwd(const void* x, const void* gamma, const void* beta, void* y, float* mean, float* rstd,
            int64_t M, int64_t N, float eps, int dtype, void* stream) {
-    return run(OP_LN, x, nullptr, gamma, beta, y, nullptr, mean, rstd, M, N, eps, dtype, stream);
+    return run(OP_LN, x, nullptr, gamma, beta, y, nullptr, mean, rstd, M, N, eps, 1.0f, dtype, stream);
 }
 
 int rms_fwd(const void* x, const void* gamma, const void* beta, void* y, float* mean, float* rstd,
             int64_t M, int64_t N, float eps, int dtype, void* stream) {
-    return run(OP_RMS, x, nullptr, gamma, beta, y, nullptr, mean, rstd, M, N, eps, dtype, stream);
+    return run(OP_RMS, x, nullptr, gamma, beta, y, nullptr, mean, rstd, M, N, eps, 1.0f, dtype, stream);
 }
 
 int add_rms_fwd(const void* x, const void* residual, const void* gamma, void* y, void* residual_out,
                 float* rstd, int64_t M, int64_t N, float eps, int dtype, void* stream) {
-    return run(OP_ADD_RMS, x, residual, gamma, nullptr, y, residual_out, nullptr, rstd, M, N, eps, dtype,
+    return run(OP_ADD_RMS, x, residual, gamma, nullptr, y, residual_out, nullptr, rstd, M, N, eps, 1.0f,
+               dtype, stream);
+}
+
+int rms_fp8_fwd(const void* x, const void* gamma, void* y, float* rstd, int64_t M, int64_t N, float eps,
+                float scale, int dtype, void* stream) {
+    return run(OP_RMS_Q8, x, nullptr, gamma, nullptr, y, nullptr, nullptr, rstd, M, N, eps, scale, dtype,
                stream);
+}
+
+int add_rms_fp8_fwd(const void* x, const void* residual, const void* gamma, void* y, void* residual_out,
+                    float* rstd, int64_t M, int64_t N, float eps, float scale, int dtype, void* stream) {
+    return run(OP_ADD_RMS_Q8, x, residual, gamma, nullptr, y, residual_out, nullptr, rstd, M, N, eps, scale,
+               dtype, stream);
 }
 
 const char* norm_status_str(int status) {
@@ -422,7 +443,7 @@ const char* norm_status_str(int status) {
     case NORM_ERR_BAD_SHAPE: return "bad shape: need M >= 0, 1 <= N <= 2^24 and M*N*elem within int64";
     case NORM_ERR_BAD_DTYPE: return "unknown dtype (0 = f32, 1 = f16, 2 = bf16)";
     case NORM_ERR_BAD_EPS: return "eps must be finite and >= 0";
-    case NORM_ERR_BAD_ARG: return "bad argument: misaligned pointer, beta/mean given to rms_fwd, or an unusable override";
+    case NORM_ERR_BAD_ARG: return "bad argument: misaligned pointer, beta/mean given to an RMSNorm, a bad FP8 scale, or an unusable override";
     case NORM_ERR_ALIAS: return "buffers overlap (in-place use is not supported)";
     case NORM_ERR_HIP: return "HIP runtime call or kernel launch failed";
     }
@@ -432,7 +453,7 @@ const char* norm_status_str(int status) {
 const char* norm_last_error(void) { return g_last_error; }
 
 int norm_describe(int op, int64_t M, int64_t N, int dtype, int aligned, char* buf, int buflen) {
-    if (op != OP_LN && op != OP_RMS && op != OP_ADD_RMS) return NORM_ERR_BAD_ARG;
+    if (op < 0 || op >= kOps) return NORM_ERR_BAD_ARG;
     if (dtype != NORM_F32 && dtype != NORM_F16 && dtype != NORM_BF16) return NORM_ERR_BAD_DTYPE;
     if (M < 0 || N < 1 || N > kMaxN) return NORM_ERR_BAD_SHAPE;
     const int e = elem_bytes(dtype);

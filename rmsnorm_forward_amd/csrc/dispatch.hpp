@@ -7,8 +7,10 @@
 
 namespace mi355norm {
 
-// Operations: LayerNorm, RMSNorm, and residual add followed by RMSNorm.
-enum { OP_LN = 0, OP_RMS = 1, OP_ADD_RMS = 2 };
+// Operations: LayerNorm, RMSNorm, residual add followed by RMSNorm, and the
+// two RMSNorm forms with FP8 (E4M3) output.
+enum { OP_LN = 0, OP_RMS = 1, OP_ADD_RMS = 2, OP_RMS_Q8 = 3, OP_ADD_RMS_Q8 = 4 };
+constexpr int kOps = 5;
 
 struct NormCall {
     const void* x;
@@ -23,6 +25,7 @@ struct NormCall {
     int N;
     float eps;
     hipStream_t stream;
+    float qinv;          // FP8 output: 1 / scale
 };
 
 enum { PATH_ROWS = 0, PATH_SPLIT = 1 };

@@ -16,13 +16,15 @@ using St = typename T::storage;
 template <bool B>
 using bc = std::integral_constant<bool, B>;
 
-// Calls f(bc<RMS>, bc<ADD>) for the operation.
+// Calls f(bc<RMS>, bc<ADD>, bc<Q8>) for the operation.
 template <class F>
 hipError_t with_op(int op, F&& f) {
     switch (op) {
-    case OP_LN: return f(bc<false>{}, bc<false>{});
-    case OP_RMS: return f(bc<true>{}, bc<false>{});
-    case OP_ADD_RMS: return f(bc<true>{}, bc<true>{});
+    case OP_LN: return f(bc<false>{}, bc<false>{}, bc<false>{});
+    case OP_RMS: return f(bc<true>{}, bc<false>{}, bc<false>{});
+    case OP_ADD_RMS: return f(bc<true>{}, bc<true>{}, bc<false>{});
+    case OP_RMS_Q8: return f(bc<true>{}, bc<false>{}, bc<true>{});
+    case OP_ADD_RMS_Q8: return f(bc<true>{}, bc<true>{}, bc<true>{});
     }
     return hipErrorInvalidValue;
 }
@@ -40,57 +42,59 @@ hipError_t with_epv(int epv, F&& f) {
 // row kernel
 // ---------------------------------------------------------------------------
 
-template <class T, bool RMS, bool ADD, int TEAM, int VPL, int EPV>
+template <class T, bool RMS, bool ADD, bool Q8, int TEAM, int VPL, int EPV>
 hipError_t go_rows(const NormCall& c, const Plan& p) {
     const St<T>* x = static_cast<const St<T>*>(c.x);
     const St<T>* r = static_cast<const St<T>*>(c.res);
     const St<T>* g = static_cast<const St<T>*>(c.gamma);
     const St<T>* b = static_cast<const St<T>*>(c.beta);
-    St<T>* y = static_cast<St<T>*>(c.y);
+    void* y = c.y;
     St<T>* h = static_cast<St<T>*>(c.hout);
     float* mean = c.mean;
     float* rstd = c.rstd;
     int64_t M = c.M;
     int N = c.N;
     float eps = c.eps;
-    void* args[] = {&x, &r, &g, &b, &y, &h, &mean, &rstd, &M, &N, &eps};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&norm_rows_kernel<T, RMS, ADD, TEAM, VPL, EPV>),
+    float qinv = c.qinv;
+    void* args[] = {&x, &r, &g, &b, &y, &h, &mean, &rstd, &M, &N, &eps, &qinv};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&norm_rows_kernel<T, RMS, ADD, Q8, TEAM, VPL, EPV>),
                            dim3((unsigned)p.grid), dim3(TeamGeom<TEAM>::WG), args, 0, c.stream);
 }
 
-template <class T, bool RMS, bool ADD, int TEAM, int EPV>
+template <class T, bool RMS, bool ADD, bool Q8, int TEAM, int EPV>
 hipError_t rows_by_vpl(const NormCall& c, const Plan& p) {
     switch (p.vpl) {
-    case 1: return go_rows<T, RMS, ADD, TEAM, 1, EPV>(c, p);
-    case 2: return go_rows<T, RMS, ADD, TEAM, 2, EPV>(c, p);
-    case 4: return go_rows<T, RMS, ADD, TEAM, 4, EPV>(c, p);
-    case 8: return go_rows<T, RMS, ADD, TEAM, 8, EPV>(c, p);
-    case 16: return go_rows<T, RMS, ADD, TEAM, 16, EPV>(c, p);
+    case 1: return go_rows<T, RMS, ADD, Q8, TEAM, 1, EPV>(c, p);
+    case 2: return go_rows<T, RMS, ADD, Q8, TEAM, 2, EPV>(c, p);
+    case 4: return go_rows<T, RMS, ADD, Q8, TEAM, 4, EPV>(c, p);
+    case 8: return go_rows<T, RMS, ADD, Q8, TEAM, 8, EPV>(c, p);
+    case 16: return go_rows<T, RMS, ADD, Q8, TEAM, 16, EPV>(c, p);
     }
     return hipErrorInvalidValue;
 }
 
-template <class T, bool RMS, bool ADD, int EPV>
+template <class T, bool RMS, bool ADD, bool Q8, int EPV>
 hipError_t rows_by_team(const NormCall& c, const Plan& p) {
     switch (p.team) {
-    case 4: return rows_by_vpl<T, RMS, ADD, 4, EPV>(c, p);
-    case 8: return rows_by_vpl<T, RMS, ADD, 8, EPV>(c, p);
-    case 16: return rows_by_vpl<T, RMS, ADD, 16, EPV>(c, p);
-    case 32: return rows_by_vpl<T, RMS, ADD, 32, EPV>(c, p);
-    case 64: return rows_by_vpl<T, RMS, ADD, 64, EPV>(c, p);
-    case 128: return rows_by_vpl<T, RMS, ADD, 128, EPV>(c, p);
-    case 256: return rows_by_vpl<T, RMS, ADD, 256, EPV>(c, p);
-    case 512: return rows_by_vpl<T, RMS, ADD, 512, EPV>(c, p);
-    case 1024: return rows_by_vpl<T, RMS, ADD, 1024, EPV>(c, p);
+    case 4: return rows_by_vpl<T, RMS, ADD, Q8, 4, EPV>(c, p);
+    case 8: return rows_by_vpl<T, RMS, ADD, Q8, 8, EPV>(c, p);
+    case 16: return rows_by_vpl<T, RMS, ADD, Q8, 16, EPV>(c, p);
+    case 32: return rows_by_vpl<T, RMS, ADD, Q8, 32, EPV>(c, p);
+    case 64: return rows_by_vpl<T, RMS, ADD, Q8, 64, EPV>(c, p);
+    case 128: return rows_by_vpl<T, RMS, ADD, Q8, 128, EPV>(c, p);
+    case 256: return rows_by_vpl<T, RMS, ADD, Q8, 256, EPV>(c, p);
+    case 512: return rows_by_vpl<T, RMS, ADD, Q8, 512, EPV>(c, p);
+    case 1024: return rows_by_vpl<T, RMS, ADD, Q8, 1024, EPV>(c, p);
     }
     return hipErrorInvalidValue;
 }
 
 template <class T>
 hipError_t launch_rows(int op, const NormCall& c, const Plan& p) {
-    return with_op(op, [&](auto rms, auto add) {
+    return with_op(op, [&](auto rms, auto add, auto q8) {
         return with_epv<T>(p.epv, [&](auto epv) {
-            return rows_by_team<T, decltype(rms)::value, decltype(add)::value, decltype(epv)::value>(c, p);
+            return rows_by_team<T, decltype(rms)::value, decltype(add)::value, decltype(q8)::value,
+                                decltype(epv)::value>(c, p);
         });
     });
 }
@@ -99,13 +103,13 @@ hipError_t launch_rows(int op, const NormCall& c, const Plan& p) {
 // split rows, two kernels
 // ---------------------------------------------------------------------------
 
-template <class T, bool RMS, bool ADD, int EPV>
+template <class T, bool RMS, bool ADD, bool Q8, int EPV>
 hipError_t go_split(const NormCall& c, const Plan& p, float2* ws) {
     const St<T>* x = static_cast<const St<T>*>(c.x);
     const St<T>* r = static_cast<const St<T>*>(c.res);
     const St<T>* g = static_cast<const St<T>*>(c.gamma);
     const St<T>* b = static_cast<const St<T>*>(c.beta);
-    St<T>* y = static_cast<St<T>*>(c.y);
+    void* y = c.y;
     St<T>* h = static_cast<St<T>*>(c.hout);
     float* mean = c.mean;
     float* rstd = c.rstd;
@@ -115,6 +119,7 @@ hipError_t go_split(const NormCall& c, const Plan& p, float2* ws) {
     int CE = kStatsWG * kStatsVPL * EPV;
     int A = p.apply_chunks;
     float eps = c.eps;
+    float qinv = c.qinv;
     {
         void* args[] = {&x, &r, &h, &ws, &M, &N, &S};
         hipError_t e = hipLaunchKernel(
@@ -125,17 +130,18 @@ hipError_t go_split(const NormCall& c, const Plan& p, float2* ws) {
     // with the residual add the normalising kernel reads the stored sum
     const St<T>* src = ADD ? h : x;
     const float2* pp = ws;
-    void* args[] = {&src, &g, &b, &y, &pp, &mean, &rstd, &M, &N, &S, &CE, &A, &eps};
+    void* args[] = {&src, &g, &b, &y, &pp, &mean, &rstd, &M, &N, &S, &CE, &A, &eps, &qinv};
     return hipLaunchKernel(
-        reinterpret_cast<const void*>(&norm_split_apply_kernel<T, RMS, kApplyWG, kApplyVPL, EPV>),
+        reinterpret_cast<const void*>(&norm_split_apply_kernel<T, RMS, Q8, kApplyWG, kApplyVPL, EPV>),
         dim3((unsigned)p.apply_grid), dim3(kApplyWG), args, 0, c.stream);
 }
 
 template <class T>
 hipError_t launch_split(int op, const NormCall& c, const Plan& p, float2* ws) {
-    return with_op(op, [&](auto rms, auto add) {
+    return with_op(op, [&](auto rms, auto add, auto q8) {
         return with_epv<T>(p.epv, [&](auto epv) {
-            return go_split<T, decltype(rms)::value, decltype(add)::value, decltype(epv)::value>(c, p, ws);
+            return go_split<T, decltype(rms)::value, decltype(add)::value, decltype(q8)::value,
+                            decltype(epv)::value>(c, p, ws);
         });
     });
 }
@@ -144,17 +150,18 @@ hipError_t launch_split(int op, const NormCall& c, const Plan& p, float2* ws) {
 // split rows, single cooperative pass
 // ---------------------------------------------------------------------------
 
-template <class T, bool RMS, bool ADD, int EPV>
+template <class T, bool RMS, bool ADD, bool Q8, int EPV>
 const void* coop_kernel() {
-    return reinterpret_cast<const void*>(&norm_split_coop_kernel<T, RMS, ADD, kCoopWG, kCoopVPL, EPV>);
+    return reinterpret_cast<const void*>(&norm_split_coop_kernel<T, RMS, ADD, Q8, kCoopWG, kCoopVPL, EPV>);
 }
 
 template <class T>
 int coop_blocks_per_cu(int op, int epv) {
     const void* f = nullptr;
-    (void)with_op(op, [&](auto rms, auto add) {
+    (void)with_op(op, [&](auto rms, auto add, auto q8) {
         return with_epv<T>(epv, [&](auto e) {
-            f = coop_kernel<T, decltype(rms)::value, decltype(add)::value, decltype(e)::value>();
+            f = coop_kernel<T, decltype(rms)::value, decltype(add)::value, decltype(q8)::value,
+                            decltype(e)::value>();
             return hipSuccess;
         });
     });
@@ -164,14 +171,14 @@ int coop_blocks_per_cu(int op, int epv) {
     return n;
 }
 
-template <class T, bool RMS, bool ADD, int EPV>
+template <class T, bool RMS, bool ADD, bool Q8, int EPV>
 hipError_t go_split_coop(const NormCall& c, const Plan& p, float2* ws, unsigned* sync,
                          unsigned need, unsigned spin_limit) {
     const St<T>* x = static_cast<const St<T>*>(c.x);
     const St<T>* r = static_cast<const St<T>*>(c.res);
     const St<T>* g = static_cast<const St<T>*>(c.gamma);
     const St<T>* b = static_cast<const St<T>*>(c.beta);
-    St<T>* y = static_cast<St<T>*>(c.y);
+    void* y = c.y;
     St<T>* h = static_cast<St<T>*>(c.hout);
     float* mean = c.mean;
     float* rstd = c.rstd;
@@ -180,19 +187,20 @@ hipError_t go_split_coop(const NormCall& c, const Plan& p, float2* ws, unsigned*
     int S = p.chunks;
     int teams = p.teams;
     float eps = c.eps;
-    void* args[] = {&x, &r, &g, &b, &y, &h, &mean, &rstd, &ws, &sync, &M, &N, &S, &teams, &eps, &need,
-                    &spin_limit};
-    return hipLaunchCooperativeKernel(coop_kernel<T, RMS, ADD, EPV>(), dim3((unsigned)(teams * S)),
+    float qinv = c.qinv;
+    void* args[] = {&x, &r, &g, &b, &y, &h, &mean, &rstd, &ws, &sync, &M, &N, &S, &teams, &eps, &qinv,
+                    &need, &spin_limit};
+    return hipLaunchCooperativeKernel(coop_kernel<T, RMS, ADD, Q8, EPV>(), dim3((unsigned)(teams * S)),
                                       dim3(kCoopWG), args, 0, c.stream);
 }
 
 template <class T>
 hipError_t launch_split_coop(int op, const NormCall& c, const Plan& p, float2* ws, unsigned* sync,
                              unsigned need, unsigned spin_limit) {
-    return with_op(op, [&](auto rms, auto add) {
+    return with_op(op, [&](auto rms, auto add, auto q8) {
         return with_epv<T>(p.epv, [&](auto epv) {
-            return go_split_coop<T, decltype(rms)::value, decltype(add)::value, decltype(epv)::value>(
-                c, p, ws, sync, need, spin_limit);
+            return go_split_coop<T, decltype(rms)::value, decltype(add)::value, decltype(q8)::value,
+                                 decltype(epv)::value>(c, p, ws, sync, need, spin_limit);
         });
     });
 }

@@ -172,6 +172,39 @@ __device__ __forceinline__ void add_into(Vec<T, EPV>& x, const Vec<T, EPV>& r) {
     x.set(h);
 }
 
+// --------------------------------------------------------------------------
+// FP8 output (OCP E4M3, the format gfx950's v_cvt_pk_fp8_f32 produces):
+// values are saturated to +-448 first (the conversion itself turns anything
+// that rounds past 448 into NaN), NaN passes through; rounding is to nearest
+// even.  One vector of EPV results becomes EPV bytes, stored nontemporal.
+// --------------------------------------------------------------------------
+
+__device__ __forceinline__ float sat_e4m3(float v) {
+    return v > 448.0f ? 448.0f : (v < -448.0f ? -448.0f : v);   // comparisons keep NaN
+}
+
+__device__ __forceinline__ unsigned e4m3x4(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(a), sat_e4m3(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(c), sat_e4m3(d), w, true);
+    return (unsigned)w;
+}
+
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+template <int EPV>
+__device__ __forceinline__ void store_e4m3(uint8_t* p, const float (&v)[EPV]) {
+    if constexpr (EPV == 8) {
+        u32x2 w = {e4m3x4(v[0], v[1], v[2], v[3]), e4m3x4(v[4], v[5], v[6], v[7])};
+        st_stream(w, reinterpret_cast<u32x2*>(p));
+    } else if constexpr (EPV == 4) {
+        st_stream(e4m3x4(v[0], v[1], v[2], v[3]), reinterpret_cast<unsigned*>(p));
+    } else {
+        static_assert(EPV == 1, "EPV");
+        const int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(v[0]), 0.0f, 0, false);
+        st_stream((uint8_t)(w & 0xff), p);
+    }
+}
+
 // 1/sqrt(v) with the hardware reciprocal square root (v_rsq_f32, about one
 // ulp): one instruction per row instead of a correctly rounded square root
 // and divide.  rsq(0) = +inf as IEEE requires.

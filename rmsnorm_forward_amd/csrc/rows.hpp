@@ -78,19 +78,22 @@ __device__ __forceinline__ float vec_sum_shifted(const V& v, float K) {
 // type; h is stored to hout (the updated residual) and normalised in place of
 // x.  res / hout may be the same buffer, and y may be x: every element is
 // read into registers by the lane that later writes it, before it writes.
-template <class T, bool RMS, bool ADD, int TEAM, int VPL, int EPV>
+// Q8 (RMSNorm only): y is FP8 E4M3 codes of (the normalised value * qinv),
+// one byte per element, instead of the I/O dtype.
+template <class T, bool RMS, bool ADD, bool Q8, int TEAM, int VPL, int EPV>
 __global__ __launch_bounds__(TeamGeom<TEAM>::WG)
 void norm_rows_kernel(const typename T::storage* x,
                       const typename T::storage* res,
                       const typename T::storage* __restrict__ gamma,
                       const typename T::storage* __restrict__ beta,
-                      typename T::storage* y,
+                      void* yv,
                       typename T::storage* hout,
                       float* __restrict__ mean_out,
                       float* __restrict__ rstd_out,
-                      int64_t M, int N, float eps)
+                      int64_t M, int N, float eps, float qinv)
 {
     static_assert(!ADD || RMS, "the residual add is fused with RMSNorm only");
+    static_assert(!Q8 || RMS, "FP8 output is fused with RMSNorm only");
     using G = TeamGeom<TEAM>;
     using S = typename T::storage;
     using V = Vec<T, EPV>;
@@ -117,7 +120,8 @@ void norm_rows_kernel(const typename T::storage* x,
         // row base (wavefront-uniform when TEAM >= 64) plus 32-bit lane offsets
         const int64_t base = (row_ok ? row : 0) * (int64_t)N;
         const S* xr = x + base;
-        S* yr = y + base;
+        S* yr = static_cast<S*>(yv) + base;
+        uint8_t* yq = static_cast<uint8_t*>(yv) + base;
 
         V xv[VPL];
         bool ok[VPL];
@@ -229,7 +233,13 @@ void norm_rows_kernel(const typename T::storage* x,
                     else if constexpr (HB) o[k] = t + bl.get(k);
                     else o[k] = t;
                 }
-                V::store(yr + off, o);
+                if constexpr (Q8) {
+#pragma unroll
+                    for (int k = 0; k < EPV; ++k) o[k] *= qinv;
+                    store_e4m3<EPV>(yq + off, o);
+                } else {
+                    V::store(yr + off, o);
+                }
             }
         };
         using TT = bool_c<true>;

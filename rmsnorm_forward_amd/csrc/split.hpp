@@ -145,10 +145,12 @@ struct Chunk {
 
     // normalise the chunk from registers, apply the affine, store; gamma /
     // beta loads run at most four vectors ahead of their use
-    template <bool RMS>
-    __device__ __forceinline__ void apply(typename T::storage* yr, const typename T::storage* gamma,
+    // Q8: yr points at one byte per element and receives the E4M3 codes of
+    // the results times qinv
+    template <bool RMS, bool Q8 = false>
+    __device__ __forceinline__ void apply(void* yr, const typename T::storage* gamma,
                                           const typename T::storage* beta, float K, float mu,
-                                          float rs) {
+                                          float rs, float qinv = 1.0f) {
         const bool has_g = gamma != nullptr;
         const bool has_b = beta != nullptr;
         opaque();
@@ -167,7 +169,13 @@ struct Chunk {
                 if constexpr (RMS) o[k] = (xv[j].get(k) * rs) * g;
                 else o[k] = __builtin_fmaf(((xv[j].get(k) - K) - mu) * rs, g, has_b ? bv.get(k) : 0.0f);
             }
-            V::store(yr + off, o);
+            if constexpr (Q8) {
+#pragma unroll
+                for (int k = 0; k < EPV; ++k) o[k] *= qinv;
+                store_e4m3<EPV>(static_cast<uint8_t*>(yr) + off, o);
+            } else {
+                V::store(static_cast<typename T::storage*>(yr) + off, o);
+            }
         }
     }
 };
@@ -191,6 +199,13 @@ __device__ __forceinline__ float2 load_partial_coherent(const float2* p) {
         reinterpret_cast<unsigned long long*>(const_cast<float2*>(p)), __ATOMIC_RELAXED,
         __HIP_MEMORY_SCOPE_AGENT);
     return make_float2(__uint_as_float((unsigned)bits), __uint_as_float((unsigned)(bits >> 32)));
+}
+
+// start of row `row` of an output of the I/O dtype, or of FP8 codes
+template <class T, bool Q8>
+__device__ __forceinline__ void* row_out(void* y, int64_t row, int N) {
+    if constexpr (Q8) return static_cast<uint8_t*>(y) + row * (int64_t)N;
+    else return static_cast<typename T::storage*>(y) + row * (int64_t)N;
 }
 
 template <bool COHERENT>
@@ -251,23 +266,24 @@ __device__ __forceinline__ float2 row_stats(const float2* pr, int S, int CE, int
 // scope release / acquire would cost one of each per workgroup and row).
 
 
-template <class T, bool RMS, bool ADD, int WG, int VPL, int EPV>
+template <class T, bool RMS, bool ADD, bool Q8, int WG, int VPL, int EPV>
 __global__ __launch_bounds__(WG)
 void norm_split_coop_kernel(const typename T::storage* x,
                             const typename T::storage* res,
                             const typename T::storage* __restrict__ gamma,
                             const typename T::storage* __restrict__ beta,
-                            typename T::storage* y,
+                            void* y,
                             typename T::storage* hout,
                             float* __restrict__ mean_out,
                             float* __restrict__ rstd_out,
                             float2* __restrict__ part,      // [M, S] partials
                             unsigned* __restrict__ sync,    // row r: [64r], [64r+32]; zero at
                                                             // launch and again at exit
-                            int64_t M, int N, int S, int teams, float eps,
+                            int64_t M, int N, int S, int teams, float eps, float qinv,
                             unsigned need, unsigned spin_limit)
 {
     static_assert(!ADD || RMS, "the residual add is fused with RMSNorm only");
+    static_assert(!Q8 || RMS, "FP8 output is fused with RMSNorm only");
     using C = Chunk<T, WG, VPL, EPV>;
     __shared__ float red[2][WG / 64];
     __shared__ int late;
@@ -321,7 +337,7 @@ void norm_split_coop_kernel(const typename T::storage* x,
             if (!RMS && mean_out) mean_out[row] = K + st.x;
             if (rstd_out) rstd_out[row] = st.y;
         }
-        ch.template apply<RMS>(y + row * (int64_t)N, gamma, beta, K, st.x, st.y);
+        ch.template apply<RMS, Q8>(row_out<T, Q8>(y, row, N), gamma, beta, K, st.x, st.y, qinv);
     }
 }
 
@@ -365,17 +381,18 @@ void norm_split_stats_kernel(const typename T::storage* x,
 // they are in flight, normalise and store.  Every wavefront runs the same
 // merge in chunk order, so every chunk of a row uses the same bits of mean
 // and rstd.  The row's first chunk stores mean and rstd.
-template <class T, bool RMS, int WG, int VPL, int EPV>
+template <class T, bool RMS, bool Q8, int WG, int VPL, int EPV>
 __global__ __launch_bounds__(WG)
 void norm_split_apply_kernel(const typename T::storage* x,
                              const typename T::storage* __restrict__ gamma,
                              const typename T::storage* __restrict__ beta,
-                             typename T::storage* y,
+                             void* y,
                              const float2* __restrict__ part,
                              float* __restrict__ mean_out,
                              float* __restrict__ rstd_out,
-                             int64_t M, int N, int S, int CE, int A, float eps)
+                             int64_t M, int N, int S, int CE, int A, float eps, float qinv)
 {
+    static_assert(!Q8 || RMS, "FP8 output is fused with RMSNorm only");
     using C = Chunk<T, WG, VPL, EPV>;
     const int NV = N / EPV;
     const int64_t items = M * (int64_t)A;
@@ -391,7 +408,7 @@ void norm_split_apply_kernel(const typename T::storage* x,
             if (!RMS && mean_out) mean_out[row] = K + st.x;
             if (rstd_out) rstd_out[row] = st.y;
         }
-        ch.template apply<RMS>(y + row * (int64_t)N, gamma, beta, K, st.x, st.y);
+        ch.template apply<RMS, Q8>(row_out<T, Q8>(y, row, N), gamma, beta, K, st.x, st.y, qinv);
     }
 }
 

@@ -82,3 +82,31 @@ def run_add(dtype: str, x: np.ndarray, res: np.ndarray, gamma, eps: float, *, st
     h = to_host(ht, dtype).reshape(M, N)
     r = rstd.cpu().numpy() if rstd is not None else None
     return y, h, r
+
+
+def run_fp8(dtype: str, x: np.ndarray, res, gamma, eps: float, scale: float, *, stats: bool = True,
+            offset: int = 0, inplace: bool = False):
+    """One rms_fp8_fwd (res None) or add_rms_fp8_fwd call; returns (codes
+    uint8, h or None, rstd) as host arrays."""
+    M, N = x.shape
+    xt = to_device(x, dtype, offset)
+    rt = to_device(res, dtype, offset) if res is not None else None
+    gt = to_device(gamma, dtype, offset) if gamma is not None else None
+    qt = torch.zeros(M * N + 16, dtype=torch.uint8, device="cuda")[offset:offset + M * N]
+    ht = None
+    if res is not None:
+        ht = rt if inplace else torch.empty(M * N + offset, dtype=TORCH_DT[dtype], device="cuda")[offset:]
+    rstd = torch.empty(M, dtype=torch.float32, device="cuda") if stats else None
+    p = lambda t: t.data_ptr() if t is not None else None
+    stream = torch.cuda.current_stream().cuda_stream
+    if res is None:
+        st = rn.rms_fp8_fwd(p(xt), p(gt), p(qt), p(rstd), M, N, eps, scale, CODE[dtype], stream)
+    else:
+        st = rn.add_rms_fp8_fwd(p(xt), p(rt), p(gt), p(qt), p(ht), p(rstd), M, N, eps, scale, CODE[dtype],
+                                stream)
+    assert st == rn.NORM_OK, f"{rn.STATUS.get(st)}: {rn.norm_status_str(st)} [{rn.norm_last_error()}]"
+    torch.cuda.synchronize()
+    q = qt.cpu().numpy().reshape(M, N)
+    h = to_host(ht, dtype).reshape(M, N) if ht is not None else None
+    r = rstd.cpu().numpy() if rstd is not None else None
+    return q, h, r

@@ -13,6 +13,12 @@ marked):
                 mean is near zero, so the row's scale bounds it from below
   rstd          relative error <= 1e-5
   stress rows   no NaN, no infinity, variance >= 0 (rstd <= 1/sqrt(eps))
+  FP8 codes     equal to the oracle's code of y / scale; where the two differ
+                they must be neighbours and the oracle's y / scale must lie
+                within FP8_TIE_REL of the midpoint between them (the kernel
+                takes the decision on its fp32 y, which carries a few fp32
+                ulps: reading), at most FP8_TIE_FRAC of all elements; a
+                zero may be coded +0 or -0, a NaN with either sign
 """
 from __future__ import annotations
 
@@ -24,6 +30,53 @@ Y_F32_ABS = 2e-5
 STAT_REL = 1e-5
 HALF_FLOOR = 2.0 ** -20
 SIG_BITS = {"bf16": 8, "f16": 11}
+FP8_TIE_REL = 4e-6
+FP8_TIE_FRAC = 1e-3
+
+
+def _e4m3_table() -> np.ndarray:
+    v = np.empty(256)
+    for c in range(256):
+        s = -1.0 if c & 0x80 else 1.0
+        e, f = (c >> 3) & 0xF, c & 7
+        if e == 0xF and f == 7:
+            v[c] = np.nan
+        elif e == 0:
+            v[c] = s * f / 8.0 * 2.0 ** -6
+        else:
+            v[c] = s * (1.0 + f / 8.0) * 2.0 ** (e - 7)
+    return v
+
+
+E4M3 = _e4m3_table()
+
+
+def check_fp8(q_gpu: np.ndarray, q_ref: np.ndarray, y_ref: np.ndarray, scale: float, what: str = "") -> dict:
+    """q_gpu, q_ref: uint8 codes; y_ref: the oracle's float64 y (before
+    quantisation)."""
+    g = E4M3[q_gpu.astype(np.int64)]
+    r = E4M3[q_ref.astype(np.int64)]
+    same = (q_gpu == q_ref) | ((g == 0) & (r == 0)) | (np.isnan(g) & np.isnan(r))
+    diff = ~same
+    n_tie = int(diff.sum())
+    if n_tie:
+        v = y_ref[diff] / float(np.float32(scale))
+        gd, rd = g[diff], r[diff]
+        mid = (gd + rd) / 2
+        finite = np.isfinite(gd) & np.isfinite(rd)
+        # neighbours: nothing representable strictly between them
+        lo, hi = np.minimum(gd, rd), np.maximum(gd, rd)
+        fin = E4M3[np.isfinite(E4M3)]
+        between = np.array([np.any((fin > a) & (fin < b)) for a, b in zip(lo, hi)]) if finite.any() else \
+            np.zeros(0, bool)
+        near = np.abs(v - mid) <= FP8_TIE_REL * np.abs(v) + 1e-30
+        bad = ~(finite & ~between & near)
+        if bad.any():
+            i = np.flatnonzero(diff)[np.flatnonzero(bad)[0]]
+            raise AssertionError(f"{what}: FP8 code {q_gpu.flat[i]:#x} vs oracle {q_ref.flat[i]:#x} "
+                                 f"for y/scale={y_ref.flat[i] / float(np.float32(scale))!r}")
+        assert n_tie <= FP8_TIE_FRAC * q_gpu.size + 1, f"{what}: {n_tie} near-tie differences"
+    return {"fp8_near_ties": n_tie}
 
 
 def ulp_of(v: np.ndarray, dtype: str) -> np.ndarray:

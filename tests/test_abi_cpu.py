@@ -26,8 +26,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["add_rms_fwd", "ln_fwd", "norm_describe", "norm_last_error",
-                                    "norm_status_str", "rms_fwd"]
+    assert declared_functions() == ["add_rms_fp8_fwd", "add_rms_fwd", "ln_fwd", "norm_describe",
+                                    "norm_last_error", "norm_status_str", "rms_fp8_fwd", "rms_fwd"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -143,6 +143,33 @@ def test_add_rms_plans_like_rms():
         a = parse(rn.norm_describe("add_rms", 64, N, "bf16"))
         b = parse(rn.norm_describe("rms", 64, N, "bf16"))
         assert a == b, (N, a, b)
+
+
+def test_fp8_validation():
+    Q = 0x900000
+    ok = lambda st: st not in (ALIAS, BAD_ARG, NULL_ARG, BAD_SHAPE, BAD_DTYPE, BAD_EPS)
+    assert rn.rms_fp8_fwd(X, G, Q, RSTD, 4, 64, 1e-6, 0.0, 2, None) == BAD_ARG        # scale 0
+    assert rn.rms_fp8_fwd(X, G, Q, RSTD, 4, 64, 1e-6, -1.0, 2, None) == BAD_ARG
+    assert rn.rms_fp8_fwd(X, G, Q, RSTD, 4, 64, 1e-6, float("inf"), 2, None) == BAD_ARG
+    assert rn.rms_fp8_fwd(X, G, Q, RSTD, 4, 64, 1e-6, float("nan"), 2, None) == BAD_ARG
+    assert rn.rms_fp8_fwd(X, G, Q, RSTD, 4, 64, 1e-6, 1e-45, 2, None) == BAD_ARG     # 1/scale overflows
+    assert rn.rms_fp8_fwd(X, G, None, RSTD, 4, 64, 1e-6, 1.0, 2, None) == NULL_ARG
+    assert rn.rms_fp8_fwd(X, G, X, RSTD, 4, 64, 1e-6, 1.0, 2, None) == ALIAS          # codes over x
+    assert rn.rms_fp8_fwd(X, G, X + 128, RSTD, 4, 64, 1e-6, 1.0, 2, None) == ALIAS
+    assert ok(rn.rms_fp8_fwd(X, G, X + 4 * 64 * 2, RSTD, 4, 64, 1e-6, 1.0, 2, None))  # right after x
+    assert rn.rms_fp8_fwd(X, G, Q, Q + 200, 4, 64, 1e-6, 1.0, 2, None) == ALIAS       # rstd inside codes
+    assert ok(rn.rms_fp8_fwd(X, G, Q, Q + 256, 4, 64, 1e-6, 1.0, 2, None))            # 4 x 64 bytes
+    # with the residual add: the sum may go over the residual, the codes never over x
+    assert ok(rn.add_rms_fp8_fwd(X, R, G, Q, R, RSTD, 4, 64, 1e-6, 0.5, 2, None))
+    assert rn.add_rms_fp8_fwd(X, R, G, X, H, RSTD, 4, 64, 1e-6, 0.5, 2, None) == ALIAS
+    assert rn.add_rms_fp8_fwd(X, None, G, Q, H, RSTD, 4, 64, 1e-6, 0.5, 2, None) == NULL_ARG
+    assert ok(rn.rms_fp8_fwd(X, G, Q + 1, RSTD, 4, 64, 1e-6, 1.0, 2, None))          # codes: any byte address
+
+
+def test_fp8_plans_like_rms():
+    for N in (1024, 8192, 1 << 20):
+        for op in ("rms_fp8", "add_rms_fp8"):
+            assert parse(rn.norm_describe(op, 64, N, "bf16")) == parse(rn.norm_describe("rms", 64, N, "bf16"))
 
 
 def test_rms_rejects_beta_and_mean():

@@ -76,6 +76,14 @@ def test_measured_configuration(name):
     w = workloads.CONFIGS[name]
     print(f"[gpu] config {name}: {w.op} {w.dtype} M={w.M} N={w.N}", flush=True)
     inp = workloads.generate(name)
+    if w.op == "rms_fp8":
+        q, _, rstd = gpu_runner.run_fp8(w.dtype, inp["x"], None, inp["gamma"], w.eps, w.scale)
+        rows = sample_rows(w.M, 256, seed=w.seed)
+        qr, yr, rr = oracle.rms_fp8_fwd(inp["x"][rows], inp["gamma"], w.dtype, w.eps, w.scale)
+        st = parity.check_fp8(q[rows], qr, yr, w.scale, name)
+        st.update(parity.check_stats(None, rstd[rows], None, rr, w.eps, name))
+        print(f"[gpu] {name}: {st}", flush=True)
+        return
     if w.op == "add_rms":
         y, h, rstd = gpu_runner.run_add(w.dtype, inp["x"], inp["res"], inp["gamma"], w.eps)
         rows = sample_rows(w.M, 256, seed=w.seed)
@@ -431,6 +439,92 @@ def test_fused_add_rms_norm_tensor_api():
     assert y2.data_ptr() == xt.data_ptr() and h2.data_ptr() == rt.data_ptr()
     assert np.array_equal(gpu_runner.to_host(xt.reshape(30, 1024), "bf16"), yh)
     assert np.array_equal(gpu_runner.to_host(rt.reshape(30, 1024), "bf16"), hh)
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) output
+# ---------------------------------------------------------------------------
+
+def compare_fp8(dtype, x, res, gamma, eps, scale, q, h, rstd, what=""):
+    if res is None:
+        qr, yr, rr = oracle.rms_fp8_fwd(x, gamma, dtype, eps, scale)
+    else:
+        hr, qr, yr, rr = oracle.add_rms_fp8_fwd(x, res, gamma, dtype, eps, scale)
+        assert np.array_equal(h.view(np.uint8), hr.view(np.uint8)), f"{what}: residual sum differs"
+    out = parity.check_fp8(q, qr, yr, scale, what)
+    if rstd is not None:
+        out.update(parity.check_stats(None, rstd, None, rr, eps, what))
+    return out
+
+
+@pytest.mark.parametrize("scale", [1.0, 1.0 / 64])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("N", EDGE_N)
+def test_rms_fp8_edge_shapes(dtype, N, scale):
+    M = 37 if N <= 8192 else 5
+    print(f"[gpu] rms_fp8 {dtype} M={M} N={N} scale={scale}", flush=True)
+    inp = inputs("rms", dtype, M, N, seed=N + 11)
+    q, _, rstd = gpu_runner.run_fp8(dtype, inp["x"], None, inp["gamma"], 1e-6, scale)
+    compare_fp8(dtype, inp["x"], None, inp["gamma"], 1e-6, scale, q, None, rstd, what=f"rms_fp8 N={N}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("N", [1, 5, 1000, 4096, 8192, 16384, 65536, 131080])
+def test_add_rms_fp8(dtype, N):
+    M = 13 if N <= 8192 else 4
+    print(f"[gpu] add_rms_fp8 {dtype} M={M} N={N}", flush=True)
+    inp = add_inputs(dtype, M, N, seed=N + 12)
+    q, h, rstd = gpu_runner.run_fp8(dtype, inp["x"], inp["res"], inp["gamma"], 1e-6, 0.05)
+    compare_fp8(dtype, inp["x"], inp["res"], inp["gamma"], 1e-6, 0.05, q, h, rstd, what=f"add_rms_fp8 N={N}")
+    qi, hi, ri = gpu_runner.run_fp8(dtype, inp["x"], inp["res"], inp["gamma"], 1e-6, 0.05, inplace=True)
+    assert np.array_equal(qi, q) and np.array_equal(hi.view(np.uint8), h.view(np.uint8))
+
+
+@pytest.mark.parametrize("mode", ["split2", "splitcoop"])
+@pytest.mark.parametrize("add", [False, True])
+def test_fp8_forced_split(monkeypatch, mode, add):
+    monkeypatch.setenv("MI355NORM_PATH", mode)
+    M, N = 7, 300000
+    inp = add_inputs("bf16", M, N, seed=14)
+    res = inp["res"] if add else None
+    q, h, rstd = gpu_runner.run_fp8("bf16", inp["x"], res, inp["gamma"], 1e-6, 0.02)
+    compare_fp8("bf16", inp["x"], res, inp["gamma"], 1e-6, 0.02, q, h, rstd, what=f"fp8 {mode} add={add}")
+
+
+def test_fp8_saturation_nan_and_unaligned():
+    """A scale small enough to push many values past 448 saturates them to
+    +-448; eps = 0 on an all-zero row gives NaN codes; unaligned pointers take
+    the element-wise path with byte stores."""
+    M, N = 9, 3000
+    inp = inputs("rms", "bf16", M, N, seed=15)
+    x = inp["x"].copy()
+    x[3] = 0                                          # all-zero row
+    q, _, rstd = gpu_runner.run_fp8("bf16", x, None, inp["gamma"], 0.0, 1e-3)
+    assert np.all(np.isnan(parity.E4M3[q[3]]))
+    assert np.isinf(rstd[3])
+    keep = np.ones(M, bool)
+    keep[3] = False
+    vals = parity.E4M3[q[keep]]
+    assert np.mean(np.abs(vals) == 448.0) > 0.3          # |y| > 0.448 saturates: about 40%
+    compare_fp8("bf16", x[keep], None, inp["gamma"], 0.0, 1e-3, q[keep], None, rstd[keep], what="saturated")
+    q2, _, r2 = gpu_runner.run_fp8("bf16", inp["x"], None, inp["gamma"], 1e-6, 0.1, offset=1)
+    compare_fp8("bf16", inp["x"], None, inp["gamma"], 1e-6, 0.1, q2, None, r2, what="fp8 unaligned")
+
+
+def test_fp8_tensor_api():
+    import rmsnorm_forward_amd as rn
+    inp = add_inputs("bf16", 24, 2048, seed=16)
+    xt = gpu_runner.to_device(inp["x"], "bf16").view(4, 6, 2048)
+    rt = gpu_runner.to_device(inp["res"], "bf16").view(4, 6, 2048)
+    gt = gpu_runner.to_device(inp["gamma"], "bf16")
+    q, rstd = rn.rms_norm_fp8(xt, gt, scale=0.03, eps=1e-6)
+    assert q.dtype == torch.float8_e4m3fn and q.shape == xt.shape
+    compare_fp8("bf16", inp["x"], None, inp["gamma"], 1e-6, 0.03, q.view(torch.uint8).reshape(24, 2048).cpu().numpy(),
+                None, rstd.cpu().numpy(), what="fp8 tensor api")
+    q, h, rstd = rn.fused_add_rms_norm_fp8(xt, rt, gt, scale=0.03, eps=1e-6)
+    compare_fp8("bf16", inp["x"], inp["res"], inp["gamma"], 1e-6, 0.03,
+                q.view(torch.uint8).reshape(24, 2048).cpu().numpy(),
+                gpu_runner.to_host(h.reshape(24, 2048), "bf16"), rstd.cpu().numpy(), what="fp8 add tensor api")
 
 
 def test_m_zero_launches_nothing():

@@ -168,13 +168,14 @@ def check_row_f32() -> np.ndarray:
 @dataclass(frozen=True)
 class Workload:
     name: str
-    op: str          # "ln", "rms" or "add_rms" (residual add, then RMSNorm)
+    op: str          # "ln", "rms", "add_rms" (residual add, then RMSNorm), "rms_fp8"
     dtype: str       # "f32", "bf16", "f16"
     M: int
     N: int
     eps: float
     seed: int
     recipe: str
+    scale: float = 1.0   # FP8 output: the static scale
 
     @property
     def elem_bytes(self) -> int:
@@ -185,7 +186,10 @@ class Workload:
         (and beta for LN) read once, fp32 mean+rstd (LN) or rstd (RMS); with
         the residual add also the residual read once and the sum written once."""
         e = self.elem_bytes
-        b = (4 if self.op == "add_rms" else 2) * self.M * self.N * e
+        if self.op == "rms_fp8":
+            b = self.M * self.N * (e + 1)          # x read, one byte per code written
+        else:
+            b = (4 if self.op == "add_rms" else 2) * self.M * self.N * e
         b += self.N * e * (2 if self.op == "ln" else 1)
         if with_stats:
             b += self.M * (8 if self.op == "ln" else 4)
@@ -217,6 +221,9 @@ CONFIGS = {
     "add_rms_bf16_16384x8192": Workload(
         "add_rms_bf16_16384x8192", "add_rms", "bf16", 16384, 8192, 1e-6, 1006,
         "x~U(-1,1), residual~N(0,1), weight~U(0,1); residual add then RMSNorm"),
+    "rms_fp8_bf16_16384x8192": Workload(
+        "rms_fp8_bf16_16384x8192", "rms_fp8", "bf16", 16384, 8192, 1e-6, 1007,
+        "x~U(-1,1), weight~U(0,1); RMSNorm with FP8 E4M3 output of y / (1/64)", 1.0 / 64),
 }
 
 
@@ -238,4 +245,6 @@ def generate(name: str) -> dict:
         return gen_ln_normal(0, w.M, w.N, w.dtype, loc=3.0, scale=2.0, rng=rng)
     if name == "add_rms_bf16_16384x8192":
         return gen_add_rms(w.seed, w.M, w.N, w.dtype)
+    if name == "rms_fp8_bf16_16384x8192":
+        return gen_rms_uniform(w.seed, w.M, w.N, w.dtype)
     raise KeyError(name)
