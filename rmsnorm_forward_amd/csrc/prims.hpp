@@ -179,8 +179,12 @@ __device__ __forceinline__ void add_into(Vec<T, EPV>& x, const Vec<T, EPV>& r) {
 // even.  One vector of EPV results becomes EPV bytes, stored nontemporal.
 // --------------------------------------------------------------------------
 
+// v_med3_f32 clamps in one instruction but maps NaN to -448 on gfx950, so a
+// NaN is put back with one compare and select (three instructions instead of
+// the four of two compare-selects)
 __device__ __forceinline__ float sat_e4m3(float v) {
-    return v > 448.0f ? 448.0f : (v < -448.0f ? -448.0f : v);   // comparisons keep NaN
+    const float c = __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f);
+    return __builtin_isnan(v) ? v : c;
 }
 
 __device__ __forceinline__ unsigned e4m3x4(float a, float b, float c, float d) {

@@ -211,6 +211,8 @@ void norm_rows_kernel(const typename T::storage* x,
         // normalise from the register copy, apply the affine, store; the
         // presence of gamma / beta is resolved by a uniform branch, so the
         // inner loop carries no per-element selects
+        // FP8 output: the 1/scale factor rides on rstd (one multiply per row)
+        const float rsy = Q8 ? rs * qinv : rs;
         auto emit = [&](auto hg, auto hb) {
             constexpr bool HG = decltype(hg)::value;
             constexpr bool HB = !RMS && decltype(hb)::value;
@@ -225,7 +227,7 @@ void norm_rows_kernel(const typename T::storage* x,
 #pragma unroll
                 for (int k = 0; k < EPV; ++k) {
                     float t;
-                    if constexpr (RMS) t = xv[j].get(k) * rs;
+                    if constexpr (RMS) t = xv[j].get(k) * rsy;
                     else if constexpr (CACHE_F32) t = d[j][k] * rs;
                     else t = ((xv[j].get(k) - K) - mu) * rs;
                     if constexpr (HG && HB) o[k] = __builtin_fmaf(t, gl.get(k), bl.get(k));
@@ -234,8 +236,6 @@ void norm_rows_kernel(const typename T::storage* x,
                     else o[k] = t;
                 }
                 if constexpr (Q8) {
-#pragma unroll
-                    for (int k = 0; k < EPV; ++k) o[k] *= qinv;
                     store_e4m3<EPV>(yq + off, o);
                 } else {
                     V::store(yr + off, o);

@@ -153,6 +153,7 @@ struct Chunk {
                                           float rs, float qinv = 1.0f) {
         const bool has_g = gamma != nullptr;
         const bool has_b = beta != nullptr;
+        if constexpr (Q8) rs *= qinv;      // the 1/scale factor rides on rstd
         opaque();
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
@@ -170,8 +171,6 @@ struct Chunk {
                 else o[k] = __builtin_fmaf(((xv[j].get(k) - K) - mu) * rs, g, has_b ? bv.get(k) : 0.0f);
             }
             if constexpr (Q8) {
-#pragma unroll
-                for (int k = 0; k < EPV; ++k) o[k] *= qinv;
                 store_e4m3<EPV>(static_cast<uint8_t*>(yr) + off, o);
             } else {
                 V::store(static_cast<typename T::storage*>(yr) + off, o);
