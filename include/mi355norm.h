@@ -153,6 +153,50 @@ int add_rms_fp8_fwd(const void *x, const void *residual, const void *gamma, void
                     void *residual_out, float *rstd, int64_t M, int64_t N, float eps,
                     float scale, int dtype, void *stream);
 
+/*
+ * Every operation above, with row strides (non-contiguous rows, such as a
+ * slice of columns of a wider matrix, without a copy).
+ */
+typedef enum {
+    NORM_OP_LN = 0,           /* ln_fwd          */
+    NORM_OP_RMS = 1,          /* rms_fwd         */
+    NORM_OP_ADD_RMS = 2,      /* add_rms_fwd     */
+    NORM_OP_RMS_FP8 = 3,      /* rms_fp8_fwd     */
+    NORM_OP_ADD_RMS_FP8 = 4   /* add_rms_fp8_fwd */
+} norm_op;
+
+typedef struct {
+    int op;                       /* norm_op                                       */
+    int dtype;                    /* norm_dtype of every matrix but an FP8 y        */
+    int64_t M, N;
+    const void *x;                /* row r at x + r * ld_x elements                 */
+    int64_t ld_x;                 /* row stride in elements, >= N; 0 means N        */
+    const void *residual;         /* add_rms ops only, else NULL                    */
+    int64_t ld_residual;
+    const void *gamma;            /* [N] or NULL                                    */
+    const void *beta;             /* [N] or NULL; LayerNorm only                    */
+    void *y;
+    int64_t ld_y;                 /* elements of y's type (bytes for FP8 codes)     */
+    void *residual_out;           /* add_rms ops only, else NULL                    */
+    int64_t ld_residual_out;
+    float *mean;                  /* fp32 [M] or NULL; LayerNorm only               */
+    float *rstd;                  /* fp32 [M] or NULL                               */
+    float eps;
+    float scale;                  /* FP8 ops only (ignored otherwise)               */
+} norm_args;
+
+/*
+ * Runs args->op with the conventions of its entry point above, rows being
+ * ld_* elements apart (ld_* < N, or an ld_* so large that the matrix does
+ * not fit 2^63 bytes, is NORM_ERR_BAD_SHAPE; NULL args is NORM_ERR_NULL_ARG).
+ * The 16-byte vector path is taken when every row start is 16-byte aligned
+ * (EPV-byte for FP8 codes); otherwise the element-wise path.  Overlaps are
+ * checked row by row when the two matrices share a stride or one is a
+ * vector (interleaved matrices that share no byte are accepted), and over
+ * their whole spans otherwise.  Returns a norm_status.
+ */
+int norm_fwd(const norm_args *args, void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *norm_status_str(int status);
 

@@ -6,9 +6,9 @@ only marshals arguments.  PyTorch is used for device memory and streams.
 
 Two layers:
   * ln_fwd / rms_fwd / add_rms_fwd / rms_fp8_fwd / add_rms_fp8_fwd /
-    norm_status_str / norm_last_error / norm_describe -- the C ABI entry
-    points under the same names, taking raw device addresses (ints) and
-    returning the status code;
+    norm_fwd (row strides) / norm_status_str / norm_last_error /
+    norm_describe -- the C ABI entry points under the same names, taking raw
+    device addresses (ints) and returning the status code;
   * layer_norm / rms_norm / fused_add_rms_norm / rms_norm_fp8 /
     fused_add_rms_norm_fp8 -- the same calls on torch tensors: they allocate
     y (and fp32 mean / rstd), pass the current stream, and raise
@@ -106,6 +106,31 @@ def add_rms_fp8_fwd(x, residual, gamma, y, residual_out, rstd, M, N, eps, scale,
                                 _addr(stream))
 
 
+class NormArgs(ctypes.Structure):
+    """norm_args of include/mi355norm.h."""
+    _fields_ = [("op", _int), ("dtype", _int), ("M", _i64), ("N", _i64),
+                ("x", _vp), ("ld_x", _i64), ("residual", _vp), ("ld_residual", _i64),
+                ("gamma", _vp), ("beta", _vp), ("y", _vp), ("ld_y", _i64),
+                ("residual_out", _vp), ("ld_residual_out", _i64), ("mean", _vp), ("rstd", _vp),
+                ("eps", _f32), ("scale", _f32)]
+
+
+_lib.norm_fwd.argtypes = [ctypes.POINTER(NormArgs), _vp]
+_lib.norm_fwd.restype = _int
+OPS = {"ln": 0, "rms": 1, "add_rms": 2, "rms_fp8": 3, "add_rms_fp8": 4}
+
+
+def norm_fwd(op, dtype, M, N, x, y, *, ld_x=0, residual=None, ld_residual=0, gamma=None, beta=None,
+             ld_y=0, residual_out=None, ld_residual_out=0, mean=None, rstd=None, eps=1e-5, scale=1.0,
+             stream=None) -> int:
+    """Any operation with row strides (elements; 0 = N), on device addresses;
+    returns the norm_status code."""
+    a = NormArgs(OPS.get(op, op), DTYPE_NAMES.get(dtype, dtype), int(M), int(N), _addr(x), int(ld_x),
+                 _addr(residual), int(ld_residual), _addr(gamma), _addr(beta), _addr(y), int(ld_y),
+                 _addr(residual_out), int(ld_residual_out), _addr(mean), _addr(rstd), float(eps), float(scale))
+    return _lib.norm_fwd(ctypes.byref(a), _addr(stream))
+
+
 def norm_status_str(status: int) -> str:
     return _lib.norm_status_str(int(status)).decode()
 
@@ -117,7 +142,7 @@ def norm_last_error() -> str:
 
 def norm_describe(op: str, M: int, N: int, dtype, aligned: bool = True) -> str:
     """How the library would run this call (path, tile, grid); launches nothing."""
-    code = {"ln": 0, "rms": 1, "add_rms": 2, "rms_fp8": 3, "add_rms_fp8": 4}[op]
+    code = OPS[op]
     dt = DTYPE_NAMES.get(dtype, dtype)
     buf = ctypes.create_string_buffer(256)
     st = _lib.norm_describe(code, int(M), int(N), int(dt), int(bool(aligned)), buf, 256)
@@ -146,85 +171,106 @@ def _param(p, N, x):
     return p.contiguous()
 
 
+def _rows(t, N):
+    """(M, N) view of t and its row stride: rows may be strided (a slice of
+    a wider matrix), elements within a row must be contiguous; anything else
+    is copied to a contiguous matrix."""
+    if t.dim() >= 1 and t.stride(-1) == 1:
+        try:
+            v = t.view(-1, N)
+            return v, (v.stride(0) if v.shape[0] > 1 else N)
+        except RuntimeError:
+            pass
+    v = t.reshape(-1, N).contiguous()
+    return v, N
+
+
 def _check(st):
     if st != NORM_OK:
         extra = f" [{norm_last_error()}]" if st == NORM_ERR_HIP else ""
         raise RuntimeError(f"{STATUS.get(st, st)}: {norm_status_str(st)}{extra}")
 
 
+def _ptr(t):
+    return t.data_ptr() if t is not None else None
+
+
+def _run(op, x2, ldx, y, ldy, *, res=None, ldr=0, hout=None, ldh=0, gamma=None, beta=None, mean=None,
+         rstd=None, eps=1e-5, scale=1.0):
+    import torch
+    M, N = x2.shape
+    with torch.cuda.device(x2.device):
+        stream = torch.cuda.current_stream(x2.device).cuda_stream
+        _check(norm_fwd(op, _torch_dtype_code(x2), M, N, _ptr(x2), _ptr(y), ld_x=ldx, residual=_ptr(res),
+                        ld_residual=ldr, gamma=_ptr(gamma), beta=_ptr(beta), ld_y=ldy,
+                        residual_out=_ptr(hout), ld_residual_out=ldh, mean=_ptr(mean), rstd=_ptr(rstd),
+                        eps=eps, scale=scale, stream=stream))
+
+
 def layer_norm(x, gamma=None, beta=None, eps: float = 1e-5, want_stats: bool = True):
-    """LayerNorm over the last dimension.  Returns (y, mean, rstd); mean and
-    rstd are fp32 [M] (None when want_stats is False)."""
+    """LayerNorm over the last dimension.  Returns (y, mean, rstd); y is
+    contiguous, mean and rstd are fp32 [M] (None when want_stats is False).
+    Rows of x may be strided (no copy)."""
     import torch
     N = x.shape[-1]
-    x2 = x.reshape(-1, N)
-    if not x2.is_contiguous():
-        x2 = x2.contiguous()
+    x2, ldx = _rows(x, N)
     M = x2.shape[0]
-    g, b = _param(gamma, N, x), _param(beta, N, x)
-    y = torch.empty_like(x2)
+    y = torch.empty((M, N), dtype=x.dtype, device=x.device)
     mean = torch.empty(M, device=x.device, dtype=torch.float32) if want_stats else None
     rstd = torch.empty(M, device=x.device, dtype=torch.float32) if want_stats else None
-    with torch.cuda.device(x.device):
-        stream = torch.cuda.current_stream(x.device).cuda_stream
-        _check(ln_fwd(x2.data_ptr(), g.data_ptr() if g is not None else None,
-                      b.data_ptr() if b is not None else None, y.data_ptr(),
-                      mean.data_ptr() if mean is not None else None,
-                      rstd.data_ptr() if rstd is not None else None,
-                      M, N, eps, _torch_dtype_code(x2), stream))
+    _run("ln", x2, ldx, y, N, gamma=_param(gamma, N, x), beta=_param(beta, N, x), mean=mean, rstd=rstd,
+         eps=eps)
     return y.view(x.shape), mean, rstd
 
 
 def rms_norm(x, gamma=None, eps: float = 1e-6, want_rstd: bool = True):
     """RMSNorm over the last dimension.  Returns (y, rstd); rstd is fp32 [M]
-    (None when want_rstd is False)."""
+    (None when want_rstd is False).  Rows of x may be strided (no copy)."""
     import torch
     N = x.shape[-1]
-    x2 = x.reshape(-1, N)
-    if not x2.is_contiguous():
-        x2 = x2.contiguous()
+    x2, ldx = _rows(x, N)
     M = x2.shape[0]
-    g = _param(gamma, N, x)
-    y = torch.empty_like(x2)
+    y = torch.empty((M, N), dtype=x.dtype, device=x.device)
     rstd = torch.empty(M, device=x.device, dtype=torch.float32) if want_rstd else None
-    with torch.cuda.device(x.device):
-        stream = torch.cuda.current_stream(x.device).cuda_stream
-        _check(rms_fwd(x2.data_ptr(), g.data_ptr() if g is not None else None, None,
-                       y.data_ptr(), None, rstd.data_ptr() if rstd is not None else None,
-                       M, N, eps, _torch_dtype_code(x2), stream))
+    _run("rms", x2, ldx, y, N, gamma=_param(gamma, N, x), rstd=rstd, eps=eps)
     return y.view(x.shape), rstd
+
+
+def _add_operands(x, residual, inplace):
+    if residual.shape != x.shape or residual.dtype != x.dtype or residual.device != x.device:
+        raise ValueError("residual must have x's shape, dtype and device")
+    N = x.shape[-1]
+    x2, ldx = _rows(x, N)
+    r2, ldr = _rows(residual, N)
+    if inplace and (r2.data_ptr() != residual.data_ptr() or
+                    (residual.dim() > 1 and r2.shape[0] > 1 and residual.view(-1, N).stride(0) != ldr)):
+        raise ValueError("inplace=True needs a residual whose rows can be viewed without a copy")
+    return x2, ldx, r2, ldr
 
 
 def fused_add_rms_norm(x, residual, gamma=None, eps: float = 1e-6, inplace: bool = False,
                        want_rstd: bool = True):
     """h = x + residual (rounded to x's dtype), y = RMSNorm(h) over the last
     dimension.  Returns (y, h, rstd).  With inplace=True, y is written into
-    x and h into residual (both must be contiguous), the way a transformer
+    x and h into residual (their rows may be strided), the way a transformer
     block updates its residual stream."""
     import torch
     N = x.shape[-1]
-    if residual.shape != x.shape or residual.dtype != x.dtype or residual.device != x.device:
-        raise ValueError("residual must have x's shape, dtype and device")
-    if inplace and not (x.is_contiguous() and residual.is_contiguous()):
-        raise ValueError("inplace=True needs contiguous x and residual")
-    x2 = x.reshape(-1, N).contiguous()
-    r2 = residual.reshape(-1, N).contiguous()
+    x2, ldx, r2, ldr = _add_operands(x, residual, inplace)
+    if inplace and x2.data_ptr() != x.data_ptr():
+        raise ValueError("inplace=True needs an x whose rows can be viewed without a copy")
     M = x2.shape[0]
-    g = _param(gamma, N, x)
-    y = x2 if inplace else torch.empty_like(x2)
-    h = r2 if inplace else torch.empty_like(r2)
+    if inplace:
+        y, ldy, h, ldh = x2, ldx, r2, ldr
+    else:
+        y, ldy = torch.empty((M, N), dtype=x.dtype, device=x.device), N
+        h, ldh = torch.empty((M, N), dtype=x.dtype, device=x.device), N
     rstd = torch.empty(M, device=x.device, dtype=torch.float32) if want_rstd else None
-    with torch.cuda.device(x.device):
-        stream = torch.cuda.current_stream(x.device).cuda_stream
-        _check(add_rms_fwd(x2.data_ptr(), r2.data_ptr(), g.data_ptr() if g is not None else None,
-                           y.data_ptr(), h.data_ptr(), rstd.data_ptr() if rstd is not None else None,
-                           M, N, eps, _torch_dtype_code(x2), stream))
+    _run("add_rms", x2, ldx, y, ldy, res=r2, ldr=ldr, hout=h, ldh=ldh, gamma=_param(gamma, N, x),
+         rstd=rstd, eps=eps)
+    if inplace:
+        return x, residual, rstd
     return y.view(x.shape), h.view(x.shape), rstd
-
-
-def _fp8_tensor(shape, device):
-    import torch
-    return torch.empty(shape, dtype=torch.uint8, device=device)
 
 
 def rms_norm_fp8(x, gamma=None, scale: float = 1.0, eps: float = 1e-6, want_rstd: bool = True):
@@ -232,16 +278,11 @@ def rms_norm_fp8(x, gamma=None, scale: float = 1.0, eps: float = 1e-6, want_rstd
     Returns (codes, rstd); codes is a torch.float8_e4m3fn tensor of x's shape."""
     import torch
     N = x.shape[-1]
-    x2 = x.reshape(-1, N).contiguous()
+    x2, ldx = _rows(x, N)
     M = x2.shape[0]
-    g = _param(gamma, N, x)
-    y = _fp8_tensor(x2.shape, x.device)
+    y = torch.empty((M, N), dtype=torch.uint8, device=x.device)
     rstd = torch.empty(M, device=x.device, dtype=torch.float32) if want_rstd else None
-    with torch.cuda.device(x.device):
-        stream = torch.cuda.current_stream(x.device).cuda_stream
-        _check(rms_fp8_fwd(x2.data_ptr(), g.data_ptr() if g is not None else None, y.data_ptr(),
-                           rstd.data_ptr() if rstd is not None else None, M, N, eps, scale,
-                           _torch_dtype_code(x2), stream))
+    _run("rms_fp8", x2, ldx, y, N, gamma=_param(gamma, N, x), rstd=rstd, eps=eps, scale=scale)
     return y.view(torch.float8_e4m3fn).view(x.shape), rstd
 
 
@@ -251,26 +292,21 @@ def fused_add_rms_norm_fp8(x, residual, gamma=None, scale: float = 1.0, eps: flo
     Returns (codes, h, rstd); with inplace=True h is written into residual."""
     import torch
     N = x.shape[-1]
-    if residual.shape != x.shape or residual.dtype != x.dtype or residual.device != x.device:
-        raise ValueError("residual must have x's shape, dtype and device")
-    if inplace and not residual.is_contiguous():
-        raise ValueError("inplace=True needs a contiguous residual")
-    x2 = x.reshape(-1, N).contiguous()
-    r2 = residual.reshape(-1, N).contiguous()
+    x2, ldx, r2, ldr = _add_operands(x, residual, inplace)
     M = x2.shape[0]
-    g = _param(gamma, N, x)
-    y = _fp8_tensor(x2.shape, x.device)
-    h = r2 if inplace else torch.empty_like(r2)
+    y = torch.empty((M, N), dtype=torch.uint8, device=x.device)
+    if inplace:
+        h, ldh = r2, ldr
+    else:
+        h, ldh = torch.empty((M, N), dtype=x.dtype, device=x.device), N
     rstd = torch.empty(M, device=x.device, dtype=torch.float32) if want_rstd else None
-    with torch.cuda.device(x.device):
-        stream = torch.cuda.current_stream(x.device).cuda_stream
-        _check(add_rms_fp8_fwd(x2.data_ptr(), r2.data_ptr(), g.data_ptr() if g is not None else None,
-                               y.data_ptr(), h.data_ptr(), rstd.data_ptr() if rstd is not None else None,
-                               M, N, eps, scale, _torch_dtype_code(x2), stream))
-    return y.view(torch.float8_e4m3fn).view(x.shape), h.view(x.shape), rstd
+    _run("add_rms_fp8", x2, ldx, y, N, res=r2, ldr=ldr, hout=h, ldh=ldh, gamma=_param(gamma, N, x),
+         rstd=rstd, eps=eps, scale=scale)
+    codes = y.view(torch.float8_e4m3fn).view(x.shape)
+    return codes, (residual if inplace else h.view(x.shape)), rstd
 
 
-__all__ = ["ln_fwd", "rms_fwd", "add_rms_fwd", "rms_fp8_fwd", "add_rms_fp8_fwd", "norm_status_str",
-           "norm_last_error", "norm_describe", "layer_norm", "rms_norm", "fused_add_rms_norm",
-           "rms_norm_fp8", "fused_add_rms_norm_fp8",
-           "NORM_F32", "NORM_F16", "NORM_BF16", "NORM_OK", "STATUS", "LIB_PATH"]
+__all__ = ["ln_fwd", "rms_fwd", "add_rms_fwd", "rms_fp8_fwd", "add_rms_fp8_fwd", "norm_fwd", "NormArgs",
+           "norm_status_str", "norm_last_error", "norm_describe", "layer_norm", "rms_norm",
+           "fused_add_rms_norm", "rms_norm_fp8", "fused_add_rms_norm_fp8",
+           "NORM_F32", "NORM_F16", "NORM_BF16", "NORM_OK", "STATUS", "LIB_PATH", "OPS"]

@@ -63,10 +63,43 @@ constexpr int64_t kMaxGrid = int64_t(1) << 20;
 
 int elem_bytes(int dtype) { return dtype == NORM_F32 ? 4 : 2; }
 
-bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
-    if (!a || !b || na <= 0 || nb <= 0) return false;
-    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
-    return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
+// A matrix in memory: `rows` rows of `row` bytes, `ld` bytes apart (a
+// vector is one row).
+struct Mat {
+    const void* p;
+    int64_t rows, row, ld;
+};
+
+int64_t floor_div(int64_t a, int64_t b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }   // b > 0
+int64_t ceil_div(int64_t a, int64_t b) { return -floor_div(-a, b); }
+
+// Whether some byte belongs to both.  Exact when one of them is a single row
+// or both have the same stride; otherwise any overlap of their spans counts.
+bool overlaps(const Mat& a, const Mat& b) {
+    if (!a.p || !b.p || a.rows <= 0 || b.rows <= 0 || a.row <= 0 || b.row <= 0) return false;
+    const int64_t a0 = (int64_t)(uintptr_t)a.p, b0 = (int64_t)(uintptr_t)b.p;
+    const int64_t a1 = a0 + (a.rows - 1) * a.ld + a.row, b1 = b0 + (b.rows - 1) * b.ld + b.row;
+    if (a1 <= b0 || b1 <= a0) return false;
+    if (a.rows == 1 && b.rows == 1) return true;
+    if (b.rows == 1 || a.rows == 1) {
+        // row i of the strided one meets the single row [s0, s0 + w)
+        const Mat& m = b.rows == 1 ? a : b;
+        const int64_t m0 = m.p == a.p ? a0 : b0;
+        const int64_t s0 = b.rows == 1 ? b0 : a0, w = b.rows == 1 ? b.row : a.row;
+        int64_t lo = floor_div(s0 - m0 - m.row, m.ld) + 1, hi = ceil_div(s0 + w - m0, m.ld) - 1;
+        lo = std::max<int64_t>(lo, 0);
+        hi = std::min<int64_t>(hi, m.rows - 1);
+        return lo <= hi;
+    }
+    if (a.ld == b.ld) {
+        // row i of a meets row j of b iff -b.row < (b0 - a0) + (j - i) * ld < a.row
+        const int64_t d = b0 - a0, L = a.ld;
+        int64_t lo = floor_div(-b.row - d, L) + 1, hi = ceil_div(a.row - d, L) - 1;
+        lo = std::max<int64_t>(lo, -(a.rows - 1));
+        hi = std::min<int64_t>(hi, b.rows - 1);
+        return lo <= hi;
+    }
+    return true;
 }
 
 bool misaligned(const void* p, int a) { return p && ((uintptr_t)p % (uintptr_t)a) != 0; }
@@ -74,37 +107,57 @@ bool misaligned(const void* p, int a) { return p && ((uintptr_t)p % (uintptr_t)a
 bool has_add(int op) { return op == OP_ADD_RMS || op == OP_ADD_RMS_Q8; }
 bool has_q8(int op) { return op == OP_RMS_Q8 || op == OP_ADD_RMS_Q8; }
 
-int validate(int op, const void* x, const void* res, const void* gamma, const void* beta, const void* y,
-             const void* hout, const float* mean, const float* rstd, int64_t M, int64_t N, float eps,
-             float scale, int dtype) {
-    if (dtype != NORM_F32 && dtype != NORM_F16 && dtype != NORM_BF16) return NORM_ERR_BAD_DTYPE;
+// Arguments of one call, row strides resolved (elements; bytes for FP8 y).
+struct Args {
+    int op, dtype;
+    int64_t M, N;
+    const void* x;
+    const void* res;
+    const void* gamma;
+    const void* beta;
+    void* y;
+    void* hout;
+    float* mean;
+    float* rstd;
+    float eps, scale;
+    int64_t ldx, ldr, ldy, ldh;
+};
+
+int validate(const Args& a) {
+    const int op = a.op;
+    if (op < 0 || op >= kOps) return NORM_ERR_BAD_ARG;
+    if (a.dtype != NORM_F32 && a.dtype != NORM_F16 && a.dtype != NORM_BF16) return NORM_ERR_BAD_DTYPE;
+    const int64_t M = a.M, N = a.N;
     if (M < 0 || N < 1 || N > kMaxN) return NORM_ERR_BAD_SHAPE;
-    const int e = elem_bytes(dtype);
-    if (M > INT64_MAX / N / e) return NORM_ERR_BAD_SHAPE;
-    if (!(eps >= 0.0f) || std::isinf(eps)) return NORM_ERR_BAD_EPS;
-    if (op != OP_LN && (beta || mean)) return NORM_ERR_BAD_ARG;
-    if (has_q8(op) && !(scale > 0.0f && std::isfinite(scale) && std::isfinite(1.0f / scale)))
+    const int e = elem_bytes(a.dtype);
+    const int ye = has_q8(op) ? 1 : e;
+    for (int64_t ld : {a.ldx, a.ldr, a.ldy, a.ldh})
+        if (ld < N || ld > INT64_MAX / 8 || (M > 0 && M - 1 > (INT64_MAX / 8 - N) / ld)) return NORM_ERR_BAD_SHAPE;
+    if (!(a.eps >= 0.0f) || std::isinf(a.eps)) return NORM_ERR_BAD_EPS;
+    if (op != OP_LN && (a.beta || a.mean)) return NORM_ERR_BAD_ARG;
+    if (has_q8(op) && !(a.scale > 0.0f && std::isfinite(a.scale) && std::isfinite(1.0f / a.scale)))
         return NORM_ERR_BAD_ARG;
     if (M == 0) return NORM_OK;
-    if (!x || !y) return NORM_ERR_NULL_ARG;
-    if (has_add(op) && (!res || !hout)) return NORM_ERR_NULL_ARG;
-    if (misaligned(x, e) || misaligned(y, has_q8(op) ? 1 : e) || misaligned(gamma, e) || misaligned(beta, e) ||
-        misaligned(res, e) || misaligned(hout, e) || misaligned(mean, 4) || misaligned(rstd, 4))
+    if (!a.x || !a.y) return NORM_ERR_NULL_ARG;
+    if (has_add(op) && (!a.res || !a.hout)) return NORM_ERR_NULL_ARG;
+    if (misaligned(a.x, e) || misaligned(a.y, ye) || misaligned(a.gamma, e) || misaligned(a.beta, e) ||
+        misaligned(a.res, e) || misaligned(a.hout, e) || misaligned(a.mean, 4) || misaligned(a.rstd, 4))
         return NORM_ERR_BAD_ARG;
-    const int64_t nx = M * N * e, nv = N * e, ns = M * 4;
-    const int64_t ny = has_q8(op) ? M * N : nx;      // FP8 output: one byte per element
     // in: 0 x, 1 res, 2 gamma, 3 beta;  out: 4 y, 5 hout, 6 mean, 7 rstd
-    struct R { const void* p; int64_t n; bool out; } r[8] = {
-        {x, nx, false}, {res, nx, false}, {gamma, nv, false}, {beta, nv, false},
-        {y, ny, true}, {hout, nx, true}, {mean, ns, true}, {rstd, ns, true}};
+    const Mat m[8] = {{a.x, M, N * e, a.ldx * e},   {a.res, M, N * e, a.ldr * e},
+                      {a.gamma, 1, N * e, N * e},   {a.beta, 1, N * e, N * e},
+                      {a.y, M, N * ye, a.ldy * ye}, {a.hout, M, N * e, a.ldh * e},
+                      {a.mean, 1, M * 4, M * 4},    {a.rstd, 1, M * 4, M * 4}};
+    const bool out[8] = {false, false, false, false, true, true, true, true};
     for (int i = 0; i < 8; ++i)
         for (int j = i + 1; j < 8; ++j) {
-            if (!(r[i].out || r[j].out) || !overlaps(r[i].p, r[i].n, r[j].p, r[j].n)) continue;
+            if (!(out[i] || out[j]) || !overlaps(m[i], m[j])) continue;
             // with the residual add, y or the sum may be written exactly over
-            // x or the residual when the element sizes match: each element is
-            // read by the lane that writes it, before it writes
+            // x or the residual (same pointer, stride and element size): each
+            // element is read by the lane that writes it, before it writes
             const bool row_io = (i == 0 || i == 1) && (j == 4 || j == 5);
-            if (has_add(op) && row_io && r[i].p == r[j].p && r[i].n == r[j].n) continue;
+            if (has_add(op) && row_io && m[i].p == m[j].p && m[i].row == m[j].row && m[i].ld == m[j].ld)
+                continue;
             return NORM_ERR_ALIAS;
         }
     return NORM_OK;
@@ -332,22 +385,31 @@ bool stream_workspace(hipStream_t stream, size_t sync_words, size_t part_bytes, 
     return true;
 }
 
-bool all_aligned16(const void* x, const void* g, const void* b, const void* y, int64_t N, int e) {
-    auto a = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
-    return (N * e) % 16 == 0 && a(x) && a(y) && a(g) && a(b);
+// The 16-byte vector path: every matrix row and vector starts on a vector
+// boundary of its own type, and N fills whole vectors.
+bool vector_aligned(const Args& a) {
+    const int e = elem_bytes(a.dtype);
+    const int epv = 16 / e;
+    auto al = [](const void* q, int b) { return ((uintptr_t)q % (uintptr_t)b) == 0; };
+    if ((a.N * e) % 16) return false;
+    for (const void* q : {a.x, a.res, (const void*)a.hout, a.gamma, a.beta})
+        if (!al(q, 16)) return false;
+    if ((a.ldx * e) % 16 || (a.ldr * e) % 16 || (a.ldh * e) % 16) return false;
+    if (has_q8(a.op)) return al(a.y, epv) && a.ldy % epv == 0;       // EPV one-byte codes
+    return al(a.y, 16) && (a.ldy * e) % 16 == 0;
 }
 
-int run(int op, const void* x, const void* res, const void* gamma, const void* beta, void* y, void* hout,
-        float* mean, float* rstd, int64_t M, int64_t N, float eps, float scale, int dtype, void* stream) {
-    int st = validate(op, x, res, gamma, beta, y, hout, mean, rstd, M, N, eps, scale, dtype);
-    if (st != NORM_OK || M == 0) return st;
+int run(const Args& a, void* stream) {
+    int st = validate(a);
+    if (st != NORM_OK || a.M == 0) return st;
+    const int op = a.op, dtype = a.dtype;
+    const int64_t M = a.M, N = a.N;
     const int e = elem_bytes(dtype);
     Plan p;
-    const bool aligned = all_aligned16(x, gamma, beta, y, N, e) && all_aligned16(res, hout, nullptr, nullptr, N, e);
-    st = make_plan(op, M, N, dtype, aligned, read_overrides(), &p);
+    st = make_plan(op, M, N, dtype, vector_aligned(a), read_overrides(), &p);
     if (st != NORM_OK) return st;
-    NormCall c{x, res, gamma, beta, y, hout, mean, rstd, M, (int)N, eps, (hipStream_t)stream,
-               has_q8(op) ? 1.0f / scale : 1.0f};
+    NormCall c{a.x, a.res, a.gamma, a.beta, a.y, a.hout, a.mean, a.rstd, M, (int)N, a.eps, (hipStream_t)stream,
+               has_q8(op) ? 1.0f / a.scale : 1.0f, Strides{a.ldx, a.ldr, a.ldy, a.ldh}};
     const int ye = has_q8(op) ? 1 : e;    // bytes per element of y
     hipError_t err;
     if (p.path == PATH_ROWS) {
@@ -383,10 +445,10 @@ int run(int op, const void* x, const void* res, const void* gamma, const void* b
         for (int64_t r0 = 0; r0 < M && err == hipSuccess; r0 += rows) {
             const int64_t mb = std::min(rows, M - r0);
             NormCall cb = c;
-            cb.x = static_cast<const char*>(c.x) + r0 * N * e;
-            cb.y = static_cast<char*>(c.y) + r0 * N * ye;
-            if (c.res) cb.res = static_cast<const char*>(c.res) + r0 * N * e;
-            if (c.hout) cb.hout = static_cast<char*>(c.hout) + r0 * N * e;
+            cb.x = static_cast<const char*>(c.x) + r0 * c.ld.x * e;
+            cb.y = static_cast<char*>(c.y) + r0 * c.ld.y * ye;
+            if (c.res) cb.res = static_cast<const char*>(c.res) + r0 * c.ld.r * e;
+            if (c.hout) cb.hout = static_cast<char*>(c.hout) + r0 * c.ld.h * e;
             cb.mean = c.mean ? c.mean + r0 : nullptr;
             cb.rstd = c.rstd ? c.rstd + r0 : nullptr;
             cb.M = mb;
@@ -408,32 +470,46 @@ int run(int op, const void* x, const void* res, const void* gamma, const void* b
 
 extern "C" {
 
+int norm_fwd(const norm_args* args, void* stream) {
+    if (!args) return NORM_ERR_NULL_ARG;
+    const norm_args& g = *args;
+    auto ld = [&](int64_t v) { return v == 0 ? g.N : v; };
+    Args a{g.op, g.dtype, g.M, g.N, g.x, g.residual, g.gamma, g.beta, g.y, g.residual_out, g.mean, g.rstd,
+           g.eps, g.scale, ld(g.ld_x), ld(g.ld_residual), ld(g.ld_y), ld(g.ld_residual_out)};
+    return run(a, stream);
+}
+
 int ln_fwd(const void* x, const void* gamma, const void* beta, void* y, float* mean, float* rstd,
            int64_t M, int64_t N, float eps, int dtype, void* stream) {
-    return run(OP_LN, x, nullptr, gamma, beta, y, nullptr, mean, rstd, M, N, eps, 1.0f, dtype, stream);
+    return run(Args{OP_LN, dtype, M, N, x, nullptr, gamma, beta, y, nullptr, mean, rstd, eps, 1.0f, N, N, N, N},
+               stream);
 }
 
 int rms_fwd(const void* x, const void* gamma, const void* beta, void* y, float* mean, float* rstd,
             int64_t M, int64_t N, float eps, int dtype, void* stream) {
-    return run(OP_RMS, x, nullptr, gamma, beta, y, nullptr, mean, rstd, M, N, eps, 1.0f, dtype, stream);
+    return run(Args{OP_RMS, dtype, M, N, x, nullptr, gamma, beta, y, nullptr, mean, rstd, eps, 1.0f, N, N, N, N},
+               stream);
 }
 
 int add_rms_fwd(const void* x, const void* residual, const void* gamma, void* y, void* residual_out,
                 float* rstd, int64_t M, int64_t N, float eps, int dtype, void* stream) {
-    return run(OP_ADD_RMS, x, residual, gamma, nullptr, y, residual_out, nullptr, rstd, M, N, eps, 1.0f,
-               dtype, stream);
+    return run(Args{OP_ADD_RMS, dtype, M, N, x, residual, gamma, nullptr, y, residual_out, nullptr, rstd, eps,
+                    1.0f, N, N, N, N},
+               stream);
 }
 
 int rms_fp8_fwd(const void* x, const void* gamma, void* y, float* rstd, int64_t M, int64_t N, float eps,
                 float scale, int dtype, void* stream) {
-    return run(OP_RMS_Q8, x, nullptr, gamma, nullptr, y, nullptr, nullptr, rstd, M, N, eps, scale, dtype,
+    return run(Args{OP_RMS_Q8, dtype, M, N, x, nullptr, gamma, nullptr, y, nullptr, nullptr, rstd, eps, scale,
+                    N, N, N, N},
                stream);
 }
 
 int add_rms_fp8_fwd(const void* x, const void* residual, const void* gamma, void* y, void* residual_out,
                     float* rstd, int64_t M, int64_t N, float eps, float scale, int dtype, void* stream) {
-    return run(OP_ADD_RMS_Q8, x, residual, gamma, nullptr, y, residual_out, nullptr, rstd, M, N, eps, scale,
-               dtype, stream);
+    return run(Args{OP_ADD_RMS_Q8, dtype, M, N, x, residual, gamma, nullptr, y, residual_out, nullptr, rstd, eps,
+                    scale, N, N, N, N},
+               stream);
 }
 
 const char* norm_status_str(int status) {

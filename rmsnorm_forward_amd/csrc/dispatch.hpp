@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "layout.hpp"
+
 namespace mi355norm {
 
 // Operations: LayerNorm, RMSNorm, residual add followed by RMSNorm, and the
@@ -26,6 +28,7 @@ struct NormCall {
     float eps;
     hipStream_t stream;
     float qinv;          // FP8 output: 1 / scale
+    Strides ld;          // row strides of x, res, y, hout
 };
 
 enum { PATH_ROWS = 0, PATH_SPLIT = 1 };

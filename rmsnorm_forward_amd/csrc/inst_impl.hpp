@@ -56,7 +56,8 @@ hipError_t go_rows(const NormCall& c, const Plan& p) {
     int N = c.N;
     float eps = c.eps;
     float qinv = c.qinv;
-    void* args[] = {&x, &r, &g, &b, &y, &h, &mean, &rstd, &M, &N, &eps, &qinv};
+    Strides ld = c.ld;
+    void* args[] = {&x, &r, &g, &b, &y, &h, &mean, &rstd, &M, &N, &ld, &eps, &qinv};
     return hipLaunchKernel(reinterpret_cast<const void*>(&norm_rows_kernel<T, RMS, ADD, Q8, TEAM, VPL, EPV>),
                            dim3((unsigned)p.grid), dim3(TeamGeom<TEAM>::WG), args, 0, c.stream);
 }
@@ -120,8 +121,9 @@ hipError_t go_split(const NormCall& c, const Plan& p, float2* ws) {
     int A = p.apply_chunks;
     float eps = c.eps;
     float qinv = c.qinv;
+    Strides ld = c.ld;
     {
-        void* args[] = {&x, &r, &h, &ws, &M, &N, &S};
+        void* args[] = {&x, &r, &h, &ws, &M, &N, &ld, &S};
         hipError_t e = hipLaunchKernel(
             reinterpret_cast<const void*>(&norm_split_stats_kernel<T, RMS, ADD, kStatsWG, kStatsVPL, EPV>),
             dim3((unsigned)p.grid), dim3(kStatsWG), args, 0, c.stream);
@@ -129,8 +131,10 @@ hipError_t go_split(const NormCall& c, const Plan& p, float2* ws) {
     }
     // with the residual add the normalising kernel reads the stored sum
     const St<T>* src = ADD ? h : x;
+    Strides lda = ld;
+    if (ADD) lda.x = ld.h;
     const float2* pp = ws;
-    void* args[] = {&src, &g, &b, &y, &pp, &mean, &rstd, &M, &N, &S, &CE, &A, &eps, &qinv};
+    void* args[] = {&src, &g, &b, &y, &pp, &mean, &rstd, &M, &N, &lda, &S, &CE, &A, &eps, &qinv};
     return hipLaunchKernel(
         reinterpret_cast<const void*>(&norm_split_apply_kernel<T, RMS, Q8, kApplyWG, kApplyVPL, EPV>),
         dim3((unsigned)p.apply_grid), dim3(kApplyWG), args, 0, c.stream);
@@ -188,7 +192,8 @@ hipError_t go_split_coop(const NormCall& c, const Plan& p, float2* ws, unsigned*
     int teams = p.teams;
     float eps = c.eps;
     float qinv = c.qinv;
-    void* args[] = {&x, &r, &g, &b, &y, &h, &mean, &rstd, &ws, &sync, &M, &N, &S, &teams, &eps, &qinv,
+    Strides ld = c.ld;
+    void* args[] = {&x, &r, &g, &b, &y, &h, &mean, &rstd, &ws, &sync, &M, &N, &ld, &S, &teams, &eps, &qinv,
                     &need, &spin_limit};
     return hipLaunchCooperativeKernel(coop_kernel<T, RMS, ADD, Q8, EPV>(), dim3((unsigned)(teams * S)),
                                       dim3(kCoopWG), args, 0, c.stream);

@@ -6,9 +6,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "layout.hpp"
+
 namespace mi355norm {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));

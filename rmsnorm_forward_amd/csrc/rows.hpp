@@ -90,7 +90,7 @@ void norm_rows_kernel(const typename T::storage* x,
                       typename T::storage* hout,
                       float* __restrict__ mean_out,
                       float* __restrict__ rstd_out,
-                      int64_t M, int N, float eps, float qinv)
+                      int64_t M, int N, Strides ld, float eps, float qinv)
 {
     static_assert(!ADD || RMS, "the residual add is fused with RMSNorm only");
     static_assert(!Q8 || RMS, "FP8 output is fused with RMSNorm only");
@@ -117,11 +117,11 @@ void norm_rows_kernel(const typename T::storage* x,
     for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x, par ^= 1) {
         const int64_t row = grp * G::ROWS + team;
         const bool row_ok = row < M;
-        // row base (wavefront-uniform when TEAM >= 64) plus 32-bit lane offsets
-        const int64_t base = (row_ok ? row : 0) * (int64_t)N;
-        const S* xr = x + base;
-        S* yr = static_cast<S*>(yv) + base;
-        uint8_t* yq = static_cast<uint8_t*>(yv) + base;
+        // row bases (wavefront-uniform when TEAM >= 64) plus 32-bit lane offsets
+        const int64_t rr = row_ok ? row : 0;
+        const S* xr = x + rr * ld.x;
+        S* yr = static_cast<S*>(yv) + rr * ld.y;
+        uint8_t* yq = static_cast<uint8_t*>(yv) + rr * ld.y;
 
         V xv[VPL];
         bool ok[VPL];
@@ -135,12 +135,12 @@ void norm_rows_kernel(const typename T::storage* x,
             V rv[VPL];
 #pragma unroll
             for (int j = 0; j < VPL; ++j)
-                if (ok[j]) rv[j].load_stream(res + base + (unsigned)(j * TEAM + tl) * EPV);
+                if (ok[j]) rv[j].load_stream(res + rr * ld.r + (unsigned)(j * TEAM + tl) * EPV);
 #pragma unroll
             for (int j = 0; j < VPL; ++j) {
                 if (!ok[j]) continue;
                 add_into(xv[j], rv[j]);
-                xv[j].put_stream(hout + base + (unsigned)(j * TEAM + tl) * EPV);
+                xv[j].put_stream(hout + rr * ld.h + (unsigned)(j * TEAM + tl) * EPV);
             }
         }
         float rs, mu = 0.0f, K = 0.0f;

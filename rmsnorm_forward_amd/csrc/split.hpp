@@ -202,9 +202,9 @@ __device__ __forceinline__ float2 load_partial_coherent(const float2* p) {
 
 // start of row `row` of an output of the I/O dtype, or of FP8 codes
 template <class T, bool Q8>
-__device__ __forceinline__ void* row_out(void* y, int64_t row, int N) {
-    if constexpr (Q8) return static_cast<uint8_t*>(y) + row * (int64_t)N;
-    else return static_cast<typename T::storage*>(y) + row * (int64_t)N;
+__device__ __forceinline__ void* row_out(void* y, int64_t row, int64_t ldy) {
+    if constexpr (Q8) return static_cast<uint8_t*>(y) + row * ldy;
+    else return static_cast<typename T::storage*>(y) + row * ldy;
 }
 
 template <bool COHERENT>
@@ -278,7 +278,7 @@ void norm_split_coop_kernel(const typename T::storage* x,
                             float2* __restrict__ part,      // [M, S] partials
                             unsigned* __restrict__ sync,    // row r: [64r], [64r+32]; zero at
                                                             // launch and again at exit
-                            int64_t M, int N, int S, int teams, float eps, float qinv,
+                            int64_t M, int N, Strides ld, int S, int teams, float eps, float qinv,
                             unsigned need, unsigned spin_limit)
 {
     static_assert(!ADD || RMS, "the residual add is fused with RMSNorm only");
@@ -292,10 +292,10 @@ void norm_split_coop_kernel(const typename T::storage* x,
     const int c = blockIdx.x - team * S;
 
     for (int64_t row = team; row < M; row += teams) {
-        const typename T::storage* xr = x + row * (int64_t)N;
+        const typename T::storage* xr = x + row * ld.x;
         C ch;
         ch.load(xr, c, NV);
-        if constexpr (ADD) ch.template add_residual<true>(res + row * (int64_t)N, hout + row * (int64_t)N);
+        if constexpr (ADD) ch.template add_residual<true>(res + row * ld.r, hout + row * ld.h);
         const float K = RMS ? 0.0f : T::widen(xr[0]);
         const float2 p = ch.template partial<RMS>(K, NV, red);
         // one 256-byte line per row: rows in flight never share a line
@@ -336,7 +336,7 @@ void norm_split_coop_kernel(const typename T::storage* x,
             if (!RMS && mean_out) mean_out[row] = K + st.x;
             if (rstd_out) rstd_out[row] = st.y;
         }
-        ch.template apply<RMS, Q8>(row_out<T, Q8>(y, row, N), gamma, beta, K, st.x, st.y, qinv);
+        ch.template apply<RMS, Q8>(row_out<T, Q8>(y, row, ld.y), gamma, beta, K, st.x, st.y, qinv);
     }
 }
 
@@ -354,7 +354,7 @@ void norm_split_stats_kernel(const typename T::storage* x,
                              const typename T::storage* res,
                              typename T::storage* hout,
                              float2* __restrict__ part,      // [M, S] partials
-                             int64_t M, int N, int S)
+                             int64_t M, int N, Strides ld, int S)
 {
     static_assert(!ADD || RMS, "the residual add is fused with RMSNorm only");
     using C = Chunk<T, WG, VPL, EPV>;
@@ -364,10 +364,10 @@ void norm_split_stats_kernel(const typename T::storage* x,
     for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
         const int64_t row = it / S;
         const int c = (int)(it - row * S);
-        const typename T::storage* xr = x + row * (int64_t)N;
+        const typename T::storage* xr = x + row * ld.x;
         C ch;
         ch.template load<false>(xr, c, NV);
-        if constexpr (ADD) ch.template add_residual<false>(res + row * (int64_t)N, hout + row * (int64_t)N);
+        if constexpr (ADD) ch.template add_residual<false>(res + row * ld.r, hout + row * ld.h);
         const float K = RMS ? 0.0f : T::widen(xr[0]);
         const float2 p = ch.template partial<RMS>(K, NV, red);
         if (threadIdx.x == 0) part[row * S + c] = p;
@@ -389,7 +389,7 @@ void norm_split_apply_kernel(const typename T::storage* x,
                              const float2* __restrict__ part,
                              float* __restrict__ mean_out,
                              float* __restrict__ rstd_out,
-                             int64_t M, int N, int S, int CE, int A, float eps, float qinv)
+                             int64_t M, int N, Strides ld, int S, int CE, int A, float eps, float qinv)
 {
     static_assert(!Q8 || RMS, "FP8 output is fused with RMSNorm only");
     using C = Chunk<T, WG, VPL, EPV>;
@@ -398,7 +398,7 @@ void norm_split_apply_kernel(const typename T::storage* x,
     for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
         const int64_t row = it / A;
         const int c = (int)(it - row * A);
-        const typename T::storage* xr = x + row * (int64_t)N;
+        const typename T::storage* xr = x + row * ld.x;
         C ch;
         ch.load(xr, c, NV);
         const float K = RMS ? 0.0f : T::widen(xr[0]);
@@ -407,7 +407,7 @@ void norm_split_apply_kernel(const typename T::storage* x,
             if (!RMS && mean_out) mean_out[row] = K + st.x;
             if (rstd_out) rstd_out[row] = st.y;
         }
-        ch.template apply<RMS, Q8>(row_out<T, Q8>(y, row, N), gamma, beta, K, st.x, st.y, qinv);
+        ch.template apply<RMS, Q8>(row_out<T, Q8>(y, row, ld.y), gamma, beta, K, st.x, st.y, qinv);
     }
 }
 

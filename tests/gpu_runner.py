@@ -110,3 +110,81 @@ def run_fp8(dtype: str, x: np.ndarray, res, gamma, eps: float, scale: float, *, 
     h = to_host(ht, dtype).reshape(M, N) if ht is not None else None
     r = rstd.cpu().numpy() if rstd is not None else None
     return q, h, r
+
+
+def _embed(a: np.ndarray, dtype: str, ld: int, offset: int, fill_bits: int):
+    """Device buffer holding the [M, N] storage array `a` with rows `ld`
+    elements apart, starting `offset` elements in; every other element holds
+    the bit pattern fill_bits.  Returns (buffer, view of the first element)."""
+    M, N = a.shape
+    tdt = TORCH_DT[dtype] if dtype != "u8" else torch.uint8
+    n = offset + (M - 1) * ld + N if M else offset
+    host = np.empty(n + 8, NP_STORAGE.get(dtype, np.uint8))
+    host.view(np.uint8 if dtype == "u8" else (np.uint32 if dtype == "f32" else np.uint16))[:] = fill_bits
+    for r in range(M):
+        host[offset + r * ld: offset + r * ld + N] = a[r]
+    if dtype == "bf16":
+        t = torch.from_numpy(host.view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(host)
+    buf = t.to("cuda")
+    return buf, buf[offset:]
+
+
+def _extract(buf, dtype: str, M: int, N: int, ld: int, offset: int):
+    """Rows out of a strided buffer, and the buffer's bytes outside the rows."""
+    h = buf.cpu()
+    if dtype == "bf16":
+        h = h.view(torch.int16).numpy().view(np.uint16)
+    else:
+        h = h.numpy()
+    rows = np.stack([h[offset + r * ld: offset + r * ld + N] for r in range(M)]) if M else h[:0]
+    mask = np.ones(h.size, bool)
+    for r in range(M):
+        mask[offset + r * ld: offset + r * ld + N] = False
+    return rows, h[mask]
+
+
+FILL = {"f32": 0x7FA5A5A5, "bf16": 0x7FA5, "f16": 0x7E5A, "u8": 0xA5}
+
+
+def run_strided(op: str, dtype: str, x, gamma, beta, eps: float, *, res=None, scale: float = 1.0,
+                ldx: int, ldy: int, ldr: int = 0, ldh: int = 0, offset: int = 0, inplace: bool = False):
+    """One norm_fwd call with strided rows.  Returns (y, h, mean, rstd) and
+    asserts that no byte between or around the rows of the outputs changed."""
+    M, N = x.shape
+    q8 = op.endswith("fp8")
+    ydt = "u8" if q8 else dtype
+    xb, xt = _embed(x, dtype, ldx, offset, FILL[dtype])
+    gt = to_device(gamma, dtype) if gamma is not None else None
+    bt = to_device(beta, dtype) if beta is not None else None
+    rb = rt = hb = ht = None
+    if res is not None:
+        rb, rt = _embed(res, dtype, ldr or N, offset, FILL[dtype])
+        if inplace:
+            hb, ht, ldh = rb, rt, (ldr or N)
+        else:
+            hb, ht = _embed(np.zeros((M, N), NP_STORAGE[dtype]), dtype, ldh or N, offset, FILL[dtype])
+    if inplace and not q8:
+        yb, yt = xb, xt
+    else:
+        yb, yt = _embed(np.zeros((M, N), np.uint8 if q8 else NP_STORAGE[dtype]), ydt, ldy, offset, FILL[ydt])
+    mean = torch.empty(M, dtype=torch.float32, device="cuda") if op == "ln" else None
+    rstd = torch.empty(M, dtype=torch.float32, device="cuda")
+    p = lambda t: t.data_ptr() if t is not None else None
+    st = rn.norm_fwd(op, CODE[dtype], M, N, p(xt), p(yt), ld_x=ldx, residual=p(rt), ld_residual=ldr,
+                     gamma=p(gt), beta=p(bt), ld_y=ldy, residual_out=p(ht), ld_residual_out=ldh,
+                     mean=p(mean), rstd=p(rstd), eps=eps, scale=scale,
+                     stream=torch.cuda.current_stream().cuda_stream)
+    assert st == rn.NORM_OK, f"{rn.STATUS.get(st)}: {rn.norm_status_str(st)} [{rn.norm_last_error()}]"
+    torch.cuda.synchronize()
+    def bits(a, dt):
+        return a.view({"f32": np.uint32, "f16": np.uint16}.get(dt, a.dtype))
+
+    y, ygap = _extract(yb, ydt, M, N, ldy, offset)
+    assert np.all(bits(ygap, ydt) == FILL[ydt]), "a write landed outside the rows of y"
+    h = None
+    if ht is not None:
+        h, hgap = _extract(hb, dtype, M, N, ldh or N, offset)
+        assert np.all(bits(hgap, dtype) == FILL[dtype]), "a write landed outside the rows of the residual sum"
+    return (y, h, mean.cpu().numpy() if mean is not None else None, rstd.cpu().numpy())

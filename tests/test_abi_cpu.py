@@ -26,7 +26,7 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["add_rms_fp8_fwd", "add_rms_fwd", "ln_fwd", "norm_describe",
+    assert declared_functions() == ["add_rms_fp8_fwd", "add_rms_fwd", "ln_fwd", "norm_describe", "norm_fwd",
                                     "norm_last_error", "norm_status_str", "rms_fp8_fwd", "rms_fwd"]
 
 
@@ -293,3 +293,67 @@ def test_overrides(monkeypatch):
     monkeypatch.delenv("MI355NORM_TILE")
     monkeypatch.setenv("MI355NORM_GRID", "1024")
     assert parse(rn.norm_describe("ln", 16384, 8192, "bf16"))["grid"] == "1024"
+
+
+# ---------------------------------------------------------------------------
+# norm_fwd: row strides
+# ---------------------------------------------------------------------------
+
+def strided(op="ln", M=4, N=64, dtype=0, **kw):
+    args = dict(x=X, y=Y, gamma=G, rstd=RSTD, eps=1e-5, scale=1.0)
+    if op == "ln":
+        args.update(beta=B, mean=MEAN)
+    if op.startswith("add"):
+        args.update(residual=R, residual_out=H)
+    args.update(kw)
+    x, y = args.pop("x"), args.pop("y")
+    return rn.norm_fwd(op, dtype, M, N, x, y, **args)
+
+
+def passes(st):
+    return st not in (ALIAS, BAD_ARG, NULL_ARG, BAD_SHAPE, BAD_DTYPE, BAD_EPS)
+
+
+def test_norm_args_layout_matches_the_header(tmp_path):
+    import subprocess
+    fields = [f[0] for f in rn.NormArgs._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "mi355norm.h"\nint main(void){\n'
+                   'printf("%zu", sizeof(norm_args));\n'
+                   + "".join(f'printf(" %zu", offsetof(norm_args, {f}));\n' for f in fields)
+                   + "return 0;}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(os.path.dirname(HEADER)), str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    want = [ctypes.sizeof(rn.NormArgs)] + [getattr(rn.NormArgs, f).offset for f in fields]
+    assert got == want
+
+
+def test_strides_are_validated():
+    assert strided(ld_x=63) == BAD_SHAPE                 # shorter than a row
+    assert strided(ld_y=1) == BAD_SHAPE
+    assert strided(op="add_rms", ld_residual=10) == BAD_SHAPE
+    assert strided(ld_x=1 << 62) == BAD_SHAPE            # the matrix would not fit 2^63 bytes
+    assert passes(strided(ld_x=0, ld_y=0))               # 0 means N
+    assert passes(strided(ld_x=100, ld_y=64))
+    assert rn.norm_fwd("ln", 0, 4, 64, X, None) == NULL_ARG
+    assert rn.norm_fwd(7, 0, 4, 64, X, Y) == BAD_ARG
+
+
+def test_strided_overlaps_are_exact_for_one_shared_stride():
+    # x and y interleaved in one [M, 2N] fp32 buffer: no common byte
+    assert passes(strided(x=X, y=X + 64 * 4, ld_x=128, ld_y=128, M=8))
+    assert strided(x=X, y=X + 32 * 4, ld_x=128, ld_y=128, M=8) == ALIAS      # half a row over
+    assert strided(x=X, y=X + 127 * 4, ld_x=128, ld_y=128, M=8) == ALIAS     # last row's tail
+    assert passes(strided(x=X + 64 * 4, y=X, ld_x=128, ld_y=128, M=8))
+    # a vector in the gap between rows of y is fine, on a row it is not
+    assert passes(strided(y=Y, ld_y=128, M=8, gamma=Y + 64 * 4, beta=None))
+    assert strided(y=Y, ld_y=128, M=8, gamma=Y + 256 * 4, beta=None) == ALIAS
+    # different strides with intersecting spans: rejected (not resolved exactly)
+    assert strided(x=X, y=X + 64 * 4, ld_x=128, ld_y=192, M=8) == ALIAS
+
+
+def test_strided_in_place_residual_needs_the_same_stride():
+    assert passes(strided(op="add_rms", residual=R, residual_out=R, ld_residual=80, ld_residual_out=80))
+    assert strided(op="add_rms", residual=R, residual_out=R, ld_residual=80, ld_residual_out=96) == ALIAS
+    assert passes(strided(op="add_rms", x=X, y=X, ld_x=72, ld_y=72))

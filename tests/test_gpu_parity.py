@@ -527,6 +527,92 @@ def test_fp8_tensor_api():
                 gpu_runner.to_host(h.reshape(24, 2048), "bf16"), rstd.cpu().numpy(), what="fp8 add tensor api")
 
 
+# ---------------------------------------------------------------------------
+# row strides (norm_fwd)
+# ---------------------------------------------------------------------------
+
+STRIDE_CASES = [
+    # (dtype, N, ldx, ldy, offset): vector path, element-wise path (row
+    # starts off 16 bytes), long rows on the split path, odd widths
+    ("bf16", 4096, 4096 + 64, 4096 + 8, 0),
+    ("bf16", 4096, 4096 + 3, 4096 + 8, 0),
+    ("f32", 1000, 1024, 1000, 4),
+    ("f16", 2056, 2056 + 8, 2056 + 16, 8),
+    ("bf16", 140000, 140000 + 8, 140008, 0),
+    ("f32", 70000, 70004, 70000 + 36, 0),
+]
+
+
+@pytest.mark.parametrize("op", ["ln", "rms", "add_rms", "rms_fp8", "add_rms_fp8"])
+@pytest.mark.parametrize("dtype,N,ldx,ldy,offset", STRIDE_CASES)
+def test_strided_rows(op, dtype, N, ldx, ldy, offset):
+    """Rows ld elements apart (no copy) give the contiguous results, and no
+    byte between the rows of an output is written."""
+    M = 5
+    print(f"[gpu] strided {op} {dtype} N={N} ldx={ldx} ldy={ldy} offset={offset}", flush=True)
+    add = op.startswith("add")
+    inp = add_inputs(dtype, M, N, seed=N + 21) if add else inputs("rms" if "rms" in op else "ln", dtype, M, N,
+                                                                   seed=N + 21)
+    scale = 0.05
+    beta = inp["beta"] if op == "ln" else None
+    y, h, mean, rstd = gpu_runner.run_strided(op, dtype, inp["x"], inp["gamma"], beta, 1e-5,
+                                              res=inp.get("res"), scale=scale, ldx=ldx, ldy=ldy,
+                                              ldr=ldx + 8, ldh=ldy + 24, offset=offset)
+    if op == "ln":
+        compare("ln", dtype, inp["x"], inp["gamma"], beta, 1e-5, y, mean, rstd, what="strided ln")
+    elif op == "rms":
+        compare("rms", dtype, inp["x"], inp["gamma"], None, 1e-5, y, None, rstd, what="strided rms")
+    elif op == "add_rms":
+        compare_add(dtype, inp["x"], inp["res"], inp["gamma"], 1e-5, y, h, rstd, what="strided add_rms")
+    else:
+        compare_fp8(dtype, inp["x"], inp.get("res"), inp["gamma"], 1e-5, scale, y, h, rstd,
+                    what=f"strided {op}")
+
+
+@pytest.mark.parametrize("N", [2048, 140000])
+def test_strided_in_place_and_interleaved(N):
+    """The fused residual add in place on strided rows; and LayerNorm of the
+    left half of a [M, 2N] buffer into its right half."""
+    M, dtype = 4, "bf16"
+    inp = add_inputs(dtype, M, N, seed=N + 22)
+    a = gpu_runner.run_strided("add_rms", dtype, inp["x"], inp["gamma"], None, 1e-6, res=inp["res"],
+                               ldx=N + 64, ldy=N + 64, ldr=N + 32, inplace=True)
+    compare_add(dtype, inp["x"], inp["res"], inp["gamma"], 1e-6, a[0], a[1], a[3], what="strided in place")
+    # interleaved: x in columns [0, N), y in [N, 2N) of one buffer
+    import rmsnorm_forward_amd as rn
+    li = inputs("ln", dtype, M, N, seed=N + 23)
+    buf = torch.zeros(M, 2 * N, dtype=torch.bfloat16, device="cuda")
+    buf[:, :N] = gpu_runner.to_device(li["x"], dtype).view(M, N)
+    gt, bt = gpu_runner.to_device(li["gamma"], dtype), gpu_runner.to_device(li["beta"], dtype)
+    mean = torch.empty(M, device="cuda")
+    rstd = torch.empty(M, device="cuda")
+    st = rn.norm_fwd("ln", dtype, M, N, buf.data_ptr(), buf[:, N:].data_ptr(), ld_x=2 * N, ld_y=2 * N,
+                     gamma=gt.data_ptr(), beta=bt.data_ptr(), mean=mean.data_ptr(), rstd=rstd.data_ptr(),
+                     eps=1e-5, stream=torch.cuda.current_stream().cuda_stream)
+    assert st == rn.NORM_OK
+    torch.cuda.synchronize()
+    y = gpu_runner.to_host(buf[:, N:].contiguous().view(-1), dtype).reshape(M, N)
+    x_after = gpu_runner.to_host(buf[:, :N].contiguous().view(-1), dtype).reshape(M, N)
+    assert np.array_equal(x_after, li["x"])
+    compare("ln", dtype, li["x"], li["gamma"], li["beta"], 1e-5, y, mean.cpu().numpy(), rstd.cpu().numpy(),
+            what="interleaved")
+
+
+def test_tensor_api_takes_strided_rows_without_copy():
+    import rmsnorm_forward_amd as rn
+    M, N = 6, 1024
+    li = inputs("ln", "bf16", M, N, seed=24)
+    big = torch.zeros(M, N + 128, dtype=torch.bfloat16, device="cuda")
+    big[:, 64:64 + N] = gpu_runner.to_device(li["x"], "bf16").view(M, N)
+    xv = big[:, 64:64 + N]                          # strided view, not contiguous
+    assert not xv.is_contiguous()
+    y, mean, rstd = rn.layer_norm(xv, gpu_runner.to_device(li["gamma"], "bf16"),
+                                  gpu_runner.to_device(li["beta"], "bf16"), eps=1e-5)
+    compare("ln", "bf16", li["x"], li["gamma"], li["beta"], 1e-5,
+            gpu_runner.to_host(y.reshape(-1), "bf16").reshape(M, N), mean.cpu().numpy(), rstd.cpu().numpy(),
+            what="tensor api strided")
+
+
 def test_m_zero_launches_nothing():
     import rmsnorm_forward_amd as rn
     st = rn.ln_fwd(None, None, None, None, None, None, 0, 128, 1e-5, rn.NORM_BF16,
