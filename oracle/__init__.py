@@ -81,6 +81,10 @@ class Oracle:
         lib.oracle_add_rms_fwd.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64,
                                            ctypes.c_double, vp, vp, vp]
         lib.oracle_add_rms_fwd.restype = ctypes.c_int
+        lib.oracle_ln_bwd.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, vp, vp, vp, vp, vp]
+        lib.oracle_ln_bwd.restype = ctypes.c_int
+        lib.oracle_rms_bwd.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, vp, vp, vp]
+        lib.oracle_rms_bwd.restype = ctypes.c_int
         lib.oracle_quant_e4m3.argtypes = [vp, i64, ctypes.c_double, vp]
         lib.oracle_quant_e4m3.restype = None
         lib.oracle_round.argtypes = [vp, i64, ctypes.c_int, vp]
@@ -139,6 +143,39 @@ class Oracle:
             raise ValueError("oracle_add_rms_fwd rejected its arguments")
         return h, y, rstd
 
+    def ln_bwd(self, dy, x, gamma, dtype: str, mean, rstd):
+        """LayerNorm backward from the forward's mean / rstd (any float
+        arrays, used as doubles) -> (dx, dgamma, dbeta) float64."""
+        x = _check_storage(x, dtype)
+        M, N = x.shape
+        dy = _check_storage(dy, dtype, M * N)
+        gamma = _check_storage(gamma, dtype, N)
+        mean = np.ascontiguousarray(mean, np.float64)
+        rstd = np.ascontiguousarray(rstd, np.float64)
+        dx = np.empty((M, N), np.float64)
+        dg = np.empty(N, np.float64)
+        db = np.empty(N, np.float64)
+        rc = self.lib.oracle_ln_bwd(_ptr(dy), _ptr(x), _ptr(gamma), DTYPE_CODE[dtype], M, N, _ptr(mean),
+                                    _ptr(rstd), _ptr(dx), _ptr(dg), _ptr(db))
+        if rc != 0:
+            raise ValueError("oracle_ln_bwd rejected its arguments")
+        return dx, dg, db
+
+    def rms_bwd(self, dy, x, gamma, dtype: str, rstd):
+        """RMSNorm backward from the forward's rstd -> (dx, dgamma) float64."""
+        x = _check_storage(x, dtype)
+        M, N = x.shape
+        dy = _check_storage(dy, dtype, M * N)
+        gamma = _check_storage(gamma, dtype, N)
+        rstd = np.ascontiguousarray(rstd, np.float64)
+        dx = np.empty((M, N), np.float64)
+        dg = np.empty(N, np.float64)
+        rc = self.lib.oracle_rms_bwd(_ptr(dy), _ptr(x), _ptr(gamma), DTYPE_CODE[dtype], M, N, _ptr(rstd),
+                                     _ptr(dx), _ptr(dg))
+        if rc != 0:
+            raise ValueError("oracle_rms_bwd rejected its arguments")
+        return dx, dg
+
     def quant_e4m3(self, v, scale: float):
         """OCP E4M3 codes (uint8) of v / scale, saturated to +-448, RNE."""
         v = np.ascontiguousarray(v, dtype=np.float64)
@@ -194,6 +231,14 @@ def rms_fwd(x, gamma, dtype: str, eps: float):
 
 def add_rms_fwd(x, res, gamma, dtype: str, eps: float):
     return default().add_rms_fwd(x, res, gamma, dtype, eps)
+
+
+def ln_bwd(dy, x, gamma, dtype: str, mean, rstd):
+    return default().ln_bwd(dy, x, gamma, dtype, mean, rstd)
+
+
+def rms_bwd(dy, x, gamma, dtype: str, rstd):
+    return default().rms_bwd(dy, x, gamma, dtype, rstd)
 
 
 def quant_e4m3(v, scale: float):

@@ -33,6 +33,13 @@
  *                 as code = FP8(clamp(y / scale, +-max)) with one static fp32
  *                 scale per call, FP8 being OCP E4M3 (the format gfx950
  *                 converts to natively), round-to-nearest-even.
+ *   Backward     -- "CUDA 算子工程" ch. 7, section 7.7: the LayerNorm gradients
+ *                 dgamma_i = sum_n dy_i xhat_i, dbeta_i = sum_n dy_i and
+ *                 dx_i = rstd (g_i - mean(g) - xhat_i mean(g xhat)) with
+ *                 g = dy * gamma and xhat = (x - mean) rstd, from the mean and
+ *                 rstd the forward pass stored; RMSNorm's needs one in-row sum,
+ *                 of dy gamma x (its formula is the derivative of the forward
+ *                 definition, worked out below).
  *   Output rounding -- round-to-nearest-even from the double result straight
  *                 to the storage type (no intermediate float rounding).  The
  *                 pages only say the result is cast to the output dtype
@@ -307,4 +314,79 @@ void oracle_quant_e4m3(const double *v, int64_t n, double scale, uint8_t *code)
 {
     for (int64_t i = 0; i < n; ++i)
         code[i] = double_to_e4m3_code(v[i] / scale);
+}
+
+/* ---- LayerNorm backward ---------------------------------------------------
+ *
+ * For every row r, with mean_r and rstd_r as given (the forward pass's):
+ *   xhat_i = (x_i - mean_r) * rstd_r,   g_i = dy_i * gamma_i
+ *   gbar   = (sum_i g_i) / N,           gxbar = (sum_i g_i * xhat_i) / N
+ *   dx_i   = rstd_r * (g_i - gbar - xhat_i * gxbar)
+ * and over all rows
+ *   dgamma_i = sum_r dy_i * xhat_i,     dbeta_i = sum_r dy_i
+ * gamma == NULL means gamma_i = 1.  dx, dgamma, dbeta are written in double
+ * and may each be NULL.  Returns 0 or -1.
+ */
+int oracle_ln_bwd(const void *dy, const void *x, const void *gamma, int dtype, int64_t M, int64_t N,
+                  const double *mean, const double *rstd, double *dx, double *dgamma, double *dbeta)
+{
+    if (dtype < OR_F32 || dtype > OR_F64 || M < 0 || N < 1 || !mean || !rstd)
+        return -1;
+    if (dgamma) for (int64_t i = 0; i < N; ++i) dgamma[i] = 0.0;
+    if (dbeta) for (int64_t i = 0; i < N; ++i) dbeta[i] = 0.0;
+    for (int64_t r = 0; r < M; ++r) {
+        int64_t base = r * N;
+        double sg = 0.0, sgx = 0.0;
+        for (int64_t i = 0; i < N; ++i) {
+            double xhat = (load_elem(x, base + i, dtype) - mean[r]) * rstd[r];
+            double g = load_elem(dy, base + i, dtype) * (gamma ? load_elem(gamma, i, dtype) : 1.0);
+            sg += g;
+            sgx += g * xhat;
+        }
+        double gbar = sg / (double)N, gxbar = sgx / (double)N;
+        for (int64_t i = 0; i < N; ++i) {
+            double d = load_elem(dy, base + i, dtype);
+            double xhat = (load_elem(x, base + i, dtype) - mean[r]) * rstd[r];
+            double g = d * (gamma ? load_elem(gamma, i, dtype) : 1.0);
+            if (dx) dx[base + i] = rstd[r] * (g - gbar - xhat * gxbar);
+            if (dgamma) dgamma[i] += d * xhat;
+            if (dbeta) dbeta[i] += d;
+        }
+    }
+    return 0;
+}
+
+/* ---- RMSNorm backward -----------------------------------------------------
+ *
+ * y_i = x_i * rstd * gamma_i with rstd = (sum_j x_j^2 / N + eps)^(-1/2), so
+ * d rstd / d x_j = -rstd^3 x_j / N and, with g = dy * gamma,
+ *   dx_i     = rstd * g_i - x_i * rstd^3 * (sum_j g_j x_j) / N
+ *   dgamma_i = sum_r dy_i * x_i * rstd_r
+ * rstd_r as given (the forward pass's).  dx, dgamma may be NULL.  Returns 0
+ * or -1.
+ */
+int oracle_rms_bwd(const void *dy, const void *x, const void *gamma, int dtype, int64_t M, int64_t N,
+                   const double *rstd, double *dx, double *dgamma)
+{
+    if (dtype < OR_F32 || dtype > OR_F64 || M < 0 || N < 1 || !rstd)
+        return -1;
+    if (dgamma) for (int64_t i = 0; i < N; ++i) dgamma[i] = 0.0;
+    for (int64_t r = 0; r < M; ++r) {
+        int64_t base = r * N;
+        double sgx = 0.0;
+        for (int64_t i = 0; i < N; ++i) {
+            double g = load_elem(dy, base + i, dtype) * (gamma ? load_elem(gamma, i, dtype) : 1.0);
+            sgx += g * load_elem(x, base + i, dtype);
+        }
+        double rs = rstd[r];
+        double c = rs * rs * rs * sgx / (double)N;
+        for (int64_t i = 0; i < N; ++i) {
+            double d = load_elem(dy, base + i, dtype);
+            double xv = load_elem(x, base + i, dtype);
+            double g = d * (gamma ? load_elem(gamma, i, dtype) : 1.0);
+            if (dx) dx[base + i] = rs * g - xv * c;
+            if (dgamma) dgamma[i] += d * xv * rs;
+        }
+    }
+    return 0;
 }

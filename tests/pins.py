@@ -614,6 +614,100 @@ def pin_rms_fp8_brute_force(orc):
                 assert q[r, i] == want, (dtype, n, r, i)
 
 
+# --------------------------------------------------------------------------
+# backward
+# --------------------------------------------------------------------------
+
+def _bwd_cases(seed=51):
+    rng = np.random.default_rng(seed)
+    out = []
+    for n in (1, 2, 5, 16, 33):
+        x = (rng.choice([0.0, 4.0, -30.0]) + rng.choice([1.0, 0.2]) * rng.standard_normal((3, n)))
+        dy = rng.standard_normal((3, n))
+        gm = rng.uniform(-1.5, 1.5, n)
+        bt = rng.normal(0, 0.3, n)
+        out.append((x, dy, gm, bt, float(rng.choice([1e-5, 0.1]))))
+    return out
+
+
+def pin_backward_finite_differences(orc):
+    """Central differences of the (pinned) forward oracle: L = sum(dy * y),
+    dL/dx, dL/dgamma, dL/dbeta against the backward oracle."""
+    for x, dy, gm, bt, eps in _bwd_cases():
+        M, n = x.shape
+        _, mean, rstd = orc.ln_fwd(x, gm, bt, "f64", eps, exact_eps=True)
+        dx, dg, db = orc.ln_bwd(dy, x, gm, "f64", mean, rstd)
+        _, rr = orc.rms_fwd(x, gm, "f64", eps, exact_eps=True)
+        rdx, rdg = orc.rms_bwd(dy, x, gm, "f64", rr)
+
+        def L(xx, gg, bb, rms=False):
+            if rms:
+                return float((dy * orc.rms_fwd(xx, gg, "f64", eps, exact_eps=True)[0]).sum())
+            return float((dy * orc.ln_fwd(xx, gg, bb, "f64", eps, exact_eps=True)[0]).sum())
+
+        for rms, gx, gg, gb in ((False, dx, dg, db), (True, rdx, rdg, None)):
+            scale = max(1.0, float(np.abs(gx).max()), float(np.abs(gg).max()))
+            for r in range(M):
+                for i in range(n):
+                    h = 1e-6 * max(1.0, abs(x[r, i]))
+                    xp, xm = x.copy(), x.copy()
+                    xp[r, i] += h
+                    xm[r, i] -= h
+                    num = (L(xp, gm, bt, rms) - L(xm, gm, bt, rms)) / (2 * h)
+                    assert abs(num - gx[r, i]) <= 1e-6 * scale, (rms, n, r, i, num, gx[r, i])
+            for i in range(n):
+                gp, gmn = gm.copy(), gm.copy()
+                gp[i] += 1e-6
+                gmn[i] -= 1e-6
+                num = (L(x, gp, bt, rms) - L(x, gmn, bt, rms)) / 2e-6
+                assert abs(num - gg[i]) <= 1e-6 * scale, (rms, n, i, num, gg[i])
+                if gb is not None:
+                    bp, bm = bt.copy(), bt.copy()
+                    bp[i] += 1e-6
+                    bm[i] -= 1e-6
+                    num = (L(x, gm, bp) - L(x, gm, bm)) / 2e-6
+                    assert abs(num - gb[i]) <= 1e-6 * scale, (n, i, num, gb[i])
+
+
+def pin_backward_library_and_invariants(orc):
+    """float64 torch autograd of layer_norm / rms_norm, and the invariants:
+    LayerNorm dx sums to 0 over a row, and (eps = 0) dx is orthogonal to
+    xhat; RMSNorm (eps = 0) dx is orthogonal to x."""
+    import torch
+    import torch.nn.functional as F
+    rng = np.random.default_rng(53)
+    for n in (7, 256, 1000):
+        x = (2.0 + rng.standard_normal((4, n))).astype(np.float32)
+        dy = rng.standard_normal((4, n)).astype(np.float32)
+        gm = rng.uniform(0.5, 1.5, n).astype(np.float32)
+        bt = rng.normal(0, 0.1, n).astype(np.float32)
+        e = float(np.float32(1e-5))
+        _, mean, rstd = orc.ln_fwd(x, gm, bt, "f32", 1e-5)
+        dx, dg, db = orc.ln_bwd(dy, x, gm, "f32", mean, rstd)
+        xt = torch.from_numpy(x).double().requires_grad_()
+        gt = torch.from_numpy(gm).double().requires_grad_()
+        bt_ = torch.from_numpy(bt).double().requires_grad_()
+        F.layer_norm(xt, (n,), gt, bt_, e).backward(torch.from_numpy(dy).double())
+        assert np.max(np.abs(dx - xt.grad.numpy())) <= 1e-10
+        assert np.max(np.abs(dg - gt.grad.numpy())) <= 1e-9 and np.max(np.abs(db - bt_.grad.numpy())) <= 1e-9
+        assert np.max(np.abs(dx.sum(axis=1))) <= 1e-10 * np.abs(dx).max()
+        _, r = orc.rms_fwd(x, gm, "f32", 1e-6)
+        rdx, rdg = orc.rms_bwd(dy, x, gm, "f32", r)
+        xt = torch.from_numpy(x).double().requires_grad_()
+        gt = torch.from_numpy(gm).double().requires_grad_()
+        F.rms_norm(xt, (n,), gt, float(np.float32(1e-6))).backward(torch.from_numpy(dy).double())
+        assert np.max(np.abs(rdx - xt.grad.numpy())) <= 1e-10
+        assert np.max(np.abs(rdg - gt.grad.numpy())) <= 1e-9
+        # eps = 0 orthogonality
+        _, mean0, rstd0 = orc.ln_fwd(x, gm, bt, "f32", 0.0)
+        dx0, _, _ = orc.ln_bwd(dy, x, gm, "f32", mean0, rstd0)
+        xhat = (x.astype(np.float64) - mean0[:, None]) * rstd0[:, None]
+        assert np.max(np.abs((dx0 * xhat).sum(axis=1))) <= 1e-9 * np.abs(dx0).max() * n
+        _, r0 = orc.rms_fwd(x, gm, "f32", 0.0)
+        rdx0, _ = orc.rms_bwd(dy, x, gm, "f32", r0)
+        assert np.max(np.abs((rdx0 * x).sum(axis=1))) <= 1e-9 * np.abs(rdx0 * x).max() * n
+
+
 ALL_PINS = [
     pin_large_mean_row_decimal,
     pin_large_mean_row_fp32,
@@ -632,4 +726,6 @@ ALL_PINS = [
     pin_add_rms_library,
     pin_e4m3_quantisation,
     pin_rms_fp8_brute_force,
+    pin_backward_finite_differences,
+    pin_backward_library_and_invariants,
 ]

@@ -43,7 +43,8 @@ MUTANTS = {
     "ln_naive_variance": ("double d = load_elem(x, base + i, dtype) - mu;\n            q += d * d;",
                           "double d = load_elem(x, base + i, dtype);\n            q += d * d - mu * mu;"),
     "ln_mean_divisor": ("double mu = s / (double)N;", "double mu = s / (double)(N + 1);"),
-    "ln_row_stride": ("int64_t base = r * N;\n        double s", "int64_t base = r * (N - 1);\n        double s"),
+    "ln_row_stride": ("int64_t base = r * N;\n        double s = 0.0;",
+                      "int64_t base = r * (N - 1);\n        double s = 0.0;"),
     "rms_drop_gamma": ("y[base + i] = load_elem(x, base + i, dtype) * rs * g;",
                        "y[base + i] = load_elem(x, base + i, dtype) * rs;"),
     "rms_eps_outside_root": ("double rs = 1.0 / sqrt(ms + eps);", "double rs = 1.0 / sqrt(ms) + eps;"),
@@ -65,6 +66,17 @@ MUTANTS = {
     "fp8_exponent_bias_8": ("(e - 1 + 7) << 3", "(e - 1 + 8) << 3"),
     "fp8_subnormal_threshold": ("if (e - 1 < -6)", "if (e - 1 < -7)"),
     "fp8_precision_off_by_one": ("rne_to_format(a, 4, -6)", "rne_to_format(a, 3, -6)"),
+    "bwd_gamma_outside_bracket": ("if (dx) dx[base + i] = rstd[r] * (g - gbar - xhat * gxbar);",
+                                  "if (dx) dx[base + i] = (gamma ? load_elem(gamma, i, dtype) : 1.0) * rstd[r]"
+                                  " * (d - gbar - xhat * gxbar);"),
+    "bwd_missing_gbar": ("rstd[r] * (g - gbar - xhat * gxbar)", "rstd[r] * (g - xhat * gxbar)"),
+    "bwd_xhat_term_sign": ("rstd[r] * (g - gbar - xhat * gxbar)", "rstd[r] * (g - gbar + xhat * gxbar)"),
+    "bwd_dgamma_without_xhat": ("if (dgamma) dgamma[i] += d * xhat;", "if (dgamma) dgamma[i] += d;"),
+    "bwd_dbeta_with_xhat": ("if (dbeta) dbeta[i] += d;", "if (dbeta) dbeta[i] += d * xhat;"),
+    "bwd_gxbar_divisor": ("gxbar = sgx / (double)N;", "gxbar = sgx / (double)(N - 1);"),
+    "rms_bwd_missing_x_term": ("if (dx) dx[base + i] = rs * g - xv * c;", "if (dx) dx[base + i] = rs * g;"),
+    "rms_bwd_rstd_squared": ("double c = rs * rs * rs * sgx / (double)N;", "double c = rs * rs * sgx / (double)N;"),
+    "rms_bwd_dgamma_without_rstd": ("if (dgamma) dgamma[i] += d * xv * rs;", "if (dgamma) dgamma[i] += d * xv;"),
     "add_rms_wrong_operand": ("double s = load_elem(x, i, dtype) + load_elem(res, i, dtype);",
                               "double s = load_elem(x, i, dtype) + load_elem(x, i, dtype);"),
 }
