@@ -1,5 +1,6 @@
 /*
- * mi355norm.h -- C ABI of the row-wise LayerNorm / RMSNorm forward library
+ * mi355norm.h -- C ABI of the row-wise LayerNorm / RMSNorm library (forward,
+ * fused residual add, FP8 output, and the backward)
  * for AMD Instinct MI355X (gfx950, CDNA4).  Library: libmi355norm.so.
  *
  * The operations (page titles as printed on the pages they come from):
@@ -197,6 +198,44 @@ typedef struct {
  */
 int norm_fwd(const norm_args *args, void *stream);
 
+/*
+ * Backward of ln_fwd and rms_fwd ("CUDA 算子工程" ch. 7, section 7.7), from
+ * the fp32 mean and rstd the forward stored per row.  With g = dy * gamma:
+ *
+ *   LayerNorm   xhat[r,i] = (x[r,i] - mean_r) * rstd_r
+ *               dx[r,i]   = rstd_r * (g[r,i] - (1/N) sum_j g[r,j]
+ *                                    - xhat[r,i] * (1/N) sum_j g[r,j] xhat[r,j])
+ *               dgamma[i] = sum_r dy[r,i] * xhat[r,i],   dbeta[i] = sum_r dy[r,i]
+ *   RMSNorm     dx[r,i]   = rstd_r * g[r,i]
+ *                           - x[r,i] * rstd_r^3 * (1/N) sum_j g[r,j] x[r,j]
+ *               dgamma[i] = sum_r dy[r,i] * x[r,i] * rstd_r
+ *
+ *   dy, x, dx   device pointers to contiguous [M, N] arrays of `dtype`.  dx
+ *               may be exactly dy or x (in place); any other overlap of an
+ *               output with an input or another output is NORM_ERR_ALIAS.
+ *   gamma       [N] of `dtype`, or NULL meaning gamma = 1.
+ *   mean, rstd  fp32 [M] as ln_fwd / rms_fwd wrote them (mean: LayerNorm only).
+ *               Required when M > 0 (NORM_ERR_NULL_ARG otherwise).
+ *   dgamma,     fp32 [N] device pointers, or NULL: not computed.  Written
+ *   dbeta       (zeros when M == 0); dbeta exists for LayerNorm only.
+ *   M, N        M >= 0; 1 <= N <= 32768 when dy, x, gamma and dx are 16-byte
+ *               aligned and N * element size is a multiple of 16, N <= 16384
+ *               otherwise (longer rows: NORM_ERR_BAD_SHAPE).
+ *
+ * Arithmetic is fp32; dx is rounded to `dtype` (round-to-nearest-even).
+ * dgamma and dbeta are summed in a fixed order (per-workgroup partial rows,
+ * then a column sum over them), so repeated calls on one device give the
+ * same bits.  The partial rows (fp32 [grid, N] each) live in a workspace the
+ * library keeps per (device, stream), grown when a call needs more; growing
+ * waits for the stream.  Calls run asynchronously on `stream`.  Returns a
+ * norm_status.
+ */
+int ln_bwd(const void *dy, const void *x, const void *gamma, const float *mean, const float *rstd,
+           void *dx, float *dgamma, float *dbeta, int64_t M, int64_t N, int dtype, void *stream);
+
+int rms_bwd(const void *dy, const void *x, const void *gamma, const float *rstd, void *dx,
+            float *dgamma, int64_t M, int64_t N, int dtype, void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *norm_status_str(int status);
 
@@ -219,6 +258,14 @@ const char *norm_last_error(void);
  */
 int norm_describe(int op, int64_t M, int64_t N, int dtype, int aligned,
                   char *buf, int buflen);
+
+/*
+ * As norm_describe, for ln_bwd (rms = 0) or rms_bwd (rms = 1): lanes per
+ * row, vectors per lane, workgroup size, grid (= partial rows of dgamma and
+ * dbeta).  Returns NORM_ERR_BAD_SHAPE for rows the backward cannot hold.
+ */
+int norm_bwd_describe(int rms, int64_t M, int64_t N, int dtype, int aligned,
+                      char *buf, int buflen);
 
 #ifdef __cplusplus
 }

@@ -6,13 +6,17 @@ only marshals arguments.  PyTorch is used for device memory and streams.
 
 Two layers:
   * ln_fwd / rms_fwd / add_rms_fwd / rms_fp8_fwd / add_rms_fp8_fwd /
-    norm_fwd (row strides) / norm_status_str / norm_last_error /
-    norm_describe -- the C ABI entry points under the same names, taking raw
-    device addresses (ints) and returning the status code;
+    norm_fwd (row strides) / ln_bwd / rms_bwd / norm_status_str /
+    norm_last_error / norm_describe / norm_bwd_describe -- the C ABI entry
+    points under the same names, taking raw device addresses (ints) and
+    returning the status code;
   * layer_norm / rms_norm / fused_add_rms_norm / rms_norm_fp8 /
     fused_add_rms_norm_fp8 -- the same calls on torch tensors: they allocate
     y (and fp32 mean / rstd), pass the current stream, and raise
-    RuntimeError with the library's message on a non-zero status.
+    RuntimeError with the library's message on a non-zero status;
+    layer_norm_backward / rms_norm_backward take the saved statistics, and
+    layer_norm_autograd / rms_norm_autograd wrap forward and backward as
+    torch autograd functions.
 
 Importing this package raises ImportError if the library has not been built
 (`python rmsnorm_forward_amd/build.py`): there is no fallback path.
@@ -58,6 +62,12 @@ _lib.norm_last_error.argtypes = []
 _lib.norm_last_error.restype = ctypes.c_char_p
 _lib.norm_describe.argtypes = [_int, _i64, _i64, _int, _int, ctypes.c_char_p, _int]
 _lib.norm_describe.restype = _int
+_lib.ln_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _int, _vp]
+_lib.ln_bwd.restype = _int
+_lib.rms_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _int, _vp]
+_lib.rms_bwd.restype = _int
+_lib.norm_bwd_describe.argtypes = [_int, _i64, _i64, _int, _int, ctypes.c_char_p, _int]
+_lib.norm_bwd_describe.restype = _int
 
 NORM_F32, NORM_F16, NORM_BF16 = 0, 1, 2
 NORM_OK = 0
@@ -106,6 +116,19 @@ def add_rms_fp8_fwd(x, residual, gamma, y, residual_out, rstd, M, N, eps, scale,
                                 _addr(stream))
 
 
+def ln_bwd(dy, x, gamma, mean, rstd, dx, dgamma, dbeta, M, N, dtype, stream) -> int:
+    """LayerNorm backward on device addresses (dgamma / dbeta fp32 [N] or
+    None); returns the norm_status code."""
+    return _lib.ln_bwd(_addr(dy), _addr(x), _addr(gamma), _addr(mean), _addr(rstd), _addr(dx), _addr(dgamma),
+                       _addr(dbeta), int(M), int(N), int(dtype), _addr(stream))
+
+
+def rms_bwd(dy, x, gamma, rstd, dx, dgamma, M, N, dtype, stream) -> int:
+    """RMSNorm backward on device addresses; returns the norm_status code."""
+    return _lib.rms_bwd(_addr(dy), _addr(x), _addr(gamma), _addr(rstd), _addr(dx), _addr(dgamma), int(M),
+                        int(N), int(dtype), _addr(stream))
+
+
 class NormArgs(ctypes.Structure):
     """norm_args of include/mi355norm.h."""
     _fields_ = [("op", _int), ("dtype", _int), ("M", _i64), ("N", _i64),
@@ -146,6 +169,18 @@ def norm_describe(op: str, M: int, N: int, dtype, aligned: bool = True) -> str:
     dt = DTYPE_NAMES.get(dtype, dtype)
     buf = ctypes.create_string_buffer(256)
     st = _lib.norm_describe(code, int(M), int(N), int(dt), int(bool(aligned)), buf, 256)
+    if st != NORM_OK:
+        raise RuntimeError(norm_status_str(st))
+    return buf.value.decode()
+
+
+def norm_bwd_describe(op: str, M: int, N: int, dtype, aligned: bool = True) -> str:
+    """How ln_bwd (op "ln") or rms_bwd (op "rms") would run; launches nothing."""
+    if op not in ("ln", "rms"):
+        raise ValueError("op must be 'ln' or 'rms'")
+    dt = DTYPE_NAMES.get(dtype, dtype)
+    buf = ctypes.create_string_buffer(256)
+    st = _lib.norm_bwd_describe(int(op == "rms"), int(M), int(N), int(dt), int(bool(aligned)), buf, 256)
     if st != NORM_OK:
         raise RuntimeError(norm_status_str(st))
     return buf.value.decode()
@@ -306,7 +341,106 @@ def fused_add_rms_norm_fp8(x, residual, gamma=None, scale: float = 1.0, eps: flo
     return codes, (residual if inplace else h.view(x.shape)), rstd
 
 
+def _bwd_operands(dy, x, gamma, stats):
+    import torch
+    if dy.shape != x.shape or dy.dtype != x.dtype or dy.device != x.device:
+        raise ValueError("dy must have x's shape, dtype and device")
+    N = x.shape[-1]
+    M = x.numel() // N if N else 0
+    for s in stats:
+        if s.dtype != torch.float32 or s.numel() != M or s.device != x.device:
+            raise ValueError("mean / rstd must be fp32 with one value per row, on x's device")
+    return (M, N, dy.reshape(M, N).contiguous(), x.reshape(M, N).contiguous(), _param(gamma, N, x),
+            [s.contiguous() for s in stats])
+
+
+def layer_norm_backward(dy, x, mean, rstd, gamma=None, want_dgamma: bool = True, want_dbeta: bool = True):
+    """Gradients of layer_norm from its saved fp32 mean and rstd: returns
+    (dx, dgamma, dbeta); dx has x's shape and dtype, dgamma and dbeta are
+    fp32 [N] (None when not wanted)."""
+    import torch
+    M, N, dy2, x2, g, (mean, rstd) = _bwd_operands(dy, x, gamma, (mean, rstd))
+    dx = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    dgamma = torch.empty(N, dtype=torch.float32, device=x.device) if want_dgamma else None
+    dbeta = torch.empty(N, dtype=torch.float32, device=x.device) if want_dbeta else None
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        _check(ln_bwd(_ptr(dy2), _ptr(x2), _ptr(g), _ptr(mean), _ptr(rstd), _ptr(dx), _ptr(dgamma),
+                      _ptr(dbeta), M, N, _torch_dtype_code(x), stream))
+    return dx.view(x.shape), dgamma, dbeta
+
+
+def rms_norm_backward(dy, x, rstd, gamma=None, want_dgamma: bool = True):
+    """Gradients of rms_norm from its saved fp32 rstd: returns (dx, dgamma);
+    dgamma is fp32 [N] (None when not wanted)."""
+    import torch
+    M, N, dy2, x2, g, (rstd,) = _bwd_operands(dy, x, gamma, (rstd,))
+    dx = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    dgamma = torch.empty(N, dtype=torch.float32, device=x.device) if want_dgamma else None
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        _check(rms_bwd(_ptr(dy2), _ptr(x2), _ptr(g), _ptr(rstd), _ptr(dx), _ptr(dgamma), M, N,
+                       _torch_dtype_code(x), stream))
+    return dx.view(x.shape), dgamma
+
+
+def _autograd():
+    import torch
+
+    class LayerNormFn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, x, gamma, beta, eps):
+            y, mean, rstd = layer_norm(x, gamma, beta, eps)
+            ctx.save_for_backward(x, gamma, mean, rstd)
+            ctx.has_beta = beta is not None
+            return y
+
+        @staticmethod
+        def backward(ctx, dy):
+            x, gamma, mean, rstd = ctx.saved_tensors
+            need_g = gamma is not None and ctx.needs_input_grad[1]
+            need_b = ctx.has_beta and ctx.needs_input_grad[2]
+            dx, dg, db = layer_norm_backward(dy, x, mean, rstd, gamma, need_g, need_b)
+            return (dx, dg.to(gamma.dtype) if need_g else None,
+                    db.to(x.dtype) if need_b else None, None)
+
+    class RMSNormFn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, x, gamma, eps):
+            y, rstd = rms_norm(x, gamma, eps)
+            ctx.save_for_backward(x, gamma, rstd)
+            return y
+
+        @staticmethod
+        def backward(ctx, dy):
+            x, gamma, rstd = ctx.saved_tensors
+            need_g = gamma is not None and ctx.needs_input_grad[1]
+            dx, dg = rms_norm_backward(dy, x, rstd, gamma, need_g)
+            return dx, dg.to(gamma.dtype) if need_g else None, None
+
+    return LayerNormFn, RMSNormFn
+
+
+_FNS = None
+
+
+def layer_norm_autograd(x, gamma=None, beta=None, eps: float = 1e-5):
+    """layer_norm as a differentiable torch op (backward: ln_bwd)."""
+    global _FNS
+    _FNS = _FNS or _autograd()
+    return _FNS[0].apply(x, gamma, beta, eps)
+
+
+def rms_norm_autograd(x, gamma=None, eps: float = 1e-6):
+    """rms_norm as a differentiable torch op (backward: rms_bwd)."""
+    global _FNS
+    _FNS = _FNS or _autograd()
+    return _FNS[1].apply(x, gamma, eps)
+
+
 __all__ = ["ln_fwd", "rms_fwd", "add_rms_fwd", "rms_fp8_fwd", "add_rms_fp8_fwd", "norm_fwd", "NormArgs",
            "norm_status_str", "norm_last_error", "norm_describe", "layer_norm", "rms_norm",
            "fused_add_rms_norm", "rms_norm_fp8", "fused_add_rms_norm_fp8",
+           "ln_bwd", "rms_bwd", "norm_bwd_describe", "layer_norm_backward", "rms_norm_backward",
+           "layer_norm_autograd", "rms_norm_autograd",
            "NORM_F32", "NORM_F16", "NORM_BF16", "NORM_OK", "STATUS", "LIB_PATH", "OPS"]

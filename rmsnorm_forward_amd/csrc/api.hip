@@ -466,6 +466,153 @@ int run(const Args& a, void* stream) {
                                                                                                : NORM_ERR_HIP;
 }
 
+// ---------------------------------------------------------------------------
+// backward
+// ---------------------------------------------------------------------------
+
+// Arguments of one backward call (row strides N).
+struct BwdArgs {
+    bool rms;
+    int dtype;
+    int64_t M, N;
+    const void* dy;
+    const void* x;
+    const void* gamma;
+    const float* mean;
+    const float* rstd;
+    void* dx;
+    float* dgamma;
+    float* dbeta;
+};
+
+bool bwd_vector_aligned(const BwdArgs& a) {
+    const int e = elem_bytes(a.dtype);
+    if ((a.N * e) % 16) return false;
+    for (const void* q : {a.dy, a.x, a.gamma, (const void*)a.dx})
+        if ((uintptr_t)q % 16) return false;
+    return true;
+}
+
+bool bwd_tile_ok(int team, int vpl, int epv) {
+    return team >= kBwdMinTeam && tile_instantiated(team, vpl) && vpl * epv <= kBwdMaxElems;
+}
+
+// The backward grid: this many workgroups per CU, each writing one partial
+// row of dgamma / dbeta (fewer partial rows cost less traffic, more
+// workgroups hide more latency).
+constexpr int kBwdWgPerCu = 2;
+
+int device_cus() {
+    static std::mutex mu;
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!cache[dev]) {
+        int cus = 0;
+        cache[dev] = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+                             cus > 0 ? cus : 256;
+    }
+    return cache[dev];
+}
+
+// A row kernel tile for the backward: about two 16-byte vectors per lane
+// (eight elements unaligned), at most kBwdMaxElems elements per lane, teams
+// of 8..1024 lanes.  Rows longer than 1024 x kBwdMaxElems (16384 when
+// unaligned) are NORM_ERR_BAD_SHAPE.  cus = 0 asks the device.
+int make_bwd_plan(int64_t M, int64_t N, int dtype, bool aligned, const Overrides& o, int cus, Plan* p) {
+    const int e = elem_bytes(dtype);
+    std::memset(p, 0, sizeof *p);
+    p->epv = aligned ? 16 / e : 1;
+    const int64_t NV = N / p->epv;
+    int team, vpl;
+    if (o.team) {
+        team = o.team;
+        vpl = o.vpl;
+        if (!bwd_tile_ok(team, vpl, p->epv) || int64_t(team) * vpl < NV) return NORM_ERR_BAD_ARG;
+    } else {
+        const int per_lane = p->epv == 1 ? 8 : 2;
+        team = next_pow2((NV + per_lane - 1) / per_lane);
+        team = std::max(team, kBwdMinTeam);
+        team = std::min(team, kMaxTeam);
+        vpl = round_vpl((NV + team - 1) / team);
+        if (vpl < 0 || !bwd_tile_ok(team, vpl, p->epv)) return NORM_ERR_BAD_SHAPE;
+    }
+    p->path = PATH_ROWS;
+    p->team = team;
+    p->vpl = vpl;
+    p->wg = team >= 256 ? team : 256;
+    p->rows_per_wg = p->wg / team;
+    p->work = (M + p->rows_per_wg - 1) / p->rows_per_wg;
+    const int64_t cap = o.grid > 0 ? o.grid : int64_t(kBwdWgPerCu) * (cus > 0 ? cus : device_cus());
+    p->grid = std::min(p->work, cap);
+    return NORM_OK;
+}
+
+int validate_bwd(const BwdArgs& a) {
+    if (a.dtype != NORM_F32 && a.dtype != NORM_F16 && a.dtype != NORM_BF16) return NORM_ERR_BAD_DTYPE;
+    const int64_t M = a.M, N = a.N;
+    if (M < 0 || N < 1 || N > kMaxN) return NORM_ERR_BAD_SHAPE;
+    if (M > 0 && M - 1 > (INT64_MAX / 8 - N) / N) return NORM_ERR_BAD_SHAPE;
+    if (a.rms && a.dbeta) return NORM_ERR_BAD_ARG;
+    if (M > 0 && (!a.dy || !a.x || !a.dx || !a.rstd || (!a.rms && !a.mean))) return NORM_ERR_NULL_ARG;
+    const int e = elem_bytes(a.dtype);
+    if (misaligned(a.dy, e) || misaligned(a.x, e) || misaligned(a.gamma, e) || misaligned(a.dx, e) ||
+        misaligned(a.mean, 4) || misaligned(a.rstd, 4) || misaligned(a.dgamma, 4) || misaligned(a.dbeta, 4))
+        return NORM_ERR_BAD_ARG;
+    // in: 0 dy, 1 x, 2 gamma, 3 mean, 4 rstd;  out: 5 dx, 6 dgamma, 7 dbeta
+    const Mat m[8] = {{a.dy, M, N * e, N * e},  {a.x, M, N * e, N * e},  {a.gamma, 1, N * e, N * e},
+                      {a.mean, 1, M * 4, M * 4}, {a.rstd, 1, M * 4, M * 4}, {a.dx, M, N * e, N * e},
+                      {a.dgamma, 1, N * 4, N * 4}, {a.dbeta, 1, N * 4, N * 4}};
+    for (int i = 0; i < 8; ++i)
+        for (int j = i + 1; j < 8; ++j) {
+            if (j < 5 || !overlaps(m[i], m[j])) continue;
+            // dx may be written exactly over dy or x: a lane loads the
+            // elements it owns from both before it stores any of them
+            if (j == 5 && i <= 1 && m[i].p == m[j].p) continue;
+            return NORM_ERR_ALIAS;
+        }
+    return NORM_OK;
+}
+
+int run_bwd(const BwdArgs& a, void* stream) {
+    int st = validate_bwd(a);
+    if (st != NORM_OK) return st;
+    const int64_t M = a.M, N = a.N;
+    const bool sums = a.dgamma || a.dbeta;
+    Plan p;
+    st = make_bwd_plan(M, N, a.dtype, bwd_vector_aligned(a), read_overrides(), 0, &p);
+    if (st != NORM_OK) return st;
+    const hipStream_t s = (hipStream_t)stream;
+    float* pg = nullptr;
+    float* pb = nullptr;
+    const int64_t P = p.grid;   // partial rows: one per workgroup
+    if (sums && P > 0) {
+        Workspace w;
+        const size_t per = size_t(P) * size_t(N);
+        if (!stream_workspace(s, 0, per * sizeof(float) * ((a.dgamma && a.dbeta) ? 2 : 1), &w))
+            return NORM_ERR_HIP;
+        float* base = reinterpret_cast<float*>(w.part);
+        pg = a.dgamma ? base : nullptr;
+        pb = a.dbeta ? (a.dgamma ? base + per : base) : nullptr;
+    }
+    hipError_t err = hipSuccess;
+    if (M > 0) {
+        BwdCall c{a.dy, a.x, a.gamma, a.mean, a.rstd, a.dx, pg, pb, M, (int)N, N, N, N, s};
+        const int op = a.rms ? OP_RMS : OP_LN;
+        switch (a.dtype) {
+        case NORM_F32: err = launch_bwd_f32(op, c, p); break;
+        case NORM_BF16: err = launch_bwd_bf16(op, c, p); break;
+        default: err = launch_bwd_f16(op, c, p); break;
+        }
+        if (!hip_ok(err, "backward row kernel launch")) return NORM_ERR_HIP;
+    }
+    // column sums of the partial rows (zeros when M = 0)
+    if (a.dgamma && !hip_ok(launch_colsum(pg, P, (int)N, a.dgamma, s), "column-sum launch")) return NORM_ERR_HIP;
+    if (a.dbeta && !hip_ok(launch_colsum(pb, P, (int)N, a.dbeta, s), "column-sum launch")) return NORM_ERR_HIP;
+    return NORM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -512,11 +659,39 @@ int add_rms_fp8_fwd(const void* x, const void* residual, const void* gamma, void
                stream);
 }
 
+int ln_bwd(const void* dy, const void* x, const void* gamma, const float* mean, const float* rstd, void* dx,
+           float* dgamma, float* dbeta, int64_t M, int64_t N, int dtype, void* stream) {
+    return run_bwd(BwdArgs{false, dtype, M, N, dy, x, gamma, mean, rstd, dx, dgamma, dbeta}, stream);
+}
+
+int rms_bwd(const void* dy, const void* x, const void* gamma, const float* rstd, void* dx, float* dgamma,
+            int64_t M, int64_t N, int dtype, void* stream) {
+    return run_bwd(BwdArgs{true, dtype, M, N, dy, x, gamma, nullptr, rstd, dx, dgamma, nullptr}, stream);
+}
+
+int norm_bwd_describe(int rms, int64_t M, int64_t N, int dtype, int aligned, char* buf, int buflen) {
+    if (dtype != NORM_F32 && dtype != NORM_F16 && dtype != NORM_BF16) return NORM_ERR_BAD_DTYPE;
+    if (M < 0 || N < 1 || N > kMaxN) return NORM_ERR_BAD_SHAPE;
+    const int e = elem_bytes(dtype);
+    Plan p;
+    int st = make_bwd_plan(M, N, dtype, aligned && (N * e) % 16 == 0, read_overrides(), 0, &p);
+    if (st != NORM_OK) return st;
+    if (buf && buflen > 0)
+        std::snprintf(buf, (size_t)buflen,
+                      "path=bwd op=%s team=%d vpl=%d epv=%d wg=%d rows_per_wg=%d grid=%lld work=%lld "
+                      "partial_rows=%lld",
+                      rms ? "rms" : "ln", p.team, p.vpl, p.epv, p.wg, p.rows_per_wg, (long long)p.grid,
+                      (long long)p.work, (long long)p.grid);
+    return NORM_OK;
+}
+
 const char* norm_status_str(int status) {
     switch (status) {
     case NORM_OK: return "ok";
     case NORM_ERR_NULL_ARG: return "x or y is NULL";
-    case NORM_ERR_BAD_SHAPE: return "bad shape: need M >= 0, 1 <= N <= 2^24 and M*N*elem within int64";
+    case NORM_ERR_BAD_SHAPE:
+        return "bad shape: need M >= 0, 1 <= N <= 2^24 (backward: N <= 32768, 16384 unless 16-byte aligned) "
+               "and M*N*elem within int64";
     case NORM_ERR_BAD_DTYPE: return "unknown dtype (0 = f32, 1 = f16, 2 = bf16)";
     case NORM_ERR_BAD_EPS: return "eps must be finite and >= 0";
     case NORM_ERR_BAD_ARG: return "bad argument: misaligned pointer, beta/mean given to an RMSNorm, a bad FP8 scale, or an unusable override";

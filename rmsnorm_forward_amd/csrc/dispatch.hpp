@@ -31,6 +31,24 @@ struct NormCall {
     Strides ld;          // row strides of x, res, y, hout
 };
 
+// A backward call: dy, x, dx [M, N] (row strides ld*), gamma [N] or null,
+// the forward's fp32 mean (LayerNorm) and rstd [M]; column partials of
+// dgamma / dbeta go to part_g / part_b ([P, N] fp32, either may be null).
+struct BwdCall {
+    const void* dy;
+    const void* x;
+    const void* gamma;
+    const float* mean;
+    const float* rstd;
+    void* dx;
+    float* part_g;
+    float* part_b;
+    int64_t M;
+    int N;
+    int64_t ldy, ldx, lddx;
+    hipStream_t stream;
+};
+
 enum { PATH_ROWS = 0, PATH_SPLIT = 1 };
 enum { SPLIT_TWO = 0, SPLIT_COOP = 1 };
 
@@ -56,6 +74,10 @@ constexpr int kTeams[] = {4, 8, 16, 32, 64, 128, 256, 512, 1024};
 constexpr int kVpls[] = {1, 2, 4, 8, 16};
 constexpr int kMaxTeam = 1024;
 constexpr int kMaxVpl = 16;
+// backward: at most this many elements per lane (dy, x and two column
+// accumulators live in registers); teams of 8 lanes and up
+constexpr int kBwdMaxElems = 32;
+constexpr int kBwdMinTeam = 8;
 // Split-row chunk geometry: the two kernels of the two-kernel form (each
 // its own chunk size), and the single pass (fewer, larger chunks: fewer
 // arrivals per row at its barrier).
@@ -109,6 +131,12 @@ hipError_t launch_split_coop_bf16(int op, const NormCall& c, const Plan& p, floa
                                   unsigned* sync, unsigned need, unsigned spin_limit);
 hipError_t launch_split_coop_f16(int op, const NormCall& c, const Plan& p, float2* ws,
                                  unsigned* sync, unsigned need, unsigned spin_limit);
+// backward row kernel with the plan's tile (op OP_LN or OP_RMS), grid p.grid
+hipError_t launch_bwd_f32(int op, const BwdCall& c, const Plan& p);
+hipError_t launch_bwd_bf16(int op, const BwdCall& c, const Plan& p);
+hipError_t launch_bwd_f16(int op, const BwdCall& c, const Plan& p);
+// out[c] = sum of the P partial rows of column c (fixed order)
+hipError_t launch_colsum(const float* part, int64_t P, int N, float* out, hipStream_t stream);
 // workgroups of the single-pass split kernel that fit on one CU at once
 int coop_blocks_per_cu_f32(int op, int epv);
 int coop_blocks_per_cu_bf16(int op, int epv);

@@ -1,4 +1,4 @@
-// inst_bf16.hip -- bf16 instantiations of the row and split-row kernels.
+// inst_bf16.hip -- bf16 instantiations of the row, split-row and backward kernels.
 #include "inst_impl.hpp"
 
 namespace mi355norm {
@@ -14,5 +14,8 @@ hipError_t launch_split_coop_bf16(int op, const NormCall& c, const Plan& p, floa
 }
 int coop_blocks_per_cu_bf16(int op, int epv) {
     return detail::coop_blocks_per_cu<BF16>(op, epv);
+}
+hipError_t launch_bwd_bf16(int op, const BwdCall& c, const Plan& p) {
+    return detail::launch_bwd<BF16>(op, c, p);
 }
 }  // namespace mi355norm

@@ -1,4 +1,5 @@
-// inst_f32.hip -- f32 instantiations of the row and split-row kernels.
+// inst_f32.hip -- f32 instantiations of the row, split-row and backward
+// kernels, and the launch of the (type-free) column-sum kernel.
 #include "inst_impl.hpp"
 
 namespace mi355norm {
@@ -14,5 +15,13 @@ hipError_t launch_split_coop_f32(int op, const NormCall& c, const Plan& p, float
 }
 int coop_blocks_per_cu_f32(int op, int epv) {
     return detail::coop_blocks_per_cu<F32>(op, epv);
+}
+hipError_t launch_bwd_f32(int op, const BwdCall& c, const Plan& p) {
+    return detail::launch_bwd<F32>(op, c, p);
+}
+hipError_t launch_colsum(const float* part, int64_t P, int N, float* out, hipStream_t stream) {
+    hipLaunchKernelGGL(norm_colsum_kernel<kColsumWaves>, dim3((unsigned)((N + 63) / 64)), dim3(64 * kColsumWaves), 0, stream,
+                       part, P, N, out);
+    return hipGetLastError();
 }
 }  // namespace mi355norm

@@ -3,6 +3,7 @@
 // separate translation units in parallel.
 #pragma once
 
+#include "backward.hpp"
 #include "dispatch.hpp"
 #include "rows.hpp"
 #include "split.hpp"
@@ -207,6 +208,68 @@ hipError_t launch_split_coop(int op, const NormCall& c, const Plan& p, float2* w
             return go_split_coop<T, decltype(rms)::value, decltype(add)::value, decltype(q8)::value,
                                  decltype(epv)::value>(c, p, ws, sync, need, spin_limit);
         });
+    });
+}
+
+// ---------------------------------------------------------------------------
+// backward
+// ---------------------------------------------------------------------------
+
+template <class T, bool RMS, int TEAM, int VPL, int EPV>
+hipError_t go_bwd(const BwdCall& c, const Plan& p) {
+    const St<T>* dy = static_cast<const St<T>*>(c.dy);
+    const St<T>* x = static_cast<const St<T>*>(c.x);
+    const St<T>* g = static_cast<const St<T>*>(c.gamma);
+    const float* mean = c.mean;
+    const float* rstd = c.rstd;
+    St<T>* dx = static_cast<St<T>*>(c.dx);
+    float* pg = c.part_g;
+    float* pb = c.part_b;
+    int64_t M = c.M;
+    int N = c.N;
+    int64_t ldy = c.ldy, ldx = c.ldx, lddx = c.lddx;
+    void* args[] = {&dy, &x, &g, &mean, &rstd, &dx, &pg, &pb, &M, &N, &ldy, &ldx, &lddx};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&norm_bwd_rows_kernel<T, RMS, TEAM, VPL, EPV>),
+                           dim3((unsigned)p.grid), dim3(TeamGeom<TEAM>::WG), args, 0, c.stream);
+}
+
+template <class T, bool RMS, int TEAM, int EPV>
+hipError_t bwd_by_vpl(const BwdCall& c, const Plan& p) {
+    switch (p.vpl) {
+    case 1: return go_bwd<T, RMS, TEAM, 1, EPV>(c, p);
+    case 2: return go_bwd<T, RMS, TEAM, 2, EPV>(c, p);
+    case 4: return go_bwd<T, RMS, TEAM, 4, EPV>(c, p);
+    case 8:
+        if constexpr (8 * EPV <= kBwdMaxElems) return go_bwd<T, RMS, TEAM, 8, EPV>(c, p);
+        break;
+    case 16:
+        if constexpr (16 * EPV <= kBwdMaxElems) return go_bwd<T, RMS, TEAM, 16, EPV>(c, p);
+        break;
+    }
+    return hipErrorInvalidValue;
+}
+
+template <class T, bool RMS, int EPV>
+hipError_t bwd_by_team(const BwdCall& c, const Plan& p) {
+    switch (p.team) {
+    case 8: return bwd_by_vpl<T, RMS, 8, EPV>(c, p);
+    case 16: return bwd_by_vpl<T, RMS, 16, EPV>(c, p);
+    case 32: return bwd_by_vpl<T, RMS, 32, EPV>(c, p);
+    case 64: return bwd_by_vpl<T, RMS, 64, EPV>(c, p);
+    case 128: return bwd_by_vpl<T, RMS, 128, EPV>(c, p);
+    case 256: return bwd_by_vpl<T, RMS, 256, EPV>(c, p);
+    case 512: return bwd_by_vpl<T, RMS, 512, EPV>(c, p);
+    case 1024: return bwd_by_vpl<T, RMS, 1024, EPV>(c, p);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <class T>
+hipError_t launch_bwd(int op, const BwdCall& c, const Plan& p) {
+    if (op != OP_LN && op != OP_RMS) return hipErrorInvalidValue;
+    return with_epv<T>(p.epv, [&](auto epv) {
+        constexpr int E = decltype(epv)::value;
+        return op == OP_RMS ? bwd_by_team<T, true, E>(c, p) : bwd_by_team<T, false, E>(c, p);
     });
 }
 

@@ -112,6 +112,39 @@ def run_fp8(dtype: str, x: np.ndarray, res, gamma, eps: float, scale: float, *, 
     return q, h, r
 
 
+def run_bwd(op: str, dtype: str, dy: np.ndarray, x: np.ndarray, gamma, mean, rstd, *, offset: int = 0,
+            inplace: str | None = None, want_g: bool = True, want_b: bool = True):
+    """One ln_bwd / rms_bwd call on host arrays (mean / rstd: fp32 [M]);
+    returns (dx, dgamma, dbeta) as host arrays (None where not asked for).
+    inplace = "dy" or "x" writes dx over that input."""
+    M, N = x.shape
+    dyt = to_device(dy, dtype, offset)
+    xt = to_device(x, dtype, offset)
+    gt = to_device(gamma, dtype, offset) if gamma is not None else None
+    mt = torch.from_numpy(np.ascontiguousarray(mean, np.float32)).cuda() if op == "ln" else None
+    rt = torch.from_numpy(np.ascontiguousarray(rstd, np.float32)).cuda()
+    if inplace == "dy":
+        dxt = dyt
+    elif inplace == "x":
+        dxt = xt
+    else:
+        dxt = torch.empty(M * N + offset, dtype=TORCH_DT[dtype], device="cuda")[offset:]
+    dgt = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda") if want_g else None
+    dbt = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda") if (want_b and op == "ln") else None
+    p = lambda t: t.data_ptr() if t is not None else None
+    stream = torch.cuda.current_stream().cuda_stream
+    if op == "ln":
+        st = rn.ln_bwd(p(dyt), p(xt), p(gt), p(mt), p(rt), p(dxt), p(dgt), p(dbt), M, N, CODE[dtype], stream)
+    else:
+        st = rn.rms_bwd(p(dyt), p(xt), p(gt), p(rt), p(dxt), p(dgt), M, N, CODE[dtype], stream)
+    assert st == rn.NORM_OK, f"{rn.STATUS.get(st)}: {rn.norm_status_str(st)} [{rn.norm_last_error()}]"
+    torch.cuda.synchronize()
+    dx = to_host(dxt, dtype).reshape(M, N)
+    dg = dgt.cpu().numpy() if dgt is not None else None
+    db = dbt.cpu().numpy() if dbt is not None else None
+    return dx, dg, db
+
+
 def _embed(a: np.ndarray, dtype: str, ld: int, offset: int, fill_bits: int):
     """Device buffer holding the [M, N] storage array `a` with rows `ld`
     elements apart, starting `offset` elements in; every other element holds

@@ -19,6 +19,23 @@ marked):
                 takes the decision on its fp32 y, which carries a few fp32
                 ulps: reading), at most FP8_TIE_FRAC of all elements; a
                 zero may be coded +0 or -0, a NaN with either sign
+
+Backward (ln_bwd / rms_bwd; reading: the task fixes no tolerance for it, so
+the bound is derived from the kernel's fp32 arithmetic, u = 2^-24, on the
+same fp32 mean / rstd the oracle is given):
+  dx            |dx_gpu - dx_oracle| <= B + (half an ulp of the I/O dtype at
+                |dx_oracle| + B; none for fp32) with, per element,
+                  LayerNorm  B = K u rstd (|g| + mean|g| + |xhat| mean|g xhat|)
+                  RMSNorm    B = K u (rstd |g| + |x| rstd^3 mean|g x|)
+                g = dy gamma, means over the row, K = BWD_K: each term passes
+                through at most 32 sequential lane additions, a 10-level
+                team tree, the cross-wavefront sum and a handful of
+                products, so K = 128 covers every rounding with room
+  dgamma/dbeta  |err| <= (n + 4) u sum_r |term| where n is the longest
+                chain of fp32 additions any column goes through (rows per
+                team + teams per workgroup + partial rows per wavefront of
+                the column sum + 16) and term = dy xhat (RMSNorm dy x rstd),
+                or dy for dbeta
 """
 from __future__ import annotations
 
@@ -138,3 +155,72 @@ def check_stress_invariants(rstd_gpu, y_gpu, dtype: str, eps: float, what: str =
     assert np.all(r <= (1 + 1e-6) / np.sqrt(e)), f"{what}: rstd implies a negative variance"
     yv = y_gpu.astype(np.float64) if dtype == "f32" else oracle.widen(y_gpu, dtype)
     assert np.all(np.isfinite(yv)), f"{what}: non-finite y"
+
+
+BWD_K = 128
+U32 = 2.0 ** -24
+
+
+def bwd_chain(plan: dict, M: int) -> int:
+    """Longest chain of fp32 additions behind one dgamma / dbeta column."""
+    rows_per_team = -(-plan["work"] // plan["grid"]) if plan["grid"] else 0
+    return rows_per_team + plan["rows_per_wg"] + -(-plan["grid"] // 16) + 16
+
+
+def check_bwd(op: str, dtype: str, dy, x, gamma, mean, rstd, dx, dg, db, plan: dict | None, rows=None,
+              what: str = "") -> dict:
+    """dy, x, gamma: storage arrays; mean, rstd: the fp32 statistics given to
+    both sides; dx (rows `rows` only when given), dg, db: the GPU's results
+    (None = not checked).  dg / db need every row."""
+    M, N = x.shape
+    xs = oracle.widen(x, dtype)
+    dys = oracle.widen(dy, dtype)
+    gam = np.ones(N) if gamma is None else oracle.widen(gamma, dtype)
+    rs = np.asarray(rstd, np.float64)
+    out = {}
+    sel = np.arange(M) if rows is None else np.asarray(rows)
+    if op == "ln":
+        mu = np.asarray(mean, np.float64)
+        ref = oracle.ln_bwd(dy[sel], x[sel], gamma, dtype, mu[sel], rs[sel])
+        dxr = ref[0]
+        xh = (xs[sel] - mu[sel, None]) * rs[sel, None]
+        g = dys[sel] * gam
+        B = BWD_K * U32 * rs[sel, None] * (np.abs(g) + np.abs(g).mean(1, keepdims=True)
+                                           + np.abs(xh) * np.abs(g * xh).mean(1, keepdims=True))
+    else:
+        ref = oracle.rms_bwd(dy[sel], x[sel], gamma, dtype, rs[sel])
+        dxr = ref[0]
+        g = dys[sel] * gam
+        r = rs[sel, None]
+        B = BWD_K * U32 * (r * np.abs(g) + np.abs(xs[sel]) * r ** 3 * np.abs(g * xs[sel]).mean(1, keepdims=True))
+    got = dx.astype(np.float64) if dtype == "f32" else oracle.widen(dx, dtype)
+    tol = B if dtype == "f32" else B + 0.5 * ulp_of(np.abs(dxr) + B, dtype)
+    err = np.abs(got - dxr)
+    bad = ~(err <= tol)
+    if bad.any():
+        i = np.unravel_index(np.argmax(bad), bad.shape)
+        raise AssertionError(f"{what} dx mismatch at row {sel[i[0]]} col {i[1]}: gpu={got[i]!r} "
+                             f"oracle={dxr[i]!r} tol={tol[i]:.3g} ({int(bad.sum())} bad of {bad.size})")
+    out["dx_max_err_over_tol"] = float((err / np.maximum(tol, 1e-300)).max()) if err.size else 0.0
+    if dg is not None or db is not None:
+        assert rows is None, "column sums need every row"
+        n = bwd_chain(plan, M) + 4
+        full = ref
+        if op == "ln":
+            xh_all = (xs - np.asarray(mean, np.float64)[:, None]) * rs[:, None]
+            pairs = [(dg, full[1], np.abs(dys * xh_all).sum(0), "dgamma"),
+                     (db, full[2], np.abs(dys).sum(0), "dbeta")]
+        else:
+            pairs = [(dg, full[1], np.abs(dys * xs * rs[:, None]).sum(0), "dgamma")]
+        for got_c, want_c, mag, name in pairs:
+            if got_c is None:
+                continue
+            tol_c = n * U32 * mag
+            e = np.abs(got_c.astype(np.float64) - want_c)
+            badc = ~(e <= tol_c)
+            if badc.any():
+                j = int(np.argmax(badc))
+                raise AssertionError(f"{what} {name}[{j}]: gpu={got_c[j]!r} oracle={want_c[j]!r} "
+                                     f"tol={tol_c[j]:.3g} ({int(badc.sum())} bad of {badc.size})")
+            out[f"{name}_max_err_over_tol"] = float((e / np.maximum(tol_c, 1e-300)).max()) if e.size else 0.0
+    return out

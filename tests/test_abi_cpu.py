@@ -26,8 +26,9 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["add_rms_fp8_fwd", "add_rms_fwd", "ln_fwd", "norm_describe", "norm_fwd",
-                                    "norm_last_error", "norm_status_str", "rms_fp8_fwd", "rms_fwd"]
+    assert declared_functions() == ["add_rms_fp8_fwd", "add_rms_fwd", "ln_bwd", "ln_fwd", "norm_bwd_describe",
+                                    "norm_describe", "norm_fwd", "norm_last_error", "norm_status_str",
+                                    "rms_bwd", "rms_fp8_fwd", "rms_fwd"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -357,3 +358,103 @@ def test_strided_in_place_residual_needs_the_same_stride():
     assert passes(strided(op="add_rms", residual=R, residual_out=R, ld_residual=80, ld_residual_out=80))
     assert strided(op="add_rms", residual=R, residual_out=R, ld_residual=80, ld_residual_out=96) == ALIAS
     assert passes(strided(op="add_rms", x=X, y=X, ld_x=72, ld_y=72))
+
+
+# ---------------------------------------------------------------------------
+# backward
+# ---------------------------------------------------------------------------
+
+A = 1 << 20   # fake, 16-byte aligned "device" addresses: validation rejects before any use
+
+
+def ln_bwd(dy=A, x=2 * A, gamma=None, mean=3 * A, rstd=4 * A, dx=5 * A, dgamma=None, dbeta=None, M=4, N=64,
+           dtype=rn.NORM_BF16):
+    return rn.ln_bwd(dy, x, gamma, mean, rstd, dx, dgamma, dbeta, M, N, dtype, None)
+
+
+def rms_bwd(dy=A, x=2 * A, gamma=None, rstd=4 * A, dx=5 * A, dgamma=None, M=4, N=64, dtype=rn.NORM_BF16):
+    return rn.rms_bwd(dy, x, gamma, rstd, dx, dgamma, M, N, dtype, None)
+
+
+def test_bwd_validation():
+    assert ln_bwd(dtype=7) == BAD_DTYPE
+    assert ln_bwd(M=-1) == BAD_SHAPE
+    assert ln_bwd(N=0) == BAD_SHAPE
+    assert ln_bwd(N=(1 << 24) + 1) == BAD_SHAPE
+    assert ln_bwd(N=32768 + 8) == BAD_SHAPE            # longer than the backward's tile
+    assert ln_bwd(dy=None) == NULL_ARG
+    assert ln_bwd(x=None) == NULL_ARG
+    assert ln_bwd(dx=None) == NULL_ARG
+    assert ln_bwd(mean=None) == NULL_ARG               # LayerNorm needs the mean
+    assert ln_bwd(rstd=None) == NULL_ARG
+    assert rms_bwd(rstd=None) == NULL_ARG
+    assert ln_bwd(dy=A + 1) == BAD_ARG                 # misaligned for bf16
+    assert ln_bwd(mean=3 * A + 2) == BAD_ARG
+    assert ln_bwd(dgamma=6 * A + 2) == BAD_ARG
+    # outputs overlapping inputs or each other
+    assert ln_bwd(dx=A + 64) == ALIAS                  # dx inside dy, shifted
+    assert ln_bwd(dgamma=A) == ALIAS
+    assert ln_bwd(dgamma=6 * A, dbeta=6 * A + 128) == ALIAS
+    assert ln_bwd(dbeta=3 * A) == ALIAS                # over mean
+    assert rms_bwd(dgamma=4 * A) == ALIAS              # over rstd
+
+
+def test_bwd_exact_in_place_passes_validation():
+    # dx exactly over dy or over x is allowed; with M = 0 nothing launches
+    assert ln_bwd(dx=A, M=0) == OK
+    assert ln_bwd(dx=A, dy=None, M=4) == NULL_ARG
+    assert rms_bwd(dx=2 * A, M=0) == OK
+
+
+def test_bwd_empty_needs_no_pointers():
+    assert ln_bwd(dy=None, x=None, mean=None, rstd=None, dx=None, M=0) == OK
+    assert rms_bwd(dy=None, x=None, rstd=None, dx=None, M=0) == OK
+
+
+@pytest.mark.parametrize("N,dtype,aligned,ok", [(32768, "bf16", True, True), (32776, "bf16", True, False),
+                                                (32768, "f32", True, True), (16384, "bf16", False, True),
+                                                (16385, "f16", False, False), (1, "f32", False, True)])
+def test_bwd_row_limit(N, dtype, aligned, ok):
+    for op in ("ln", "rms"):
+        if ok:
+            assert rn.norm_bwd_describe(op, 1024, N, dtype, aligned).startswith("path=bwd")
+        else:
+            with pytest.raises(RuntimeError, match="bad shape"):
+                rn.norm_bwd_describe(op, 1024, N, dtype, aligned)
+
+
+def _bwd_plan(op, M, N, dtype, aligned=True):
+    d = dict(kv.split("=") for kv in rn.norm_bwd_describe(op, M, N, dtype, aligned).split())
+    return {k: (v if k in ("path", "op") else int(v)) for k, v in d.items()}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("aligned", [True, False])
+def test_bwd_every_row_fits_its_tile(dtype, aligned):
+    e = 4 if dtype == "f32" else 2
+    limit = 32768 if aligned else 16384
+    for N in [1, 7, 8, 64, 100, 768, 1000, 1024, 4096, 5120, 8192, 12288, 16384, 24576, 32768]:
+        if N > limit or (aligned and (N * e) % 16):
+            continue
+        p = _bwd_plan("ln", 4096, N, dtype, aligned)
+        epv = p["epv"]
+        assert epv == (16 // e if aligned else 1)
+        slots = p["team"] * p["vpl"] * epv
+        assert slots >= N and (p["team"] == 8 or N >= slots // 4)
+        assert p["vpl"] * epv <= 32 and 8 <= p["team"] <= 1024
+        assert p["wg"] == max(p["team"], 256) and p["rows_per_wg"] == p["wg"] // p["team"]
+        assert p["grid"] == min(p["work"], 512) == p["partial_rows"]
+
+
+def test_bwd_grid_override(monkeypatch):
+    monkeypatch.setenv("MI355NORM_GRID", "100")
+    assert _bwd_plan("rms", 16384, 8192, "bf16")["grid"] == 100
+    monkeypatch.setenv("MI355NORM_TILE", "256x4")
+    p = _bwd_plan("rms", 16384, 8192, "bf16")
+    assert (p["team"], p["vpl"]) == (256, 4)
+    monkeypatch.setenv("MI355NORM_TILE", "128x4")        # too small for the row
+    with pytest.raises(RuntimeError):
+        rn.norm_bwd_describe("rms", 16384, 8192, "bf16")
+    monkeypatch.setenv("MI355NORM_TILE", "1024x8")       # 64 bf16 elements per lane: not instantiated
+    with pytest.raises(RuntimeError):
+        rn.norm_bwd_describe("rms", 16384, 8192, "bf16")

@@ -49,3 +49,11 @@ def test_cpu_baseline_counts_the_rows_it_ran():
     cb = bench.cpu_baseline(w, inp, seconds=5.0)
     assert cb["kind"] == "oracle" and cb["cores"] == 1 and cb["unit"] == "GB/s"
     assert cb["sample"].startswith("64 of 64 rows") and cb["value"] > 0
+
+
+def test_cpu_baseline_of_the_backward():
+    w = workloads.Workload("t", "ln_bwd", "bf16", 32, 512, 1e-5, 0, "")
+    inp = workloads.gen_bwd(0, 32, 512, "bf16", "ln_bwd")
+    cb = bench.cpu_baseline(w, inp, seconds=5.0)
+    assert cb["sample"].startswith("32 of 32 rows") and "oracle.ln_bwd" in cb["sample"] and cb["value"] > 0
+    assert w.ideal_bytes() == 3 * 32 * 512 * 2 + 512 * 2 + 512 * 8 + 32 * 8

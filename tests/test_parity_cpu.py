@@ -6,6 +6,7 @@ import pytest
 
 import oracle
 import parity
+import workloads
 
 
 def codes(v, scale=1.0):
@@ -55,3 +56,38 @@ def test_fp8_too_many_ties_fail():
     q = np.full(100, 0x38, np.uint8)
     with pytest.raises(AssertionError):
         parity.check_fp8(q, qr, y, 1.0)
+
+
+@pytest.mark.parametrize("op", ["ln", "rms"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_bound_accepts_the_rounded_oracle_and_rejects_a_dropped_term(op, dtype):
+    M, N = 40, 96
+    d = workloads.gen_bwd(3, M, N, dtype, op + "_bwd")
+    if op == "ln":
+        _, mean, rstd = oracle.ln_fwd(d["x"], d["gamma"], None, dtype, 1e-5)
+        mean = mean.astype(np.float32)
+        dx, dg, db = oracle.ln_bwd(d["dy"], d["x"], d["gamma"], dtype, mean, rstd.astype(np.float32))
+    else:
+        _, rstd = oracle.rms_fwd(d["x"], d["gamma"], dtype, 1e-6)
+        mean, db = None, None
+        dx, dg = oracle.rms_bwd(d["dy"], d["x"], d["gamma"], dtype, rstd.astype(np.float32))
+    rstd = rstd.astype(np.float32)
+    plan = {"work": M, "grid": 8, "rows_per_wg": 1}
+    store = (lambda v: v.astype(np.float32)) if dtype == "f32" else (lambda v: oracle.round_to(v, dtype))
+    parity.check_bwd(op, dtype, d["dy"], d["x"], d["gamma"], mean, rstd, store(dx), dg.astype(np.float32),
+                     None if db is None else db.astype(np.float32), plan)
+    # dx without its mean-of-g term (LayerNorm) or its rstd^3 term (RMSNorm) must fail
+    g = oracle.widen(d["dy"], dtype) * oracle.widen(d["gamma"], dtype)
+    if op == "ln":
+        wrong = dx + rstd.astype(np.float64)[:, None] * g.mean(1, keepdims=True)
+    else:
+        xs = oracle.widen(d["x"], dtype)
+        r = rstd.astype(np.float64)[:, None]
+        wrong = dx + xs * r ** 3 * (g * xs).mean(1, keepdims=True)
+    with pytest.raises(AssertionError, match="dx mismatch"):
+        parity.check_bwd(op, dtype, d["dy"], d["x"], d["gamma"], mean, rstd, store(wrong), None, None, plan)
+    # a column sum off by one row's term must fail
+    bad = dg.astype(np.float32).copy()
+    bad[5] += 1e-2
+    with pytest.raises(AssertionError, match="dgamma"):
+        parity.check_bwd(op, dtype, d["dy"], d["x"], d["gamma"], mean, rstd, store(dx), bad, None, plan)

@@ -29,6 +29,10 @@ shapes and value distributions are those of the pages' own examples:
     activation outliers of a hundredfold).
   * LN bf16 with a non-power-of-two N (5120) and a very long row (2^20): the
     padding and segmented-read cases of "T3 讲解" part ②.
+Follow-on operations at the LN bf16 16384x8192 shape: residual add +
+RMSNorm, RMSNorm with FP8 output, and the LayerNorm / RMSNorm backward
+("CUDA 算子工程" ch. 7, sections 7.7 and 7.9), with the upstream gradient
+dy ~ N(0, 1).
 """
 from __future__ import annotations
 
@@ -36,7 +40,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-__all__ = ["Workload", "CONFIGS", "generate", "gen_ln_normal", "gen_rms_uniform",
+__all__ = ["Workload", "CONFIGS", "generate", "gen_ln_normal", "gen_rms_uniform", "gen_bwd",
            "gen_ln_stress", "gen_ln_large_mean", "check_row_f32", "to_storage",
            "normal", "uniform", "ELEM_BYTES"]
 
@@ -119,6 +123,25 @@ def gen_add_rms(seed: int, M: int, N: int, dtype: str):
             "beta": None}
 
 
+def gen_bwd(seed: int, M: int, N: int, dtype: str, op: str):
+    """Backward inputs: the forward's inputs (LayerNorm: x ~ N(0, 1),
+    gamma ~ U(0.5, 1.5); RMSNorm: x ~ U(-1, 1), weight ~ U(0, 1)), then the
+    upstream gradient dy ~ N(0, 1).  The forward's mean / rstd are not drawn
+    here: they are the forward pass's outputs."""
+    rng = np.random.default_rng(seed)
+    if op == "ln_bwd":
+        x = normal(rng, (M, N), 0.0, 1.0)
+        gamma = uniform(rng, (N,), 0.5, 1.5)
+    elif op == "rms_bwd":
+        x = uniform(rng, (M, N), -1.0, 1.0)
+        gamma = uniform(rng, (N,), 0.0, 1.0)
+    else:
+        raise ValueError(op)
+    dy = normal(rng, (M, N), 0.0, 1.0)
+    return {"x": to_storage(x, dtype), "gamma": to_storage(gamma, dtype), "beta": None,
+            "dy": to_storage(dy, dtype)}
+
+
 def gen_ln_stress(seed: int, M: int, N: int, dtype: str, row_frac: float = 0.1,
                   chan_frac: float = 0.001, big_mean: float = 1000.0,
                   big_sd: float = 1e-2, outlier_scale: float = 100.0):
@@ -168,7 +191,8 @@ def check_row_f32() -> np.ndarray:
 @dataclass(frozen=True)
 class Workload:
     name: str
-    op: str          # "ln", "rms", "add_rms" (residual add, then RMSNorm), "rms_fp8"
+    op: str          # "ln", "rms", "add_rms" (residual add, then RMSNorm), "rms_fp8",
+                     # "ln_bwd", "rms_bwd" (backward from the forward's statistics)
     dtype: str       # "f32", "bf16", "f16"
     M: int
     N: int
@@ -184,8 +208,18 @@ class Workload:
     def ideal_bytes(self, with_stats: bool = True) -> int:
         """Bytes the method must move: x read once, y written once, gamma
         (and beta for LN) read once, fp32 mean+rstd (LN) or rstd (RMS); with
-        the residual add also the residual read once and the sum written once."""
+        the residual add also the residual read once and the sum written once.
+        Backward: dy and x read once, dx written once, gamma read once, the
+        stored statistics read once, fp32 dgamma (LayerNorm: and dbeta)
+        written once."""
         e = self.elem_bytes
+        if self.op in ("ln_bwd", "rms_bwd"):
+            # dy and x read, dx written, gamma read, fp32 dgamma (and dbeta) written
+            ln = self.op == "ln_bwd"
+            b = 3 * self.M * self.N * e + self.N * e + self.N * 4 * (2 if ln else 1)
+            if with_stats:
+                b += self.M * (8 if ln else 4)
+            return b
         if self.op == "rms_fp8":
             b = self.M * self.N * (e + 1)          # x read, one byte per code written
         else:
@@ -224,6 +258,12 @@ CONFIGS = {
     "rms_fp8_bf16_16384x8192": Workload(
         "rms_fp8_bf16_16384x8192", "rms_fp8", "bf16", 16384, 8192, 1e-6, 1007,
         "x~U(-1,1), weight~U(0,1); RMSNorm with FP8 E4M3 output of y / (1/64)", 1.0 / 64),
+    "ln_bwd_bf16_16384x8192": Workload(
+        "ln_bwd_bf16_16384x8192", "ln_bwd", "bf16", 16384, 8192, 1e-5, 1008,
+        "x~N(0,1), gamma~U(0.5,1.5), dy~N(0,1); mean/rstd from the forward; LayerNorm backward"),
+    "rms_bwd_bf16_16384x8192": Workload(
+        "rms_bwd_bf16_16384x8192", "rms_bwd", "bf16", 16384, 8192, 1e-6, 1009,
+        "x~U(-1,1), weight~U(0,1), dy~N(0,1); rstd from the forward; RMSNorm backward"),
 }
 
 
@@ -247,4 +287,6 @@ def generate(name: str) -> dict:
         return gen_add_rms(w.seed, w.M, w.N, w.dtype)
     if name == "rms_fp8_bf16_16384x8192":
         return gen_rms_uniform(w.seed, w.M, w.N, w.dtype)
+    if w.op in ("ln_bwd", "rms_bwd"):
+        return gen_bwd(w.seed, w.M, w.N, w.dtype, w.op)
     raise KeyError(name)
