@@ -497,10 +497,12 @@ bool bwd_tile_ok(int team, int vpl, int epv) {
     return team >= kBwdMinTeam && tile_instantiated(team, vpl) && vpl * epv <= kBwdMaxElems;
 }
 
-// The backward grid: this many workgroups per CU, each writing one partial
-// row of dgamma / dbeta (fewer partial rows cost less traffic, more
-// workgroups hide more latency).
-constexpr int kBwdWgPerCu = 2;
+// The backward grid: one 1024-lane workgroup per CU, each writing one
+// partial row of dgamma / dbeta.  Measured on MI355X, LN bf16 16384 x 8192
+// (one 1024 x 1 team per workgroup): 145.5 us at 256 workgroups, 152.3 at
+// 512, 162.7 at 768; a second resident workgroup per CU does not fit, and
+// more partial rows cost traffic.
+constexpr int kBwdWgPerCu = 1;
 
 int device_cus() {
     static std::mutex mu;
@@ -516,10 +518,13 @@ int device_cus() {
     return cache[dev];
 }
 
-// A row kernel tile for the backward: about two 16-byte vectors per lane
-// (eight elements unaligned), at most kBwdMaxElems elements per lane, teams
-// of 8..1024 lanes.  Rows longer than 1024 x kBwdMaxElems (16384 when
-// unaligned) are NORM_ERR_BAD_SHAPE.  cus = 0 asks the device.
+// A row kernel tile for the backward: one 16-byte vector per lane (eight
+// elements unaligned) as long as a team of 1024 lanes covers the row, more
+// beyond, at most kBwdMaxElems elements per lane; teams of 8..1024 lanes in
+// workgroups of 1024.  Rows longer than 1024 x kBwdMaxElems (16384 when
+// unaligned) are NORM_ERR_BAD_SHAPE.  Measured (LN bf16 16384 x 8192, one
+// workgroup per CU): 1024 x 1 145.5 us, 512 x 2 151.5.  cus = 0 asks the
+// device.
 int make_bwd_plan(int64_t M, int64_t N, int dtype, bool aligned, const Overrides& o, int cus, Plan* p) {
     const int e = elem_bytes(dtype);
     std::memset(p, 0, sizeof *p);
@@ -531,7 +536,7 @@ int make_bwd_plan(int64_t M, int64_t N, int dtype, bool aligned, const Overrides
         vpl = o.vpl;
         if (!bwd_tile_ok(team, vpl, p->epv) || int64_t(team) * vpl < NV) return NORM_ERR_BAD_ARG;
     } else {
-        const int per_lane = p->epv == 1 ? 8 : 2;
+        const int per_lane = p->epv == 1 ? 8 : 1;
         team = next_pow2((NV + per_lane - 1) / per_lane);
         team = std::max(team, kBwdMinTeam);
         team = std::min(team, kMaxTeam);
@@ -541,7 +546,7 @@ int make_bwd_plan(int64_t M, int64_t N, int dtype, bool aligned, const Overrides
     p->path = PATH_ROWS;
     p->team = team;
     p->vpl = vpl;
-    p->wg = team >= 256 ? team : 256;
+    p->wg = kBwdWG;
     p->rows_per_wg = p->wg / team;
     p->work = (M + p->rows_per_wg - 1) / p->rows_per_wg;
     const int64_t cap = o.grid > 0 ? o.grid : int64_t(kBwdWgPerCu) * (cus > 0 ? cus : device_cus());
@@ -607,9 +612,13 @@ int run_bwd(const BwdArgs& a, void* stream) {
         }
         if (!hip_ok(err, "backward row kernel launch")) return NORM_ERR_HIP;
     }
-    // column sums of the partial rows (zeros when M = 0)
-    if (a.dgamma && !hip_ok(launch_colsum(pg, P, (int)N, a.dgamma, s), "column-sum launch")) return NORM_ERR_HIP;
-    if (a.dbeta && !hip_ok(launch_colsum(pb, P, (int)N, a.dbeta, s), "column-sum launch")) return NORM_ERR_HIP;
+    // column sums of the partial rows (zeros when M = 0), both in one launch
+    if (sums) {
+        const bool g = a.dgamma != nullptr;
+        err = launch_colsum(g ? pg : pb, g ? a.dgamma : a.dbeta, g ? pb : nullptr, g ? a.dbeta : nullptr, P,
+                            (int)N, s);
+        if (!hip_ok(err, "column-sum launch")) return NORM_ERR_HIP;
+    }
     return NORM_OK;
 }
 

@@ -14,28 +14,42 @@
 // grid-strided), summed over the workgroup's teams and written as one
 // partial row per workgroup: part_* is [gridDim.x, N].
 //
+// The grid is persistent (about one workgroup per CU), so each team walks many
+// rows one after another; where registers allow, the next row's dy, x and
+// statistics are loaded while the current row is reduced and written.
+// gamma -- the same columns for every row a lane sees -- is loaded once.
+//
 // norm_colsum_kernel: sums the partial rows of each column in a fixed order,
 // so dgamma and dbeta are bitwise reproducible for a given grid.
 #pragma once
 
+#include "dispatch.hpp"
 #include "prims.hpp"
 #include "rows.hpp"
 
 namespace mi355norm {
 
+// Backward workgroups hold kBwdWG lanes, i.e. kBwdWG / TEAM rows at once.
+template <int TEAM>
+struct BwdGeom {
+    static constexpr int WG = kBwdWG;
+    static constexpr int ROWS = WG / TEAM;                 // rows per workgroup
+    static constexpr int WPT = TEAM > 64 ? TEAM / 64 : 1;  // wavefronts per team
+};
+
 template <class T, bool RMS, int TEAM, int VPL, int EPV>
-__global__ __launch_bounds__(TeamGeom<TEAM>::WG)
+__global__ __launch_bounds__(kBwdWG)
 void norm_bwd_rows_kernel(const typename T::storage* dy,      // dx may be written over dy or x
                           const typename T::storage* x,
                           const typename T::storage* __restrict__ gamma,
                           const float* __restrict__ mean,
                           const float* __restrict__ rstd,
                           typename T::storage* dx,
-                          float* __restrict__ part_g,      // [P, N] partial dgamma rows (or null)
-                          float* __restrict__ part_b,      // [P, N] partial dbeta rows (or null)
+                          float* __restrict__ part_g,      // [gridDim.x, N] partial dgamma rows (or null)
+                          float* __restrict__ part_b,      // [gridDim.x, N] partial dbeta rows (or null)
                           int64_t M, int N, int64_t ldy, int64_t ldx, int64_t lddx)
 {
-    using G = TeamGeom<TEAM>;
+    using G = BwdGeom<TEAM>;
     using S = typename T::storage;
     using V = Vec<T, EPV>;
     __shared__ float2 red[2][G::ROWS][G::WPT];
@@ -46,9 +60,27 @@ void norm_bwd_rows_kernel(const typename T::storage* dy,      // dx may be writt
     const int wave_in_team = TEAM > 64 ? __builtin_amdgcn_readfirstlane(tl >> 6) : 0;
     const int NV = N / EPV;
     const float inv_n = 1.0f / (float)N;
-    const bool has_g = gamma != nullptr;
     const bool want_g = part_g != nullptr;
     const bool want_b = part_b != nullptr;
+
+    bool col_ok[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) col_ok[j] = (int)(j * TEAM + tl) < NV;
+
+    // gamma of this lane's columns (ones without gamma), kept packed for
+    // every row
+    V gam[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+        if (gamma != nullptr && col_ok[j]) {
+            gam[j].load(gamma + (j * TEAM + tl) * EPV);
+        } else {
+            float one[EPV];
+#pragma unroll
+            for (int k = 0; k < EPV; ++k) one[k] = 1.0f;
+            gam[j].set(one);
+        }
+    }
 
     float acc_g[VPL][EPV], acc_b[RMS ? 1 : VPL][EPV];
 #pragma unroll
@@ -58,44 +90,45 @@ void norm_bwd_rows_kernel(const typename T::storage* dy,      // dx may be writt
             acc_g[j][k] = 0.0f;
             if constexpr (!RMS) acc_b[j][k] = 0.0f;
         }
-    bool col_ok[VPL];
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) col_ok[j] = (int)(j * TEAM + tl) < NV;
 
+    // the loads of one row group: dy, x and the row's statistics
     const int64_t groups = (M + G::ROWS - 1) / G::ROWS;
-    int par = 0;
-    for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x, par ^= 1) {
+    auto fetch = [&](int64_t grp, V (&d)[VPL], V (&xx)[VPL], float& m, float& r) {
         const int64_t row = grp * G::ROWS + team;
-        const bool row_ok = row < M;
+        const bool row_ok = grp < groups && row < M;
         const int64_t rr = row_ok ? row : 0;
-        const S* dyr = dy + rr * ldy;
-        const S* xr = x + rr * ldx;
-        V dv[VPL], xv[VPL];
-        bool ok[VPL];
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
             const unsigned v = (unsigned)(j * TEAM + tl);
-            ok[j] = row_ok && col_ok[j];
-            if (ok[j]) {
-                dv[j].load_stream(dyr + v * EPV);
-                xv[j].load_stream(xr + v * EPV);
+            if (row_ok && col_ok[j]) {
+                d[j].load_stream(dy + rr * ldy + v * EPV);
+                xx[j].load_stream(x + rr * ldx + v * EPV);
             }
         }
-        const float mu = RMS ? 0.0f : (row_ok ? mean[rr] : 0.0f);
-        const float rs = row_ok ? rstd[rr] : 0.0f;
+        m = (!RMS && row_ok) ? mean[rr] : 0.0f;
+        r = row_ok ? rstd[rr] : 0.0f;
+    };
+    // One row group: the two row sums, dx, and the column accumulators.
+    // d, xx, m, r hold the group's loads; par picks the LDS exchange slots
+    // (consecutive groups alternate, so one barrier per group suffices).
+    auto row_group = [&](int64_t grp, const V (&d)[VPL], const V (&xx)[VPL], float m, float r, int par,
+                         auto&& before_stores) {
+        const int64_t row = grp * G::ROWS + team;
+        const bool row_ok = row < M;
+        const int64_t rr = row_ok ? row : 0;
+        bool ok[VPL];
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) ok[j] = row_ok && col_ok[j];
 
         // the row sums: (sum g, sum g xhat) for LayerNorm, (0, sum g x) for RMSNorm
         float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
             if (!ok[j]) continue;
-            const unsigned off = (unsigned)(j * TEAM + tl) * EPV;
-            V gv;
-            if (has_g) gv.load(gamma + off);
 #pragma unroll
             for (int k = 0; k < EPV; ++k) {
-                const float g = dv[j].get(k) * (has_g ? gv.get(k) : 1.0f);
-                const float xh = RMS ? xv[j].get(k) : (xv[j].get(k) - mu) * rs;
+                const float g = d[j].get(k) * gam[j].get(k);
+                const float xh = RMS ? xx[j].get(k) : (xx[j].get(k) - m) * r;
                 if constexpr (!RMS) s1 += g;
                 s2 = __builtin_fmaf(g, xh, s2);
             }
@@ -114,35 +147,85 @@ void norm_bwd_rows_kernel(const typename T::storage* dy,      // dx may be writt
             s1 = a;
             s2 = b;
         }
-        // LayerNorm: dx = rs (g - c1 - xhat c2); RMSNorm: dx = rs g - x c2
+        // LayerNorm: dx = r (g - c1 - xhat c2); RMSNorm: dx = r g - x c2
         const float c1 = s1 * inv_n;
-        const float c2 = RMS ? rs * rs * rs * (s2 * inv_n) : s2 * inv_n;
+        const float c2 = RMS ? r * r * r * (s2 * inv_n) : s2 * inv_n;
         S* dxr = dx + rr * lddx;
+        float o[VPL][EPV];
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
             if (!ok[j]) continue;
-            const unsigned off = (unsigned)(j * TEAM + tl) * EPV;
-            V gv;
-            if (has_g) gv.load(gamma + off);
-            float o[EPV];
 #pragma unroll
             for (int k = 0; k < EPV; ++k) {
-                const float d = dv[j].get(k);
-                const float g = d * (has_g ? gv.get(k) : 1.0f);
+                const float dk = d[j].get(k);
+                const float g = dk * gam[j].get(k);
                 if constexpr (RMS) {
-                    const float xv_k = xv[j].get(k);
-                    o[k] = __builtin_fmaf(rs, g, -xv_k * c2);
-                    acc_g[j][k] = __builtin_fmaf(d, xv_k * rs, acc_g[j][k]);
+                    const float xk = xx[j].get(k);
+                    o[j][k] = __builtin_fmaf(r, g, -xk * c2);
+                    acc_g[j][k] = __builtin_fmaf(dk, xk * r, acc_g[j][k]);
                 } else {
-                    const float xh = (xv[j].get(k) - mu) * rs;
-                    o[k] = rs * ((g - c1) - xh * c2);
-                    acc_g[j][k] = __builtin_fmaf(d, xh, acc_g[j][k]);
-                    acc_b[j][k] += d;
+                    const float xh = (xx[j].get(k) - m) * r;
+                    o[j][k] = r * ((g - c1) - xh * c2);
+                    acc_g[j][k] = __builtin_fmaf(dk, xh, acc_g[j][k]);
+                    acc_b[j][k] += dk;
                 }
             }
-            V::store(dxr + off, o);
+        }
+        before_stores();
+#pragma unroll
+        for (int j = 0; j < VPL; ++j)
+            if (ok[j]) V::store(dxr + (unsigned)(j * TEAM + tl) * EPV, o[j]);
+    };
+
+    // The next row group's loads are issued before this one is worked on
+    // when the registers allow: LIVE counts the VGPRs held across rows (dy,
+    // x, gamma, the column accumulators), and a second copy of dy and x must
+    // keep the total well under the 128 a 1024-lane workgroup may use.  The
+    // loop is unrolled by two over register sets A and B, so that no copy
+    // between them forces an early wait.  Loads and stores share one
+    // completion counter and may complete out of order with respect to each
+    // other, so a wait for loads issued before a store is a wait for the
+    // store too; each row therefore waits for the next row's loads (which
+    // have been in flight during its work) before it issues its own stores.
+    constexpr int WORDS = (EPV * (int)sizeof(S) + 3) / 4;   // VGPRs per vector
+    constexpr int LIVE = 3 * VPL * WORDS + (RMS ? 1 : 2) * VPL * EPV;
+    constexpr bool PREFETCH = LIVE + 2 * VPL * WORDS <= 80;
+    const int64_t stride = gridDim.x;
+    V dA[VPL], xA[VPL];
+    float mA, rA;
+    fetch(blockIdx.x, dA, xA, mA, rA);
+    if constexpr (PREFETCH) {
+        V dB[VPL], xB[VPL];
+        float mB, rB;
+        auto ready = [&](V (&d)[VPL], V (&xx)[VPL], float& m, float& r) {
+#pragma unroll
+            for (int j = 0; j < VPL; ++j) {
+                d[j].opaque();
+                xx[j].opaque();
+            }
+            asm volatile("" : "+v"(m), "+v"(r));
+        };
+        // (ready() runs on every path, the first group's loads included: a
+        // load still pending where paths join makes its first use wait
+        // again, for everything issued since)
+        ready(dA, xA, mA, rA);
+        for (int64_t grp = blockIdx.x; grp < groups;) {
+            fetch(grp + stride, dB, xB, mB, rB);
+            row_group(grp, dA, xA, mA, rA, 0, [&] { ready(dB, xB, mB, rB); });
+            grp += stride;
+            if (grp >= groups) break;
+            fetch(grp + stride, dA, xA, mA, rA);
+            row_group(grp, dB, xB, mB, rB, 1, [&] { ready(dA, xA, mA, rA); });
+            grp += stride;
+        }
+    } else {
+        int par = 0;
+        for (int64_t grp = blockIdx.x; grp < groups; grp += stride, par ^= 1) {
+            row_group(grp, dA, xA, mA, rA, par, [] {});
+            fetch(grp + stride, dA, xA, mA, rA);
         }
     }
+
     // One partial row per workgroup.  Teams own the same columns lane for
     // lane (lane tl of every team holds vectors j*TEAM + tl), so with several
     // teams per workgroup team 0 adds the others' accumulators, one element
@@ -184,22 +267,40 @@ void norm_bwd_rows_kernel(const typename T::storage* dy,      // dx may be writt
     }
 }
 
-// out[c] = sum over p = 0 .. P-1 of part[p * N + c], in a fixed order: a
-// workgroup of 1024 lanes takes 64 columns; its 16 wavefronts sum
-// interleaved sixteenths of the partial rows (wavefront w: rows w, w + 16,
-// ...), then wavefront 0 adds the sixteen sums in order.  P = 0 gives zeros.
+// out[c] = sum over p = 0 .. P-1 of part[p * N + c], in a fixed order, for
+// up to two (part, out) pairs: blockIdx.y = 0 takes (part_g, out_g), 1 takes
+// (part_b, out_b); a null out skips its pair.  A workgroup of 64 * WAVES
+// lanes takes 64 columns; wavefront w sums rows w, w + WAVES, w + 2 WAVES,
+// ... into four accumulators in turn (row w + i WAVES goes to accumulator
+// i mod 4), adds them as (a0 + a1) + (a2 + a3), then wavefront 0 adds the
+// WAVES sums in order.  P = 0 gives zeros.
 template <int WAVES>
 __global__ __launch_bounds__(64 * WAVES)
-void norm_colsum_kernel(const float* __restrict__ part, int64_t P, int N, float* __restrict__ out)
+void norm_colsum_kernel(const float* __restrict__ part_g, float* __restrict__ out_g,
+                        const float* __restrict__ part_b, float* __restrict__ out_b, int64_t P, int N)
 {
     __shared__ float q[WAVES][64];
+    const float* part = blockIdx.y == 0 ? part_g : part_b;
+    float* out = blockIdx.y == 0 ? out_g : out_b;
+    if (out == nullptr) return;           // the same for the whole workgroup
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int64_t c = (int64_t)blockIdx.x * 64 + lane;
-    float s = 0.0f;
-    if (c < N)
-        for (int64_t p = w; p < P; p += WAVES) s += part[p * N + c];
-    q[w][lane] = s;
+    float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+    if (c < N) {
+        const float* col = part + c;
+        int64_t p = w;
+        for (; p + 3 * WAVES < P; p += 4 * WAVES) {
+            a0 += col[p * N];
+            a1 += col[(p + WAVES) * N];
+            a2 += col[(p + 2 * WAVES) * N];
+            a3 += col[(p + 3 * WAVES) * N];
+        }
+        if (p < P) a0 += col[p * N];
+        if (p + WAVES < P) a1 += col[(p + WAVES) * N];
+        if (p + 2 * WAVES < P) a2 += col[(p + 2 * WAVES) * N];
+    }
+    q[w][lane] = (a0 + a1) + (a2 + a3);
     __syncthreads();
     if (w == 0 && c < N) {
         float t = q[0][lane];

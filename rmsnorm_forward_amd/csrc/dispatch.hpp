@@ -78,6 +78,9 @@ constexpr int kMaxVpl = 16;
 // accumulators live in registers); teams of 8 lanes and up
 constexpr int kBwdMaxElems = 32;
 constexpr int kBwdMinTeam = 8;
+// backward workgroups: always 1024 lanes (16 wavefronts fill a CU's wave
+// slots at up to 128 VGPRs), 1024 / team rows at once
+constexpr int kBwdWG = 1024;
 // Split-row chunk geometry: the two kernels of the two-kernel form (each
 // its own chunk size), and the single pass (fewer, larger chunks: fewer
 // arrivals per row at its barrier).
@@ -135,8 +138,10 @@ hipError_t launch_split_coop_f16(int op, const NormCall& c, const Plan& p, float
 hipError_t launch_bwd_f32(int op, const BwdCall& c, const Plan& p);
 hipError_t launch_bwd_bf16(int op, const BwdCall& c, const Plan& p);
 hipError_t launch_bwd_f16(int op, const BwdCall& c, const Plan& p);
-// out[c] = sum of the P partial rows of column c (fixed order)
-hipError_t launch_colsum(const float* part, int64_t P, int N, float* out, hipStream_t stream);
+// out_*[c] = sum of the P partial rows part_* of column c (fixed order), for
+// dgamma and (out_b not null) dbeta in one launch
+hipError_t launch_colsum(const float* part_g, float* out_g, const float* part_b, float* out_b, int64_t P, int N,
+                         hipStream_t stream);
 // workgroups of the single-pass split kernel that fit on one CU at once
 int coop_blocks_per_cu_f32(int op, int epv);
 int coop_blocks_per_cu_bf16(int op, int epv);

@@ -19,9 +19,11 @@ int coop_blocks_per_cu_f32(int op, int epv) {
 hipError_t launch_bwd_f32(int op, const BwdCall& c, const Plan& p) {
     return detail::launch_bwd<F32>(op, c, p);
 }
-hipError_t launch_colsum(const float* part, int64_t P, int N, float* out, hipStream_t stream) {
-    hipLaunchKernelGGL(norm_colsum_kernel<kColsumWaves>, dim3((unsigned)((N + 63) / 64)), dim3(64 * kColsumWaves), 0, stream,
-                       part, P, N, out);
+hipError_t launch_colsum(const float* part_g, float* out_g, const float* part_b, float* out_b, int64_t P, int N,
+                         hipStream_t stream) {
+    const dim3 grid((unsigned)((N + 63) / 64), out_b ? 2u : 1u);
+    hipLaunchKernelGGL(norm_colsum_kernel<kColsumWaves>, grid, dim3(64 * kColsumWaves), 0, stream, part_g, out_g,
+                       part_b, out_b, P, N);
     return hipGetLastError();
 }
 }  // namespace mi355norm

@@ -230,7 +230,7 @@ hipError_t go_bwd(const BwdCall& c, const Plan& p) {
     int64_t ldy = c.ldy, ldx = c.ldx, lddx = c.lddx;
     void* args[] = {&dy, &x, &g, &mean, &rstd, &dx, &pg, &pb, &M, &N, &ldy, &ldx, &lddx};
     return hipLaunchKernel(reinterpret_cast<const void*>(&norm_bwd_rows_kernel<T, RMS, TEAM, VPL, EPV>),
-                           dim3((unsigned)p.grid), dim3(TeamGeom<TEAM>::WG), args, 0, c.stream);
+                           dim3((unsigned)p.grid), dim3(kBwdWG), args, 0, c.stream);
 }
 
 template <class T, bool RMS, int TEAM, int EPV>

@@ -442,8 +442,10 @@ def test_bwd_every_row_fits_its_tile(dtype, aligned):
         slots = p["team"] * p["vpl"] * epv
         assert slots >= N and (p["team"] == 8 or N >= slots // 4)
         assert p["vpl"] * epv <= 32 and 8 <= p["team"] <= 1024
-        assert p["wg"] == max(p["team"], 256) and p["rows_per_wg"] == p["wg"] // p["team"]
-        assert p["grid"] == min(p["work"], 512) == p["partial_rows"]
+        assert p["wg"] == 1024 and p["rows_per_wg"] == 1024 // p["team"]
+        assert p["grid"] == min(p["work"], 256) == p["partial_rows"]      # one workgroup per CU
+        if aligned and p["team"] * epv < N:
+            assert p["team"] == 1024                    # more than one vector per lane only past 1024 lanes
 
 
 def test_bwd_grid_override(monkeypatch):
