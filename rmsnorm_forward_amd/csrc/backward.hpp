@@ -111,7 +111,7 @@ void norm_bwd_rows_kernel(const typename T::storage* dy,      // dx may be writt
     // One row group: the two row sums, dx, and the column accumulators.
     // d, xx, m, r hold the group's loads; par picks the LDS exchange slots
     // (consecutive groups alternate, so one barrier per group suffices).
-    auto row_group = [&](int64_t grp, const V (&d)[VPL], const V (&xx)[VPL], float m, float r, int par,
+    auto row_group = [&](int64_t grp, V (&d)[VPL], V (&xx)[VPL], float m, float r, int par,
                          auto&& before_stores) {
         const int64_t row = grp * G::ROWS + team;
         const bool row_ok = row < M;
@@ -133,6 +133,13 @@ void norm_bwd_rows_kernel(const typename T::storage* dy,      // dx may be writt
                 s2 = __builtin_fmaf(g, xh, s2);
             }
         }
+        // re-widen dy and x after the exchange rather than keep fp32 copies
+        // live across it
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+            d[j].opaque();
+            xx[j].opaque();
+        }
         if constexpr (!RMS) s1 = team_sum<(TEAM < 64 ? TEAM : 64)>(s1);
         s2 = team_sum<(TEAM < 64 ? TEAM : 64)>(s2);
         if constexpr (TEAM > 64) {
@@ -151,30 +158,32 @@ void norm_bwd_rows_kernel(const typename T::storage* dy,      // dx may be writt
         const float c1 = s1 * inv_n;
         const float c2 = RMS ? r * r * r * (s2 * inv_n) : s2 * inv_n;
         S* dxr = dx + rr * lddx;
-        float o[VPL][EPV];
+        V out[VPL];
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
             if (!ok[j]) continue;
+            float o[EPV];
 #pragma unroll
             for (int k = 0; k < EPV; ++k) {
                 const float dk = d[j].get(k);
                 const float g = dk * gam[j].get(k);
                 if constexpr (RMS) {
                     const float xk = xx[j].get(k);
-                    o[j][k] = __builtin_fmaf(r, g, -xk * c2);
+                    o[k] = __builtin_fmaf(r, g, -xk * c2);
                     acc_g[j][k] = __builtin_fmaf(dk, xk * r, acc_g[j][k]);
                 } else {
                     const float xh = (xx[j].get(k) - m) * r;
-                    o[j][k] = r * ((g - c1) - xh * c2);
+                    o[k] = r * ((g - c1) - xh * c2);
                     acc_g[j][k] = __builtin_fmaf(dk, xh, acc_g[j][k]);
                     acc_b[j][k] += dk;
                 }
             }
+            out[j].set(o);           // rounded to the storage type (RNE)
         }
         before_stores();
 #pragma unroll
         for (int j = 0; j < VPL; ++j)
-            if (ok[j]) V::store(dxr + (unsigned)(j * TEAM + tl) * EPV, o[j]);
+            if (ok[j]) out[j].put_stream(dxr + (unsigned)(j * TEAM + tl) * EPV);
     };
 
     // The next row group's loads are issued before this one is worked on
