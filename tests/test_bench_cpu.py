@@ -27,18 +27,25 @@ def test_traffic_needs_matching_sources_and_plan(tmp_path, monkeypatch):
     (prof / "k__w_counters.txt").write_text(
         "kernel_source_sha256: abc\nplan: path=rows team=256\ntraffic_bytes_per_launch: 123\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    monkeypatch.setattr(bench, "kernel_source_digest", lambda: "abc")
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda kernel="norm_rows_kernel": "abc")
     assert bench.read_traffic("k", "w", "path=rows team=256") == 123.0
     assert bench.read_traffic("k", "w", "path=rows team=512") is None      # another tile
     assert bench.read_traffic("k", "other", "path=rows team=256") is None  # no summary
-    monkeypatch.setattr(bench, "kernel_source_digest", lambda: "def")
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda kernel="norm_rows_kernel": "def")
     assert bench.read_traffic("k", "w", "path=rows team=256") is None      # kernels changed
 
 
 def test_kernel_digest_covers_the_device_code():
-    for name in bench.KERNEL_SOURCES:
-        assert os.path.exists(os.path.join(ROOT, "rmsnorm_forward_amd", "csrc", name)), name
-    assert len(bench.kernel_source_digest()) == 64
+    for kernel, names in bench.KERNEL_SOURCES.items():
+        for name in names:
+            assert os.path.exists(os.path.join(ROOT, "rmsnorm_forward_amd", "csrc", name)), name
+        assert len(bench.kernel_source_digest(kernel)) == 64
+    # every kernel header is covered by some digest; the backward's own header
+    # does not move the forward's digest
+    covered = {n for names in bench.KERNEL_SOURCES.values() for n in names}
+    headers = {f for f in os.listdir(os.path.join(ROOT, "rmsnorm_forward_amd", "csrc")) if f.endswith(".hpp")}
+    assert headers - covered <= {"dispatch.hpp"}
+    assert "backward.hpp" not in bench.KERNEL_SOURCES["norm_rows_kernel"]
 
 
 def test_cpu_baseline_counts_the_rows_it_ran():
