@@ -236,6 +236,33 @@ int ln_bwd(const void *dy, const void *x, const void *gamma, const float *mean, 
 int rms_bwd(const void *dy, const void *x, const void *gamma, const float *rstd, void *dx,
             float *dgamma, int64_t M, int64_t N, int dtype, void *stream);
 
+/*
+ * ln_bwd (op NORM_OP_LN) or rms_bwd (op NORM_OP_RMS) with row strides: row r
+ * of dy, x and dx starts ld_* elements after row r - 1 (0 means N; ld_* < N,
+ * or so large that a matrix does not fit 2^63 bytes, is NORM_ERR_BAD_SHAPE).
+ * dx may be written over dy or x only with the same pointer and stride.  The
+ * 16-byte vector path needs every row start 16-byte aligned.  Other
+ * conventions as above; returns a norm_status.
+ */
+typedef struct {
+    int op;                       /* NORM_OP_LN or NORM_OP_RMS                     */
+    int dtype;
+    int64_t M, N;
+    const void *dy;
+    int64_t ld_dy;
+    const void *x;
+    int64_t ld_x;
+    const void *gamma;            /* [N] or NULL                                    */
+    const float *mean;            /* fp32 [M]; LayerNorm only (NULL for RMSNorm)    */
+    const float *rstd;            /* fp32 [M]                                       */
+    void *dx;
+    int64_t ld_dx;
+    float *dgamma;                /* fp32 [N] or NULL                               */
+    float *dbeta;                 /* fp32 [N] or NULL; LayerNorm only               */
+} norm_bwd_args;
+
+int norm_bwd(const norm_bwd_args *args, void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *norm_status_str(int status);
 

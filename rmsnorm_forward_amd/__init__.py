@@ -6,7 +6,8 @@ only marshals arguments.  PyTorch is used for device memory and streams.
 
 Two layers:
   * ln_fwd / rms_fwd / add_rms_fwd / rms_fp8_fwd / add_rms_fp8_fwd /
-    norm_fwd (row strides) / ln_bwd / rms_bwd / norm_status_str /
+    norm_fwd (row strides) / ln_bwd / rms_bwd / norm_bwd (row strides) /
+    norm_status_str /
     norm_last_error / norm_describe / norm_bwd_describe -- the C ABI entry
     points under the same names, taking raw device addresses (ints) and
     returning the status code;
@@ -152,6 +153,27 @@ def norm_fwd(op, dtype, M, N, x, y, *, ld_x=0, residual=None, ld_residual=0, gam
                  _addr(residual), int(ld_residual), _addr(gamma), _addr(beta), _addr(y), int(ld_y),
                  _addr(residual_out), int(ld_residual_out), _addr(mean), _addr(rstd), float(eps), float(scale))
     return _lib.norm_fwd(ctypes.byref(a), _addr(stream))
+
+
+class NormBwdArgs(ctypes.Structure):
+    """norm_bwd_args of include/mi355norm.h."""
+    _fields_ = [("op", _int), ("dtype", _int), ("M", _i64), ("N", _i64),
+                ("dy", _vp), ("ld_dy", _i64), ("x", _vp), ("ld_x", _i64), ("gamma", _vp),
+                ("mean", _vp), ("rstd", _vp), ("dx", _vp), ("ld_dx", _i64), ("dgamma", _vp), ("dbeta", _vp)]
+
+
+_lib.norm_bwd.argtypes = [ctypes.POINTER(NormBwdArgs), _vp]
+_lib.norm_bwd.restype = _int
+
+
+def norm_bwd(op, dtype, M, N, dy, x, dx, *, ld_dy=0, ld_x=0, ld_dx=0, gamma=None, mean=None, rstd=None,
+             dgamma=None, dbeta=None, stream=None) -> int:
+    """ln_bwd (op "ln") or rms_bwd (op "rms") with row strides (elements;
+    0 = N), on device addresses; returns the norm_status code."""
+    a = NormBwdArgs(OPS.get(op, op), DTYPE_NAMES.get(dtype, dtype), int(M), int(N), _addr(dy), int(ld_dy),
+                    _addr(x), int(ld_x), _addr(gamma), _addr(mean), _addr(rstd), _addr(dx), int(ld_dx),
+                    _addr(dgamma), _addr(dbeta))
+    return _lib.norm_bwd(ctypes.byref(a), _addr(stream))
 
 
 def norm_status_str(status: int) -> str:
@@ -341,47 +363,48 @@ def fused_add_rms_norm_fp8(x, residual, gamma=None, scale: float = 1.0, eps: flo
     return codes, (residual if inplace else h.view(x.shape)), rstd
 
 
-def _bwd_operands(dy, x, gamma, stats):
+def _bwd_run(op, dy, x, gamma, mean, rstd, want_dgamma, want_dbeta):
+    """One norm_bwd call on tensors: dy and x may have strided rows (no
+    copy); dx is allocated contiguous."""
     import torch
     if dy.shape != x.shape or dy.dtype != x.dtype or dy.device != x.device:
         raise ValueError("dy must have x's shape, dtype and device")
     N = x.shape[-1]
     M = x.numel() // N if N else 0
+    stats = [s for s in (mean, rstd) if s is not None]
     for s in stats:
         if s.dtype != torch.float32 or s.numel() != M or s.device != x.device:
             raise ValueError("mean / rstd must be fp32 with one value per row, on x's device")
-    return (M, N, dy.reshape(M, N).contiguous(), x.reshape(M, N).contiguous(), _param(gamma, N, x),
-            [s.contiguous() for s in stats])
-
-
-def layer_norm_backward(dy, x, mean, rstd, gamma=None, want_dgamma: bool = True, want_dbeta: bool = True):
-    """Gradients of layer_norm from its saved fp32 mean and rstd: returns
-    (dx, dgamma, dbeta); dx has x's shape and dtype, dgamma and dbeta are
-    fp32 [N] (None when not wanted)."""
-    import torch
-    M, N, dy2, x2, g, (mean, rstd) = _bwd_operands(dy, x, gamma, (mean, rstd))
+    dy2, lddy = _rows(dy, N)
+    x2, ldx = _rows(x, N)
+    mean = mean.contiguous() if mean is not None else None
+    rstd = rstd.contiguous()
     dx = torch.empty((M, N), dtype=x.dtype, device=x.device)
     dgamma = torch.empty(N, dtype=torch.float32, device=x.device) if want_dgamma else None
     dbeta = torch.empty(N, dtype=torch.float32, device=x.device) if want_dbeta else None
     with torch.cuda.device(x.device):
         stream = torch.cuda.current_stream(x.device).cuda_stream
-        _check(ln_bwd(_ptr(dy2), _ptr(x2), _ptr(g), _ptr(mean), _ptr(rstd), _ptr(dx), _ptr(dgamma),
-                      _ptr(dbeta), M, N, _torch_dtype_code(x), stream))
+        _check(norm_bwd(op, _torch_dtype_code(x), M, N, _ptr(dy2), _ptr(x2), _ptr(dx), ld_dy=lddy, ld_x=ldx,
+                        ld_dx=N, gamma=_ptr(_param(gamma, N, x)), mean=_ptr(mean), rstd=_ptr(rstd),
+                        dgamma=_ptr(dgamma), dbeta=_ptr(dbeta), stream=stream))
     return dx.view(x.shape), dgamma, dbeta
+
+
+def layer_norm_backward(dy, x, mean, rstd, gamma=None, want_dgamma: bool = True, want_dbeta: bool = True):
+    """Gradients of layer_norm from its saved fp32 mean and rstd: returns
+    (dx, dgamma, dbeta); dx has x's shape and dtype, dgamma and dbeta are
+    fp32 [N] (None when not wanted).  Rows of dy and x may be strided."""
+    if mean is None:
+        raise ValueError("layer_norm_backward needs the forward's mean")
+    return _bwd_run("ln", dy, x, gamma, mean, rstd, want_dgamma, want_dbeta)
 
 
 def rms_norm_backward(dy, x, rstd, gamma=None, want_dgamma: bool = True):
     """Gradients of rms_norm from its saved fp32 rstd: returns (dx, dgamma);
-    dgamma is fp32 [N] (None when not wanted)."""
-    import torch
-    M, N, dy2, x2, g, (rstd,) = _bwd_operands(dy, x, gamma, (rstd,))
-    dx = torch.empty((M, N), dtype=x.dtype, device=x.device)
-    dgamma = torch.empty(N, dtype=torch.float32, device=x.device) if want_dgamma else None
-    with torch.cuda.device(x.device):
-        stream = torch.cuda.current_stream(x.device).cuda_stream
-        _check(rms_bwd(_ptr(dy2), _ptr(x2), _ptr(g), _ptr(rstd), _ptr(dx), _ptr(dgamma), M, N,
-                       _torch_dtype_code(x), stream))
-    return dx.view(x.shape), dgamma
+    dgamma is fp32 [N] (None when not wanted).  Rows of dy and x may be
+    strided."""
+    dx, dgamma, _ = _bwd_run("rms", dy, x, gamma, None, rstd, want_dgamma, False)
+    return dx, dgamma
 
 
 def _autograd():
@@ -441,6 +464,6 @@ def rms_norm_autograd(x, gamma=None, eps: float = 1e-6):
 __all__ = ["ln_fwd", "rms_fwd", "add_rms_fwd", "rms_fp8_fwd", "add_rms_fp8_fwd", "norm_fwd", "NormArgs",
            "norm_status_str", "norm_last_error", "norm_describe", "layer_norm", "rms_norm",
            "fused_add_rms_norm", "rms_norm_fp8", "fused_add_rms_norm_fp8",
-           "ln_bwd", "rms_bwd", "norm_bwd_describe", "layer_norm_backward", "rms_norm_backward",
+           "ln_bwd", "rms_bwd", "norm_bwd", "NormBwdArgs", "norm_bwd_describe", "layer_norm_backward", "rms_norm_backward",
            "layer_norm_autograd", "rms_norm_autograd",
            "NORM_F32", "NORM_F16", "NORM_BF16", "NORM_OK", "STATUS", "LIB_PATH", "OPS"]

@@ -470,7 +470,7 @@ int run(const Args& a, void* stream) {
 // backward
 // ---------------------------------------------------------------------------
 
-// Arguments of one backward call (row strides N).
+// Arguments of one backward call, row strides resolved (elements).
 struct BwdArgs {
     bool rms;
     int dtype;
@@ -483,14 +483,17 @@ struct BwdArgs {
     void* dx;
     float* dgamma;
     float* dbeta;
+    int64_t lddy, ldx, lddx;
 };
 
+// The 16-byte vector path: every row start on a 16-byte boundary and N
+// filling whole vectors.
 bool bwd_vector_aligned(const BwdArgs& a) {
     const int e = elem_bytes(a.dtype);
     if ((a.N * e) % 16) return false;
     for (const void* q : {a.dy, a.x, a.gamma, (const void*)a.dx})
         if ((uintptr_t)q % 16) return false;
-    return true;
+    return (a.lddy * e) % 16 == 0 && (a.ldx * e) % 16 == 0 && (a.lddx * e) % 16 == 0;
 }
 
 bool bwd_tile_ok(int team, int vpl, int epv) {
@@ -558,23 +561,25 @@ int validate_bwd(const BwdArgs& a) {
     if (a.dtype != NORM_F32 && a.dtype != NORM_F16 && a.dtype != NORM_BF16) return NORM_ERR_BAD_DTYPE;
     const int64_t M = a.M, N = a.N;
     if (M < 0 || N < 1 || N > kMaxN) return NORM_ERR_BAD_SHAPE;
-    if (M > 0 && M - 1 > (INT64_MAX / 8 - N) / N) return NORM_ERR_BAD_SHAPE;
-    if (a.rms && a.dbeta) return NORM_ERR_BAD_ARG;
+    for (int64_t ld : {a.lddy, a.ldx, a.lddx})
+        if (ld < N || ld > INT64_MAX / 8 || (M > 0 && M - 1 > (INT64_MAX / 8 - N) / ld)) return NORM_ERR_BAD_SHAPE;
+    if (a.rms && (a.dbeta || a.mean)) return NORM_ERR_BAD_ARG;
     if (M > 0 && (!a.dy || !a.x || !a.dx || !a.rstd || (!a.rms && !a.mean))) return NORM_ERR_NULL_ARG;
     const int e = elem_bytes(a.dtype);
     if (misaligned(a.dy, e) || misaligned(a.x, e) || misaligned(a.gamma, e) || misaligned(a.dx, e) ||
         misaligned(a.mean, 4) || misaligned(a.rstd, 4) || misaligned(a.dgamma, 4) || misaligned(a.dbeta, 4))
         return NORM_ERR_BAD_ARG;
     // in: 0 dy, 1 x, 2 gamma, 3 mean, 4 rstd;  out: 5 dx, 6 dgamma, 7 dbeta
-    const Mat m[8] = {{a.dy, M, N * e, N * e},  {a.x, M, N * e, N * e},  {a.gamma, 1, N * e, N * e},
-                      {a.mean, 1, M * 4, M * 4}, {a.rstd, 1, M * 4, M * 4}, {a.dx, M, N * e, N * e},
-                      {a.dgamma, 1, N * 4, N * 4}, {a.dbeta, 1, N * 4, N * 4}};
+    const Mat m[8] = {{a.dy, M, N * e, a.lddy * e},  {a.x, M, N * e, a.ldx * e},  {a.gamma, 1, N * e, N * e},
+                      {a.mean, 1, M * 4, M * 4},      {a.rstd, 1, M * 4, M * 4}, {a.dx, M, N * e, a.lddx * e},
+                      {a.dgamma, 1, N * 4, N * 4},    {a.dbeta, 1, N * 4, N * 4}};
     for (int i = 0; i < 8; ++i)
         for (int j = i + 1; j < 8; ++j) {
             if (j < 5 || !overlaps(m[i], m[j])) continue;
-            // dx may be written exactly over dy or x: a lane loads the
-            // elements it owns from both before it stores any of them
-            if (j == 5 && i <= 1 && m[i].p == m[j].p) continue;
+            // dx may be written exactly over dy or x (same pointer and
+            // stride): a lane loads the elements it owns from both before it
+            // stores any of them
+            if (j == 5 && i <= 1 && m[i].p == m[j].p && m[i].ld == m[j].ld) continue;
             return NORM_ERR_ALIAS;
         }
     return NORM_OK;
@@ -603,7 +608,7 @@ int run_bwd(const BwdArgs& a, void* stream) {
     }
     hipError_t err = hipSuccess;
     if (M > 0) {
-        BwdCall c{a.dy, a.x, a.gamma, a.mean, a.rstd, a.dx, pg, pb, M, (int)N, N, N, N, s};
+        BwdCall c{a.dy, a.x, a.gamma, a.mean, a.rstd, a.dx, pg, pb, M, (int)N, a.lddy, a.ldx, a.lddx, s};
         const int op = a.rms ? OP_RMS : OP_LN;
         switch (a.dtype) {
         case NORM_F32: err = launch_bwd_f32(op, c, p); break;
@@ -670,12 +675,22 @@ int add_rms_fp8_fwd(const void* x, const void* residual, const void* gamma, void
 
 int ln_bwd(const void* dy, const void* x, const void* gamma, const float* mean, const float* rstd, void* dx,
            float* dgamma, float* dbeta, int64_t M, int64_t N, int dtype, void* stream) {
-    return run_bwd(BwdArgs{false, dtype, M, N, dy, x, gamma, mean, rstd, dx, dgamma, dbeta}, stream);
+    return run_bwd(BwdArgs{false, dtype, M, N, dy, x, gamma, mean, rstd, dx, dgamma, dbeta, N, N, N}, stream);
 }
 
 int rms_bwd(const void* dy, const void* x, const void* gamma, const float* rstd, void* dx, float* dgamma,
             int64_t M, int64_t N, int dtype, void* stream) {
-    return run_bwd(BwdArgs{true, dtype, M, N, dy, x, gamma, nullptr, rstd, dx, dgamma, nullptr}, stream);
+    return run_bwd(BwdArgs{true, dtype, M, N, dy, x, gamma, nullptr, rstd, dx, dgamma, nullptr, N, N, N}, stream);
+}
+
+int norm_bwd(const norm_bwd_args* args, void* stream) {
+    if (!args) return NORM_ERR_NULL_ARG;
+    const norm_bwd_args& g = *args;
+    if (g.op != NORM_OP_LN && g.op != NORM_OP_RMS) return NORM_ERR_BAD_ARG;
+    auto ld = [&](int64_t v) { return v == 0 ? g.N : v; };
+    return run_bwd(BwdArgs{g.op == NORM_OP_RMS, g.dtype, g.M, g.N, g.dy, g.x, g.gamma, g.mean, g.rstd, g.dx,
+                           g.dgamma, g.dbeta, ld(g.ld_dy), ld(g.ld_x), ld(g.ld_dx)},
+                   stream);
 }
 
 int norm_bwd_describe(int rms, int64_t M, int64_t N, int dtype, int aligned, char* buf, int buflen) {

@@ -221,3 +221,39 @@ def run_strided(op: str, dtype: str, x, gamma, beta, eps: float, *, res=None, sc
         h, hgap = _extract(hb, dtype, M, N, ldh or N, offset)
         assert np.all(bits(hgap, dtype) == FILL[dtype]), "a write landed outside the rows of the residual sum"
     return (y, h, mean.cpu().numpy() if mean is not None else None, rstd.cpu().numpy())
+
+
+def run_bwd_strided(op: str, dtype: str, dy, x, gamma, mean, rstd, *, lddy: int, ldx: int, lddx: int,
+                    offset: int = 0, inplace: str | None = None):
+    """One norm_bwd call with strided rows.  Returns (dx, dgamma, dbeta) and
+    asserts that no byte between or around the rows of dx changed (and,
+    unless dx is written over it, that dy and x are unchanged)."""
+    M, N = x.shape
+    dyb, dyt = _embed(dy, dtype, lddy, offset, FILL[dtype])
+    xb, xt = _embed(x, dtype, ldx, offset, FILL[dtype])
+    gt = to_device(gamma, dtype) if gamma is not None else None
+    mt = torch.from_numpy(np.ascontiguousarray(mean, np.float32)).cuda() if op == "ln" else None
+    rt = torch.from_numpy(np.ascontiguousarray(rstd, np.float32)).cuda()
+    if inplace == "dy":
+        dxb, dxt, lddx = dyb, dyt, lddy
+    elif inplace == "x":
+        dxb, dxt, lddx = xb, xt, ldx
+    else:
+        dxb, dxt = _embed(np.zeros((M, N), NP_STORAGE[dtype]), dtype, lddx, offset, FILL[dtype])
+    dgt = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
+    dbt = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda") if op == "ln" else None
+    p = lambda t: t.data_ptr() if t is not None else None
+    st = rn.norm_bwd(op, CODE[dtype], M, N, p(dyt), p(xt), p(dxt), ld_dy=lddy, ld_x=ldx, ld_dx=lddx,
+                     gamma=p(gt), mean=p(mt), rstd=p(rt), dgamma=p(dgt), dbeta=p(dbt),
+                     stream=torch.cuda.current_stream().cuda_stream)
+    assert st == rn.NORM_OK, f"{rn.STATUS.get(st)}: {rn.norm_status_str(st)} [{rn.norm_last_error()}]"
+    torch.cuda.synchronize()
+    bits = lambda a: a.view({"f32": np.uint32, "f16": np.uint16}.get(dtype, a.dtype))
+    dx, gap = _extract(dxb, dtype, M, N, lddx, offset)
+    assert np.all(bits(gap) == FILL[dtype]), "a write landed outside the rows of dx"
+    for name, (b, a, ld) in {"dy": (dyb, dy, lddy), "x": (xb, x, ldx)}.items():
+        if inplace == name:
+            continue
+        rows, _ = _extract(b, dtype, M, N, ld, offset)
+        assert np.array_equal(bits(rows), bits(np.ascontiguousarray(a))), f"{name} changed"
+    return dx, dgt.cpu().numpy(), dbt.cpu().numpy() if dbt is not None else None

@@ -26,9 +26,9 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["add_rms_fp8_fwd", "add_rms_fwd", "ln_bwd", "ln_fwd", "norm_bwd_describe",
-                                    "norm_describe", "norm_fwd", "norm_last_error", "norm_status_str",
-                                    "rms_bwd", "rms_fp8_fwd", "rms_fwd"]
+    assert declared_functions() == ["add_rms_fp8_fwd", "add_rms_fwd", "ln_bwd", "ln_fwd", "norm_bwd",
+                                    "norm_bwd_describe", "norm_describe", "norm_fwd", "norm_last_error",
+                                    "norm_status_str", "rms_bwd", "rms_fp8_fwd", "rms_fwd"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -315,18 +315,19 @@ def passes(st):
     return st not in (ALIAS, BAD_ARG, NULL_ARG, BAD_SHAPE, BAD_DTYPE, BAD_EPS)
 
 
-def test_norm_args_layout_matches_the_header(tmp_path):
+@pytest.mark.parametrize("cls,cname", [(rn.NormArgs, "norm_args"), (rn.NormBwdArgs, "norm_bwd_args")])
+def test_args_structs_match_the_header(tmp_path, cls, cname):
     import subprocess
-    fields = [f[0] for f in rn.NormArgs._fields_]
+    fields = [f[0] for f in cls._fields_]
     src = tmp_path / "layout.c"
     src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "mi355norm.h"\nint main(void){\n'
-                   'printf("%zu", sizeof(norm_args));\n'
-                   + "".join(f'printf(" %zu", offsetof(norm_args, {f}));\n' for f in fields)
+                   f'printf("%zu", sizeof({cname}));\n'
+                   + "".join(f'printf(" %zu", offsetof({cname}, {f}));\n' for f in fields)
                    + "return 0;}\n")
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-I", os.path.join(os.path.dirname(HEADER)), str(src), "-o", str(exe)], check=True)
     got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
-    want = [ctypes.sizeof(rn.NormArgs)] + [getattr(rn.NormArgs, f).offset for f in fields]
+    want = [ctypes.sizeof(cls)] + [getattr(cls, f).offset for f in fields]
     assert got == want
 
 
@@ -460,3 +461,30 @@ def test_bwd_grid_override(monkeypatch):
     monkeypatch.setenv("MI355NORM_TILE", "1024x8")       # 64 bf16 elements per lane: not instantiated
     with pytest.raises(RuntimeError):
         rn.norm_bwd_describe("rms", 16384, 8192, "bf16")
+
+
+def nbwd(op="ln", dy=A, x=2 * A, dx=5 * A, mean=3 * A, rstd=4 * A, M=4, N=64, **kw):
+    return rn.norm_bwd(op, "bf16", M, N, dy, x, dx, mean=mean if op == "ln" else kw.pop("mean_rms", None),
+                       rstd=rstd, **kw)
+
+
+def test_bwd_strides_are_validated():
+    assert rn._lib.norm_bwd(None, None) == NULL_ARG
+    assert nbwd(ld_dy=63) == BAD_SHAPE                       # stride below N
+    assert nbwd(ld_dx=1 << 62) == BAD_SHAPE                  # matrix beyond 2^63 bytes
+    assert nbwd(op=7) == BAD_ARG
+    assert nbwd(op="add_rms") == BAD_ARG
+    assert nbwd(op="rms", mean_rms=3 * A) == BAD_ARG         # RMSNorm takes no mean
+    assert nbwd(M=0, dy=None, x=None, dx=None, mean=None, rstd=None) == OK
+    # interleaved rows of dy and dx share no byte: accepted (nothing launches at M = 0)
+    assert nbwd(M=0, ld_dy=128, ld_dx=128, dx=A + 128) == OK
+    # dx over dy with another stride: rejected; with the same pointer and stride: accepted
+    assert nbwd(ld_dy=128, ld_dx=64, dx=A) == ALIAS
+    assert nbwd(ld_dy=128, ld_dx=128, dx=A, M=0) == OK
+    # rows of dx running into x
+    assert nbwd(ld_dx=64, dx=2 * A - 64 * 2 * 2) == ALIAS
+
+
+def test_bwd_strided_plans_need_aligned_rows():
+    assert "epv=8" in rn.norm_bwd_describe("ln", 64, 1024, "bf16", True)
+    assert "epv=1" in rn.norm_bwd_describe("ln", 64, 1024, "bf16", False)

@@ -211,3 +211,57 @@ def test_autograd_functions(dtype):
         scale = np.abs(ref[0]).max(1, keepdims=True)
         tol = 1e-4 * scale + (0 if dtype == "f32" else parity.ulp_of(np.abs(ref[0]) + 1e-4 * scale, dtype))
         assert np.all(np.abs(got - ref[0]) <= tol), op
+
+
+@pytest.mark.parametrize("dtype,N,lddy,ldx,lddx,offset", [
+    ("bf16", 4096, 4096 + 64, 4096 + 8, 4096 + 128, 0),      # 16-byte aligned rows
+    ("bf16", 4096, 4096 + 3, 4096, 4096 + 5, 0),             # unaligned strides: element-wise path
+    ("f32", 1000, 1000 + 4, 1000 + 12, 1000 + 36, 0),
+    ("f16", 7, 16, 24, 8, 1),
+    ("bf16", 16384, 16384 + 64, 16384 + 64, 16384 + 8, 0),
+])
+@pytest.mark.parametrize("op", ["ln", "rms"])
+def test_backward_strided_rows(op, dtype, N, lddy, ldx, lddx, offset):
+    M = 9
+    dy, x, g, mean, rstd = inputs(op, dtype, M, N, N + 61)
+    print(f"[bwd] strided {op} {dtype} N={N} ld={lddy},{ldx},{lddx} offset={offset}", flush=True)
+    dx, dg, db = gpu_runner.run_bwd_strided(op, dtype, dy, x, g, mean, rstd, lddy=lddy, ldx=ldx, lddx=lddx,
+                                            offset=offset)
+    aligned = offset == 0 and all((v * E[dtype]) % 16 == 0 for v in (N, lddy, ldx, lddx))
+    parity.check_bwd(op, dtype, dy, x, g, mean, rstd, dx, dg, db, plan(op, M, N, dtype, aligned),
+                     what=f"strided {op}")
+
+
+@pytest.mark.parametrize("which", ["dy", "x"])
+def test_backward_strided_in_place(which):
+    M, N = 6, 2048
+    dy, x, g, mean, rstd = inputs("ln", "bf16", M, N, 71)
+    dx, dg, db = gpu_runner.run_bwd_strided("ln", "bf16", dy, x, g, mean, rstd, lddy=N + 64, ldx=N + 128,
+                                            lddx=0, inplace=which)
+    parity.check_bwd("ln", "bf16", dy, x, g, mean, rstd, dx, dg, db, plan("ln", M, N, "bf16"), what="in place")
+
+
+def test_backward_tensor_api_takes_strided_rows():
+    """layer_norm_backward / rms_norm_backward on column slices of wider
+    tensors give the same bits as on contiguous copies."""
+    M, N = 8, 1024
+    for op in ("ln", "rms"):
+        dy, x, g, mean, rstd = inputs(op, "bf16", M, N, 81)
+        wide_x = torch.zeros(M, 2 * N, dtype=torch.bfloat16, device="cuda")
+        wide_dy = torch.zeros(M, 3 * N, dtype=torch.bfloat16, device="cuda")
+        wide_x[:, N:] = gpu_runner.to_device(x, "bf16").view(M, N)
+        wide_dy[:, :N] = gpu_runner.to_device(dy, "bf16").view(M, N)
+        xs, dys = wide_x[:, N:], wide_dy[:, :N]
+        assert not xs.is_contiguous() and not dys.is_contiguous()
+        gt = gpu_runner.to_device(g, "bf16")
+        rt = torch.from_numpy(rstd).cuda()
+        if op == "ln":
+            mt = torch.from_numpy(mean).cuda()
+            a = rn.layer_norm_backward(dys, xs, mt, rt, gt)
+            b = rn.layer_norm_backward(dys.contiguous(), xs.contiguous(), mt, rt, gt)
+        else:
+            a = rn.rms_norm_backward(dys, xs, rt, gt) + (None,)
+            b = rn.rms_norm_backward(dys.contiguous(), xs.contiguous(), rt, gt) + (None,)
+        for u, v in zip(a, b):
+            assert (u is None and v is None) or torch.equal(u.view(torch.int16) if u.dtype == torch.bfloat16 else u,
+                                                            v.view(torch.int16) if v.dtype == torch.bfloat16 else v)
