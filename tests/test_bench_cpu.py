@@ -56,6 +56,8 @@ def test_cpu_baseline_counts_the_rows_it_ran():
     cb = bench.cpu_baseline(w, inp, seconds=5.0)
     assert cb["kind"] == "oracle" and cb["cores"] == 1 and cb["unit"] == "GB/s"
     assert cb["sample"].startswith("64 of 64 rows") and cb["value"] > 0
+    mt = bench.cpu_baseline(w, inp, seconds=5.0, threads=4)
+    assert mt["cores"] == 4 and mt["sample"].startswith("64 of 64 rows") and "4 threads" in mt["sample"]
 
 
 def test_cpu_baseline_of_the_backward():
