@@ -264,6 +264,9 @@ CONFIGS = {
     "rms_bwd_bf16_16384x8192": Workload(
         "rms_bwd_bf16_16384x8192", "rms_bwd", "bf16", 16384, 8192, 1e-6, 1009,
         "x~U(-1,1), weight~U(0,1), dy~N(0,1); rstd from the forward; RMSNorm backward"),
+    "ln_bwd_bf16_4096x32768": Workload(
+        "ln_bwd_bf16_4096x32768", "ln_bwd", "bf16", 4096, 32768, 1e-5, 1010,
+        "x~N(0,1), gamma~U(0.5,1.5), dy~N(0,1); LayerNorm backward on the longest rows it takes"),
 }
 
 
