@@ -635,3 +635,30 @@ def test_tensor_api_matches_abi():
     torch.cuda.synchronize()
     y3, _, r3 = run("rms", "bf16", inp["x"], inp["gamma"], None, 1e-6)
     assert np.array_equal(gpu_runner.to_host(yr.reshape(42, 768), "bf16"), y3)
+
+
+@pytest.mark.parametrize("op,dtype,offset", [("ln", "f32", 0), ("rms", "bf16", 1)])
+def test_maximum_row_length(op, dtype, offset):
+    """N = 2^24, the largest row the ABI takes, on the split path (aligned
+    and element-wise)."""
+    M, N = 2, 1 << 24
+    print(f"[gpu] maximum N {op} {dtype} offset={offset}", flush=True)
+    inp = inputs(op, dtype, M, N, seed=24)
+    y, mean, rstd = run(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, offset=offset)
+    compare(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, y, mean, rstd, what="N = 2^24")
+
+
+@pytest.mark.parametrize("dtype,N", [("bf16", 1000), ("f32", 8192), ("bf16", 24)])
+@pytest.mark.parametrize("op", ["ln", "rms"])
+def test_grid_stride_over_row_groups(monkeypatch, op, dtype, N):
+    """A grid far smaller than the row groups (each workgroup walks many):
+    the same bits as the one-group-per-workgroup launch, and the oracle's
+    values."""
+    M = 1001
+    inp = inputs(op, dtype, M, N, seed=N + 31)
+    y0, m0, r0 = run(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5)
+    monkeypatch.setenv("MI355NORM_GRID", "7")
+    print(f"[gpu] grid 7 {op} {dtype} M={M} N={N}", flush=True)
+    y, mean, rstd = run(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5)
+    assert np.array_equal(y.view(np.uint8), y0.view(np.uint8)) and np.array_equal(rstd, r0)
+    compare(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, y, mean, rstd, what="grid 7")
