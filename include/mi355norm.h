@@ -79,6 +79,12 @@
  * call needs it (the only time a call waits for its stream), and kept until
  * the process exits.
  *
+ * Graph capture: calls on the row path launch kernels only.  Calls that use
+ * the workspace (long rows, and the backward below) may be captured into a
+ * HIP graph once a call at least as large has run on the capturing stream
+ * (the workspace then exists, and a capture records kernel launches only:
+ * no allocation, synchronisation or memset).
+ *
  * Errors: arguments are validated on the host before any HIP call; a bad
  * argument returns its status and touches nothing.  A launch failure returns
  * NORM_ERR_HIP.  Execution is asynchronous on `stream`: faults surface at the
