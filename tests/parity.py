@@ -1,7 +1,7 @@
 """GPU-vs-oracle comparison at the stated tolerances.
 
-Tolerances (fixed by the task's target; the readings where it is open are
-marked):
+Tolerances (the stated accuracy target for the forward; the readings where it
+is open are marked):
   fp32 y        max |y_gpu - y_oracle| <= 2e-5
   bf16/fp16 y   within one unit in the last place of the oracle's value
                 rounded to the I/O dtype (round-to-nearest-even), where the
@@ -20,7 +20,7 @@ marked):
                 ulps: reading), at most FP8_TIE_FRAC of all elements; a
                 zero may be coded +0 or -0, a NaN with either sign
 
-Backward (ln_bwd / rms_bwd; reading: the task fixes no tolerance for it, so
+Backward (ln_bwd / rms_bwd; reading: no tolerance is stated for it, so
 the bound is derived from the kernel's fp32 arithmetic, u = 2^-24, on the
 same fp32 mean / rstd the oracle is given):
   dx            |dx_gpu - dx_oracle| <= B + (half an ulp of the I/O dtype at
