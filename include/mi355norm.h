@@ -224,9 +224,12 @@ int norm_fwd(const norm_args *args, void *stream);
  *               Required when M > 0 (NORM_ERR_NULL_ARG otherwise).
  *   dgamma,     fp32 [N] device pointers, or NULL: not computed.  Written
  *   dbeta       (zeros when M == 0); dbeta exists for LayerNorm only.
- *   M, N        M >= 0; 1 <= N <= 32768 when dy, x, gamma and dx are 16-byte
- *               aligned and N * element size is a multiple of 16, N <= 16384
- *               otherwise (longer rows: NORM_ERR_BAD_SHAPE).
+ *   M, N        M >= 0; 1 <= N <= 2^24.  Rows up to 32768 elements (16384
+ *               unless dy, x, gamma and dx rows are 16-byte aligned and N *
+ *               element size is a multiple of 16) are handled one workgroup
+ *               per row; longer ones are split across workgroups in batches of
+ *               rows (three kernels per batch, dy and x read twice, the second
+ *               time mostly from the Infinity Cache).
  *
  * Arithmetic is fp32; dx is rounded to `dtype` (round-to-nearest-even).
  * dgamma and dbeta are summed in a fixed order (per-workgroup partial rows,
@@ -293,9 +296,9 @@ int norm_describe(int op, int64_t M, int64_t N, int dtype, int aligned,
                   char *buf, int buflen);
 
 /*
- * As norm_describe, for ln_bwd (rms = 0) or rms_bwd (rms = 1): lanes per
- * row, vectors per lane, workgroup size, grid (= partial rows of dgamma and
- * dbeta).  Returns NORM_ERR_BAD_SHAPE for rows the backward cannot hold.
+ * As norm_describe, for ln_bwd (rms = 0) or rms_bwd (rms = 1): path ("bwd"
+ * or "bwd_split"), lanes per row, vectors per lane, workgroup size, grid and
+ * the number of partial rows of dgamma and dbeta.
  */
 int norm_bwd_describe(int rms, int64_t M, int64_t N, int dtype, int aligned,
                       char *buf, int buflen);

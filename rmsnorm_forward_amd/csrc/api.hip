@@ -30,6 +30,7 @@
 //                                       force the path (rows only if it fits;
 //                                       splitcoop only if a row fits resident)
 //   MI355NORM_SPLIT_BATCH = <bytes>     bytes of x per two-kernel split batch
+//                                       (of dy and x in the split backward)
 //   MI355NORM_TILE = <team>x<vpl>       force the row-kernel tile
 //   MI355NORM_GRID = <n>                cap the number of workgroups
 //   MI355NORM_SPIN_LIMIT = <n>          bound of the single-pass split's wait
@@ -524,9 +525,13 @@ int device_cus() {
 // A row kernel tile for the backward: one 16-byte vector per lane (eight
 // elements unaligned) as long as a team of 1024 lanes covers the row, more
 // beyond, at most kBwdMaxElems elements per lane; teams of 8..1024 lanes in
-// workgroups of 1024.  Rows longer than 1024 x kBwdMaxElems (16384 when
-// unaligned) are NORM_ERR_BAD_SHAPE.  Measured (LN bf16 16384 x 8192, one
-// workgroup per CU): 1024 x 1 145.5 us, 512 x 2 151.5.  cus = 0 asks the
+// workgroups of 1024.  Measured (LN bf16 16384 x 8192, one workgroup per
+// CU): 1024 x 1 145.5 us, 512 x 2 151.5.  Rows longer than 1024 x
+// kBwdMaxElems (16384 when unaligned), or any row with MI355NORM_PATH=split,
+// take the split backward: chunk sums over kBwdSplitWG x kBwdSplitSumsVPL
+// vectors, dx over chunks of kBwdSplitWG x kBwdSplitApplyVPL vectors in a
+// grid of (chunk, row group) with about two workgroups per CU, batches of
+// rows whose dy and x hold about kBwdSplitBatchBytes.  cus = 0 asks the
 // device.
 int make_bwd_plan(int64_t M, int64_t N, int dtype, bool aligned, const Overrides& o, int cus, Plan* p) {
     const int e = elem_bytes(dtype);
@@ -544,7 +549,24 @@ int make_bwd_plan(int64_t M, int64_t N, int dtype, bool aligned, const Overrides
         team = std::max(team, kBwdMinTeam);
         team = std::min(team, kMaxTeam);
         vpl = round_vpl((NV + team - 1) / team);
-        if (vpl < 0 || !bwd_tile_ok(team, vpl, p->epv)) return NORM_ERR_BAD_SHAPE;
+        if (o.path == PATH_SPLIT || vpl < 0 || !bwd_tile_ok(team, vpl, p->epv)) {
+            const int64_t ncu = cus > 0 ? cus : device_cus();
+            const int64_t sv = int64_t(kBwdSplitWG) * kBwdSplitSumsVPL;
+            const int64_t av = int64_t(kBwdSplitWG) * kBwdSplitApplyVPL;
+            p->path = PATH_SPLIT;
+            p->wg = kBwdSplitWG;
+            p->vpl = kBwdSplitApplyVPL;
+            p->chunks = (int)((NV + sv - 1) / sv);
+            p->apply_chunks = (int)((NV + av - 1) / av);
+            const int64_t rows = o.batch_bytes > 0 ? o.batch_bytes / (2 * N * e) : kBwdSplitBatchBytes / (2 * N * e);
+            p->batch_rows = std::max<int64_t>(1, std::min<int64_t>(M, rows));
+            const int64_t gc = (2 * ncu + p->apply_chunks - 1) / p->apply_chunks;
+            p->teams = (int)std::max<int64_t>(1, std::min<int64_t>(gc, p->batch_rows));
+            p->work = p->batch_rows * p->chunks;
+            p->grid = std::min<int64_t>(p->work, o.grid > 0 ? o.grid : kMaxGrid);
+            p->apply_grid = int64_t(p->apply_chunks) * p->teams;
+            return NORM_OK;
+        }
     }
     p->path = PATH_ROWS;
     p->team = team;
@@ -585,6 +607,51 @@ int validate_bwd(const BwdArgs& a) {
     return NORM_OK;
 }
 
+// The split backward: batches of rows in stream order, then the column sums.
+// Workspace: the batch's chunk sums, its row sums, then the partial rows of
+// dgamma and dbeta (p.teams rows of N each), which every batch adds to.
+int run_bwd_split(const BwdArgs& a, const Plan& p, hipStream_t s) {
+    const int64_t M = a.M, N = a.N;
+    const int e = elem_bytes(a.dtype);
+    const size_t part_elems = size_t(p.batch_rows) * size_t(p.chunks);
+    const size_t cols = size_t(p.teams) * size_t(N);
+    const int ncol = (a.dgamma ? 1 : 0) + (a.dbeta ? 1 : 0);
+    Workspace w;
+    if (!stream_workspace(s, 0, (part_elems + size_t(p.batch_rows)) * sizeof(float2) + cols * ncol * sizeof(float),
+                          &w))
+        return NORM_ERR_HIP;
+    float2* part = w.part;
+    float2* rows = part + part_elems;
+    float* colbase = reinterpret_cast<float*>(rows + p.batch_rows);
+    float* pg = a.dgamma ? colbase : nullptr;
+    float* pb = a.dbeta ? colbase + (a.dgamma ? cols : 0) : nullptr;
+    const int op = a.rms ? OP_RMS : OP_LN;
+    hipError_t err = hipSuccess;
+    int64_t b = 0;
+    for (int64_t r0 = 0; r0 < M && err == hipSuccess; r0 += p.batch_rows, ++b) {
+        const int64_t mb = std::min(p.batch_rows, M - r0);
+        BwdCall c{static_cast<const char*>(a.dy) + r0 * a.lddy * e, static_cast<const char*>(a.x) + r0 * a.ldx * e,
+                  a.gamma, a.mean ? a.mean + r0 : nullptr, a.rstd + r0, static_cast<char*>(a.dx) + r0 * a.lddx * e,
+                  pg, pb, mb, (int)N, a.lddy, a.ldx, a.lddx, s};
+        Plan pb_ = p;
+        pb_.teams = (int)std::min<int64_t>(p.teams, mb);
+        // a shorter last batch uses fewer row groups: the partial rows it
+        // does not reach keep what the earlier batches put there
+        switch (a.dtype) {
+        case NORM_F32: err = launch_bwd_split_f32(op, c, pb_, part, rows, b > 0); break;
+        case NORM_BF16: err = launch_bwd_split_bf16(op, c, pb_, part, rows, b > 0); break;
+        default: err = launch_bwd_split_f16(op, c, pb_, part, rows, b > 0); break;
+        }
+    }
+    if (!hip_ok(err, "split backward launch")) return NORM_ERR_HIP;
+    if ((a.dgamma || a.dbeta) &&
+        !hip_ok(launch_colsum(pg ? pg : pb, pg ? a.dgamma : a.dbeta, pg ? pb : nullptr, pg ? a.dbeta : nullptr,
+                              M > 0 ? p.teams : 0, (int)N, s),   // zeros when M = 0
+                "column-sum launch"))
+        return NORM_ERR_HIP;
+    return NORM_OK;
+}
+
 int run_bwd(const BwdArgs& a, void* stream) {
     int st = validate_bwd(a);
     if (st != NORM_OK) return st;
@@ -594,6 +661,7 @@ int run_bwd(const BwdArgs& a, void* stream) {
     st = make_bwd_plan(M, N, a.dtype, bwd_vector_aligned(a), read_overrides(), 0, &p);
     if (st != NORM_OK) return st;
     const hipStream_t s = (hipStream_t)stream;
+    if (p.path == PATH_SPLIT) return run_bwd_split(a, p, s);
     float* pg = nullptr;
     float* pb = nullptr;
     const int64_t P = p.grid;   // partial rows: one per workgroup
@@ -700,7 +768,13 @@ int norm_bwd_describe(int rms, int64_t M, int64_t N, int dtype, int aligned, cha
     Plan p;
     int st = make_bwd_plan(M, N, dtype, aligned && (N * e) % 16 == 0, read_overrides(), 0, &p);
     if (st != NORM_OK) return st;
-    if (buf && buflen > 0)
+    if (buf && buflen > 0 && p.path == PATH_SPLIT)
+        std::snprintf(buf, (size_t)buflen,
+                      "path=bwd_split op=%s wg=%d sums_vpl=%d apply_vpl=%d epv=%d chunks=%d apply_chunks=%d "
+                      "batch_rows=%lld grid=%lld apply_grid=%lld partial_rows=%d",
+                      rms ? "rms" : "ln", p.wg, kBwdSplitSumsVPL, p.vpl, p.epv, p.chunks, p.apply_chunks,
+                      (long long)p.batch_rows, (long long)p.grid, (long long)p.apply_grid, p.teams);
+    else if (buf && buflen > 0)
         std::snprintf(buf, (size_t)buflen,
                       "path=bwd op=%s team=%d vpl=%d epv=%d wg=%d rows_per_wg=%d grid=%lld work=%lld "
                       "partial_rows=%lld",
@@ -714,8 +788,7 @@ const char* norm_status_str(int status) {
     case NORM_OK: return "ok";
     case NORM_ERR_NULL_ARG: return "x or y is NULL";
     case NORM_ERR_BAD_SHAPE:
-        return "bad shape: need M >= 0, 1 <= N <= 2^24 (backward: N <= 32768, 16384 unless 16-byte aligned) "
-               "and M*N*elem within int64";
+        return "bad shape: need M >= 0, 1 <= N <= 2^24 and M*N*elem within int64";
     case NORM_ERR_BAD_DTYPE: return "unknown dtype (0 = f32, 1 = f16, 2 = bf16)";
     case NORM_ERR_BAD_EPS: return "eps must be finite and >= 0";
     case NORM_ERR_BAD_ARG: return "bad argument: misaligned pointer, beta/mean given to an RMSNorm, a bad FP8 scale, or an unusable override";

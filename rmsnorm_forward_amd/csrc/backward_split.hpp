@@ -1,0 +1,248 @@
+// backward_split.hpp -- LayerNorm / RMSNorm backward for rows too long for
+// one workgroup ("CUDA 算子工程" ch. 7, section 7.7: the same formulas as
+// backward.hpp, the row sums taken over chunks of the row).
+//
+// Per batch of rows (sized so that the batch's dy and x stay in the 256 MB
+// Infinity Cache between the first and the last kernel), three kernels:
+//
+//   norm_bwd_split_sums_kernel    one workgroup per (row, chunk of 256 lanes x
+//                                 8 vectors): reads the chunk of dy and x
+//                                 through the caches and stores the chunk's
+//                                 (sum g, sum g xhat) -- (0, sum g x) for
+//                                 RMSNorm -- to part[row * S + chunk].
+//   norm_bwd_split_rowsum_kernel  one wavefront per row: the row's S chunk
+//                                 sums added in chunk order (lane l takes
+//                                 chunks l, l + 64, ...; then the wavefront
+//                                 butterfly), one float2 per row.
+//   norm_bwd_split_apply_kernel   a persistent grid of (column chunk of 256
+//                                 lanes x VPL vectors, row group) workgroups:
+//                                 each walks its rows (prefetching the next
+//                                 row's dy, x, statistics and row sums), writes
+//                                 dx and accumulates dgamma / dbeta for its
+//                                 columns in registers, then adds them into
+//                                 partial row `group` of part_g / part_b
+//                                 (stored by the first batch, added to by the
+//                                 later ones; every slot belongs to one
+//                                 workgroup per batch).
+//
+// The column sums of the partial rows follow (norm_colsum_kernel), so
+// dgamma and dbeta are summed in a fixed order throughout.
+#pragma once
+
+#include "prims.hpp"
+#include "split.hpp"
+
+namespace mi355norm {
+
+template <class T, bool RMS, int WG, int VPL, int EPV>
+__global__ __launch_bounds__(WG)
+void norm_bwd_split_sums_kernel(const typename T::storage* __restrict__ dy,
+                                const typename T::storage* __restrict__ x,
+                                const typename T::storage* __restrict__ gamma,
+                                const float* __restrict__ mean,
+                                const float* __restrict__ rstd,
+                                float2* __restrict__ part,
+                                int64_t M, int N, int64_t ldy, int64_t ldx, int S)
+{
+    using V = Vec<T, EPV>;
+    constexpr int CV = WG * VPL;   // vectors per chunk
+    __shared__ float red[2][WG / 64];
+    const int NV = N / EPV;
+    const int64_t items = M * (int64_t)S;
+    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+        const int64_t row = it / S;
+        const int c = (int)(it - row * S);
+        const typename T::storage* dyr = dy + row * ldy;
+        const typename T::storage* xr = x + row * ldx;
+        V dv[VPL], xv[VPL];
+        bool ok[VPL];
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+            const unsigned v = (unsigned)(c * CV + j * WG) + threadIdx.x;
+            ok[j] = (int)v < NV;
+            if (ok[j]) {          // cached: the apply kernel reads them again soon
+                dv[j].load(dyr + v * EPV);
+                xv[j].load(xr + v * EPV);
+            }
+        }
+        const float m = RMS ? 0.0f : mean[row];
+        const float r = rstd[row];
+        float s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+            if (!ok[j]) continue;
+            const unsigned off = ((unsigned)(c * CV + j * WG) + threadIdx.x) * EPV;
+            V gv;
+            if (gamma != nullptr) gv.load(gamma + off);
+#pragma unroll
+            for (int k = 0; k < EPV; ++k) {
+                const float g = dv[j].get(k) * (gamma != nullptr ? gv.get(k) : 1.0f);
+                const float xh = RMS ? xv[j].get(k) : (xv[j].get(k) - m) * r;
+                if constexpr (!RMS) s1 += g;
+                s2 = __builtin_fmaf(g, xh, s2);
+            }
+        }
+        // two exchanges on two slot sets: the second's barrier orders every
+        // read of the first set before the next item writes it
+        s1 = wg_sum<WG>(s1, red[0]);
+        s2 = wg_sum<WG>(s2, red[1]);
+        if (threadIdx.x == 0) part[row * S + c] = make_float2(s1, s2);
+    }
+}
+
+// rows[r] = sum over c of part[r * S + c], in chunk order per lane, then the
+// wavefront butterfly; one wavefront per row, W rows per workgroup.
+template <int W>
+__global__ __launch_bounds__(64 * W)
+void norm_bwd_split_rowsum_kernel(const float2* __restrict__ part, float2* __restrict__ rows, int64_t M, int S)
+{
+    const int64_t row = (int64_t)blockIdx.x * W + (threadIdx.x >> 6);
+    if (row >= M) return;            // the same for the whole wavefront
+    float a = 0.0f, b = 0.0f;
+    for (int c = lane_id(); c < S; c += 64) {
+        const float2 v = part[row * S + c];
+        a += v.x;
+        b += v.y;
+    }
+    a = team_sum<64>(a);
+    b = team_sum<64>(b);
+    if (lane_id() == 0) rows[row] = make_float2(a, b);
+}
+
+template <class T, bool RMS, int WG, int VPL, int EPV>
+__global__ __launch_bounds__(WG)
+void norm_bwd_split_apply_kernel(const typename T::storage* dy,      // dx may be written over dy or x
+                                 const typename T::storage* x,
+                                 const typename T::storage* __restrict__ gamma,
+                                 const float* __restrict__ mean,
+                                 const float* __restrict__ rstd,
+                                 const float2* __restrict__ rows,    // [M] row sums
+                                 typename T::storage* dx,
+                                 float* __restrict__ part_g,         // [gridDim.x / A, N] or null
+                                 float* __restrict__ part_b,         // [gridDim.x / A, N] or null
+                                 int accumulate,                     // add into the partial rows
+                                 int64_t M, int N, int64_t ldy, int64_t ldx, int64_t lddx, int A)
+{
+    using V = Vec<T, EPV>;
+    using S = typename T::storage;
+    constexpr int CV = WG * VPL;
+    const int c = (int)(blockIdx.x % (unsigned)A);         // column chunk
+    const int64_t grp = blockIdx.x / (unsigned)A;           // row group
+    const int64_t groups = gridDim.x / (unsigned)A;
+    const int NV = N / EPV;
+    const float inv_n = 1.0f / (float)N;
+
+    bool col_ok[VPL];
+    V gam[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+        const unsigned v = (unsigned)(c * CV + j * WG) + threadIdx.x;
+        col_ok[j] = (int)v < NV;
+        if (gamma != nullptr && col_ok[j]) {
+            gam[j].load(gamma + v * EPV);
+        } else {
+            float one[EPV];
+#pragma unroll
+            for (int k = 0; k < EPV; ++k) one[k] = 1.0f;
+            gam[j].set(one);
+        }
+    }
+    float acc_g[VPL][EPV], acc_b[RMS ? 1 : VPL][EPV];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j)
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) {
+            acc_g[j][k] = 0.0f;
+            if constexpr (!RMS) acc_b[j][k] = 0.0f;
+        }
+
+    // a row's loads: its chunk of dy and x, its statistics and its row sums
+    struct Row {
+        V d[VPL], xx[VPL];
+        float m, r;
+        float2 s;
+    };
+    auto fetch = [&](int64_t row, Row& q) {
+        if (row >= M) return;
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+            const unsigned v = (unsigned)(c * CV + j * WG) + threadIdx.x;
+            if (col_ok[j]) {          // nontemporal: the last read of dy and x
+                q.d[j].load_stream(dy + row * ldy + v * EPV);
+                q.xx[j].load_stream(x + row * ldx + v * EPV);
+            }
+        }
+        q.m = RMS ? 0.0f : mean[row];
+        q.r = rstd[row];
+        q.s = rows[row];
+    };
+    // wait for a row's loads (see the row kernel: a wait placed after a
+    // store would wait for the store too)
+    auto ready = [&](Row& q) {
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+            q.d[j].opaque();
+            q.xx[j].opaque();
+        }
+        asm volatile("" : "+v"(q.m), "+v"(q.r), "+v"(q.s.x), "+v"(q.s.y));
+    };
+    auto work = [&](int64_t row, Row& q, Row& next) {
+        const float c1 = q.s.x * inv_n;
+        const float c2 = RMS ? q.r * q.r * q.r * (q.s.y * inv_n) : q.s.y * inv_n;
+        V out[VPL];
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+            if (!col_ok[j]) continue;
+            float o[EPV];
+#pragma unroll
+            for (int k = 0; k < EPV; ++k) {
+                const float dk = q.d[j].get(k);
+                const float g = dk * gam[j].get(k);
+                if constexpr (RMS) {
+                    const float xk = q.xx[j].get(k);
+                    o[k] = __builtin_fmaf(q.r, g, -xk * c2);
+                    acc_g[j][k] = __builtin_fmaf(dk, xk * q.r, acc_g[j][k]);
+                } else {
+                    const float xh = (q.xx[j].get(k) - q.m) * q.r;
+                    o[k] = q.r * ((g - c1) - xh * c2);
+                    acc_g[j][k] = __builtin_fmaf(dk, xh, acc_g[j][k]);
+                    acc_b[j][k] += dk;
+                }
+            }
+            out[j].set(o);
+        }
+        ready(next);
+        S* dxr = dx + row * lddx;
+#pragma unroll
+        for (int j = 0; j < VPL; ++j)
+            if (col_ok[j]) out[j].put_stream(dxr + ((unsigned)(c * CV + j * WG) + threadIdx.x) * EPV);
+    };
+    Row qa, qb;
+    fetch(grp, qa);
+    ready(qa);
+    for (int64_t row = grp; row < M;) {
+        fetch(row + groups, qb);
+        work(row, qa, qb);
+        row += groups;
+        if (row >= M) break;
+        fetch(row + groups, qa);
+        work(row, qb, qa);
+        row += groups;
+    }
+
+    // this workgroup's columns of partial row `grp`
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+        if (!col_ok[j]) continue;
+        const int64_t base = grp * (int64_t)N + ((int64_t)(c * CV + j * WG) + threadIdx.x) * EPV;
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) {
+            if (part_g != nullptr) part_g[base + k] = accumulate ? part_g[base + k] + acc_g[j][k] : acc_g[j][k];
+            if constexpr (!RMS)
+                if (part_b != nullptr)
+                    part_b[base + k] = accumulate ? part_b[base + k] + acc_b[j][k] : acc_b[j][k];
+        }
+    }
+}
+
+}  // namespace mi355norm

@@ -75,8 +75,16 @@ constexpr int kVpls[] = {1, 2, 4, 8, 16};
 constexpr int kMaxTeam = 1024;
 constexpr int kMaxVpl = 16;
 // backward: at most this many elements per lane (dy, x and two column
-// accumulators live in registers); teams of 8 lanes and up
+// accumulators live in registers); teams of 8 lanes and up; longer rows take
+// the split backward
 constexpr int kBwdMaxElems = 32;
+// split backward: chunk sums over 256 lanes x 8 vectors, dx and the column
+// accumulators over 256 lanes x 2 vectors; batches of rows whose dy and x
+// together hold about this many bytes
+constexpr int kBwdSplitWG = 256;
+constexpr int kBwdSplitSumsVPL = 8;
+constexpr int kBwdSplitApplyVPL = 2;
+constexpr int64_t kBwdSplitBatchBytes = int64_t(256) << 20;
 constexpr int kBwdMinTeam = 8;
 // backward workgroups: always 1024 lanes (16 wavefronts fill a CU's wave
 // slots at up to 128 VGPRs), 1024 / team rows at once
@@ -138,6 +146,12 @@ hipError_t launch_split_coop_f16(int op, const NormCall& c, const Plan& p, float
 hipError_t launch_bwd_f32(int op, const BwdCall& c, const Plan& p);
 hipError_t launch_bwd_bf16(int op, const BwdCall& c, const Plan& p);
 hipError_t launch_bwd_f16(int op, const BwdCall& c, const Plan& p);
+// split backward for one batch of c.M rows: chunk sums into part
+// ([M, p.chunks]), row sums into rows ([M]), then dx and the column partials
+// (p.teams rows of N, added to the existing ones when accumulate is set)
+hipError_t launch_bwd_split_f32(int op, const BwdCall& c, const Plan& p, float2* part, float2* rows, int accumulate);
+hipError_t launch_bwd_split_bf16(int op, const BwdCall& c, const Plan& p, float2* part, float2* rows, int accumulate);
+hipError_t launch_bwd_split_f16(int op, const BwdCall& c, const Plan& p, float2* part, float2* rows, int accumulate);
 // out_*[c] = sum of the P partial rows part_* of column c (fixed order), for
 // dgamma and (out_b not null) dbeta in one launch
 hipError_t launch_colsum(const float* part_g, float* out_g, const float* part_b, float* out_b, int64_t P, int N,

@@ -18,4 +18,7 @@ int coop_blocks_per_cu_bf16(int op, int epv) {
 hipError_t launch_bwd_bf16(int op, const BwdCall& c, const Plan& p) {
     return detail::launch_bwd<BF16>(op, c, p);
 }
+hipError_t launch_bwd_split_bf16(int op, const BwdCall& c, const Plan& p, float2* part, float2* rows, int accumulate) {
+    return detail::launch_bwd_split<BF16>(op, c, p, part, rows, accumulate);
+}
 }  // namespace mi355norm

@@ -19,6 +19,9 @@ int coop_blocks_per_cu_f32(int op, int epv) {
 hipError_t launch_bwd_f32(int op, const BwdCall& c, const Plan& p) {
     return detail::launch_bwd<F32>(op, c, p);
 }
+hipError_t launch_bwd_split_f32(int op, const BwdCall& c, const Plan& p, float2* part, float2* rows, int accumulate) {
+    return detail::launch_bwd_split<F32>(op, c, p, part, rows, accumulate);
+}
 hipError_t launch_colsum(const float* part_g, float* out_g, const float* part_b, float* out_b, int64_t P, int N,
                          hipStream_t stream) {
     const dim3 grid((unsigned)((N + 63) / 64), out_b ? 2u : 1u);

@@ -3,7 +3,10 @@
 // separate translation units in parallel.
 #pragma once
 
+#include <algorithm>
+
 #include "backward.hpp"
+#include "backward_split.hpp"
 #include "dispatch.hpp"
 #include "rows.hpp"
 #include "split.hpp"
@@ -270,6 +273,52 @@ hipError_t launch_bwd(int op, const BwdCall& c, const Plan& p) {
     return with_epv<T>(p.epv, [&](auto epv) {
         constexpr int E = decltype(epv)::value;
         return op == OP_RMS ? bwd_by_team<T, true, E>(c, p) : bwd_by_team<T, false, E>(c, p);
+    });
+}
+
+template <class T, bool RMS, int EPV>
+hipError_t go_bwd_split(const BwdCall& c, const Plan& p, float2* part, float2* rows, int accumulate) {
+    const St<T>* dy = static_cast<const St<T>*>(c.dy);
+    const St<T>* x = static_cast<const St<T>*>(c.x);
+    const St<T>* g = static_cast<const St<T>*>(c.gamma);
+    const float* mean = c.mean;
+    const float* rstd = c.rstd;
+    St<T>* dx = static_cast<St<T>*>(c.dx);
+    float* pg = c.part_g;
+    float* pb = c.part_b;
+    int64_t M = c.M;
+    int N = c.N;
+    int64_t ldy = c.ldy, ldx = c.ldx, lddx = c.lddx;
+    int S = p.chunks, A = p.apply_chunks;
+    const float2* pc = part;
+    const float2* rc = rows;
+    {
+        void* args[] = {&dy, &x, &g, &mean, &rstd, &part, &M, &N, &ldy, &ldx, &S};
+        const int64_t grid = std::min<int64_t>(p.grid, M * S);
+        hipError_t e = hipLaunchKernel(
+            reinterpret_cast<const void*>(&norm_bwd_split_sums_kernel<T, RMS, kBwdSplitWG, kBwdSplitSumsVPL, EPV>),
+            dim3((unsigned)grid), dim3(kBwdSplitWG), args, 0, c.stream);
+        if (e != hipSuccess) return e;
+    }
+    {
+        void* args[] = {&pc, &rows, &M, &S};
+        hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&norm_bwd_split_rowsum_kernel<4>),
+                                       dim3((unsigned)((M + 3) / 4)), dim3(256), args, 0, c.stream);
+        if (e != hipSuccess) return e;
+    }
+    void* args[] = {&dy, &x, &g, &mean, &rstd, &rc, &dx, &pg, &pb, &accumulate, &M, &N, &ldy, &ldx, &lddx, &A};
+    return hipLaunchKernel(
+        reinterpret_cast<const void*>(&norm_bwd_split_apply_kernel<T, RMS, kBwdSplitWG, kBwdSplitApplyVPL, EPV>),
+        dim3((unsigned)(int64_t(A) * p.teams)), dim3(kBwdSplitWG), args, 0, c.stream);
+}
+
+template <class T>
+hipError_t launch_bwd_split(int op, const BwdCall& c, const Plan& p, float2* part, float2* rows, int accumulate) {
+    if (op != OP_LN && op != OP_RMS) return hipErrorInvalidValue;
+    return with_epv<T>(p.epv, [&](auto epv) {
+        constexpr int E = decltype(epv)::value;
+        return op == OP_RMS ? go_bwd_split<T, true, E>(c, p, part, rows, accumulate)
+                            : go_bwd_split<T, false, E>(c, p, part, rows, accumulate);
     });
 }
 

@@ -163,6 +163,12 @@ U32 = 2.0 ** -24
 
 def bwd_chain(plan: dict, M: int) -> int:
     """Longest chain of fp32 additions behind one dgamma / dbeta column."""
+    if plan.get("path") == "bwd_split":
+        # each partial row adds its rows of every batch in turn, then the
+        # column sums add the partial rows (16 wavefronts, then their sum)
+        P, B = plan["partial_rows"], plan["batch_rows"]
+        batches = -(-M // B) if M else 0
+        return batches * (-(-B // P) + 1) + -(-P // 16) + 16
     rows_per_team = -(-plan["work"] // plan["grid"]) if plan["grid"] else 0
     return rows_per_team + plan["rows_per_wg"] + -(-plan["grid"] // 16) + 16
 

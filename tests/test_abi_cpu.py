@@ -382,7 +382,6 @@ def test_bwd_validation():
     assert ln_bwd(M=-1) == BAD_SHAPE
     assert ln_bwd(N=0) == BAD_SHAPE
     assert ln_bwd(N=(1 << 24) + 1) == BAD_SHAPE
-    assert ln_bwd(N=32768 + 8) == BAD_SHAPE            # longer than the backward's tile
     assert ln_bwd(dy=None) == NULL_ARG
     assert ln_bwd(x=None) == NULL_ARG
     assert ln_bwd(dx=None) == NULL_ARG
@@ -412,16 +411,29 @@ def test_bwd_empty_needs_no_pointers():
     assert rms_bwd(dy=None, x=None, rstd=None, dx=None, M=0) == OK
 
 
-@pytest.mark.parametrize("N,dtype,aligned,ok", [(32768, "bf16", True, True), (32776, "bf16", True, False),
-                                                (32768, "f32", True, True), (16384, "bf16", False, True),
-                                                (16385, "f16", False, False), (1, "f32", False, True)])
-def test_bwd_row_limit(N, dtype, aligned, ok):
+@pytest.mark.parametrize("N,dtype,aligned,rows", [(32768, "bf16", True, True), (32776, "bf16", True, False),
+                                                  (32768, "f32", True, True), (16384, "bf16", False, True),
+                                                  (16385, "f16", False, False), (1, "f32", False, True),
+                                                  (1 << 24, "bf16", True, False)])
+def test_bwd_row_kernel_limit_then_split(N, dtype, aligned, rows):
     for op in ("ln", "rms"):
-        if ok:
-            assert rn.norm_bwd_describe(op, 1024, N, dtype, aligned).startswith("path=bwd")
-        else:
-            with pytest.raises(RuntimeError, match="bad shape"):
-                rn.norm_bwd_describe(op, 1024, N, dtype, aligned)
+        want = "path=bwd " if rows else "path=bwd_split "
+        assert rn.norm_bwd_describe(op, 1024, N, dtype, aligned).startswith(want)
+    with pytest.raises(RuntimeError, match="bad shape"):
+        rn.norm_bwd_describe("ln", 1024, (1 << 24) + 1, dtype, aligned)
+
+
+def test_bwd_split_plans():
+    d = dict(kv.split("=") for kv in rn.norm_bwd_describe("ln", 64, 1 << 20, "bf16", True).split())
+    # chunk sums over 256 x 8 vectors, dx over 256 x 2, about two workgroups per CU (256 here)
+    assert d["chunks"] == "64" and d["apply_chunks"] == "256" and d["apply_vpl"] == "2"
+    assert d["batch_rows"] == "64" and d["partial_rows"] == "2" and d["apply_grid"] == "512"
+    d = dict(kv.split("=") for kv in rn.norm_bwd_describe("rms", 100000, 40000, "f32", True).split())
+    # dy and x of one batch hold about 256 MiB
+    assert int(d["batch_rows"]) == (256 << 20) // (2 * 40000 * 4)
+    assert int(d["partial_rows"]) == -(-512 // int(d["apply_chunks"]))
+    d = dict(kv.split("=") for kv in rn.norm_bwd_describe("ln", 3, 1 << 24, "f16", False).split())
+    assert d["epv"] == "1" and int(d["partial_rows"]) == 1 and d["batch_rows"] == "3"
 
 
 def _bwd_plan(op, M, N, dtype, aligned=True):
@@ -447,6 +459,14 @@ def test_bwd_every_row_fits_its_tile(dtype, aligned):
         assert p["grid"] == min(p["work"], 256) == p["partial_rows"]      # one workgroup per CU
         if aligned and p["team"] * epv < N:
             assert p["team"] == 1024                    # more than one vector per lane only past 1024 lanes
+
+
+def test_bwd_split_on_request(monkeypatch):
+    monkeypatch.setenv("MI355NORM_PATH", "split")
+    assert rn.norm_bwd_describe("ln", 4096, 8192, "bf16").startswith("path=bwd_split ")
+    monkeypatch.setenv("MI355NORM_SPLIT_BATCH", str(1 << 20))
+    d = dict(kv.split("=") for kv in rn.norm_bwd_describe("ln", 4096, 8192, "bf16").split())
+    assert d["batch_rows"] == str((1 << 20) // (2 * 8192 * 2))
 
 
 def test_bwd_grid_override(monkeypatch):
