@@ -227,14 +227,16 @@ int norm_fwd(const norm_args *args, void *stream);
  *   M, N        M >= 0; 1 <= N <= 2^24.  Rows up to 32768 elements (16384
  *               unless dy, x, gamma and dx rows are 16-byte aligned and N *
  *               element size is a multiple of 16) are handled one workgroup
- *               per row; longer ones are split across workgroups in batches of
- *               rows (three kernels per batch, dy and x read twice, the second
- *               time mostly from the Infinity Cache).
+ *               per row (fp32 rows longer than 16384 for RMSNorm and 24576
+ *               for LayerNorm excepted); longer ones are split across
+ *               workgroups: chunk sums, row sums, then dx and the column
+ *               sums' partial rows (three kernels; dy and x read twice).
  *
  * Arithmetic is fp32; dx is rounded to `dtype` (round-to-nearest-even).
  * dgamma and dbeta are summed in a fixed order (per-workgroup partial rows,
  * then a column sum over them), so repeated calls on one device give the
- * same bits.  The partial rows (fp32 [grid, N] each) live in a workspace the
+ * same bits.  The partial rows (fp32 [grid, N] each; with the split rows
+ * also 8 bytes per row per 2048-vector chunk and 8 per row) live in a workspace the
  * library keeps per (device, stream), grown when a call needs more; growing
  * waits for the stream.  Calls run asynchronously on `stream`.  Returns a
  * norm_status.

@@ -527,13 +527,18 @@ int device_cus() {
 // beyond, at most kBwdMaxElems elements per lane; teams of 8..1024 lanes in
 // workgroups of 1024.  Measured (LN bf16 16384 x 8192, one workgroup per
 // CU): 1024 x 1 145.5 us, 512 x 2 151.5.  Rows longer than 1024 x
-// kBwdMaxElems (16384 when unaligned), or any row with MI355NORM_PATH=split,
+// kBwdMaxElems (16384 when unaligned), fp32 rows that would need
+// kBwdMaxElems elements per lane (RMSNorm; LayerNorm past
+// kBwdF32RowsMaxLnVectors vectors), or any row with MI355NORM_PATH=split,
 // take the split backward: chunk sums over kBwdSplitWG x kBwdSplitSumsVPL
 // vectors, dx over chunks of kBwdSplitWG x kBwdSplitApplyVPL vectors in a
-// grid of (chunk, row group) with about two workgroups per CU, batches of
-// rows whose dy and x hold about kBwdSplitBatchBytes.  cus = 0 asks the
-// device.
-int make_bwd_plan(int64_t M, int64_t N, int dtype, bool aligned, const Overrides& o, int cus, Plan* p) {
+// grid of (chunk, row group) with about two workgroups per CU, all rows in
+// one batch (measured, LN bf16 2048 x 65536: 244 us in one batch, 263 / 310
+// / 406 us in batches of 256 / 128 / 64 MiB of dy and x; the apply kernel's
+// second read of dy and x is no faster from the Infinity Cache, and every
+// batch costs its launches and tails).  cus = 0 asks the device.
+int make_bwd_plan(int64_t M, int64_t N, int dtype, bool rms, bool aligned, const Overrides& o, int cus,
+                  Plan* p) {
     const int e = elem_bytes(dtype);
     std::memset(p, 0, sizeof *p);
     p->epv = aligned ? 16 / e : 1;
@@ -549,7 +554,9 @@ int make_bwd_plan(int64_t M, int64_t N, int dtype, bool aligned, const Overrides
         team = std::max(team, kBwdMinTeam);
         team = std::min(team, kMaxTeam);
         vpl = round_vpl((NV + team - 1) / team);
-        if (o.path == PATH_SPLIT || vpl < 0 || !bwd_tile_ok(team, vpl, p->epv)) {
+        const bool f32_wide = e == 4 && vpl > 0 && vpl * p->epv == kBwdMaxElems &&
+                              (rms || NV > kBwdF32RowsMaxLnVectors);
+        if (o.path == PATH_SPLIT || vpl < 0 || !bwd_tile_ok(team, vpl, p->epv) || f32_wide) {
             const int64_t ncu = cus > 0 ? cus : device_cus();
             const int64_t sv = int64_t(kBwdSplitWG) * kBwdSplitSumsVPL;
             const int64_t av = int64_t(kBwdSplitWG) * kBwdSplitApplyVPL;
@@ -558,7 +565,7 @@ int make_bwd_plan(int64_t M, int64_t N, int dtype, bool aligned, const Overrides
             p->vpl = kBwdSplitApplyVPL;
             p->chunks = (int)((NV + sv - 1) / sv);
             p->apply_chunks = (int)((NV + av - 1) / av);
-            const int64_t rows = o.batch_bytes > 0 ? o.batch_bytes / (2 * N * e) : kBwdSplitBatchBytes / (2 * N * e);
+            const int64_t rows = o.batch_bytes > 0 ? o.batch_bytes / (2 * N * e) : M;
             p->batch_rows = std::max<int64_t>(1, std::min<int64_t>(M, rows));
             const int64_t gc = (2 * ncu + p->apply_chunks - 1) / p->apply_chunks;
             p->teams = (int)std::max<int64_t>(1, std::min<int64_t>(gc, p->batch_rows));
@@ -614,7 +621,9 @@ int run_bwd_split(const BwdArgs& a, const Plan& p, hipStream_t s) {
     const int64_t M = a.M, N = a.N;
     const int e = elem_bytes(a.dtype);
     const size_t part_elems = size_t(p.batch_rows) * size_t(p.chunks);
-    const size_t cols = size_t(p.teams) * size_t(N);
+    // one row group: its partial rows are dgamma / dbeta themselves
+    const bool direct = p.teams == 1 && M > 0;
+    const size_t cols = direct ? 0 : size_t(p.teams) * size_t(N);
     const int ncol = (a.dgamma ? 1 : 0) + (a.dbeta ? 1 : 0);
     Workspace w;
     if (!stream_workspace(s, 0, (part_elems + size_t(p.batch_rows)) * sizeof(float2) + cols * ncol * sizeof(float),
@@ -623,8 +632,8 @@ int run_bwd_split(const BwdArgs& a, const Plan& p, hipStream_t s) {
     float2* part = w.part;
     float2* rows = part + part_elems;
     float* colbase = reinterpret_cast<float*>(rows + p.batch_rows);
-    float* pg = a.dgamma ? colbase : nullptr;
-    float* pb = a.dbeta ? colbase + (a.dgamma ? cols : 0) : nullptr;
+    float* pg = direct ? a.dgamma : a.dgamma ? colbase : nullptr;
+    float* pb = direct ? a.dbeta : a.dbeta ? colbase + (a.dgamma ? cols : 0) : nullptr;
     const int op = a.rms ? OP_RMS : OP_LN;
     hipError_t err = hipSuccess;
     int64_t b = 0;
@@ -644,7 +653,7 @@ int run_bwd_split(const BwdArgs& a, const Plan& p, hipStream_t s) {
         }
     }
     if (!hip_ok(err, "split backward launch")) return NORM_ERR_HIP;
-    if ((a.dgamma || a.dbeta) &&
+    if ((a.dgamma || a.dbeta) && !direct &&
         !hip_ok(launch_colsum(pg ? pg : pb, pg ? a.dgamma : a.dbeta, pg ? pb : nullptr, pg ? a.dbeta : nullptr,
                               M > 0 ? p.teams : 0, (int)N, s),   // zeros when M = 0
                 "column-sum launch"))
@@ -658,7 +667,7 @@ int run_bwd(const BwdArgs& a, void* stream) {
     const int64_t M = a.M, N = a.N;
     const bool sums = a.dgamma || a.dbeta;
     Plan p;
-    st = make_bwd_plan(M, N, a.dtype, bwd_vector_aligned(a), read_overrides(), 0, &p);
+    st = make_bwd_plan(M, N, a.dtype, a.rms, bwd_vector_aligned(a), read_overrides(), 0, &p);
     if (st != NORM_OK) return st;
     const hipStream_t s = (hipStream_t)stream;
     if (p.path == PATH_SPLIT) return run_bwd_split(a, p, s);
@@ -766,7 +775,7 @@ int norm_bwd_describe(int rms, int64_t M, int64_t N, int dtype, int aligned, cha
     if (M < 0 || N < 1 || N > kMaxN) return NORM_ERR_BAD_SHAPE;
     const int e = elem_bytes(dtype);
     Plan p;
-    int st = make_bwd_plan(M, N, dtype, aligned && (N * e) % 16 == 0, read_overrides(), 0, &p);
+    int st = make_bwd_plan(M, N, dtype, rms != 0, aligned && (N * e) % 16 == 0, read_overrides(), 0, &p);
     if (st != NORM_OK) return st;
     if (buf && buflen > 0 && p.path == PATH_SPLIT)
         std::snprintf(buf, (size_t)buflen,

@@ -78,13 +78,15 @@ constexpr int kMaxVpl = 16;
 // accumulators live in registers); teams of 8 lanes and up; longer rows take
 // the split backward
 constexpr int kBwdMaxElems = 32;
+// fp32 rows that need 32 elements per lane run faster split (RMSNorm from
+// there on, LayerNorm past this many vectors per row)
+constexpr int kBwdF32RowsMaxLnVectors = 6144;
 // split backward: chunk sums over 256 lanes x 8 vectors, dx and the column
-// accumulators over 256 lanes x 2 vectors; batches of rows whose dy and x
-// together hold about this many bytes
+// accumulators over 256 lanes x 2 vectors; all rows in one batch unless
+// MI355NORM_SPLIT_BATCH asks for smaller ones
 constexpr int kBwdSplitWG = 256;
 constexpr int kBwdSplitSumsVPL = 8;
 constexpr int kBwdSplitApplyVPL = 2;
-constexpr int64_t kBwdSplitBatchBytes = int64_t(256) << 20;
 constexpr int kBwdMinTeam = 8;
 // backward workgroups: always 1024 lanes (16 wavefronts fill a CU's wave
 // slots at up to 128 VGPRs), 1024 / team rows at once

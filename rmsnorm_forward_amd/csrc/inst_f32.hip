@@ -24,9 +24,15 @@ hipError_t launch_bwd_split_f32(int op, const BwdCall& c, const Plan& p, float2*
 }
 hipError_t launch_colsum(const float* part_g, float* out_g, const float* part_b, float* out_b, int64_t P, int N,
                          hipStream_t stream) {
+    // wavefronts per 64 columns: as many as the partial rows keep busy
     const dim3 grid((unsigned)((N + 63) / 64), out_b ? 2u : 1u);
-    hipLaunchKernelGGL(norm_colsum_kernel<kColsumWaves>, grid, dim3(64 * kColsumWaves), 0, stream, part_g, out_g,
-                       part_b, out_b, P, N);
+    if (P >= 4 * kColsumWaves)
+        hipLaunchKernelGGL(norm_colsum_kernel<kColsumWaves>, grid, dim3(64 * kColsumWaves), 0, stream, part_g,
+                           out_g, part_b, out_b, P, N);
+    else if (P >= 16)
+        hipLaunchKernelGGL(norm_colsum_kernel<4>, grid, dim3(64 * 4), 0, stream, part_g, out_g, part_b, out_b, P, N);
+    else
+        hipLaunchKernelGGL(norm_colsum_kernel<1>, grid, dim3(64), 0, stream, part_g, out_g, part_b, out_b, P, N);
     return hipGetLastError();
 }
 }  // namespace mi355norm
