@@ -625,13 +625,14 @@ int run_bwd_split(const BwdArgs& a, const Plan& p, hipStream_t s) {
     const bool direct = p.teams == 1 && M > 0;
     const size_t cols = direct ? 0 : size_t(p.teams) * size_t(N);
     const int ncol = (a.dgamma ? 1 : 0) + (a.dbeta ? 1 : 0);
+    // the partial rows start 256-byte aligned (the column sum may read them
+    // as 16-byte vectors)
+    const size_t col_off = ((part_elems + size_t(p.batch_rows)) * sizeof(float2) + 255) & ~size_t(255);
     Workspace w;
-    if (!stream_workspace(s, 0, (part_elems + size_t(p.batch_rows)) * sizeof(float2) + cols * ncol * sizeof(float),
-                          &w))
-        return NORM_ERR_HIP;
+    if (!stream_workspace(s, 0, col_off + cols * ncol * sizeof(float), &w)) return NORM_ERR_HIP;
     float2* part = w.part;
     float2* rows = part + part_elems;
-    float* colbase = reinterpret_cast<float*>(rows + p.batch_rows);
+    float* colbase = reinterpret_cast<float*>(reinterpret_cast<char*>(part) + col_off);
     float* pg = direct ? a.dgamma : a.dgamma ? colbase : nullptr;
     float* pb = direct ? a.dbeta : a.dbeta ? colbase + (a.dgamma ? cols : 0) : nullptr;
     const int op = a.rms ? OP_RMS : OP_LN;

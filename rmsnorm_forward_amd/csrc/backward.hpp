@@ -344,4 +344,39 @@ void norm_colsum_kernel(const float* __restrict__ part_g, float* __restrict__ ou
 }
 constexpr int kColsumWaves = 16;
 
+// The same sums for few partial rows (P < 16): lane t of the grid takes
+// columns 4t .. 4t + 3 (16-byte loads when N is a multiple of 4, else one
+// column per lane) and adds rows 0, 1, ..., P - 1 in order.
+template <bool V4>
+__global__ __launch_bounds__(256)
+void norm_colsum_narrow_kernel(const float* __restrict__ part_g, float* __restrict__ out_g,
+                               const float* __restrict__ part_b, float* __restrict__ out_b, int64_t P, int N)
+{
+    const float* part = blockIdx.y == 0 ? part_g : part_b;
+    float* out = blockIdx.y == 0 ? out_g : out_b;
+    if (out == nullptr) return;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if constexpr (V4) {
+        const int64_t c = t * 4;
+        if (c >= N) return;
+        float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        for (int64_t p = 0; p < P; ++p) {
+            const float4 v = *reinterpret_cast<const float4*>(part + p * N + c);
+            a.x += v.x;
+            a.y += v.y;
+            a.z += v.z;
+            a.w += v.w;
+        }
+        out[c] = a.x;        // out is only 4-byte aligned
+        out[c + 1] = a.y;
+        out[c + 2] = a.z;
+        out[c + 3] = a.w;
+    } else {
+        if (t >= N) return;
+        float a = 0.0f;
+        for (int64_t p = 0; p < P; ++p) a += part[p * N + t];
+        out[t] = a;
+    }
+}
+
 }  // namespace mi355norm

@@ -1,4 +1,5 @@
 // inst_f16.hip -- f16 instantiations of the row, split-row and backward kernels.
+#include "inst_bwd.hpp"
 #include "inst_impl.hpp"
 
 namespace mi355norm {

@@ -1,5 +1,6 @@
 // inst_f32.hip -- f32 instantiations of the row, split-row and backward
 // kernels, and the launch of the (type-free) column-sum kernel.
+#include "inst_bwd.hpp"
 #include "inst_impl.hpp"
 
 namespace mi355norm {
@@ -24,15 +25,24 @@ hipError_t launch_bwd_split_f32(int op, const BwdCall& c, const Plan& p, float2*
 }
 hipError_t launch_colsum(const float* part_g, float* out_g, const float* part_b, float* out_b, int64_t P, int N,
                          hipStream_t stream) {
-    // wavefronts per 64 columns: as many as the partial rows keep busy
-    const dim3 grid((unsigned)((N + 63) / 64), out_b ? 2u : 1u);
-    if (P >= 4 * kColsumWaves)
+    // wavefronts per 64 columns: as many as the partial rows keep busy; few
+    // partial rows: one lane per four columns
+    const unsigned pairs = out_b ? 2u : 1u;
+    const dim3 grid((unsigned)((N + 63) / 64), pairs);
+    if (P >= 4 * kColsumWaves) {
         hipLaunchKernelGGL(norm_colsum_kernel<kColsumWaves>, grid, dim3(64 * kColsumWaves), 0, stream, part_g,
                            out_g, part_b, out_b, P, N);
-    else if (P >= 16)
+    } else if (P >= 16) {
         hipLaunchKernelGGL(norm_colsum_kernel<4>, grid, dim3(64 * 4), 0, stream, part_g, out_g, part_b, out_b, P, N);
-    else
-        hipLaunchKernelGGL(norm_colsum_kernel<1>, grid, dim3(64), 0, stream, part_g, out_g, part_b, out_b, P, N);
+    } else if (N % 4 == 0) {
+        const dim3 g4((unsigned)((N / 4 + 255) / 256), pairs);
+        hipLaunchKernelGGL(norm_colsum_narrow_kernel<true>, g4, dim3(256), 0, stream, part_g, out_g, part_b, out_b,
+                           P, N);
+    } else {
+        const dim3 g1((unsigned)((N + 255) / 256), pairs);
+        hipLaunchKernelGGL(norm_colsum_narrow_kernel<false>, g1, dim3(256), 0, stream, part_g, out_g, part_b, out_b,
+                           P, N);
+    }
     return hipGetLastError();
 }
 }  // namespace mi355norm

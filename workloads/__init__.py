@@ -266,7 +266,10 @@ CONFIGS = {
         "x~U(-1,1), weight~U(0,1), dy~N(0,1); rstd from the forward; RMSNorm backward"),
     "ln_bwd_bf16_4096x32768": Workload(
         "ln_bwd_bf16_4096x32768", "ln_bwd", "bf16", 4096, 32768, 1e-5, 1010,
-        "x~N(0,1), gamma~U(0.5,1.5), dy~N(0,1); LayerNorm backward on the longest rows it takes"),
+        "x~N(0,1), gamma~U(0.5,1.5), dy~N(0,1); LayerNorm backward on the longest rows of the row kernel"),
+    "ln_bwd_bf16_64x1048576": Workload(
+        "ln_bwd_bf16_64x1048576", "ln_bwd", "bf16", 64, 1048576, 1e-5, 1011,
+        "x~N(0,1), gamma~U(0.5,1.5), dy~N(0,1); LayerNorm backward on rows split across workgroups"),
 }
 
 
