@@ -1,6 +1,7 @@
 """Host threads calling the library at once, each on its own stream: the
-split-row forward and the backward (which keep workspaces per device and
-stream) give the same bits as the same calls made one after another."""
+split-row forward and the backward, row kernel and split rows (which keep
+workspaces per device and stream), give the same bits as the same calls made
+one after another."""
 from __future__ import annotations
 
 import threading
@@ -22,13 +23,16 @@ rn = pytest.importorskip("rmsnorm_forward_amd")
 
 
 def job(k):
-    """Inputs of thread k: a split-path LayerNorm (rows of 300000) and a
-    LayerNorm backward (512 x 4096), bf16."""
+    """Inputs of thread k: a split-path LayerNorm (rows of 300000), a
+    LayerNorm backward (512 x 4096) and a split-row LayerNorm backward
+    (3 x 70000), bf16."""
     f = workloads.gen_ln_normal(200 + k, 4, 300000, "bf16")
     b = workloads.gen_bwd(300 + k, 512, 4096, "bf16", "ln_bwd")
+    s = workloads.gen_bwd(400 + k, 3, 70000, "bf16", "ln_bwd")
     dev = lambda a: gpu_runner.to_device(a, "bf16")
     return {"x": dev(f["x"]).view(4, 300000), "g": dev(f["gamma"]), "b": dev(f["beta"]),
-            "bx": dev(b["x"]).view(512, 4096), "bg": dev(b["gamma"]), "dy": dev(b["dy"]).view(512, 4096)}
+            "bx": dev(b["x"]).view(512, 4096), "bg": dev(b["gamma"]), "dy": dev(b["dy"]).view(512, 4096),
+            "sx": dev(s["x"]).view(3, 70000), "sg": dev(s["gamma"]), "sdy": dev(s["dy"]).view(3, 70000)}
 
 
 def run_job(t, stream):
@@ -36,7 +40,9 @@ def run_job(t, stream):
         y, mean, rstd = rn.layer_norm(t["x"], t["g"], t["b"], 1e-5)
         _, bm, br = rn.layer_norm(t["bx"], t["bg"], None, 1e-5)
         dx, dg, db = rn.layer_norm_backward(t["dy"], t["bx"], bm, br, t["bg"])
-    return [y, mean, rstd, dx, dg, db]
+        _, sm, sr = rn.layer_norm(t["sx"], t["sg"], None, 1e-5)
+        sdx, sdg, sdb = rn.layer_norm_backward(t["sdy"], t["sx"], sm, sr, t["sg"])
+    return [y, mean, rstd, dx, dg, db, sdx, sdg, sdb]
 
 
 def bits(ts):

@@ -1,6 +1,6 @@
 """Calls captured into a HIP graph (torch.cuda.CUDAGraph) and replayed.
 
-The row path needs no workspace; the split path and the backward use the
+The row path needs no workspace; the split paths and the backward use the
 per-(device, stream) workspace, which exists once a call has run on the
 capturing stream, so after a warm-up call there a capture records kernel
 launches only (no allocation, no memset nodes).  Every replay, with eager
@@ -27,20 +27,25 @@ def bits(t):
 
 
 def test_capture_and_replay_forward_split_and_backward():
+    """Forward rows, split forward, row-kernel backward and split backward."""
     dev = lambda a: gpu_runner.to_device(a, "bf16")
     f = workloads.gen_ln_normal(401, 256, 4096, "bf16")
     sp = workloads.gen_rms_uniform(402, 3, 200000, "bf16")
     b = workloads.gen_bwd(403, 512, 2048, "bf16", "ln_bwd")
+    lb = workloads.gen_bwd(404, 5, 100000, "bf16", "rms_bwd")    # split backward
     x, g, be = dev(f["x"]).view(256, 4096), dev(f["gamma"]), dev(f["beta"])
     xs, gs = dev(sp["x"]).view(3, 200000), dev(sp["gamma"])
     bx, bg, dy = dev(b["x"]).view(512, 2048), dev(b["gamma"]), dev(b["dy"]).view(512, 2048)
+    lx, lg, ldy = dev(lb["x"]).view(5, 100000), dev(lb["gamma"]), dev(lb["dy"]).view(5, 100000)
 
     def body():
         y, mean, rstd = rn.layer_norm(x, g, be, 1e-5)
         ys, rs = rn.rms_norm(xs, gs, 1e-6)
         _, bm, br = rn.layer_norm(bx, bg, None, 1e-5)
         dx, dg, db = rn.layer_norm_backward(dy, bx, bm, br, bg)
-        return [y, mean, rstd, ys, rs, dx, dg, db]
+        _, lr = rn.rms_norm(lx, lg, 1e-6)
+        ldx, ldg = rn.rms_norm_backward(ldy, lx, lr, lg)
+        return [y, mean, rstd, ys, rs, dx, dg, db, lr, ldx, ldg]
 
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
