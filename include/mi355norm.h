@@ -236,7 +236,7 @@ int norm_fwd(const norm_args *args, void *stream);
  * dgamma and dbeta are summed in a fixed order (per-workgroup partial rows,
  * then a column sum over them), so repeated calls on one device give the
  * same bits.  The partial rows (fp32 [grid, N] each; with the split rows
- * also 8 bytes per row per 2048-vector chunk and 8 per row) live in a workspace the
+ * also 8 bytes per row per 512-vector chunk and 8 per row) live in a workspace the
  * library keeps per (device, stream), grown when a call needs more; growing
  * waits for the stream.  Calls run asynchronously on `stream`.  Returns a
  * norm_status.

@@ -530,8 +530,9 @@ int device_cus() {
 // kBwdMaxElems (16384 when unaligned), fp32 rows that would need
 // kBwdMaxElems elements per lane (RMSNorm; LayerNorm past
 // kBwdF32RowsMaxLnVectors vectors), or any row with MI355NORM_PATH=split,
-// take the split backward: chunk sums over kBwdSplitWG x kBwdSplitSumsVPL
-// vectors, dx over chunks of kBwdSplitWG x kBwdSplitApplyVPL vectors in a
+// take the split backward: chunk sums over kBwdSplitWG x bwd_sums_vpl
+// vectors (measured, 256 x 2 against 256 x 8 / 4, one batch: LN bf16 64 x
+// 2^20 124.6 / 131.0 / 127.8 us, 2048 x 65536 232.4 / 237.7 / 232.3), dx over chunks of kBwdSplitWG x kBwdSplitApplyVPL vectors in a
 // grid of (chunk, row group) with about two workgroups per CU, all rows in
 // one batch (measured, LN bf16 2048 x 65536: 244 us in one batch, 263 / 310
 // / 406 us in batches of 256 / 128 / 64 MiB of dy and x; the apply kernel's
@@ -558,7 +559,7 @@ int make_bwd_plan(int64_t M, int64_t N, int dtype, bool rms, bool aligned, const
                               (rms || NV > kBwdF32RowsMaxLnVectors);
         if (o.path == PATH_SPLIT || vpl < 0 || !bwd_tile_ok(team, vpl, p->epv) || f32_wide) {
             const int64_t ncu = cus > 0 ? cus : device_cus();
-            const int64_t sv = int64_t(kBwdSplitWG) * kBwdSplitSumsVPL;
+            const int64_t sv = int64_t(kBwdSplitWG) * bwd_sums_vpl(p->epv);
             const int64_t av = int64_t(kBwdSplitWG) * kBwdSplitApplyVPL;
             p->path = PATH_SPLIT;
             p->wg = kBwdSplitWG;
@@ -782,7 +783,7 @@ int norm_bwd_describe(int rms, int64_t M, int64_t N, int dtype, int aligned, cha
         std::snprintf(buf, (size_t)buflen,
                       "path=bwd_split op=%s wg=%d sums_vpl=%d apply_vpl=%d epv=%d chunks=%d apply_chunks=%d "
                       "batch_rows=%lld grid=%lld apply_grid=%lld partial_rows=%d",
-                      rms ? "rms" : "ln", p.wg, kBwdSplitSumsVPL, p.vpl, p.epv, p.chunks, p.apply_chunks,
+                      rms ? "rms" : "ln", p.wg, bwd_sums_vpl(p.epv), p.vpl, p.epv, p.chunks, p.apply_chunks,
                       (long long)p.batch_rows, (long long)p.grid, (long long)p.apply_grid, p.teams);
     else if (buf && buflen > 0)
         std::snprintf(buf, (size_t)buflen,

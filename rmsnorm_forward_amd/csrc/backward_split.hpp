@@ -6,13 +6,14 @@
 // Infinity Cache between the first and the last kernel), three kernels:
 //
 //   norm_bwd_split_sums_kernel    one workgroup per (row, chunk of 256 lanes x
-//                                 8 vectors): reads the chunk of dy and x
+//                                 2 vectors): reads the chunk of dy and x
 //                                 through the caches and stores the chunk's
 //                                 (sum g, sum g xhat) -- (0, sum g x) for
 //                                 RMSNorm -- to part[row * S + chunk].
 //   norm_bwd_split_rowsum_kernel  one wavefront per row: the row's S chunk
-//                                 sums added in chunk order (lane l takes
-//                                 chunks l, l + 64, ...; then the wavefront
+//                                 sums added in a fixed order (lane l takes
+//                                 chunks l, l + 64, ... into four
+//                                 accumulators; then the wavefront
 //                                 butterfly), one float2 per row.
 //   norm_bwd_split_apply_kernel   a persistent grid of (column chunk of 256
 //                                 lanes x VPL vectors, row group) workgroups:
@@ -90,23 +91,44 @@ void norm_bwd_split_sums_kernel(const typename T::storage* __restrict__ dy,
     }
 }
 
-// rows[r] = sum over c of part[r * S + c], in chunk order per lane, then the
-// wavefront butterfly; one wavefront per row, W rows per workgroup.
+// rows[r] = sum over c of part[r * S + c]; one wavefront per row, W rows
+// per workgroup.  Lane l takes chunks l, l + 64, l + 128, ... into four
+// accumulators in turn (chunk l + 64 i goes to accumulator i mod 4, so four
+// loads are in flight), adds them as (a0 + a1) + (a2 + a3), then the
+// wavefront butterfly: a fixed order.
 template <int W>
 __global__ __launch_bounds__(64 * W)
 void norm_bwd_split_rowsum_kernel(const float2* __restrict__ part, float2* __restrict__ rows, int64_t M, int S)
 {
     const int64_t row = (int64_t)blockIdx.x * W + (threadIdx.x >> 6);
     if (row >= M) return;            // the same for the whole wavefront
-    float a = 0.0f, b = 0.0f;
-    for (int c = lane_id(); c < S; c += 64) {
-        const float2 v = part[row * S + c];
-        a += v.x;
-        b += v.y;
+    const float2* pr = part + row * S;
+    float2 a[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = make_float2(0.0f, 0.0f);
+    int c = lane_id();
+    for (; c + 192 < S; c += 256) {
+        float2 v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = pr[c + 64 * i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            a[i].x += v[i].x;
+            a[i].y += v[i].y;
+        }
     }
-    a = team_sum<64>(a);
-    b = team_sum<64>(b);
-    if (lane_id() == 0) rows[row] = make_float2(a, b);
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+        if (c + 64 * i < S) {
+            const float2 v = pr[c + 64 * i];
+            a[i].x += v.x;
+            a[i].y += v.y;
+        }
+    float s1 = (a[0].x + a[1].x) + (a[2].x + a[3].x);
+    float s2 = (a[0].y + a[1].y) + (a[2].y + a[3].y);
+    s1 = team_sum<64>(s1);
+    s2 = team_sum<64>(s2);
+    if (lane_id() == 0) rows[row] = make_float2(s1, s2);
 }
 
 template <class T, bool RMS, int WG, int VPL, int EPV>

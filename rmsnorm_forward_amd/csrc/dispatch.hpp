@@ -81,11 +81,13 @@ constexpr int kBwdMaxElems = 32;
 // fp32 rows that need 32 elements per lane run faster split (RMSNorm from
 // there on, LayerNorm past this many vectors per row)
 constexpr int kBwdF32RowsMaxLnVectors = 6144;
-// split backward: chunk sums over 256 lanes x 8 vectors, dx and the column
-// accumulators over 256 lanes x 2 vectors; all rows in one batch unless
-// MI355NORM_SPLIT_BATCH asks for smaller ones
+// split backward: chunk sums over 256 lanes x 2 vectors (x 16 elements when
+// element-wise), dx and the column accumulators over 256 lanes x 2 vectors;
+// all rows in one batch unless MI355NORM_SPLIT_BATCH asks for smaller ones
 constexpr int kBwdSplitWG = 256;
-constexpr int kBwdSplitSumsVPL = 8;
+constexpr int kBwdSplitSumsVPL = 2;
+constexpr int kBwdSplitSumsVPLElem = 16;
+constexpr int bwd_sums_vpl(int epv) { return epv == 1 ? kBwdSplitSumsVPLElem : kBwdSplitSumsVPL; }
 constexpr int kBwdSplitApplyVPL = 2;
 constexpr int kBwdMinTeam = 8;
 // backward workgroups: always 1024 lanes (16 wavefronts fill a CU's wave

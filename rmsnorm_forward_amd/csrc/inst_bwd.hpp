@@ -94,7 +94,7 @@ hipError_t go_bwd_split(const BwdCall& c, const Plan& p, float2* part, float2* r
         void* args[] = {&dy, &x, &g, &mean, &rstd, &part, &M, &N, &ldy, &ldx, &S};
         const int64_t grid = std::min<int64_t>(p.grid, M * S);
         hipError_t e = hipLaunchKernel(
-            reinterpret_cast<const void*>(&norm_bwd_split_sums_kernel<T, RMS, kBwdSplitWG, kBwdSplitSumsVPL, EPV>),
+            reinterpret_cast<const void*>(&norm_bwd_split_sums_kernel<T, RMS, kBwdSplitWG, bwd_sums_vpl(EPV), EPV>),
             dim3((unsigned)grid), dim3(kBwdSplitWG), args, 0, c.stream);
         if (e != hipSuccess) return e;
     }

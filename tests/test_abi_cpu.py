@@ -429,8 +429,8 @@ def test_bwd_row_kernel_limit_then_split(N, dtype, aligned, ln_rows, rms_rows):
 
 def test_bwd_split_plans():
     d = dict(kv.split("=") for kv in rn.norm_bwd_describe("ln", 64, 1 << 20, "bf16", True).split())
-    # chunk sums over 256 x 8 vectors, dx over 256 x 2, about two workgroups per CU (256 here)
-    assert d["chunks"] == "64" and d["apply_chunks"] == "256" and d["apply_vpl"] == "2"
+    # chunk sums over 256 x 2 vectors, dx over 256 x 2, about two workgroups per CU (256 here)
+    assert d["chunks"] == "256" and d["apply_chunks"] == "256" and d["apply_vpl"] == "2" and d["sums_vpl"] == "2"
     assert d["batch_rows"] == "64" and d["partial_rows"] == "2" and d["apply_grid"] == "512"
     d = dict(kv.split("=") for kv in rn.norm_bwd_describe("rms", 100000, 40000, "f32", True).split())
     # every row in one batch
