@@ -91,18 +91,9 @@ void norm_bwd_split_sums_kernel(const typename T::storage* __restrict__ dy,
     }
 }
 
-// rows[r] = sum over c of part[r * S + c]; one wavefront per row, W rows
-// per workgroup.  Lane l takes chunks l, l + 64, l + 128, ... into four
-// accumulators in turn (chunk l + 64 i goes to accumulator i mod 4, so four
-// loads are in flight), adds them as (a0 + a1) + (a2 + a3), then the
-// wavefront butterfly: a fixed order.
-template <int W>
-__global__ __launch_bounds__(64 * W)
-void norm_bwd_split_rowsum_kernel(const float2* __restrict__ part, float2* __restrict__ rows, int64_t M, int S)
+// One row's chunk sums pr[0 .. S), summed by one wavefront into *out.
+__device__ __forceinline__ void rowsum_one(const float2* __restrict__ pr, float2* __restrict__ out, int S)
 {
-    const int64_t row = (int64_t)blockIdx.x * W + (threadIdx.x >> 6);
-    if (row >= M) return;            // the same for the whole wavefront
-    const float2* pr = part + row * S;
     float2 a[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[i] = make_float2(0.0f, 0.0f);
@@ -128,7 +119,20 @@ void norm_bwd_split_rowsum_kernel(const float2* __restrict__ part, float2* __res
     float s2 = (a[0].y + a[1].y) + (a[2].y + a[3].y);
     s1 = team_sum<64>(s1);
     s2 = team_sum<64>(s2);
-    if (lane_id() == 0) rows[row] = make_float2(s1, s2);
+    if (lane_id() == 0) *out = make_float2(s1, s2);
+}
+
+// rows[r] = sum over c of part[r * S + c]; one wavefront per row, W rows
+// per workgroup, rows grid-strided.  Lane l takes chunks l, l + 64,
+// l + 128, ... into four accumulators in turn (chunk l + 64 i goes to
+// accumulator i mod 4, so four loads are in flight), adds them as
+// (a0 + a1) + (a2 + a3), then the wavefront butterfly: a fixed order.
+template <int W>
+__global__ __launch_bounds__(64 * W)
+void norm_bwd_split_rowsum_kernel(const float2* __restrict__ part, float2* __restrict__ rows, int64_t M, int S)
+{
+    for (int64_t row = (int64_t)blockIdx.x * W + (threadIdx.x >> 6); row < M; row += (int64_t)gridDim.x * W)
+        rowsum_one(part + row * S, rows + row, S);   // the row is the same for the whole wavefront
 }
 
 template <class T, bool RMS, int WG, int VPL, int EPV>

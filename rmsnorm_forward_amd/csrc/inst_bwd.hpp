@@ -100,8 +100,9 @@ hipError_t go_bwd_split(const BwdCall& c, const Plan& p, float2* part, float2* r
     }
     {
         void* args[] = {&pc, &rows, &M, &S};
+        const int64_t grid = std::min<int64_t>((M + 3) / 4, int64_t(1) << 20);   // rows grid-strided
         hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&norm_bwd_split_rowsum_kernel<4>),
-                                       dim3((unsigned)((M + 3) / 4)), dim3(256), args, 0, c.stream);
+                                       dim3((unsigned)grid), dim3(256), args, 0, c.stream);
         if (e != hipSuccess) return e;
     }
     void* args[] = {&dy, &x, &g, &mean, &rstd, &rc, &dx, &pg, &pb, &accumulate, &M, &N, &ldy, &ldx, &lddx, &A};

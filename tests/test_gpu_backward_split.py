@@ -79,6 +79,13 @@ def test_split_backward_batches(monkeypatch, op, M, batch_rows):
     go(op, "bf16", M, N, seed=M + batch_rows)
 
 
+def test_split_backward_more_rows_than_the_row_sum_grid(monkeypatch):
+    """More than 2^22 rows: the row-sum kernel's grid (2^20 workgroups of
+    four wavefronts) walks the rows grid-strided."""
+    monkeypatch.setenv("MI355NORM_PATH", "split")
+    go("ln", "f32", (1 << 22) + 1000, 2, seed=99)
+
+
 @pytest.mark.parametrize("grid", [1, 3, 1000])
 def test_split_backward_forced_sums_grid(monkeypatch, grid):
     """The chunk-sum kernel's grid far below its work items (rows x chunks):
