@@ -134,6 +134,8 @@ void norm_bwd_rows_kernel(const typename T::storage* dy,      // dx may be writt
     // One row group: the two row sums, dx, and the column accumulators.
     // d, xx, m, r hold the group's loads; par picks the LDS exchange slots
     // (consecutive groups alternate, so one barrier per group suffices).
+    // before_stores runs once dx is computed (d and xx are dead then),
+    // before dx is stored.
     auto row_group = [&](int64_t grp, V (&d)[VPL], V (&xx)[VPL], float m, float r, int par,
                          auto&& before_stores) {
         const int64_t row = grp * G::ROWS + team;
@@ -254,11 +256,12 @@ void norm_bwd_rows_kernel(const typename T::storage* dy,      // dx may be writt
             grp += stride;
         }
     } else {
+        // one register set: the next group's loads go into it once this
+        // group's dx is computed, before its stores (measured, bf16
+        // 4096 x 32768: LayerNorm 222 -> 215 us, RMSNorm 156 -> 150 us)
         int par = 0;
-        for (int64_t grp = blockIdx.x; grp < groups; grp += stride, par ^= 1) {
-            row_group(grp, dA, xA, mA, rA, par, [] {});
-            fetch(grp + stride, dA, xA, mA, rA);
-        }
+        for (int64_t grp = blockIdx.x; grp < groups; grp += stride, par ^= 1)
+            row_group(grp, dA, xA, mA, rA, par, [&] { fetch(grp + stride, dA, xA, mA, rA); });
     }
 
     // One partial row per workgroup.  Teams own the same columns lane for
