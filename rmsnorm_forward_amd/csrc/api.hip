@@ -17,8 +17,13 @@
 //               batch of rows holding about 256 MiB of x: partials (x read
 //               through the caches), then merge + normalise (x re-read,
 //               mostly from the Infinity Cache).  A single pass (cooperative
-//               launch, per-row barrier, x read once) is available on request;
-//               it measured slower (LN bf16 64 x 2^20: 92 us vs 72 us).
+//               launch, per-row barrier, x read once, each workgroup loading
+//               its next row's chunk while it waits) is available on
+//               request: faster for large RMSNorm inputs (bf16 256 x 2^20
+//               209 us vs 240, fp32 256 x 2^20 367 vs 478), slower for
+//               LayerNorm bf16 (64 x 2^20: 93 vs 66), and its per-row wait
+//               depends on all of a row's workgroups running at once, which
+//               the two-kernel form does not.
 // Measured on MI355X in steady state (200 back-to-back launches): bf16
 // 1024-wide RMSNorm 32x4 (2 rows per wavefront) 85.3 us vs 64x2 87.1, 16x8
 // 95.1; bf16 2048-wide 64x4 87.6 vs 32x8 99.4; fp32 2048-wide 256x2 175.0

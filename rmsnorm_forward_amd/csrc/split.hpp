@@ -24,11 +24,11 @@
 //                            (all S workgroups of a team are co-resident:
 //                            cooperative launch), merges and normalises from
 //                            registers.  Teams walk the rows with a stride of
-//                            the team count.  The barrier's counters return
-//                            to zero by the end of every launch, so a kept
-//                            workspace needs no reset.  Waiting workgroups
-//                            issue no loads, which makes it the slower of
-//                            the two on MI355X.
+//                            the team count, each workgroup loading its
+//                            next row's chunk while it waits and normalises.
+//                            The barrier's counters return to zero by the
+//                            end of every launch, so a kept workspace needs
+//                            no reset.
 #pragma once
 
 #include "prims.hpp"
@@ -291,26 +291,29 @@ void norm_split_coop_kernel(const typename T::storage* x,
     const int team = blockIdx.x / S;          // grid is exactly teams * S
     const int c = blockIdx.x - team * S;
 
-    for (int64_t row = team; row < M; row += teams) {
-        const typename T::storage* xr = x + row * ld.x;
-        C ch;
-        ch.load(xr, c, NV);
-        if constexpr (ADD) ch.template add_residual<true>(res + row * ld.r, hout + row * ld.h);
-        const float K = RMS ? 0.0f : T::widen(xr[0]);
+    // One row's chunk: partial, publish, wait, merge, normalise.  during_wait
+    // runs between the publication and the wait (the next row's loads go
+    // there), before_stores once the statistics are known, before y is
+    // stored.
+    auto finish = [&](C& ch, float K, int64_t row, auto&& during_wait, auto&& before_stores) {
         const float2 p = ch.template partial<RMS>(K, NV, red);
-        // one 256-byte line per row: rows in flight never share a line
+        // one 256-byte line of counters per row: rows in flight never share one
         unsigned* arrived = sync + row * 64;
         unsigned* departed = arrived + 32;
         if (tid == 0) {
-            // publish the partial before the arrival count, then wait for the
-            // row's other S-1 workgroups.  Polling uses relaxed loads.  The
-            // wait is bounded so a broken co-residency assumption cannot hang.
+            // publish the partial before the arrival count
             store_partial_coherent(part + row * S + c, p);
             __builtin_amdgcn_s_waitcnt(0);     // the store has completed
             __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        during_wait();
+        if (tid == 0) {
+            // wait for the row's other S-1 workgroups.  Polling uses relaxed
+            // loads.  The wait is bounded so a broken co-residency assumption
+            // cannot hang; need = S (a host test hook can ask for S + 1,
+            // which never comes).
             unsigned spins = 0;
             int timed_out = 0;
-            // need = S (a host test hook can ask for S + 1, which never comes)
             while (__hip_atomic_load(arrived, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
                 if (++spins > spin_limit) {
                     timed_out = 1;
@@ -336,7 +339,48 @@ void norm_split_coop_kernel(const typename T::storage* x,
             if (!RMS && mean_out) mean_out[row] = K + st.x;
             if (rstd_out) rstd_out[row] = st.y;
         }
+        before_stores();
         ch.template apply<RMS, Q8>(row_out<T, Q8>(y, row, ld.y), gamma, beta, K, st.x, st.y, qinv);
+    };
+
+    if constexpr (ADD) {
+        for (int64_t row = team; row < M; row += teams) {
+            const typename T::storage* xr = x + row * ld.x;
+            C ch;
+            ch.load(xr, c, NV);
+            ch.template add_residual<true>(res + row * ld.r, hout + row * ld.h);
+            finish(ch, 0.0f, row, [] {}, [] {});   // RMSNorm only: no shift
+        }
+    } else {
+        // the next row's chunk is loaded while this row waits at its barrier
+        // and is normalised: two chunk register sets, the loop unrolled by
+        // two so that no copy between them forces an early wait.  Loads and
+        // stores share one completion counter, so the next chunk's loads are
+        // waited for (ready) before this chunk's stores are issued; the merge
+        // of the row's partials, whose loads come after them, waits for them
+        // anyway.  (The residual add keeps one set: its chunk is added and
+        // stored as soon as it arrives.)
+        C ca, cb;
+        float Ka = 0.0f, Kb = 0.0f;
+        auto fetch = [&](C& ch, float& K, int64_t row) {
+            if (row >= M) return;
+            const typename T::storage* xr = x + row * ld.x;
+            ch.load(xr, c, NV);
+            K = RMS ? 0.0f : T::widen(xr[0]);
+        };
+        auto ready = [&](C& ch, float& K) {
+            ch.opaque();
+            asm volatile("" : "+v"(K));
+        };
+        fetch(ca, Ka, team);
+        ready(ca, Ka);
+        for (int64_t row = team; row < M;) {
+            finish(ca, Ka, row, [&] { fetch(cb, Kb, row + teams); }, [&] { ready(cb, Kb); });
+            row += teams;
+            if (row >= M) break;
+            finish(cb, Kb, row, [&] { fetch(ca, Ka, row + teams); }, [&] { ready(ca, Ka); });
+            row += teams;
+        }
     }
 }
 
