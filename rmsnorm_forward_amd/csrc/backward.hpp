@@ -78,6 +78,12 @@ void norm_bwd_rows_kernel(const typename T::storage* dy,      // dx may be writt
     // slower (154 -> 170 us), so RMSNorm keeps it in registers.
     constexpr int E = VPL * EPV;
     constexpr bool LACC = !RMS && (E > 16 || (EPV == 1 && E > 8));
+    // With at most 8 elements per lane, g and xhat (RMSNorm: x) stay in fp32
+    // registers across the exchange and the column sums are taken in the
+    // first pass, so the second pass only forms dx (LN bf16 16384 x 8192:
+    // 148.8 -> 147.9 us, 65536 x 2048: 137.6 -> 135.8; at 16 elements per
+    // lane the copies spill: 167 -> 184 us).  Longer lanes re-widen dy and x.
+    constexpr bool KEEP = !LACC && E <= 8;
 
     // gamma of this lane's columns (ones without gamma), kept packed for
     // every row
@@ -147,24 +153,38 @@ void norm_bwd_rows_kernel(const typename T::storage* dy,      // dx may be writt
 
         // the row sums: (sum g, sum g xhat) for LayerNorm, (0, sum g x) for RMSNorm
         float s1 = 0.0f, s2 = 0.0f;
+        float gk[KEEP ? VPL : 1][KEEP ? EPV : 1], hk[KEEP ? VPL : 1][KEEP ? EPV : 1];
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
             if (!ok[j]) continue;
             const V gj = gam_at(j);
 #pragma unroll
             for (int k = 0; k < EPV; ++k) {
-                const float g = d[j].get(k) * gj.get(k);
+                const float dk = d[j].get(k);
+                const float g = dk * gj.get(k);
                 const float xh = RMS ? xx[j].get(k) : (xx[j].get(k) - m) * r;
                 if constexpr (!RMS) s1 += g;
                 s2 = __builtin_fmaf(g, xh, s2);
+                if constexpr (KEEP) {
+                    gk[j][k] = g;
+                    hk[j][k] = xh;
+                    if constexpr (RMS) {
+                        acc_g[j][k] = __builtin_fmaf(dk, xh * r, acc_g[j][k]);
+                    } else {
+                        acc_g[j][k] = __builtin_fmaf(dk, xh, acc_g[j][k]);
+                        acc_b[j][k] += dk;
+                    }
+                }
             }
         }
-        // re-widen dy and x after the exchange rather than keep fp32 copies
-        // live across it
+        if constexpr (!KEEP) {
+            // re-widen dy and x after the exchange rather than keep fp32
+            // copies live across it
 #pragma unroll
-        for (int j = 0; j < VPL; ++j) {
-            d[j].opaque();
-            xx[j].opaque();
+            for (int j = 0; j < VPL; ++j) {
+                d[j].opaque();
+                xx[j].opaque();
+            }
         }
         if constexpr (!RMS) s1 = team_sum<(TEAM < 64 ? TEAM : 64)>(s1);
         s2 = team_sum<(TEAM < 64 ? TEAM : 64)>(s2);
@@ -192,6 +212,11 @@ void norm_bwd_rows_kernel(const typename T::storage* dy,      // dx may be writt
             float o[EPV];
 #pragma unroll
             for (int k = 0; k < EPV; ++k) {
+                if constexpr (KEEP) {
+                    if constexpr (RMS) o[k] = __builtin_fmaf(r, gk[j][k], -hk[j][k] * c2);
+                    else o[k] = r * ((gk[j][k] - c1) - hk[j][k] * c2);
+                    continue;
+                }
                 const float dk = d[j].get(k);
                 const float g = dk * gj.get(k);
                 if constexpr (RMS) {
