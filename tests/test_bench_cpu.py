@@ -66,3 +66,30 @@ def test_cpu_baseline_of_the_backward():
     cb = bench.cpu_baseline(w, inp, seconds=5.0)
     assert cb["sample"].startswith("32 of 32 rows") and "oracle.ln_bwd" in cb["sample"] and cb["value"] > 0
     assert w.ideal_bytes() == 3 * 32 * 512 * 2 + 512 * 2 + 512 * 8 + 32 * 8
+
+
+def test_launches_per_step_follow_the_plan(monkeypatch):
+    """Launch counts of one call, read from the library's own plan strings."""
+    import rmsnorm_forward_amd as rn
+    N = 1 << 20
+    assert bench.launches_per_step(rn.norm_describe("ln", 16384, 8192, "bf16"), 16384) == 1
+    assert bench.launches_per_step(rn.norm_describe("ln", 64, N, "bf16"), 64) == 2
+    monkeypatch.setenv("MI355NORM_PATH", "splitcoop")
+    try:
+        coop = rn.norm_describe("ln", 64, N, "bf16")
+    except RuntimeError:          # no device here: the single pass cannot be planned
+        coop = None
+    if coop is not None:
+        assert bench.launches_per_step(coop, 64) == 1
+    monkeypatch.delenv("MI355NORM_PATH")
+    monkeypatch.setenv("MI355NORM_SPLIT_BATCH", str(3 * N * 2))   # forward: 3 rows of x per batch
+    assert bench.launches_per_step(rn.norm_describe("ln", 7, N, "bf16"), 7) == 6
+    assert bench.launches_per_step(rn.norm_bwd_describe("ln", 16384, 8192, "bf16"), 16384) == 2
+    monkeypatch.setenv("MI355NORM_SPLIT_BATCH", str(3 * 2 * N * 2))   # backward: 3 rows of dy and x
+    p = rn.norm_bwd_describe("ln", 64, N, "bf16")
+    assert "batch_rows=3" in p and "partial_rows=2" in p
+    assert bench.launches_per_step(p, 64) == 3 * 22 + 1       # sums, row sums, apply per batch; column sums
+    monkeypatch.delenv("MI355NORM_SPLIT_BATCH")
+    assert bench.launches_per_step(rn.norm_bwd_describe("ln", 64, N, "bf16"), 64) == 4
+    p = rn.norm_bwd_describe("rms", 8, 1 << 24, "bf16")
+    assert "partial_rows=1" in p and bench.launches_per_step(p, 8) == 3   # one row group: no column sums
