@@ -33,7 +33,10 @@
 // Test/benchmark hooks (environment, read per call):
 //   MI355NORM_PATH = rows | split | split2 | splitcoop
 //                                       force the path (rows only if it fits;
-//                                       splitcoop only if a row fits resident)
+//                                       splitcoop only if a row fits resident;
+//                                       for the backward, split and split2
+//                                       take the three-kernel split, splitcoop
+//                                       its single cooperative pass)
 //   MI355NORM_SPLIT_BATCH = <bytes>     bytes of x per two-kernel split batch
 //                                       (of dy and x in the split backward)
 //   MI355NORM_TILE = <team>x<vpl>       force the row-kernel tile
@@ -218,33 +221,41 @@ bool tile_instantiated(int team, int vpl) {
     return t && v;
 }
 
-// How many workgroups of the single-pass split kernel the current device can
-// hold at once (0 if cooperative launch is unavailable or no device is
-// present).  Cached per (device, dtype, op, vector width).
-int64_t coop_capacity(int dtype, int op, int epv) {
+// How many workgroups of the single-pass split kernel (bwd: of the single-
+// pass split backward) the current device can hold at once (0 if cooperative
+// launch is unavailable or no device is present).  Cached per (device, dtype,
+// op, vector width, direction).
+int64_t coop_capacity(int dtype, int op, int epv, bool bwd = false) {
     static std::mutex mu;
-    static int64_t cache[64][3][kOps][2];
-    static bool known[64][3][kOps][2];
+    static int64_t cache[64][3][kOps][2][2];
+    static bool known[64][3][kOps][2][2];
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) return 0;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
     const int vi = epv == 1 ? 0 : 1;
+    const int bi = bwd ? 1 : 0;
     std::lock_guard<std::mutex> lock(mu);
-    if (!known[dev][dtype][op][vi]) {
+    if (!known[dev][dtype][op][vi][bi]) {
         int coop = 0, cus = 0;
         int64_t cap = 0;
         if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && coop &&
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) {
-            int per_cu = dtype == NORM_F32 ? coop_blocks_per_cu_f32(op, epv)
+            int per_cu;
+            if (bwd)
+                per_cu = dtype == NORM_F32 ? bwd_coop_blocks_per_cu_f32(op, epv)
+                         : dtype == NORM_BF16 ? bwd_coop_blocks_per_cu_bf16(op, epv)
+                                              : bwd_coop_blocks_per_cu_f16(op, epv);
+            else
+                per_cu = dtype == NORM_F32 ? coop_blocks_per_cu_f32(op, epv)
                          : dtype == NORM_BF16 ? coop_blocks_per_cu_bf16(op, epv)
                                               : coop_blocks_per_cu_f16(op, epv);
             cap = int64_t(per_cu) * cus;
         }
-        cache[dev][dtype][op][vi] = cap;
-        known[dev][dtype][op][vi] = true;
+        cache[dev][dtype][op][vi][bi] = cap;
+        known[dev][dtype][op][vi][bi] = true;
     }
-    return cache[dev][dtype][op][vi];
+    return cache[dev][dtype][op][vi][bi];
 }
 
 // Returns NORM_OK and fills *p, or NORM_ERR_BAD_ARG if an override cannot run.
@@ -562,6 +573,24 @@ int make_bwd_plan(int64_t M, int64_t N, int dtype, bool rms, bool aligned, const
         vpl = round_vpl((NV + team - 1) / team);
         const bool f32_wide = e == 4 && vpl > 0 && vpl * p->epv == kBwdMaxElems &&
                               (rms || NV > kBwdF32RowsMaxLnVectors);
+        if (o.path == PATH_SPLIT && o.split_mode == SPLIT_COOP) {
+            // one cooperative pass, on request, when every chunk of a row and
+            // at least one row's worth of teams can be resident
+            const int64_t ccv = int64_t(kBwdCoopWG) * kBwdCoopVPL;
+            const int64_t cchunks = (NV + ccv - 1) / ccv;
+            const int64_t cap = coop_capacity(dtype, rms ? OP_RMS : OP_LN, p->epv, true);
+            if (cap < cchunks) return NORM_ERR_BAD_ARG;
+            p->path = PATH_SPLIT;
+            p->split_mode = SPLIT_COOP;
+            p->wg = kBwdCoopWG;
+            p->vpl = kBwdCoopVPL;
+            p->chunks = (int)cchunks;
+            p->teams = (int)std::max<int64_t>(1, std::min<int64_t>(M, cap / cchunks));
+            p->batch_rows = M;
+            p->work = M * p->chunks;
+            p->grid = int64_t(p->teams) * p->chunks;
+            return NORM_OK;
+        }
         if (o.path == PATH_SPLIT || vpl < 0 || !bwd_tile_ok(team, vpl, p->epv) || f32_wide) {
             const int64_t ncu = cus > 0 ? cus : device_cus();
             const int64_t sv = int64_t(kBwdSplitWG) * bwd_sums_vpl(p->epv);
@@ -634,8 +663,10 @@ int run_bwd_split(const BwdArgs& a, const Plan& p, hipStream_t s) {
     // the partial rows start 256-byte aligned (the column sum may read them
     // as 16-byte vectors)
     const size_t col_off = ((part_elems + size_t(p.batch_rows)) * sizeof(float2) + 255) & ~size_t(255);
+    const bool coop = p.split_mode == SPLIT_COOP;
     Workspace w;
-    if (!stream_workspace(s, 0, col_off + cols * ncol * sizeof(float), &w)) return NORM_ERR_HIP;
+    if (!stream_workspace(s, coop ? size_t(M) * kSyncStride : 0, col_off + cols * ncol * sizeof(float), &w))
+        return NORM_ERR_HIP;
     float2* part = w.part;
     float2* rows = part + part_elems;
     float* colbase = reinterpret_cast<float*>(reinterpret_cast<char*>(part) + col_off);
@@ -643,8 +674,21 @@ int run_bwd_split(const BwdArgs& a, const Plan& p, hipStream_t s) {
     float* pb = direct ? a.dbeta : a.dbeta ? colbase + (a.dgamma ? cols : 0) : nullptr;
     const int op = a.rms ? OP_RMS : OP_LN;
     hipError_t err = hipSuccess;
+    if (coop && M > 0) {
+        // every row in one cooperative launch; the row barriers' counters
+        // are zero at the start of every call (see the forward's single pass)
+        const Overrides o = read_overrides();
+        const unsigned need = (unsigned)p.chunks + (o.force_timeout ? 1u : 0u);
+        const unsigned spin = o.force_timeout ? 64u : o.spin_limit;
+        BwdCall c{a.dy, a.x, a.gamma, a.mean, a.rstd, a.dx, pg, pb, M, (int)N, a.lddy, a.ldx, a.lddx, s};
+        switch (a.dtype) {
+        case NORM_F32: err = launch_bwd_coop_f32(op, c, p, part, w.sync, need, spin); break;
+        case NORM_BF16: err = launch_bwd_coop_bf16(op, c, p, part, w.sync, need, spin); break;
+        default: err = launch_bwd_coop_f16(op, c, p, part, w.sync, need, spin); break;
+        }
+    }
     int64_t b = 0;
-    for (int64_t r0 = 0; r0 < M && err == hipSuccess; r0 += p.batch_rows, ++b) {
+    for (int64_t r0 = 0; !coop && r0 < M && err == hipSuccess; r0 += p.batch_rows, ++b) {
         const int64_t mb = std::min(p.batch_rows, M - r0);
         BwdCall c{static_cast<const char*>(a.dy) + r0 * a.lddy * e, static_cast<const char*>(a.x) + r0 * a.ldx * e,
                   a.gamma, a.mean ? a.mean + r0 : nullptr, a.rstd + r0, static_cast<char*>(a.dx) + r0 * a.lddx * e,
@@ -786,9 +830,10 @@ int norm_bwd_describe(int rms, int64_t M, int64_t N, int dtype, int aligned, cha
     if (st != NORM_OK) return st;
     if (buf && buflen > 0 && p.path == PATH_SPLIT)
         std::snprintf(buf, (size_t)buflen,
-                      "path=bwd_split op=%s wg=%d sums_vpl=%d apply_vpl=%d epv=%d chunks=%d apply_chunks=%d "
-                      "batch_rows=%lld grid=%lld apply_grid=%lld partial_rows=%d",
-                      rms ? "rms" : "ln", p.wg, bwd_sums_vpl(p.epv), p.vpl, p.epv, p.chunks, p.apply_chunks,
+                      "path=bwd_split mode=%s op=%s wg=%d sums_vpl=%d apply_vpl=%d epv=%d chunks=%d "
+                      "apply_chunks=%d batch_rows=%lld grid=%lld apply_grid=%lld partial_rows=%d",
+                      p.split_mode == SPLIT_COOP ? "coop" : "three", rms ? "rms" : "ln", p.wg,
+                      p.split_mode == SPLIT_COOP ? p.vpl : bwd_sums_vpl(p.epv), p.vpl, p.epv, p.chunks, p.apply_chunks,
                       (long long)p.batch_rows, (long long)p.grid, (long long)p.apply_grid, p.teams);
     else if (buf && buflen > 0)
         std::snprintf(buf, (size_t)buflen,

@@ -28,6 +28,14 @@
 //
 // The column sums of the partial rows follow (norm_colsum_kernel), so
 // dgamma and dbeta are summed in a fixed order throughout.
+//
+// On request, norm_bwd_coop_kernel does it in one cooperative pass (dy and x
+// read once): teams of S co-resident workgroups, one per chunk of a row, walk
+// the rows; each keeps its chunk of dy and x in registers, publishes its
+// chunk sums, loads its next row's chunk, waits at the row's barrier (the
+// protocol of the forward's single pass), adds the row's S chunk sums in
+// chunk order, forms dx from registers and accumulates dgamma / dbeta for
+// its columns; partial row `team` holds them at the end.
 #pragma once
 
 #include "prims.hpp"
@@ -267,6 +275,232 @@ void norm_bwd_split_apply_kernel(const typename T::storage* dy,      // dx may b
             if constexpr (!RMS)
                 if (part_b != nullptr)
                     part_b[base + k] = accumulate ? part_b[base + k] + acc_b[j][k] : acc_b[j][k];
+        }
+    }
+}
+
+// Sum of a row's S chunk sums, read with coherent loads, in the fixed order
+// of rowsum_one (lane l takes chunks l, l + 64, ... into four accumulators in
+// turn, then the wavefront butterfly): the same bits in every wavefront.
+__device__ __forceinline__ float2 rowsum_coherent(const float2* pr, int S) {
+    float2 a[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = make_float2(0.0f, 0.0f);
+    int c = lane_id();
+    for (; c + 192 < S; c += 256) {
+        float2 v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = load_partial_coherent(pr + c + 64 * i);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            a[i].x += v[i].x;
+            a[i].y += v[i].y;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+        if (c + 64 * i < S) {
+            const float2 v = load_partial_coherent(pr + c + 64 * i);
+            a[i].x += v.x;
+            a[i].y += v.y;
+        }
+    float s1 = (a[0].x + a[1].x) + (a[2].x + a[3].x);
+    float s2 = (a[0].y + a[1].y) + (a[2].y + a[3].y);
+    return make_float2(team_sum<64>(s1), team_sum<64>(s2));
+}
+
+template <class T, bool RMS, int WG, int VPL, int EPV>
+__global__ __launch_bounds__(WG)
+void norm_bwd_coop_kernel(const typename T::storage* dy,      // dx may be written over dy or x
+                          const typename T::storage* x,
+                          const typename T::storage* __restrict__ gamma,
+                          const float* __restrict__ mean,
+                          const float* __restrict__ rstd,
+                          typename T::storage* dx,
+                          float* __restrict__ part_g,         // [teams, N] or null
+                          float* __restrict__ part_b,         // [teams, N] or null
+                          float2* __restrict__ part,          // [M, S] chunk sums
+                          unsigned* __restrict__ sync,        // row r: [64r], [64r+32]; zero at
+                                                              // launch and again at exit
+                          int64_t M, int N, int64_t ldy, int64_t ldx, int64_t lddx, int S, int teams,
+                          unsigned need, unsigned spin_limit)
+{
+    using V = Vec<T, EPV>;
+    using St = typename T::storage;
+    constexpr int CV = WG * VPL;
+    __shared__ float red[2][WG / 64];
+    __shared__ int late;
+    const int tid = threadIdx.x;
+    const int team = blockIdx.x / S;          // grid is exactly teams * S
+    const int c = blockIdx.x - team * S;
+    const int NV = N / EPV;
+    const float inv_n = 1.0f / (float)N;
+
+    bool col_ok[VPL];
+    V gam[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+        const unsigned v = (unsigned)(c * CV + j * WG) + tid;
+        col_ok[j] = (int)v < NV;
+        if (gamma != nullptr && col_ok[j]) {
+            gam[j].load(gamma + v * EPV);
+        } else {
+            float one[EPV];
+#pragma unroll
+            for (int k = 0; k < EPV; ++k) one[k] = 1.0f;
+            gam[j].set(one);
+        }
+    }
+    float acc_g[VPL][EPV], acc_b[RMS ? 1 : VPL][EPV];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j)
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) {
+            acc_g[j][k] = 0.0f;
+            if constexpr (!RMS) acc_b[j][k] = 0.0f;
+        }
+
+    struct Row {
+        V d[VPL], xx[VPL];
+        float m, r;
+    };
+    auto fetch = [&](int64_t row, Row& q) {
+        if (row >= M) return;
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+            const unsigned v = (unsigned)(c * CV + j * WG) + tid;
+            if (col_ok[j]) {          // nontemporal: dy and x are read once
+                q.d[j].load_stream(dy + row * ldy + v * EPV);
+                q.xx[j].load_stream(x + row * ldx + v * EPV);
+            }
+        }
+        q.m = RMS ? 0.0f : mean[row];
+        q.r = rstd[row];
+    };
+    auto ready = [&](Row& q) {
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+            q.d[j].opaque();
+            q.xx[j].opaque();
+        }
+        asm volatile("" : "+v"(q.m), "+v"(q.r));
+    };
+    // One row: chunk sums, publication, (the next row's loads), the wait,
+    // the row sums, dx and the column accumulators.
+    auto finish = [&](Row& q, int64_t row, auto&& during_wait, auto&& before_stores) {
+        float s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+            if (!col_ok[j]) continue;
+#pragma unroll
+            for (int k = 0; k < EPV; ++k) {
+                const float g = q.d[j].get(k) * gam[j].get(k);
+                const float xh = RMS ? q.xx[j].get(k) : (q.xx[j].get(k) - q.m) * q.r;
+                if constexpr (!RMS) s1 += g;
+                s2 = __builtin_fmaf(g, xh, s2);
+            }
+        }
+        // re-widen dy and x after the exchanges rather than keep fp32 copies
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+            q.d[j].opaque();
+            q.xx[j].opaque();
+        }
+        // two exchanges on two slot sets: the second's barrier orders every
+        // read of the first set before the next row writes it
+        if constexpr (!RMS) s1 = wg_sum<WG>(s1, red[0]);
+        s2 = wg_sum<WG>(s2, red[1]);
+        // one 256-byte line of counters per row: rows in flight never share one
+        unsigned* arrived = sync + row * 64;
+        unsigned* departed = arrived + 32;
+        if (tid == 0) {
+            // publish the chunk sums before the arrival count
+            store_partial_coherent(part + row * S + c, make_float2(s1, s2));
+            __builtin_amdgcn_s_waitcnt(0);     // the store has completed
+            __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        during_wait();
+        if (tid == 0) {
+            // wait for the row's other S-1 workgroups; relaxed polling, bounded
+            // so that a broken co-residency assumption cannot hang (need = S;
+            // a host test hook can ask for S + 1, which never comes)
+            unsigned spins = 0;
+            int timed_out = 0;
+            while (__hip_atomic_load(arrived, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+                if (++spins > spin_limit) {
+                    timed_out = 1;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(8);
+            }
+            late = timed_out;
+        }
+        __syncthreads();
+        float2 rs = rowsum_coherent(part + row * S, S);
+        if (late) rs = make_float2(__builtin_nanf(""), __builtin_nanf(""));   // visible failure
+        if (tid == 0) {
+            // the last workgroup of the row to depart returns both counters
+            // to zero for the next call
+            if (__hip_atomic_fetch_add(departed, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                (unsigned)S - 1) {
+                __hip_atomic_store(arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(departed, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        const float c1 = rs.x * inv_n;
+        const float c2 = RMS ? q.r * q.r * q.r * (rs.y * inv_n) : rs.y * inv_n;
+        V out[VPL];
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+            if (!col_ok[j]) continue;
+            float o[EPV];
+#pragma unroll
+            for (int k = 0; k < EPV; ++k) {
+                const float dk = q.d[j].get(k);
+                const float g = dk * gam[j].get(k);
+                if constexpr (RMS) {
+                    const float xk = q.xx[j].get(k);
+                    o[k] = __builtin_fmaf(q.r, g, -xk * c2);
+                    acc_g[j][k] = __builtin_fmaf(dk, xk * q.r, acc_g[j][k]);
+                } else {
+                    const float xh = (q.xx[j].get(k) - q.m) * q.r;
+                    o[k] = q.r * ((g - c1) - xh * c2);
+                    acc_g[j][k] = __builtin_fmaf(dk, xh, acc_g[j][k]);
+                    acc_b[j][k] += dk;
+                }
+            }
+            out[j].set(o);
+        }
+        before_stores();
+        St* dxr = dx + row * lddx;
+#pragma unroll
+        for (int j = 0; j < VPL; ++j)
+            if (col_ok[j]) out[j].put_stream(dxr + ((unsigned)(c * CV + j * WG) + tid) * EPV);
+    };
+
+    // two row register sets, the loop unrolled by two (see the forward's
+    // single pass for the ordering of the waits)
+    Row qa, qb;
+    fetch(team, qa);
+    ready(qa);
+    for (int64_t row = team; row < M;) {
+        finish(qa, row, [&] { fetch(row + teams, qb); }, [&] { ready(qb); });
+        row += teams;
+        if (row >= M) break;
+        finish(qb, row, [&] { fetch(row + teams, qa); }, [&] { ready(qa); });
+        row += teams;
+    }
+
+    // this workgroup's columns of partial row `team`
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+        if (!col_ok[j]) continue;
+        const int64_t base = (int64_t)team * N + ((int64_t)(c * CV + j * WG) + tid) * EPV;
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) {
+            if (part_g != nullptr) part_g[base + k] = acc_g[j][k];
+            if constexpr (!RMS)
+                if (part_b != nullptr) part_b[base + k] = acc_b[j][k];
         }
     }
 }

@@ -89,6 +89,10 @@ constexpr int kBwdSplitSumsVPL = 2;
 constexpr int kBwdSplitSumsVPLElem = 16;
 constexpr int bwd_sums_vpl(int epv) { return epv == 1 ? kBwdSplitSumsVPLElem : kBwdSplitSumsVPL; }
 constexpr int kBwdSplitApplyVPL = 2;
+// split backward in one cooperative pass (on request): chunks of 1024 lanes x
+// 2 vectors, one workgroup per chunk, every chunk of a team's row resident
+constexpr int kBwdCoopWG = 1024;
+constexpr int kBwdCoopVPL = 2;
 constexpr int kBwdMinTeam = 8;
 // backward workgroups: always 1024 lanes (16 wavefronts fill a CU's wave
 // slots at up to 128 VGPRs), 1024 / team rows at once
@@ -156,6 +160,18 @@ hipError_t launch_bwd_f16(int op, const BwdCall& c, const Plan& p);
 hipError_t launch_bwd_split_f32(int op, const BwdCall& c, const Plan& p, float2* part, float2* rows, int accumulate);
 hipError_t launch_bwd_split_bf16(int op, const BwdCall& c, const Plan& p, float2* part, float2* rows, int accumulate);
 hipError_t launch_bwd_split_f16(int op, const BwdCall& c, const Plan& p, float2* part, float2* rows, int accumulate);
+// split backward in one cooperative pass over all c.M rows: chunk sums in
+// part ([M, p.chunks]), row barriers in sync, partial rows p.teams x N
+hipError_t launch_bwd_coop_f32(int op, const BwdCall& c, const Plan& p, float2* part, unsigned* sync, unsigned need,
+                               unsigned spin_limit);
+hipError_t launch_bwd_coop_bf16(int op, const BwdCall& c, const Plan& p, float2* part, unsigned* sync, unsigned need,
+                                unsigned spin_limit);
+hipError_t launch_bwd_coop_f16(int op, const BwdCall& c, const Plan& p, float2* part, unsigned* sync, unsigned need,
+                               unsigned spin_limit);
+// workgroups of the single-pass split backward that fit on one CU at once
+int bwd_coop_blocks_per_cu_f32(int op, int epv);
+int bwd_coop_blocks_per_cu_bf16(int op, int epv);
+int bwd_coop_blocks_per_cu_f16(int op, int epv);
 // out_*[c] = sum of the P partial rows part_* of column c (fixed order), for
 // dgamma and (out_b not null) dbeta in one launch
 hipError_t launch_colsum(const float* part_g, float* out_g, const float* part_b, float* out_b, int64_t P, int N,

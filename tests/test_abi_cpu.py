@@ -442,7 +442,7 @@ def test_bwd_split_plans():
 
 def _bwd_plan(op, M, N, dtype, aligned=True):
     d = dict(kv.split("=") for kv in rn.norm_bwd_describe(op, M, N, dtype, aligned).split())
-    return {k: (v if k in ("path", "op") else int(v)) for k, v in d.items()}
+    return {k: (v if k in ("path", "op", "mode") else int(v)) for k, v in d.items()}
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])

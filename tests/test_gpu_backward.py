@@ -45,7 +45,7 @@ def inputs(op, dtype, M, N, seed):
 
 def plan(op, M, N, dtype, aligned=True):
     d = dict(kv.split("=") for kv in rn.norm_bwd_describe(op, M, N, dtype, aligned).split())
-    return {k: (v if k in ("path", "op") else int(v)) for k, v in d.items()}
+    return {k: (v if k in ("path", "op", "mode") else int(v)) for k, v in d.items()}
 
 
 def go(op, dtype, M, N, seed=0, offset=0, **kw):

@@ -7,7 +7,9 @@ the ABI takes, short rows forced onto the split path (ragged chunk tails),
 several batches of rows with a short last batch (the accumulating partial
 rows), a sums grid far smaller than its work items, unaligned pointers,
 strided rows, in-place dx, the optional gamma / dgamma / dbeta, M = 0, and
-bitwise determinism.
+bitwise determinism; the single cooperative pass (on request) on long and
+short rows, in place, deterministic, and with its bounded wait forced to
+time out from the host.
 """
 from __future__ import annotations
 
@@ -180,3 +182,46 @@ def test_split_agrees_with_row_kernel(monkeypatch):
     assert not np.array_equal(rows[0], np.zeros_like(rows[0]))
     d = np.abs(oracle.widen(rows[0], dtype) - oracle.widen(split[0], dtype))
     assert d.max() <= 4 * parity.ulp_of(np.abs(oracle.widen(rows[0], dtype)).max(), dtype)
+
+
+# ---------------------------------------------------------------------------
+# the single cooperative pass (MI355NORM_PATH=splitcoop)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,N,M", [("bf16", 40000, 24), ("f16", 65544, 9), ("bf16", 1 << 20, 6),
+                                       ("f32", 1 << 20, 5), ("bf16", 30001, 17), ("f32", 1000, 300),
+                                       ("bf16", 8192, 700), ("f16", 7, 50)])
+@pytest.mark.parametrize("op", ["ln", "rms"])
+def test_single_pass_split_backward(monkeypatch, op, dtype, N, M):
+    """Every chunk of a row in its own co-resident workgroup, the row sums
+    exchanged through a per-row barrier, dy and x read once; rows past the
+    team count are walked by the teams."""
+    monkeypatch.setenv("MI355NORM_PATH", "splitcoop")
+    aligned = (N * E[dtype]) % 16 == 0
+    p = plan(op, M, N, dtype, aligned)
+    assert p["mode"] == "coop", p
+    go(op, dtype, M, N, seed=N + M)
+
+
+def test_single_pass_split_backward_in_place_and_deterministic(monkeypatch):
+    monkeypatch.setenv("MI355NORM_PATH", "splitcoop")
+    _, (dx0, dg0, db0) = go("ln", "bf16", 40, 70000, seed=5)
+    _, (dx1, dg1, db1) = go("ln", "bf16", 40, 70000, seed=5)
+    _, (dx2, dg2, db2) = go("ln", "bf16", 40, 70000, seed=5, inplace="dy")
+    for a, b in ((dx0, dx1), (dg0, dg1), (db0, db1), (dx0, dx2), (dg0, dg2), (db0, db2)):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_single_pass_split_backward_bounded_wait(monkeypatch):
+    """Forced from the host, every row waits for one arrival more than it has
+    chunks, with a short bound: every workgroup stops waiting, the kernel
+    completes, the failure is visible (dx all NaN), the counters are back at
+    zero, and the next normal call is correct."""
+    monkeypatch.setenv("MI355NORM_PATH", "splitcoop")
+    dy, x, g, mean, rstd = inputs("ln", "bf16", 6, 1 << 18, 62)
+    monkeypatch.setenv("MI355NORM_FORCE_TIMEOUT", "1")
+    print("[bwd coop] forced timeout", flush=True)
+    dx, dg, db = gpu_runner.run_bwd("ln", "bf16", dy, x, g, mean, rstd)
+    assert np.isnan(oracle.widen(dx, "bf16")).all()
+    monkeypatch.delenv("MI355NORM_FORCE_TIMEOUT")
+    go("ln", "bf16", 6, 1 << 18, seed=62)
