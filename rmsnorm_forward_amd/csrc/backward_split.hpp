@@ -2,11 +2,12 @@
 // one workgroup ("CUDA 算子工程" ch. 7, section 7.7: the same formulas as
 // backward.hpp, the row sums taken over chunks of the row).
 //
-// Per batch of rows (sized so that the batch's dy and x stay in the 256 MB
-// Infinity Cache between the first and the last kernel), three kernels:
+// Per batch of rows (every row in one batch unless smaller batches are asked
+// for), three kernels:
 //
 //   norm_bwd_split_sums_kernel    one workgroup per (row, chunk of 256 lanes x
-//                                 2 vectors): reads the chunk of dy and x
+//                                 2 vectors; 16 elements per lane on the
+//                                 element-wise path): reads the chunk of dy and x
 //                                 through the caches and stores the chunk's
 //                                 (sum g, sum g xhat) -- (0, sum g x) for
 //                                 RMSNorm -- to part[row * S + chunk].

@@ -93,3 +93,12 @@ def test_launches_per_step_follow_the_plan(monkeypatch):
     assert bench.launches_per_step(rn.norm_bwd_describe("ln", 64, N, "bf16"), 64) == 4
     p = rn.norm_bwd_describe("rms", 8, 1 << 24, "bf16")
     assert "partial_rows=1" in p and bench.launches_per_step(p, 8) == 3   # one row group: no column sums
+
+
+def test_source_digest_ignores_comments_only():
+    """A change to comments or blank lines leaves the digest (and so the
+    committed counter measurements) valid; a change to code does not."""
+    a = "int f(int x) {  // one\n    return x + 1;\n}\n"
+    b = "/* header\n   text */\nint f(int x) {\n\n    return x + 1;   // two\n}\n"
+    c = "int f(int x) {\n    return x + 2;\n}\n"
+    assert bench._code_only(a) == bench._code_only(b) != bench._code_only(c)
