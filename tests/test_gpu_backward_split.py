@@ -225,3 +225,34 @@ def test_single_pass_split_backward_bounded_wait(monkeypatch):
     assert np.isnan(oracle.widen(dx, "bf16")).all()
     monkeypatch.delenv("MI355NORM_FORCE_TIMEOUT")
     go("ln", "bf16", 6, 1 << 18, seed=62)
+
+
+@pytest.mark.parametrize("dtype,N,lddy,ldx,lddx,offset", [
+    ("bf16", 40000, 40000 + 64, 40000 + 8, 40000 + 128, 0),
+    ("bf16", 40000, 40000 + 3, 40000, 40000 + 5, 0),
+    ("f32", 33000, 33000 + 4, 33000 + 12, 33000 + 36, 1),
+])
+@pytest.mark.parametrize("op", ["ln", "rms"])
+def test_single_pass_split_backward_strided_rows(monkeypatch, op, dtype, N, lddy, ldx, lddx, offset):
+    monkeypatch.setenv("MI355NORM_PATH", "splitcoop")
+    M = 7
+    dy, x, g, mean, rstd = inputs(op, dtype, M, N, N + 67)
+    aligned = offset == 0 and all((v * E[dtype]) % 16 == 0 for v in (N, lddy, ldx, lddx))
+    p = plan(op, M, N, dtype, aligned)
+    assert p["mode"] == "coop"
+    print(f"[bwd coop] strided {op} {dtype} N={N} ld={lddy},{ldx},{lddx} offset={offset}", flush=True)
+    dx, dg, db = gpu_runner.run_bwd_strided(op, dtype, dy, x, g, mean, rstd, lddy=lddy, ldx=ldx, lddx=lddx,
+                                            offset=offset)
+    parity.check_bwd(op, dtype, dy, x, g, mean, rstd, dx, dg, db, p, what=f"coop strided {op}")
+
+
+@pytest.mark.parametrize("op", ["ln", "rms"])
+def test_single_pass_split_backward_optional_outputs_and_gamma(monkeypatch, op):
+    monkeypatch.setenv("MI355NORM_PATH", "splitcoop")
+    M, N = 20, 40000
+    dy, x, g, mean, rstd = inputs(op, "f32", M, N, 13)
+    for gamma, want_g, want_b in [(None, True, True), (g, False, True), (g, True, False), (g, False, False)]:
+        print(f"[bwd coop] optional gamma={gamma is not None} dg={want_g} db={want_b}", flush=True)
+        dx, dg, db = gpu_runner.run_bwd(op, "f32", dy, x, gamma, mean, rstd, want_g=want_g, want_b=want_b)
+        parity.check_bwd(op, "f32", dy, x, gamma, mean, rstd, dx, dg, db, plan(op, M, N, "f32"),
+                         what=f"coop gamma={gamma is not None} dg={want_g} db={want_b}")
