@@ -300,7 +300,9 @@ int norm_describe(int op, int64_t M, int64_t N, int dtype, int aligned,
 /*
  * As norm_describe, for ln_bwd (rms = 0) or rms_bwd (rms = 1): path ("bwd"
  * or "bwd_split"), lanes per row, vectors per lane, workgroup size, grid and
- * the number of partial rows of dgamma and dbeta.
+ * the number of partial rows of dgamma and dbeta; for split rows also the
+ * mode ("three" kernels per batch, or "coop", the single cooperative pass
+ * taken only on request), chunks per row and rows per batch.
  */
 int norm_bwd_describe(int rms, int64_t M, int64_t N, int dtype, int aligned,
                       char *buf, int buflen);
