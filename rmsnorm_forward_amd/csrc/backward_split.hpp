@@ -411,43 +411,14 @@ void norm_bwd_coop_kernel(const typename T::storage* dy,      // dx may be writt
         // read of the first set before the next row writes it
         if constexpr (!RMS) s1 = wg_sum<WG>(s1, red[0]);
         s2 = wg_sum<WG>(s2, red[1]);
-        // one 256-byte line of counters per row: rows in flight never share one
-        unsigned* arrived = sync + row * 64;
-        unsigned* departed = arrived + 32;
-        if (tid == 0) {
-            // publish the chunk sums before the arrival count
-            store_partial_coherent(part + row * S + c, make_float2(s1, s2));
-            __builtin_amdgcn_s_waitcnt(0);     // the store has completed
-            __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        const RowBarrier bar(sync, row);
+        if (tid == 0) bar.arrive(part + row * S + c, make_float2(s1, s2));
         during_wait();
-        if (tid == 0) {
-            // wait for the row's other S-1 workgroups; relaxed polling, bounded
-            // so that a broken co-residency assumption cannot hang (need = S;
-            // a host test hook can ask for S + 1, which never comes)
-            unsigned spins = 0;
-            int timed_out = 0;
-            while (__hip_atomic_load(arrived, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
-                if (++spins > spin_limit) {
-                    timed_out = 1;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(8);
-            }
-            late = timed_out;
-        }
+        if (tid == 0) late = bar.wait(need, spin_limit);
         __syncthreads();
         float2 rs = rowsum_coherent(part + row * S, S);
         if (late) rs = make_float2(__builtin_nanf(""), __builtin_nanf(""));   // visible failure
-        if (tid == 0) {
-            // the last workgroup of the row to depart returns both counters
-            // to zero for the next call
-            if (__hip_atomic_fetch_add(departed, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                (unsigned)S - 1) {
-                __hip_atomic_store(arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(departed, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
+        if (tid == 0) bar.depart(S);
         const float c1 = rs.x * inv_n;
         const float c2 = RMS ? q.r * q.r * q.r * (rs.y * inv_n) : rs.y * inv_n;
         V out[VPL];

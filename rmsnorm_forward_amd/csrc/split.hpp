@@ -200,6 +200,46 @@ __device__ __forceinline__ float2 load_partial_coherent(const float2* p) {
     return make_float2(__uint_as_float((unsigned)bits), __uint_as_float((unsigned)(bits >> 32)));
 }
 
+// The per-row barrier of the single-pass kernels.  Row r's counters sit in
+// one 256-byte line at sync + 64 r (arrivals) and + 32 (departures), so rows
+// in flight never share a line; they are zero at launch and again at exit.
+// Every member is called by one thread of the workgroup.
+struct RowBarrier {
+    unsigned* arrived;
+    unsigned* departed;
+    __device__ RowBarrier(unsigned* sync, int64_t row) : arrived(sync + row * 64), departed(arrived + 32) {}
+
+    // publish this workgroup's partial (a coherent 64-bit store, complete
+    // before the count), then count its arrival
+    __device__ void arrive(float2* slot, float2 v) const {
+        store_partial_coherent(slot, v);
+        __builtin_amdgcn_s_waitcnt(0);
+        __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // wait for `need` arrivals (the row's chunk count; a host test hook can
+    // ask for one more, which never comes), polling with relaxed loads at most
+    // spin_limit times so that a broken co-residency assumption cannot hang;
+    // returns 1 if the bound was reached
+    __device__ int wait(unsigned need, unsigned spin_limit) const {
+        unsigned spins = 0;
+        while (__hip_atomic_load(arrived, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+            if (++spins > spin_limit) return 1;
+            __builtin_amdgcn_s_sleep(8);
+        }
+        return 0;
+    }
+
+    // count this workgroup's departure (it has read every partial); the last
+    // of the row's S returns both counters to zero for the next call
+    __device__ void depart(int S) const {
+        if (__hip_atomic_fetch_add(departed, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)S - 1) {
+            __hip_atomic_store(arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(departed, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+};
+
 // start of row `row` of an output of the I/O dtype, or of FP8 codes
 template <class T, bool Q8>
 __device__ __forceinline__ void* row_out(void* y, int64_t row, int64_t ldy) {
@@ -297,44 +337,14 @@ void norm_split_coop_kernel(const typename T::storage* x,
     // stored.
     auto finish = [&](C& ch, float K, int64_t row, auto&& during_wait, auto&& before_stores) {
         const float2 p = ch.template partial<RMS>(K, NV, red);
-        // one 256-byte line of counters per row: rows in flight never share one
-        unsigned* arrived = sync + row * 64;
-        unsigned* departed = arrived + 32;
-        if (tid == 0) {
-            // publish the partial before the arrival count
-            store_partial_coherent(part + row * S + c, p);
-            __builtin_amdgcn_s_waitcnt(0);     // the store has completed
-            __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        const RowBarrier bar(sync, row);
+        if (tid == 0) bar.arrive(part + row * S + c, p);
         during_wait();
-        if (tid == 0) {
-            // wait for the row's other S-1 workgroups.  Polling uses relaxed
-            // loads.  The wait is bounded so a broken co-residency assumption
-            // cannot hang; need = S (a host test hook can ask for S + 1,
-            // which never comes).
-            unsigned spins = 0;
-            int timed_out = 0;
-            while (__hip_atomic_load(arrived, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
-                if (++spins > spin_limit) {
-                    timed_out = 1;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(8);
-            }
-            late = timed_out;
-        }
+        if (tid == 0) late = bar.wait(need, spin_limit);
         __syncthreads();
         float2 st = row_stats<RMS, true>(part + row * S, S, C::CV * EPV, N, eps);
         if (late) st = make_float2(__builtin_nanf(""), __builtin_nanf(""));   // visible failure
-        if (tid == 0) {
-            // every workgroup has passed the wait once all S have departed:
-            // the last one out returns both counters to zero for the next call
-            if (__hip_atomic_fetch_add(departed, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                (unsigned)S - 1) {
-                __hip_atomic_store(arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(departed, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
+        if (tid == 0) bar.depart(S);
         if (c == 0 && tid == 0) {
             if (!RMS && mean_out) mean_out[row] = K + st.x;
             if (rstd_out) rstd_out[row] = st.y;
