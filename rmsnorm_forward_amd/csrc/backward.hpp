@@ -306,9 +306,22 @@ void norm_bwd_rows_kernel(const typename T::storage* dy,      // dx may be writt
         }
     };
     const int64_t prow = blockIdx.x;
+    // a lane's EPV consecutive columns go out as 16-byte vectors where EPV
+    // allows (the partial rows are 16-byte aligned then)
+    auto put_row = [&](float* dst, const float (&v)[EPV]) {
+        if constexpr (EPV % 4 == 0) {
+#pragma unroll
+            for (int k = 0; k < EPV; k += 4)
+                *reinterpret_cast<float4*>(dst + k) = make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < EPV; ++k) dst[k] = v[k];
+        }
+    };
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
         const unsigned off = (unsigned)(j * TEAM + tl) * EPV;
+        float vg[EPV], vb[EPV];
 #pragma unroll
         for (int k = 0; k < EPV; ++k) {
             float ag = acc_g[j][k], ab = 0.0f;
@@ -319,11 +332,13 @@ void norm_bwd_rows_kernel(const typename T::storage* dy,      // dx may be writt
                 if constexpr (!RMS)
                     if (want_b) fold(ab);
             }
-            if (team == 0 && col_ok[j]) {
-                if (want_g) part_g[prow * N + off + k] = ag;
-                if constexpr (!RMS)
-                    if (want_b) part_b[prow * N + off + k] = ab;
-            }
+            vg[k] = ag;
+            vb[k] = ab;
+        }
+        if (team == 0 && col_ok[j]) {
+            if (want_g) put_row(part_g + prow * N + off, vg);
+            if constexpr (!RMS)
+                if (want_b) put_row(part_b + prow * N + off, vb);
         }
     }
 }

@@ -44,6 +44,30 @@
 
 namespace mi355norm {
 
+// A lane's EPV consecutive columns of a partial row: written (or, with
+// accumulate, added to) as 16-byte vectors when EPV and the row's alignment
+// allow -- the partial rows may be dgamma / dbeta themselves, which need be
+// 4-byte aligned only -- else one element at a time.
+template <int EPV>
+__device__ __forceinline__ void put_partial(float* dst, const float (&v)[EPV], bool vec, int accumulate) {
+    if constexpr (EPV % 4 == 0) {
+        if (vec) {
+#pragma unroll
+            for (int k = 0; k < EPV; k += 4) {
+                float4 o = make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]);
+                if (accumulate) {
+                    const float4 a = *reinterpret_cast<const float4*>(dst + k);
+                    o = make_float4(a.x + o.x, a.y + o.y, a.z + o.z, a.w + o.w);
+                }
+                *reinterpret_cast<float4*>(dst + k) = o;
+            }
+            return;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < EPV; ++k) dst[k] = accumulate ? dst[k] + v[k] : v[k];
+}
+
 template <class T, bool RMS, int WG, int VPL, int EPV>
 __global__ __launch_bounds__(WG)
 void norm_bwd_split_sums_kernel(const typename T::storage* __restrict__ dy,
@@ -266,17 +290,15 @@ void norm_bwd_split_apply_kernel(const typename T::storage* dy,      // dx may b
     }
 
     // this workgroup's columns of partial row `grp`
+    const bool vg = (reinterpret_cast<uintptr_t>(part_g) & 15) == 0;
+    const bool vb = (reinterpret_cast<uintptr_t>(part_b) & 15) == 0;
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
         if (!col_ok[j]) continue;
         const int64_t base = grp * (int64_t)N + ((int64_t)(c * CV + j * WG) + threadIdx.x) * EPV;
-#pragma unroll
-        for (int k = 0; k < EPV; ++k) {
-            if (part_g != nullptr) part_g[base + k] = accumulate ? part_g[base + k] + acc_g[j][k] : acc_g[j][k];
-            if constexpr (!RMS)
-                if (part_b != nullptr)
-                    part_b[base + k] = accumulate ? part_b[base + k] + acc_b[j][k] : acc_b[j][k];
-        }
+        if (part_g != nullptr) put_partial<EPV>(part_g + base, acc_g[j], vg, accumulate);
+        if constexpr (!RMS)
+            if (part_b != nullptr) put_partial<EPV>(part_b + base, acc_b[j], vb, accumulate);
     }
 }
 
@@ -464,16 +486,15 @@ void norm_bwd_coop_kernel(const typename T::storage* dy,      // dx may be writt
     }
 
     // this workgroup's columns of partial row `team`
+    const bool vg = (reinterpret_cast<uintptr_t>(part_g) & 15) == 0;
+    const bool vb = (reinterpret_cast<uintptr_t>(part_b) & 15) == 0;
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
         if (!col_ok[j]) continue;
         const int64_t base = (int64_t)team * N + ((int64_t)(c * CV + j * WG) + tid) * EPV;
-#pragma unroll
-        for (int k = 0; k < EPV; ++k) {
-            if (part_g != nullptr) part_g[base + k] = acc_g[j][k];
-            if constexpr (!RMS)
-                if (part_b != nullptr) part_b[base + k] = acc_b[j][k];
-        }
+        if (part_g != nullptr) put_partial<EPV>(part_g + base, acc_g[j], vg, 0);
+        if constexpr (!RMS)
+            if (part_b != nullptr) put_partial<EPV>(part_b + base, acc_b[j], vb, 0);
     }
 }
 
