@@ -109,7 +109,11 @@ void norm_bwd_rows_kernel(const typename T::storage* dy,      // dx may be writt
         else return gam[j];
     };
 
-    __shared__ float acc_lds[LACC ? E : 1][kBwdWG];
+    // with 16-byte vectors a lane's four consecutive columns share one LDS
+    // slot ([column / 4][lane], float4), else [column][lane]
+    constexpr bool LACC4 = LACC && EPV % 4 == 0;
+    __shared__ float acc_lds[LACC && !LACC4 ? E : 1][kBwdWG];
+    __shared__ float4 acc_lds4[LACC4 ? E / 4 : 1][kBwdWG];
     float acc_g[VPL][EPV], acc_b[(RMS || LACC) ? 1 : VPL][EPV];
 #pragma unroll
     for (int j = 0; j < VPL; ++j)
@@ -117,7 +121,9 @@ void norm_bwd_rows_kernel(const typename T::storage* dy,      // dx may be writt
         for (int k = 0; k < EPV; ++k) {
             acc_g[j][k] = 0.0f;
             if constexpr (!RMS && !LACC) acc_b[j][k] = 0.0f;
-            if constexpr (LACC) acc_lds[j * EPV + k][tid] = 0.0f;
+            if constexpr (LACC && !LACC4) acc_lds[j * EPV + k][tid] = 0.0f;
+            if constexpr (LACC4)
+                if (k % 4 == 0) acc_lds4[(j * EPV + k) / 4][tid] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         }
 
     // the loads of one row group: dy, x and the row's statistics
@@ -227,8 +233,19 @@ void norm_bwd_rows_kernel(const typename T::storage* dy,      // dx may be writt
                     const float xh = (xx[j].get(k) - m) * r;
                     o[k] = r * ((g - c1) - xh * c2);
                     acc_g[j][k] = __builtin_fmaf(dk, xh, acc_g[j][k]);
-                    if constexpr (LACC) acc_lds[j * EPV + k][tid] += dk;
-                    else acc_b[j][k] += dk;
+                    if constexpr (LACC && !LACC4) acc_lds[j * EPV + k][tid] += dk;
+                    else if constexpr (!LACC) acc_b[j][k] += dk;
+                }
+            }
+            if constexpr (LACC4) {
+#pragma unroll
+                for (int q = 0; q < EPV / 4; ++q) {
+                    float4 a = acc_lds4[j * (EPV / 4) + q][tid];
+                    a.x += d[j].get(4 * q);
+                    a.y += d[j].get(4 * q + 1);
+                    a.z += d[j].get(4 * q + 2);
+                    a.w += d[j].get(4 * q + 3);
+                    acc_lds4[j * (EPV / 4) + q][tid] = a;
                 }
             }
             out[j].set(o);           // rounded to the storage type (RNE)
@@ -325,8 +342,14 @@ void norm_bwd_rows_kernel(const typename T::storage* dy,      // dx may be writt
 #pragma unroll
         for (int k = 0; k < EPV; ++k) {
             float ag = acc_g[j][k], ab = 0.0f;
-            if constexpr (LACC) ab = acc_lds[j * EPV + k][tid];
-            else if constexpr (!RMS) ab = acc_b[j][k];
+            if constexpr (LACC4) {
+                const float4 a = acc_lds4[(j * EPV + k) / 4][tid];
+                ab = k % 4 == 0 ? a.x : k % 4 == 1 ? a.y : k % 4 == 2 ? a.z : a.w;
+            } else if constexpr (LACC) {
+                ab = acc_lds[j * EPV + k][tid];
+            } else if constexpr (!RMS) {
+                ab = acc_b[j][k];
+            }
             if constexpr (G::ROWS > 1) {
                 if (want_g) fold(ag);
                 if constexpr (!RMS)
