@@ -256,3 +256,35 @@ def test_single_pass_split_backward_optional_outputs_and_gamma(monkeypatch, op):
         dx, dg, db = gpu_runner.run_bwd(op, "f32", dy, x, gamma, mean, rstd, want_g=want_g, want_b=want_b)
         parity.check_bwd(op, "f32", dy, x, gamma, mean, rstd, dx, dg, db, plan(op, M, N, "f32"),
                          what=f"coop gamma={gamma is not None} dg={want_g} db={want_b}")
+
+
+@pytest.mark.parametrize("mode", ["split", "splitcoop"])
+def test_split_backward_unaligned_column_sums(monkeypatch, mode):
+    """One row group writes dgamma / dbeta itself (batches of one row force
+    it on the three-kernel form; one team on the single pass): with those
+    outputs only 4-byte aligned the writes fall back from 16-byte vectors to
+    single elements and still add up every batch."""
+    monkeypatch.setenv("MI355NORM_PATH", mode)
+    if mode == "split":
+        M, N = 5, 2048
+        monkeypatch.setenv("MI355NORM_SPLIT_BATCH", str(2 * N * 2))     # one row per batch
+    else:
+        M, N = 3, 3 << 20                                               # 192 chunks: one team
+    dy, x, g, mean, rstd = inputs("ln", "bf16", M, N, 91)
+    p = plan("ln", M, N, "bf16")
+    if p["partial_rows"] != 1:
+        pytest.skip(f"this device plans {p['partial_rows']} row groups here")
+    dyt, xt, gt = (gpu_runner.to_device(a, "bf16") for a in (dy, x, g))
+    mt, rt = torch.from_numpy(mean).cuda(), torch.from_numpy(rstd).cuda()
+    dxt = torch.empty(M * N, dtype=torch.bfloat16, device="cuda")
+    buf = torch.full((2 * N + 8,), float("nan"), device="cuda")
+    dgt, dbt = buf[1:N + 1], buf[N + 5:2 * N + 5]          # 4-byte aligned, not 16
+    assert dgt.data_ptr() % 16 and dbt.data_ptr() % 16
+    print(f"[bwd {mode}] unaligned dgamma/dbeta {p}", flush=True)
+    st = rn.ln_bwd(dyt.data_ptr(), xt.data_ptr(), gt.data_ptr(), mt.data_ptr(), rt.data_ptr(), dxt.data_ptr(),
+                   dgt.data_ptr(), dbt.data_ptr(), M, N, rn.NORM_BF16, torch.cuda.current_stream().cuda_stream)
+    assert st == rn.NORM_OK
+    torch.cuda.synchronize()
+    dx = gpu_runner.to_host(dxt, "bf16").reshape(M, N)
+    parity.check_bwd("ln", "bf16", dy, x, g, mean, rstd, dx, dgt.cpu().numpy(), dbt.cpu().numpy(), p,
+                     what=f"{mode} unaligned column sums")
