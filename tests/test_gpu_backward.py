@@ -7,7 +7,7 @@ backward configurations at full size, every row length class of the row
 kernel (up to 32768; longer rows are in test_gpu_backward_split.py) with
 ragged row counts, unaligned pointers, in-place dx, the
 optional gamma / dgamma / dbeta, M = 0, every tile, forced grids, and bitwise
-determinism.
+determinism, and the large-mean stress rows of the forward.
 """
 from __future__ import annotations
 
@@ -264,3 +264,23 @@ def test_backward_tensor_api_takes_strided_rows():
         for u, v in zip(a, b):
             assert (u is None and v is None) or torch.equal(u.view(torch.int16) if u.dtype == torch.bfloat16 else u,
                                                             v.view(torch.int16) if v.dtype == torch.bfloat16 else v)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_on_large_mean_stress_rows(dtype):
+    """The forward's stress recipe (rows of 1000 + N(0, 1e-2), outlier
+    channels x100) under the LayerNorm backward: x - mean cancels almost
+    completely on the large-mean rows, and both sides take the same fp32
+    statistics; dx, dgamma and dbeta meet the bound and stay finite."""
+    M, N = 512, 8192
+    s = workloads.gen_ln_stress(1012, M, N, dtype)
+    rng = np.random.default_rng(1013)
+    dy = workloads.to_storage(rng.standard_normal((M, N)), dtype)
+    _, mean, rstd = oracle.ln_fwd(s["x"], s["gamma"], None, dtype, 1e-5)
+    mean, rstd = mean.astype(np.float32), rstd.astype(np.float32)
+    print(f"[bwd] stress {dtype}", flush=True)
+    dx, dg, db = gpu_runner.run_bwd("ln", dtype, dy, s["x"], s["gamma"], mean, rstd)
+    parity.check_bwd("ln", dtype, dy, s["x"], s["gamma"], mean, rstd, dx, dg, db, plan("ln", M, N, dtype),
+                     what=f"stress {dtype}")
+    got = dx.astype(np.float64) if dtype == "f32" else oracle.widen(dx, dtype)
+    assert np.isfinite(got).all() and np.isfinite(dg).all() and np.isfinite(db).all()
