@@ -221,6 +221,20 @@ bool tile_instantiated(int team, int vpl) {
     return t && v;
 }
 
+// one wavefront per row with 5 or 10 vectors per lane (forward row kernel only): for
+// rows of 320 or 640 16-byte vectors when there are at most
+// kWaveTileMaxRows rows
+constexpr int kWaveTileVpls[] = {5, 10};
+constexpr int64_t kWaveTileMaxRows = 4096;
+
+// the forward row kernel also has the one-wavefront tiles
+bool fwd_tile_instantiated(int team, int vpl) {
+    if (team == 64)
+        for (int c : kWaveTileVpls)
+            if (c == vpl) return true;
+    return tile_instantiated(team, vpl);
+}
+
 // How many workgroups of the single-pass split kernel (bwd: of the single-
 // pass split backward) the current device can hold at once (0 if cooperative
 // launch is unavailable or no device is present).  Cached per (device, dtype,
@@ -281,7 +295,7 @@ int make_plan(int op, int64_t M, int64_t N, int dtype, bool aligned, const Overr
         if (o.team) {
             team = o.team;
             vpl = o.vpl;
-            if (!tile_instantiated(team, vpl) || int64_t(team) * vpl < NV) return NORM_ERR_BAD_ARG;
+            if (!fwd_tile_instantiated(team, vpl) || int64_t(team) * vpl < NV) return NORM_ERR_BAD_ARG;
         } else {
             const int per_lane = e == 2 ? 4 : 2;
             team = next_pow2((NV + per_lane - 1) / per_lane);
@@ -297,6 +311,16 @@ int make_plan(int op, int64_t M, int64_t N, int dtype, bool aligned, const Overr
                 while ((NV + team - 1) / team > 8 && team < kMaxTeam) team *= 2;
             }
             vpl = round_vpl((NV + team - 1) / team);
+            // few rows whose 16-byte vectors fill one wavefront x 5 or 10
+            // exactly: one wavefront per row (no LDS exchange, every load
+            // of the row issued at once) beats the ragged wider tile
+            // (steady state, us, LN bf16 4096 x 5120: 64 x 10 14.7 vs
+            // 256 x 4 18.4; 2048 x 5120 9.4 vs 11.0; LN bf16 4096 x 2560:
+            // 64 x 5 9.0 vs 128 x 4 11.0; from 8192 rows on it is level or
+            // slower: RMS bf16 8192 x 5120 32.5 vs 30.0)
+            if (p->epv > 1 && M <= kWaveTileMaxRows)
+                for (int c : kWaveTileVpls)
+                    if (NV == int64_t(64) * c) { team = 64; vpl = c; }
         }
         p->team = team;
         p->vpl = vpl;

@@ -70,6 +70,12 @@ hipError_t rows_by_vpl(const NormCall& c, const Plan& p) {
     case 4: return go_rows<T, RMS, ADD, Q8, TEAM, 4, EPV>(c, p);
     case 8: return go_rows<T, RMS, ADD, Q8, TEAM, 8, EPV>(c, p);
     case 16: return go_rows<T, RMS, ADD, Q8, TEAM, 16, EPV>(c, p);
+    case 5:
+        if constexpr (TEAM == 64) return go_rows<T, RMS, ADD, Q8, TEAM, 5, EPV>(c, p);
+        break;
+    case 10:
+        if constexpr (TEAM == 64) return go_rows<T, RMS, ADD, Q8, TEAM, 10, EPV>(c, p);
+        break;
     }
     return hipErrorInvalidValue;
 }

@@ -193,7 +193,7 @@ def parse(desc):
     ("ln", 16384, 8192, "bf16", dict(path="rows", team="256", vpl="4", epv="8")),
     ("rms", 65536, 2048, "f32", dict(path="rows", team="256", vpl="2", epv="4")),
     ("rms", 65536, 2048, "bf16", dict(path="rows", team="64", vpl="4", epv="8")),
-    ("ln", 4096, 5120, "bf16", dict(path="rows", team="256", vpl="4", epv="8")),
+    ("ln", 4096, 5120, "bf16", dict(path="rows", team="64", vpl="10", epv="8")),
     ("ln", 64, 1 << 20, "bf16", dict(path="split", mode="two", chunks="64", apply_chunks="64", epv="8",
                                       batch_rows="64", grid="4096", apply_grid="4096")),
 ])
@@ -238,6 +238,21 @@ def test_unaligned_plans_take_the_elementwise_path():
     assert d["epv"] == "1" and d["path"] == "rows"
     d = parse(rn.norm_describe("ln", 64, 4096, "bf16", aligned=False))
     assert d["epv"] == "1"
+
+
+def test_one_wavefront_tiles_only_for_few_rows_that_fill_them():
+    """64 lanes x 5 or 10 vectors when that covers a row of 16-byte vectors
+    exactly and there are at most 4096 rows; the wider tiles otherwise."""
+    for dtype, N, vpl in (("bf16", 5120, 10), ("f16", 5120, 10), ("bf16", 2560, 5), ("f32", 2560, 10),
+                          ("f32", 1280, 5)):
+        for op in ("ln", "rms", "add_rms", "rms_fp8", "add_rms_fp8"):
+            d = parse(rn.norm_describe(op, 4096, N, dtype))
+            assert (d["team"], d["vpl"], d["rows_per_wg"], d["grid"]) == ("64", str(vpl), "4", "1024"), (op, d)
+        assert parse(rn.norm_describe("ln", 4097, N, dtype))["team"] != "64"
+        assert parse(rn.norm_describe("ln", 4096, N, dtype, False))["epv"] == "1"
+        assert parse(rn.norm_describe("ln", 4096, N, dtype, False))["vpl"] not in ("5", "10")
+    for dtype, N in (("bf16", 5128), ("bf16", 4096), ("f32", 2048), ("bf16", 1280)):
+        assert parse(rn.norm_describe("ln", 100, N, dtype))["vpl"] not in ("5", "10")
 
 
 def test_every_row_fits_its_tile():

@@ -155,7 +155,7 @@ def test_forced_split_path(monkeypatch, op, dtype, N, mode):
     compare(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, y, mean, rstd, what=f"split N={N}")
 
 
-TILES = [(t, v) for t in (4, 8, 16, 32, 64, 128, 256, 512, 1024) for v in (1, 2, 4, 8, 16)]
+TILES = [(t, v) for t in (4, 8, 16, 32, 64, 128, 256, 512, 1024) for v in (1, 2, 4, 8, 16)] + [(64, 5), (64, 10)]
 
 
 @pytest.mark.parametrize("dtype,N", [("bf16", 4096), ("f32", 1000), ("f16", 2056)])
@@ -187,6 +187,33 @@ def test_unaligned_pointers(op, dtype):
     inp = inputs(op, dtype, M, N, seed=5)
     y, mean, rstd = run(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, offset=1)
     compare(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, y, mean, rstd, what="unaligned")
+
+
+@pytest.mark.parametrize("dtype,N", [("bf16", 5120), ("bf16", 2560), ("f32", 2560), ("f32", 1280), ("f16", 5120)])
+@pytest.mark.parametrize("M", [1, 1001, 4096])
+def test_one_wavefront_tiles(M, dtype, N):
+    """Rows of 320 or 640 16-byte vectors and at most 4096 rows take one
+    wavefront per row with 5 or 10 vectors per lane: every operation against
+    the oracle, ragged row counts included (4 rows per workgroup)."""
+    import rmsnorm_forward_amd as rn
+    e = 4 if dtype == "f32" else 2
+    d = dict(kv.split("=") for kv in rn.norm_describe("ln", M, N, dtype).split())
+    assert (d["team"], d["vpl"]) == ("64", str(N * e // 16 // 64)), d
+    rows = None if M <= 1001 else sample_rows(M, 64, seed=N)
+    what = f"one-wavefront {dtype} {M}x{N}"
+    print(f"[gpu] {what}", flush=True)
+    for op in ("ln", "rms"):
+        inp = inputs(op, dtype, M, N, seed=M + N)
+        y, mean, rstd = run(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5)
+        compare(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, y, mean, rstd, rows, what=f"{op} {what}")
+    inp = workloads.gen_add_rms(M + N, M, N, dtype)
+    y, h, rstd = gpu_runner.run_add(dtype, inp["x"], inp["res"], inp["gamma"], 1e-6)
+    compare_add(dtype, inp["x"], inp["res"], inp["gamma"], 1e-6, y, h, rstd, rows, what=f"add_rms {what}")
+    if rows is None:
+        for res in (None, inp["res"]):
+            q, hq, rq = gpu_runner.run_fp8(dtype, inp["x"], res, inp["gamma"], 1e-6, 1.0 / 64)
+            compare_fp8(dtype, inp["x"], res, inp["gamma"], 1e-6, 1.0 / 64, q, hq, rq,
+                        what=f"fp8 add={res is not None} {what}")
 
 
 @pytest.mark.parametrize("has_g,has_b", [(False, False), (True, False), (False, True)])
