@@ -80,6 +80,24 @@ __device__ __forceinline__ float vec_sum_shifted(const V& v, float K) {
 // read into registers by the lane that later writes it, before it writes.
 // Q8 (RMSNorm only): y is FP8 E4M3 codes of (the normalised value * qinv),
 // one byte per element, instead of the I/O dtype.
+//
+// Two memory schedules, fixed per (operation, team) by measurement on MI355X
+// (steady state, 200 launches, us):
+//   hoisted (RMSNorm, teams of at most 256 lanes): every load of the row (x,
+//     the residual, gamma) is issued before any arithmetic, unconditionally,
+//     from an address clamped into the row (a vector past the row's end
+//     reads the row's last vector, a row past M reads row M - 1; those values
+//     are never used), and only the stores are masked, so no load waits
+//     behind a branch or a store.  RMS bf16 65536 x 2048 64x4: 84.8 vs 87.6;
+//     fp32 65536 x 2048 256x2: 171.5 vs 175.0; 2 rows per wavefront (bf16
+//     32x8) 86.4 vs 100.5.
+//   interleaved (LayerNorm; RMSNorm teams of 512+ lanes): x loaded under the
+//     per-vector mask, gamma / beta loaded vector by vector in the output
+//     loop, each vector's loads waited for (with the previous vector's store)
+//     just before it is computed and stored.  LN bf16 16384 x 8192 256x4: 89.0
+//     vs 93.0 with gamma / beta hoisted before the statistics (their 32 VGPRs
+//     cost a wave per SIMD) and 98.7 hoisted after them; RMS fp32 8192 x 4096
+//     512x2: 44.0 vs 44.9.
 template <class T, bool RMS, bool ADD, bool Q8, int TEAM, int VPL, int EPV>
 __global__ __launch_bounds__(TeamGeom<TEAM>::WG)
 void norm_rows_kernel(const typename T::storage* x,
@@ -99,6 +117,7 @@ void norm_rows_kernel(const typename T::storage* x,
     using V = Vec<T, EPV>;
     constexpr int E = VPL * EPV;               // elements per lane
     constexpr bool CACHE_F32 = E <= MI355_CACHE_F32_MAX;
+    constexpr bool HOIST = RMS && TEAM <= 256;
 
     // cross-wavefront exchange slots: two sets, one float per wavefront
     __shared__ float red[2][G::ROWS][G::WPT];
@@ -112,36 +131,56 @@ void norm_rows_kernel(const typename T::storage* x,
     const bool has_g = gamma != nullptr;
     const bool has_b = beta != nullptr;
 
+    // this lane's vectors: in-row flags and (hoisted schedule) element
+    // offsets clamped into the row; the same for every row
+    bool vin[VPL];
+    unsigned off[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+        const int v = j * TEAM + tl;
+        vin[j] = v < NV;
+        off[j] = (unsigned)(vin[j] || !HOIST ? v : NV - 1) * EPV;
+    }
+
     const int64_t groups = (M + G::ROWS - 1) / G::ROWS;
     int par = 0;    // RMS alternates LDS slot sets between iterations
     for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x, par ^= 1) {
         const int64_t row = grp * G::ROWS + team;
         const bool row_ok = row < M;
         // row bases (wavefront-uniform when TEAM >= 64) plus 32-bit lane offsets
-        const int64_t rr = row_ok ? row : 0;
+        const int64_t rr = row_ok ? row : (HOIST ? M - 1 : 0);
         const S* xr = x + rr * ld.x;
         S* yr = static_cast<S*>(yv) + rr * ld.y;
         uint8_t* yq = static_cast<uint8_t*>(yv) + rr * ld.y;
 
         V xv[VPL];
         bool ok[VPL];
+        V gl[HOIST ? VPL : 1];
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
-            const unsigned v = (unsigned)(j * TEAM + tl);
-            ok[j] = row_ok && (int)v < NV;
-            if (ok[j]) xv[j].load_stream(xr + v * EPV);   // masked vectors stay undefined:
-        }                                                 // every use below is masked per vector
+            ok[j] = row_ok && vin[j];
+            if (HOIST || ok[j]) xv[j].load_stream(xr + off[j]);   // masked vectors: never used
+        }
         if constexpr (ADD) {
             V rv[VPL];
 #pragma unroll
             for (int j = 0; j < VPL; ++j)
-                if (ok[j]) rv[j].load_stream(res + rr * ld.r + (unsigned)(j * TEAM + tl) * EPV);
+                if (HOIST || ok[j]) rv[j].load_stream(res + rr * ld.r + off[j]);
+            if constexpr (HOIST) {
+#pragma unroll
+                for (int j = 0; j < VPL; ++j)
+                    if (has_g) gl[j].load(gamma + off[j]);
+            }
 #pragma unroll
             for (int j = 0; j < VPL; ++j) {
-                if (!ok[j]) continue;
+                if (!HOIST && !ok[j]) continue;
                 add_into(xv[j], rv[j]);
-                xv[j].put_stream(hout + rr * ld.h + (unsigned)(j * TEAM + tl) * EPV);
+                if (ok[j]) xv[j].put_stream(hout + rr * ld.h + off[j]);
             }
+        } else if constexpr (HOIST) {
+#pragma unroll
+            for (int j = 0; j < VPL; ++j)
+                if (has_g) gl[j].load(gamma + off[j]);
         }
         float rs, mu = 0.0f, K = 0.0f;
         float d[CACHE_F32 ? VPL : 1][EPV];
@@ -218,11 +257,11 @@ void norm_rows_kernel(const typename T::storage* x,
             constexpr bool HB = !RMS && decltype(hb)::value;
 #pragma unroll
             for (int j = 0; j < VPL; ++j) {
-                if (!ok[j]) continue;
-                const unsigned off = (unsigned)(j * TEAM + tl) * EPV;
-                V gl, bl;
-                if constexpr (HG) gl.load(gamma + off);
-                if constexpr (HB) bl.load(beta + off);
+                if (!HOIST && !ok[j]) continue;
+                V gv, bl;
+                if constexpr (HG && !HOIST) gv.load(gamma + off[j]);
+                if constexpr (HB) bl.load(beta + off[j]);
+                const V& g = HOIST ? gl[j] : gv;
                 float o[EPV];
 #pragma unroll
                 for (int k = 0; k < EPV; ++k) {
@@ -230,15 +269,16 @@ void norm_rows_kernel(const typename T::storage* x,
                     if constexpr (RMS) t = xv[j].get(k) * rsy;
                     else if constexpr (CACHE_F32) t = d[j][k] * rs;
                     else t = ((xv[j].get(k) - K) - mu) * rs;
-                    if constexpr (HG && HB) o[k] = __builtin_fmaf(t, gl.get(k), bl.get(k));
-                    else if constexpr (HG) o[k] = t * gl.get(k);
+                    if constexpr (HG && HB) o[k] = __builtin_fmaf(t, g.get(k), bl.get(k));
+                    else if constexpr (HG) o[k] = t * g.get(k);
                     else if constexpr (HB) o[k] = t + bl.get(k);
                     else o[k] = t;
                 }
+                if (HOIST && !ok[j]) continue;
                 if constexpr (Q8) {
-                    store_e4m3<EPV>(yq + off, o);
+                    store_e4m3<EPV>(yq + off[j], o);
                 } else {
-                    V::store(yr + off, o);
+                    V::store(yr + off[j], o);
                 }
             }
         };
