@@ -111,7 +111,9 @@ typedef enum {
     NORM_ERR_BAD_ARG = 5,    /* misaligned pointer; beta or mean given to an
                                 RMSNorm; a bad FP8 scale                      */
     NORM_ERR_ALIAS = 6,      /* two of the buffers overlap                       */
-    NORM_ERR_HIP = 7         /* a HIP runtime call or kernel launch failed       */
+    NORM_ERR_HIP = 7,        /* a HIP runtime call or kernel launch failed       */
+    NORM_ERR_SCRATCH = 8     /* norm_fwd_noalloc: the call needs more scratch
+                                than its fixed buffer holds                    */
 } norm_status;
 
 /* LayerNorm forward.  Returns a norm_status. */
@@ -203,6 +205,26 @@ typedef struct {
  * their whole spans otherwise.  Returns a norm_status.
  */
 int norm_fwd(const norm_args *args, void *stream);
+
+/*
+ * norm_fwd without any allocation, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, conventions and results as norm_fwd
+ * (the very same kernels), but rows too long for one workgroup keep their
+ * per-chunk partial statistics in a fixed 1 MiB device array that the
+ * library holds on every GPU it runs on until the process exits (its address
+ * is looked up on the first call on each device, with that device current),
+ * instead of in a workspace it allocates.  That covers every shape of the
+ * default two-kernel schedule (at most about 576 KiB of partials per batch
+ * of rows); a call needing more (a larger MI355NORM_SPLIT_BATCH) returns
+ * NORM_ERR_SCRATCH, and the single-pass schedule (MI355NORM_PATH=splitcoop)
+ * NORM_ERR_BAD_ARG, both before any launch.  No hipMalloc, hipFree or
+ * allocating routine is called.  Calls on one GPU share the array: calls
+ * that overlap in time on one GPU (different streams, or graph replays
+ * overlapping eager calls) race on it and must be ordered by the caller.
+ * Returns a norm_status.
+ */
+int norm_fwd_noalloc(const norm_args *args, void *stream);
 
 /*
  * Backward of ln_fwd and rms_fwd ("CUDA 算子工程" ch. 7, section 7.7), from

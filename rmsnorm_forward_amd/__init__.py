@@ -6,7 +6,8 @@ only marshals arguments.  PyTorch is used for device memory and streams.
 
 Two layers:
   * ln_fwd / rms_fwd / add_rms_fwd / rms_fp8_fwd / add_rms_fp8_fwd /
-    norm_fwd (row strides) / ln_bwd / rms_bwd / norm_bwd (row strides) /
+    norm_fwd (row strides) / norm_fwd_noalloc (the same, allocating
+    nothing) / ln_bwd / rms_bwd / norm_bwd (row strides) /
     norm_status_str /
     norm_last_error / norm_describe / norm_bwd_describe -- the C ABI entry
     points under the same names, taking raw device addresses (ints) and
@@ -72,9 +73,11 @@ _lib.norm_bwd_describe.restype = _int
 
 NORM_F32, NORM_F16, NORM_BF16 = 0, 1, 2
 NORM_OK = 0
-NORM_ERR_HIP = 7
+NORM_ERR_NULL_ARG, NORM_ERR_BAD_SHAPE, NORM_ERR_BAD_DTYPE, NORM_ERR_BAD_EPS = 1, 2, 3, 4
+NORM_ERR_BAD_ARG, NORM_ERR_ALIAS, NORM_ERR_HIP, NORM_ERR_SCRATCH = 5, 6, 7, 8
 STATUS = {0: "NORM_OK", 1: "NORM_ERR_NULL_ARG", 2: "NORM_ERR_BAD_SHAPE", 3: "NORM_ERR_BAD_DTYPE",
-          4: "NORM_ERR_BAD_EPS", 5: "NORM_ERR_BAD_ARG", 6: "NORM_ERR_ALIAS", 7: "NORM_ERR_HIP"}
+          4: "NORM_ERR_BAD_EPS", 5: "NORM_ERR_BAD_ARG", 6: "NORM_ERR_ALIAS", 7: "NORM_ERR_HIP",
+          8: "NORM_ERR_SCRATCH"}
 DTYPE_NAMES = {"f32": NORM_F32, "f16": NORM_F16, "bf16": NORM_BF16}
 
 
@@ -153,6 +156,21 @@ def norm_fwd(op, dtype, M, N, x, y, *, ld_x=0, residual=None, ld_residual=0, gam
                  _addr(residual), int(ld_residual), _addr(gamma), _addr(beta), _addr(y), int(ld_y),
                  _addr(residual_out), int(ld_residual_out), _addr(mean), _addr(rstd), float(eps), float(scale))
     return _lib.norm_fwd(ctypes.byref(a), _addr(stream))
+
+
+_lib.norm_fwd_noalloc.argtypes = [ctypes.POINTER(NormArgs), _vp]
+_lib.norm_fwd_noalloc.restype = _int
+
+
+def norm_fwd_noalloc(op, dtype, M, N, x, y, *, ld_x=0, residual=None, ld_residual=0, gamma=None, beta=None,
+                     ld_y=0, residual_out=None, ld_residual_out=0, mean=None, rstd=None, eps=1e-5, scale=1.0,
+                     stream=None) -> int:
+    """norm_fwd that allocates nothing (split rows use the library's fixed
+    scratch); same arguments; returns the norm_status code."""
+    a = NormArgs(OPS.get(op, op), DTYPE_NAMES.get(dtype, dtype), int(M), int(N), _addr(x), int(ld_x),
+                 _addr(residual), int(ld_residual), _addr(gamma), _addr(beta), _addr(y), int(ld_y),
+                 _addr(residual_out), int(ld_residual_out), _addr(mean), _addr(rstd), float(eps), float(scale))
+    return _lib.norm_fwd_noalloc(ctypes.byref(a), _addr(stream))
 
 
 class NormBwdArgs(ctypes.Structure):

@@ -426,6 +426,35 @@ bool stream_workspace(hipStream_t stream, size_t sync_words, size_t part_bytes, 
     return true;
 }
 
+// Scratch of the allocation-free entry point (norm_fwd_noalloc): the
+// partials of the two-kernel split, in a fixed array every GPU the library
+// runs on holds until the process ends.  Calls of that entry point on one GPU
+// share it, so calls that overlap on one GPU race.  In host code `scratch`
+// names a host-side stand-in; kernels get the device address looked up below.
+constexpr size_t kScratchBytes = size_t(1) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// The device address of `scratch` on the current device, looked up once per
+// device (that device current) and kept; nullptr (norm_last_error set) on
+// failure.
+void* scratch_address() {
+    static std::mutex mu;
+    static void* addr[64];
+    int dev = 0;
+    if (!hip_ok(hipGetDevice(&dev), "hipGetDevice")) return nullptr;
+    if (dev < 0 || dev >= 64) {
+        std::snprintf(g_last_error, sizeof g_last_error, "device %d: scratch is kept for devices 0..63", dev);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        if (!hip_ok(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress (scratch)")) return nullptr;
+        addr[dev] = p;
+    }
+    return addr[dev];
+}
+
 // The 16-byte vector path: every matrix row and vector starts on a vector
 // boundary of its own type, and N fills whole vectors.
 bool vector_aligned(const Args& a) {
@@ -440,7 +469,10 @@ bool vector_aligned(const Args& a) {
     return al(a.y, 16) && (a.ldy * e) % 16 == 0;
 }
 
-int run(const Args& a, void* stream) {
+// noalloc: the two-kernel split's partials go to `scratch` (no allocation
+// anywhere on the call's path); a call that needs more than it holds, or the
+// single pass, is refused before any launch.
+int run(const Args& a, void* stream, bool noalloc = false) {
     int st = validate(a);
     if (st != NORM_OK || a.M == 0) return st;
     const int op = a.op, dtype = a.dtype;
@@ -470,8 +502,16 @@ int run(const Args& a, void* stream) {
     const unsigned spin = o.force_timeout ? 64u : o.spin_limit;
     Workspace w;
     const size_t sync_words = coop ? size_t(rows) * kSyncStride : 0;
-    if (!stream_workspace(c.stream, sync_words, size_t(rows) * size_t(p.chunks) * sizeof(float2), &w))
+    const size_t part_bytes = size_t(rows) * size_t(p.chunks) * sizeof(float2);
+    if (noalloc) {
+        if (coop) return NORM_ERR_BAD_ARG;
+        if (part_bytes > kScratchBytes) return NORM_ERR_SCRATCH;
+        void* base = scratch_address();
+        if (!base) return NORM_ERR_HIP;
+        w = Workspace{nullptr, static_cast<float2*>(base)};
+    } else if (!stream_workspace(c.stream, sync_words, part_bytes, &w)) {
         return NORM_ERR_HIP;
+    }
     float2* part = w.part;
     if (coop) {
         unsigned* sync = w.sync;
@@ -792,6 +832,15 @@ int norm_fwd(const norm_args* args, void* stream) {
     return run(a, stream);
 }
 
+int norm_fwd_noalloc(const norm_args* args, void* stream) {
+    if (!args) return NORM_ERR_NULL_ARG;
+    const norm_args& g = *args;
+    auto ld = [&](int64_t v) { return v == 0 ? g.N : v; };
+    Args a{g.op, g.dtype, g.M, g.N, g.x, g.residual, g.gamma, g.beta, g.y, g.residual_out, g.mean, g.rstd,
+           g.eps, g.scale, ld(g.ld_x), ld(g.ld_residual), ld(g.ld_y), ld(g.ld_residual_out)};
+    return run(a, stream, true);
+}
+
 int ln_fwd(const void* x, const void* gamma, const void* beta, void* y, float* mean, float* rstd,
            int64_t M, int64_t N, float eps, int dtype, void* stream) {
     return run(Args{OP_LN, dtype, M, N, x, nullptr, gamma, beta, y, nullptr, mean, rstd, eps, 1.0f, N, N, N, N},
@@ -879,6 +928,8 @@ const char* norm_status_str(int status) {
     case NORM_ERR_BAD_ARG: return "bad argument: misaligned pointer, beta/mean given to an RMSNorm, a bad FP8 scale, or an unusable override";
     case NORM_ERR_ALIAS: return "buffers overlap (in-place use is not supported)";
     case NORM_ERR_HIP: return "HIP runtime call or kernel launch failed";
+    case NORM_ERR_SCRATCH:
+        return "the call needs more than the 1 MiB fixed scratch of norm_fwd_noalloc (use norm_fwd)";
     }
     return "unknown status";
 }

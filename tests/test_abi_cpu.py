@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["add_rms_fp8_fwd", "add_rms_fwd", "ln_bwd", "ln_fwd", "norm_bwd",
-                                    "norm_bwd_describe", "norm_describe", "norm_fwd", "norm_last_error",
+                                    "norm_bwd_describe", "norm_describe", "norm_fwd", "norm_fwd_noalloc", "norm_last_error",
                                     "norm_status_str", "rms_bwd", "rms_fp8_fwd", "rms_fwd"]
 
 
@@ -53,7 +53,7 @@ def test_one_hip_runtime_in_the_process():
 
 
 def test_status_strings():
-    for code in range(8):
+    for code in range(9):
         s = rn.norm_status_str(code)
         assert s and s != "unknown status"
     assert rn.norm_status_str(99) == "unknown status"
@@ -530,3 +530,29 @@ def test_bwd_strides_are_validated():
 def test_bwd_strided_plans_need_aligned_rows():
     assert "epv=8" in rn.norm_bwd_describe("ln", 64, 1024, "bf16", True)
     assert "epv=1" in rn.norm_bwd_describe("ln", 64, 1024, "bf16", False)
+
+
+def test_noalloc_validates_and_refuses_on_the_host(monkeypatch):
+    """norm_fwd_noalloc: the same validation as norm_fwd, and the refusals of
+    what its fixed scratch cannot hold, all before any HIP call."""
+    assert rn._lib.norm_fwd_noalloc(None, None) == NULL_ARG
+    fake = 1 << 40   # never dereferenced: every case below returns before a launch
+    assert rn.norm_fwd_noalloc("ln", "bf16", 0, 1024, None, None) == OK
+    assert rn.norm_fwd_noalloc("ln", 7, 4, 1024, fake, fake + (1 << 30)) == BAD_DTYPE
+    assert rn.norm_fwd_noalloc("ln", "bf16", 4, 1024, fake, fake + 1024) == ALIAS
+    # a forced split of 2^20 short rows needs 8 MiB of partials in one batch
+    monkeypatch.setenv("MI355NORM_PATH", "split")
+    assert rn.norm_fwd_noalloc("rms", "f32", 1 << 20, 64, fake, fake + (1 << 30), eps=1e-6) == 8
+    monkeypatch.setenv("MI355NORM_PATH", "splitcoop")
+    assert rn.norm_fwd_noalloc("rms", "f32", 40, 100000, fake, fake + (1 << 30), eps=1e-6) == BAD_ARG
+
+
+@pytest.mark.parametrize("dtype,N,aligned", [("bf16", 16385, False), ("f32", 16385, False), ("bf16", 65544, True),
+                                             ("f32", 32772, True), ("bf16", 1 << 20, True), ("f16", 1 << 24, True)])
+def test_noalloc_scratch_holds_every_default_split_batch(dtype, N, aligned):
+    """The largest partials of the default two-kernel schedule (rows of one
+    batch x chunks per row x 8 bytes) fit the 1 MiB scratch: the worst case is
+    the shortest split rows of a 2-byte type on the element-wise path."""
+    d = dict(kv.split("=") for kv in rn.norm_describe("ln", 1 << 30, N, dtype, aligned=aligned).split())
+    assert d["path"] == "split" and d["mode"] == "two"
+    assert int(d["batch_rows"]) * int(d["chunks"]) * 8 <= 1 << 20
