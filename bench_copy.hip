@@ -1,8 +1,10 @@
-// bench_copy.hip -- a plain device copy of known size, used by bench.py only:
-// (1) as the copy ceiling the norm kernels are compared with, and (2) to
+// bench_copy.hip -- plain device streams of known size, used by bench.py only:
+// (1) as the ceilings the norm kernels are compared with (a copy of x's bytes
+// into y, and read-only / write-only streams of the same bytes), and (2) to
 // calibrate rocprofv3's FETCH_SIZE / WRITE_SIZE counters (bytes counted per
 // byte actually moved).  One 16-byte vector per lane, one workgroup of 256
-// lanes per 4 KiB, cached loads and stores: the simplest streaming kernel.
+// lanes per 4 KiB: the simplest streaming kernels, with ordinary (cached) or
+// nontemporal accesses.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -14,15 +16,49 @@ __global__ __launch_bounds__(256) void plain_copy16(const u32x4* __restrict__ sr
     if (i < n16) dst[i] = src[i];
 }
 
-// bytes must be a multiple of 16 and both pointers 16-byte aligned.
-// Returns 0 on success, 1 on a bad argument, 2 if the launch failed.
-extern "C" int bench_plain_copy(const void* src, void* dst, uint64_t bytes, void* stream) {
-    if (!src || !dst || bytes % 16 || ((uintptr_t)src & 15) || ((uintptr_t)dst & 15)) return 1;
+__global__ __launch_bounds__(256) void nt_copy16(const u32x4* __restrict__ src,
+                                                 u32x4* __restrict__ dst, uint64_t n16) {
+    const uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n16) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
+// reads every vector; writes one only if its four words XOR to a value the
+// caller's data never holds (the store keeps the loads from being removed)
+__global__ __launch_bounds__(256) void nt_read16(const u32x4* __restrict__ src,
+                                                 u32x4* __restrict__ dst, uint64_t n16) {
+    const uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n16) {
+        const u32x4 v = __builtin_nontemporal_load(src + i);
+        if ((v.x ^ v.y ^ v.z ^ v.w) == 0x9e3779b9u && v.x == 0x7f800001u) dst[i] = v;
+    }
+}
+
+__global__ __launch_bounds__(256) void nt_write16(const u32x4* __restrict__ src,
+                                                  u32x4* __restrict__ dst, uint64_t n16) {
+    const uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n16) __builtin_nontemporal_store(u32x4{(unsigned)i, 0u, 0u, 0u}, dst + i);
+}
+
+// kind: 0 cached copy, 1 nontemporal copy, 2 nontemporal read of src (dst is
+// only written where the impossible value above occurs), 3 nontemporal write
+// of dst (src unused).  bytes must be a multiple of 16 and both pointers
+// 16-byte aligned.  Returns 0 on success, 1 on a bad argument, 2 if the
+// launch failed.
+extern "C" int bench_stream(int kind, const void* src, void* dst, uint64_t bytes, void* stream) {
+    if (kind < 0 || kind > 3 || !src || !dst || bytes % 16 || ((uintptr_t)src & 15) || ((uintptr_t)dst & 15))
+        return 1;
     const uint64_t n16 = bytes / 16;
     if (n16 == 0) return 0;
     const uint64_t blocks = (n16 + 255) / 256;
     if (blocks > 0xffffffffull) return 1;
-    hipLaunchKernelGGL(plain_copy16, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+    void (*k)(const u32x4*, u32x4*, uint64_t) =
+        kind == 0 ? plain_copy16 : kind == 1 ? nt_copy16 : kind == 2 ? nt_read16 : nt_write16;
+    hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
                        static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16);
     return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// the cached copy (kind 0), the counter calibration reference
+extern "C" int bench_plain_copy(const void* src, void* dst, uint64_t bytes, void* stream) {
+    return bench_stream(0, src, dst, bytes, stream);
 }

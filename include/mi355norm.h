@@ -75,15 +75,20 @@
  * are processed in batches of rows holding about 256 MiB of x, two kernel
  * launches per batch, and use a library-owned device workspace of at most a
  * few MiB (per row of a batch: 264 bytes plus 8 bytes per chunk of the row),
- * one per (device, stream), allocated on first need, grown when a larger
- * call needs it (the only time a call waits for its stream), and kept until
- * the process exits.
+ * one per (device, stream), allocated on first need and replaced by a larger
+ * one when a larger call needs it (no call waits for its stream); every
+ * workspace is kept until the process exits.
  *
  * Graph capture: calls on the row path launch kernels only.  Calls that use
  * the workspace (long rows, and the backward below) may be captured into a
  * HIP graph once a call at least as large has run on the capturing stream
  * (the workspace then exists, and a capture records kernel launches only:
- * no allocation, synchronisation or memset).
+ * no allocation, synchronisation or memset).  A captured call keeps the
+ * workspace it was captured with, which stays valid after later, larger
+ * calls; its replays share it with the calls on the capturing stream and
+ * with the other replays of graphs captured there, so none of those may
+ * overlap in time (order them, e.g. replay on the capturing stream).  See
+ * also norm_fwd_noalloc.
  *
  * Errors: arguments are validated on the host before any HIP call; a bad
  * argument returns its status and touches nothing.  A launch failure returns

@@ -54,6 +54,7 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "../../include/mi355norm.h"
 #include "dispatch.hpp"
@@ -375,8 +376,10 @@ int make_plan(int op, int64_t M, int64_t N, int dtype, bool aligned, const Overr
 // the per-chunk partials.  Everything is zero when allocated, and the
 // single-pass kernel leaves every counter it used at zero when it finishes,
 // so counters are zero at the start of every call whatever its shape.
-// Growing (only on a new largest call) waits for the stream, since the old
-// buffer may still be in use, and reallocates both regions.
+// Growing (only on a new largest call) allocates a larger buffer and keeps the
+// old one until the process exits: work already queued on the stream, and any
+// HIP graph captured with it, go on using the old buffer, so nothing waits and
+// no captured pointer dangles.
 struct Workspace {
     unsigned* sync;   // single pass: >= 64 counters per row of a launch
     float2* part;     // >= rows * chunks partials
@@ -396,15 +399,13 @@ bool stream_workspace(hipStream_t stream, size_t sync_words, size_t part_bytes, 
     struct Buf { void* ptr; size_t sync_words; size_t part_bytes; };   // sync_words >= 64 * M
     static std::mutex mu;
     static std::map<std::pair<int, hipStream_t>, Buf> bufs;
+    static std::vector<void*> retired;   // outgrown workspaces, never freed
     int dev = 0;
     if (!hip_ok(hipGetDevice(&dev), "hipGetDevice")) return false;
     std::lock_guard<std::mutex> lock(mu);
     Buf& b = bufs[{dev, stream}];
     if (!b.ptr || b.sync_words < sync_words || b.part_bytes < part_bytes) {
-        if (b.ptr) {
-            if (!hip_ok(hipStreamSynchronize(stream), "hipStreamSynchronize (workspace growth)")) return false;
-            (void)hipFree(b.ptr);   // the stream is idle: nothing uses it any more
-        }
+        if (b.ptr) retired.push_back(b.ptr);
         const size_t sw = std::max({sync_words, 2 * b.sync_words, size_t(4096)});
         const size_t pb = std::max({part_bytes, 2 * b.part_bytes, size_t(1) << 20});
         const size_t sync_bytes = (sw * sizeof(unsigned) + 255) & ~size_t(255);

@@ -102,3 +102,37 @@ def test_source_digest_ignores_comments_only():
     b = "/* header\n   text */\nint f(int x) {\n\n    return x + 1;   // two\n}\n"
     c = "int f(int x) {\n    return x + 2;\n}\n"
     assert bench._code_only(a) == bench._code_only(b) != bench._code_only(c)
+
+
+def test_ceiling_streams_refuse_buffers_smaller_than_x_before_any_launch():
+    """The ceiling streams copy x's bytes; y of FP8 codes is a quarter (bf16: a
+    half) of them, so handing it over must fail on the host, before a launch."""
+    import torch
+    x = [torch.empty(4096, dtype=torch.bfloat16) for _ in range(2)]
+    nbytes = x[0].numel() * x[0].element_size()
+    y_fp8 = [torch.empty(4096, dtype=torch.uint8) for _ in range(2)]
+    launched = []
+
+    class Lib:
+        def bench_stream(self, *a):
+            launched.append(a)
+            return 0
+
+    try:
+        bench.stream_ceilings(Lib(), x, y_fp8, nbytes, None, 1)
+    except ValueError as e:
+        assert "smaller" in str(e)
+    else:
+        raise AssertionError("FP8-sized destinations were accepted")
+    assert not launched
+    bench.check_stream_buffers(x, [torch.empty_like(t) for t in x], nbytes)   # x-sized: accepted
+
+
+def test_cpu_baseline_reports_the_median_of_three_passes_and_the_cpu():
+    w = workloads.Workload("t", "rms", "f32", 32, 512, 1e-6, 0, "")
+    rng = np.random.default_rng(1)
+    inp = {"x": rng.standard_normal((32, 512)).astype(np.float32), "gamma": np.ones(512, np.float32)}
+    cb = bench.cpu_baseline(w, inp, seconds=3.0)
+    assert cb["runs"] == 3 and len(cb["run_seconds"]) == 3
+    assert cb["cpu_model"] and "median of 3 passes" in cb["sample"]
+    assert 1 <= bench.host_cores() <= 16

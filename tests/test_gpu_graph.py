@@ -71,3 +71,38 @@ def test_capture_and_replay_forward_split_and_backward():
         junk = rn.layer_norm(x, g, be, 1e-5)[0]
         torch.cuda.synchronize()
         del junk
+
+
+def test_replay_after_a_larger_eager_call_grew_the_workspace():
+    """A graph captured with the split path's workspace keeps using it after a
+    larger eager call on the capturing stream replaced it: the old workspace
+    is never freed, so the replays still give the eager bits."""
+    dev = lambda a: gpu_runner.to_device(a, "bf16")
+    small = workloads.gen_ln_normal(411, 2, 100000, "bf16")
+    big = workloads.gen_ln_normal(412, 40, 200000, "bf16")
+    xs, gs, bs = dev(small["x"]).view(2, 100000), dev(small["gamma"]), dev(small["beta"])
+    xb, gb, bb = dev(big["x"]).view(40, 200000), dev(big["gamma"]), dev(big["beta"])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        eager = [t.clone() for t in rn.layer_norm(xs, gs, bs, 1e-5)]   # workspace for the small call
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    print("[gpu] capturing the small split call", flush=True)
+    with torch.cuda.graph(graph, stream=s):
+        static = rn.layer_norm(xs, gs, bs, 1e-5)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        with torch.cuda.stream(s):
+            yb, _, rb = rn.layer_norm(xb, gb, bb, 1e-5)     # larger: a new workspace for s
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(rb).all())
+        for t in static:
+            t.fill_(float("nan"))
+        with torch.cuda.stream(s):
+            graph.replay()
+        torch.cuda.synchronize()
+        for k, (a, e) in enumerate(zip(static, eager)):
+            assert torch.equal(bits(a), bits(e)), f"replay {rep}: output {k} differs from the eager result"
+        del yb, rb
