@@ -12,18 +12,14 @@
 //               N <= 32768): 64..1024 lanes per row, one LDS exchange per
 //               reduction across the row's wavefronts;
 //   long rows   (beyond 1024 lanes x 8 vectors): split across workgroups
-//               in chunks of 256 lanes x 8 vectors; per-chunk partial
-//               statistics merged in chunk order (Chan).  Two kernels per
-//               batch of rows holding about 256 MiB of x: partials (x read
-//               through the caches), then merge + normalise (x re-read,
-//               mostly from the Infinity Cache).  A single pass (cooperative
-//               launch, per-row barrier, x read once, each workgroup loading
-//               its next row's chunk while it waits) is available on
-//               request: faster for large RMSNorm inputs (bf16 256 x 2^20
-//               209 us vs 240, fp32 256 x 2^20 367 vs 478), slower for
-//               LayerNorm bf16 (64 x 2^20: 93 vs 66), and its per-row wait
-//               depends on all of a row's workgroups running at once, which
-//               the two-kernel form does not.
+//               in chunks; per-chunk partial statistics merged in chunk order
+//               (Chan).  Two kernels per batch of rows holding about 256 MiB
+//               of x: partials (x read through the caches), then merge +
+//               normalise (x read again, partly from the Infinity Cache).  A
+//               single pass (ordinary launch, x read once; every chunk's
+//               partial published in the row's slots, a bounded wait for the
+//               row's other chunks, recomputing the row's partials from x when
+//               the wait runs out) is available on request.
 // Measured on MI355X in steady state (200 back-to-back launches): bf16
 // 1024-wide RMSNorm 32x4 (2 rows per wavefront) 85.3 us vs 64x2 87.1, 16x8
 // 95.1; bf16 2048-wide 64x4 87.6 vs 32x8 99.4; fp32 2048-wide 256x2 175.0
@@ -31,18 +27,27 @@
 // lane, or 4-lane teams, always lost.
 //
 // Test/benchmark hooks (environment, read per call):
-//   MI355NORM_PATH = rows | split | split2 | splitcoop
+//   MI355NORM_PATH = rows | split | split2 | split1 | splitcoop
 //                                       force the path (rows only if it fits;
-//                                       splitcoop only if a row fits resident;
-//                                       for the backward, split and split2
-//                                       take the three-kernel split, splitcoop
-//                                       its single cooperative pass)
+//                                       split2 the two-kernel split; split1 or
+//                                       splitcoop the single pass, only if a
+//                                       row's chunks fit resident, and not for
+//                                       the residual add, which keeps two
+//                                       kernels; for the backward, split and
+//                                       split2 take the three-kernel split,
+//                                       splitcoop its single cooperative pass)
 //   MI355NORM_SPLIT_BATCH = <bytes>     bytes of x per two-kernel split batch
 //                                       (of dy and x in the split backward)
 //   MI355NORM_TILE = <team>x<vpl>       force the row-kernel tile
 //   MI355NORM_GRID = <n>                cap the number of workgroups
-//   MI355NORM_SPIN_LIMIT = <n>          bound of the single-pass split's wait
-//   MI355NORM_FORCE_TIMEOUT = 1         make that wait time out (failure-path test)
+//   MI355NORM_SPIN_LIMIT = <n>          bound of the backward single pass's wait
+//   MI355NORM_WAIT_TICKS = <n>          bound of the forward single pass's wait
+//                                       (100 MHz ticks)
+//   MI355NORM_STAGGER = <n>             start delay of the second half of the
+//                                       forward single pass's teams (ticks)
+//   MI355NORM_FORCE_TIMEOUT = 1         make the single passes' waits run out
+//                                       (forward: recompute at once; backward:
+//                                       the failure path)
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -192,6 +197,8 @@ struct Overrides {
     int team = 0, vpl = 0;
     int64_t grid = 0;
     unsigned spin_limit = 1u << 20;
+    unsigned wait_ticks = 100000;   // forward single pass: 1 ms
+    unsigned stagger = 0;
     bool force_timeout = false;
     int64_t batch_bytes = 0;  // two-kernel split: bytes of x per batch (0: default)
 };
@@ -202,10 +209,16 @@ Overrides read_overrides() {
         if (!std::strcmp(s, "rows")) o.path = PATH_ROWS;
         else if (!std::strcmp(s, "split")) o.path = PATH_SPLIT;
         else if (!std::strcmp(s, "split2")) { o.path = PATH_SPLIT; o.split_mode = SPLIT_TWO; }
-        else if (!std::strcmp(s, "splitcoop")) { o.path = PATH_SPLIT; o.split_mode = SPLIT_COOP; }
+        else if (!std::strcmp(s, "splitcoop") || !std::strcmp(s, "split1")) {
+            o.path = PATH_SPLIT;
+            o.split_mode = SPLIT_COOP;   // the single pass (forward: SPLIT_PASS)
+        }
     }
     if (const char* s = std::getenv("MI355NORM_SPIN_LIMIT")) o.spin_limit = (unsigned)std::strtoul(s, nullptr, 10);
     if (const char* s = std::getenv("MI355NORM_FORCE_TIMEOUT")) o.force_timeout = std::atoi(s) != 0;
+    if (const char* s = std::getenv("MI355NORM_WAIT_TICKS")) o.wait_ticks = (unsigned)std::strtoul(s, nullptr, 10);
+    if (const char* s = std::getenv("MI355NORM_STAGGER")) o.stagger = (unsigned)std::strtoul(s, nullptr, 10);
+    if (o.force_timeout) o.wait_ticks = 0;
     if (const char* s = std::getenv("MI355NORM_TILE")) {
         int t = 0, v = 0;
         if (std::sscanf(s, "%dx%d", &t, &v) == 2) { o.team = t; o.vpl = v; }
@@ -236,11 +249,11 @@ bool fwd_tile_instantiated(int team, int vpl) {
     return tile_instantiated(team, vpl);
 }
 
-// How many workgroups of the single-pass split kernel (bwd: of the single-
-// pass split backward) the current device can hold at once (0 if cooperative
-// launch is unavailable or no device is present).  Cached per (device, dtype,
-// op, vector width, direction).
-int64_t coop_capacity(int dtype, int op, int epv, bool bwd = false) {
+// How many workgroups of the forward's single-pass kernel (bwd: of the
+// backward's cooperative single pass) the current device can hold at once (0
+// if no device is present, or, for the backward, if cooperative launch is
+// unavailable).  Cached per (device, dtype, op, vector width, direction).
+int64_t resident_capacity(int dtype, int op, int epv, bool bwd = false) {
     static std::mutex mu;
     static int64_t cache[64][3][kOps][2][2];
     static bool known[64][3][kOps][2][2];
@@ -254,17 +267,18 @@ int64_t coop_capacity(int dtype, int op, int epv, bool bwd = false) {
     if (!known[dev][dtype][op][vi][bi]) {
         int coop = 0, cus = 0;
         int64_t cap = 0;
-        if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && coop &&
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) {
+        const bool launchable =
+            !bwd || (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && coop);
+        if (launchable && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) {
             int per_cu;
             if (bwd)
                 per_cu = dtype == NORM_F32 ? bwd_coop_blocks_per_cu_f32(op, epv)
                          : dtype == NORM_BF16 ? bwd_coop_blocks_per_cu_bf16(op, epv)
                                               : bwd_coop_blocks_per_cu_f16(op, epv);
             else
-                per_cu = dtype == NORM_F32 ? coop_blocks_per_cu_f32(op, epv)
-                         : dtype == NORM_BF16 ? coop_blocks_per_cu_bf16(op, epv)
-                                              : coop_blocks_per_cu_f16(op, epv);
+                per_cu = dtype == NORM_F32 ? pass_blocks_per_cu_f32(op, epv)
+                         : dtype == NORM_BF16 ? pass_blocks_per_cu_bf16(op, epv)
+                                              : pass_blocks_per_cu_f16(op, epv);
             cap = int64_t(per_cu) * cus;
         }
         cache[dev][dtype][op][vi][bi] = cap;
@@ -329,20 +343,19 @@ int make_plan(int op, int64_t M, int64_t N, int dtype, bool aligned, const Overr
         p->rows_per_wg = p->wg / team;
         p->work = (M + p->rows_per_wg - 1) / p->rows_per_wg;
     } else {
-        // Two kernels by default: they measure faster than the single pass
-        // here because x's second read is served by the Infinity Cache.  The
-        // single pass runs when asked for and every chunk of at least one row
-        // can be resident.
-        if (o.split_mode == SPLIT_COOP) {
-            const int64_t ccv = int64_t(kCoopWG) * kCoopVPL;
-            const int64_t cchunks = (NV + ccv - 1) / ccv;
-            const int64_t cap = coop_capacity(dtype, op, p->epv);
-            if (cap < cchunks) return NORM_ERR_BAD_ARG;
-            p->split_mode = SPLIT_COOP;
-            p->wg = kCoopWG;
-            p->vpl = kCoopVPL;
-            p->chunks = (int)cchunks;
-            p->teams = (int)std::min<int64_t>(M, cap / cchunks);
+        // Two kernels by default.  The single pass runs when asked for (not
+        // for the residual add, which keeps two kernels) and every chunk of
+        // at least one row can be resident.
+        if (o.split_mode == SPLIT_COOP && !has_add(op)) {
+            const int64_t pv = int64_t(kPassWG) * kPassVPL;
+            const int64_t pchunks = (NV + pv - 1) / pv;
+            const int64_t cap = resident_capacity(dtype, op, p->epv);
+            if (cap < pchunks) return NORM_ERR_BAD_ARG;
+            p->split_mode = SPLIT_PASS;
+            p->wg = kPassWG;
+            p->vpl = kPassVPL;
+            p->chunks = (int)pchunks;
+            p->teams = (int)std::min<int64_t>(M, cap / pchunks);
             p->batch_rows = M;
             p->work = M * p->chunks;
         } else {
@@ -361,7 +374,7 @@ int make_plan(int op, int64_t M, int64_t N, int dtype, bool aligned, const Overr
     }
     int64_t cap = o.grid > 0 ? o.grid : kMaxGrid;
     p->grid = p->work < cap ? p->work : cap;
-    if (p->path == PATH_SPLIT && p->split_mode == SPLIT_COOP) p->grid = int64_t(p->teams) * p->chunks;
+    if (p->path == PATH_SPLIT && p->split_mode == SPLIT_PASS) p->grid = int64_t(p->teams) * p->chunks;
     if (p->path == PATH_SPLIT && p->split_mode == SPLIT_TWO) {
         const int64_t aw = p->batch_rows * p->apply_chunks;
         p->apply_grid = aw < cap ? aw : cap;
@@ -494,18 +507,17 @@ int run(const Args& a, void* stream, bool noalloc = false) {
         }
         return hip_ok(err, "row kernel launch") ? NORM_OK : NORM_ERR_HIP;
     }
-    // split path: partials and counters live in the workspace this (device,
-    // stream) keeps
-    const bool coop = p.split_mode == SPLIT_COOP;
+    // split path: partials (two kernels) or the single pass's departure
+    // counters and slots live in the workspace this (device, stream) keeps
+    const bool pass = p.split_mode == SPLIT_PASS;
     const int64_t rows = p.batch_rows;   // rows per launch (two-kernel form: per pair)
     const Overrides o = read_overrides();
-    const unsigned need = (unsigned)p.chunks + (o.force_timeout ? 1u : 0u);
-    const unsigned spin = o.force_timeout ? 64u : o.spin_limit;
     Workspace w;
-    const size_t sync_words = coop ? size_t(rows) * kSyncStride : 0;
-    const size_t part_bytes = size_t(rows) * size_t(p.chunks) * sizeof(float2);
+    // single pass: rows x 64 counter words, then rows x chunks 8-byte slots
+    const size_t sync_words = pass ? size_t(rows) * (kSyncStride + 2 * size_t(p.chunks)) : 0;
+    const size_t part_bytes = pass ? 0 : size_t(rows) * size_t(p.chunks) * sizeof(float2);
     if (noalloc) {
-        if (coop) return NORM_ERR_BAD_ARG;
+        if (pass) return NORM_ERR_BAD_ARG;
         if (part_bytes > kScratchBytes) return NORM_ERR_SCRATCH;
         void* base = scratch_address();
         if (!base) return NORM_ERR_HIP;
@@ -514,12 +526,13 @@ int run(const Args& a, void* stream, bool noalloc = false) {
         return NORM_ERR_HIP;
     }
     float2* part = w.part;
-    if (coop) {
-        unsigned* sync = w.sync;
+    if (pass) {
+        unsigned* dep = w.sync;
+        auto* slots = reinterpret_cast<unsigned long long*>(w.sync + size_t(rows) * kSyncStride);
         switch (dtype) {
-        case NORM_F32: err = launch_split_coop_f32(op, c, p, part, sync, need, spin); break;
-        case NORM_BF16: err = launch_split_coop_bf16(op, c, p, part, sync, need, spin); break;
-        default: err = launch_split_coop_f16(op, c, p, part, sync, need, spin); break;
+        case NORM_F32: err = launch_split_pass_f32(op, c, p, slots, dep, o.wait_ticks, o.stagger); break;
+        case NORM_BF16: err = launch_split_pass_bf16(op, c, p, slots, dep, o.wait_ticks, o.stagger); break;
+        default: err = launch_split_pass_f16(op, c, p, slots, dep, o.wait_ticks, o.stagger); break;
         }
     } else {
         // Row batches in stream order; each batch reuses the partials.
@@ -544,7 +557,7 @@ int run(const Args& a, void* stream, bool noalloc = false) {
             }
         }
     }
-    return hip_ok(err, coop ? "single-pass split kernel launch" : "two-kernel split launch") ? NORM_OK
+    return hip_ok(err, pass ? "single-pass split kernel launch" : "two-kernel split launch") ? NORM_OK
                                                                                                : NORM_ERR_HIP;
 }
 
@@ -643,7 +656,7 @@ int make_bwd_plan(int64_t M, int64_t N, int dtype, bool rms, bool aligned, const
             // at least one row's worth of teams can be resident
             const int64_t ccv = int64_t(kBwdCoopWG) * kBwdCoopVPL;
             const int64_t cchunks = (NV + ccv - 1) / ccv;
-            const int64_t cap = coop_capacity(dtype, rms ? OP_RMS : OP_LN, p->epv, true);
+            const int64_t cap = resident_capacity(dtype, rms ? OP_RMS : OP_LN, p->epv, true);
             if (cap < cchunks) return NORM_ERR_BAD_ARG;
             p->path = PATH_SPLIT;
             p->split_mode = SPLIT_COOP;
@@ -955,12 +968,12 @@ int norm_describe(int op, int64_t M, int64_t N, int dtype, int aligned, char* bu
                       "path=split mode=%s wg=%d vpl=%d epv=%d chunks=%d apply_wg=%d apply_vpl=%d "
                       "apply_chunks=%d teams=%d batch_rows=%lld grid=%lld apply_grid=%lld work=%lld "
                       "workspace=%lld",
-                      p.split_mode == SPLIT_COOP ? "coop" : "two", p.wg, p.vpl, p.epv, p.chunks,
+                      p.split_mode == SPLIT_PASS ? "pass" : "two", p.wg, p.vpl, p.epv, p.chunks,
                       p.split_mode == SPLIT_TWO ? kApplyWG : 0, p.split_mode == SPLIT_TWO ? kApplyVPL : 0,
                       p.apply_chunks, p.teams, (long long)p.batch_rows, (long long)p.grid,
                       (long long)p.apply_grid, (long long)p.work,
                       (long long)(p.batch_rows * p.chunks * 8 +
-                                  (p.split_mode == SPLIT_COOP ? p.batch_rows * kSyncStride * 4 : 0)));
+                                  (p.split_mode == SPLIT_PASS ? p.batch_rows * kSyncStride * 4 : 0)));
     return NORM_OK;
 }
 

@@ -50,7 +50,9 @@ struct BwdCall {
 };
 
 enum { PATH_ROWS = 0, PATH_SPLIT = 1 };
-enum { SPLIT_TWO = 0, SPLIT_COOP = 1 };
+// split rows: two kernels per batch; the backward's single cooperative pass;
+// the forward's single pass (ordinary launch)
+enum { SPLIT_TWO = 0, SPLIT_COOP = 1, SPLIT_PASS = 2 };
 
 struct Plan {
     int path;       // PATH_ROWS or PATH_SPLIT
@@ -64,8 +66,8 @@ struct Plan {
     int apply_chunks;     // two-kernel form: chunks per row of the normalising kernel
     int64_t apply_grid;   // two-kernel form: workgroups of the normalising kernel
     int64_t work;   // rows: row groups; split: M * chunks
-    int split_mode; // SPLIT_TWO or SPLIT_COOP
-    int teams;      // coop: rows processed concurrently (grid = teams * chunks)
+    int split_mode; // SPLIT_TWO, SPLIT_COOP (backward) or SPLIT_PASS (forward)
+    int teams;      // single pass: rows processed concurrently (grid = teams * chunks)
     int64_t batch_rows;  // two-kernel split: rows per pair of launches
 };
 
@@ -116,14 +118,18 @@ constexpr int kStatsWG = MI355_STATS_WG;
 constexpr int kStatsVPL = MI355_STATS_VPL;
 constexpr int kApplyWG = MI355_APPLY_WG;
 constexpr int kApplyVPL = MI355_APPLY_VPL;
-#ifndef MI355_COOP_WG
-#define MI355_COOP_WG 1024
+// the forward's single pass: chunks of kPassWG lanes x kPassVPL vectors, two
+// workgroups per CU (measured on MI355X, LN bf16 64 x 2^20, us: 512 x 8
+// 66.6-68.6; 1024 x 8 72-78 (one per CU); 512 x 16 70-74; 512 x 4 79; 1024 x 4
+// 84-89)
+#ifndef MI355_PASS_WG
+#define MI355_PASS_WG 512
 #endif
-#ifndef MI355_COOP_VPL
-#define MI355_COOP_VPL 8
+#ifndef MI355_PASS_VPL
+#define MI355_PASS_VPL 8
 #endif
-constexpr int kCoopWG = MI355_COOP_WG;
-constexpr int kCoopVPL = MI355_COOP_VPL;
+constexpr int kPassWG = MI355_PASS_WG;
+constexpr int kPassVPL = MI355_PASS_VPL;
 // Two-kernel split: rows per pair of launches are chosen so that one batch of
 // x (about this many bytes) mostly stays in the 256 MB Infinity Cache between the
 // statistics pass and the normalising pass.
@@ -141,15 +147,17 @@ hipError_t launch_rows_f16(int op, const NormCall& c, const Plan& p);
 hipError_t launch_split_f32(int op, const NormCall& c, const Plan& p, float2* ws);
 hipError_t launch_split_bf16(int op, const NormCall& c, const Plan& p, float2* ws);
 hipError_t launch_split_f16(int op, const NormCall& c, const Plan& p, float2* ws);
-// single-pass split: ws holds M*chunks partials, sync 2*M counters that are
-// zero before the launch and zero again after it; each row waits for `need`
-// arrivals (its chunk count) for at most spin_limit polls
-hipError_t launch_split_coop_f32(int op, const NormCall& c, const Plan& p, float2* ws,
-                                 unsigned* sync, unsigned need, unsigned spin_limit);
-hipError_t launch_split_coop_bf16(int op, const NormCall& c, const Plan& p, float2* ws,
-                                  unsigned* sync, unsigned need, unsigned spin_limit);
-hipError_t launch_split_coop_f16(int op, const NormCall& c, const Plan& p, float2* ws,
-                                 unsigned* sync, unsigned need, unsigned spin_limit);
+// single-pass split (LayerNorm, RMSNorm and its FP8 form): slots holds
+// M*chunks published partials and dep one departure counter per row, 64
+// words apart, all zero before the launch and zero again after it; a row's
+// wait is bounded by wait_ticks of the 100 MHz clock (0: recompute at once),
+// and the second half of the teams starts `stagger` ticks late
+hipError_t launch_split_pass_f32(int op, const NormCall& c, const Plan& p, unsigned long long* slots,
+                                 unsigned* dep, unsigned wait_ticks, unsigned stagger);
+hipError_t launch_split_pass_bf16(int op, const NormCall& c, const Plan& p, unsigned long long* slots,
+                                  unsigned* dep, unsigned wait_ticks, unsigned stagger);
+hipError_t launch_split_pass_f16(int op, const NormCall& c, const Plan& p, unsigned long long* slots,
+                                 unsigned* dep, unsigned wait_ticks, unsigned stagger);
 // backward row kernel with the plan's tile (op OP_LN or OP_RMS), grid p.grid
 hipError_t launch_bwd_f32(int op, const BwdCall& c, const Plan& p);
 hipError_t launch_bwd_bf16(int op, const BwdCall& c, const Plan& p);
@@ -176,9 +184,9 @@ int bwd_coop_blocks_per_cu_f16(int op, int epv);
 // dgamma and (out_b not null) dbeta in one launch
 hipError_t launch_colsum(const float* part_g, float* out_g, const float* part_b, float* out_b, int64_t P, int N,
                          hipStream_t stream);
-// workgroups of the single-pass split kernel that fit on one CU at once
-int coop_blocks_per_cu_f32(int op, int epv);
-int coop_blocks_per_cu_bf16(int op, int epv);
-int coop_blocks_per_cu_f16(int op, int epv);
+// workgroups of the forward's single-pass kernel that fit on one CU at once
+int pass_blocks_per_cu_f32(int op, int epv);
+int pass_blocks_per_cu_bf16(int op, int epv);
+int pass_blocks_per_cu_f16(int op, int epv);
 
 }  // namespace mi355norm

@@ -9,12 +9,12 @@ hipError_t launch_rows_bf16(int op, const NormCall& c, const Plan& p) {
 hipError_t launch_split_bf16(int op, const NormCall& c, const Plan& p, float2* ws) {
     return detail::launch_split<BF16>(op, c, p, ws);
 }
-hipError_t launch_split_coop_bf16(int op, const NormCall& c, const Plan& p, float2* ws, unsigned* sync,
-                                  unsigned need, unsigned spin_limit) {
-    return detail::launch_split_coop<BF16>(op, c, p, ws, sync, need, spin_limit);
+hipError_t launch_split_pass_bf16(int op, const NormCall& c, const Plan& p, unsigned long long* slots,
+                                  unsigned* dep, unsigned wait_ticks, unsigned stagger) {
+    return detail::launch_split_pass<BF16>(op, c, p, slots, dep, wait_ticks, stagger);
 }
-int coop_blocks_per_cu_bf16(int op, int epv) {
-    return detail::coop_blocks_per_cu<BF16>(op, epv);
+int pass_blocks_per_cu_bf16(int op, int epv) {
+    return detail::pass_blocks_per_cu<BF16>(op, epv);
 }
 hipError_t launch_bwd_bf16(int op, const BwdCall& c, const Plan& p) {
     return detail::launch_bwd<BF16>(op, c, p);

@@ -157,39 +157,47 @@ hipError_t launch_split(int op, const NormCall& c, const Plan& p, float2* ws) {
 }
 
 // ---------------------------------------------------------------------------
-// split rows, single cooperative pass
+// split rows, single pass (LayerNorm, RMSNorm, RMSNorm with FP8 output)
 // ---------------------------------------------------------------------------
 
-template <class T, bool RMS, bool ADD, bool Q8, int EPV>
-const void* coop_kernel() {
-    return reinterpret_cast<const void*>(&norm_split_coop_kernel<T, RMS, ADD, Q8, kCoopWG, kCoopVPL, EPV>);
+template <class T, bool RMS, bool Q8, int EPV>
+const void* pass_kernel() {
+    return reinterpret_cast<const void*>(&norm_split_pass_kernel<T, RMS, Q8, kPassWG, kPassVPL, EPV>);
+}
+
+// Calls f(bc<RMS>, bc<Q8>) for the operations the single pass runs.
+template <class F>
+hipError_t with_pass_op(int op, F&& f) {
+    switch (op) {
+    case OP_LN: return f(bc<false>{}, bc<false>{});
+    case OP_RMS: return f(bc<true>{}, bc<false>{});
+    case OP_RMS_Q8: return f(bc<true>{}, bc<true>{});
+    }
+    return hipErrorInvalidValue;
 }
 
 template <class T>
-int coop_blocks_per_cu(int op, int epv) {
+int pass_blocks_per_cu(int op, int epv) {
     const void* f = nullptr;
-    (void)with_op(op, [&](auto rms, auto add, auto q8) {
+    (void)with_pass_op(op, [&](auto rms, auto q8) {
         return with_epv<T>(epv, [&](auto e) {
-            f = coop_kernel<T, decltype(rms)::value, decltype(add)::value, decltype(q8)::value,
-                            decltype(e)::value>();
+            f = pass_kernel<T, decltype(rms)::value, decltype(q8)::value, decltype(e)::value>();
             return hipSuccess;
         });
     });
     if (!f) return 0;
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, kCoopWG, 0) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, kPassWG, 0) != hipSuccess) return 0;
     return n;
 }
 
-template <class T, bool RMS, bool ADD, bool Q8, int EPV>
-hipError_t go_split_coop(const NormCall& c, const Plan& p, float2* ws, unsigned* sync,
-                         unsigned need, unsigned spin_limit) {
+template <class T, bool RMS, bool Q8, int EPV>
+hipError_t go_split_pass(const NormCall& c, const Plan& p, unsigned long long* slots, unsigned* dep,
+                         unsigned wait_ticks, unsigned stagger) {
     const St<T>* x = static_cast<const St<T>*>(c.x);
-    const St<T>* r = static_cast<const St<T>*>(c.res);
     const St<T>* g = static_cast<const St<T>*>(c.gamma);
     const St<T>* b = static_cast<const St<T>*>(c.beta);
     void* y = c.y;
-    St<T>* h = static_cast<St<T>*>(c.hout);
     float* mean = c.mean;
     float* rstd = c.rstd;
     int64_t M = c.M;
@@ -199,19 +207,19 @@ hipError_t go_split_coop(const NormCall& c, const Plan& p, float2* ws, unsigned*
     float eps = c.eps;
     float qinv = c.qinv;
     Strides ld = c.ld;
-    void* args[] = {&x, &r, &g, &b, &y, &h, &mean, &rstd, &ws, &sync, &M, &N, &ld, &S, &teams, &eps, &qinv,
-                    &need, &spin_limit};
-    return hipLaunchCooperativeKernel(coop_kernel<T, RMS, ADD, Q8, EPV>(), dim3((unsigned)(teams * S)),
-                                      dim3(kCoopWG), args, 0, c.stream);
+    void* args[] = {&x, &g, &b, &y, &mean, &rstd, &slots, &dep, &M, &N, &ld, &S, &teams, &eps, &qinv,
+                    &wait_ticks, &stagger};
+    return hipLaunchKernel(pass_kernel<T, RMS, Q8, EPV>(), dim3((unsigned)(teams * S)), dim3(kPassWG), args, 0,
+                           c.stream);
 }
 
 template <class T>
-hipError_t launch_split_coop(int op, const NormCall& c, const Plan& p, float2* ws, unsigned* sync,
-                             unsigned need, unsigned spin_limit) {
-    return with_op(op, [&](auto rms, auto add, auto q8) {
+hipError_t launch_split_pass(int op, const NormCall& c, const Plan& p, unsigned long long* slots, unsigned* dep,
+                             unsigned wait_ticks, unsigned stagger) {
+    return with_pass_op(op, [&](auto rms, auto q8) {
         return with_epv<T>(p.epv, [&](auto epv) {
-            return go_split_coop<T, decltype(rms)::value, decltype(add)::value, decltype(q8)::value,
-                                 decltype(epv)::value>(c, p, ws, sync, need, spin_limit);
+            return go_split_pass<T, decltype(rms)::value, decltype(q8)::value, decltype(epv)::value>(
+                c, p, slots, dep, wait_ticks, stagger);
         });
     });
 }

@@ -11,24 +11,36 @@
 // associative merge of "CUDA 算子工程" ch. 7 section 7.4.1.
 //
 // Two schedules:
-//   norm_split_stats_kernel  the default: two kernels.  Partials (x read
-//   + norm_split_apply_kernel  through the caches), then a second kernel that
-//                            merges the row's partials, re-reads x and
-//                            stores y (the two may cut rows into chunks of
-//                            different sizes).  When a batch of rows fits in
-//                            the 256 MB Infinity Cache the re-read is served
-//                            on-die, so HBM sees x about once.
-//   norm_split_coop_kernel   on request: single pass, x read once.  Each
+//   norm_split_stats_kernel  two kernels.  Partials (x read through the
+//   + norm_split_apply_kernel  caches), then a second kernel that merges
+//                            the row's partials, re-reads x and stores y (the
+//                            two may cut rows into chunks of different
+//                            sizes).  x crosses from memory to the CUs twice;
+//                            measured on MI355X, the second read is served
+//                            partly from the Infinity Cache (the normalising
+//                            kernel takes 42-44 us after the statistics
+//                            kernel on LN bf16 64 x 2^20, 52.5 us when x
+//                            comes from HBM), while rocprofv3's FETCH_SIZE
+//                            counts both reads either way.
+//   norm_split_pass_kernel   single pass, x read once, ordinary launch.  Each
 //                            workgroup keeps its chunk in VGPRs, publishes
-//                            its partial, waits at a per-row team barrier
-//                            (all S workgroups of a team are co-resident:
-//                            cooperative launch), merges and normalises from
-//                            registers.  Teams walk the rows with a stride of
-//                            the team count, each workgroup loading its
-//                            next row's chunk while it waits and normalises.
-//                            The barrier's counters return to zero by the
-//                            end of every launch, so a kept workspace needs
-//                            no reset.
+//                            its partial in the row's slot for it, waits
+//                            (one wavefront polling, bounded in time) until
+//                            every slot of the row holds a partial, merges
+//                            them and normalises from registers.  Teams of S
+//                            workgroups walk the rows.  A slot holds its
+//                            partial's bits inverted, zero meaning "not yet
+//                            published", so waiting on the slots themselves
+//                            needs no ordering between separate variables;
+//                            the last workgroup of a row to finish returns
+//                            the row's slots and departure counter to zero.
+//                            If the wait runs out (a workgroup of the team
+//                            is not resident, e.g. while another kernel
+//                            holds CUs), the workgroup computes every
+//                            chunk's partial of the row itself from x,
+//                            publishes them and goes on: the same bits,
+//                            just slower, so the result never depends on
+//                            co-residency and nothing can hang.
 #pragma once
 
 #include "prims.hpp"
@@ -111,34 +123,48 @@ struct Chunk {
 
     // LayerNorm: (mean of x - K, M2 about that mean) over the chunk's valid
     // elements; RMSNorm: (sum of squares, 0).  Uses both LDS slot sets.
+    // Masked vectors are dropped by one select per vector.
     template <bool RMS>
     __device__ __forceinline__ float2 partial(float K, int NV, float (*red)[WG / 64]) {
         if constexpr (RMS) {
             float q = 0.0f;
 #pragma unroll
-            for (int j = 0; j < VPL; ++j)
+            for (int j = 0; j < VPL; ++j) {
+                float t = 0.0f;
 #pragma unroll
-                for (int k = 0; k < EPV; ++k) q = __builtin_fmaf(xv[j].get(k), xv[j].get(k), q);
+                for (int k = 0; k < EPV; ++k) t = __builtin_fmaf(xv[j].get(k), xv[j].get(k), t);
+                q += ok[j] ? t : 0.0f;
+            }
             return make_float2(wg_sum<WG>(q, red[0]), 0.0f);
         } else {
             const int nvec = min(CV, NV - v0);
             const float nc = (float)nvec * (float)EPV;
             float s = 0.0f;
 #pragma unroll
-            for (int j = 0; j < VPL; ++j)
+            for (int j = 0; j < VPL; ++j) {
+                float t[EPV];
 #pragma unroll
-                for (int k = 0; k < EPV; ++k) s += ok[j] ? xv[j].get(k) - K : 0.0f;
+                for (int k = 0; k < EPV; ++k) t[k] = xv[j].get(k) - K;
+#pragma unroll
+                for (int h = 1; h < EPV; h *= 2)
+#pragma unroll
+                    for (int k = 0; k + h < EPV; k += 2 * h) t[k] += t[k + h];
+                s += ok[j] ? t[0] : 0.0f;
+            }
             s = wg_sum<WG>(s, red[0]);
             const float mc = s / nc;
             opaque();
             float q = 0.0f;
 #pragma unroll
-            for (int j = 0; j < VPL; ++j)
+            for (int j = 0; j < VPL; ++j) {
+                float t = 0.0f;
 #pragma unroll
                 for (int k = 0; k < EPV; ++k) {
-                    const float e = ok[j] ? (xv[j].get(k) - K) - mc : 0.0f;
-                    q = __builtin_fmaf(e, e, q);
+                    const float e = (xv[j].get(k) - K) - mc;
+                    t = __builtin_fmaf(e, e, t);
                 }
+                q += ok[j] ? t : 0.0f;
+            }
             return make_float2(mc, wg_sum<WG>(q, red[1]));
         }
     }
@@ -177,6 +203,7 @@ struct Chunk {
             }
         }
     }
+
 };
 
 // Merge a row's S partials (S arbitrary) inside one wavefront; the result is
@@ -253,12 +280,18 @@ __device__ __forceinline__ float2 read_partial(const float2* p) {
     else return *p;
 }
 
-template <bool COHERENT = false>
-__device__ __forceinline__ Welford merge_row_partials(const float2* p, int S, int CE, int N) {
+// Merge a row's S partials (read(c) gives partial c; S arbitrary) inside one
+// wavefront; the result is wave-uniform and identical in every wavefront
+// that runs it on the same data.  Lane l folds partials l, l+64, l+128, ...
+// in order; the 64 lane states are then merged by a butterfly whose every
+// step puts the lower lane's state first, so partners compute bitwise-
+// identical results.
+template <class Read>
+__device__ __forceinline__ Welford merge_partials(Read&& read, int S, int CE, int N) {
     const int l = lane_id();
     Welford a = {0.0f, 0.0f, 0.0f};
     for (int c = l; c < S; c += 64) {
-        const float2 v = read_partial<COHERENT>(p + c);
+        const float2 v = read(c);
         const int n = min(CE, N - c * CE);
         a = chan_merge(a, Welford{(float)n, v.x, v.y});
     }
@@ -280,117 +313,163 @@ __device__ __forceinline__ Welford merge_row_partials(const float2* p, int S, in
     return chan_merge(chan_merge(r[0], r[1]), chan_merge(r[2], r[3]));
 }
 
-// Row statistics from its S partials: (mean about K, rstd).
-template <bool RMS, bool COHERENT = false>
-__device__ __forceinline__ float2 row_stats(const float2* pr, int S, int CE, int N, float eps) {
+// Row statistics from its S partials (read(c) gives partial c): (mean about
+// K, rstd), wave-uniform.
+template <bool RMS, class Read>
+__device__ __forceinline__ float2 row_stats(Read&& read, int S, int CE, int N, float eps) {
     const float inv_n = 1.0f / (float)N;
     if constexpr (RMS) {
         float q = 0.0f;
-        for (int cc = lane_id(); cc < S; cc += 64) q += read_partial<COHERENT>(pr + cc).x;
+        for (int cc = lane_id(); cc < S; cc += 64) q += read(cc).x;
         q = team_sum<64>(q);
         return make_float2(0.0f, rsqrt_hw(__builtin_fmaf(q, inv_n, eps)));
     } else {
-        const Welford w = merge_row_partials<COHERENT>(pr, S, CE, N);
+        const Welford w = merge_partials(read, S, CE, N);
         return make_float2(w.mean, rsqrt_hw(__builtin_fmaf(w.m2, inv_n, eps)));
     }
 }
 
+// x[row, 0] through the scalar cache: the aligned dword that holds it (split
+// rows have more than two elements, so that dword lies within the row, or
+// takes the element before it).
+template <class T>
+__device__ __forceinline__ float shift_scalar(const typename T::storage* xr) {
+    typedef __attribute__((address_space(4))) const unsigned cu32;
+    const uintptr_t a = (uintptr_t)xr;
+    const unsigned w = *(cu32*)(a & ~uintptr_t(3));
+    if constexpr (sizeof(typename T::storage) == 4) return __uint_as_float(w);
+    else return T::widen((uint16_t)((a & 2) ? (w >> 16) : (w & 0xffffu)));
+}
+
 // ---------------------------------------------------------------------------
-// single pass, cooperative
+// single pass
 // ---------------------------------------------------------------------------
 
-// Publication of the partials: each is one coherent 64-bit atomic store,
-// complete before the arrival count is incremented, and read back with
-// coherent 64-bit loads; no L2 write-back or invalidation is needed (agent-
-// scope release / acquire would cost one of each per workgroup and row).
+// A published partial is its 64 bits inverted, so that zero -- what the
+// workspace holds when allocated and after each row's reset -- means "not
+// yet published".  Only a partial of two NaNs with every payload bit set
+// inverts to zero; such a row waits out its bound and takes the recompute
+// path, which gives the same (NaN) result.
+__device__ __forceinline__ void publish_slot(unsigned long long* slot, float2 v) {
+    const unsigned long long bits =
+        ((unsigned long long)__float_as_uint(v.y) << 32) | (unsigned long long)__float_as_uint(v.x);
+    __hip_atomic_store(slot, ~bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
+__device__ __forceinline__ unsigned long long read_slot(const unsigned long long* slot) {
+    return __hip_atomic_load(const_cast<unsigned long long*>(slot), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
-template <class T, bool RMS, bool ADD, bool Q8, int WG, int VPL, int EPV>
+__device__ __forceinline__ float2 slot_value(unsigned long long s) {
+    const unsigned long long bits = ~s;
+    return make_float2(__uint_as_float((unsigned)bits), __uint_as_float((unsigned)(bits >> 32)));
+}
+
+// One wavefront: whether all S slots hold a partial, polling until they do
+// or `ticks` of the 100 MHz real-time clock have passed (ticks == 0: no
+// polling at all, the caller recomputes).
+__device__ __forceinline__ bool wait_slots(const unsigned long long* slots, int S, unsigned ticks) {
+    if (ticks == 0) return false;
+    const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+    const int l = lane_id();
+    while (true) {
+        bool have = true;
+        for (int c = l; c < S; c += 64) have = have && read_slot(slots + c) != 0ull;
+        if (__builtin_amdgcn_ballot_w64(!have) == 0ull) return true;
+        if (__builtin_amdgcn_s_memrealtime() - t0 >= ticks) return false;
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
+// One wavefront, after merging the row: count this workgroup's departure;
+// the last of the row's S returns the S slots and the counter to zero.
+__device__ __forceinline__ void depart_row(unsigned* dep, unsigned long long* slots, int S) {
+    unsigned last = 0;
+    if (lane_id() == 0)
+        last = __hip_atomic_fetch_add(dep, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)S - 1;
+    last = __builtin_amdgcn_readfirstlane(last);
+    if (last) {
+        for (int c = lane_id(); c < S; c += 64)
+            __hip_atomic_store(slots + c, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane_id() == 0) __hip_atomic_store(dep, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Workgroup (team, c) handles chunk c of rows team, team + teams, ...  slots:
+// [M, S] published partials; dep: row r's departure counter at dep[64 r].
+// Both are zero at launch and again at exit.  The second half of the teams
+// starts `stagger` ticks late, so that on a CU holding one workgroup of each
+// half their loads, arithmetic and waits interleave.
+template <class T, bool RMS, bool Q8, int WG, int VPL, int EPV>
 __global__ __launch_bounds__(WG)
-void norm_split_coop_kernel(const typename T::storage* x,
-                            const typename T::storage* res,
+void norm_split_pass_kernel(const typename T::storage* __restrict__ x,
                             const typename T::storage* __restrict__ gamma,
                             const typename T::storage* __restrict__ beta,
                             void* y,
-                            typename T::storage* hout,
                             float* __restrict__ mean_out,
                             float* __restrict__ rstd_out,
-                            float2* __restrict__ part,      // [M, S] partials
-                            unsigned* __restrict__ sync,    // row r: [64r], [64r+32]; zero at
-                                                            // launch and again at exit
+                            unsigned long long* __restrict__ slots,
+                            unsigned* __restrict__ dep,
                             int64_t M, int N, Strides ld, int S, int teams, float eps, float qinv,
-                            unsigned need, unsigned spin_limit)
+                            unsigned wait_ticks, unsigned stagger)
 {
-    static_assert(!ADD || RMS, "the residual add is fused with RMSNorm only");
     static_assert(!Q8 || RMS, "FP8 output is fused with RMSNorm only");
     using C = Chunk<T, WG, VPL, EPV>;
+    constexpr int CE = C::CV * EPV;           // elements per chunk
     __shared__ float red[2][WG / 64];
+    __shared__ float2 stats;                  // (mean about K, rstd) of the current row
     __shared__ int late;
     const int tid = threadIdx.x;
     const int NV = N / EPV;
     const int team = blockIdx.x / S;          // grid is exactly teams * S
     const int c = blockIdx.x - team * S;
 
-    // One row's chunk: partial, publish, wait, merge, normalise.  during_wait
-    // runs between the publication and the wait (the next row's loads go
-    // there), before_stores once the statistics are known, before y is
-    // stored.
-    auto finish = [&](C& ch, float K, int64_t row, auto&& during_wait, auto&& before_stores) {
+    if (stagger && 2 * team >= teams) {
+        const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+        while (__builtin_amdgcn_s_memrealtime() - t0 < stagger) __builtin_amdgcn_s_sleep(8);
+    }
+    auto read = [](const unsigned long long* sl) { return [sl](int cc) { return slot_value(read_slot(sl + cc)); }; };
+    for (int64_t row = team; row < M; row += teams) {
+        const typename T::storage* xr = x + row * ld.x;
+        unsigned long long* rs = slots + row * S;
+        const float K = RMS ? 0.0f : shift_scalar<T>(xr);
+        C ch;
+        ch.load(xr, c, NV);
         const float2 p = ch.template partial<RMS>(K, NV, red);
-        const RowBarrier bar(sync, row);
-        if (tid == 0) bar.arrive(part + row * S + c, p);
-        during_wait();
-        if (tid == 0) late = bar.wait(need, spin_limit);
+        if (tid == 0) publish_slot(rs + c, p);
+        if (tid < 64) {
+            const bool have = wait_slots(rs, S, wait_ticks);
+            if (have) {
+                const float2 st = row_stats<RMS>(read(rs), S, CE, N, eps);
+                if (tid == 0) stats = st;
+                depart_row(dep + row * 64, rs, S);
+            }
+            if (tid == 0) late = !have;
+        }
         __syncthreads();
-        float2 st = row_stats<RMS, true>(part + row * S, S, C::CV * EPV, N, eps);
-        if (late) st = make_float2(__builtin_nanf(""), __builtin_nanf(""));   // visible failure
-        if (tid == 0) bar.depart(S);
+        if (late) {
+            // recompute: every chunk's partial of the row from x, published
+            // (the same bits its own workgroup publishes), then the merge
+            for (int cc = 0; cc < S; ++cc) {
+                ch.load(xr, cc, NV);
+                const float2 q = ch.template partial<RMS>(K, NV, red);
+                if (tid == 0) publish_slot(rs + cc, q);
+            }
+            if (tid < 64) {
+                const float2 st = row_stats<RMS>(read(rs), S, CE, N, eps);
+                if (tid == 0) stats = st;
+                depart_row(dep + row * 64, rs, S);
+            }
+            __syncthreads();
+            ch.load(xr, c, NV);
+        }
+        const float2 st = stats;
         if (c == 0 && tid == 0) {
             if (!RMS && mean_out) mean_out[row] = K + st.x;
             if (rstd_out) rstd_out[row] = st.y;
         }
-        before_stores();
         ch.template apply<RMS, Q8>(row_out<T, Q8>(y, row, ld.y), gamma, beta, K, st.x, st.y, qinv);
-    };
-
-    if constexpr (ADD) {
-        for (int64_t row = team; row < M; row += teams) {
-            const typename T::storage* xr = x + row * ld.x;
-            C ch;
-            ch.load(xr, c, NV);
-            ch.template add_residual<true>(res + row * ld.r, hout + row * ld.h);
-            finish(ch, 0.0f, row, [] {}, [] {});   // RMSNorm only: no shift
-        }
-    } else {
-        // the next row's chunk is loaded while this row waits at its barrier
-        // and is normalised: two chunk register sets, the loop unrolled by
-        // two so that no copy between them forces an early wait.  Loads and
-        // stores share one completion counter, so the next chunk's loads are
-        // waited for (ready) before this chunk's stores are issued; the merge
-        // of the row's partials, whose loads come after them, waits for them
-        // anyway.  (The residual add keeps one set: its chunk is added and
-        // stored as soon as it arrives.)
-        C ca, cb;
-        float Ka = 0.0f, Kb = 0.0f;
-        auto fetch = [&](C& ch, float& K, int64_t row) {
-            if (row >= M) return;
-            const typename T::storage* xr = x + row * ld.x;
-            ch.load(xr, c, NV);
-            K = RMS ? 0.0f : T::widen(xr[0]);
-        };
-        auto ready = [&](C& ch, float& K) {
-            ch.opaque();
-            asm volatile("" : "+v"(K));
-        };
-        fetch(ca, Ka, team);
-        ready(ca, Ka);
-        for (int64_t row = team; row < M;) {
-            finish(ca, Ka, row, [&] { fetch(cb, Kb, row + teams); }, [&] { ready(cb, Kb); });
-            row += teams;
-            if (row >= M) break;
-            finish(cb, Kb, row, [&] { fetch(ca, Ka, row + teams); }, [&] { ready(ca, Ka); });
-            row += teams;
-        }
+        __syncthreads();           // `stats` and `late` are rewritten for the next row
     }
 }
 
@@ -456,7 +535,8 @@ void norm_split_apply_kernel(const typename T::storage* x,
         C ch;
         ch.load(xr, c, NV);
         const float K = RMS ? 0.0f : T::widen(xr[0]);
-        const float2 st = row_stats<RMS>(part + row * S, S, CE, N, eps);
+        const float2* pr = part + row * S;
+        const float2 st = row_stats<RMS>([pr](int cc) { return pr[cc]; }, S, CE, N, eps);
         if (c == 0 && threadIdx.x == 0) {
             if (!RMS && mean_out) mean_out[row] = K + st.x;
             if (rstd_out) rstd_out[row] = st.y;

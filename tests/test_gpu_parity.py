@@ -364,19 +364,42 @@ def test_split_workspace_reused_across_shapes(monkeypatch, mode):
                     what=f"reuse {mode} {op} M={M} N={N}")
 
 
-def test_single_pass_split_bounded_wait(monkeypatch):
-    """Forced from the host, every row waits for one arrival more than it has
-    chunks, with a short bound: every workgroup stops waiting, the kernel
-    completes, the failure is visible (all outputs NaN), the counters are
-    back at zero, and the next normal call is correct."""
-    inp = inputs("ln", "bf16", 6, 1 << 18, seed=62)
-    monkeypatch.setenv("MI355NORM_PATH", "splitcoop")
+@pytest.mark.parametrize("op,dtype,M,N,offset", [("ln", "bf16", 6, 1 << 18, 0), ("rms", "f32", 5, 100003, 1),
+                                                  ("ln", "f16", 40, 70000, 0), ("ln", "f32", 33, 65544, 0)])
+def test_single_pass_recompute_gives_the_same_bits(monkeypatch, op, dtype, M, N, offset):
+    """The single pass's bounded wait, forced from the host to give up at
+    once: every workgroup then computes all of its rows' partials from x
+    itself.  The outputs must be the bits of the normal single pass, and the
+    kept workspace (slots, departure counters) must be back at zero for the
+    next call, which must give those bits again."""
+    monkeypatch.setenv("MI355NORM_PATH", "split1")
+    inp = inputs(op, dtype, M, N, seed=62 + M)
+    print(f"[gpu] single pass {op} {dtype} M={M} N={N} offset={offset}: normal, recompute, normal", flush=True)
+    a = run(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, offset=offset)
     monkeypatch.setenv("MI355NORM_FORCE_TIMEOUT", "1")
-    y, mean, rstd = run("ln", "bf16", inp["x"], inp["gamma"], inp["beta"], 1e-5)
-    assert np.isnan(oracle.widen(y, "bf16")).all() and np.isnan(rstd).all() and np.isnan(mean).all()
+    b = run(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, offset=offset)
     monkeypatch.delenv("MI355NORM_FORCE_TIMEOUT")
-    y, mean, rstd = run("ln", "bf16", inp["x"], inp["gamma"], inp["beta"], 1e-5)
-    compare("ln", "bf16", inp["x"], inp["gamma"], inp["beta"], 1e-5, y, mean, rstd, what="after timeout")
+    c = run(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, offset=offset)
+    for u, v, w in zip(a, b, c):
+        if u is None:
+            continue
+        assert np.array_equal(u.view(np.uint8), v.view(np.uint8)), "recompute path differs"
+        assert np.array_equal(u.view(np.uint8), w.view(np.uint8)), "call after the recompute differs"
+    compare(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, *a, what="single pass")
+
+
+def test_single_pass_plan():
+    """On the GPU the single pass plans whole teams of resident workgroups:
+    the grid is teams x chunks and holds at least one row's chunks."""
+    import rmsnorm_forward_amd as rn
+    import os
+    os.environ["MI355NORM_PATH"] = "split1"
+    try:
+        d = dict(kv.split("=") for kv in rn.norm_describe("ln", 64, 1 << 20, "bf16").split())
+    finally:
+        del os.environ["MI355NORM_PATH"]
+    assert d["mode"] == "pass" and int(d["grid"]) == int(d["teams"]) * int(d["chunks"])
+    assert 1 <= int(d["teams"]) <= 64
 
 
 # ---------------------------------------------------------------------------
