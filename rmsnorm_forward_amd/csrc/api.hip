@@ -35,19 +35,18 @@
 //                                       the residual add, which keeps two
 //                                       kernels; for the backward, split and
 //                                       split2 take the three-kernel split,
-//                                       splitcoop its single cooperative pass)
+//                                       split1 / splitcoop its single pass)
 //   MI355NORM_SPLIT_BATCH = <bytes>     bytes of x per two-kernel split batch
 //                                       (of dy and x in the split backward)
 //   MI355NORM_TILE = <team>x<vpl>       force the row-kernel tile
 //   MI355NORM_GRID = <n>                cap the number of workgroups
-//   MI355NORM_SPIN_LIMIT = <n>          bound of the backward single pass's wait
-//   MI355NORM_WAIT_TICKS = <n>          bound of the forward single pass's wait
+//   MI355NORM_WAIT_TICKS = <n>          bound of the single passes' waits
 //                                       (100 MHz ticks)
 //   MI355NORM_STAGGER = <n>             start delay of the second half of the
 //                                       forward single pass's teams (ticks)
 //   MI355NORM_FORCE_TIMEOUT = 1         make the single passes' waits run out
-//                                       (forward: recompute at once; backward:
-//                                       the failure path)
+//                                       at once (every workgroup recomputes
+//                                       its rows' partials from the inputs)
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -196,8 +195,7 @@ struct Overrides {
     int split_mode = -1;  // -1 auto
     int team = 0, vpl = 0;
     int64_t grid = 0;
-    unsigned spin_limit = 1u << 20;
-    unsigned wait_ticks = 100000;   // forward single pass: 1 ms
+    unsigned wait_ticks = 100000;   // single passes: 1 ms
     unsigned stagger = 0;
     bool force_timeout = false;
     int64_t batch_bytes = 0;  // two-kernel split: bytes of x per batch (0: default)
@@ -211,10 +209,9 @@ Overrides read_overrides() {
         else if (!std::strcmp(s, "split2")) { o.path = PATH_SPLIT; o.split_mode = SPLIT_TWO; }
         else if (!std::strcmp(s, "splitcoop") || !std::strcmp(s, "split1")) {
             o.path = PATH_SPLIT;
-            o.split_mode = SPLIT_COOP;   // the single pass (forward: SPLIT_PASS)
+            o.split_mode = SPLIT_PASS;
         }
     }
-    if (const char* s = std::getenv("MI355NORM_SPIN_LIMIT")) o.spin_limit = (unsigned)std::strtoul(s, nullptr, 10);
     if (const char* s = std::getenv("MI355NORM_FORCE_TIMEOUT")) o.force_timeout = std::atoi(s) != 0;
     if (const char* s = std::getenv("MI355NORM_WAIT_TICKS")) o.wait_ticks = (unsigned)std::strtoul(s, nullptr, 10);
     if (const char* s = std::getenv("MI355NORM_STAGGER")) o.stagger = (unsigned)std::strtoul(s, nullptr, 10);
@@ -249,10 +246,9 @@ bool fwd_tile_instantiated(int team, int vpl) {
     return tile_instantiated(team, vpl);
 }
 
-// How many workgroups of the forward's single-pass kernel (bwd: of the
-// backward's cooperative single pass) the current device can hold at once (0
-// if no device is present, or, for the backward, if cooperative launch is
-// unavailable).  Cached per (device, dtype, op, vector width, direction).
+// How many workgroups of the forward's (bwd: the backward's) single-pass
+// kernel the current device can hold at once (0 if no device is present).
+// Cached per (device, dtype, op, vector width, direction).
 int64_t resident_capacity(int dtype, int op, int epv, bool bwd = false) {
     static std::mutex mu;
     static int64_t cache[64][3][kOps][2][2];
@@ -265,16 +261,14 @@ int64_t resident_capacity(int dtype, int op, int epv, bool bwd = false) {
     const int bi = bwd ? 1 : 0;
     std::lock_guard<std::mutex> lock(mu);
     if (!known[dev][dtype][op][vi][bi]) {
-        int coop = 0, cus = 0;
+        int cus = 0;
         int64_t cap = 0;
-        const bool launchable =
-            !bwd || (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && coop);
-        if (launchable && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) {
             int per_cu;
             if (bwd)
-                per_cu = dtype == NORM_F32 ? bwd_coop_blocks_per_cu_f32(op, epv)
-                         : dtype == NORM_BF16 ? bwd_coop_blocks_per_cu_bf16(op, epv)
-                                              : bwd_coop_blocks_per_cu_f16(op, epv);
+                per_cu = dtype == NORM_F32 ? bwd_pass_blocks_per_cu_f32(op, epv)
+                         : dtype == NORM_BF16 ? bwd_pass_blocks_per_cu_bf16(op, epv)
+                                              : bwd_pass_blocks_per_cu_f16(op, epv);
             else
                 per_cu = dtype == NORM_F32 ? pass_blocks_per_cu_f32(op, epv)
                          : dtype == NORM_BF16 ? pass_blocks_per_cu_bf16(op, epv)
@@ -346,7 +340,7 @@ int make_plan(int op, int64_t M, int64_t N, int dtype, bool aligned, const Overr
         // Two kernels by default.  The single pass runs when asked for (not
         // for the residual add, which keeps two kernels) and every chunk of
         // at least one row can be resident.
-        if (o.split_mode == SPLIT_COOP && !has_add(op)) {
+        if (o.split_mode == SPLIT_PASS && !has_add(op)) {
             const int64_t pv = int64_t(kPassWG) * kPassVPL;
             const int64_t pchunks = (NV + pv - 1) / pv;
             const int64_t cap = resident_capacity(dtype, op, p->epv);
@@ -651,17 +645,16 @@ int make_bwd_plan(int64_t M, int64_t N, int dtype, bool rms, bool aligned, const
         vpl = round_vpl((NV + team - 1) / team);
         const bool f32_wide = e == 4 && vpl > 0 && vpl * p->epv == kBwdMaxElems &&
                               (rms || NV > kBwdF32RowsMaxLnVectors);
-        if (o.path == PATH_SPLIT && o.split_mode == SPLIT_COOP) {
-            // one cooperative pass, on request, when every chunk of a row and
-            // at least one row's worth of teams can be resident
-            const int64_t ccv = int64_t(kBwdCoopWG) * kBwdCoopVPL;
+        if (o.path == PATH_SPLIT && o.split_mode == SPLIT_PASS) {
+            // one pass, on request, when every chunk of a row can be resident
+            const int64_t ccv = int64_t(kBwdPassWG) * kBwdPassVPL;
             const int64_t cchunks = (NV + ccv - 1) / ccv;
             const int64_t cap = resident_capacity(dtype, rms ? OP_RMS : OP_LN, p->epv, true);
             if (cap < cchunks) return NORM_ERR_BAD_ARG;
             p->path = PATH_SPLIT;
-            p->split_mode = SPLIT_COOP;
-            p->wg = kBwdCoopWG;
-            p->vpl = kBwdCoopVPL;
+            p->split_mode = SPLIT_PASS;
+            p->wg = kBwdPassWG;
+            p->vpl = kBwdPassVPL;
             p->chunks = (int)cchunks;
             p->teams = (int)std::max<int64_t>(1, std::min<int64_t>(M, cap / cchunks));
             p->batch_rows = M;
@@ -741,10 +734,12 @@ int run_bwd_split(const BwdArgs& a, const Plan& p, hipStream_t s) {
     // the partial rows start 256-byte aligned (the column sum may read them
     // as 16-byte vectors)
     const size_t col_off = ((part_elems + size_t(p.batch_rows)) * sizeof(float2) + 255) & ~size_t(255);
-    const bool coop = p.split_mode == SPLIT_COOP;
+    const bool pass = p.split_mode == SPLIT_PASS;
     Workspace w;
-    if (!stream_workspace(s, coop ? size_t(M) * kSyncStride : 0, col_off + cols * ncol * sizeof(float), &w))
-        return NORM_ERR_HIP;
+    // single pass: M x 64 counter words, then M x chunks 8-byte slots, in the
+    // counter region
+    const size_t sync_words = pass ? size_t(M) * (kSyncStride + 2 * size_t(p.chunks)) : 0;
+    if (!stream_workspace(s, sync_words, col_off + cols * ncol * sizeof(float), &w)) return NORM_ERR_HIP;
     float2* part = w.part;
     float2* rows = part + part_elems;
     float* colbase = reinterpret_cast<float*>(reinterpret_cast<char*>(part) + col_off);
@@ -752,21 +747,21 @@ int run_bwd_split(const BwdArgs& a, const Plan& p, hipStream_t s) {
     float* pb = direct ? a.dbeta : a.dbeta ? colbase + (a.dgamma ? cols : 0) : nullptr;
     const int op = a.rms ? OP_RMS : OP_LN;
     hipError_t err = hipSuccess;
-    if (coop && M > 0) {
-        // every row in one cooperative launch; the row barriers' counters
-        // are zero at the start of every call (see the forward's single pass)
+    if (pass && M > 0) {
+        // every row in one launch; slots and counters are zero at the start
+        // of every call (see the forward's single pass)
         const Overrides o = read_overrides();
-        const unsigned need = (unsigned)p.chunks + (o.force_timeout ? 1u : 0u);
-        const unsigned spin = o.force_timeout ? 64u : o.spin_limit;
+        unsigned* dep = w.sync;
+        auto* slots = reinterpret_cast<unsigned long long*>(w.sync + size_t(M) * kSyncStride);
         BwdCall c{a.dy, a.x, a.gamma, a.mean, a.rstd, a.dx, pg, pb, M, (int)N, a.lddy, a.ldx, a.lddx, s};
         switch (a.dtype) {
-        case NORM_F32: err = launch_bwd_coop_f32(op, c, p, part, w.sync, need, spin); break;
-        case NORM_BF16: err = launch_bwd_coop_bf16(op, c, p, part, w.sync, need, spin); break;
-        default: err = launch_bwd_coop_f16(op, c, p, part, w.sync, need, spin); break;
+        case NORM_F32: err = launch_bwd_pass_f32(op, c, p, slots, dep, o.wait_ticks); break;
+        case NORM_BF16: err = launch_bwd_pass_bf16(op, c, p, slots, dep, o.wait_ticks); break;
+        default: err = launch_bwd_pass_f16(op, c, p, slots, dep, o.wait_ticks); break;
         }
     }
     int64_t b = 0;
-    for (int64_t r0 = 0; !coop && r0 < M && err == hipSuccess; r0 += p.batch_rows, ++b) {
+    for (int64_t r0 = 0; !pass && r0 < M && err == hipSuccess; r0 += p.batch_rows, ++b) {
         const int64_t mb = std::min(p.batch_rows, M - r0);
         BwdCall c{static_cast<const char*>(a.dy) + r0 * a.lddy * e, static_cast<const char*>(a.x) + r0 * a.ldx * e,
                   a.gamma, a.mean ? a.mean + r0 : nullptr, a.rstd + r0, static_cast<char*>(a.dx) + r0 * a.lddx * e,
@@ -919,8 +914,8 @@ int norm_bwd_describe(int rms, int64_t M, int64_t N, int dtype, int aligned, cha
         std::snprintf(buf, (size_t)buflen,
                       "path=bwd_split mode=%s op=%s wg=%d sums_vpl=%d apply_vpl=%d epv=%d chunks=%d "
                       "apply_chunks=%d batch_rows=%lld grid=%lld apply_grid=%lld partial_rows=%d",
-                      p.split_mode == SPLIT_COOP ? "coop" : "three", rms ? "rms" : "ln", p.wg,
-                      p.split_mode == SPLIT_COOP ? p.vpl : bwd_sums_vpl(p.epv), p.vpl, p.epv, p.chunks, p.apply_chunks,
+                      p.split_mode == SPLIT_PASS ? "pass" : "three", rms ? "rms" : "ln", p.wg,
+                      p.split_mode == SPLIT_PASS ? p.vpl : bwd_sums_vpl(p.epv), p.vpl, p.epv, p.chunks, p.apply_chunks,
                       (long long)p.batch_rows, (long long)p.grid, (long long)p.apply_grid, p.teams);
     else if (buf && buflen > 0)
         std::snprintf(buf, (size_t)buflen,

@@ -30,13 +30,17 @@
 // The column sums of the partial rows follow (norm_colsum_kernel), so
 // dgamma and dbeta are summed in a fixed order throughout.
 //
-// On request, norm_bwd_coop_kernel does it in one cooperative pass (dy and x
-// read once): teams of S co-resident workgroups, one per chunk of a row, walk
+// On request, norm_bwd_pass_kernel does it in one pass (dy and x read once,
+// an ordinary launch): teams of S workgroups, one per chunk of a row, walk
 // the rows; each keeps its chunk of dy and x in registers, publishes its
-// chunk sums, loads its next row's chunk, waits at the row's barrier (the
-// protocol of the forward's single pass), adds the row's S chunk sums in
-// chunk order, forms dx from registers and accumulates dgamma / dbeta for
-// its columns; partial row `team` holds them at the end.
+// chunk sums in the row's slot for it (the forward single pass's protocol:
+// a slot holds its value's bits inverted, zero meaning "not yet"), loads its
+// next row's chunk, waits (bounded in time) until every slot of the row is
+// filled, adds the row's S chunk sums in chunk order, forms dx from registers
+// and accumulates dgamma / dbeta for its columns; partial row `team` holds
+// them at the end.  If the wait runs out, the workgroup computes every
+// chunk's sums of the row from dy and x itself (the same bits) and goes on,
+// so nothing depends on the team being resident at once.
 #pragma once
 
 #include "prims.hpp"
@@ -302,10 +306,11 @@ void norm_bwd_split_apply_kernel(const typename T::storage* dy,      // dx may b
     }
 }
 
-// Sum of a row's S chunk sums, read with coherent loads, in the fixed order
+// Sum of a row's S chunk sums (read(c) gives chunk c's), in the fixed order
 // of rowsum_one (lane l takes chunks l, l + 64, ... into four accumulators in
 // turn, then the wavefront butterfly): the same bits in every wavefront.
-__device__ __forceinline__ float2 rowsum_coherent(const float2* pr, int S) {
+template <class Read>
+__device__ __forceinline__ float2 rowsum_read(Read&& read, int S) {
     float2 a[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[i] = make_float2(0.0f, 0.0f);
@@ -313,7 +318,7 @@ __device__ __forceinline__ float2 rowsum_coherent(const float2* pr, int S) {
     for (; c + 192 < S; c += 256) {
         float2 v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = load_partial_coherent(pr + c + 64 * i);
+        for (int i = 0; i < 4; ++i) v[i] = read(c + 64 * i);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             a[i].x += v[i].x;
@@ -323,7 +328,7 @@ __device__ __forceinline__ float2 rowsum_coherent(const float2* pr, int S) {
 #pragma unroll
     for (int i = 0; i < 3; ++i)
         if (c + 64 * i < S) {
-            const float2 v = load_partial_coherent(pr + c + 64 * i);
+            const float2 v = read(c + 64 * i);
             a[i].x += v.x;
             a[i].y += v.y;
         }
@@ -334,7 +339,7 @@ __device__ __forceinline__ float2 rowsum_coherent(const float2* pr, int S) {
 
 template <class T, bool RMS, int WG, int VPL, int EPV>
 __global__ __launch_bounds__(WG)
-void norm_bwd_coop_kernel(const typename T::storage* dy,      // dx may be written over dy or x
+void norm_bwd_pass_kernel(const typename T::storage* dy,      // dx may be written over dy or x
                           const typename T::storage* x,
                           const typename T::storage* __restrict__ gamma,
                           const float* __restrict__ mean,
@@ -342,16 +347,16 @@ void norm_bwd_coop_kernel(const typename T::storage* dy,      // dx may be writt
                           typename T::storage* dx,
                           float* __restrict__ part_g,         // [teams, N] or null
                           float* __restrict__ part_b,         // [teams, N] or null
-                          float2* __restrict__ part,          // [M, S] chunk sums
-                          unsigned* __restrict__ sync,        // row r: [64r], [64r+32]; zero at
-                                                              // launch and again at exit
+                          unsigned long long* __restrict__ slots,   // [M, S] published chunk sums
+                          unsigned* __restrict__ dep,         // row r's departures at dep[64 r]
                           int64_t M, int N, int64_t ldy, int64_t ldx, int64_t lddx, int S, int teams,
-                          unsigned need, unsigned spin_limit)
+                          unsigned wait_ticks)
 {
     using V = Vec<T, EPV>;
     using St = typename T::storage;
     constexpr int CV = WG * VPL;
     __shared__ float red[2][WG / 64];
+    __shared__ float2 row_sums;               // of the row being finished
     __shared__ int late;
     const int tid = threadIdx.x;
     const int team = blockIdx.x / S;          // grid is exactly teams * S
@@ -359,21 +364,25 @@ void norm_bwd_coop_kernel(const typename T::storage* dy,      // dx may be writt
     const int NV = N / EPV;
     const float inv_n = 1.0f / (float)N;
 
+    // the columns of chunk cc: in-row flags and gamma (1 where absent)
+    auto columns = [&](int cc, bool (&okv)[VPL], V (&gm)[VPL]) {
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+            const unsigned v = (unsigned)(cc * CV + j * WG) + tid;
+            okv[j] = (int)v < NV;
+            if (gamma != nullptr && okv[j]) {
+                gm[j].load(gamma + v * EPV);
+            } else {
+                float one[EPV];
+#pragma unroll
+                for (int k = 0; k < EPV; ++k) one[k] = 1.0f;
+                gm[j].set(one);
+            }
+        }
+    };
     bool col_ok[VPL];
     V gam[VPL];
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-        const unsigned v = (unsigned)(c * CV + j * WG) + tid;
-        col_ok[j] = (int)v < NV;
-        if (gamma != nullptr && col_ok[j]) {
-            gam[j].load(gamma + v * EPV);
-        } else {
-            float one[EPV];
-#pragma unroll
-            for (int k = 0; k < EPV; ++k) one[k] = 1.0f;
-            gam[j].set(one);
-        }
-    }
+    columns(c, col_ok, gam);
     float acc_g[VPL][EPV], acc_b[RMS ? 1 : VPL][EPV];
 #pragma unroll
     for (int j = 0; j < VPL; ++j)
@@ -387,12 +396,13 @@ void norm_bwd_coop_kernel(const typename T::storage* dy,      // dx may be writt
         V d[VPL], xx[VPL];
         float m, r;
     };
-    auto fetch = [&](int64_t row, Row& q) {
+    // chunk cc of dy and x of `row`, with its statistics
+    auto fetch_chunk = [&](int64_t row, Row& q, int cc, const bool (&okv)[VPL]) {
         if (row >= M) return;
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
-            const unsigned v = (unsigned)(c * CV + j * WG) + tid;
-            if (col_ok[j]) {          // nontemporal: dy and x are read once
+            const unsigned v = (unsigned)(cc * CV + j * WG) + tid;
+            if (okv[j]) {          // nontemporal: dy and x are read once
                 q.d[j].load_stream(dy + row * ldy + v * EPV);
                 q.xx[j].load_stream(x + row * ldx + v * EPV);
             }
@@ -400,6 +410,7 @@ void norm_bwd_coop_kernel(const typename T::storage* dy,      // dx may be writt
         q.m = RMS ? 0.0f : mean[row];
         q.r = rstd[row];
     };
+    auto fetch = [&](int64_t row, Row& q) { fetch_chunk(row, q, c, col_ok); };
     auto ready = [&](Row& q) {
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
@@ -408,16 +419,20 @@ void norm_bwd_coop_kernel(const typename T::storage* dy,      // dx may be writt
         }
         asm volatile("" : "+v"(q.m), "+v"(q.r));
     };
-    // One row: chunk sums, publication, (the next row's loads), the wait,
-    // the row sums, dx and the column accumulators.
-    auto finish = [&](Row& q, int64_t row, auto&& during_wait, auto&& before_stores) {
+    // (sum g, sum g xhat) -- (0, sum g x) for RMSNorm -- over a chunk, every
+    // workgroup computing the same bits for the same chunk: contraction is
+    // off, so each inlined copy performs exactly these IEEE operations (the
+    // compiler would otherwise fuse some copies' products into dot-product
+    // instructions that round differently)
+    auto chunk_sums = [&](Row& q, const bool (&okv)[VPL], const V (&gm)[VPL]) {
+#pragma clang fp contract(off)
         float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
-            if (!col_ok[j]) continue;
+            if (!okv[j]) continue;
 #pragma unroll
             for (int k = 0; k < EPV; ++k) {
-                const float g = q.d[j].get(k) * gam[j].get(k);
+                const float g = q.d[j].get(k) * gm[j].get(k);
                 const float xh = RMS ? q.xx[j].get(k) : (q.xx[j].get(k) - q.m) * q.r;
                 if constexpr (!RMS) s1 += g;
                 s2 = __builtin_fmaf(g, xh, s2);
@@ -430,17 +445,50 @@ void norm_bwd_coop_kernel(const typename T::storage* dy,      // dx may be writt
             q.xx[j].opaque();
         }
         // two exchanges on two slot sets: the second's barrier orders every
-        // read of the first set before the next row writes it
+        // read of the first set before the next write
         if constexpr (!RMS) s1 = wg_sum<WG>(s1, red[0]);
         s2 = wg_sum<WG>(s2, red[1]);
-        const RowBarrier bar(sync, row);
-        if (tid == 0) bar.arrive(part + row * S + c, make_float2(s1, s2));
+        return make_float2(s1, s2);
+    };
+    auto read = [](const unsigned long long* sl) { return [sl](int cc) { return slot_value(read_slot(sl + cc)); }; };
+    // One row: chunk sums, publication, (the next row's loads), the wait,
+    // the row sums, dx and the column accumulators.
+    auto finish = [&](Row& q, int64_t row, auto&& during_wait, auto&& before_stores) {
+        unsigned long long* rsl = slots + row * S;
+        const float2 cs = chunk_sums(q, col_ok, gam);
+        if (tid == 0) publish_slot(rsl + c, cs);
         during_wait();
-        if (tid == 0) late = bar.wait(need, spin_limit);
+        if (tid < 64) {
+            const bool have = wait_slots(rsl, S, wait_ticks);
+            if (have) {
+                const float2 r = rowsum_read(read(rsl), S);
+                if (tid == 0) row_sums = r;
+                depart_row(dep + row * 64, rsl, S);
+            }
+            if (tid == 0) late = !have;
+        }
         __syncthreads();
-        float2 rs = rowsum_coherent(part + row * S, S);
-        if (late) rs = make_float2(__builtin_nanf(""), __builtin_nanf(""));   // visible failure
-        if (tid == 0) bar.depart(S);
+        if (late) {
+            // recompute: every chunk's sums of the row from dy and x,
+            // published (the bits its own workgroup publishes), then the sum
+            for (int cc = 0; cc < S; ++cc) {
+                bool okv[VPL];
+                V gm[VPL];
+                columns(cc, okv, gm);
+                fetch_chunk(row, q, cc, okv);
+                const float2 s = chunk_sums(q, okv, gm);
+                if (tid == 0) publish_slot(rsl + cc, s);
+            }
+            if (tid < 64) {
+                const float2 r = rowsum_read(read(rsl), S);
+                if (tid == 0) row_sums = r;
+                depart_row(dep + row * 64, rsl, S);
+            }
+            __syncthreads();
+            fetch(row, q);
+            ready(q);
+        }
+        const float2 rs = row_sums;
         const float c1 = rs.x * inv_n;
         const float c2 = RMS ? q.r * q.r * q.r * (rs.y * inv_n) : rs.y * inv_n;
         V out[VPL];
@@ -470,10 +518,11 @@ void norm_bwd_coop_kernel(const typename T::storage* dy,      // dx may be writt
 #pragma unroll
         for (int j = 0; j < VPL; ++j)
             if (col_ok[j]) out[j].put_stream(dxr + ((unsigned)(c * CV + j * WG) + tid) * EPV);
+        __syncthreads();           // `row_sums` and `late` are rewritten for the next row
     };
 
-    // two row register sets, the loop unrolled by two (see the forward's
-    // single pass for the ordering of the waits)
+    // two row register sets, the loop unrolled by two: the next row's loads
+    // are issued during this row's wait and waited for before its stores
     Row qa, qb;
     fetch(team, qa);
     ready(qa);

@@ -50,9 +50,8 @@ struct BwdCall {
 };
 
 enum { PATH_ROWS = 0, PATH_SPLIT = 1 };
-// split rows: two kernels per batch; the backward's single cooperative pass;
-// the forward's single pass (ordinary launch)
-enum { SPLIT_TWO = 0, SPLIT_COOP = 1, SPLIT_PASS = 2 };
+// split rows: two kernels per batch (three for the backward) or one pass
+enum { SPLIT_TWO = 0, SPLIT_PASS = 2 };
 
 struct Plan {
     int path;       // PATH_ROWS or PATH_SPLIT
@@ -66,7 +65,7 @@ struct Plan {
     int apply_chunks;     // two-kernel form: chunks per row of the normalising kernel
     int64_t apply_grid;   // two-kernel form: workgroups of the normalising kernel
     int64_t work;   // rows: row groups; split: M * chunks
-    int split_mode; // SPLIT_TWO, SPLIT_COOP (backward) or SPLIT_PASS (forward)
+    int split_mode; // SPLIT_TWO or SPLIT_PASS
     int teams;      // single pass: rows processed concurrently (grid = teams * chunks)
     int64_t batch_rows;  // two-kernel split: rows per pair of launches
 };
@@ -91,10 +90,10 @@ constexpr int kBwdSplitSumsVPL = 2;
 constexpr int kBwdSplitSumsVPLElem = 16;
 constexpr int bwd_sums_vpl(int epv) { return epv == 1 ? kBwdSplitSumsVPLElem : kBwdSplitSumsVPL; }
 constexpr int kBwdSplitApplyVPL = 2;
-// split backward in one cooperative pass (on request): chunks of 1024 lanes x
-// 2 vectors, one workgroup per chunk, every chunk of a team's row resident
-constexpr int kBwdCoopWG = 1024;
-constexpr int kBwdCoopVPL = 2;
+// split backward in one pass (on request): chunks of 1024 lanes x 2
+// vectors, one workgroup per chunk
+constexpr int kBwdPassWG = 1024;
+constexpr int kBwdPassVPL = 2;
 constexpr int kBwdMinTeam = 8;
 // backward workgroups: always 1024 lanes (16 wavefronts fill a CU's wave
 // slots at up to 128 VGPRs), 1024 / team rows at once
@@ -168,18 +167,20 @@ hipError_t launch_bwd_f16(int op, const BwdCall& c, const Plan& p);
 hipError_t launch_bwd_split_f32(int op, const BwdCall& c, const Plan& p, float2* part, float2* rows, int accumulate);
 hipError_t launch_bwd_split_bf16(int op, const BwdCall& c, const Plan& p, float2* part, float2* rows, int accumulate);
 hipError_t launch_bwd_split_f16(int op, const BwdCall& c, const Plan& p, float2* part, float2* rows, int accumulate);
-// split backward in one cooperative pass over all c.M rows: chunk sums in
-// part ([M, p.chunks]), row barriers in sync, partial rows p.teams x N
-hipError_t launch_bwd_coop_f32(int op, const BwdCall& c, const Plan& p, float2* part, unsigned* sync, unsigned need,
-                               unsigned spin_limit);
-hipError_t launch_bwd_coop_bf16(int op, const BwdCall& c, const Plan& p, float2* part, unsigned* sync, unsigned need,
-                                unsigned spin_limit);
-hipError_t launch_bwd_coop_f16(int op, const BwdCall& c, const Plan& p, float2* part, unsigned* sync, unsigned need,
-                               unsigned spin_limit);
+// split backward in one pass over all c.M rows: chunk sums published in
+// slots ([M, p.chunks], zero before and after), departure counters in dep
+// (64 words apart), partial rows p.teams x N; a row's wait is bounded by
+// wait_ticks of the 100 MHz clock (0: recompute at once)
+hipError_t launch_bwd_pass_f32(int op, const BwdCall& c, const Plan& p, unsigned long long* slots, unsigned* dep,
+                               unsigned wait_ticks);
+hipError_t launch_bwd_pass_bf16(int op, const BwdCall& c, const Plan& p, unsigned long long* slots, unsigned* dep,
+                                unsigned wait_ticks);
+hipError_t launch_bwd_pass_f16(int op, const BwdCall& c, const Plan& p, unsigned long long* slots, unsigned* dep,
+                               unsigned wait_ticks);
 // workgroups of the single-pass split backward that fit on one CU at once
-int bwd_coop_blocks_per_cu_f32(int op, int epv);
-int bwd_coop_blocks_per_cu_bf16(int op, int epv);
-int bwd_coop_blocks_per_cu_f16(int op, int epv);
+int bwd_pass_blocks_per_cu_f32(int op, int epv);
+int bwd_pass_blocks_per_cu_bf16(int op, int epv);
+int bwd_pass_blocks_per_cu_f16(int op, int epv);
 // out_*[c] = sum of the P partial rows part_* of column c (fixed order), for
 // dgamma and (out_b not null) dbeta in one launch
 hipError_t launch_colsum(const float* part_g, float* out_g, const float* part_b, float* out_b, int64_t P, int N,

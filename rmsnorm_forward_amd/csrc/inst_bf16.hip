@@ -22,11 +22,11 @@ hipError_t launch_bwd_bf16(int op, const BwdCall& c, const Plan& p) {
 hipError_t launch_bwd_split_bf16(int op, const BwdCall& c, const Plan& p, float2* part, float2* rows, int accumulate) {
     return detail::launch_bwd_split<BF16>(op, c, p, part, rows, accumulate);
 }
-hipError_t launch_bwd_coop_bf16(int op, const BwdCall& c, const Plan& p, float2* part, unsigned* sync, unsigned need,
-                               unsigned spin_limit) {
-    return detail::launch_bwd_coop<BF16>(op, c, p, part, sync, need, spin_limit);
+hipError_t launch_bwd_pass_bf16(int op, const BwdCall& c, const Plan& p, unsigned long long* slots, unsigned* dep,
+                               unsigned wait_ticks) {
+    return detail::launch_bwd_pass<BF16>(op, c, p, slots, dep, wait_ticks);
 }
-int bwd_coop_blocks_per_cu_bf16(int op, int epv) {
-    return detail::bwd_coop_blocks_per_cu<BF16>(op, epv);
+int bwd_pass_blocks_per_cu_bf16(int op, int epv) {
+    return detail::bwd_pass_blocks_per_cu<BF16>(op, epv);
 }
 }  // namespace mi355norm

@@ -122,32 +122,32 @@ hipError_t launch_bwd_split(int op, const BwdCall& c, const Plan& p, float2* par
 }
 
 // ---------------------------------------------------------------------------
-// split backward, single cooperative pass
+// split backward, single pass
 // ---------------------------------------------------------------------------
 
 template <class T, bool RMS, int EPV>
-const void* bwd_coop_kernel() {
-    return reinterpret_cast<const void*>(&norm_bwd_coop_kernel<T, RMS, kBwdCoopWG, kBwdCoopVPL, EPV>);
+const void* bwd_pass_kernel() {
+    return reinterpret_cast<const void*>(&norm_bwd_pass_kernel<T, RMS, kBwdPassWG, kBwdPassVPL, EPV>);
 }
 
 template <class T>
-int bwd_coop_blocks_per_cu(int op, int epv) {
+int bwd_pass_blocks_per_cu(int op, int epv) {
     if (op != OP_LN && op != OP_RMS) return 0;
     const void* f = nullptr;
     (void)with_epv<T>(epv, [&](auto e) {
         constexpr int E = decltype(e)::value;
-        f = op == OP_RMS ? bwd_coop_kernel<T, true, E>() : bwd_coop_kernel<T, false, E>();
+        f = op == OP_RMS ? bwd_pass_kernel<T, true, E>() : bwd_pass_kernel<T, false, E>();
         return hipSuccess;
     });
     if (!f) return 0;
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, kBwdCoopWG, 0) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, kBwdPassWG, 0) != hipSuccess) return 0;
     return n;
 }
 
 template <class T, bool RMS, int EPV>
-hipError_t go_bwd_coop(const BwdCall& c, const Plan& p, float2* part, unsigned* sync, unsigned need,
-                       unsigned spin_limit) {
+hipError_t go_bwd_pass(const BwdCall& c, const Plan& p, unsigned long long* slots, unsigned* dep,
+                       unsigned wait_ticks) {
     const St<T>* dy = static_cast<const St<T>*>(c.dy);
     const St<T>* x = static_cast<const St<T>*>(c.x);
     const St<T>* g = static_cast<const St<T>*>(c.gamma);
@@ -160,20 +160,20 @@ hipError_t go_bwd_coop(const BwdCall& c, const Plan& p, float2* part, unsigned* 
     int N = c.N;
     int64_t ldy = c.ldy, ldx = c.ldx, lddx = c.lddx;
     int S = p.chunks, teams = p.teams;
-    void* args[] = {&dy, &x, &g, &mean, &rstd, &dx, &pg, &pb, &part, &sync, &M, &N, &ldy, &ldx, &lddx, &S,
-                    &teams, &need, &spin_limit};
-    return hipLaunchCooperativeKernel(bwd_coop_kernel<T, RMS, EPV>(), dim3((unsigned)(teams * S)),
-                                      dim3(kBwdCoopWG), args, 0, c.stream);
+    void* args[] = {&dy, &x, &g, &mean, &rstd, &dx, &pg, &pb, &slots, &dep, &M, &N, &ldy, &ldx, &lddx, &S,
+                    &teams, &wait_ticks};
+    return hipLaunchKernel(bwd_pass_kernel<T, RMS, EPV>(), dim3((unsigned)(teams * S)), dim3(kBwdPassWG), args, 0,
+                           c.stream);
 }
 
 template <class T>
-hipError_t launch_bwd_coop(int op, const BwdCall& c, const Plan& p, float2* part, unsigned* sync, unsigned need,
-                           unsigned spin_limit) {
+hipError_t launch_bwd_pass(int op, const BwdCall& c, const Plan& p, unsigned long long* slots, unsigned* dep,
+                           unsigned wait_ticks) {
     if (op != OP_LN && op != OP_RMS) return hipErrorInvalidValue;
     return with_epv<T>(p.epv, [&](auto epv) {
         constexpr int E = decltype(epv)::value;
-        return op == OP_RMS ? go_bwd_coop<T, true, E>(c, p, part, sync, need, spin_limit)
-                            : go_bwd_coop<T, false, E>(c, p, part, sync, need, spin_limit);
+        return op == OP_RMS ? go_bwd_pass<T, true, E>(c, p, slots, dep, wait_ticks)
+                            : go_bwd_pass<T, false, E>(c, p, slots, dep, wait_ticks);
     });
 }
 

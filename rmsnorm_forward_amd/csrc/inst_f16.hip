@@ -22,11 +22,11 @@ hipError_t launch_bwd_f16(int op, const BwdCall& c, const Plan& p) {
 hipError_t launch_bwd_split_f16(int op, const BwdCall& c, const Plan& p, float2* part, float2* rows, int accumulate) {
     return detail::launch_bwd_split<F16>(op, c, p, part, rows, accumulate);
 }
-hipError_t launch_bwd_coop_f16(int op, const BwdCall& c, const Plan& p, float2* part, unsigned* sync, unsigned need,
-                               unsigned spin_limit) {
-    return detail::launch_bwd_coop<F16>(op, c, p, part, sync, need, spin_limit);
+hipError_t launch_bwd_pass_f16(int op, const BwdCall& c, const Plan& p, unsigned long long* slots, unsigned* dep,
+                               unsigned wait_ticks) {
+    return detail::launch_bwd_pass<F16>(op, c, p, slots, dep, wait_ticks);
 }
-int bwd_coop_blocks_per_cu_f16(int op, int epv) {
-    return detail::bwd_coop_blocks_per_cu<F16>(op, epv);
+int bwd_pass_blocks_per_cu_f16(int op, int epv) {
+    return detail::bwd_pass_blocks_per_cu<F16>(op, epv);
 }
 }  // namespace mi355norm

@@ -23,12 +23,12 @@ hipError_t launch_bwd_f32(int op, const BwdCall& c, const Plan& p) {
 hipError_t launch_bwd_split_f32(int op, const BwdCall& c, const Plan& p, float2* part, float2* rows, int accumulate) {
     return detail::launch_bwd_split<F32>(op, c, p, part, rows, accumulate);
 }
-hipError_t launch_bwd_coop_f32(int op, const BwdCall& c, const Plan& p, float2* part, unsigned* sync, unsigned need,
-                               unsigned spin_limit) {
-    return detail::launch_bwd_coop<F32>(op, c, p, part, sync, need, spin_limit);
+hipError_t launch_bwd_pass_f32(int op, const BwdCall& c, const Plan& p, unsigned long long* slots, unsigned* dep,
+                               unsigned wait_ticks) {
+    return detail::launch_bwd_pass<F32>(op, c, p, slots, dep, wait_ticks);
 }
-int bwd_coop_blocks_per_cu_f32(int op, int epv) {
-    return detail::bwd_coop_blocks_per_cu<F32>(op, epv);
+int bwd_pass_blocks_per_cu_f32(int op, int epv) {
+    return detail::bwd_pass_blocks_per_cu<F32>(op, epv);
 }
 hipError_t launch_colsum(const float* part_g, float* out_g, const float* part_b, float* out_b, int64_t P, int N,
                          hipStream_t stream) {

@@ -124,8 +124,12 @@ struct Chunk {
     // LayerNorm: (mean of x - K, M2 about that mean) over the chunk's valid
     // elements; RMSNorm: (sum of squares, 0).  Uses both LDS slot sets.
     // Masked vectors are dropped by one select per vector.
+    // Contraction is off: every inlined copy (the single pass computes the
+    // same chunk's partial in two places) performs exactly these IEEE
+    // operations, so all copies give the same bits.
     template <bool RMS>
     __device__ __forceinline__ float2 partial(float K, int NV, float (*red)[WG / 64]) {
+#pragma clang fp contract(off)
         if constexpr (RMS) {
             float q = 0.0f;
 #pragma unroll
@@ -211,73 +215,11 @@ struct Chunk {
 // Lane l folds partials l, l+64, l+128, ... in order; the 64 lane states are
 // then merged by a butterfly whose every step puts the lower lane's state
 // first, so partners compute bitwise-identical results.
-// A partial as one 64-bit atomic access at agent scope: coherent across the
-// XCDs' L2 caches without any cache write-back or invalidation.
-__device__ __forceinline__ void store_partial_coherent(float2* p, float2 v) {
-    const unsigned long long bits =
-        ((unsigned long long)__float_as_uint(v.y) << 32) | (unsigned long long)__float_as_uint(v.x);
-    __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), bits, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ float2 load_partial_coherent(const float2* p) {
-    const unsigned long long bits = __hip_atomic_load(
-        reinterpret_cast<unsigned long long*>(const_cast<float2*>(p)), __ATOMIC_RELAXED,
-        __HIP_MEMORY_SCOPE_AGENT);
-    return make_float2(__uint_as_float((unsigned)bits), __uint_as_float((unsigned)(bits >> 32)));
-}
-
-// The per-row barrier of the single-pass kernels.  Row r's counters sit in
-// one 256-byte line at sync + 64 r (arrivals) and + 32 (departures), so rows
-// in flight never share a line; they are zero at launch and again at exit.
-// Every member is called by one thread of the workgroup.
-struct RowBarrier {
-    unsigned* arrived;
-    unsigned* departed;
-    __device__ RowBarrier(unsigned* sync, int64_t row) : arrived(sync + row * 64), departed(arrived + 32) {}
-
-    // publish this workgroup's partial (a coherent 64-bit store, complete
-    // before the count), then count its arrival
-    __device__ void arrive(float2* slot, float2 v) const {
-        store_partial_coherent(slot, v);
-        __builtin_amdgcn_s_waitcnt(0);
-        __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-
-    // wait for `need` arrivals (the row's chunk count; a host test hook can
-    // ask for one more, which never comes), polling with relaxed loads at most
-    // spin_limit times so that a broken co-residency assumption cannot hang;
-    // returns 1 if the bound was reached
-    __device__ int wait(unsigned need, unsigned spin_limit) const {
-        unsigned spins = 0;
-        while (__hip_atomic_load(arrived, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
-            if (++spins > spin_limit) return 1;
-            __builtin_amdgcn_s_sleep(8);
-        }
-        return 0;
-    }
-
-    // count this workgroup's departure (it has read every partial); the last
-    // of the row's S returns both counters to zero for the next call
-    __device__ void depart(int S) const {
-        if (__hip_atomic_fetch_add(departed, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)S - 1) {
-            __hip_atomic_store(arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(departed, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
-};
-
 // start of row `row` of an output of the I/O dtype, or of FP8 codes
 template <class T, bool Q8>
 __device__ __forceinline__ void* row_out(void* y, int64_t row, int64_t ldy) {
     if constexpr (Q8) return static_cast<uint8_t*>(y) + row * ldy;
     else return static_cast<typename T::storage*>(y) + row * ldy;
-}
-
-template <bool COHERENT>
-__device__ __forceinline__ float2 read_partial(const float2* p) {
-    if constexpr (COHERENT) return load_partial_coherent(p);
-    else return *p;
 }
 
 // Merge a row's S partials (read(c) gives partial c; S arbitrary) inside one

@@ -7,7 +7,7 @@ the ABI takes, short rows forced onto the split path (ragged chunk tails),
 several batches of rows with a short last batch (the accumulating partial
 rows), a sums grid far smaller than its work items, unaligned pointers,
 strided rows, in-place dx, the optional gamma / dgamma / dbeta, M = 0, and
-bitwise determinism; the single cooperative pass (on request) on long and
+bitwise determinism; the single pass (on request) on long and
 short rows, in place, deterministic, and with its bounded wait forced to
 time out from the host.
 """
@@ -185,7 +185,7 @@ def test_split_agrees_with_row_kernel(monkeypatch):
 
 
 # ---------------------------------------------------------------------------
-# the single cooperative pass (MI355NORM_PATH=splitcoop)
+# the single pass (MI355NORM_PATH=splitcoop)
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("dtype,N,M", [("bf16", 40000, 24), ("f16", 65544, 9), ("bf16", 1 << 20, 6),
@@ -193,13 +193,13 @@ def test_split_agrees_with_row_kernel(monkeypatch):
                                        ("bf16", 8192, 700), ("f16", 7, 50)])
 @pytest.mark.parametrize("op", ["ln", "rms"])
 def test_single_pass_split_backward(monkeypatch, op, dtype, N, M):
-    """Every chunk of a row in its own co-resident workgroup, the row sums
-    exchanged through a per-row barrier, dy and x read once; rows past the
-    team count are walked by the teams."""
+    """Every chunk of a row in its own workgroup, the chunk sums exchanged
+    through the row's slots, dy and x read once; rows past the team count are
+    walked by the teams."""
     monkeypatch.setenv("MI355NORM_PATH", "splitcoop")
     aligned = (N * E[dtype]) % 16 == 0
     p = plan(op, M, N, dtype, aligned)
-    assert p["mode"] == "coop", p
+    assert p["mode"] == "pass", p
     go(op, dtype, M, N, seed=N + M)
 
 
@@ -212,19 +212,26 @@ def test_single_pass_split_backward_in_place_and_deterministic(monkeypatch):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
-def test_single_pass_split_backward_bounded_wait(monkeypatch):
-    """Forced from the host, every row waits for one arrival more than it has
-    chunks, with a short bound: every workgroup stops waiting, the kernel
-    completes, the failure is visible (dx all NaN), the counters are back at
-    zero, and the next normal call is correct."""
+@pytest.mark.parametrize("op,dtype,M,N", [("ln", "bf16", 6, 1 << 18), ("rms", "f32", 5, 70001), ("ln", "f16", 40, 40000)])
+def test_single_pass_split_backward_recompute_gives_the_same_bits(monkeypatch, op, dtype, M, N):
+    """The bounded wait, forced from the host to give up at once: every
+    workgroup computes its rows' chunk sums from dy and x itself.  dx, dgamma
+    and dbeta must be the normal single pass's bits, and the next normal call
+    (slots and counters back at zero) must give them again."""
     monkeypatch.setenv("MI355NORM_PATH", "splitcoop")
-    dy, x, g, mean, rstd = inputs("ln", "bf16", 6, 1 << 18, 62)
+    dy, x, g, mean, rstd = inputs(op, dtype, M, N, 62 + M)
+    print(f"[bwd pass] {op} {dtype} M={M} N={N}: normal, recompute, normal", flush=True)
+    a = gpu_runner.run_bwd(op, dtype, dy, x, g, mean, rstd)
     monkeypatch.setenv("MI355NORM_FORCE_TIMEOUT", "1")
-    print("[bwd coop] forced timeout", flush=True)
-    dx, dg, db = gpu_runner.run_bwd("ln", "bf16", dy, x, g, mean, rstd)
-    assert np.isnan(oracle.widen(dx, "bf16")).all()
+    b = gpu_runner.run_bwd(op, dtype, dy, x, g, mean, rstd)
     monkeypatch.delenv("MI355NORM_FORCE_TIMEOUT")
-    go("ln", "bf16", 6, 1 << 18, seed=62)
+    c = gpu_runner.run_bwd(op, dtype, dy, x, g, mean, rstd)
+    for u, v, w in zip(a, b, c):
+        if u is None:
+            continue
+        assert np.array_equal(u.view(np.uint8), v.view(np.uint8)), "recompute path differs"
+        assert np.array_equal(u.view(np.uint8), w.view(np.uint8)), "call after the recompute differs"
+    go(op, dtype, M, N, seed=62 + M)
 
 
 @pytest.mark.parametrize("dtype,N,lddy,ldx,lddx,offset", [
@@ -239,11 +246,11 @@ def test_single_pass_split_backward_strided_rows(monkeypatch, op, dtype, N, lddy
     dy, x, g, mean, rstd = inputs(op, dtype, M, N, N + 67)
     aligned = offset == 0 and all((v * E[dtype]) % 16 == 0 for v in (N, lddy, ldx, lddx))
     p = plan(op, M, N, dtype, aligned)
-    assert p["mode"] == "coop"
-    print(f"[bwd coop] strided {op} {dtype} N={N} ld={lddy},{ldx},{lddx} offset={offset}", flush=True)
+    assert p["mode"] == "pass"
+    print(f"[bwd pass] strided {op} {dtype} N={N} ld={lddy},{ldx},{lddx} offset={offset}", flush=True)
     dx, dg, db = gpu_runner.run_bwd_strided(op, dtype, dy, x, g, mean, rstd, lddy=lddy, ldx=ldx, lddx=lddx,
                                             offset=offset)
-    parity.check_bwd(op, dtype, dy, x, g, mean, rstd, dx, dg, db, p, what=f"coop strided {op}")
+    parity.check_bwd(op, dtype, dy, x, g, mean, rstd, dx, dg, db, p, what=f"pass strided {op}")
 
 
 @pytest.mark.parametrize("op", ["ln", "rms"])
@@ -252,10 +259,10 @@ def test_single_pass_split_backward_optional_outputs_and_gamma(monkeypatch, op):
     M, N = 20, 40000
     dy, x, g, mean, rstd = inputs(op, "f32", M, N, 13)
     for gamma, want_g, want_b in [(None, True, True), (g, False, True), (g, True, False), (g, False, False)]:
-        print(f"[bwd coop] optional gamma={gamma is not None} dg={want_g} db={want_b}", flush=True)
+        print(f"[bwd pass] optional gamma={gamma is not None} dg={want_g} db={want_b}", flush=True)
         dx, dg, db = gpu_runner.run_bwd(op, "f32", dy, x, gamma, mean, rstd, want_g=want_g, want_b=want_b)
         parity.check_bwd(op, "f32", dy, x, gamma, mean, rstd, dx, dg, db, plan(op, M, N, "f32"),
-                         what=f"coop gamma={gamma is not None} dg={want_g} db={want_b}")
+                         what=f"pass gamma={gamma is not None} dg={want_g} db={want_b}")
 
 
 @pytest.mark.parametrize("mode", ["split", "splitcoop"])
