@@ -222,7 +222,7 @@ int norm_fwd(const norm_args *args, void *stream);
  * instead of in a workspace it allocates.  That covers every shape of the
  * default two-kernel schedule (at most about 576 KiB of partials per batch
  * of rows); a call needing more (a larger MI355NORM_SPLIT_BATCH) returns
- * NORM_ERR_SCRATCH, and the single-pass schedule (MI355NORM_PATH=splitcoop)
+ * NORM_ERR_SCRATCH, and the single-pass schedule (MI355NORM_PATH=splitpass)
  * NORM_ERR_BAD_ARG, both before any launch.  No hipMalloc, hipFree or
  * allocating routine is called.  Calls on one GPU share the array: calls
  * that overlap in time on one GPU (different streams, or graph replays
@@ -328,7 +328,7 @@ int norm_describe(int op, int64_t M, int64_t N, int dtype, int aligned,
  * As norm_describe, for ln_bwd (rms = 0) or rms_bwd (rms = 1): path ("bwd"
  * or "bwd_split"), lanes per row, vectors per lane, workgroup size, grid and
  * the number of partial rows of dgamma and dbeta; for split rows also the
- * mode ("three" kernels per batch, or "coop", the single cooperative pass
+ * mode ("three" kernels per batch, or "pass", the single pass in one launch,
  * taken only on request), chunks per row and rows per batch.
  */
 int norm_bwd_describe(int rms, int64_t M, int64_t N, int dtype, int aligned,

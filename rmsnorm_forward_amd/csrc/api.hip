@@ -27,15 +27,16 @@
 // lane, or 4-lane teams, always lost.
 //
 // Test/benchmark hooks (environment, read per call):
-//   MI355NORM_PATH = rows | split | split2 | split1 | splitcoop
+//   MI355NORM_PATH = rows | split | split2 | split1 | splitpass
 //                                       force the path (rows only if it fits;
 //                                       split2 the two-kernel split; split1 or
-//                                       splitcoop the single pass, only if a
-//                                       row's chunks fit resident, and not for
-//                                       the residual add, which keeps two
-//                                       kernels; for the backward, split and
-//                                       split2 take the three-kernel split,
-//                                       split1 / splitcoop its single pass)
+//                                       splitpass the single pass, only if
+//                                       every chunk of a row can be resident
+//                                       at once, and not for the residual
+//                                       add, which keeps two kernels; for the
+//                                       backward, split and split2 take the
+//                                       three-kernel split, split1 /
+//                                       splitpass its single pass)
 //   MI355NORM_SPLIT_BATCH = <bytes>     bytes of x per two-kernel split batch
 //                                       (of dy and x in the split backward)
 //   MI355NORM_TILE = <team>x<vpl>       force the row-kernel tile
@@ -207,7 +208,7 @@ Overrides read_overrides() {
         if (!std::strcmp(s, "rows")) o.path = PATH_ROWS;
         else if (!std::strcmp(s, "split")) o.path = PATH_SPLIT;
         else if (!std::strcmp(s, "split2")) { o.path = PATH_SPLIT; o.split_mode = SPLIT_TWO; }
-        else if (!std::strcmp(s, "splitcoop") || !std::strcmp(s, "split1")) {
+        else if (!std::strcmp(s, "splitpass") || !std::strcmp(s, "split1")) {
             o.path = PATH_SPLIT;
             o.split_mode = SPLIT_PASS;
         }

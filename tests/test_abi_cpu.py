@@ -543,7 +543,7 @@ def test_noalloc_validates_and_refuses_on_the_host(monkeypatch):
     # a forced split of 2^20 short rows needs 8 MiB of partials in one batch
     monkeypatch.setenv("MI355NORM_PATH", "split")
     assert rn.norm_fwd_noalloc("rms", "f32", 1 << 20, 64, fake, fake + (1 << 30), eps=1e-6) == 8
-    monkeypatch.setenv("MI355NORM_PATH", "splitcoop")
+    monkeypatch.setenv("MI355NORM_PATH", "splitpass")
     assert rn.norm_fwd_noalloc("rms", "f32", 40, 100000, fake, fake + (1 << 30), eps=1e-6) == BAD_ARG
 
 

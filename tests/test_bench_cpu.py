@@ -74,20 +74,20 @@ def test_launches_per_step_follow_the_plan(monkeypatch):
     N = 1 << 20
     assert bench.launches_per_step(rn.norm_describe("ln", 16384, 8192, "bf16"), 16384) == 1
     assert bench.launches_per_step(rn.norm_describe("ln", 64, N, "bf16"), 64) == 2
-    monkeypatch.setenv("MI355NORM_PATH", "splitcoop")
+    monkeypatch.setenv("MI355NORM_PATH", "splitpass")
     try:
-        coop = rn.norm_describe("ln", 64, N, "bf16")
+        one = rn.norm_describe("ln", 64, N, "bf16")
     except RuntimeError:          # no device here: the single pass cannot be planned
-        coop = None
-    if coop is not None:
-        assert bench.launches_per_step(coop, 64) == 1
+        one = None
+    if one is not None:
+        assert bench.launches_per_step(one, 64) == 1
     # plan strings as the library writes them for the single passes
     fwd_pass = ("path=split mode=pass wg=512 vpl=8 epv=8 chunks=32 apply_wg=0 apply_vpl=0 apply_chunks=0 "
                 "teams=16 batch_rows=64 grid=512 apply_grid=0 work=2048 workspace=32768")
     assert bench.launches_per_step(fwd_pass, 64) == 1
-    bwd_coop = ("path=bwd_split mode=coop op=ln wg=1024 sums_vpl=2 apply_vpl=2 epv=8 chunks=64 apply_chunks=0 "
+    bwd_pass = ("path=bwd_split mode=pass op=ln wg=1024 sums_vpl=2 apply_vpl=2 epv=8 chunks=64 apply_chunks=0 "
                 "batch_rows=64 grid=256 apply_grid=0 partial_rows=4")
-    assert bench.launches_per_step(bwd_coop, 64) == 2           # the pass, then the column sums
+    assert bench.launches_per_step(bwd_pass, 64) == 2           # the pass, then the column sums
     monkeypatch.delenv("MI355NORM_PATH")
     monkeypatch.setenv("MI355NORM_SPLIT_BATCH", str(3 * N * 2))   # forward: 3 rows of x per batch
     assert bench.launches_per_step(rn.norm_describe("ln", 7, N, "bf16"), 7) == 6

@@ -185,7 +185,7 @@ def test_split_agrees_with_row_kernel(monkeypatch):
 
 
 # ---------------------------------------------------------------------------
-# the single pass (MI355NORM_PATH=splitcoop)
+# the single pass (MI355NORM_PATH=splitpass)
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("dtype,N,M", [("bf16", 40000, 24), ("f16", 65544, 9), ("bf16", 1 << 20, 6),
@@ -196,7 +196,7 @@ def test_single_pass_split_backward(monkeypatch, op, dtype, N, M):
     """Every chunk of a row in its own workgroup, the chunk sums exchanged
     through the row's slots, dy and x read once; rows past the team count are
     walked by the teams."""
-    monkeypatch.setenv("MI355NORM_PATH", "splitcoop")
+    monkeypatch.setenv("MI355NORM_PATH", "splitpass")
     aligned = (N * E[dtype]) % 16 == 0
     p = plan(op, M, N, dtype, aligned)
     assert p["mode"] == "pass", p
@@ -204,7 +204,7 @@ def test_single_pass_split_backward(monkeypatch, op, dtype, N, M):
 
 
 def test_single_pass_split_backward_in_place_and_deterministic(monkeypatch):
-    monkeypatch.setenv("MI355NORM_PATH", "splitcoop")
+    monkeypatch.setenv("MI355NORM_PATH", "splitpass")
     _, (dx0, dg0, db0) = go("ln", "bf16", 40, 70000, seed=5)
     _, (dx1, dg1, db1) = go("ln", "bf16", 40, 70000, seed=5)
     _, (dx2, dg2, db2) = go("ln", "bf16", 40, 70000, seed=5, inplace="dy")
@@ -218,7 +218,7 @@ def test_single_pass_split_backward_recompute_gives_the_same_bits(monkeypatch, o
     workgroup computes its rows' chunk sums from dy and x itself.  dx, dgamma
     and dbeta must be the normal single pass's bits, and the next normal call
     (slots and counters back at zero) must give them again."""
-    monkeypatch.setenv("MI355NORM_PATH", "splitcoop")
+    monkeypatch.setenv("MI355NORM_PATH", "splitpass")
     dy, x, g, mean, rstd = inputs(op, dtype, M, N, 62 + M)
     print(f"[bwd pass] {op} {dtype} M={M} N={N}: normal, recompute, normal", flush=True)
     a = gpu_runner.run_bwd(op, dtype, dy, x, g, mean, rstd)
@@ -241,7 +241,7 @@ def test_single_pass_split_backward_recompute_gives_the_same_bits(monkeypatch, o
 ])
 @pytest.mark.parametrize("op", ["ln", "rms"])
 def test_single_pass_split_backward_strided_rows(monkeypatch, op, dtype, N, lddy, ldx, lddx, offset):
-    monkeypatch.setenv("MI355NORM_PATH", "splitcoop")
+    monkeypatch.setenv("MI355NORM_PATH", "splitpass")
     M = 7
     dy, x, g, mean, rstd = inputs(op, dtype, M, N, N + 67)
     aligned = offset == 0 and all((v * E[dtype]) % 16 == 0 for v in (N, lddy, ldx, lddx))
@@ -255,7 +255,7 @@ def test_single_pass_split_backward_strided_rows(monkeypatch, op, dtype, N, lddy
 
 @pytest.mark.parametrize("op", ["ln", "rms"])
 def test_single_pass_split_backward_optional_outputs_and_gamma(monkeypatch, op):
-    monkeypatch.setenv("MI355NORM_PATH", "splitcoop")
+    monkeypatch.setenv("MI355NORM_PATH", "splitpass")
     M, N = 20, 40000
     dy, x, g, mean, rstd = inputs(op, "f32", M, N, 13)
     for gamma, want_g, want_b in [(None, True, True), (g, False, True), (g, True, False), (g, False, False)]:
@@ -265,7 +265,7 @@ def test_single_pass_split_backward_optional_outputs_and_gamma(monkeypatch, op):
                          what=f"pass gamma={gamma is not None} dg={want_g} db={want_b}")
 
 
-@pytest.mark.parametrize("mode", ["split", "splitcoop"])
+@pytest.mark.parametrize("mode", ["split", "splitpass"])
 def test_split_backward_unaligned_column_sums(monkeypatch, mode):
     """One row group writes dgamma / dbeta itself (batches of one row force
     it on the three-kernel form; one team on the single pass): with those

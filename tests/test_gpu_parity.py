@@ -142,7 +142,7 @@ def test_edge_shapes(op, dtype, N):
     compare(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, y, mean, rstd, what=f"N={N}")
 
 
-@pytest.mark.parametrize("mode", ["split2", "splitcoop"])
+@pytest.mark.parametrize("mode", ["split2", "splitpass"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("op", ["ln", "rms"])
 @pytest.mark.parametrize("N", [10, 1000, 8192, 65544, 300000])
@@ -282,7 +282,7 @@ def test_stress_rows_small_bf16():
     compare("ln", "bf16", inp["x"], inp["gamma"], inp["beta"], 1e-5, y, mean, rstd, what="bf16 stress")
 
 
-@pytest.mark.parametrize("path", ["auto", "split2", "splitcoop"])
+@pytest.mark.parametrize("path", ["auto", "split2", "splitpass"])
 def test_bitwise_deterministic(monkeypatch, path):
     if path != "auto":
         monkeypatch.setenv("MI355NORM_PATH", path)
@@ -324,7 +324,7 @@ def test_two_kernel_split_is_the_default_and_agrees_with_the_single_pass(monkeyp
     d = dict(kv.split("=") for kv in rn.norm_describe("ln", 64, 1 << 20, "bf16").split())
     assert d["path"] == "split" and d["mode"] == "two", d
     inp = inputs("ln", "bf16", 40, 1 << 18, seed=61)
-    monkeypatch.setenv("MI355NORM_PATH", "splitcoop")
+    monkeypatch.setenv("MI355NORM_PATH", "splitpass")
     a = run("ln", "bf16", inp["x"], inp["gamma"], inp["beta"], 1e-5)
     monkeypatch.delenv("MI355NORM_PATH")
     b = run("ln", "bf16", inp["x"], inp["gamma"], inp["beta"], 1e-5)
@@ -348,7 +348,7 @@ def test_split_row_batches(monkeypatch, op, dtype, N, offset):
     compare(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, y, mean, rstd, what=f"batches N={N}")
 
 
-@pytest.mark.parametrize("mode", ["split2", "splitcoop"])
+@pytest.mark.parametrize("mode", ["split2", "splitpass"])
 def test_split_workspace_reused_across_shapes(monkeypatch, mode):
     """Split calls of different shapes back to back on one stream share the
     kept workspace; each must see its counters at zero (a regression test:
@@ -434,7 +434,7 @@ def test_add_rms_in_place(dtype, N):
     compare_add(dtype, inp["x"], inp["res"], inp["gamma"], 1e-6, *b, what="in place")
 
 
-@pytest.mark.parametrize("mode", ["split2", "splitcoop"])
+@pytest.mark.parametrize("mode", ["split2", "splitpass"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("N", [1000, 8192, 65544, 300000])
 def test_add_rms_forced_split(monkeypatch, dtype, N, mode):
@@ -530,7 +530,7 @@ def test_add_rms_fp8(dtype, N):
     assert np.array_equal(qi, q) and np.array_equal(hi.view(np.uint8), h.view(np.uint8))
 
 
-@pytest.mark.parametrize("mode", ["split2", "splitcoop"])
+@pytest.mark.parametrize("mode", ["split2", "splitpass"])
 @pytest.mark.parametrize("add", [False, True])
 def test_fp8_forced_split(monkeypatch, mode, add):
     monkeypatch.setenv("MI355NORM_PATH", mode)

@@ -91,7 +91,7 @@ def test_noalloc_refuses_what_its_scratch_cannot_hold(monkeypatch):
     st = rn.norm_fwd_noalloc("rms", "f32", Ms, Ns, xs.data_ptr(), ys.data_ptr(), eps=1e-6,
                              stream=torch.cuda.current_stream().cuda_stream)
     assert st == rn.NORM_ERR_SCRATCH, rn.STATUS.get(st)
-    monkeypatch.setenv("MI355NORM_PATH", "splitcoop")
+    monkeypatch.setenv("MI355NORM_PATH", "splitpass")
     st = rn.norm_fwd_noalloc("rms", "f32", M, N, x.data_ptr(), y.data_ptr(), eps=1e-6,
                              stream=torch.cuda.current_stream().cuda_stream)
     assert st == rn.NORM_ERR_BAD_ARG, rn.STATUS.get(st)
