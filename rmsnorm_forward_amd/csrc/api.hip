@@ -331,6 +331,18 @@ int make_plan(int op, int64_t M, int64_t N, int dtype, bool aligned, const Overr
             if (p->epv > 1 && M <= kWaveTileMaxRows)
                 for (int c : kWaveTileVpls)
                     if (NV == int64_t(64) * c) { team = 64; vpl = c; }
+            // RMSNorm fp32 rows of 2048: two rows per wavefront, 16 vectors
+            // per lane (every load issued up front) beat one row per
+            // wavefront in three separate runs (65536 x 2048, us: 170.3 vs
+            // 172.2, 173.4 vs 174.8, 169.6 vs 171.4).  Not taken elsewhere:
+            // bf16 rows of 2048 32 x 8 86.4 vs 64 x 4 84.5; fp32 rows of
+            // 1024 16 x 16 172.8 vs 128 x 2 170.5, of 4096 64 x 16 171.5 vs
+            // 512 x 2 170.4; the residual add would hold x and the residual
+            // (128 VGPRs) before its first use
+            if (op == OP_RMS && dtype == NORM_F32 && p->epv == 4 && NV == 512) {
+                team = 32;
+                vpl = 16;
+            }
         }
         p->team = team;
         p->vpl = vpl;

@@ -191,7 +191,7 @@ def parse(desc):
     ("ln", 128, 1024, "f32", dict(path="rows", team="128", vpl="2", epv="4")),
     ("rms", 8192, 4096, "f32", dict(path="rows", team="512", vpl="2", epv="4")),
     ("ln", 16384, 8192, "bf16", dict(path="rows", team="256", vpl="4", epv="8")),
-    ("rms", 65536, 2048, "f32", dict(path="rows", team="256", vpl="2", epv="4")),
+    ("rms", 65536, 2048, "f32", dict(path="rows", team="32", vpl="16", epv="4", rows_per_wg="8")),
     ("rms", 65536, 2048, "bf16", dict(path="rows", team="64", vpl="4", epv="8")),
     ("ln", 4096, 5120, "bf16", dict(path="rows", team="64", vpl="10", epv="8")),
     ("ln", 64, 1 << 20, "bf16", dict(path="split", mode="two", chunks="64", apply_chunks="64", epv="8",
