@@ -214,16 +214,20 @@ int norm_fwd(const norm_args *args, void *stream);
 /*
  * norm_fwd without any allocation, for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that
- * forbid hipMalloc.  Same arguments, conventions and results as norm_fwd
- * (the very same kernels), but rows too long for one workgroup keep their
- * per-chunk partial statistics in a fixed 1 MiB device array that the
- * library holds on every GPU it runs on until the process exits (its address
- * is looked up on the first call on each device, with that device current),
- * instead of in a workspace it allocates.  That covers every shape of the
- * default two-kernel schedule (at most about 576 KiB of partials per batch
- * of rows); a call needing more (a larger MI355NORM_SPLIT_BATCH) returns
- * NORM_ERR_SCRATCH, and the single-pass schedule (MI355NORM_PATH=splitpass)
- * NORM_ERR_BAD_ARG, both before any launch.  No hipMalloc, hipFree or
+ * forbid hipMalloc.  Same arguments and conventions as norm_fwd, and the same
+ * kernels, but rows too long for one workgroup always run the two-kernel
+ * schedule, with their per-chunk partial statistics in a fixed 1 MiB device
+ * array that the library holds on every GPU it runs on until the process
+ * exits (its address is looked up on the first call on each device, with
+ * that device current), instead of in a workspace it allocates.  Where
+ * norm_fwd picks the two kernels the results are its bits; where it picks
+ * the single pass (RMSNorm, fp32 LayerNorm; see norm_describe) the two
+ * forms chunk rows differently and agree within rounding.  1 MiB covers
+ * every shape of the two-kernel schedule at its default batch (at most
+ * about 576 KiB of partials per batch of rows); a call needing more (a
+ * larger MI355NORM_SPLIT_BATCH) returns NORM_ERR_SCRATCH, and an explicit
+ * request for the single pass (MI355NORM_PATH=splitpass) NORM_ERR_BAD_ARG,
+ * both before any launch.  No hipMalloc, hipFree or
  * allocating routine is called.  Calls on one GPU share the array: calls
  * that overlap in time on one GPU (different streams, or graph replays
  * overlapping eager calls) race on it and must be ordered by the caller.
@@ -315,7 +319,11 @@ const char *norm_last_error(void);
 /*
  * Describe, without launching anything, how a call with these arguments
  * would be executed: path ("rows" or "split"), lanes per row, 16-byte vectors
- * per lane, workgroup size, grid size, and the vector width.  `op` is 0 for
+ * per lane, workgroup size, grid size, and the vector width; for split rows
+ * the mode: "pass" (one launch, x read once: RMSNorm and fp32 LayerNorm on
+ * 16-byte vectors, when every chunk of a row can be resident on the current
+ * device) or "two" (two kernels per batch of rows: LayerNorm with 16-bit
+ * I/O, the residual add, element-wise rows, or no device present).  `op` is 0 for
  * LayerNorm, 1 for RMSNorm, 2 for residual add + RMSNorm, 3 and 4 for the
  * same two RMSNorms with FP8 output; `aligned` says whether every pointer is
  * 16-byte aligned.  Writes at most buflen bytes (NUL-terminated) into buf and
@@ -329,7 +337,7 @@ int norm_describe(int op, int64_t M, int64_t N, int dtype, int aligned,
  * or "bwd_split"), lanes per row, vectors per lane, workgroup size, grid and
  * the number of partial rows of dgamma and dbeta; for split rows also the
  * mode ("three" kernels per batch, or "pass", the single pass in one launch,
- * taken only on request), chunks per row and rows per batch.
+ * taken only on request: it was slower), chunks per row and rows per batch.
  */
 int norm_bwd_describe(int rms, int64_t M, int64_t N, int dtype, int aligned,
                       char *buf, int buflen);

@@ -13,18 +13,21 @@
 //               reduction across the row's wavefronts;
 //   long rows   (beyond 1024 lanes x 8 vectors): split across workgroups
 //               in chunks; per-chunk partial statistics merged in chunk order
-//               (Chan).  Two kernels per batch of rows holding about 256 MiB
-//               of x: partials (x read through the caches), then merge +
-//               normalise (x read again, partly from the Infinity Cache).  A
+//               (Chan).  RMSNorm and fp32 LayerNorm on 16-byte vectors: a
 //               single pass (ordinary launch, x read once; every chunk's
 //               partial published in the row's slots, a bounded wait for the
-//               row's other chunks, recomputing the row's partials from x when
-//               the wait runs out) is available on request.
+//               row's other chunks, recomputing the row's partials from x
+//               when the wait runs out; the next row's chunk loaded into LDS
+//               during the wait).  LayerNorm with 16-bit I/O, the residual
+//               add and element-wise rows: two kernels per batch of rows
+//               holding about 256 MiB of x, partials (x read through the
+//               caches), then merge + normalise (x read again, partly from
+//               the Infinity Cache).
 // Measured on MI355X in steady state (200 back-to-back launches): bf16
 // 1024-wide RMSNorm 32x4 (2 rows per wavefront) 85.3 us vs 64x2 87.1, 16x8
 // 95.1; bf16 2048-wide 64x4 87.6 vs 32x8 99.4; fp32 2048-wide 256x2 175.0
-// vs 128x4 177.6, 64x8 189.6.  At these widths more than four vectors per
-// lane, or 4-lane teams, always lost.
+// vs 128x4 177.6, 64x8 189.6 (all before every load of a row was issued up
+// front; with that, fp32 2048-wide RMSNorm 32x16 won, see make_plan).
 //
 // Test/benchmark hooks (environment, read per call):
 //   MI355NORM_PATH = rows | split | split2 | split1 | splitpass
@@ -350,14 +353,25 @@ int make_plan(int op, int64_t M, int64_t N, int dtype, bool aligned, const Overr
         p->rows_per_wg = p->wg / team;
         p->work = (M + p->rows_per_wg - 1) / p->rows_per_wg;
     } else {
-        // Two kernels by default.  The single pass runs when asked for (not
-        // for the residual add, which keeps two kernels) and every chunk of
-        // at least one row can be resident.
-        if (o.split_mode == SPLIT_PASS && !has_add(op)) {
-            const int64_t pv = int64_t(kPassWG) * kPassVPL;
-            const int64_t pchunks = (NV + pv - 1) / pv;
-            const int64_t cap = resident_capacity(dtype, op, p->epv);
-            if (cap < pchunks) return NORM_ERR_BAD_ARG;
+        // The single pass (x read once) is the automatic choice for RMSNorm
+        // and fp32 LayerNorm rows of 16-byte vectors, where it beat the two
+        // kernels (steady state, us, two kernels vs single pass: RMS bf16
+        // 64 x 2^20 58.9 vs 53.9, 512 x 2^18 118.9 vs 102.2, 2048 x 2^18
+        // 468.9 vs 392.0; RMS f32 256 x 2^20 469.7 vs 396.2; LN f32
+        // 64 x 2^20 119.4 vs 113.5, 256 x 2^20 477.3 vs 429.8).  LayerNorm
+        // with 16-bit I/O keeps two kernels: level or slower in one pass
+        // (LN bf16 64 x 2^20 62.8 vs 63.2, 1024 x 131072 121.3 vs 124.4,
+        // f16 128 x 2^19 63.2 vs 65.9).  The residual add keeps two kernels.
+        // The pass runs when every chunk of a row can be resident; asked for
+        // and impossible, the call fails; chosen automatically and
+        // impossible (no device, say), the two kernels run.
+        const bool pass_auto = o.split_mode < 0 && p->epv > 1 && (op != OP_LN || dtype == NORM_F32);
+        const int64_t pv = int64_t(kPassWG) * kPassVPL;
+        const int64_t pchunks = (NV + pv - 1) / pv;
+        const int64_t cap = (o.split_mode == SPLIT_PASS || pass_auto) && !has_add(op)
+                                ? resident_capacity(dtype, op, p->epv) : 0;
+        if (o.split_mode == SPLIT_PASS && !has_add(op) && cap < pchunks) return NORM_ERR_BAD_ARG;
+        if ((o.split_mode == SPLIT_PASS || pass_auto) && !has_add(op) && cap >= pchunks) {
             p->split_mode = SPLIT_PASS;
             p->wg = kPassWG;
             p->vpl = kPassVPL;
@@ -500,7 +514,11 @@ int run(const Args& a, void* stream, bool noalloc = false) {
     const int64_t M = a.M, N = a.N;
     const int e = elem_bytes(dtype);
     Plan p;
-    st = make_plan(op, M, N, dtype, vector_aligned(a), read_overrides(), &p);
+    Overrides ov = read_overrides();
+    // the single pass needs the workspace's slots: without allocation the
+    // automatic choice is the two kernels (asked for, the pass is refused)
+    if (noalloc && ov.split_mode < 0) ov.split_mode = SPLIT_TWO;
+    st = make_plan(op, M, N, dtype, vector_aligned(a), ov, &p);
     if (st != NORM_OK) return st;
     NormCall c{a.x, a.res, a.gamma, a.beta, a.y, a.hout, a.mean, a.rstd, M, (int)N, a.eps, (hipStream_t)stream,
                has_q8(op) ? 1.0f / a.scale : 1.0f, Strides{a.ldx, a.ldr, a.ldy, a.ldh}};

@@ -388,6 +388,47 @@ def test_single_pass_recompute_gives_the_same_bits(monkeypatch, op, dtype, M, N,
     compare(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, *a, what="single pass")
 
 
+@pytest.mark.parametrize("op,dtype,M,N", [("ln", "bf16", 200, 1 << 18), ("rms", "f32", 150, 131080),
+                                           ("ln", "f16", 230, 131080)])
+def test_single_pass_teams_walk_several_rows(monkeypatch, op, dtype, M, N):
+    """More rows than teams of resident workgroups: each team walks several
+    rows, and from its second row on every workgroup normalises the chunk it
+    loaded into LDS while waiting on the previous row.  The normal run and a
+    run forced onto the recomputation path must give the same bits, and both
+    the oracle's values."""
+    import rmsnorm_forward_amd as rn
+    monkeypatch.setenv("MI355NORM_PATH", "split1")
+    plan = dict(kv.split("=") for kv in rn.norm_describe(op, M, N, dtype).split())
+    assert plan["mode"] == "pass" and int(plan["teams"]) < M, plan
+    inp = inputs(op, dtype, M, N, seed=90 + M)
+    print(f"[gpu] single pass, {plan['teams']} teams over {M} rows: {op} {dtype} N={N}", flush=True)
+    a = run(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5)
+    monkeypatch.setenv("MI355NORM_FORCE_TIMEOUT", "1")
+    b = run(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5)
+    monkeypatch.delenv("MI355NORM_FORCE_TIMEOUT")
+    for u, v in zip(a, b):
+        if u is not None:
+            assert np.array_equal(u.view(np.uint8), v.view(np.uint8)), "recompute path differs"
+    compare(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, *a, what="single pass, several rows per team")
+
+
+def test_split_mode_chosen_automatically():
+    """On the GPU, rows split across workgroups take the single pass for
+    RMSNorm (plain and with FP8 output) and fp32 LayerNorm on 16-byte
+    vectors, and the two kernels for LayerNorm with 16-bit I/O, the residual
+    add and rows that are not 16-byte vectors."""
+    import rmsnorm_forward_amd as rn
+    N = 1 << 20
+    mode = lambda op, dtype, aligned=True: dict(kv.split("=") for kv in
+                                                rn.norm_describe(op, 64, N, dtype, aligned=aligned).split())["mode"]
+    assert mode("rms", "bf16") == "pass" and mode("rms", "f32") == "pass" and mode("rms", "f16") == "pass"
+    assert mode("rms_fp8", "bf16") == "pass"
+    assert mode("ln", "f32") == "pass"
+    assert mode("ln", "bf16") == "two" and mode("ln", "f16") == "two"
+    assert mode("add_rms", "bf16") == "two" and mode("add_rms", "f32") == "two"
+    assert mode("rms", "bf16", aligned=False) == "two"
+
+
 def test_single_pass_plan():
     """On the GPU the single pass plans whole teams of resident workgroups:
     the grid is teams x chunks and holds at least one row's chunks."""

@@ -79,6 +79,26 @@ def test_noalloc_gives_norm_fwd_bits_on_consecutive_calls():
         assert np.all(np.isfinite(got[1]))
 
 
+def test_noalloc_takes_the_two_kernels_where_norm_fwd_takes_the_single_pass():
+    """RMSNorm rows split across workgroups: norm_fwd's automatic choice is
+    the single pass, whose per-row slots live in the allocated workspace;
+    norm_fwd_noalloc then runs the two-kernel form on its fixed scratch.  The
+    two chunk a row differently, so the bits may differ: each is compared
+    with the oracle at the parity bar (fp32 y within 2e-5, rstd within 1e-5
+    relative; bf16 y within one ulp)."""
+    import parity
+    import oracle
+    for k, (dtype, M, N) in enumerate([("f32", 4, 100000), ("bf16", 3, 1 << 18)]):
+        plan = dict(kv.split("=") for kv in rn.norm_describe("rms", M, N, dtype).split())
+        assert plan["path"] == "split" and plan["mode"] == "pass", plan
+        inp = _inputs("rms", dtype, M, N, 950 + k)
+        yr, rr = oracle.rms_fwd(inp["x"], inp["gamma"], dtype, 1e-6)
+        for fn in (rn.norm_fwd_noalloc, rn.norm_fwd):
+            y, rstd = _call(fn, "rms", dtype, M, N, 0, inp)
+            parity.check_y(y.reshape(M, N), yr, dtype, f"{fn.__name__} rms {dtype} {M}x{N}")
+            parity.check_stats(None, rstd, None, rr, 1e-6, f"{fn.__name__} rms {dtype} {M}x{N}")
+
+
 def test_noalloc_refuses_what_its_scratch_cannot_hold(monkeypatch):
     M, N = 40, 100000
     x = torch.zeros(M * N, dtype=torch.float32, device="cuda")
