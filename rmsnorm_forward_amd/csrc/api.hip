@@ -32,6 +32,7 @@
 // Test/benchmark hooks (environment, read per call):
 //   MI355NORM_PATH = rows | split | split2 | split1 | splitpass
 //                                       force the path (rows only if it fits;
+//                                       split the split form make_plan picks;
 //                                       split2 the two-kernel split; split1 or
 //                                       splitpass the single pass, only if
 //                                       every chunk of a row can be resident
