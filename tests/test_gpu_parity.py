@@ -412,6 +412,33 @@ def test_single_pass_teams_walk_several_rows(monkeypatch, op, dtype, M, N):
     compare(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, *a, what="single pass, several rows per team")
 
 
+@pytest.mark.parametrize("mode", ["auto", "split2", "split1"])
+@pytest.mark.parametrize("op,dtype,offset", [("ln", "bf16", 0), ("rms", "bf16", 0), ("rms", "f32", 0),
+                                             ("ln", "f32", 1)])
+def test_longest_rows(monkeypatch, op, dtype, offset, mode):
+    """Rows of 2^24 elements, the longest the library takes, in every split
+    form.  The single pass needs every chunk of a row resident at once: bf16
+    rows of 16-byte vectors fit (512 chunks of 512 lanes x 8 vectors), fp32
+    rows (1024 chunks) and element-wise rows do not, so asking for it is
+    refused before any launch, while the automatic choice falls back to the
+    two kernels."""
+    import rmsnorm_forward_amd as rn
+    M, N = 2, 1 << 24
+    aligned = offset == 0
+    if mode != "auto":
+        monkeypatch.setenv("MI355NORM_PATH", mode)
+    if mode == "split1" and (dtype == "f32" or not aligned):
+        with pytest.raises(RuntimeError):
+            rn.norm_describe(op, M, N, dtype, aligned=aligned)
+        return
+    plan = dict(kv.split("=") for kv in rn.norm_describe(op, M, N, dtype, aligned=aligned).split())
+    print(f"[gpu] longest rows {op} {dtype} offset={offset} {mode}: mode={plan['mode']} chunks={plan['chunks']}",
+          flush=True)
+    inp = inputs(op, dtype, M, N, seed=24 + offset)
+    y, mean, rstd = run(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, offset=offset)
+    compare(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, y, mean, rstd, what=f"N=2^24 {mode}")
+
+
 def test_split_mode_chosen_automatically():
     """On the GPU, rows split across workgroups take the single pass for
     RMSNorm (plain and with FP8 output) and fp32 LayerNorm on 16-byte
