@@ -90,8 +90,8 @@ constexpr int kBwdSplitSumsVPL = 2;
 constexpr int kBwdSplitSumsVPLElem = 16;
 constexpr int bwd_sums_vpl(int epv) { return epv == 1 ? kBwdSplitSumsVPLElem : kBwdSplitSumsVPL; }
 constexpr int kBwdSplitApplyVPL = 2;
-// split backward in one pass (on request): chunks of 1024 lanes x 2
-// vectors, one workgroup per chunk
+// split backward in one pass (on request; the three kernels measured
+// faster): chunks of 1024 lanes x 2 vectors, one workgroup per chunk
 constexpr int kBwdPassWG = 1024;
 constexpr int kBwdPassVPL = 2;
 constexpr int kBwdMinTeam = 8;
@@ -100,7 +100,7 @@ constexpr int kBwdMinTeam = 8;
 constexpr int kBwdWG = 1024;
 // Split-row chunk geometry: the two kernels of the two-kernel form (each
 // its own chunk size), and the single pass (fewer, larger chunks: fewer
-// arrivals per row at its barrier).
+// partials to wait for per row).
 #ifndef MI355_STATS_WG
 #define MI355_STATS_WG 256
 #endif
@@ -118,9 +118,10 @@ constexpr int kStatsVPL = MI355_STATS_VPL;
 constexpr int kApplyWG = MI355_APPLY_WG;
 constexpr int kApplyVPL = MI355_APPLY_VPL;
 // the forward's single pass: chunks of kPassWG lanes x kPassVPL vectors, two
-// workgroups per CU (measured on MI355X, LN bf16 64 x 2^20, us: 512 x 8
-// 66.6-68.6; 1024 x 8 72-78 (one per CU); 512 x 16 70-74; 512 x 4 79; 1024 x 4
-// 84-89)
+// workgroups per CU (measured on MI355X, LN bf16 64 x 2^20, us, without /
+// with the next row's chunk loaded into LDS during the wait: 512 x 8
+// 66.6-68.6 / 64.6-65.9; 1024 x 8 72-78 / 68.6-68.9 (one per CU); 512 x 16
+// 70-74 / 68.2-68.4; 512 x 4 79 / 74; 1024 x 4 84-89 / 72.7-72.9)
 #ifndef MI355_PASS_WG
 #define MI355_PASS_WG 512
 #endif
@@ -136,7 +137,8 @@ constexpr int kPassVPL = MI355_PASS_VPL;
 #define MI355_SPLIT_BATCH_BYTES (int64_t(256) << 20)
 #endif
 constexpr int64_t kSplitBatchBytes = MI355_SPLIT_BATCH_BYTES;
-// barrier counters of one row are 64 words (256 bytes) apart
+// single passes: the departure counters of consecutive rows are 64 words
+// (256 bytes) apart
 constexpr int kSyncStride = 64;
 
 hipError_t launch_rows_f32(int op, const NormCall& c, const Plan& p);
