@@ -258,6 +258,35 @@ def test_constant_rows(dtype, N):
     assert np.all(np.isnan(yv))
 
 
+@pytest.mark.parametrize("mode", ["split2", "split1"])
+@pytest.mark.parametrize("dtype,N", [("f32", 100000), ("bf16", 1 << 18)])
+def test_constant_split_rows(monkeypatch, mode, dtype, N):
+    """Constant rows split across workgroups, in both split forms: every
+    chunk's partial has M2 = 0, so the merged variance is exactly 0, y is
+    beta exactly, the mean is the constant and rstd = 1/sqrt(eps); with
+    eps = 0, rstd = inf and y = NaN.  RMSNorm of a zero row with eps = 0:
+    rstd = inf, y = NaN; of a constant row, the oracle's values."""
+    monkeypatch.setenv("MI355NORM_PATH", mode)
+    M = 6
+    x32 = np.repeat(np.array([0.0, 1.0, -3.5, 1000.0, 99840.0, 2.0 ** -10], np.float32)[:, None], N, axis=1)
+    x = workloads.to_storage(x32, dtype)
+    rng = np.random.default_rng(5)
+    g = workloads.to_storage(rng.uniform(0.5, 1.5, N).astype(np.float32), dtype)
+    b = workloads.to_storage(rng.normal(0, 0.1, N).astype(np.float32), dtype)
+    print(f"[gpu] constant split rows {mode} {dtype} N={N}", flush=True)
+    y, mean, rstd = run("ln", dtype, x, g, b, 1e-5)
+    assert np.array_equal(y, np.broadcast_to(b, y.shape))
+    assert np.array_equal(mean.astype(np.float64), oracle.widen(x[:, 0], dtype))
+    compare("ln", dtype, x, g, b, 1e-5, y, mean, rstd, what="constant split rows")
+    y0, _, rstd0 = run("ln", dtype, x, g, b, 0.0)
+    assert np.all(np.isinf(rstd0))
+    assert np.all(np.isnan(y0.astype(np.float64) if dtype == "f32" else oracle.widen(y0, dtype)))
+    yr, _, rr = run("rms", dtype, x, g, None, 1e-6)
+    compare("rms", dtype, x, g, None, 1e-6, yr, None, rr, what="constant split rows, rms")
+    yz, _, rz = run("rms", dtype, x[:1], g, None, 0.0)
+    assert np.isinf(rz[0]) and np.all(np.isnan(yz.astype(np.float64) if dtype == "f32" else oracle.widen(yz, dtype)))
+
+
 def test_rms_zero_row_eps0():
     x = np.zeros((3, 256), np.float32)
     y, _, rstd = run("rms", "f32", x, None, None, 0.0)
