@@ -65,8 +65,12 @@
  *
  *   Every pointer must be aligned to its element size.  16-byte aligned x, y,
  *   gamma, beta with N * sizeof(dtype) a multiple of 16 take the 128-bit
- *   vector path; anything else takes an element-wise path (slower, same
- *   results).  Buffers must not overlap (y may not alias x: no in-place use).
+ *   vector path.  When only x is off a 16-byte boundary (a view into a wider
+ *   buffer), rows that fit one workgroup still take it, x being read in
+ *   aligned 16-byte blocks realigned in registers (same tile, so the same
+ *   results as on an aligned copy of x).  Anything else takes an
+ *   element-wise path (slower, same accuracy).  Buffers must not overlap (y
+ *   may not alias x: no in-place use).
  *
  * Ownership: the caller allocates and owns every buffer and keeps it alive
  * until the stream has passed the call.  The library keeps no pointer to
@@ -204,7 +208,9 @@ typedef struct {
  * ld_* elements apart (ld_* < N, or an ld_* so large that the matrix does
  * not fit 2^63 bytes, is NORM_ERR_BAD_SHAPE; NULL args is NORM_ERR_NULL_ARG).
  * The 16-byte vector path is taken when every row start is 16-byte aligned
- * (EPV-byte for FP8 codes); otherwise the element-wise path.  Overlaps are
+ * (EPV-byte for FP8 codes); for LayerNorm, RMSNorm and RMSNorm with FP8
+ * output also when only the rows of x are not (any ld_x), on rows that fit
+ * one workgroup; otherwise the element-wise path.  Overlaps are
  * checked row by row when the two matrices share a stride or one is a
  * vector (interleaved matrices that share no byte are accepted), and over
  * their whole spans otherwise.  Returns a norm_status.
@@ -326,7 +332,8 @@ const char *norm_last_error(void);
  * I/O, the residual add, element-wise rows, or no device present).  `op` is 0 for
  * LayerNorm, 1 for RMSNorm, 2 for residual add + RMSNorm, 3 and 4 for the
  * same two RMSNorms with FP8 output; `aligned` says whether every pointer is
- * 16-byte aligned.  Writes at most buflen bytes (NUL-terminated) into buf and
+ * 16-byte aligned (1) or not (0), or that only the rows of x are not (2: the
+ * realigned row kernel where it applies, reported as "x=realigned").  Writes at most buflen bytes (NUL-terminated) into buf and
  * returns a norm_status.  For tests and the benchmark's reports.
  */
 int norm_describe(int op, int64_t M, int64_t N, int dtype, int aligned,

@@ -203,12 +203,15 @@ def norm_last_error() -> str:
     return _lib.norm_last_error().decode()
 
 
-def norm_describe(op: str, M: int, N: int, dtype, aligned: bool = True) -> str:
-    """How the library would run this call (path, tile, grid); launches nothing."""
+def norm_describe(op: str, M: int, N: int, dtype, aligned=True) -> str:
+    """How the library would run this call (path, tile, grid); launches nothing.
+    aligned: True (every pointer 16-byte aligned), False, or "x" (x alone is
+    not: the realigned row kernel)."""
     code = OPS[op]
     dt = DTYPE_NAMES.get(dtype, dtype)
     buf = ctypes.create_string_buffer(256)
-    st = _lib.norm_describe(code, int(M), int(N), int(dt), int(bool(aligned)), buf, 256)
+    al = 2 if aligned == "x" else int(bool(aligned))
+    st = _lib.norm_describe(code, int(M), int(N), int(dt), al, buf, 256)
     if st != NORM_OK:
         raise RuntimeError(norm_status_str(st))
     return buf.value.decode()

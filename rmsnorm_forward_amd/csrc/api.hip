@@ -23,6 +23,14 @@
 //               holding about 256 MiB of x, partials (x read through the
 //               caches), then merge + normalise (x read again, partly from
 //               the Infinity Cache).
+// x alone off a 16-byte boundary (a view into a wider buffer, any row
+// stride), the other operands aligned and N filling whole vectors: the row
+// tiles read x in aligned 16-byte blocks and realign them in registers (a
+// DPP shift from the next lane, byte alignment), LayerNorm, RMSNorm and
+// RMSNorm with FP8 output; split rows and the residual add take the
+// element-wise path.  Steady state, realigned vs aligned vs element-wise, us:
+// LN bf16 16384 x 8192 105.2 / 88.8 / 228.7, RMS bf16 65536 x 2048 88.5 /
+// 84.9 / 175.2, LN bf16 1024 x 32768 33.8 / 27.8 / 111.7.
 // Measured on MI355X in steady state (200 back-to-back launches): bf16
 // 1024-wide RMSNorm 32x4 (2 rows per wavefront) 85.3 us vs 64x2 87.1, 16x8
 // 95.1; bf16 2048-wide 64x4 87.6 vs 32x8 99.4; fp32 2048-wide 256x2 175.0
@@ -287,7 +295,9 @@ int64_t resident_capacity(int dtype, int op, int epv, bool bwd = false) {
 }
 
 // Returns NORM_OK and fills *p, or NORM_ERR_BAD_ARG if an override cannot run.
-int make_plan(int op, int64_t M, int64_t N, int dtype, bool aligned, const Overrides& o, Plan* p) {
+// realign: x is read through the realigned row kernel (aligned must be set)
+int make_plan(int op, int64_t M, int64_t N, int dtype, bool aligned, const Overrides& o, Plan* p,
+              bool realign = false) {
     const int e = elem_bytes(dtype);
     std::memset(p, 0, sizeof *p);
     p->epv = aligned ? 16 / e : 1;
@@ -332,7 +342,10 @@ int make_plan(int op, int64_t M, int64_t N, int dtype, bool aligned, const Overr
             // 256 x 4 18.4; 2048 x 5120 9.4 vs 11.0; LN bf16 4096 x 2560:
             // 64 x 5 9.0 vs 128 x 4 11.0; from 8192 rows on it is level or
             // slower: RMS bf16 8192 x 5120 32.5 vs 30.0)
-            if (p->epv > 1 && M <= kWaveTileMaxRows)
+            // (not with realigned x: the realignment's registers halve these
+            // tiles' occupancy; realigned 4096 x 5120: 64 x 10 23.4 us,
+            // 256 x 4 23.1, 512 x 2 21.9)
+            if (p->epv > 1 && M <= kWaveTileMaxRows && !realign)
                 for (int c : kWaveTileVpls)
                     if (NV == int64_t(64) * c) { team = 64; vpl = c; }
             // RMSNorm fp32 rows of 2048: two rows per wavefront, 16 vectors
@@ -343,7 +356,9 @@ int make_plan(int op, int64_t M, int64_t N, int dtype, bool aligned, const Overr
             // 1024 16 x 16 172.8 vs 128 x 2 170.5, of 4096 64 x 16 171.5 vs
             // 512 x 2 170.4; the residual add would hold x and the residual
             // (128 VGPRs) before its first use
-            if (op == OP_RMS && dtype == NORM_F32 && p->epv == 4 && NV == 512) {
+            // (not with realigned x: 256 VGPRs, one wavefront per SIMD;
+            // realigned 32 x 16 297 us, 256 x 2 177.5)
+            if (op == OP_RMS && dtype == NORM_F32 && p->epv == 4 && NV == 512 && !realign) {
                 team = 32;
                 vpl = 16;
             }
@@ -505,6 +520,21 @@ bool vector_aligned(const Args& a) {
     return al(a.y, 16) && (a.ldy * e) % 16 == 0;
 }
 
+// The row kernel's realigned form: x (any element-aligned address and row
+// stride) is read in aligned 16-byte blocks realigned in registers, while
+// gamma, beta and y keep the vector path's alignment.  LayerNorm, RMSNorm and
+// RMSNorm with FP8 output; N fills whole vectors.
+bool realign_ok(const Args& a) {
+    if (a.op != OP_LN && a.op != OP_RMS && a.op != OP_RMS_Q8) return false;
+    const int e = elem_bytes(a.dtype);
+    const int epv = 16 / e;
+    auto al = [](const void* q, int b) { return ((uintptr_t)q % (uintptr_t)b) == 0; };
+    if ((a.N * e) % 16 || !al(a.x, e)) return false;
+    if (!al(a.gamma, 16) || !al(a.beta, 16)) return false;
+    if (has_q8(a.op)) return al(a.y, epv) && a.ldy % epv == 0;
+    return al(a.y, 16) && (a.ldy * e) % 16 == 0;
+}
+
 // noalloc: the two-kernel split's partials go to `scratch` (no allocation
 // anywhere on the call's path); a call that needs more than it holds, or the
 // single pass, is refused before any launch.
@@ -519,7 +549,15 @@ int run(const Args& a, void* stream, bool noalloc = false) {
     // the single pass needs the workspace's slots: without allocation the
     // automatic choice is the two kernels (asked for, the pass is refused)
     if (noalloc && ov.split_mode < 0) ov.split_mode = SPLIT_TWO;
-    st = make_plan(op, M, N, dtype, vector_aligned(a), ov, &p);
+    // x alone misaligned: the realigned row kernel where the plan is a row
+    // tile, else the element-wise path
+    const bool aligned = vector_aligned(a);
+    bool realign = !aligned && realign_ok(a);
+    st = make_plan(op, M, N, dtype, aligned || realign, ov, &p, realign);
+    if (st == NORM_OK && realign && p.path != PATH_ROWS) {
+        realign = false;
+        st = make_plan(op, M, N, dtype, false, ov, &p);
+    }
     if (st != NORM_OK) return st;
     NormCall c{a.x, a.res, a.gamma, a.beta, a.y, a.hout, a.mean, a.rstd, M, (int)N, a.eps, (hipStream_t)stream,
                has_q8(op) ? 1.0f / a.scale : 1.0f, Strides{a.ldx, a.ldr, a.ldy, a.ldh}};
@@ -527,9 +565,9 @@ int run(const Args& a, void* stream, bool noalloc = false) {
     hipError_t err;
     if (p.path == PATH_ROWS) {
         switch (dtype) {
-        case NORM_F32: err = launch_rows_f32(op, c, p); break;
-        case NORM_BF16: err = launch_rows_bf16(op, c, p); break;
-        default: err = launch_rows_f16(op, c, p); break;
+        case NORM_F32: err = realign ? launch_rows_realigned_f32(op, c, p) : launch_rows_f32(op, c, p); break;
+        case NORM_BF16: err = realign ? launch_rows_realigned_bf16(op, c, p) : launch_rows_bf16(op, c, p); break;
+        default: err = realign ? launch_rows_realigned_f16(op, c, p) : launch_rows_f16(op, c, p); break;
         }
         return hip_ok(err, "row kernel launch") ? NORM_OK : NORM_ERR_HIP;
     }
@@ -983,13 +1021,20 @@ int norm_describe(int op, int64_t M, int64_t N, int dtype, int aligned, char* bu
     if (M < 0 || N < 1 || N > kMaxN) return NORM_ERR_BAD_SHAPE;
     const int e = elem_bytes(dtype);
     Plan p;
-    int st = make_plan(op, M, N, dtype, aligned && (N * e) % 16 == 0, read_overrides(), &p);
+    const bool vec = aligned && (N * e) % 16 == 0;
+    // aligned == 2: x alone off 16 bytes (the realigned row kernel, where the
+    // plan is a row tile and the operation has that form)
+    bool realign = vec && aligned == 2 && (op == OP_LN || op == OP_RMS || op == OP_RMS_Q8);
+    int st = make_plan(op, M, N, dtype, vec && (aligned != 2 || realign), read_overrides(), &p, realign);
+    if (st == NORM_OK && realign && p.path != PATH_ROWS)
+        st = make_plan(op, M, N, dtype, false, read_overrides(), &p);
     if (st != NORM_OK) return st;
     if (!buf || buflen <= 0) return NORM_OK;
     if (p.path == PATH_ROWS)
         std::snprintf(buf, (size_t)buflen,
-                      "path=rows team=%d vpl=%d epv=%d wg=%d rows_per_wg=%d grid=%lld work=%lld",
-                      p.team, p.vpl, p.epv, p.wg, p.rows_per_wg, (long long)p.grid, (long long)p.work);
+                      "path=rows team=%d vpl=%d epv=%d wg=%d rows_per_wg=%d grid=%lld work=%lld%s",
+                      p.team, p.vpl, p.epv, p.wg, p.rows_per_wg, (long long)p.grid, (long long)p.work,
+                      realign ? " x=realigned" : "");
     else
         std::snprintf(buf, (size_t)buflen,
                       "path=split mode=%s wg=%d vpl=%d epv=%d chunks=%d apply_wg=%d apply_vpl=%d "

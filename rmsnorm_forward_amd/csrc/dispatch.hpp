@@ -144,6 +144,11 @@ constexpr int kSyncStride = 64;
 hipError_t launch_rows_f32(int op, const NormCall& c, const Plan& p);
 hipError_t launch_rows_bf16(int op, const NormCall& c, const Plan& p);
 hipError_t launch_rows_f16(int op, const NormCall& c, const Plan& p);
+// row kernel with realigned loads of x (LayerNorm, RMSNorm, RMSNorm with FP8
+// output; 16-byte vectors; x misaligned, every other operand aligned)
+hipError_t launch_rows_realigned_f32(int op, const NormCall& c, const Plan& p);
+hipError_t launch_rows_realigned_bf16(int op, const NormCall& c, const Plan& p);
+hipError_t launch_rows_realigned_f16(int op, const NormCall& c, const Plan& p);
 // two-kernel split: ws holds M*chunks partials
 hipError_t launch_split_f32(int op, const NormCall& c, const Plan& p, float2* ws);
 hipError_t launch_split_bf16(int op, const NormCall& c, const Plan& p, float2* ws);

@@ -42,7 +42,7 @@ hipError_t with_epv(int epv, F&& f) {
 // row kernel
 // ---------------------------------------------------------------------------
 
-template <class T, bool RMS, bool ADD, bool Q8, int TEAM, int VPL, int EPV>
+template <class T, bool RMS, bool ADD, bool Q8, int TEAM, int VPL, int EPV, bool RA>
 hipError_t go_rows(const NormCall& c, const Plan& p) {
     const St<T>* x = static_cast<const St<T>*>(c.x);
     const St<T>* r = static_cast<const St<T>*>(c.res);
@@ -58,40 +58,40 @@ hipError_t go_rows(const NormCall& c, const Plan& p) {
     float qinv = c.qinv;
     Strides ld = c.ld;
     void* args[] = {&x, &r, &g, &b, &y, &h, &mean, &rstd, &M, &N, &ld, &eps, &qinv};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&norm_rows_kernel<T, RMS, ADD, Q8, TEAM, VPL, EPV>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&norm_rows_kernel<T, RMS, ADD, Q8, TEAM, VPL, EPV, RA>),
                            dim3((unsigned)p.grid), dim3(TeamGeom<TEAM>::WG), args, 0, c.stream);
 }
 
-template <class T, bool RMS, bool ADD, bool Q8, int TEAM, int EPV>
+template <class T, bool RMS, bool ADD, bool Q8, int TEAM, int EPV, bool RA>
 hipError_t rows_by_vpl(const NormCall& c, const Plan& p) {
     switch (p.vpl) {
-    case 1: return go_rows<T, RMS, ADD, Q8, TEAM, 1, EPV>(c, p);
-    case 2: return go_rows<T, RMS, ADD, Q8, TEAM, 2, EPV>(c, p);
-    case 4: return go_rows<T, RMS, ADD, Q8, TEAM, 4, EPV>(c, p);
-    case 8: return go_rows<T, RMS, ADD, Q8, TEAM, 8, EPV>(c, p);
-    case 16: return go_rows<T, RMS, ADD, Q8, TEAM, 16, EPV>(c, p);
+    case 1: return go_rows<T, RMS, ADD, Q8, TEAM, 1, EPV, RA>(c, p);
+    case 2: return go_rows<T, RMS, ADD, Q8, TEAM, 2, EPV, RA>(c, p);
+    case 4: return go_rows<T, RMS, ADD, Q8, TEAM, 4, EPV, RA>(c, p);
+    case 8: return go_rows<T, RMS, ADD, Q8, TEAM, 8, EPV, RA>(c, p);
+    case 16: return go_rows<T, RMS, ADD, Q8, TEAM, 16, EPV, RA>(c, p);
     case 5:
-        if constexpr (TEAM == 64) return go_rows<T, RMS, ADD, Q8, TEAM, 5, EPV>(c, p);
+        if constexpr (TEAM == 64) return go_rows<T, RMS, ADD, Q8, TEAM, 5, EPV, RA>(c, p);
         break;
     case 10:
-        if constexpr (TEAM == 64) return go_rows<T, RMS, ADD, Q8, TEAM, 10, EPV>(c, p);
+        if constexpr (TEAM == 64) return go_rows<T, RMS, ADD, Q8, TEAM, 10, EPV, RA>(c, p);
         break;
     }
     return hipErrorInvalidValue;
 }
 
-template <class T, bool RMS, bool ADD, bool Q8, int EPV>
+template <class T, bool RMS, bool ADD, bool Q8, int EPV, bool RA = false>
 hipError_t rows_by_team(const NormCall& c, const Plan& p) {
     switch (p.team) {
-    case 4: return rows_by_vpl<T, RMS, ADD, Q8, 4, EPV>(c, p);
-    case 8: return rows_by_vpl<T, RMS, ADD, Q8, 8, EPV>(c, p);
-    case 16: return rows_by_vpl<T, RMS, ADD, Q8, 16, EPV>(c, p);
-    case 32: return rows_by_vpl<T, RMS, ADD, Q8, 32, EPV>(c, p);
-    case 64: return rows_by_vpl<T, RMS, ADD, Q8, 64, EPV>(c, p);
-    case 128: return rows_by_vpl<T, RMS, ADD, Q8, 128, EPV>(c, p);
-    case 256: return rows_by_vpl<T, RMS, ADD, Q8, 256, EPV>(c, p);
-    case 512: return rows_by_vpl<T, RMS, ADD, Q8, 512, EPV>(c, p);
-    case 1024: return rows_by_vpl<T, RMS, ADD, Q8, 1024, EPV>(c, p);
+    case 4: return rows_by_vpl<T, RMS, ADD, Q8, 4, EPV, RA>(c, p);
+    case 8: return rows_by_vpl<T, RMS, ADD, Q8, 8, EPV, RA>(c, p);
+    case 16: return rows_by_vpl<T, RMS, ADD, Q8, 16, EPV, RA>(c, p);
+    case 32: return rows_by_vpl<T, RMS, ADD, Q8, 32, EPV, RA>(c, p);
+    case 64: return rows_by_vpl<T, RMS, ADD, Q8, 64, EPV, RA>(c, p);
+    case 128: return rows_by_vpl<T, RMS, ADD, Q8, 128, EPV, RA>(c, p);
+    case 256: return rows_by_vpl<T, RMS, ADD, Q8, 256, EPV, RA>(c, p);
+    case 512: return rows_by_vpl<T, RMS, ADD, Q8, 512, EPV, RA>(c, p);
+    case 1024: return rows_by_vpl<T, RMS, ADD, Q8, 1024, EPV, RA>(c, p);
     }
     return hipErrorInvalidValue;
 }
@@ -104,6 +104,21 @@ hipError_t launch_rows(int op, const NormCall& c, const Plan& p) {
                                 decltype(epv)::value>(c, p);
         });
     });
+}
+
+// Row kernel with realigned loads of x (x not 16-byte aligned, the other
+// operands aligned): LayerNorm, RMSNorm and RMSNorm with FP8 output on
+// 16-byte vectors.  Instantiated in translation units of their own.
+template <class T>
+hipError_t launch_rows_realigned(int op, const NormCall& c, const Plan& p) {
+    constexpr int VEC = 16 / T::bytes;
+    if (p.epv != VEC) return hipErrorInvalidValue;
+    switch (op) {
+    case OP_LN: return rows_by_team<T, false, false, false, VEC, true>(c, p);
+    case OP_RMS: return rows_by_team<T, true, false, false, VEC, true>(c, p);
+    case OP_RMS_Q8: return rows_by_team<T, true, false, true, VEC, true>(c, p);
+    }
+    return hipErrorInvalidValue;
 }
 
 // ---------------------------------------------------------------------------

@@ -182,13 +182,16 @@ FILL = {"f32": 0x7FA5A5A5, "bf16": 0x7FA5, "f16": 0x7E5A, "u8": 0xA5}
 
 
 def run_strided(op: str, dtype: str, x, gamma, beta, eps: float, *, res=None, scale: float = 1.0,
-                ldx: int, ldy: int, ldr: int = 0, ldh: int = 0, offset: int = 0, inplace: bool = False):
+                ldx: int, ldy: int, ldr: int = 0, ldh: int = 0, offset: int = 0, inplace: bool = False,
+                x_offset: int | None = None):
     """One norm_fwd call with strided rows.  Returns (y, h, mean, rstd) and
-    asserts that no byte between or around the rows of the outputs changed."""
+    asserts that no byte between or around the rows of the outputs changed.
+    x_offset (default: offset) places x alone that many elements into its
+    allocation."""
     M, N = x.shape
     q8 = op.endswith("fp8")
     ydt = "u8" if q8 else dtype
-    xb, xt = _embed(x, dtype, ldx, offset, FILL[dtype])
+    xb, xt = _embed(x, dtype, ldx, offset if x_offset is None else x_offset, FILL[dtype])
     gt = to_device(gamma, dtype) if gamma is not None else None
     bt = to_device(beta, dtype) if beta is not None else None
     rb = rt = hb = ht = None

@@ -716,6 +716,47 @@ def test_strided_rows(op, dtype, N, ldx, ldy, offset):
                     what=f"strided {op}")
 
 
+# x alone off a 16-byte boundary (a view into a larger buffer), everything
+# else aligned: the row kernel reads x in aligned 16-byte blocks and realigns
+# them in registers.  (dtype, N, M): row tiles of 8 to 1024 lanes, several
+# rows per wavefront with ragged vector rows (f16 1000, bf16 8 and 24), one
+# wavefront per row (bf16 5120), 16 vectors per lane (RMSNorm fp32 2048).
+REALIGN_CASES = [("bf16", 4096, 6), ("f16", 1000, 37), ("bf16", 8, 70), ("bf16", 24, 41), ("f32", 8192, 5),
+                 ("bf16", 5120, 4), ("bf16", 65536, 3), ("f32", 2048, 9), ("f16", 256, 19)]
+
+
+@pytest.mark.parametrize("op", ["ln", "rms", "rms_fp8"])
+@pytest.mark.parametrize("dtype,N,M", REALIGN_CASES)
+def test_realigned_x(monkeypatch, op, dtype, N, M):
+    """Misaligned x by every element offset within 16 bytes, with row strides
+    that keep or change the offset from row to row: the same bits as the same
+    call, on the same tile, on an aligned contiguous copy of x (the arithmetic
+    is the same), and the oracle's results."""
+    import rmsnorm_forward_amd as rn
+    plan = rn.norm_describe(op, M, N, dtype, aligned="x")
+    assert "x=realigned" in plan, plan
+    f = dict(kv.split("=") for kv in plan.split())
+    monkeypatch.setenv("MI355NORM_TILE", f"{f['team']}x{f['vpl']}")
+    epv = 16 // {"f32": 4, "bf16": 2, "f16": 2}[dtype]
+    inp = inputs("rms" if "rms" in op else "ln", dtype, M, N, seed=N + 31)
+    beta = inp["beta"] if op == "ln" else None
+    scale = 0.05
+    ref = gpu_runner.run_strided(op, dtype, inp["x"], inp["gamma"], beta, 1e-5, scale=scale, ldx=N, ldy=N)
+    for k in range(1, epv):
+        for ldx in (N, N + 1, N + epv - 1, N + 3 * epv):
+            print(f"[gpu] realigned x {op} {dtype} M={M} N={N} x_offset={k} ldx={ldx}", flush=True)
+            got = gpu_runner.run_strided(op, dtype, inp["x"], inp["gamma"], beta, 1e-5, scale=scale, ldx=ldx,
+                                         ldy=N, x_offset=k)
+            for name, a, b in zip(("y", "h", "mean", "rstd"), got, ref):
+                if a is None:
+                    continue
+                assert a.tobytes() == b.tobytes(), f"{name} differs from the aligned call (x_offset={k}, ldx={ldx})"
+    if op == "rms_fp8":
+        compare_fp8(dtype, inp["x"], None, inp["gamma"], 1e-5, scale, got[0], None, got[3], what="realigned fp8")
+    else:
+        compare(op, dtype, inp["x"], inp["gamma"], beta, 1e-5, got[0], got[2], got[3], what=f"realigned {op}")
+
+
 @pytest.mark.parametrize("N", [2048, 140000])
 def test_strided_in_place_and_interleaved(N):
     """The fused residual add in place on strided rows; and LayerNorm of the
