@@ -66,10 +66,11 @@
  *   Every pointer must be aligned to its element size.  16-byte aligned x, y,
  *   gamma, beta with N * sizeof(dtype) a multiple of 16 take the 128-bit
  *   vector path.  When only x is off a 16-byte boundary (a view into a wider
- *   buffer), rows that fit one workgroup still take it, x being read in
- *   aligned 16-byte blocks realigned in registers (same tile, so the same
- *   results as on an aligned copy of x).  Anything else takes an
- *   element-wise path (slower, same accuracy).  Buffers must not overlap (y
+ *   buffer), the call still takes it, x being read in aligned 16-byte
+ *   blocks realigned in registers (same tile, so the same results as on an
+ *   aligned copy of x; rows split across workgroups then take the two
+ *   kernels).  Anything else takes an element-wise path (slower, same
+ *   accuracy).  Buffers must not overlap (y
  *   may not alias x: no in-place use).
  *
  * Ownership: the caller allocates and owns every buffer and keeps it alive
@@ -209,8 +210,8 @@ typedef struct {
  * not fit 2^63 bytes, is NORM_ERR_BAD_SHAPE; NULL args is NORM_ERR_NULL_ARG).
  * The 16-byte vector path is taken when every row start is 16-byte aligned
  * (EPV-byte for FP8 codes); for LayerNorm, RMSNorm and RMSNorm with FP8
- * output also when only the rows of x are not (any ld_x), on rows that fit
- * one workgroup; otherwise the element-wise path.  Overlaps are
+ * output also when only the rows of x are not (any ld_x; split rows then
+ * take the two kernels); otherwise the element-wise path.  Overlaps are
  * checked row by row when the two matrices share a stride or one is a
  * vector (interleaved matrices that share no byte are accepted), and over
  * their whole spans otherwise.  Returns a norm_status.

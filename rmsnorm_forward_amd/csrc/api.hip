@@ -25,12 +25,13 @@
 //               the Infinity Cache).
 // x alone off a 16-byte boundary (a view into a wider buffer, any row
 // stride), the other operands aligned and N filling whole vectors: the row
-// tiles read x in aligned 16-byte blocks and realign them in registers (a
-// DPP shift from the next lane, byte alignment), LayerNorm, RMSNorm and
-// RMSNorm with FP8 output; split rows and the residual add take the
-// element-wise path.  Steady state, realigned vs aligned vs element-wise, us:
+// tiles and the split rows' two kernels read x in aligned 16-byte blocks and
+// realign them in registers (a DPP shift from the next lane, byte
+// alignment), LayerNorm, RMSNorm and RMSNorm with FP8 output; the residual
+// add takes the element-wise path.  Steady state, realigned vs aligned vs element-wise, us:
 // LN bf16 16384 x 8192 105.2 / 88.8 / 228.7, RMS bf16 65536 x 2048 88.5 /
-// 84.9 / 175.2, LN bf16 1024 x 32768 33.8 / 27.8 / 111.7.
+// 84.9 / 175.2, LN bf16 1024 x 32768 33.8 / 27.8 / 111.7, LN bf16 64 x 2^20
+// (split) 80.5 / 64.6 / 264.2.
 // Measured on MI355X in steady state (200 back-to-back launches): bf16
 // 1024-wide RMSNorm 32x4 (2 rows per wavefront) 85.3 us vs 64x2 87.1, 16x8
 // 95.1; bf16 2048-wide 64x4 87.6 vs 32x8 99.4; fp32 2048-wide 256x2 175.0
@@ -380,8 +381,10 @@ int make_plan(int op, int64_t M, int64_t N, int dtype, bool aligned, const Overr
         // f16 128 x 2^19 63.2 vs 65.9).  The residual add keeps two kernels.
         // The pass runs when every chunk of a row can be resident; asked for
         // and impossible, the call fails; chosen automatically and
-        // impossible (no device, say), the two kernels run.
-        const bool pass_auto = o.split_mode < 0 && p->epv > 1 && (op != OP_LN || dtype == NORM_F32);
+        // impossible (no device, say), the two kernels run.  Realigned x
+        // takes the two kernels: the pass kernel has no registers to spare
+        // for the realignment (LayerNorm bf16: 121 VGPRs of 128).
+        const bool pass_auto = o.split_mode < 0 && p->epv > 1 && (op != OP_LN || dtype == NORM_F32) && !realign;
         const int64_t pv = int64_t(kPassWG) * kPassVPL;
         const int64_t pchunks = (NV + pv - 1) / pv;
         const int64_t cap = (o.split_mode == SPLIT_PASS || pass_auto) && !has_add(op)
@@ -549,12 +552,12 @@ int run(const Args& a, void* stream, bool noalloc = false) {
     // the single pass needs the workspace's slots: without allocation the
     // automatic choice is the two kernels (asked for, the pass is refused)
     if (noalloc && ov.split_mode < 0) ov.split_mode = SPLIT_TWO;
-    // x alone misaligned: the realigned row kernel where the plan is a row
-    // tile, else the element-wise path
+    // x alone misaligned: the realigned row kernel, or the realigned two
+    // kernels for split rows; the single pass, asked for, runs element-wise
     const bool aligned = vector_aligned(a);
     bool realign = !aligned && realign_ok(a);
     st = make_plan(op, M, N, dtype, aligned || realign, ov, &p, realign);
-    if (st == NORM_OK && realign && p.path != PATH_ROWS) {
+    if (st == NORM_OK && realign && p.path == PATH_SPLIT && p.split_mode != SPLIT_TWO) {
         realign = false;
         st = make_plan(op, M, N, dtype, false, ov, &p);
     }
@@ -615,9 +618,15 @@ int run(const Args& a, void* stream, bool noalloc = false) {
             pb.grid = std::min(p.grid, mb * p.chunks);
             pb.apply_grid = std::min(p.apply_grid, mb * p.apply_chunks);
             switch (dtype) {
-            case NORM_F32: err = launch_split_f32(op, cb, pb, part); break;
-            case NORM_BF16: err = launch_split_bf16(op, cb, pb, part); break;
-            default: err = launch_split_f16(op, cb, pb, part); break;
+            case NORM_F32:
+                err = realign ? launch_split_realigned_f32(op, cb, pb, part) : launch_split_f32(op, cb, pb, part);
+                break;
+            case NORM_BF16:
+                err = realign ? launch_split_realigned_bf16(op, cb, pb, part) : launch_split_bf16(op, cb, pb, part);
+                break;
+            default:
+                err = realign ? launch_split_realigned_f16(op, cb, pb, part) : launch_split_f16(op, cb, pb, part);
+                break;
             }
         }
     }
@@ -1026,8 +1035,10 @@ int norm_describe(int op, int64_t M, int64_t N, int dtype, int aligned, char* bu
     // plan is a row tile and the operation has that form)
     bool realign = vec && aligned == 2 && (op == OP_LN || op == OP_RMS || op == OP_RMS_Q8);
     int st = make_plan(op, M, N, dtype, vec && (aligned != 2 || realign), read_overrides(), &p, realign);
-    if (st == NORM_OK && realign && p.path != PATH_ROWS)
+    if (st == NORM_OK && realign && p.path == PATH_SPLIT && p.split_mode != SPLIT_TWO) {
+        realign = false;
         st = make_plan(op, M, N, dtype, false, read_overrides(), &p);
+    }
     if (st != NORM_OK) return st;
     if (!buf || buflen <= 0) return NORM_OK;
     if (p.path == PATH_ROWS)
@@ -1039,13 +1050,14 @@ int norm_describe(int op, int64_t M, int64_t N, int dtype, int aligned, char* bu
         std::snprintf(buf, (size_t)buflen,
                       "path=split mode=%s wg=%d vpl=%d epv=%d chunks=%d apply_wg=%d apply_vpl=%d "
                       "apply_chunks=%d teams=%d batch_rows=%lld grid=%lld apply_grid=%lld work=%lld "
-                      "workspace=%lld",
+                      "workspace=%lld%s",
                       p.split_mode == SPLIT_PASS ? "pass" : "two", p.wg, p.vpl, p.epv, p.chunks,
                       p.split_mode == SPLIT_TWO ? kApplyWG : 0, p.split_mode == SPLIT_TWO ? kApplyVPL : 0,
                       p.apply_chunks, p.teams, (long long)p.batch_rows, (long long)p.grid,
                       (long long)p.apply_grid, (long long)p.work,
                       (long long)(p.batch_rows * p.chunks * 8 +
-                                  (p.split_mode == SPLIT_PASS ? p.batch_rows * kSyncStride * 4 : 0)));
+                                  (p.split_mode == SPLIT_PASS ? p.batch_rows * kSyncStride * 4 : 0)),
+                      realign ? " x=realigned" : "");
     return NORM_OK;
 }
 

@@ -149,6 +149,10 @@ hipError_t launch_rows_f16(int op, const NormCall& c, const Plan& p);
 hipError_t launch_rows_realigned_f32(int op, const NormCall& c, const Plan& p);
 hipError_t launch_rows_realigned_bf16(int op, const NormCall& c, const Plan& p);
 hipError_t launch_rows_realigned_f16(int op, const NormCall& c, const Plan& p);
+// the same for the two-kernel split
+hipError_t launch_split_realigned_f32(int op, const NormCall& c, const Plan& p, float2* ws);
+hipError_t launch_split_realigned_bf16(int op, const NormCall& c, const Plan& p, float2* ws);
+hipError_t launch_split_realigned_f16(int op, const NormCall& c, const Plan& p, float2* ws);
 // two-kernel split: ws holds M*chunks partials
 hipError_t launch_split_f32(int op, const NormCall& c, const Plan& p, float2* ws);
 hipError_t launch_split_bf16(int op, const NormCall& c, const Plan& p, float2* ws);

@@ -108,7 +108,8 @@ hipError_t launch_rows(int op, const NormCall& c, const Plan& p) {
 
 // Row kernel with realigned loads of x (x not 16-byte aligned, the other
 // operands aligned): LayerNorm, RMSNorm and RMSNorm with FP8 output on
-// 16-byte vectors.  Instantiated in translation units of their own.
+// 16-byte vectors.  Instantiated, with the split rows' two kernels below, in
+// translation units of their own.
 template <class T>
 hipError_t launch_rows_realigned(int op, const NormCall& c, const Plan& p) {
     constexpr int VEC = 16 / T::bytes;
@@ -125,7 +126,7 @@ hipError_t launch_rows_realigned(int op, const NormCall& c, const Plan& p) {
 // split rows, two kernels
 // ---------------------------------------------------------------------------
 
-template <class T, bool RMS, bool ADD, bool Q8, int EPV>
+template <class T, bool RMS, bool ADD, bool Q8, int EPV, bool RA = false>
 hipError_t go_split(const NormCall& c, const Plan& p, float2* ws) {
     const St<T>* x = static_cast<const St<T>*>(c.x);
     const St<T>* r = static_cast<const St<T>*>(c.res);
@@ -146,7 +147,7 @@ hipError_t go_split(const NormCall& c, const Plan& p, float2* ws) {
     {
         void* args[] = {&x, &r, &h, &ws, &M, &N, &ld, &S};
         hipError_t e = hipLaunchKernel(
-            reinterpret_cast<const void*>(&norm_split_stats_kernel<T, RMS, ADD, kStatsWG, kStatsVPL, EPV>),
+            reinterpret_cast<const void*>(&norm_split_stats_kernel<T, RMS, ADD, kStatsWG, kStatsVPL, EPV, RA>),
             dim3((unsigned)p.grid), dim3(kStatsWG), args, 0, c.stream);
         if (e != hipSuccess) return e;
     }
@@ -157,7 +158,7 @@ hipError_t go_split(const NormCall& c, const Plan& p, float2* ws) {
     const float2* pp = ws;
     void* args[] = {&src, &g, &b, &y, &pp, &mean, &rstd, &M, &N, &lda, &S, &CE, &A, &eps, &qinv};
     return hipLaunchKernel(
-        reinterpret_cast<const void*>(&norm_split_apply_kernel<T, RMS, Q8, kApplyWG, kApplyVPL, EPV>),
+        reinterpret_cast<const void*>(&norm_split_apply_kernel<T, RMS, Q8, kApplyWG, kApplyVPL, EPV, RA>),
         dim3((unsigned)p.apply_grid), dim3(kApplyWG), args, 0, c.stream);
 }
 
@@ -169,6 +170,19 @@ hipError_t launch_split(int op, const NormCall& c, const Plan& p, float2* ws) {
                             decltype(epv)::value>(c, p, ws);
         });
     });
+}
+
+// The two kernels with realigned loads of x (as the row kernel's).
+template <class T>
+hipError_t launch_split_realigned(int op, const NormCall& c, const Plan& p, float2* ws) {
+    constexpr int VEC = 16 / T::bytes;
+    if (p.epv != VEC) return hipErrorInvalidValue;
+    switch (op) {
+    case OP_LN: return go_split<T, false, false, false, VEC, true>(c, p, ws);
+    case OP_RMS: return go_split<T, true, false, false, VEC, true>(c, p, ws);
+    case OP_RMS_Q8: return go_split<T, true, false, true, VEC, true>(c, p, ws);
+    }
+    return hipErrorInvalidValue;
 }
 
 // ---------------------------------------------------------------------------

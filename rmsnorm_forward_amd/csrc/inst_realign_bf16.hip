@@ -1,9 +1,13 @@
-// inst_realign_bf16.hip -- bf16 instantiations of the row kernel with realigned
-// loads of x (x not 16-byte aligned; the other operands aligned).
+// inst_realign_bf16.hip -- bf16 instantiations of the row kernel and the split
+// rows' two kernels with realigned loads of x (x not 16-byte aligned; the
+// other operands aligned).
 #include "inst_impl.hpp"
 
 namespace mi355norm {
 hipError_t launch_rows_realigned_bf16(int op, const NormCall& c, const Plan& p) {
     return detail::launch_rows_realigned<BF16>(op, c, p);
+}
+hipError_t launch_split_realigned_bf16(int op, const NormCall& c, const Plan& p, float2* ws) {
+    return detail::launch_split_realigned<BF16>(op, c, p, ws);
 }
 }  // namespace mi355norm

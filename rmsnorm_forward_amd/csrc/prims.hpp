@@ -287,4 +287,57 @@ __device__ __forceinline__ Welford chan_merge(Welford a, Welford b) {
     return r;
 }
 
+// Realigned loads of x (16-byte vectors when x alone is not 16-byte
+// aligned, e.g. a view into a larger tensor, while y, gamma and beta are),
+// used by the row and split-row kernels.  Each lane loads the aligned
+// 16-byte block holding the start of its vector and takes the following
+// block from the next lane (DPP wave_shl:1: lane l reads lane l + 1); a lane
+// whose next block no lane of its wavefront and team holds (the team's and
+// the wavefront's last lanes, and the row's last vector) loads it itself.
+// Every block loaded holds at least one byte of the row, so no load leaves
+// the row's pages.  `mb` is the row's byte misalignment (a multiple of the
+// element size); the lane's vector is bytes [mb, mb + 16) of the 32 bytes
+// cur:nxt.
+template <bool UNIFORM>
+__device__ __forceinline__ u32x4 realign_words(u32x4 cur, u32x4 nxt, unsigned mb) {
+    const unsigned c0 = cur[0], c1 = cur[1], c2 = cur[2], c3 = cur[3];
+    const unsigned c4 = nxt[0], c5 = nxt[1], c6 = nxt[2], c7 = nxt[3];
+    const unsigned r = mb & 3u;
+    auto shift = [r](unsigned lo, unsigned hi) { return __builtin_amdgcn_alignbyte(hi, lo, r); };
+    const unsigned q = mb >> 2;
+    if constexpr (UNIFORM) {
+        // q is the same for the whole wavefront: one scalar branch
+        switch (q) {
+        case 0: return u32x4{shift(c0, c1), shift(c1, c2), shift(c2, c3), shift(c3, c4)};
+        case 1: return u32x4{shift(c1, c2), shift(c2, c3), shift(c3, c4), shift(c4, c5)};
+        case 2: return u32x4{shift(c2, c3), shift(c3, c4), shift(c4, c5), shift(c5, c6)};
+        default: return u32x4{shift(c3, c4), shift(c4, c5), shift(c5, c6), shift(c6, c7)};
+        }
+    } else {
+        // rows of different lanes may differ: select per lane
+        const unsigned s0 = q == 0 ? c0 : q == 1 ? c1 : q == 2 ? c2 : c3;
+        const unsigned s1 = q == 0 ? c1 : q == 1 ? c2 : q == 2 ? c3 : c4;
+        const unsigned s2 = q == 0 ? c2 : q == 1 ? c3 : q == 2 ? c4 : c5;
+        const unsigned s3 = q == 0 ? c3 : q == 1 ? c4 : q == 2 ? c5 : c6;
+        const unsigned s4 = q == 0 ? c4 : q == 1 ? c5 : q == 2 ? c6 : c7;
+        return u32x4{shift(s0, s1), shift(s1, s2), shift(s2, s3), shift(s3, s4)};
+    }
+}
+
+// The exchange has to run with every lane of the wavefront active: a DPP read
+// of an inactive lane returns nothing.  The empty asm consumes the result in
+// every lane, so the compiler cannot move the exchange into a branch taken
+// only by the lanes that use it.
+__device__ __forceinline__ u32x4 next_lane_words(u32x4 v) {
+    u32x4 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const unsigned w = v[k];
+        unsigned r = (unsigned)__builtin_amdgcn_update_dpp(0, (int)w, 0x130 /* wave_shl:1 */, 0xf, 0xf, false);
+        asm volatile("" : "+v"(r));
+        o[k] = r;
+    }
+    return o;
+}
+
 }  // namespace mi355norm

@@ -71,10 +71,14 @@ __device__ __forceinline__ float wg_sum(float v, float* slots) {
 // cache-policy operand of global_load_lds for a nontemporal load (gfx950)
 constexpr int kAuxNontemporal = 2;
 
-template <class T, int WG, int VPL, int EPV>
+// RA: x's rows may start off a 16-byte boundary (16-byte vectors only); the
+// chunk is read in aligned blocks and realigned in registers.
+template <class T, int WG, int VPL, int EPV, bool RA = false>
 struct Chunk {
     using V = Vec<T, EPV>;
+    using S = typename T::storage;
     static constexpr int CV = WG * VPL;      // vectors per chunk
+    static_assert(!RA || EPV * sizeof(S) == 16, "realigned chunks hold 16-byte vectors");
     V xv[VPL];
     bool ok[VPL];
     int v0;                                  // first vector of the chunk
@@ -83,17 +87,45 @@ struct Chunk {
     // STREAM: nontemporal (x's last read); otherwise cached, so that a second
     // read soon after can be served by the on-die caches.
     template <bool STREAM = true>
-    __device__ __forceinline__ void load(const typename T::storage* xr, int c, int NV) {
+    __device__ __forceinline__ void load(const S* xr, int c, int NV) {
         v0 = c * CV;
+        // realigned: the row's byte misalignment (one row per workgroup, so
+        // wave-uniform) and the aligned address below the row's start
+        unsigned mb = 0;
+        const S* xa = xr;
+        if constexpr (RA) {
+            mb = __builtin_amdgcn_readfirstlane((unsigned)(reinterpret_cast<uintptr_t>(xr) & 15u));
+            xa = reinterpret_cast<const S*>(reinterpret_cast<uintptr_t>(xr) - mb);
+        }
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
             const unsigned v = (unsigned)(v0 + j * WG) + threadIdx.x;
             ok[j] = (int)v < NV;
             if (ok[j]) {
-                if constexpr (STREAM) xv[j].load_stream(xr + v * EPV);
-                else xv[j].load(xr + v * EPV);
+                if constexpr (STREAM) xv[j].load_stream(xa + v * EPV);
+                else xv[j].load(xa + v * EPV);
             } else {
                 xv[j].zero();
+            }
+        }
+        if constexpr (RA) {
+            // the block after the lane's own: from the next lane, or loaded
+            // by the wavefront's last lane and the row's last vector
+            V ex[VPL];
+            bool own[VPL];
+#pragma unroll
+            for (int j = 0; j < VPL; ++j) {
+                const unsigned v = (unsigned)(v0 + j * WG) + threadIdx.x;
+                own[j] = mb != 0u && ok[j] && (lane_id() == 63 || (int)v == NV - 1);
+                if (own[j]) {
+                    if constexpr (STREAM) ex[j].load_stream(xa + (v + 1) * EPV);
+                    else ex[j].load(xa + (v + 1) * EPV);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < VPL; ++j) {
+                const u32x4 nl = next_lane_words(xv[j].w);    // every lane active
+                xv[j].w = realign_words<true>(xv[j].w, own[j] ? ex[j].w : nl, mb);
             }
         }
     }
@@ -474,7 +506,7 @@ void norm_split_pass_kernel(const typename T::storage* __restrict__ x,
 // soon after is served on-die).  Chunks of CV = WG*VPL vectors.
 // ADD: the chunk is h = x + res (rounded), stored to hout through the caches;
 // the normalising kernel then reads hout in place of x.
-template <class T, bool RMS, bool ADD, int WG, int VPL, int EPV>
+template <class T, bool RMS, bool ADD, int WG, int VPL, int EPV, bool RA = false>
 __global__ __launch_bounds__(WG)
 void norm_split_stats_kernel(const typename T::storage* x,
                              const typename T::storage* res,
@@ -483,7 +515,8 @@ void norm_split_stats_kernel(const typename T::storage* x,
                              int64_t M, int N, Strides ld, int S)
 {
     static_assert(!ADD || RMS, "the residual add is fused with RMSNorm only");
-    using C = Chunk<T, WG, VPL, EPV>;
+    static_assert(!RA || !ADD, "realigned x: no residual");
+    using C = Chunk<T, WG, VPL, EPV, RA>;
     __shared__ float red[2][WG / 64];
     const int NV = N / EPV;
     const int64_t items = M * (int64_t)S;
@@ -506,7 +539,7 @@ void norm_split_stats_kernel(const typename T::storage* x,
 // they are in flight, normalise and store.  Every wavefront runs the same
 // merge in chunk order, so every chunk of a row uses the same bits of mean
 // and rstd.  The row's first chunk stores mean and rstd.
-template <class T, bool RMS, bool Q8, int WG, int VPL, int EPV>
+template <class T, bool RMS, bool Q8, int WG, int VPL, int EPV, bool RA = false>
 __global__ __launch_bounds__(WG)
 void norm_split_apply_kernel(const typename T::storage* x,
                              const typename T::storage* __restrict__ gamma,
@@ -518,7 +551,7 @@ void norm_split_apply_kernel(const typename T::storage* x,
                              int64_t M, int N, Strides ld, int S, int CE, int A, float eps, float qinv)
 {
     static_assert(!Q8 || RMS, "FP8 output is fused with RMSNorm only");
-    using C = Chunk<T, WG, VPL, EPV>;
+    using C = Chunk<T, WG, VPL, EPV, RA>;
     const int NV = N / EPV;
     const int64_t items = M * (int64_t)A;
     for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {

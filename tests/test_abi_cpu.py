@@ -206,8 +206,8 @@ def test_plans_of_the_measured_configurations(op, M, N, dtype, want):
 def test_realigned_plans():
     """x alone off 16 bytes: the aligned plan's row tile on the realigned
     kernel, except the two tiles whose registers the realignment would push
-    to a lower occupancy; the residual add, N off whole vectors and split
-    rows keep the element-wise plan."""
+    to a lower occupancy; split rows on the realigned two kernels; the
+    residual add and N off whole vectors keep the element-wise plan."""
     def d(op, M, N, dtype, al):
         return parse(rn.norm_describe(op, M, N, dtype, aligned=al))
     for op, M, N, dtype in [("ln", 16384, 8192, "bf16"), ("rms", 65536, 2048, "bf16"), ("rms_fp8", 512, 4096, "f16"),
@@ -218,8 +218,11 @@ def test_realigned_plans():
     assert x["x"] == "realigned" and (x["team"], x["vpl"]) != ("64", "10"), x
     x = d("rms", 65536, 2048, "f32", "x")
     assert x["x"] == "realigned" and (x["team"], x["vpl"]) != ("32", "16"), x
-    for op, N, dtype in [("add_rms", 4096, "bf16"), ("ln", 4100, "bf16"), ("ln", 1 << 20, "bf16"),
-                         ("rms", 1 << 20, "f32")]:
+    for op, N, dtype in [("ln", 1 << 20, "bf16"), ("rms", 1 << 20, "f32"), ("rms_fp8", 140000, "f16")]:
+        x = d(op, 64, N, dtype, "x")
+        assert x["path"] == "split" and x["mode"] == "two" and x["x"] == "realigned", x
+        assert x["epv"] == str(16 // (4 if dtype == "f32" else 2)), x
+    for op, N, dtype in [("add_rms", 4096, "bf16"), ("ln", 4100, "bf16"), ("add_rms", 1 << 20, "bf16")]:
         assert "x" not in d(op, 64, N, dtype, "x") and d(op, 64, N, dtype, "x") == d(op, 64, N, dtype, False)
 
 

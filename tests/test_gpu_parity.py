@@ -717,12 +717,15 @@ def test_strided_rows(op, dtype, N, ldx, ldy, offset):
 
 
 # x alone off a 16-byte boundary (a view into a larger buffer), everything
-# else aligned: the row kernel reads x in aligned 16-byte blocks and realigns
-# them in registers.  (dtype, N, M): row tiles of 8 to 1024 lanes, several
-# rows per wavefront with ragged vector rows (f16 1000, bf16 8 and 24), one
-# wavefront per row (bf16 5120), 16 vectors per lane (RMSNorm fp32 2048).
+# else aligned: the kernels read x in aligned 16-byte blocks and realign them
+# in registers.  (dtype, N, M): row tiles of 8 to 1024 lanes, several rows
+# per wavefront with ragged vector rows (f16 1000, bf16 8 and 24), one
+# wavefront per row (bf16 5120), 16 vectors per lane (RMSNorm fp32 2048);
+# split rows on the two kernels, with a ragged last chunk (bf16 140000, fp32
+# 70000) and without (f16 2^20).
 REALIGN_CASES = [("bf16", 4096, 6), ("f16", 1000, 37), ("bf16", 8, 70), ("bf16", 24, 41), ("f32", 8192, 5),
-                 ("bf16", 5120, 4), ("bf16", 65536, 3), ("f32", 2048, 9), ("f16", 256, 19)]
+                 ("bf16", 5120, 4), ("bf16", 65536, 3), ("f32", 2048, 9), ("f16", 256, 19),
+                 ("bf16", 140000, 3), ("f32", 70000, 3), ("f16", 1 << 20, 2)]
 
 
 @pytest.mark.parametrize("op", ["ln", "rms", "rms_fp8"])
@@ -736,7 +739,11 @@ def test_realigned_x(monkeypatch, op, dtype, N, M):
     plan = rn.norm_describe(op, M, N, dtype, aligned="x")
     assert "x=realigned" in plan, plan
     f = dict(kv.split("=") for kv in plan.split())
-    monkeypatch.setenv("MI355NORM_TILE", f"{f['team']}x{f['vpl']}")
+    if f["path"] == "rows":
+        monkeypatch.setenv("MI355NORM_TILE", f"{f['team']}x{f['vpl']}")
+    else:
+        assert f["mode"] == "two", plan
+        monkeypatch.setenv("MI355NORM_PATH", "split2")
     epv = 16 // {"f32": 4, "bf16": 2, "f16": 2}[dtype]
     inp = inputs("rms" if "rms" in op else "ln", dtype, M, N, seed=N + 31)
     beta = inp["beta"] if op == "ln" else None

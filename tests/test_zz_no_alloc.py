@@ -41,9 +41,9 @@ def _inputs(op, dtype, M, N, seed):
     return workloads.gen_rms_uniform(seed, M, N, dtype)
 
 
-def _call(fn, op, dtype, M, N, off, inp):
+def _call(fn, op, dtype, M, N, off, inp, x_off=None):
     dev = lambda a: gpu_runner.to_device(a, dtype, off) if a is not None else None
-    x = dev(inp["x"])
+    x = gpu_runner.to_device(inp["x"], dtype, off if x_off is None else x_off)
     g = dev(inp["gamma"])
     b = dev(inp.get("beta")) if op == "ln" else None
     res = dev(inp["res"]) if op == "add_rms" else None
@@ -54,7 +54,7 @@ def _call(fn, op, dtype, M, N, off, inp):
     rstd = torch.full((M,), float("nan"), device="cuda")
     p = lambda t: t.data_ptr() if t is not None else None
     eps = 1e-5 if op == "ln" else 1e-6
-    print(f"[gpu] {fn.__name__} {op} {dtype} {M}x{N} offset {off}", flush=True)
+    print(f"[gpu] {fn.__name__} {op} {dtype} {M}x{N} offset {off} x offset {x_off}", flush=True)
     st = fn(op, dtype, M, N, p(x), p(y), residual=p(res), gamma=p(g), beta=p(b), residual_out=p(h),
             mean=p(mean), rstd=p(rstd), eps=eps, stream=torch.cuda.current_stream().cuda_stream)
     assert st == rn.NORM_OK, f"{rn.STATUS.get(st)}: {rn.norm_status_str(st)} [{rn.norm_last_error()}]"
@@ -74,6 +74,23 @@ def test_noalloc_gives_norm_fwd_bits_on_consecutive_calls():
         inp = _inputs(op, dtype, M, N, 900 + k)
         got = _call(rn.norm_fwd_noalloc, op, dtype, M, N, off, inp)
         want = _call(rn.norm_fwd, op, dtype, M, N, off, inp)
+        for a, b in zip(got, want):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"call {k} ({op} {dtype} {M}x{N}) differs"
+        assert np.all(np.isfinite(got[1]))
+
+
+def test_noalloc_realigned_x_gives_norm_fwd_bits():
+    """x alone off 16 bytes: both entry points take the realigned kernels
+    (split rows: the two kernels, partials in the fixed scratch for
+    norm_fwd_noalloc), so the bits are the same; consecutive calls, each
+    smaller than the one before."""
+    for k, (op, dtype, M, N, x_off) in enumerate([("rms", "bf16", 4, 1 << 18, 3), ("ln", "f32", 3, 70000, 1),
+                                                  ("ln", "bf16", 9, 4096, 5)]):
+        plan = dict(kv.split("=") for kv in rn.norm_describe(op, M, N, dtype, aligned="x").split())
+        assert plan["x"] == "realigned" and plan.get("mode", "two") == "two", plan
+        inp = _inputs(op, dtype, M, N, 970 + k)
+        got = _call(rn.norm_fwd_noalloc, op, dtype, M, N, 0, inp, x_off=x_off)
+        want = _call(rn.norm_fwd, op, dtype, M, N, 0, inp, x_off=x_off)
         for a, b in zip(got, want):
             assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"call {k} ({op} {dtype} {M}x{N}) differs"
         assert np.all(np.isfinite(got[1]))
