@@ -343,10 +343,9 @@ int make_plan(int op, int64_t M, int64_t N, int dtype, bool aligned, const Overr
             // 256 x 4 18.4; 2048 x 5120 9.4 vs 11.0; LN bf16 4096 x 2560:
             // 64 x 5 9.0 vs 128 x 4 11.0; from 8192 rows on it is level or
             // slower: RMS bf16 8192 x 5120 32.5 vs 30.0)
-            // (not with realigned x: the realignment's registers halve these
-            // tiles' occupancy; realigned 4096 x 5120: 64 x 10 23.4 us,
-            // 256 x 4 23.1, 512 x 2 21.9)
-            if (p->epv > 1 && M <= kWaveTileMaxRows && !realign)
+            // (realigned x too: 4096 x 5120 64 x 10 21.5 us, 512 x 2 21.9,
+            // 256 x 4 22.4)
+            if (p->epv > 1 && M <= kWaveTileMaxRows)
                 for (int c : kWaveTileVpls)
                     if (NV == int64_t(64) * c) { team = 64; vpl = c; }
             // RMSNorm fp32 rows of 2048: two rows per wavefront, 16 vectors
@@ -357,8 +356,7 @@ int make_plan(int op, int64_t M, int64_t N, int dtype, bool aligned, const Overr
             // 1024 16 x 16 172.8 vs 128 x 2 170.5, of 4096 64 x 16 171.5 vs
             // 512 x 2 170.4; the residual add would hold x and the residual
             // (128 VGPRs) before its first use
-            // (not with realigned x: 256 VGPRs, one wavefront per SIMD;
-            // realigned 32 x 16 297 us, 256 x 2 177.5)
+            // (not with realigned x: 32 x 16 209 us, 256 x 2 177.5)
             if (op == OP_RMS && dtype == NORM_F32 && p->epv == 4 && NV == 512 && !realign) {
                 team = 32;
                 vpl = 16;

@@ -340,4 +340,23 @@ __device__ __forceinline__ u32x4 next_lane_words(u32x4 v) {
     return o;
 }
 
+// Teams of at most 64 lanes lie within one wavefront: lane t of a team
+// reads lane t + 1 of the same team, the team's last lane its first lane
+// (ds_bpermute; every lane active, as above).
+template <int TEAM>
+__device__ __forceinline__ u32x4 team_rotate_words(u32x4 v) {
+    static_assert(TEAM <= 64 && (TEAM & (TEAM - 1)) == 0, "a power-of-two team within one wavefront");
+    const int l = lane_id();
+    const int src = ((l & ~(TEAM - 1)) | ((l + 1) & (TEAM - 1))) << 2;
+    u32x4 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const unsigned w = v[k];
+        unsigned r = (unsigned)__builtin_amdgcn_ds_bpermute(src, (int)w);
+        asm volatile("" : "+v"(r));
+        o[k] = r;
+    }
+    return o;
+}
+
 }  // namespace mi355norm

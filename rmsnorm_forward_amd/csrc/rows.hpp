@@ -171,16 +171,14 @@ void norm_rows_kernel(const typename T::storage* x,
             ok[j] = row_ok && vin[j];
             if (HOIST || ok[j]) xv[j].load_stream(xa + off[j]);   // masked vectors: never used
         }
-        if constexpr (REALIGN) {
-            V ex[VPL];
-            bool own[VPL];
+        if constexpr (REALIGN && TEAM <= 64) {
+            // the team lies within this wavefront: the block after lane t's
+            // is lane t + 1's, and for the team's last lane the team's first
+            // lane's next vector; only the row's last vector loads its own
+            V tail;
 #pragma unroll
-            for (int j = 0; j < VPL; ++j) {
-                const int v = j * TEAM + tl;
-                own[j] = mb != 0u && ok[j] &&
-                         (tl == TEAM - 1 || lane_id() == 63 || v == NV - 1);
-                if (own[j]) ex[j].load_stream(xa + (unsigned)(v + 1) * EPV);
-            }
+            for (int j = 0; j < VPL; ++j)
+                if (mb != 0u && ok[j] && j * TEAM + tl == NV - 1) tail.load_stream(xa + (unsigned)NV * EPV);
             // several rows per wavefront: one scalar branch when they share
             // the misalignment (row strides that keep 16-byte steps), else a
             // select per lane
@@ -190,11 +188,51 @@ void norm_rows_kernel(const typename T::storage* x,
                 mbu = __builtin_amdgcn_readfirstlane(mb);
                 uniform = __builtin_amdgcn_readfirstlane((int)(__builtin_amdgcn_ballot_w64(mb != mbu) == 0)) != 0;
             }
+            const bool last = tl == TEAM - 1;
+            u32x4 rc = TEAM == 64 ? next_lane_words(xv[0].w) : team_rotate_words<(TEAM < 64 ? TEAM : 64)>(xv[0].w);
+#pragma unroll
+            for (int j = 0; j < VPL; ++j) {
+                // lane t + 1's block of vector j + 1 (team-rotated), read
+                // before vector j + 1 is realigned
+                u32x4 rn = rc;
+                if (j + 1 < VPL) {
+                    const u32x4 nx = xv[j + 1 < VPL ? j + 1 : j].w;
+                    if constexpr (TEAM == 64) {
+                        // the wavefront's first lane, for its last lane
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const unsigned w = nx[k];
+                            rn[k] = __builtin_amdgcn_readlane(w, 0);
+                        }
+                    } else {
+                        rn = team_rotate_words<(TEAM < 64 ? TEAM : 64)>(nx);
+                    }
+                }
+                const u32x4 nb = j * TEAM + tl == NV - 1 ? tail.w : (last ? rn : rc);
+                xv[j].w = uniform ? realign_words<true>(xv[j].w, nb, mbu) : realign_words<false>(xv[j].w, nb, mb);
+                // the next vector's own-lane neighbours
+                if (j + 1 < VPL) {
+                    if constexpr (TEAM == 64) rc = next_lane_words(xv[j + 1 < VPL ? j + 1 : j].w);
+                    else rc = rn;
+                }
+            }
+        }
+        if constexpr (REALIGN && TEAM > 64) {
+            // teams of several wavefronts: the wavefronts' last lanes, and
+            // the row's last vector, load their next block themselves
+            V ex[VPL];
+            bool own[VPL];
+#pragma unroll
+            for (int j = 0; j < VPL; ++j) {
+                const int v = j * TEAM + tl;
+                own[j] = mb != 0u && ok[j] &&
+                         (tl == TEAM - 1 || lane_id() == 63 || v == NV - 1);
+                if (own[j]) ex[j].load_stream(xa + (unsigned)(v + 1) * EPV);
+            }
 #pragma unroll
             for (int j = 0; j < VPL; ++j) {
                 const u32x4 nl = next_lane_words(xv[j].w);    // every lane active
-                const u32x4 nb = own[j] ? ex[j].w : nl;
-                xv[j].w = uniform ? realign_words<true>(xv[j].w, nb, mbu) : realign_words<false>(xv[j].w, nb, mb);
+                xv[j].w = realign_words<true>(xv[j].w, own[j] ? ex[j].w : nl, mb);
             }
         }
         if constexpr (ADD) {

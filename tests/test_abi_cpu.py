@@ -205,17 +205,16 @@ def test_plans_of_the_measured_configurations(op, M, N, dtype, want):
 
 def test_realigned_plans():
     """x alone off 16 bytes: the aligned plan's row tile on the realigned
-    kernel, except the two tiles whose registers the realignment would push
-    to a lower occupancy; split rows on the realigned two kernels; the
-    residual add and N off whole vectors keep the element-wise plan."""
+    kernel, except RMSNorm fp32's 32 x 16 (slower realigned); split rows on
+    the realigned two kernels; the residual add and N off whole vectors keep
+    the element-wise plan."""
     def d(op, M, N, dtype, al):
         return parse(rn.norm_describe(op, M, N, dtype, aligned=al))
     for op, M, N, dtype in [("ln", 16384, 8192, "bf16"), ("rms", 65536, 2048, "bf16"), ("rms_fp8", 512, 4096, "f16"),
-                            ("ln", 262144, 256, "bf16"), ("ln", 8192, 8192, "f32"), ("ln", 64, 65536, "bf16")]:
+                            ("ln", 262144, 256, "bf16"), ("ln", 8192, 8192, "f32"), ("ln", 64, 65536, "bf16"),
+                            ("ln", 4096, 5120, "bf16")]:
         a, x = d(op, M, N, dtype, True), d(op, M, N, dtype, "x")
         assert x.pop("x") == "realigned" and x == a, (op, M, N, dtype, a, x)
-    x = d("ln", 4096, 5120, "bf16", "x")
-    assert x["x"] == "realigned" and (x["team"], x["vpl"]) != ("64", "10"), x
     x = d("rms", 65536, 2048, "f32", "x")
     assert x["x"] == "realigned" and (x["team"], x["vpl"]) != ("32", "16"), x
     for op, N, dtype in [("ln", 1 << 20, "bf16"), ("rms", 1 << 20, "f32"), ("rms_fp8", 140000, "f16")]:

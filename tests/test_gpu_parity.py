@@ -720,10 +720,12 @@ def test_strided_rows(op, dtype, N, ldx, ldy, offset):
 # else aligned: the kernels read x in aligned 16-byte blocks and realign them
 # in registers.  (dtype, N, M): row tiles of 8 to 1024 lanes, several rows
 # per wavefront with ragged vector rows (f16 1000, bf16 8 and 24), one
-# wavefront per row (bf16 5120), 16 vectors per lane (RMSNorm fp32 2048);
+# wavefront per row (bf16 2048 and 5120), 16 vectors per lane (RMSNorm fp32
+# 2048);
 # split rows on the two kernels, with a ragged last chunk (bf16 140000, fp32
 # 70000) and without (f16 2^20).
 REALIGN_CASES = [("bf16", 4096, 6), ("f16", 1000, 37), ("bf16", 8, 70), ("bf16", 24, 41), ("f32", 8192, 5),
+                 ("bf16", 2048, 9),
                  ("bf16", 5120, 4), ("bf16", 65536, 3), ("f32", 2048, 9), ("f16", 256, 19),
                  ("bf16", 140000, 3), ("f32", 70000, 3), ("f16", 1 << 20, 2)]
 
