@@ -80,6 +80,11 @@ __device__ __forceinline__ float vec_sum_shifted(const V& v, float K) {
 // read into registers by the lane that later writes it, before it writes.
 // Q8 (RMSNorm only): y is FP8 E4M3 codes of (the normalised value * qinv),
 // one byte per element, instead of the I/O dtype.
+// REALIGN (no residual; 16-byte vectors): rows of x may start off a 16-byte
+// boundary while gamma, beta and y do not.  Each lane loads the aligned
+// blocks below its vectors and realigns them in registers with the next
+// block, taken from the next lane (see realign_words in prims.hpp); the
+// tile, the arithmetic and so the results are those of an aligned x.
 //
 // Two memory schedules, fixed per (operation, team) by measurement on MI355X
 // (steady state, 200 launches, us):
