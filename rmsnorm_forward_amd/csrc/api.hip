@@ -46,9 +46,10 @@
 //                                       splitpass the single pass, only if
 //                                       every chunk of a row can be resident
 //                                       at once, and not for the residual
-//                                       add, which keeps two kernels; for the
-//                                       backward, split and split2 take the
-//                                       three-kernel split, split1 /
+//                                       add, which keeps two kernels; with x
+//                                       alone misaligned it runs element-wise;
+//                                       for the backward, split and split2
+//                                       take the three-kernel split, split1 /
 //                                       splitpass its single pass)
 //   MI355NORM_SPLIT_BATCH = <bytes>     bytes of x per two-kernel split batch
 //                                       (of dy and x in the split backward)
