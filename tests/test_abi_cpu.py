@@ -140,10 +140,19 @@ def test_add_rms_exact_in_place_passes_validation():
 
 
 def test_add_rms_plans_like_rms():
-    for N in (1024, 2048, 8192, 16384, 1 << 20):
+    # the same tiles up to 512 vectors a row and on split rows; past that
+    # plain RMSNorm with 16-bit I/O takes two vectors per lane, the residual
+    # add four
+    for N in (1024, 2048, 4096, 1 << 20):
         a = parse(rn.norm_describe("add_rms", 64, N, "bf16"))
         b = parse(rn.norm_describe("rms", 64, N, "bf16"))
         assert a == b, (N, a, b)
+    for N in (8192, 16384):
+        a = parse(rn.norm_describe("add_rms", 64, N, "bf16"))
+        b = parse(rn.norm_describe("rms", 64, N, "bf16"))
+        assert (a["vpl"], b["vpl"]) == ("4", "2") and int(a["team"]) * 2 == int(b["team"]), (N, a, b)
+    for N in (8192, 16384):
+        assert parse(rn.norm_describe("add_rms", 64, N, "f32")) == parse(rn.norm_describe("rms", 64, N, "f32"))
 
 
 def test_fp8_validation():
@@ -168,9 +177,16 @@ def test_fp8_validation():
 
 
 def test_fp8_plans_like_rms():
-    for N in (1024, 8192, 1 << 20):
+    # FP8 output: the RMSNorm tiles up to 512 vectors a row and on split
+    # rows (the residual add's tiles with it); 8 vectors per lane past 1024
+    for N in (1024, 4096, 1 << 20):
         for op in ("rms_fp8", "add_rms_fp8"):
             assert parse(rn.norm_describe(op, 64, N, "bf16")) == parse(rn.norm_describe("rms", 64, N, "bf16"))
+    for N in (8192, 16384):
+        assert parse(rn.norm_describe("add_rms_fp8", 64, N, "bf16")) == parse(rn.norm_describe("add_rms", 64, N, "bf16"))
+    assert parse(rn.norm_describe("rms_fp8", 64, 8192, "bf16")) == parse(rn.norm_describe("add_rms", 64, 8192, "bf16"))
+    d = parse(rn.norm_describe("rms_fp8", 64, 16384, "bf16"))
+    assert (d["team"], d["vpl"]) == ("256", "8"), d
 
 
 def test_rms_rejects_beta_and_mean():
@@ -234,7 +250,15 @@ def test_realigned_plans():
     ("ln", 16384, "f32", ("rows", "512", "8")),
     ("ln", 32768, "f32", ("rows", "1024", "8")),
     ("ln", 65536, "f32", ("split", None, None)),
-    ("rms", 16384, "bf16", ("rows", "512", "4")),
+    ("rms", 16384, "bf16", ("rows", "1024", "2")),
+    ("rms", 8192, "bf16", ("rows", "512", "2")),
+    ("rms", 4096, "bf16", ("rows", "128", "4")),
+    ("rms", 6144, "f16", ("rows", "512", "2")),
+    ("add_rms", 8192, "bf16", ("rows", "256", "4")),
+    ("rms_fp8", 8192, "bf16", ("rows", "256", "4")),
+    ("rms_fp8", 12288, "bf16", ("rows", "256", "8")),
+    ("rms_fp8", 32768, "bf16", ("rows", "512", "8")),
+    ("rms_fp8", 8192, "f32", ("rows", "256", "8")),
     ("rms", 8192, "f32", ("rows", "1024", "2")),
     ("rms", 131072, "bf16", ("split", None, None)),
 ])

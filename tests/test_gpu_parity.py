@@ -189,6 +189,27 @@ def test_unaligned_pointers(op, dtype):
     compare(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, y, mean, rstd, what="unaligned")
 
 
+@pytest.mark.parametrize("op,dtype,M,N,tile", [("rms", "bf16", 64, 8192, "512x2"), ("rms", "f16", 37, 6144, "512x2"),
+                                               ("rms", "bf16", 16, 16384, "1024x2"),
+                                               ("rms_fp8", "bf16", 9, 12288, "256x8"),
+                                               ("rms_fp8", "f32", 9, 8192, "256x8"),
+                                               ("rms_fp8", "bf16", 5, 32768, "512x8")])
+def test_long_rms_row_tiles(op, dtype, M, N, tile):
+    """The tiles the planner picks for long RMSNorm rows (two vectors per
+    lane with 16-bit I/O, eight with FP8 output), against the oracle."""
+    import rmsnorm_forward_amd as rn
+    d = dict(kv.split("=") for kv in rn.norm_describe(op, M, N, dtype).split())
+    assert f"{d['team']}x{d['vpl']}" == tile, d
+    print(f"[gpu] long rms rows {op} {dtype} {M}x{N} tile {tile}", flush=True)
+    inp = inputs("rms", dtype, M, N, seed=N + 41)
+    if op == "rms":
+        y, _, rstd = run("rms", dtype, inp["x"], inp["gamma"], None, 1e-6)
+        compare("rms", dtype, inp["x"], inp["gamma"], None, 1e-6, y, None, rstd, what=f"rms {tile}")
+    else:
+        q, _, r = gpu_runner.run_fp8(dtype, inp["x"], None, inp["gamma"], 1e-6, 0.05)
+        compare_fp8(dtype, inp["x"], None, inp["gamma"], 1e-6, 0.05, q, None, r, what=f"fp8 {tile}")
+
+
 @pytest.mark.parametrize("dtype,N", [("bf16", 5120), ("bf16", 2560), ("f32", 2560), ("f32", 1280), ("f16", 5120)])
 @pytest.mark.parametrize("M", [1, 1001, 4096])
 def test_one_wavefront_tiles(M, dtype, N):
