@@ -328,15 +328,17 @@ int make_plan(int op, int64_t M, int64_t N, int dtype, bool aligned, const Overr
             // lane (steady state, us, 4 vs 2 per lane, bf16: 16384 x 6144 66.8
             // vs 65.1, 16384 x 8192 90.7 vs 85.6, 65536 x 8192 361.4 vs 343.0,
             // 8192 x 16384 88.7 vs 87.7; fp16 16384 x 8192 89.3 vs 86.8; level
-            // at 4096 wide).  Not with the residual add (level or slower: bf16
-            // 8192 x 12288 133.3 vs 137.0) or the FP8 output (below).
-            if (op == OP_RMS && e == 2 && p->epv > 1 && NV > 512 && !realign) per_lane = 2;
+            // at 4096 wide; realigned x too: bf16 16384 x 8192 89.2 vs 87.7).
+            // Not with the residual add (level or slower: bf16 8192 x 12288
+            // 133.3 vs 137.0) or the FP8 output (below).
+            if (op == OP_RMS && e == 2 && p->epv > 1 && NV > 512) per_lane = 2;
             // RMSNorm with FP8 output past 1024 vectors a row: eight vectors
             // per lane (teams of 256 lanes and under take the hoisted
             // schedule): bf16 8192 x 10240 46.1 us vs 53.9, 8192 x 12288 52.9
             // vs 61.5, 8192 x 16384 67.7 vs 78.2, 4096 x 32768 77.2 vs 83.5;
             // fp32 16384 x 8192 107.8 vs 116.7; at 1024 vectors 8 per lane
-            // lost (bf16 16384 x 8192 66.4 vs 65.4)
+            // lost (bf16 16384 x 8192 66.4 vs 65.4).  Not measured with
+            // realigned x, which keeps the four.
             if (op == OP_RMS_Q8 && p->epv > 1 && NV > 1024 && !realign) per_lane = 8;
             team = next_pow2((NV + per_lane - 1) / per_lane);
             if (team < 8) team = 8;

@@ -228,7 +228,7 @@ def test_realigned_plans():
         return parse(rn.norm_describe(op, M, N, dtype, aligned=al))
     for op, M, N, dtype in [("ln", 16384, 8192, "bf16"), ("rms", 65536, 2048, "bf16"), ("rms_fp8", 512, 4096, "f16"),
                             ("ln", 262144, 256, "bf16"), ("ln", 8192, 8192, "f32"), ("ln", 64, 65536, "bf16"),
-                            ("ln", 4096, 5120, "bf16")]:
+                            ("ln", 4096, 5120, "bf16"), ("rms", 16384, 8192, "bf16")]:
         a, x = d(op, M, N, dtype, True), d(op, M, N, dtype, "x")
         assert x.pop("x") == "realigned" and x == a, (op, M, N, dtype, a, x)
     x = d("rms", 65536, 2048, "f32", "x")
