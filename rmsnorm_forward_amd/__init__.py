@@ -1,6 +1,7 @@
 """rmsnorm_forward_amd -- row-wise LayerNorm / RMSNorm forward on AMD MI355X.
 
-A thin ctypes binding of libmi355norm.so (C ABI in include/mi355norm.h).
+A thin binding of libmi355norm.so (C ABI in include/mi355norm.h): ctypes,
+with the per-call entry points through a small CPython module when built.
 Every step of the computation runs in the library's HIP kernels; this module
 only marshals arguments.  PyTorch is used for device memory and streams.
 
@@ -131,6 +132,24 @@ def rms_bwd(dy, x, gamma, rstd, dx, dgamma, M, N, dtype, stream) -> int:
     """RMSNorm backward on device addresses; returns the norm_status code."""
     return _lib.rms_bwd(_addr(dy), _addr(x), _addr(gamma), _addr(rstd), _addr(dx), _addr(dgamma), int(M),
                         int(N), int(dtype), _addr(stream))
+
+
+# The per-call entry points above go through the CPython module built from
+# csrc/pycalls.c when it is present: the same library calls with the same
+# arguments and results, about 1.7 us cheaper per call than ctypes'
+# conversion of their arguments.  It is handed the addresses of the loaded
+# library's entry points, so both paths call one copy of the library.
+try:
+    from . import _calls
+except ImportError:  # not built: the ctypes calls above stay
+    _calls = None
+if _calls is not None:
+    _calls._bind(*(ctypes.cast(getattr(_lib, _n), ctypes.c_void_p).value
+                   for _n in ("ln_fwd", "rms_fwd", "add_rms_fwd", "rms_fp8_fwd", "add_rms_fp8_fwd", "ln_bwd",
+                              "rms_bwd")))
+    ln_fwd, rms_fwd, add_rms_fwd = _calls.ln_fwd, _calls.rms_fwd, _calls.add_rms_fwd
+    rms_fp8_fwd, add_rms_fp8_fwd = _calls.rms_fp8_fwd, _calls.add_rms_fp8_fwd
+    ln_bwd, rms_bwd = _calls.ln_bwd, _calls.rms_bwd
 
 
 class NormArgs(ctypes.Structure):

@@ -1,7 +1,8 @@
 """Build libmi355norm.so (gfx950) in-tree with hipcc.
 
 Each .hip translation unit under csrc/ is compiled in parallel, then linked
-into rmsnorm_forward_amd/libmi355norm.so.  Run as
+into rmsnorm_forward_amd/libmi355norm.so; csrc/pycalls.c (host C) becomes
+the package's CPython module of the per-call entry points.  Run as
 `python rmsnorm_forward_amd/build.py` or through `__graft_entry__.build()`
 (the package itself refuses to import until the library exists).
 """
@@ -54,7 +55,23 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_calls()
     return LIB
+
+
+def build_calls() -> str:
+    """The CPython module of the per-call entry points (host C, gcc): it
+    links nothing and is bound to the loaded library at import."""
+    import sysconfig
+    out = os.path.join(HERE, "_calls" + sysconfig.get_config_var("EXT_SUFFIX"))
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [os.environ.get("CC", "gcc"), "-O2", "-shared", "-fPIC", "-Wall", "-Werror",
+           "-I" + sysconfig.get_paths()["include"], os.path.join(CSRC, "pycalls.c"), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"building the CPython module failed:\n{r.stderr}")
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

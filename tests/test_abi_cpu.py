@@ -70,7 +70,21 @@ def test_last_error_starts_empty():
 
 
 # fake, never dereferenced device addresses: validation only does arithmetic
+def _device_present() -> bool:
+    """Whether a GPU is visible (device_count does not initialise HIP)."""
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
 X, G, B, Y, MEAN, RSTD = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000, 0x600000
+
+# calls that pass validation with the made-up addresses above go on to a
+# launch: without a device it fails at once, with one it would read them
+no_device_only = pytest.mark.skipif(_device_present(), reason="calls pass validation with made-up addresses; "
+                                                             "they may only run where no device is present")
 
 
 def call(op="ln", x=X, g=G, b=B, y=Y, mean=MEAN, rstd=RSTD, M=4, N=64, eps=1e-5, dtype=0):
@@ -131,6 +145,7 @@ def test_add_rms_validation():
     assert call_add(rstd=H) == ALIAS
 
 
+@no_device_only
 def test_add_rms_exact_in_place_passes_validation():
     # y over x and the sum over the residual (exactly the same pointers) are
     # allowed; without a GPU the call then fails at the first HIP call
@@ -155,6 +170,7 @@ def test_add_rms_plans_like_rms():
         assert parse(rn.norm_describe("add_rms", 64, N, "f32")) == parse(rn.norm_describe("rms", 64, N, "f32"))
 
 
+@no_device_only
 def test_fp8_validation():
     Q = 0x900000
     ok = lambda st: st not in (ALIAS, BAD_ARG, NULL_ARG, BAD_SHAPE, BAD_DTYPE, BAD_EPS)
@@ -392,6 +408,7 @@ def test_args_structs_match_the_header(tmp_path, cls, cname):
     assert got == want
 
 
+@no_device_only
 def test_strides_are_validated():
     assert strided(ld_x=63) == BAD_SHAPE                 # shorter than a row
     assert strided(ld_y=1) == BAD_SHAPE
@@ -403,6 +420,7 @@ def test_strides_are_validated():
     assert rn.norm_fwd(7, 0, 4, 64, X, Y) == BAD_ARG
 
 
+@no_device_only
 def test_strided_overlaps_are_exact_for_one_shared_stride():
     # x and y interleaved in one [M, 2N] fp32 buffer: no common byte
     assert passes(strided(x=X, y=X + 64 * 4, ld_x=128, ld_y=128, M=8))
@@ -416,6 +434,7 @@ def test_strided_overlaps_are_exact_for_one_shared_stride():
     assert strided(x=X, y=X + 64 * 4, ld_x=128, ld_y=192, M=8) == ALIAS
 
 
+@no_device_only
 def test_strided_in_place_residual_needs_the_same_stride():
     assert passes(strided(op="add_rms", residual=R, residual_out=R, ld_residual=80, ld_residual_out=80))
     assert strided(op="add_rms", residual=R, residual_out=R, ld_residual=80, ld_residual_out=96) == ALIAS
@@ -602,3 +621,42 @@ def test_noalloc_scratch_holds_every_default_split_batch(dtype, N, aligned):
     d = dict(kv.split("=") for kv in rn.norm_describe("ln", 1 << 30, N, dtype, aligned=aligned).split())
     assert d["path"] == "split" and d["mode"] == "two"
     assert int(d["batch_rows"]) * int(d["chunks"]) * 8 <= 1 << 20
+
+
+def test_cpython_calls_match_ctypes():
+    """The CPython module of the per-call entry points is built and bound,
+    and returns what the ctypes call of the same library function returns
+    for every validation outcome (no device is touched: each case fails
+    before any launch, or has M == 0)."""
+    assert rn._calls is not None and rn.ln_fwd is rn._calls.ln_fwd
+    P, Q, S = 0x100000, 0x200000, 0x300000          # 16-byte aligned, disjoint for small shapes
+    cases = {
+        "ln_fwd": [(P, None, None, S, None, None, 0, 64, 1e-5, 2, None),                  # M = 0
+                   (P, None, None, S, None, None, 4, 64, 1e-5, 9, None),                  # dtype
+                   (P, None, None, S, None, None, 4, 0, 1e-5, 2, None),                   # N
+                   (P, None, None, S, None, None, 4, 64, -1.0, 2, None),                  # eps
+                   (None, None, None, S, None, None, 4, 64, 1e-5, 2, None),               # null x
+                   (P + 1, None, None, S, None, None, 4, 64, 1e-5, 2, None),              # misaligned
+                   (P, None, None, P + 64, None, None, 4, 64, 1e-5, 2, None)],            # alias
+        "rms_fwd": [(P, None, Q, S, None, None, 4, 64, 1e-6, 2, None),                  # beta given
+                    (P, None, None, S, None, None, -1, 64, 1e-6, 0, None)],
+        "add_rms_fwd": [(P, None, None, S, None, None, 4, 64, 1e-6, 2, None),           # null residual
+                        (P, Q, None, S, Q, None, 0, 64, 1e-6, 2, None)],
+        "rms_fp8_fwd": [(P, None, S, None, 4, 64, 1e-6, 0.0, 2, None),                  # scale
+                        (P, None, S, None, 0, 64, 1e-6, 1.0, 2, None)],
+        "add_rms_fp8_fwd": [(P, None, None, S, Q, None, 4, 64, 1e-6, 1.0, 2, None),
+                            (P, Q, None, S, None, None, 4, 64, 1e-6, 1.0, 1, None)],
+        "ln_bwd": [(P, Q, None, None, None, S, None, None, 4, 64, 2, None),             # null statistics
+                   (P, Q, None, S, S + 64, None, None, None, 0, 64, 2, None)],
+        "rms_bwd": [(P, Q, None, None, S, None, 4, 64, 2, None),
+                    (P, Q, None, S, S + 64, None, 4, 64, 7, None)],
+    }
+    for name, calls in cases.items():
+        for args in calls:
+            got = getattr(rn._calls, name)(*args)
+            want = getattr(rn._lib, name)(*args)
+            assert got == want, (name, args, got, want)
+    with pytest.raises(TypeError):
+        rn._calls.ln_fwd(P, None, None, S, None, None, 4, 64, 1e-5, 2)             # one argument short
+    with pytest.raises(TypeError):
+        rn._calls.rms_fwd("x", None, None, S, None, None, 4, 64, 1e-6, 2, None)     # not an address
