@@ -12,6 +12,7 @@
  * arguments, and these functions are called once per normalisation. */
 #define PY_SSIZE_T_CLEAN
 #include <Python.h>
+#include <limits.h>
 #include <stdint.h>
 
 typedef int (*fwd_fn)(const void*, const void*, const void*, void*, float*, float*, int64_t, int64_t, float, int,
@@ -58,6 +59,18 @@ static int i64(PyObject* o, int64_t* out) {
     return 1;
 }
 
+/* the dtype code: an int of the ABI (out of range raises, never wraps) */
+static int code(PyObject* o, int* out) {
+    int64_t v;
+    if (!i64(o, &v)) return 0;
+    if (v < INT_MIN || v > INT_MAX) {
+        PyErr_SetString(PyExc_OverflowError, "dtype code out of the range of a C int");
+        return 0;
+    }
+    *out = (int)v;
+    return 1;
+}
+
 static int f32(PyObject* o, float* out) {
     const double v = PyFloat_AsDouble(o);
     if (v == -1.0 && PyErr_Occurred()) return 0;
@@ -81,15 +94,16 @@ static int bound(const void* f, const char* name) {
 static PyObject* call_fwd(fwd_fn f, const char* name, PyObject* const* a, Py_ssize_t n) {
     void* p[6];
     void* stream;
-    int64_t M, N, dt;
+    int64_t M, N;
+    int dt;
     float eps;
     if (!nargs(name, n, 11) || !bound((const void*)f, name)) return NULL;
     for (int k = 0; k < 6; ++k)
         if (!addr(a[k], &p[k])) return NULL;
-    if (!i64(a[6], &M) || !i64(a[7], &N) || !f32(a[8], &eps) || !i64(a[9], &dt) || !addr(a[10], &stream)) return NULL;
+    if (!i64(a[6], &M) || !i64(a[7], &N) || !f32(a[8], &eps) || !code(a[9], &dt) || !addr(a[10], &stream)) return NULL;
     int st;
     Py_BEGIN_ALLOW_THREADS
-    st = f(p[0], p[1], p[2], p[3], (float*)p[4], (float*)p[5], M, N, eps, (int)dt, stream);
+    st = f(p[0], p[1], p[2], p[3], (float*)p[4], (float*)p[5], M, N, eps, dt, stream);
     Py_END_ALLOW_THREADS
     return PyLong_FromLong(st);
 }
@@ -109,15 +123,16 @@ static PyObject* m_add_rms_fwd(PyObject* s, PyObject* const* a, Py_ssize_t n) {
     (void)s;
     void* p[6];
     void* stream;
-    int64_t M, N, dt;
+    int64_t M, N;
+    int dt;
     float eps;
     if (!nargs("add_rms_fwd", n, 11) || !bound((const void*)p_add_rms_fwd, "add_rms_fwd")) return NULL;
     for (int k = 0; k < 6; ++k)
         if (!addr(a[k], &p[k])) return NULL;
-    if (!i64(a[6], &M) || !i64(a[7], &N) || !f32(a[8], &eps) || !i64(a[9], &dt) || !addr(a[10], &stream)) return NULL;
+    if (!i64(a[6], &M) || !i64(a[7], &N) || !f32(a[8], &eps) || !code(a[9], &dt) || !addr(a[10], &stream)) return NULL;
     int st;
     Py_BEGIN_ALLOW_THREADS
-    st = p_add_rms_fwd(p[0], p[1], p[2], p[3], p[4], (float*)p[5], M, N, eps, (int)dt, stream);
+    st = p_add_rms_fwd(p[0], p[1], p[2], p[3], p[4], (float*)p[5], M, N, eps, dt, stream);
     Py_END_ALLOW_THREADS
     return PyLong_FromLong(st);
 }
@@ -127,17 +142,18 @@ static PyObject* m_rms_fp8_fwd(PyObject* s, PyObject* const* a, Py_ssize_t n) {
     (void)s;
     void* p[4];
     void* stream;
-    int64_t M, N, dt;
+    int64_t M, N;
+    int dt;
     float eps, scale;
     if (!nargs("rms_fp8_fwd", n, 10) || !bound((const void*)p_rms_fp8_fwd, "rms_fp8_fwd")) return NULL;
     for (int k = 0; k < 4; ++k)
         if (!addr(a[k], &p[k])) return NULL;
-    if (!i64(a[4], &M) || !i64(a[5], &N) || !f32(a[6], &eps) || !f32(a[7], &scale) || !i64(a[8], &dt) ||
+    if (!i64(a[4], &M) || !i64(a[5], &N) || !f32(a[6], &eps) || !f32(a[7], &scale) || !code(a[8], &dt) ||
         !addr(a[9], &stream))
         return NULL;
     int st;
     Py_BEGIN_ALLOW_THREADS
-    st = p_rms_fp8_fwd(p[0], p[1], p[2], (float*)p[3], M, N, eps, scale, (int)dt, stream);
+    st = p_rms_fp8_fwd(p[0], p[1], p[2], (float*)p[3], M, N, eps, scale, dt, stream);
     Py_END_ALLOW_THREADS
     return PyLong_FromLong(st);
 }
@@ -147,17 +163,18 @@ static PyObject* m_add_rms_fp8_fwd(PyObject* s, PyObject* const* a, Py_ssize_t n
     (void)s;
     void* p[6];
     void* stream;
-    int64_t M, N, dt;
+    int64_t M, N;
+    int dt;
     float eps, scale;
     if (!nargs("add_rms_fp8_fwd", n, 12) || !bound((const void*)p_add_rms_fp8_fwd, "add_rms_fp8_fwd")) return NULL;
     for (int k = 0; k < 6; ++k)
         if (!addr(a[k], &p[k])) return NULL;
-    if (!i64(a[6], &M) || !i64(a[7], &N) || !f32(a[8], &eps) || !f32(a[9], &scale) || !i64(a[10], &dt) ||
+    if (!i64(a[6], &M) || !i64(a[7], &N) || !f32(a[8], &eps) || !f32(a[9], &scale) || !code(a[10], &dt) ||
         !addr(a[11], &stream))
         return NULL;
     int st;
     Py_BEGIN_ALLOW_THREADS
-    st = p_add_rms_fp8_fwd(p[0], p[1], p[2], p[3], p[4], (float*)p[5], M, N, eps, scale, (int)dt, stream);
+    st = p_add_rms_fp8_fwd(p[0], p[1], p[2], p[3], p[4], (float*)p[5], M, N, eps, scale, dt, stream);
     Py_END_ALLOW_THREADS
     return PyLong_FromLong(st);
 }
@@ -167,15 +184,16 @@ static PyObject* m_ln_bwd(PyObject* s, PyObject* const* a, Py_ssize_t n) {
     (void)s;
     void* p[8];
     void* stream;
-    int64_t M, N, dt;
+    int64_t M, N;
+    int dt;
     if (!nargs("ln_bwd", n, 12) || !bound((const void*)p_ln_bwd, "ln_bwd")) return NULL;
     for (int k = 0; k < 8; ++k)
         if (!addr(a[k], &p[k])) return NULL;
-    if (!i64(a[8], &M) || !i64(a[9], &N) || !i64(a[10], &dt) || !addr(a[11], &stream)) return NULL;
+    if (!i64(a[8], &M) || !i64(a[9], &N) || !code(a[10], &dt) || !addr(a[11], &stream)) return NULL;
     int st;
     Py_BEGIN_ALLOW_THREADS
     st = p_ln_bwd(p[0], p[1], p[2], (const float*)p[3], (const float*)p[4], p[5], (float*)p[6], (float*)p[7], M, N,
-                  (int)dt, stream);
+                  dt, stream);
     Py_END_ALLOW_THREADS
     return PyLong_FromLong(st);
 }
@@ -185,14 +203,15 @@ static PyObject* m_rms_bwd(PyObject* s, PyObject* const* a, Py_ssize_t n) {
     (void)s;
     void* p[6];
     void* stream;
-    int64_t M, N, dt;
+    int64_t M, N;
+    int dt;
     if (!nargs("rms_bwd", n, 10) || !bound((const void*)p_rms_bwd, "rms_bwd")) return NULL;
     for (int k = 0; k < 6; ++k)
         if (!addr(a[k], &p[k])) return NULL;
-    if (!i64(a[6], &M) || !i64(a[7], &N) || !i64(a[8], &dt) || !addr(a[9], &stream)) return NULL;
+    if (!i64(a[6], &M) || !i64(a[7], &N) || !code(a[8], &dt) || !addr(a[9], &stream)) return NULL;
     int st;
     Py_BEGIN_ALLOW_THREADS
-    st = p_rms_bwd(p[0], p[1], p[2], (const float*)p[3], p[4], (float*)p[5], M, N, (int)dt, stream);
+    st = p_rms_bwd(p[0], p[1], p[2], (const float*)p[3], p[4], (float*)p[5], M, N, dt, stream);
     Py_END_ALLOW_THREADS
     return PyLong_FromLong(st);
 }

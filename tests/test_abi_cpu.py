@@ -660,3 +660,5 @@ def test_cpython_calls_match_ctypes():
         rn._calls.ln_fwd(P, None, None, S, None, None, 4, 64, 1e-5, 2)             # one argument short
     with pytest.raises(TypeError):
         rn._calls.rms_fwd("x", None, None, S, None, None, 4, 64, 1e-6, 2, None)     # not an address
+    with pytest.raises(OverflowError):
+        rn._calls.ln_fwd(P, None, None, S, None, None, 0, 64, 1e-5, 2 ** 32 + 2, None)   # would wrap to bf16
