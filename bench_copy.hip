@@ -1,6 +1,8 @@
 // bench_copy.hip -- plain device streams of known size, used by bench.py only:
 // (1) as the ceilings the norm kernels are compared with (a copy of x's bytes
-// into y, and read-only / write-only streams of the same bytes), and (2) to
+// into y, read-only / write-only streams of the same bytes, and copies with
+// a kernel's own mix of streams: two in and two out for the residual add,
+// two in and one out for the backward), and (2) to
 // calibrate rocprofv3's FETCH_SIZE / WRITE_SIZE counters (bytes counted per
 // byte actually moved).  One 16-byte vector per lane, one workgroup of 256
 // lanes per 4 KiB: the simplest streaming kernels, with ordinary (cached) or
@@ -61,4 +63,42 @@ extern "C" int bench_stream(int kind, const void* src, void* dst, uint64_t bytes
 // the cached copy (kind 0), the counter calibration reference
 extern "C" int bench_plain_copy(const void* src, void* dst, uint64_t bytes, void* stream) {
     return bench_stream(0, src, dst, bytes, stream);
+}
+
+// Two sources of n16 vectors each: kind 0 copies src0 to dst0 and src1 to
+// dst1 (two streams in, two out); kind 1 writes src0 ^ src1 to dst0 (two in,
+// one out; dst1 unused).  All nontemporal.
+__global__ __launch_bounds__(256) void nt_copy22(const u32x4* __restrict__ s0, const u32x4* __restrict__ s1,
+                                                 u32x4* __restrict__ d0, u32x4* __restrict__ d1, uint64_t n16) {
+    const uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n16) {
+        const u32x4 a = __builtin_nontemporal_load(s0 + i), b = __builtin_nontemporal_load(s1 + i);
+        __builtin_nontemporal_store(a, d0 + i);
+        __builtin_nontemporal_store(b, d1 + i);
+    }
+}
+
+__global__ __launch_bounds__(256) void nt_copy21(const u32x4* __restrict__ s0, const u32x4* __restrict__ s1,
+                                                 u32x4* __restrict__ d0, u32x4* __restrict__ d1, uint64_t n16) {
+    (void)d1;
+    const uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n16) __builtin_nontemporal_store(__builtin_nontemporal_load(s0 + i) ^ __builtin_nontemporal_load(s1 + i), d0 + i);
+}
+
+// kind 0: two streams in, two out; 1: two in, one out (dst1 may be NULL).
+// Same argument rules and return codes as bench_stream.
+extern "C" int bench_stream2(int kind, const void* src0, const void* src1, void* dst0, void* dst1, uint64_t bytes,
+                             void* stream) {
+    auto al = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+    if (kind < 0 || kind > 1 || !src0 || !src1 || !dst0 || (kind == 0 && !dst1) || bytes % 16 || !al(src0) ||
+        !al(src1) || !al(dst0) || !al(dst1))
+        return 1;
+    const uint64_t n16 = bytes / 16;
+    if (n16 == 0) return 0;
+    const uint64_t blocks = (n16 + 255) / 256;
+    if (blocks > 0xffffffffull) return 1;
+    hipLaunchKernelGGL(kind == 0 ? nt_copy22 : nt_copy21, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                       static_cast<const u32x4*>(src0), static_cast<const u32x4*>(src1), static_cast<u32x4*>(dst0),
+                       static_cast<u32x4*>(dst1), n16);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
 }

@@ -135,6 +135,31 @@ def test_ceiling_streams_refuse_buffers_smaller_than_x_before_any_launch():
     bench.check_stream_buffers(x, [torch.empty_like(t) for t in x], nbytes)   # x-sized: accepted
 
 
+def test_matched_ceiling_refuses_short_buffers_before_any_launch():
+    """The copies with a kernel's own streams check every source and every
+    destination they write (kind 0: two; kind 1: one) before a launch."""
+    import torch
+    x = [torch.empty(4096, dtype=torch.bfloat16) for _ in range(2)]
+    nbytes = x[0].numel() * x[0].element_size()
+    short = [torch.empty(2048, dtype=torch.bfloat16) for _ in range(2)]
+    launched = []
+
+    class Lib:
+        def bench_stream2(self, *a):
+            launched.append(a)
+            return 0
+
+    for kind, s0, s1, d0, d1 in [(0, x, x, x, short), (0, x, short, x, x), (1, x, x, short, None),
+                                 (1, short, x, x, None)]:
+        try:
+            bench.matched_ceiling(Lib(), kind, s0, s1, d0, d1, nbytes, None, 1)
+        except ValueError as e:
+            assert "smaller" in str(e)
+        else:
+            raise AssertionError(f"kind {kind}: a short buffer was accepted")
+    assert not launched
+
+
 def test_cpu_baseline_reports_the_median_of_three_passes_and_the_cpu():
     w = workloads.Workload("t", "rms", "f32", 32, 512, 1e-6, 0, "")
     rng = np.random.default_rng(1)
