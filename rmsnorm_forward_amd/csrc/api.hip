@@ -262,38 +262,41 @@ bool fwd_tile_instantiated(int team, int vpl) {
 }
 
 // How many workgroups of the forward's (bwd: the backward's) single-pass
-// kernel the current device can hold at once (0 if no device is present).
-// Cached per (device, dtype, op, vector width, direction).
-int64_t resident_capacity(int dtype, int op, int epv, bool bwd = false) {
+// kernel the current device can hold at once (0 if no device is present, or
+// if the forward's wide chunks are not built for the operation).  Cached per
+// (device, dtype, op, vector width, direction, chunk width).
+int64_t resident_capacity(int dtype, int op, int epv, bool bwd = false, bool wide = false) {
     static std::mutex mu;
-    static int64_t cache[64][3][kOps][2][2];
-    static bool known[64][3][kOps][2][2];
+    static int64_t cache[64][3][kOps][2][2][2];
+    static bool known[64][3][kOps][2][2][2];
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) return 0;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
     const int vi = epv == 1 ? 0 : 1;
     const int bi = bwd ? 1 : 0;
+    const int wi = wide && !bwd ? 1 : 0;
     std::lock_guard<std::mutex> lock(mu);
-    if (!known[dev][dtype][op][vi][bi]) {
+    if (!known[dev][dtype][op][vi][bi][wi]) {
         int cus = 0;
         int64_t cap = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) {
             int per_cu;
+            const int wg = wi ? kPassWideWG : kPassWG;
             if (bwd)
                 per_cu = dtype == NORM_F32 ? bwd_pass_blocks_per_cu_f32(op, epv)
                          : dtype == NORM_BF16 ? bwd_pass_blocks_per_cu_bf16(op, epv)
                                               : bwd_pass_blocks_per_cu_f16(op, epv);
             else
-                per_cu = dtype == NORM_F32 ? pass_blocks_per_cu_f32(op, epv)
-                         : dtype == NORM_BF16 ? pass_blocks_per_cu_bf16(op, epv)
-                                              : pass_blocks_per_cu_f16(op, epv);
+                per_cu = dtype == NORM_F32 ? pass_blocks_per_cu_f32(op, epv, wg)
+                         : dtype == NORM_BF16 ? pass_blocks_per_cu_bf16(op, epv, wg)
+                                              : pass_blocks_per_cu_f16(op, epv, wg);
             cap = int64_t(per_cu) * cus;
         }
-        cache[dev][dtype][op][vi][bi] = cap;
-        known[dev][dtype][op][vi][bi] = true;
+        cache[dev][dtype][op][vi][bi][wi] = cap;
+        known[dev][dtype][op][vi][bi][wi] = true;
     }
-    return cache[dev][dtype][op][vi][bi];
+    return cache[dev][dtype][op][vi][bi][wi];
 }
 
 // Returns NORM_OK and fills *p, or NORM_ERR_BAD_ARG if an override cannot run.
@@ -399,15 +402,22 @@ int make_plan(int op, int64_t M, int64_t N, int dtype, bool aligned, const Overr
         // impossible (no device, say), the two kernels run.  Realigned x
         // takes the two kernels: the pass kernel has no registers to spare
         // for the realignment (LayerNorm bf16: 121 VGPRs of 128).
+        // Rows of at least kPassWideMinChunks wide chunks take them when a
+        // row's worth can be resident (RMSNorm, fp32 LayerNorm).
         const bool pass_auto = o.split_mode < 0 && p->epv > 1 && (op != OP_LN || dtype == NORM_F32) && !realign;
-        const int64_t pv = int64_t(kPassWG) * kPassVPL;
+        const bool try_pass = (o.split_mode == SPLIT_PASS || pass_auto) && !has_add(op);
+        const int64_t wv = int64_t(kPassWideWG) * kPassVPL;
+        const int64_t wchunks = (NV + wv - 1) / wv;
+        const bool wide_shape = p->epv > 1 && (op != OP_LN || dtype == NORM_F32) && NV >= kPassWideMinChunks * wv;
+        const bool wide = try_pass && wide_shape && resident_capacity(dtype, op, p->epv, false, true) >= wchunks;
+        const int pwg = wide ? kPassWideWG : kPassWG;
+        const int64_t pv = int64_t(pwg) * kPassVPL;
         const int64_t pchunks = (NV + pv - 1) / pv;
-        const int64_t cap = (o.split_mode == SPLIT_PASS || pass_auto) && !has_add(op)
-                                ? resident_capacity(dtype, op, p->epv) : 0;
+        const int64_t cap = try_pass ? resident_capacity(dtype, op, p->epv, false, wide) : 0;
         if (o.split_mode == SPLIT_PASS && !has_add(op) && cap < pchunks) return NORM_ERR_BAD_ARG;
-        if ((o.split_mode == SPLIT_PASS || pass_auto) && !has_add(op) && cap >= pchunks) {
+        if (try_pass && cap >= pchunks) {
             p->split_mode = SPLIT_PASS;
-            p->wg = kPassWG;
+            p->wg = pwg;
             p->vpl = kPassVPL;
             p->chunks = (int)pchunks;
             p->teams = (int)std::min<int64_t>(M, cap / pchunks);

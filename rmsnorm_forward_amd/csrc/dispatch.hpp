@@ -130,6 +130,21 @@ constexpr int kApplyVPL = MI355_APPLY_VPL;
 #endif
 constexpr int kPassWG = MI355_PASS_WG;
 constexpr int kPassVPL = MI355_PASS_VPL;
+// Wide chunks (kPassWideWG lanes x kPassVPL vectors, one workgroup per CU)
+// for RMSNorm and fp32 LayerNorm rows of at least kPassWideMinChunks of them:
+// half the workgroups per row to wait on.  Measured on MI355X (steady state,
+// us, 512 / 1024 lanes): RMS bf16 64 x 2^20 53.9 / 50.7, 256 x 2^20 198.8 /
+// 195.4; RMS fp32 64 x 2^20 107.0 / 99.3, 256 x 2^20 395.2 / 353.1; FP8 out
+// of bf16 / fp32 64 x 2^20 52.5 / 51.3, 81.9 / 74.1; LN fp32 64 x 2^20
+// 113.7 / 111.4, 256 x 2^20 431.3 / 416.8.  Shorter rows keep 512 lanes:
+// with few chunks a row's last one is mostly empty or the teams are too few
+// (RMS bf16 4096 x 81920 260.3 / 306.3, 2048 x 98304 157.6 / 163.3, 256 x
+// 2^19 101.7 / 102.3; LN fp32 512 x 2^18 203.5 / 224.9).
+#ifndef MI355_PASS_WIDE_WG
+#define MI355_PASS_WIDE_WG 1024
+#endif
+constexpr int kPassWideWG = MI355_PASS_WIDE_WG;
+constexpr int kPassWideMinChunks = 16;
 // Two-kernel split: rows per pair of launches are chosen so that one batch of
 // x (about this many bytes) mostly stays in the 256 MB Infinity Cache between the
 // statistics pass and the normalising pass.
@@ -197,8 +212,8 @@ int bwd_pass_blocks_per_cu_f16(int op, int epv);
 hipError_t launch_colsum(const float* part_g, float* out_g, const float* part_b, float* out_b, int64_t P, int N,
                          hipStream_t stream);
 // workgroups of the forward's single-pass kernel that fit on one CU at once
-int pass_blocks_per_cu_f32(int op, int epv);
-int pass_blocks_per_cu_bf16(int op, int epv);
-int pass_blocks_per_cu_f16(int op, int epv);
+int pass_blocks_per_cu_f32(int op, int epv, int wg);
+int pass_blocks_per_cu_bf16(int op, int epv, int wg);
+int pass_blocks_per_cu_f16(int op, int epv, int wg);
 
 }  // namespace mi355norm

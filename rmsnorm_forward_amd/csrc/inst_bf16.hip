@@ -13,8 +13,8 @@ hipError_t launch_split_pass_bf16(int op, const NormCall& c, const Plan& p, unsi
                                   unsigned* dep, unsigned wait_ticks, unsigned stagger) {
     return detail::launch_split_pass<BF16>(op, c, p, slots, dep, wait_ticks, stagger);
 }
-int pass_blocks_per_cu_bf16(int op, int epv) {
-    return detail::pass_blocks_per_cu<BF16>(op, epv);
+int pass_blocks_per_cu_bf16(int op, int epv, int wg) {
+    return detail::pass_blocks_per_cu<BF16>(op, epv, wg);
 }
 hipError_t launch_bwd_bf16(int op, const BwdCall& c, const Plan& p) {
     return detail::launch_bwd<BF16>(op, c, p);

@@ -13,8 +13,8 @@ hipError_t launch_split_pass_f16(int op, const NormCall& c, const Plan& p, unsig
                                   unsigned* dep, unsigned wait_ticks, unsigned stagger) {
     return detail::launch_split_pass<F16>(op, c, p, slots, dep, wait_ticks, stagger);
 }
-int pass_blocks_per_cu_f16(int op, int epv) {
-    return detail::pass_blocks_per_cu<F16>(op, epv);
+int pass_blocks_per_cu_f16(int op, int epv, int wg) {
+    return detail::pass_blocks_per_cu<F16>(op, epv, wg);
 }
 hipError_t launch_bwd_f16(int op, const BwdCall& c, const Plan& p) {
     return detail::launch_bwd<F16>(op, c, p);

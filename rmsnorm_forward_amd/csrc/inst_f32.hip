@@ -14,8 +14,8 @@ hipError_t launch_split_pass_f32(int op, const NormCall& c, const Plan& p, unsig
                                   unsigned* dep, unsigned wait_ticks, unsigned stagger) {
     return detail::launch_split_pass<F32>(op, c, p, slots, dep, wait_ticks, stagger);
 }
-int pass_blocks_per_cu_f32(int op, int epv) {
-    return detail::pass_blocks_per_cu<F32>(op, epv);
+int pass_blocks_per_cu_f32(int op, int epv, int wg) {
+    return detail::pass_blocks_per_cu<F32>(op, epv, wg);
 }
 hipError_t launch_bwd_f32(int op, const BwdCall& c, const Plan& p) {
     return detail::launch_bwd<F32>(op, c, p);

@@ -189,9 +189,9 @@ hipError_t launch_split_realigned(int op, const NormCall& c, const Plan& p, floa
 // split rows, single pass (LayerNorm, RMSNorm, RMSNorm with FP8 output)
 // ---------------------------------------------------------------------------
 
-template <class T, bool RMS, bool Q8, int EPV>
+template <class T, bool RMS, bool Q8, int EPV, int WG>
 const void* pass_kernel() {
-    return reinterpret_cast<const void*>(&norm_split_pass_kernel<T, RMS, Q8, kPassWG, kPassVPL, EPV>);
+    return reinterpret_cast<const void*>(&norm_split_pass_kernel<T, RMS, Q8, WG, kPassVPL, EPV>);
 }
 
 // Calls f(bc<RMS>, bc<Q8>) for the operations the single pass runs.
@@ -205,22 +205,45 @@ hipError_t with_pass_op(int op, F&& f) {
     return hipErrorInvalidValue;
 }
 
+// Whether the wide chunks (kPassWideWG lanes) are built for this operation,
+// dtype and vector width: 16-byte vectors, RMSNorm of every dtype and fp32
+// LayerNorm (LayerNorm with 16-bit I/O runs 128 VGPRs and spills at that
+// width).
+template <class T, bool RMS, int EPV>
+constexpr bool pass_wide_built() {
+    return EPV * sizeof(St<T>) == 16 && (RMS || std::is_same<T, F32>::value);
+}
+
+// Calls f(integral_constant<int, WG>) for the plan's chunk width.
+template <class T, bool RMS, int EPV, class F>
+hipError_t with_pass_wg(int wg, F&& f) {
+    if (wg == kPassWG) return f(std::integral_constant<int, kPassWG>{});
+    if constexpr (pass_wide_built<T, RMS, EPV>())
+        if (wg == kPassWideWG) return f(std::integral_constant<int, kPassWideWG>{});
+    return hipErrorInvalidValue;
+}
+
+// Workgroups of the single pass resident per CU for this chunk width (0 if
+// that width is not built for the operation).
 template <class T>
-int pass_blocks_per_cu(int op, int epv) {
+int pass_blocks_per_cu(int op, int epv, int wg) {
     const void* f = nullptr;
     (void)with_pass_op(op, [&](auto rms, auto q8) {
         return with_epv<T>(epv, [&](auto e) {
-            f = pass_kernel<T, decltype(rms)::value, decltype(q8)::value, decltype(e)::value>();
-            return hipSuccess;
+            return with_pass_wg<T, decltype(rms)::value, decltype(e)::value>(wg, [&](auto w) {
+                f = pass_kernel<T, decltype(rms)::value, decltype(q8)::value, decltype(e)::value,
+                                decltype(w)::value>();
+                return hipSuccess;
+            });
         });
     });
     if (!f) return 0;
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, kPassWG, 0) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, wg, 0) != hipSuccess) return 0;
     return n;
 }
 
-template <class T, bool RMS, bool Q8, int EPV>
+template <class T, bool RMS, bool Q8, int EPV, int WG>
 hipError_t go_split_pass(const NormCall& c, const Plan& p, unsigned long long* slots, unsigned* dep,
                          unsigned wait_ticks, unsigned stagger) {
     const St<T>* x = static_cast<const St<T>*>(c.x);
@@ -238,7 +261,7 @@ hipError_t go_split_pass(const NormCall& c, const Plan& p, unsigned long long* s
     Strides ld = c.ld;
     void* args[] = {&x, &g, &b, &y, &mean, &rstd, &slots, &dep, &M, &N, &ld, &S, &teams, &eps, &qinv,
                     &wait_ticks, &stagger};
-    return hipLaunchKernel(pass_kernel<T, RMS, Q8, EPV>(), dim3((unsigned)(teams * S)), dim3(kPassWG), args, 0,
+    return hipLaunchKernel(pass_kernel<T, RMS, Q8, EPV, WG>(), dim3((unsigned)(teams * S)), dim3(WG), args, 0,
                            c.stream);
 }
 
@@ -247,8 +270,10 @@ hipError_t launch_split_pass(int op, const NormCall& c, const Plan& p, unsigned 
                              unsigned wait_ticks, unsigned stagger) {
     return with_pass_op(op, [&](auto rms, auto q8) {
         return with_epv<T>(p.epv, [&](auto epv) {
-            return go_split_pass<T, decltype(rms)::value, decltype(q8)::value, decltype(epv)::value>(
-                c, p, slots, dep, wait_ticks, stagger);
+            return with_pass_wg<T, decltype(rms)::value, decltype(epv)::value>(p.wg, [&](auto w) {
+                return go_split_pass<T, decltype(rms)::value, decltype(q8)::value, decltype(epv)::value,
+                                     decltype(w)::value>(c, p, slots, dep, wait_ticks, stagger);
+            });
         });
     });
 }

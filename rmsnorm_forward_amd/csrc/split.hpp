@@ -277,11 +277,6 @@ struct Chunk {
 
 };
 
-// Merge a row's S partials (S arbitrary) inside one wavefront; the result is
-// wave-uniform and identical in every wavefront that runs it on the same data.
-// Lane l folds partials l, l+64, l+128, ... in order; the 64 lane states are
-// then merged by a butterfly whose every step puts the lower lane's state
-// first, so partners compute bitwise-identical results.
 // start of row `row` of an output of the I/O dtype, or of FP8 codes
 template <class T, bool Q8>
 __device__ __forceinline__ void* row_out(void* y, int64_t row, int64_t ldy) {

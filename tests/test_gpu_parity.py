@@ -462,16 +462,48 @@ def test_single_pass_teams_walk_several_rows(monkeypatch, op, dtype, M, N):
     compare(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, *a, what="single pass, several rows per team")
 
 
+@pytest.mark.parametrize("op,dtype,M,N", [("rms", "bf16", 40, 1 << 20), ("rms", "f16", 20, (1 << 20) + 8),
+                                           ("rms", "f32", 20, (1 << 19) + 4), ("ln", "f32", 10, 1 << 20),
+                                           ("rms_fp8", "bf16", 20, (1 << 20) + 8), ("rms_fp8", "f32", 18, 1 << 19)])
+def test_single_pass_wide_chunks(monkeypatch, op, dtype, M, N):
+    """Rows of at least 16 chunks of 1024 lanes x 8 vectors take those wide
+    chunks in the single pass (RMSNorm, its FP8 output, fp32 LayerNorm):
+    teams walk several rows, a ragged row's last chunk holds one vector, a
+    run forced onto the recomputation path gives the same bits, and both
+    give the oracle's values."""
+    import rmsnorm_forward_amd as rn
+    plan = dict(kv.split("=") for kv in rn.norm_describe(op, M, N, dtype).split())
+    assert plan["mode"] == "pass" and plan["wg"] == "1024" and int(plan["teams"]) < M, plan
+    inp = inputs("ln" if op == "ln" else "rms", dtype, M, N, seed=95 + M)
+    print(f"[gpu] wide single pass {op} {dtype} M={M} N={N}: {plan['chunks']} chunks, {plan['teams']} teams",
+          flush=True)
+    if op == "rms_fp8":
+        go = lambda: gpu_runner.run_fp8(dtype, inp["x"], None, inp["gamma"], 1e-6, 0.05)
+    else:
+        go = lambda: run(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5)
+    a = go()
+    monkeypatch.setenv("MI355NORM_FORCE_TIMEOUT", "1")
+    b = go()
+    monkeypatch.delenv("MI355NORM_FORCE_TIMEOUT")
+    for u, v in zip(a, b):
+        if u is not None:
+            assert np.array_equal(u.view(np.uint8), v.view(np.uint8)), "recompute path differs"
+    if op == "rms_fp8":
+        compare_fp8(dtype, inp["x"], None, inp["gamma"], 1e-6, 0.05, a[0], None, a[2], what="wide single pass")
+    else:
+        compare(op, dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, *a, what="wide single pass")
+
+
 @pytest.mark.parametrize("mode", ["auto", "split2", "split1"])
 @pytest.mark.parametrize("op,dtype,offset", [("ln", "bf16", 0), ("rms", "bf16", 0), ("rms", "f32", 0),
                                              ("ln", "f32", 1)])
 def test_longest_rows(monkeypatch, op, dtype, offset, mode):
     """Rows of 2^24 elements, the longest the library takes, in every split
     form.  The single pass needs every chunk of a row resident at once: bf16
-    rows of 16-byte vectors fit (512 chunks of 512 lanes x 8 vectors), fp32
-    rows (1024 chunks) and element-wise rows do not, so asking for it is
-    refused before any launch, while the automatic choice falls back to the
-    two kernels."""
+    rows of 16-byte vectors fit (RMSNorm: 256 chunks of 1024 lanes x 8
+    vectors; LayerNorm: 512 of 512 lanes), fp32 rows (512 or 1024 chunks) and
+    element-wise rows do not, so asking for it is refused before any launch,
+    while the automatic choice falls back to the two kernels."""
     import rmsnorm_forward_amd as rn
     M, N = 2, 1 << 24
     aligned = offset == 0
@@ -504,6 +536,12 @@ def test_split_mode_chosen_automatically():
     assert mode("ln", "bf16") == "two" and mode("ln", "f16") == "two"
     assert mode("add_rms", "bf16") == "two" and mode("add_rms", "f32") == "two"
     assert mode("rms", "bf16", aligned=False) == "two"
+    wg = lambda op, dtype, n: dict(kv.split("=") for kv in rn.norm_describe(op, 64, n, dtype).split())["wg"]
+    # wide chunks from 16 of them a row (2^17 vectors); 512 lanes below, and
+    # always for LayerNorm with 16-bit I/O (taken only on request)
+    assert wg("rms", "bf16", N) == wg("rms_fp8", "f16", N) == wg("ln", "f32", N) == "1024"
+    assert wg("rms", "f32", N // 2) == "1024" and wg("rms", "f32", N // 2 - 4) == "512"
+    assert wg("rms", "bf16", N - 8) == "512" and wg("rms", "bf16", N // 4) == "512"
 
 
 def test_single_pass_plan():
