@@ -344,8 +344,10 @@ int norm_describe(int op, int64_t M, int64_t N, int dtype, int aligned,
  * As norm_describe, for ln_bwd (rms = 0) or rms_bwd (rms = 1): path ("bwd"
  * or "bwd_split"), lanes per row, vectors per lane, workgroup size, grid and
  * the number of partial rows of dgamma and dbeta; for split rows also the
- * mode ("three" kernels per batch, or "pass", the single pass in one launch,
- * taken only on request: it was slower), chunks per row and rows per batch.
+ * mode ("three" kernels per batch, or "pass", the single pass in one launch:
+ * for rows of 16-byte vectors, except LayerNorm with fp16 I/O, when a row's
+ * chunks fit on the device at once and there are at least 32 rows per team
+ * of them, or on request), chunks per row and rows per batch.
  */
 int norm_bwd_describe(int rms, int64_t M, int64_t N, int dtype, int aligned,
                       char *buf, int buflen);

@@ -747,24 +747,33 @@ int make_bwd_plan(int64_t M, int64_t N, int dtype, bool rms, bool aligned, const
         team = std::max(team, kBwdMinTeam);
         team = std::min(team, kMaxTeam);
         vpl = round_vpl((NV + team - 1) / team);
-        const bool f32_wide = e == 4 && vpl > 0 && vpl * p->epv == kBwdMaxElems &&
-                              (rms || NV > kBwdF32RowsMaxLnVectors);
-        if (o.path == PATH_SPLIT && o.split_mode == SPLIT_PASS) {
-            // one pass, on request, when every chunk of a row can be resident
+        const bool f32_32 = e == 4 && vpl > 0 && vpl * p->epv == kBwdMaxElems;
+        const bool f32_wide = f32_32 && (rms || NV > kBwdF32RowsMaxLnVectors);
+        const bool forced_pass = o.path == PATH_SPLIT && o.split_mode == SPLIT_PASS;
+        // the single pass by itself (kBwdPassMinRowsPerTeam): rows of
+        // 16-byte vectors the row kernel would not take, or fp32 rows of 32
+        // elements per lane, with enough rows per team
+        const bool pass_shape = o.path < 0 && p->epv > 1 && (rms || dtype != NORM_F16) &&
+                                (vpl < 0 || !bwd_tile_ok(team, vpl, p->epv) || f32_32);
+        if (forced_pass || pass_shape) {
             const int64_t ccv = int64_t(kBwdPassWG) * kBwdPassVPL;
             const int64_t cchunks = (NV + ccv - 1) / ccv;
             const int64_t cap = resident_capacity(dtype, rms ? OP_RMS : OP_LN, p->epv, true);
-            if (cap < cchunks) return NORM_ERR_BAD_ARG;
-            p->path = PATH_SPLIT;
-            p->split_mode = SPLIT_PASS;
-            p->wg = kBwdPassWG;
-            p->vpl = kBwdPassVPL;
-            p->chunks = (int)cchunks;
-            p->teams = (int)std::max<int64_t>(1, std::min<int64_t>(M, cap / cchunks));
-            p->batch_rows = M;
-            p->work = M * p->chunks;
-            p->grid = int64_t(p->teams) * p->chunks;
-            return NORM_OK;
+            const int64_t teams = std::max<int64_t>(1, std::min<int64_t>(M, cap / std::max<int64_t>(1, cchunks)));
+            const bool take = forced_pass || (cap >= cchunks && M >= int64_t(kBwdPassMinRowsPerTeam) * teams);
+            if (forced_pass && cap < cchunks) return NORM_ERR_BAD_ARG;
+            if (take) {
+                p->path = PATH_SPLIT;
+                p->split_mode = SPLIT_PASS;
+                p->wg = kBwdPassWG;
+                p->vpl = kBwdPassVPL;
+                p->chunks = (int)cchunks;
+                p->teams = (int)teams;
+                p->batch_rows = M;
+                p->work = M * p->chunks;
+                p->grid = int64_t(p->teams) * p->chunks;
+                return NORM_OK;
+            }
         }
         if (o.path == PATH_SPLIT || vpl < 0 || !bwd_tile_ok(team, vpl, p->epv) || f32_wide) {
             const int64_t ncu = cus > 0 ? cus : device_cus();

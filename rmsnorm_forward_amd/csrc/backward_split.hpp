@@ -401,7 +401,10 @@ void norm_bwd_pass_kernel(const typename T::storage* dy,      // dx may be writt
         if (row >= M) return;
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
-            const unsigned v = (unsigned)(cc * CV + j * WG) + tid;
+            unsigned v = (unsigned)(cc * CV + j * WG) + tid;
+            // recomputed per row rather than kept: the compiler would hold
+            // row-invariant addresses across the loop and spill
+            asm volatile("" : "+v"(v));
             if (okv[j]) {          // nontemporal: dy and x are read once
                 q.d[j].load_stream(dy + row * ldy + v * EPV);
                 q.xx[j].load_stream(x + row * ldx + v * EPV);
@@ -516,8 +519,11 @@ void norm_bwd_pass_kernel(const typename T::storage* dy,      // dx may be writt
         before_stores();
         St* dxr = dx + row * lddx;
 #pragma unroll
-        for (int j = 0; j < VPL; ++j)
-            if (col_ok[j]) out[j].put_stream(dxr + ((unsigned)(c * CV + j * WG) + tid) * EPV);
+        for (int j = 0; j < VPL; ++j) {
+            unsigned o = ((unsigned)(c * CV + j * WG) + tid) * EPV;
+            asm volatile("" : "+v"(o));
+            if (col_ok[j]) out[j].put_stream(dxr + o);
+        }
         __syncthreads();           // `row_sums` and `late` are rewritten for the next row
     };
 

@@ -90,10 +90,27 @@ constexpr int kBwdSplitSumsVPL = 2;
 constexpr int kBwdSplitSumsVPLElem = 16;
 constexpr int bwd_sums_vpl(int epv) { return epv == 1 ? kBwdSplitSumsVPLElem : kBwdSplitSumsVPL; }
 constexpr int kBwdSplitApplyVPL = 2;
-// split backward in one pass (on request; the three kernels measured
-// faster): chunks of 1024 lanes x 2 vectors, one workgroup per chunk
+// split backward in one pass: chunks of 1024 lanes x 2 vectors, one
+// workgroup per chunk
 constexpr int kBwdPassWG = 1024;
 constexpr int kBwdPassVPL = 2;
+// The backward's single pass is taken by itself for rows of 16-byte vectors
+// that leave the row kernel (split rows, and fp32 rows of 32 elements per
+// lane) when every chunk of a row can be resident and each team walks at
+// least this many rows; LayerNorm with fp16 I/O keeps the three kernels.
+// Measured on MI355X (steady state, us, three kernels or row kernel / single
+// pass): LN bf16 4096 x 40000 295.1 / 255.8, 2048 x 65536 213.8 / 200.8,
+// 512 x 2^18 216.2 / 204.9, 768 x 2^18 322.8 / 291.4, 128 x 2^20 219.5 /
+// 215.8, 256 x 2^20 439.5 / 393.3; RMS bf16 2048 x 65536 209.7 / 176.6,
+// 128 x 2^20 211.5 / 189.9; RMS fp16 2048 x 65536 212.1 / 185.5; LN / RMS
+// fp32 4096 x 32768 427.4 / 320.9, 428.4 / 300.2; 64 x 2^20 208.4 / 199.2,
+// 204.8 / 183.2; LN fp32 2048 x 65536 430.3 / 338.4; row kernel LN fp32
+// 8192 x 20000 486.8 / 412.5, 4096 x 24576 309.3 / 248.9.  With fewer rows
+// per team the teams' skew is not amortised (LN bf16 64 x 2^20, 16 rows per
+// team, 111.4 / 123.8; 96 x 2^20 162.8 / 169.2; 16 x 2^22 112.5 / 150.4),
+// and LayerNorm with fp16 I/O gained nothing (2048 x 65536 219.5 / 221.5,
+// 512 x 2^18 218.2 / 224.0, 256 x 2^20 439.9 / 428.8).
+constexpr int kBwdPassMinRowsPerTeam = 32;
 constexpr int kBwdMinTeam = 8;
 // backward workgroups: always 1024 lanes (16 wavefronts fill a CU's wave
 // slots at up to 128 VGPRs), 1024 / team rows at once

@@ -7,7 +7,8 @@ the ABI takes, short rows forced onto the split path (ragged chunk tails),
 several batches of rows with a short last batch (the accumulating partial
 rows), a sums grid far smaller than its work items, unaligned pointers,
 strided rows, in-place dx, the optional gamma / dgamma / dbeta, M = 0, and
-bitwise determinism; the single pass (on request) on long and
+bitwise determinism; the single pass (forced, and where the planner takes
+it by itself) on long and
 short rows, in place, deterministic, and with its bounded wait forced to
 time out from the host.
 """
@@ -201,6 +202,35 @@ def test_single_pass_split_backward(monkeypatch, op, dtype, N, M):
     p = plan(op, M, N, dtype, aligned)
     assert p["mode"] == "pass", p
     go(op, dtype, M, N, seed=N + M)
+
+
+def test_single_pass_split_backward_chosen_automatically():
+    """Without an override the backward takes the single pass for rows of
+    16-byte vectors that leave the row kernel (and fp32 rows of 32 elements
+    per lane) when a row's chunks fit at once and every team walks at least
+    32 rows; fewer rows per team, or LayerNorm with fp16 I/O, keep the three
+    kernels, and shorter rows the row kernel."""
+    mode = lambda op, dtype, M, N: plan(op, M, N, dtype).get("mode", "rows")
+    assert mode("ln", "bf16", 4096, 40000) == "pass"
+    assert mode("rms", "f16", 2048, 65536) == "pass"
+    assert mode("ln", "f32", 8192, 20000) == "pass"
+    assert mode("rms", "f32", 2048, 32768) == "pass"
+    assert mode("ln", "bf16", 64, 1 << 20) == "three"          # 16 rows per team
+    assert mode("ln", "f16", 4096, 40000) == "three"
+    assert mode("ln", "bf16", 4096, 40000 + 1) == "three"      # not 16-byte vectors
+    assert mode("ln", "f32", 16384, 8192) == "rows"
+    assert mode("ln", "bf16", 4096, 32768) == "rows"
+
+
+@pytest.mark.parametrize("op", ["ln", "rms"])
+def test_single_pass_split_backward_automatic_shape(op):
+    """An fp32 shape the planner sends to the single pass by itself (64
+    teams of 4 chunks over 2048 rows), every row and column against the
+    oracle."""
+    M, N = 2048, 32768
+    p = plan(op, M, N, "f32")
+    assert p["mode"] == "pass" and p["partial_rows"] * 32 <= M, p
+    go(op, "f32", M, N, seed=77)
 
 
 def test_single_pass_split_backward_in_place_and_deterministic(monkeypatch):
