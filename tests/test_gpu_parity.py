@@ -746,6 +746,9 @@ STRIDE_CASES = [
     ("f16", 2056, 2056 + 8, 2056 + 16, 8),
     ("bf16", 140000, 140000 + 8, 140008, 0),
     ("f32", 70000, 70004, 70000 + 36, 0),
+    # rows of 2^17 16-byte vectors: the single pass's wide chunks
+    ("bf16", 1 << 20, (1 << 20) + 64, (1 << 20) + 8, 0),
+    ("f32", 1 << 19, (1 << 19) + 4, (1 << 19) + 12, 0),
 ]
 
 
