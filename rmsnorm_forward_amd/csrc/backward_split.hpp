@@ -30,8 +30,9 @@
 // The column sums of the partial rows follow (norm_colsum_kernel), so
 // dgamma and dbeta are summed in a fixed order throughout.
 //
-// On request, norm_bwd_pass_kernel does it in one pass (dy and x read once,
-// an ordinary launch): teams of S workgroups, one per chunk of a row, walk
+// norm_bwd_pass_kernel does it in one pass (dy and x read once, an ordinary
+// launch), where the planner finds it faster or on request: teams of S
+// workgroups, one per chunk of a row, walk
 // the rows; each keeps its chunk of dy and x in registers, publishes its
 // chunk sums in the row's slot for it (the forward single pass's protocol:
 // a slot holds its value's bits inverted, zero meaning "not yet"), loads its
