@@ -394,17 +394,19 @@ int make_plan(int op, int64_t M, int64_t N, int dtype, bool aligned, const Overr
         // 64 x 2^20 58.9 vs 53.9, 512 x 2^18 118.9 vs 102.2, 2048 x 2^18
         // 468.9 vs 392.0; RMS f32 256 x 2^20 469.7 vs 396.2; LN f32
         // 64 x 2^20 119.4 vs 113.5, 256 x 2^20 477.3 vs 429.8).  LayerNorm
-        // with 16-bit I/O keeps two kernels: level or slower in one pass
-        // (LN bf16 64 x 2^20 62.8 vs 63.2, 1024 x 131072 121.3 vs 124.4,
-        // f16 128 x 2^19 63.2 vs 65.9).  The residual add keeps two kernels.
+        // with 16-bit I/O takes it only for few rows per team (see
+        // kPassLn16MaxRowsPerTeam).  The residual add keeps two kernels.
         // The pass runs when every chunk of a row can be resident; asked for
         // and impossible, the call fails; chosen automatically and
         // impossible (no device, say), the two kernels run.  Realigned x
         // takes the two kernels: the pass kernel has no registers to spare
         // for the realignment (LayerNorm bf16: 121 VGPRs of 128).
         // Rows of at least kPassWideMinChunks wide chunks take them when a
-        // row's worth can be resident (RMSNorm, fp32 LayerNorm).
-        const bool pass_auto = o.split_mode < 0 && p->epv > 1 && (op != OP_LN || dtype == NORM_F32) && !realign;
+        // row's worth can be resident (RMSNorm, fp32 LayerNorm).  LayerNorm
+        // with 16-bit I/O takes the pass only when each team has at most
+        // kPassLn16MaxRowsPerTeam rows to walk.
+        const bool ln16 = op == OP_LN && dtype != NORM_F32;
+        const bool pass_auto = o.split_mode < 0 && p->epv > 1 && !realign;
         const bool try_pass = (o.split_mode == SPLIT_PASS || pass_auto) && !has_add(op);
         const int64_t wv = int64_t(kPassWideWG) * kPassVPL;
         const int64_t wchunks = (NV + wv - 1) / wv;
@@ -415,7 +417,8 @@ int make_plan(int op, int64_t M, int64_t N, int dtype, bool aligned, const Overr
         const int64_t pchunks = (NV + pv - 1) / pv;
         const int64_t cap = try_pass ? resident_capacity(dtype, op, p->epv, false, wide) : 0;
         if (o.split_mode == SPLIT_PASS && !has_add(op) && cap < pchunks) return NORM_ERR_BAD_ARG;
-        if (try_pass && cap >= pchunks) {
+        const bool few_rows = cap >= pchunks && M <= int64_t(kPassLn16MaxRowsPerTeam) * (cap / pchunks);
+        if (try_pass && cap >= pchunks && (o.split_mode == SPLIT_PASS || !ln16 || few_rows)) {
             p->split_mode = SPLIT_PASS;
             p->wg = pwg;
             p->vpl = kPassVPL;

@@ -471,7 +471,7 @@ void norm_bwd_pass_kernel(const typename T::storage* dy,      // dx may be writt
             }
             if (tid == 0) late = !have;
         }
-        __syncthreads();
+        lds_barrier();
         if (late) {
             // recompute: every chunk's sums of the row from dy and x,
             // published (the bits its own workgroup publishes), then the sum
@@ -488,7 +488,7 @@ void norm_bwd_pass_kernel(const typename T::storage* dy,      // dx may be writt
                 if (tid == 0) row_sums = r;
                 depart_row(dep + row * 64, rsl, S);
             }
-            __syncthreads();
+            lds_barrier();
             fetch(row, q);
             ready(q);
         }
@@ -525,7 +525,7 @@ void norm_bwd_pass_kernel(const typename T::storage* dy,      // dx may be writt
             asm volatile("" : "+v"(o));
             if (col_ok[j]) out[j].put_stream(dxr + o);
         }
-        __syncthreads();           // `row_sums` and `late` are rewritten for the next row
+        lds_barrier();           // `row_sums` and `late` are rewritten for the next row
     };
 
     // two row register sets, the loop unrolled by two: the next row's loads

@@ -162,6 +162,18 @@ constexpr int kPassVPL = MI355_PASS_VPL;
 #endif
 constexpr int kPassWideWG = MI355_PASS_WIDE_WG;
 constexpr int kPassWideMinChunks = 16;
+// LayerNorm with 16-bit I/O takes the single pass by itself only when every
+// team walks at most this many rows: there the two kernels' second launch
+// and second read of x cost more than the teams' wait.  Measured on MI355X
+// (steady state, us, two kernels / single pass, rows per team): bf16 256 x
+// 131072 34.4 / 29.5 (2), 128 x 2^18 34.1 / 29.5 (2), 64 x 2^19 35.0 / 30.2
+// (2), 16 x 2^21 35.0 / 32.1 (2), 8 x 2^22 38.1 / 34.4 (2), 48 x 2^20 48.9 /
+// 45.9 (3), 16 x 2^20 18.6 / 17.2 (1); fp16 64 x 2^19 34.4 / 30.9, 256 x
+// 131072 34.6 / 31.0 (2).  From four rows per team the two are level or the
+// two kernels win: bf16 64 x 2^20 63.9 / 63.5 (4), 512 x 131072 63.8 / 63.6
+// (4), 16 x 2^22 69.0 / 72.4 (4), 128 x 2^20 123.6 / 126.1 (8), 512 x 2^18
+// 122.9 / 124.9 (8); fp16 128 x 2^19 64.8 / 65.8 (4).
+constexpr int kPassLn16MaxRowsPerTeam = 3;
 // Two-kernel split: rows per pair of launches are chosen so that one batch of
 // x (about this many bytes) mostly stays in the 256 MB Infinity Cache between the
 // statistics pass and the normalising pass.

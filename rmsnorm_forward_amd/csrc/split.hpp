@@ -51,6 +51,18 @@
 
 namespace mi355norm {
 
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// waits for every global load and store in flight (s_waitcnt vmcnt(0)
+// before s_barrier), which in the single passes would stall on the next
+// row's chunk streaming in and on the previous row's stores.  Where it is
+// used the wavefronts exchange only LDS values (partial sums, the row's
+// statistics, the late flag), so the LDS counter is all that must drain.
+// The memory clobber keeps the compiler from moving memory accesses across
+// it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // workgroup-wide sum (WG/64 wavefronts), bitwise identical in every lane
 template <int WG>
 __device__ __forceinline__ float wg_sum(float v, float* slots) {
@@ -59,7 +71,7 @@ __device__ __forceinline__ float wg_sum(float v, float* slots) {
         constexpr int W = WG / 64;
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         if (lane_id() == 0) slots[wave] = v;
-        __syncthreads();
+        lds_barrier();
         float s = slots[0];
 #pragma unroll
         for (int w = 1; w < W; ++w) s += slots[w];
@@ -466,7 +478,7 @@ void norm_split_pass_kernel(const typename T::storage* __restrict__ x,
             }
             if (tid == 0) late = !have;
         }
-        __syncthreads();
+        lds_barrier();
         if (late) {
             // recompute: every chunk's partial of the row from x, published
             // (the same bits its own workgroup publishes), then the merge
@@ -480,7 +492,7 @@ void norm_split_pass_kernel(const typename T::storage* __restrict__ x,
                 if (tid == 0) stats = st;
                 depart_row(dep + row * 64, rs, S);
             }
-            __syncthreads();
+            lds_barrier();
             ch.load(xr, c, NV);
         }
         const float2 st = stats;
@@ -489,7 +501,7 @@ void norm_split_pass_kernel(const typename T::storage* __restrict__ x,
             if (rstd_out) rstd_out[row] = st.y;
         }
         ch.template apply<RMS, Q8>(row_out<T, Q8>(y, row, ld.y), gamma, beta, K, st.x, st.y, qinv);
-        __syncthreads();           // `stats` and `late` are rewritten for the next row
+        lds_barrier();           // `stats` and `late` are rewritten for the next row
     }
 }
 

@@ -367,17 +367,19 @@ def test_split_statistics_shared_by_all_chunks():
 
 
 def test_two_kernel_split_is_the_default_and_agrees_with_the_single_pass(monkeypatch):
-    """The long-row configuration runs the two-kernel split by default.  It
-    and the single pass (different chunk sizes, so different partials) both
-    meet the oracle's bar, and their statistics agree to fp32 rounding."""
+    """The long-row configuration runs the two-kernel split by default.  The
+    two kernels and the single pass (different chunk sizes, so different
+    partials) both meet the oracle's bar, and their statistics agree to fp32
+    rounding."""
     import rmsnorm_forward_amd as rn
     d = dict(kv.split("=") for kv in rn.norm_describe("ln", 64, 1 << 20, "bf16").split())
     assert d["path"] == "split" and d["mode"] == "two", d
     inp = inputs("ln", "bf16", 40, 1 << 18, seed=61)
     monkeypatch.setenv("MI355NORM_PATH", "splitpass")
     a = run("ln", "bf16", inp["x"], inp["gamma"], inp["beta"], 1e-5)
-    monkeypatch.delenv("MI355NORM_PATH")
+    monkeypatch.setenv("MI355NORM_PATH", "split2")
     b = run("ln", "bf16", inp["x"], inp["gamma"], inp["beta"], 1e-5)
+    monkeypatch.delenv("MI355NORM_PATH")
     compare("ln", "bf16", inp["x"], inp["gamma"], inp["beta"], 1e-5, *a, what="single pass")
     compare("ln", "bf16", inp["x"], inp["gamma"], inp["beta"], 1e-5, *b, what="two-kernel")
     assert np.max(np.abs(a[2] / b[2] - 1)) < 1e-5 and np.max(np.abs(a[1] - b[1])) < 1e-4
@@ -386,10 +388,11 @@ def test_two_kernel_split_is_the_default_and_agrees_with_the_single_pass(monkeyp
 @pytest.mark.parametrize("dtype,N,offset", [("bf16", 140000, 0), ("f32", 70000, 0), ("f16", 20000, 1)])
 @pytest.mark.parametrize("op", ["ln", "rms"])
 def test_split_row_batches(monkeypatch, op, dtype, N, offset):
-    """Rows split across workgroups run in batches (here 3 rows, so batches of
-    3, 3 and 1): every batch's rows, means and rstds land at their own offsets
-    and meet the oracle's bar."""
+    """The two kernels run rows split across workgroups in batches (here 3
+    rows, so batches of 3, 3 and 1): every batch's rows, means and rstds land
+    at their own offsets and meet the oracle's bar."""
     e = 4 if dtype == "f32" else 2
+    monkeypatch.setenv("MI355NORM_PATH", "split2")
     monkeypatch.setenv("MI355NORM_SPLIT_BATCH", str(3 * N * e))
     M = 7
     print(f"[gpu] split batches {op} {dtype} M={M} N={N} offset={offset}", flush=True)
@@ -524,21 +527,24 @@ def test_longest_rows(monkeypatch, op, dtype, offset, mode):
 def test_split_mode_chosen_automatically():
     """On the GPU, rows split across workgroups take the single pass for
     RMSNorm (plain and with FP8 output) and fp32 LayerNorm on 16-byte
-    vectors, and the two kernels for LayerNorm with 16-bit I/O, the residual
-    add and rows that are not 16-byte vectors."""
+    vectors, and for LayerNorm with 16-bit I/O when every team walks at most
+    three rows; otherwise the two kernels, which the residual add and rows
+    that are not 16-byte vectors always take."""
     import rmsnorm_forward_amd as rn
     N = 1 << 20
-    mode = lambda op, dtype, aligned=True: dict(kv.split("=") for kv in
-                                                rn.norm_describe(op, 64, N, dtype, aligned=aligned).split())["mode"]
+    mode = lambda op, dtype, aligned=True, M=64: dict(kv.split("=") for kv in
+                                                      rn.norm_describe(op, M, N, dtype, aligned=aligned).split())["mode"]
     assert mode("rms", "bf16") == "pass" and mode("rms", "f32") == "pass" and mode("rms", "f16") == "pass"
     assert mode("rms_fp8", "bf16") == "pass"
     assert mode("ln", "f32") == "pass"
-    assert mode("ln", "bf16") == "two" and mode("ln", "f16") == "two"
+    assert mode("ln", "bf16") == "two" and mode("ln", "f16") == "two"          # 4 rows per team
+    assert mode("ln", "bf16", M=16) == "pass" and mode("ln", "f16", M=48) == "pass"   # 1 and 3 rows per team
+    assert mode("ln", "bf16", aligned=False, M=16) == "two"
     assert mode("add_rms", "bf16") == "two" and mode("add_rms", "f32") == "two"
     assert mode("rms", "bf16", aligned=False) == "two"
     wg = lambda op, dtype, n: dict(kv.split("=") for kv in rn.norm_describe(op, 64, n, dtype).split())["wg"]
     # wide chunks from 16 of them a row (2^17 vectors); 512 lanes below, and
-    # always for LayerNorm with 16-bit I/O (taken only on request)
+    # always for LayerNorm with 16-bit I/O
     assert wg("rms", "bf16", N) == wg("rms_fp8", "f16", N) == wg("ln", "f32", N) == "1024"
     assert wg("rms", "f32", N // 2) == "1024" and wg("rms", "f32", N // 2 - 4) == "512"
     assert wg("rms", "bf16", N - 8) == "512" and wg("rms", "bf16", N // 4) == "512"
