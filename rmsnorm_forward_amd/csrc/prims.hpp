@@ -66,6 +66,19 @@ struct F16 {
     }
 };
 
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// waits for every global load and store in flight (s_waitcnt vmcnt(0)
+// before s_barrier), which would stall the reductions on loads still in
+// flight (the single passes' next row streaming into LDS, hoisted gamma
+// loads) and on earlier stores (the previous row's y, the residual sum).
+// Where it is used the wavefronts exchange only LDS values (partial sums,
+// a row's statistics, a flag), so the LDS counter is all that must drain.
+// The memory clobber keeps the compiler from moving memory accesses across
+// it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // --------------------------------------------------------------------------
 // Cache policy.  x is read exactly once and y written exactly once, so their
 // accesses carry the nontemporal hint (streamed through the caches without

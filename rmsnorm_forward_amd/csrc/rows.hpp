@@ -41,7 +41,7 @@ __device__ __forceinline__ float team_reduce(float v, float* slots, int wave_in_
     if constexpr (TEAM > 64) {
         constexpr int WPT = TEAM / 64;
         if (lane_id() == 0) slots[wave_in_team] = v;
-        __syncthreads();
+        lds_barrier();
         float s = slots[0];
 #pragma unroll
         for (int w = 1; w < WPT; ++w) s += slots[w];

@@ -51,18 +51,6 @@
 
 namespace mi355norm {
 
-// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
-// waits for every global load and store in flight (s_waitcnt vmcnt(0)
-// before s_barrier), which in the single passes would stall on the next
-// row's chunk streaming in and on the previous row's stores.  Where it is
-// used the wavefronts exchange only LDS values (partial sums, the row's
-// statistics, the late flag), so the LDS counter is all that must drain.
-// The memory clobber keeps the compiler from moving memory accesses across
-// it.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 // workgroup-wide sum (WG/64 wavefronts), bitwise identical in every lane
 template <int WG>
 __device__ __forceinline__ float wg_sum(float v, float* slots) {
