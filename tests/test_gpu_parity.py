@@ -550,6 +550,20 @@ def test_split_mode_chosen_automatically():
     assert wg("rms", "bf16", N - 8) == "512" and wg("rms", "bf16", N // 4) == "512"
 
 
+@pytest.mark.parametrize("dtype,M,N", [("bf16", 16, 1 << 20), ("f16", 40, 1 << 19), ("bf16", 300, 131072 + 8)])
+def test_ln16_single_pass_for_few_rows_per_team(dtype, M, N):
+    """LayerNorm with 16-bit I/O takes the single pass by itself when every
+    team walks at most three rows (here one to three, the last shape with a
+    ragged last chunk), and meets the oracle's bar."""
+    import rmsnorm_forward_amd as rn
+    plan = dict(kv.split("=") for kv in rn.norm_describe("ln", M, N, dtype).split())
+    assert plan["mode"] == "pass" and M <= 3 * int(plan["teams"]), plan
+    inp = inputs("ln", dtype, M, N, seed=M + 5)
+    print(f"[gpu] LN {dtype} {M}x{N} single pass by itself: {plan['teams']} teams", flush=True)
+    y, mean, rstd = run("ln", dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5)
+    compare("ln", dtype, inp["x"], inp["gamma"], inp["beta"], 1e-5, y, mean, rstd, what="LN 16-bit single pass")
+
+
 def test_single_pass_plan():
     """On the GPU the single pass plans whole teams of resident workgroups:
     the grid is teams x chunks and holds at least one row's chunks."""
