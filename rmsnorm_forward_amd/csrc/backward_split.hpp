@@ -482,6 +482,10 @@ void norm_bwd_pass_kernel(const typename T::storage* dy,      // dx may be writt
                 fetch_chunk(row, q, cc, okv);
                 const float2 s = chunk_sums(q, okv, gm);
                 if (tid == 0) publish_slot(rsl + cc, s);
+                // RMSNorm's sums have one reduction, whose LDS slots the
+                // next chunk's would otherwise rewrite while a wavefront
+                // still reads them
+                if constexpr (RMS) lds_barrier();
             }
             if (tid < 64) {
                 const float2 r = rowsum_read(read(rsl), S);

@@ -474,6 +474,10 @@ void norm_split_pass_kernel(const typename T::storage* __restrict__ x,
                 ch.load(xr, cc, NV);
                 const float2 q = ch.template partial<RMS>(K, NV, red);
                 if (tid == 0) publish_slot(rs + cc, q);
+                // RMSNorm's partial has one reduction, whose LDS slots the
+                // next chunk's would otherwise rewrite while a wavefront
+                // still reads them
+                if constexpr (RMS) lds_barrier();
             }
             if (tid < 64) {
                 const float2 st = row_stats<RMS>(read(rs), S, CE, N, eps);
