@@ -242,7 +242,8 @@ def test_single_pass_split_backward_in_place_and_deterministic(monkeypatch):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
-@pytest.mark.parametrize("op,dtype,M,N", [("ln", "bf16", 6, 1 << 18), ("rms", "f32", 5, 70001), ("ln", "f16", 40, 40000)])
+@pytest.mark.parametrize("op,dtype,M,N", [("ln", "bf16", 6, 1 << 18), ("rms", "f32", 5, 70001), ("ln", "f16", 40, 40000),
+                                         ("rms", "bf16", 6, 1 << 18)])
 def test_single_pass_split_backward_recompute_gives_the_same_bits(monkeypatch, op, dtype, M, N):
     """The bounded wait, forced from the host to give up at once: every
     workgroup computes its rows' chunk sums from dy and x itself.  dx, dgamma

@@ -417,8 +417,11 @@ def test_split_workspace_reused_across_shapes(monkeypatch, mode):
                     what=f"reuse {mode} {op} M={M} N={N}")
 
 
+# RMSNorm on 16-byte vectors: 16 wide chunks a row (bf16) and 8 chunks of
+# 512 lanes (f16), whose one-reduction partials the recompute runs back to back
 @pytest.mark.parametrize("op,dtype,M,N,offset", [("ln", "bf16", 6, 1 << 18, 0), ("rms", "f32", 5, 100003, 1),
-                                                  ("ln", "f16", 40, 70000, 0), ("ln", "f32", 33, 65544, 0)])
+                                                  ("ln", "f16", 40, 70000, 0), ("ln", "f32", 33, 65544, 0),
+                                                  ("rms", "bf16", 8, 1 << 20, 0), ("rms", "f16", 6, 1 << 18, 0)])
 def test_single_pass_recompute_gives_the_same_bits(monkeypatch, op, dtype, M, N, offset):
     """The single pass's bounded wait, forced from the host to give up at
     once: every workgroup then computes all of its rows' partials from x
